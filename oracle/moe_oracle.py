@@ -1,0 +1,328 @@
+"""Plain CPU oracle for the forward pass of one Mixture-of-Experts layer.
+
+TEST INFRASTRUCTURE ONLY.  This module is the independent definition that the
+GPU path is checked against.  Only the test suite, the smoke check and the
+CPU-baseline leg of the benchmark may import it; the product path never does.
+It shares no code, table or helper with the HIP library.
+
+Everything is computed in float64 from the exact values of the inputs (bf16 or
+fp32 inputs convert to float64 without rounding).  Loops are written the way the
+method is stated, not the way a GPU would run it.  Library primitives used as
+single steps: numpy matmul, exp/log1p, and a stable argsort.
+
+Sources (all on the page "MoE 与专家并行", hs-black.github.io/posts/scaling-moe,
+unless another page is named):
+  * SwiGLU expert, section "从稠密 FFN 到 MoE", equation FFN(u).
+  * Layer output with residual, same section, equation h'_t = u_t + sum g FFN.
+  * Router logits H = U W_r, section "路由器：打分、top-k、加权求和".
+  * Noisy top-k logits, same section, equation G(x) (Shazeer 2017).
+  * Scoring/gating variants, section "softmax 门控还是 sigmoid 门控", table.
+  * Capacity C = ceil(CF * T * k / E) and token-order fill with drops,
+    section "专家容量与丢 token", equation C and its figure; the GShard fill
+    order (all first choices, then second choices) in the same section.
+    The top-1 form ceil((T/E) * capacity_factor) is on the page
+    "Ai大模型训练教程" (aissn.com/133.html), section on capacity and padding.
+  * f_i, P_i and L_aux = alpha * E * sum f_i P_i, section
+    "负载均衡辅助损失：推导与梯度"; for sigmoid scores P uses the scores
+    normalised over all experts (same section, DeepSeek-V3 paragraph).
+  * MaxVio, section "无辅助损失的负载均衡".
+
+Readings where the pages are silent or ambiguous are listed in the design doc of the
+repository; the ones that change arithmetic are restated next to the code.
+
+Pins: every function here is pinned by tests/test_oracle_pins.py against the
+pages' worked numbers, closed forms, special cases that reduce to library
+routines, and brute force on tiny inputs.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+SOFTMAX = "softmax"
+SIGMOID = "sigmoid"
+GATE_RAW = "raw"          # g = s for the selected experts (Switch, DeepSeekMoE)
+GATE_RENORM = "renorm"    # g = s / sum over selected s (GShard top-2, V3, Mixtral)
+FILL_RANK_MAJOR = "rank_major"    # all first choices in token order, then all second ...
+FILL_TOKEN_MAJOR = "token_major"  # token by token, each token's choices in rank order
+CAP_ASSIGNMENTS = "assignments"   # C = ceil(CF * T * k / E)
+CAP_TOKENS = "tokens"             # C = ceil((T / E) * CF)
+
+
+def f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------- router
+def softplus(v: np.ndarray) -> np.ndarray:
+    """log(1 + e^v), written in the overflow-free form log(e^0 + e^v)."""
+    return np.logaddexp(0.0, v)
+
+
+def router_logits(U, W_r, b_r=None, W_noise=None, noise=None) -> np.ndarray:
+    """Routing logits H[t, i] for every token t and expert i.
+
+    H = U W_r with W_r of shape [h, E] (router section, eq. H = U W_r).
+    b_r, when given, is a per-expert bias added to every token's logits.
+    W_noise/noise, when given, add the noisy top-k term
+    noise[t, i] * softplus((U W_noise)[t, i]) (eq. G(x)); noise holds the
+    standard-normal draws, supplied by the caller.
+    """
+    U = f64(U)
+    H = U @ f64(W_r)
+    if b_r is not None:
+        H = H + f64(b_r)[None, :]
+    if W_noise is not None:
+        if noise is None:
+            raise ValueError("noisy routing needs the standard-normal draws")
+        H = H + f64(noise) * softplus(U @ f64(W_noise))
+    return H
+
+
+def scores(H, score: str) -> np.ndarray:
+    """Affinities s[t, i]: softmax over the experts of each token, or sigmoid."""
+    H = f64(H)
+    if score == SOFTMAX:
+        m = H.max(axis=1, keepdims=True)
+        e = np.exp(H - m)
+        return e / e.sum(axis=1, keepdims=True)
+    if score == SIGMOID:
+        return 1.0 / (1.0 + np.exp(-H))
+    raise ValueError(score)
+
+
+def select_topk(H, k: int) -> np.ndarray:
+    """The k experts of each token, best first.
+
+    Experts are ordered by the key (-H[t, i], i): larger logit first, and the
+    lower expert index first among equal logits.  Softmax and sigmoid are
+    strictly increasing, so this is the top-k of the scores in exact arithmetic.
+    A stable argsort of -H realises exactly this key.
+    """
+    H = f64(H)
+    order = np.argsort(-H, axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+def gates(s, idx, gate: str) -> np.ndarray:
+    """Gate values of the selected experts, in rank order.
+
+    RAW: g = s.  RENORM: g = s / sum of the selected s.  For softmax scores the
+    renormalised gates equal a softmax over the selected logits, which is also
+    Softmax(KeepTopK(H)) of the noisy router.
+    """
+    sel = np.take_along_axis(f64(s), np.asarray(idx), axis=1)
+    if gate == GATE_RAW:
+        return sel
+    if gate == GATE_RENORM:
+        return sel / sel.sum(axis=1, keepdims=True)
+    raise ValueError(gate)
+
+
+# --------------------------------------------------------------------------- capacity
+def capacity(T: int, E: int, k: int, capacity_factor: float,
+             cap_mode: str = CAP_ASSIGNMENTS, min_capacity: int = 0) -> int:
+    """Expert capacity C as an exact rational ceiling.
+
+    ASSIGNMENTS: C = ceil(CF * T * k / E) (capacity section, eq. C).
+    TOKENS:      C = ceil((T / E) * CF), the top-1 form of the training-course page.
+    capacity_factor <= 0 means no capacity limit (dropless): C = T, which no
+    expert can exceed because a token picks an expert at most once.
+    The result is raised to min_capacity when that is larger.
+    """
+    if capacity_factor <= 0:
+        return max(T, int(min_capacity))
+    n = T * k if cap_mode == CAP_ASSIGNMENTS else T
+    if cap_mode not in (CAP_ASSIGNMENTS, CAP_TOKENS):
+        raise ValueError(cap_mode)
+    C = math.ceil(Fraction(capacity_factor) * n / E)
+    return max(C, int(min_capacity))
+
+
+def fill(idx, E: int, C: int, order: str = FILL_RANK_MAJOR) -> dict:
+    """Give every (token, rank) assignment its place in its expert's buffer.
+
+    Assignments are visited one at a time in fill order; each takes the next
+    free position of its expert; positions >= C are dropped (the token then
+    passes only the residual for that expert).  Kept assignments of expert e
+    occupy rows offset[e] .. offset[e] + kept[e] - 1 of the permuted matrix, in
+    fill order.  Returns count (before the cut), kept, offset[E+1], slot[T, k]
+    (row index, -1 when dropped), pos[T, k] and row_token[rows].
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    if order == FILL_RANK_MAJOR:
+        visit = [(t, r) for r in range(k) for t in range(T)]
+    elif order == FILL_TOKEN_MAJOR:
+        visit = [(t, r) for t in range(T) for r in range(k)]
+    else:
+        raise ValueError(order)
+    counter = [0] * E
+    pos = np.full((T, k), -1, dtype=np.int64)
+    for t, r in visit:
+        e = int(idx[t, r])
+        pos[t, r] = counter[e]
+        counter[e] += 1
+    count = np.array(counter, dtype=np.int64)
+    kept = np.minimum(count, C)
+    offset = np.zeros(E + 1, dtype=np.int64)
+    offset[1:] = np.cumsum(kept)
+    slot = np.full((T, k), -1, dtype=np.int64)
+    row_token = np.full(int(offset[-1]), -1, dtype=np.int64)
+    for t, r in visit:
+        if pos[t, r] < C:
+            row = int(offset[idx[t, r]] + pos[t, r])
+            slot[t, r] = row
+            row_token[row] = t
+    return {"count": count, "kept": kept, "offset": offset, "slot": slot,
+            "pos": pos, "row_token": row_token, "C": C}
+
+
+# --------------------------------------------------------------------------- experts
+def silu(v: np.ndarray) -> np.ndarray:
+    """SiLU(v) = v * sigmoid(v) = v / (1 + e^-v)."""
+    v = f64(v)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def swiglu_expert(x, W_gate, W_up, W_down) -> np.ndarray:
+    """FFN(u) = W_down (SiLU(W_gate u) * (W_up u)) for each row u of x.
+
+    W_gate, W_up have shape [f, h] and W_down [h, f] (FFN equation), so for a
+    row-major batch x [n, h] the products are x W_gate^T and a W_down^T.
+    """
+    x = f64(x)
+    a = silu(x @ f64(W_gate).T) * (x @ f64(W_up).T)
+    return a @ f64(W_down).T
+
+
+# --------------------------------------------------------------------------- stats
+def load_stats(s, idx, fill_result: dict, score: str) -> dict:
+    """Load-balance statistics of one batch.
+
+    count_e: assignments to expert e before the capacity cut.
+    f_e = count_e / (T k): fraction of the T k assignments (sums to 1).
+    P_e = mean over tokens of s_e (softmax), or of s_e / sum_j s_j (sigmoid).
+    aux = E * sum_e f_e P_e (alpha = 1; a caller scales it).
+    MaxVio = (max_e count_e - mean count) / mean count, mean = T k / E.
+    n_dropped = sum_e (count_e - kept_e).
+    """
+    s = f64(s)
+    T, k = np.asarray(idx).shape
+    E = s.shape[1]
+    count = fill_result["count"].astype(np.float64)
+    f = count / (T * k)
+    if score == SOFTMAX:
+        st = s
+    elif score == SIGMOID:
+        st = s / s.sum(axis=1, keepdims=True)
+    else:
+        raise ValueError(score)
+    prob_sum = st.sum(axis=0)
+    P = prob_sum / T
+    aux = E * float(np.sum(f * P))
+    mean = T * k / E
+    maxvio = (count.max() - mean) / mean
+    n_dropped = int(np.sum(fill_result["count"] - fill_result["kept"]))
+    return {"f": f, "P": P, "prob_sum": prob_sum, "aux": aux, "maxvio": float(maxvio),
+            "n_dropped": n_dropped}
+
+
+# --------------------------------------------------------------------------- layer
+def route(H, k: int, score: str, gate: str, C: int, fill_order: str = FILL_RANK_MAJOR) -> dict:
+    """All routing decisions from given logits: top-k, gates, fill and statistics."""
+    H = f64(H)
+    s = scores(H, score)
+    idx = select_topk(H, k)
+    g = gates(s, idx, gate)
+    fr = fill(idx, H.shape[1], C, fill_order)
+    st = load_stats(s, idx, fr, score)
+    out = {"logits": H, "s": s, "idx": idx, "gate": g}
+    out.update(fr)
+    out.update(st)
+    return out
+
+
+def combine(U, Y, slot, gate) -> np.ndarray:
+    """out_t = u_t + sum over kept ranks r (in rank order) of g[t, r] * Y[slot[t, r]].
+
+    Dropped assignments add nothing and the remaining gates are not rescaled;
+    a token with every assignment dropped is returned as its residual u_t.
+    """
+    out = f64(U).copy()
+    Y = f64(Y)
+    slot = np.asarray(slot)
+    g = f64(gate)
+    for r in range(slot.shape[1]):
+        m = slot[:, r] >= 0
+        out[m] += g[m, r, None] * Y[slot[m, r]]
+    return out
+
+
+def expert_outputs(X, offset, W_gate, W_up, W_down) -> np.ndarray:
+    """Y rows for the permuted matrix X: rows offset[e]..offset[e+1]-1 use expert e."""
+    X = f64(X)
+    Y = np.zeros((X.shape[0], np.asarray(W_down).shape[1]), dtype=np.float64)
+    for e in range(len(offset) - 1):
+        a, b = int(offset[e]), int(offset[e + 1])
+        if b > a:
+            Y[a:b] = swiglu_expert(X[a:b], W_gate[e], W_up[e], W_down[e])
+    return Y
+
+
+def layer_forward(U, W_r, W_gate, W_up, W_down, *, k: int, score: str, gate: str,
+                  capacity_factor: float, cap_mode: str = CAP_ASSIGNMENTS,
+                  fill_order: str = FILL_RANK_MAJOR, min_capacity: int = 0,
+                  b_r=None, W_noise=None, noise=None, logits=None) -> dict:
+    """The whole layer for small inputs.
+
+    logits, when given, replaces the router product (used to route from exactly
+    the logits another implementation produced).
+    """
+    U = f64(U)
+    T = U.shape[0]
+    E = np.asarray(W_r).shape[1]
+    H = router_logits(U, W_r, b_r, W_noise, noise) if logits is None else f64(logits)
+    C = capacity(T, E, k, capacity_factor, cap_mode, min_capacity)
+    r = route(H, k, score, gate, C, fill_order)
+    X = U[r["row_token"]]
+    Y = expert_outputs(X, r["offset"], W_gate, W_up, W_down)
+    r["X"] = X
+    r["Y"] = Y
+    r["out"] = combine(U, Y, r["slot"], r["gate"])
+    return r
+
+
+def token_outputs(tokens, U, idx, slot, gate, expert_weights) -> np.ndarray:
+    """out_t for a few tokens, one at a time.
+
+    expert_weights(e) returns (W_gate[e], W_up[e], W_down[e]); only the experts
+    the given tokens keep are requested.
+    """
+    U = f64(U)
+    res = []
+    for t in tokens:
+        o = U[t].copy()
+        for r in range(idx.shape[1]):
+            if slot[t, r] >= 0:
+                Wg, Wu, Wd = expert_weights(int(idx[t, r]))
+                o += float(gate[t, r]) * swiglu_expert(U[t:t + 1], Wg, Wu, Wd)[0]
+        res.append(o)
+    return np.stack(res) if res else np.zeros((0, U.shape[1]))
+
+
+def dense_masked_forward(U, W_gate, W_up, W_down, g_dense) -> np.ndarray:
+    """The layer equation taken literally: every expert on every token.
+
+    out_t = u_t + sum over all E experts of g_dense[t, e] * FFN_e(u_t), where
+    g_dense holds the gate of a kept assignment and 0 elsewhere.  Only for tiny
+    inputs; used to check the sparse path above by brute force.
+    """
+    U = f64(U)
+    out = U.copy()
+    for e in range(np.asarray(W_gate).shape[0]):
+        out += f64(g_dense)[:, e:e + 1] * swiglu_expert(U, W_gate[e], W_up[e], W_down[e])
+    return out

@@ -1,0 +1,398 @@
+"""Pins of the CPU oracle to facts fixed outside it.
+
+Each test ties one oracle function to something other than the oracle itself:
+numbers printed on the pages (tests/golden, each with its citation), closed
+forms, special cases that reduce to a library routine (torch in float64), or
+brute force on tiny inputs.  The oracle's own formulas are never retyped here.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ----------------------------------------------------------------- printed examples
+def test_renorm_figure_direct():
+    g = golden("renorm_figure.json")
+    s = np.array([[0.80, 0.49, 0.10, 0.05, 0.20, 0.01, 0.30, 0.02]])
+    idx = O.select_topk(np.log(s), 2)
+    assert idx.tolist() == [[0, 1]]
+    gates = O.gates(s, idx, O.GATE_RENORM)
+    np.testing.assert_allclose(np.round(gates[0], g["printed_decimals"]), g["gates"])
+    assert abs(gates.sum() - 1.0) < 1e-15
+
+
+def test_renorm_figure_through_sigmoid_router():
+    # Logits whose sigmoid is exactly the printed scores: ln(0.8/0.2), ln(0.49/0.51).
+    g = golden("renorm_figure.json")
+    H = np.full((1, 8), -3.0)
+    H[0, 3] = math.log(4.0)
+    H[0, 6] = math.log(49.0 / 51.0)
+    r = O.route(H, 2, O.SIGMOID, O.GATE_RENORM, C=1)
+    assert r["idx"].tolist() == [[3, 6]]
+    np.testing.assert_allclose(r["s"][0, [3, 6]], g["selected_scores"], rtol=1e-14)
+    np.testing.assert_allclose(np.round(r["gate"][0], 2), g["gates"])
+
+
+def test_renorm_figure_through_softmax_router():
+    # softmax + renorm depends only on the gap of the two selected logits.
+    g = golden("renorm_figure.json")
+    a = 0.3
+    H = np.array([[a - 5, a, a - 4, a - math.log(0.80 / 0.49), a - 6, a - 7, a - 3, a - 2]])
+    r = O.route(H, 2, O.SOFTMAX, O.GATE_RENORM, C=1)
+    assert r["idx"].tolist() == [[1, 3]]
+    np.testing.assert_allclose(r["gate"][0], [0.80 / 1.29, 0.49 / 1.29], rtol=1e-14)
+    np.testing.assert_allclose(np.round(r["gate"][0], 2), g["gates"])
+
+
+def test_capacity_worked_numbers():
+    g = golden("capacity_examples.json")
+    fig, w = g["figure"], g["worked"]
+    assert O.capacity(fig["T"], fig["E"], fig["k"], fig["capacity_factor"]) == fig["C"]
+    C = O.capacity(w["T"], w["E"], w["k"], w["capacity_factor"])
+    assert C == w["C"]
+    assert w["T"] * w["k"] // w["E"] == w["balanced"]
+    assert w["hot_load"] - C == w["hot_dropped"]
+    assert C - w["cold_load"] == w["cold_idle"]
+    # the top-1 form ceil((T/E) * CF) agrees with the assignments form at k = 1
+    for T, E, cf in [(12, 4, 1.0), (8192, 128, 1.25), (1000, 7, 1.1), (5, 3, 0.3)]:
+        assert O.capacity(T, E, 1, cf, O.CAP_TOKENS) == O.capacity(T, E, 1, cf)
+    # and differs from it at k > 1, as the two readings predict (640 vs 80)
+    assert O.capacity(4096, 64, 8, 1.25, O.CAP_TOKENS) == 80
+
+
+def test_capacity_exact_ceiling_and_floor():
+    # exact rational ceiling: 1.25 * 8 * 2 / 8 = 2.5 -> 3; 1.25 * 16 / 8 = 2.5 -> 3
+    assert O.capacity(8, 8, 2, 1.25) == 3
+    assert O.capacity(16, 8, 1, 1.25) == 3
+    assert O.capacity(64, 8, 1, 1.0) == 8          # exact integer stays
+    assert O.capacity(10, 3, 1, 0.1) == 1          # the double 0.1 is just above 1/10
+    assert Fraction(0.1) > Fraction(1, 10)
+    assert O.capacity(10, 3, 1, 0.1, min_capacity=4) == 4
+    assert O.capacity(100, 4, 2, 0.0) == 100       # dropless: nothing can exceed T
+    assert O.capacity(256, 8, 2, 1.25) == 80
+    assert O.capacity(4096, 256, 8, 2.0) == 256
+    assert O.capacity(32768, 64, 2, 1.0) == 1024
+
+
+def test_capacity_figure_fill():
+    # Rebuild the figure's case with loads (5, 3, 3, 1) over 12 tokens in an
+    # interleaved token order; capacity 3.  The two dropped tokens must be the
+    # last two that chose expert 1 (index 0 here), in token order.
+    g = golden("capacity_examples.json")["figure"]
+    choice = [0, 1, 0, 2, 1, 0, 3, 2, 0, 1, 2, 0]
+    idx = np.array(choice)[:, None]
+    C = O.capacity(g["T"], g["E"], g["k"], g["capacity_factor"])
+    fr = O.fill(idx, g["E"], C)
+    assert fr["count"].tolist() == [5, 3, 3, 1]
+    assert fr["count"][0] == g["printed_loads"]["1"]
+    assert fr["count"][3] == g["printed_loads"]["4"]
+    dropped = [t for t in range(12) if fr["slot"][t, 0] < 0]
+    assert dropped == [8, 11]
+    assert len(dropped) == g["printed_dropped"]["1"]
+    assert C - fr["kept"][3] == g["printed_padding"]["4"]
+    assert fr["kept"].tolist() == [3, 3, 3, 1]
+    assert fr["offset"].tolist() == [0, 3, 6, 9, 10]
+    # expert 0's kept rows are tokens 0, 2, 5 in that order
+    assert fr["row_token"][:3].tolist() == [0, 2, 5]
+
+
+def test_zloss_bf16_example():
+    g = golden("zloss_bf16_softmax.json")
+    H = np.array([g["logits"]], dtype=np.float32)
+    s32 = O.scores(H, O.SOFTMAX)[0, 0]
+    assert round(s32, g["printed_decimals"]) == g["softmax_first_fp32_logits"]
+    assert abs(s32 - 1.0 / (1.0 + 10.0 * math.exp(-0.5))) < 1e-14
+    Hb = torch.tensor(g["logits"]).to(torch.bfloat16).double().numpy()[None, :]
+    sb = O.scores(Hb, O.SOFTMAX)[0, 0]
+    assert round(sb, g["printed_decimals"]) == g["softmax_first_bf16_logits"]
+    assert abs(sb - 1.0 / 11.0) < 1e-15
+
+
+# ----------------------------------------------------------------- selection
+def test_topk_ties_lower_index_wins():
+    H = np.zeros((5, 8))
+    idx = O.select_topk(H, 3)
+    assert (idx == np.array([0, 1, 2])).all()
+    s = O.scores(H, O.SOFTMAX)
+    np.testing.assert_allclose(O.gates(s, idx, O.GATE_RENORM), 1.0 / 3, rtol=1e-15)
+    np.testing.assert_allclose(O.gates(s, idx, O.GATE_RAW), 1.0 / 8, rtol=1e-15)
+    # partial tie: the two equal best logits keep index order
+    H = np.array([[0.5, 2.0, 1.0, 2.0]])
+    assert O.select_topk(H, 3).tolist() == [[1, 3, 2]]
+
+
+def test_topk_matches_python_sorted_and_torch():
+    r = rng(1)
+    H = np.round(r.normal(size=(50, 13)), 1)   # rounding creates many ties
+    idx = O.select_topk(H, 4)
+    for t in range(H.shape[0]):
+        ref = sorted(range(13), key=lambda i: (-H[t, i], i))[:4]
+        assert idx[t].tolist() == ref
+    vals = torch.topk(torch.from_numpy(H), 4, dim=1).values.numpy()
+    np.testing.assert_array_equal(np.take_along_axis(H, idx, 1), vals)
+
+
+def test_renorm_identity_topk_then_softmax():
+    # softmax -> renormalise over the selected == softmax of the selected logits
+    r = rng(2)
+    H = r.normal(size=(40, 16)) * 3
+    idx = O.select_topk(H, 4)
+    g = O.gates(O.scores(H, O.SOFTMAX), idx, O.GATE_RENORM)
+    ref = torch.softmax(torch.from_numpy(np.take_along_axis(H, idx, 1)), dim=1).numpy()
+    np.testing.assert_allclose(g, ref, rtol=1e-13)
+
+
+def test_scores_vs_library():
+    r = rng(3)
+    H = r.normal(size=(20, 9)) * 4
+    np.testing.assert_allclose(O.scores(H, O.SOFTMAX),
+                               torch.softmax(torch.from_numpy(H), 1).numpy(), rtol=1e-13)
+    np.testing.assert_allclose(O.scores(H, O.SIGMOID),
+                               torch.sigmoid(torch.from_numpy(H)).numpy(), rtol=1e-13)
+    # very large logits must not overflow (softmax is shift invariant)
+    Hbig = np.array([[800.0, 799.0, -800.0], [1e3, 1e3, 1e3]])
+    np.testing.assert_allclose(O.scores(Hbig, O.SOFTMAX),
+                               torch.softmax(torch.from_numpy(Hbig), 1).numpy(), rtol=1e-13)
+
+
+# ----------------------------------------------------------------- router
+def test_router_one_hot_rows_pick_rows_of_Wr():
+    r = rng(4)
+    h, E = 6, 5
+    W = r.normal(size=(h, E))
+    U = np.eye(h)[[3, 0, 5]]
+    np.testing.assert_array_equal(O.router_logits(U, W), W[[3, 0, 5]])
+
+
+def test_router_vs_library_with_bias_and_noise():
+    r = rng(5)
+    T, h, E = 7, 11, 6
+    U, W, Wn = r.normal(size=(T, h)), r.normal(size=(h, E)), r.normal(size=(h, E))
+    b, z = r.normal(size=E), r.normal(size=(T, E))
+    Ut, Wt, Wnt = map(torch.from_numpy, (U, W, Wn))
+    ref = F.linear(Ut, Wt.T) + torch.from_numpy(b) + torch.from_numpy(z) * F.softplus(F.linear(Ut, Wnt.T))
+    np.testing.assert_allclose(O.router_logits(U, W, b, Wn, z), ref.numpy(), rtol=1e-13, atol=1e-13)
+    # softplus stays finite and exact-ish far out
+    assert O.softplus(np.array([800.0]))[0] == 800.0
+    assert O.softplus(np.array([-800.0]))[0] == 0.0
+
+
+# ----------------------------------------------------------------- fill
+def brute_positions(idx, order):
+    """Position of each assignment = number of earlier assignments (in fill order) to its expert."""
+    T, k = idx.shape
+    seq = [(t, r) for r in range(k) for t in range(T)] if order == O.FILL_RANK_MAJOR \
+        else [(t, r) for t in range(T) for r in range(k)]
+    pos = np.zeros((T, k), dtype=np.int64)
+    for n, (t, r) in enumerate(seq):
+        pos[t, r] = sum(1 for (t2, r2) in seq[:n] if idx[t2, r2] == idx[t, r])
+    return pos
+
+
+@pytest.mark.parametrize("order", [O.FILL_RANK_MAJOR, O.FILL_TOKEN_MAJOR])
+def test_fill_brute_force(order):
+    r = rng(6)
+    T, E, k = 23, 5, 3
+    H = r.normal(size=(T, E)) + np.array([1.5, 0, 0, -1, 0.5])
+    idx = O.select_topk(H, k)
+    C = 4
+    fr = O.fill(idx, E, C, order)
+    pos = brute_positions(idx, order)
+    np.testing.assert_array_equal(fr["pos"], pos)
+    # slot is a bijection between kept assignments and rows, grouped by expert
+    kept = pos < C
+    assert fr["offset"][-1] == kept.sum()
+    rows = sorted(fr["slot"][kept].tolist())
+    assert rows == list(range(int(kept.sum())))
+    for t in range(T):
+        for j in range(k):
+            s = fr["slot"][t, j]
+            if kept[t, j]:
+                e = idx[t, j]
+                assert fr["offset"][e] <= s < fr["offset"][e + 1]
+                assert fr["row_token"][s] == t
+            else:
+                assert s == -1
+
+
+def test_fill_rank_major_keeps_first_choices():
+    # token 0's second choice and token 5's first choice land on expert 2 with C = 1.
+    idx = np.array([[0, 2], [1, 3], [1, 3], [3, 1], [0, 1], [2, 0]])
+    rm = O.fill(idx, 4, 1, O.FILL_RANK_MAJOR)
+    tm = O.fill(idx, 4, 1, O.FILL_TOKEN_MAJOR)
+    assert rm["slot"][5, 0] >= 0 and rm["slot"][0, 1] == -1
+    assert tm["slot"][0, 1] >= 0 and tm["slot"][5, 0] == -1
+
+
+# ----------------------------------------------------------------- experts and layer
+def make_layer(T, h, f, E, seed):
+    r = rng(seed)
+    return (r.normal(size=(T, h)), r.normal(size=(h, E)) / math.sqrt(h),
+            r.normal(size=(E, f, h)) / math.sqrt(h), r.normal(size=(E, f, h)) / math.sqrt(h),
+            r.normal(size=(E, h, f)) / math.sqrt(f))
+
+
+def torch_swiglu(x, Wg, Wu, Wd):
+    x, Wg, Wu, Wd = (torch.from_numpy(np.asarray(a, dtype=np.float64)) for a in (x, Wg, Wu, Wd))
+    return F.linear(F.silu(F.linear(x, Wg)) * F.linear(x, Wu), Wd).numpy()
+
+
+def test_swiglu_vs_library():
+    U, _, Wg, Wu, Wd = make_layer(9, 12, 20, 2, 7)
+    np.testing.assert_allclose(O.swiglu_expert(U, Wg[1], Wu[1], Wd[1]),
+                               torch_swiglu(U, Wg[1], Wu[1], Wd[1]), rtol=1e-12, atol=1e-13)
+    v = np.linspace(-50, 50, 101)
+    np.testing.assert_allclose(O.silu(v), F.silu(torch.from_numpy(v)).numpy(), rtol=1e-14, atol=1e-300)
+
+
+def test_single_expert_is_dense_swiglu_plus_residual():
+    U, W, Wg, Wu, Wd = make_layer(17, 8, 24, 1, 8)
+    r = O.layer_forward(U, W, Wg, Wu, Wd, k=1, score=O.SOFTMAX, gate=O.GATE_RENORM,
+                        capacity_factor=1.0)
+    assert r["n_dropped"] == 0
+    np.testing.assert_allclose(r["out"], U + torch_swiglu(U, Wg[0], Wu[0], Wd[0]),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_k_equals_E_is_soft_mixture():
+    T, h, f, E = 13, 6, 10, 4
+    U, W, Wg, Wu, Wd = make_layer(T, h, f, E, 9)
+    r = O.layer_forward(U, W, Wg, Wu, Wd, k=E, score=O.SOFTMAX, gate=O.GATE_RENORM,
+                        capacity_factor=1.0)
+    p = torch.softmax(torch.from_numpy(U @ W), dim=1).numpy()
+    ref = U + sum(p[:, e:e + 1] * torch_swiglu(U, Wg[e], Wu[e], Wd[e]) for e in range(E))
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("score,gate,cf,order", [
+    (O.SOFTMAX, O.GATE_RENORM, 0.75, O.FILL_RANK_MAJOR),
+    (O.SOFTMAX, O.GATE_RAW, 0.5, O.FILL_TOKEN_MAJOR),
+    (O.SIGMOID, O.GATE_RENORM, 1.25, O.FILL_RANK_MAJOR),
+])
+def test_sparse_equals_dense_masked_brute_force(score, gate, cf, order):
+    T, h, f, E, k = 40, 8, 12, 6, 2
+    U, W, Wg, Wu, Wd = make_layer(T, h, f, E, 10)
+    W[:, 0] += 0.6  # skew the load so some assignments drop
+    r = O.layer_forward(U, W, Wg, Wu, Wd, k=k, score=score, gate=gate, capacity_factor=cf,
+                        fill_order=order)
+    if cf < 1:
+        assert r["n_dropped"] > 0
+    gd = np.zeros((T, E))
+    for t in range(T):
+        for j in range(k):
+            if r["slot"][t, j] >= 0:
+                gd[t, r["idx"][t, j]] = r["gate"][t, j]
+    np.testing.assert_allclose(r["out"], O.dense_masked_forward(U, Wg, Wu, Wd, gd),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_token_outputs_match_layer():
+    T, h, f, E, k = 30, 8, 12, 5, 2
+    U, W, Wg, Wu, Wd = make_layer(T, h, f, E, 11)
+    r = O.layer_forward(U, W, Wg, Wu, Wd, k=k, score=O.SOFTMAX, gate=O.GATE_RENORM,
+                        capacity_factor=0.8)
+    toks = [0, 7, 29]
+    o = O.token_outputs(toks, U, r["idx"], r["slot"], r["gate"], lambda e: (Wg[e], Wu[e], Wd[e]))
+    np.testing.assert_allclose(o, r["out"][toks], rtol=1e-12, atol=1e-12)
+
+
+def test_fully_dropped_tokens_pass_residual():
+    T, h, f, E, k = 64, 8, 12, 4, 2
+    U, W, Wg, Wu, Wd = make_layer(T, h, f, E, 12)
+    r = O.layer_forward(U, W, Wg, Wu, Wd, k=k, score=O.SOFTMAX, gate=O.GATE_RENORM,
+                        capacity_factor=1e-3)
+    assert r["C"] == 1
+    assert r["kept"].tolist() == [min(1, c) for c in r["count"]]
+    full_drop = (r["slot"] < 0).all(axis=1)
+    assert full_drop.sum() >= T - E
+    np.testing.assert_array_equal(r["out"][full_drop], U[full_drop])
+
+
+# ----------------------------------------------------------------- statistics
+def test_aux_balanced_is_one_and_minimum():
+    g = golden("aux_balance.json")
+    E, k, T = 8, 2, 64
+    # every expert receives exactly T k / E assignments and P is uniform (W_r = 0)
+    idx = np.array([[(2 * t) % E, (2 * t + 1) % E] for t in range(T)])
+    s = np.full((T, E), 1.0 / E)
+    fr = O.fill(idx, E, T)
+    st = O.load_stats(s, idx, fr, O.SOFTMAX)
+    assert abs(st["aux"] - g["balanced_aux"]) < 1e-14
+    assert abs(st["f"].sum() - 1) < 1e-15 and abs(st["maxvio"]) < 1e-15
+    # uniform P gives 1 for any load; any load satisfies sum f^2 >= 1/E (equality iff balanced)
+    r = rng(13)
+    for _ in range(5):
+        idx = O.select_topk(r.normal(size=(T, E)) + r.normal(size=E) * 2, k)
+        fr = O.fill(idx, E, T)
+        st = O.load_stats(s, idx, fr, O.SOFTMAX)
+        assert abs(st["aux"] - 1.0) < 1e-13
+        assert (st["f"] ** 2).sum() >= 1.0 / E - 1e-15
+    # with real softmax scores, the loss equals E sum(importance * load) with
+    # importance = probs.sum(0) / probs.sum() and load = one-hot counts / their sum
+    H = r.normal(size=(T, E)) * 2
+    s = O.scores(H, O.SOFTMAX)
+    idx = O.select_topk(H, k)
+    st = O.load_stats(s, idx, O.fill(idx, E, T), O.SOFTMAX)
+    probs = torch.from_numpy(s)
+    importance = probs.sum(0) / probs.sum()
+    load = F.one_hot(torch.from_numpy(idx), E).double().sum((0, 1))
+    load = load / load.sum()
+    assert abs(st["aux"] - float(E * (importance * load).sum())) < 1e-13
+    assert st["aux"] >= 0
+
+
+def test_maxvio_and_efficiency_example():
+    g = golden("aux_balance.json")
+    # mean load 4 (T k / E = 16 * 2 / 8), busiest expert 6: MaxVio = 0.5
+    counts = [6, 4, 4, 4, 4, 4, 3, 3]
+    idx = np.array([e for e, c in enumerate(counts) for _ in range(c)]).reshape(16, 2)
+    fr = O.fill(idx, 8, 100)
+    st = O.load_stats(np.full((16, 8), 1 / 8), idx, fr, O.SOFTMAX)
+    assert abs(st["maxvio"] - g["maxvio_example"]) < 1e-15
+    assert round(1 / (1 + st["maxvio"]), 2) == g["efficiency_example"]
+
+
+def test_P_sums_to_one_for_both_scores():
+    r = rng(14)
+    H = r.normal(size=(50, 7)) * 3
+    for score in (O.SOFTMAX, O.SIGMOID):
+        s = O.scores(H, score)
+        idx = O.select_topk(H, 2)
+        st = O.load_stats(s, idx, O.fill(idx, 7, 50), score)
+        assert abs(st["P"].sum() - 1.0) < 1e-14
+    # sigmoid P is the token mean of s / sum_j s (not of raw s)
+    s = O.scores(H, O.SIGMOID)
+    st = O.load_stats(s, idx, O.fill(idx, 7, 50), O.SIGMOID)
+    ref = (torch.from_numpy(s) / torch.from_numpy(s).sum(1, keepdim=True)).mean(0).numpy()
+    np.testing.assert_allclose(st["P"], ref, rtol=1e-13)
+
+
+def test_gate_sums_and_dropped_count():
+    r = rng(15)
+    T, E, k = 200, 16, 4
+    H = r.normal(size=(T, E)) + np.linspace(2, -2, E)
+    for score in (O.SOFTMAX, O.SIGMOID):
+        C = O.capacity(T, E, k, 1.0)
+        res = O.route(H, k, score, O.GATE_RENORM, C)
+        np.testing.assert_allclose(res["gate"].sum(1), 1.0, rtol=1e-14)
+        assert res["n_dropped"] == int((res["slot"] < 0).sum())
+        assert res["n_dropped"] > 0
