@@ -1,0 +1,205 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+One step = one moe_layer_forward (router, dispatch, grouped SwiGLU experts,
+combine, statistics) over one batch of seeded synthetic tokens whose inputs
+are resident in HBM.  Prints one JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--cpu-baseline-seconds S | --no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_bf16")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, x, g, budget_s: float) -> dict:
+    """The float64 oracle, as it is, on a bounded sample of the same workload.
+
+    Routing (router product, scores, top-k, capacity fill, statistics) runs on
+    all T tokens.  The expert products run on whole experts taken in order
+    until the time budget is used (each expert's weights converted to float64
+    plus its SwiGLU over its rows); combine runs on all tokens.  The time of the
+    expert part is scaled by (all kept rows / sampled rows) plus the weight
+    conversion of the experts not sampled.
+    """
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as O
+
+    def f64(t):
+        return t.detach().cpu().float().numpy().astype(np.float64)
+
+    t0 = time.perf_counter()
+    U = f64(x["U"])
+    H = O.router_logits(U, f64(x["W_r"]), None if x["b_r"] is None else f64(x["b_r"]),
+                        None if x["W_noise"] is None else f64(x["W_noise"]),
+                        None if x["noise"] is None else f64(x["noise"]))
+    C = O.capacity(w.T, w.E, w.k, w.capacity_factor)
+    r = O.route(H, w.k, w.score, w.gate, C, w.fill)
+    t_route = time.perf_counter() - t0
+
+    rows_total = int(r["offset"][-1])
+    active = [e for e in range(w.E) if r["offset"][e + 1] > r["offset"][e]]
+    t_conv, t_ffn, rows_done, experts_done = 0.0, 0.0, 0, 0
+    Y = np.zeros((rows_total, w.h))
+    for e in active:
+        if t_conv + t_ffn > budget_s and experts_done > 0:
+            break
+        t1 = time.perf_counter()
+        Wg, Wu, Wd = f64(x["W_gate"][e]), f64(x["W_up"][e]), f64(x["W_down"][e])
+        t2 = time.perf_counter()
+        a, b = int(r["offset"][e]), int(r["offset"][e + 1])
+        # cap the rows of one expert so a single expert stays inside the budget
+        n = min(b - a, 256)
+        Y[a:a + n] = O.swiglu_expert(U[r["row_token"][a:a + n]], Wg, Wu, Wd)
+        t3 = time.perf_counter()
+        t_conv += t2 - t1
+        t_ffn += t3 - t2
+        rows_done += n
+        experts_done += 1
+    t4 = time.perf_counter()
+    O.combine(U, Y, r["slot"], r["gate"])
+    t_comb = time.perf_counter() - t4
+    est = (t_route + t_comb + t_conv * len(active) / experts_done
+           + t_ffn * rows_total / max(rows_done, 1))
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": w.T / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"routing, statistics and combine on all {w.T} tokens; expert SwiGLU on "
+                       f"{rows_done} of {rows_total} kept rows from {experts_done} of "
+                       f"{len(active)} active experts (float64), scaled by rows; measured "
+                       f"{t_route + t_comb + t_conv + t_ffn:.1f} s, estimated {est:.1f} s "
+                       f"per full forward")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from mixture_experts_layer_37_amd import binding as B
+    from mixture_experts_layer_37_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = I.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"workload {w}")
+    x = I.make_inputs(w, seed=args.seed, device=dev)
+    cfg = B.make_config(w)
+    ws = B.new_workspace(cfg, B.MOE_WS_LAYER, dev)
+    aux = B.alloc_aux(cfg, dev, ["kept", "n_dropped", "aux_loss", "maxvio"])
+    out = torch.empty((w.T, w.h), dtype=I.torch_dtype(w), device=dev)
+    nst = B.MOE_NUM_STAGES
+
+    def step(events=None):
+        B.moe_layer_forward(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], x["noise"],
+                            x["W_gate"], x["W_up"], x["W_down"], out, aux=aux,
+                            stage_events=events, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
+              for _ in range(args.steps)]
+    for evs in events:  # create the HIP events outside the timed region
+        for e in evs:
+            e.record()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {n: 0.0 for n in B.STAGE_NAMES}
+    for evs in events:
+        for j, n in enumerate(B.STAGE_NAMES):
+            stage_ms[n] += evs[j].elapsed_time(evs[j + 1]) / args.steps
+    ms = elapsed * 1e3 / args.steps
+    tokens_per_s = w.T * args.steps / elapsed
+
+    kept = int(aux["kept"].sum().item())
+    n_drop = int(aux["n_dropped"].item())
+    bf16 = w.dtype == "bf16"
+    eb = 2 if bf16 else 4
+    # algorithmic work: 6 h f FLOPs per kept (token, expert) row; the gate/up
+    # GEMM is 4 h f of it
+    f_exec = 6.0 * w.h * w.f * kept
+    f_nom = 6.0 * w.h * w.f * w.k * w.T
+    f_gate_up = 4.0 * w.h * w.f * kept
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    gu_ms = stage_ms["gate_up"]
+    achieved = f_gate_up / (gu_ms * 1e-3) / 1e12
+    kept_per_e = aux["kept"].cpu().tolist()
+    e_active = sum(1 for c in kept_per_e if c > 0)
+    b_alg = eb * (3.0 * w.h * w.f * e_active + 2.0 * w.T * w.h + w.h * w.E * (2 if w.noisy else 1))
+
+    res = {
+        "metric": "MoE layer fwd tokens/sec on 1 MI355X",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "h": w.h, "f": w.f, "E": w.E, "k": w.k,
+                   "score": w.score, "gate": w.gate, "capacity_factor": w.capacity_factor,
+                   "noisy": w.noisy, "seed": args.seed},
+        "roofline": {"kernel": "grouped gate/up GEMM + SwiGLU", "bound": "mfma",
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None},
+        "layer": {"mfma_frac_nominal": f_nom / (ms * 1e-3) / 1e12 / peak,
+                  "mfma_frac_exec": f_exec / (ms * 1e-3) / 1e12 / peak,
+                  "hbm_frac_alg": b_alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                  "kept_rows": kept, "dropped": n_drop, "active_experts": e_active,
+                  "aux_loss": float(aux["aux_loss"].item()),
+                  "maxvio": float(aux["maxvio"].item())},
+        "stage_ms": stage_ms,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline(w, x, aux, args.cpu_baseline_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+/*
+ * moe.h - C ABI of libmoe: the forward pass of one Mixture-of-Experts layer
+ * on one gfx950 GPU (MI355X).
+ *
+ * The layer (page "MoE 与专家并行", hs-black.github.io/posts/scaling-moe):
+ *   logits  H = U W_r (+ b_r) (+ noise * softplus(U W_noise))
+ *                      section "路由器：打分、top-k、加权求和", eq. H and G(x)
+ *   scores  softmax or sigmoid; top-k; gates raw or renormalised
+ *                      section "softmax 门控还是 sigmoid 门控", table
+ *   capacity C and token-order fill with drops
+ *                      section "专家容量与丢 token", eq. C and its figure
+ *   experts FFN(u) = W_down (SiLU(W_gate u) * W_up u)
+ *                      section "从稠密 FFN 到 MoE", eq. FFN
+ *   output  out_t = u_t + sum_r g_{t,r} FFN_{e(t,r)}(u_t) over kept (t,r)
+ *                      same section, eq. h'_t
+ *   stats   f_e, P_e, aux = E sum f_e P_e, MaxVio
+ *                      sections "负载均衡辅助损失：推导与梯度" and
+ *                      "无辅助损失的负载均衡"
+ * The staged calls follow the single-GPU dataflow of the router section
+ * (route, group rows by expert, grouped FFN over per-expert counts, scatter
+ * back) and the grouped-GEMM option of section "专家计算：padding、
+ * block-sparse 与 grouped GEMM".
+ *
+ * Conventions for every call:
+ *  - Data pointers are DEVICE pointers owned by the caller.  The library never
+ *    allocates, frees or synchronises; all work is enqueued on `stream` (a
+ *    hipStream_t; NULL is the default stream) and the buffers must stay valid
+ *    until it has run.  There is no global state: calls are re-entrant.
+ *  - Arguments are validated on the host before anything is launched; on any
+ *    error nothing is enqueued.  MOE_ERR_INVALID_ARG: a bad value or a NULL
+ *    required pointer.  MOE_ERR_UNSUPPORTED: a valid shape this library does
+ *    not handle (see moe_config).  MOE_ERR_WORKSPACE: ws_bytes smaller than
+ *    moe_workspace_size().  MOE_ERR_HIP: a launch failed (hipGetLastError).
+ *  - Layouts are row-major in the pages' shapes.  U, X, Y, out: [rows, h].
+ *    W_r, W_noise: [h, E].  W_gate, W_up: [E, f, h].  W_down: [E, h, f].
+ *    These and the expert weights have element type cfg->dtype.  b_r, noise,
+ *    logits, gates, prob_sum, f, P and the scalar statistics are float32.
+ *    Expert ids, slots, counts and offsets are int32.
+ *  - Variable-size outputs (X, Y, row_token) are sized by the static bound
+ *    moe_max_rows(), so no host synchronisation is ever needed.
+ *  - Results are deterministic: no floating-point atomics decide any value.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Scoring (section "softmax 门控还是 sigmoid 门控"). */
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+
+/* Gates: RAW g = s (Switch, DeepSeekMoE); RENORM g = s / sum of selected s
+ * (GShard top-2, DeepSeek-V3; with softmax this equals Softmax(KeepTopK)). */
+typedef enum { MOE_GATE_RAW = 0, MOE_GATE_RENORM = 1 } moe_gate;
+
+/* Fill order of capacity slots.  RANK_MAJOR: every token's first choice in
+ * token order, then every second choice, ... (the GShard order in section
+ * "专家容量与丢 token").  TOKEN_MAJOR: token by token, choices in rank order. */
+typedef enum { MOE_FILL_RANK_MAJOR = 0, MOE_FILL_TOKEN_MAJOR = 1 } moe_fill;
+
+/* Capacity.  ASSIGNMENTS: C = ceil(CF * T * k / E) (eq. C of section
+ * "专家容量与丢 token").  TOKENS: C = ceil((T / E) * CF), the top-1 form on the
+ * page "Ai大模型训练教程" (aissn.com/133.html), capacity section. */
+typedef enum { MOE_CAP_ASSIGNMENTS = 0, MOE_CAP_TOKENS = 1 } moe_cap;
+
+typedef struct {
+  int64_t T;      /* tokens on this GPU, >= 0                                  */
+  int64_t h;      /* hidden size                                               */
+  int64_t f;      /* expert intermediate size (d_e)                            */
+  int64_t E;      /* experts, 1..256                                           */
+  int64_t k;      /* experts per token, 1..min(E, 8)                           */
+  int32_t dtype;  /* moe_dtype.  BF16 needs h % 64 == 0 and f % 64 == 0;
+                     F32 needs h % 4 == 0 and f % 4 == 0 (else UNSUPPORTED)     */
+  int32_t score;  /* moe_score                                                 */
+  int32_t gate;   /* moe_gate                                                  */
+  int32_t cap_mode; /* moe_cap                                                 */
+  int32_t fill;   /* moe_fill                                                  */
+  int32_t noisy;  /* 1: add noise * softplus(U W_noise) to the logits          */
+  double capacity_factor; /* > 0, finite, in [1e-6, 1e6]; <= 0 means no limit
+                             (dropless: C = T)                                 */
+  int64_t min_capacity;   /* C is raised to at least this (0: no floor)        */
+} moe_config;
+
+/* Optional outputs of moe_layer_forward.  Any NULL field is kept in the
+ * workspace instead (or not produced).  Shapes as in the staged calls. */
+typedef struct {
+  int32_t* topk_idx;   /* [T, k] expert ids, best first                       */
+  float* topk_gate;    /* [T, k] gates in the same order                      */
+  float* logits;       /* [T, E] the float32 logits routing used              */
+  int32_t* slot;       /* [T, k] row of the permuted matrix, -1 when dropped  */
+  int32_t* row_token;  /* [rows_max] token of each permuted row               */
+  int32_t* count;      /* [E] assignments before the capacity cut             */
+  int32_t* kept;       /* [E] min(count, C)                                   */
+  int32_t* offset;     /* [E+1] exclusive scan of kept                        */
+  float* prob_sum;     /* [E] sum over tokens of the score used by P          */
+  float* f;            /* [E] count / (T k)                                   */
+  float* P;            /* [E] prob_sum / T                                    */
+  float* aux_loss;     /* [1] E * sum f P (alpha = 1)                         */
+  float* maxvio;       /* [1] (max count - T k / E) / (T k / E)               */
+  int32_t* n_dropped;  /* [1] sum (count - kept)                              */
+  void* X;             /* [rows_max, h] permuted expert inputs                */
+  void* Y;             /* [rows_max, h] expert outputs                        */
+} moe_aux_outputs;
+
+/* Workspace sizes per entry point. */
+typedef enum {
+  MOE_WS_ROUTE = 0,
+  MOE_WS_DISPATCH = 1,
+  MOE_WS_EXPERT_FFN = 2,
+  MOE_WS_LAYER = 3
+} moe_ws_entry;
+
+/* Stage boundaries recorded by moe_layer_forward when stage_events != NULL:
+ * events[0] before the router ... events[MOE_NUM_STAGES] after the last stage. */
+enum { MOE_NUM_STAGES = 6 }; /* route, dispatch, gate_up, down, combine, stats */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(int32_t status);
+
+/* Capacity C of cfg, on the host, as an exact rational ceiling (the double
+ * capacity_factor is taken at its exact binary value).  Pure; no GPU use. */
+int32_t moe_capacity(const moe_config* cfg, int64_t* C);
+
+/* Static bound on kept assignments: min(T k, E min(C, T)).  Pure. */
+int32_t moe_max_rows(const moe_config* cfg, int64_t* rows_max);
+
+/* Bytes of device workspace that entry `entry` (moe_ws_entry) needs.  Pure. */
+int32_t moe_workspace_size(const moe_config* cfg, int32_t entry, size_t* bytes);
+
+/* Router: logits, scores, top-k and gates (router section; scoring table).
+ *  U [T,h], W_r [h,E]: required.  b_r [E]: optional per-expert logit bias.
+ *  W_noise [h,E] and noise [T,E] (standard-normal draws supplied by the
+ *  caller): required iff cfg->noisy.
+ *  topk_idx [T,k], topk_gate [T,k]: required outputs, rank order, selection by
+ *  the key (-H, expert index) on the float32 logits.
+ *  logits [T,E]: optional output of exactly the logits used.
+ *  prob_sum [E]: optional output of sum_t s (softmax) or sum_t s/sum_j s
+ *  (sigmoid), the numerator of P.
+ *  ws: MOE_WS_ROUTE bytes. */
+int32_t moe_route(const moe_config* cfg, const void* U, const void* W_r, const float* b_r,
+                  const void* W_noise, const float* noise, int32_t* topk_idx,
+                  float* topk_gate, float* logits, float* prob_sum, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/* Dispatch: capacity cut and permutation (capacity section).
+ *  topk_idx [T,k] in: expert ids (values outside [0,E) are undefined input).
+ *  count [E], kept [E], offset [E+1], slot [T,k], row_token [rows_max]: outputs
+ *  (count is before the cut; offset is the exclusive scan of kept; rows of
+ *  expert e are offset[e]..offset[e+1]-1 in fill order).
+ *  X [rows_max, h]: output, X[row] = U[row_token[row]]; rows beyond
+ *  offset[E] are left untouched.  All outputs required.  ws: MOE_WS_DISPATCH. */
+int32_t moe_dispatch(const moe_config* cfg, const void* U, const int32_t* topk_idx,
+                     void* X, int32_t* row_token, int32_t* slot, int32_t* count,
+                     int32_t* kept, int32_t* offset, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Grouped SwiGLU experts (FFN eq.; grouped-GEMM option of the expert-compute
+ * section): for every expert e and row r in offset[e]..offset[e+1]-1,
+ * Y[r] = W_down[e] (SiLU(W_gate[e] X[r]) * W_up[e] X[r]).  Accumulation is
+ * float32; the SiLU product is rounded to cfg->dtype before the down
+ * projection.  Rows beyond offset[E] are left untouched.  ws: MOE_WS_EXPERT_FFN. */
+int32_t moe_expert_ffn(const moe_config* cfg, const void* X, const int32_t* offset,
+                       const void* W_gate, const void* W_up, const void* W_down, void* Y,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Combine with residual (eq. h'_t): out[t] = U[t] + sum over r with
+ * slot[t,r] >= 0, in rank order, of topk_gate[t,r] * Y[slot[t,r]].  Float32
+ * accumulation; out has cfg->dtype and may not alias U or Y. */
+int32_t moe_combine(const moe_config* cfg, const void* U, const void* Y, const int32_t* slot,
+                    const float* topk_gate, void* out, void* stream);
+
+/* Load-balance statistics from dispatch counts and the router's prob_sum
+ * (aux-loss section; MaxVio of the loss-free section).  count, kept,
+ * prob_sum in; f [E], P [E], aux_loss [1], maxvio [1], n_dropped [1] out
+ * (each output optional).  With T = 0 every output is 0. */
+int32_t moe_stats(const moe_config* cfg, const int32_t* count, const int32_t* kept,
+                  const float* prob_sum, float* f, float* P, float* aux_loss, float* maxvio,
+                  int32_t* n_dropped, void* stream);
+
+/* The whole layer: route, dispatch, experts, combine, statistics.
+ *  out [T,h] required.  aux: optional outputs (struct pointer may be NULL).
+ *  stage_events: NULL, or MOE_NUM_STAGES + 1 hipEvent_t handles recorded on
+ *  `stream` at the stage boundaries (for timing).  ws: MOE_WS_LAYER bytes. */
+int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
+                          const float* b_r, const void* W_noise, const float* noise,
+                          const void* W_gate, const void* W_up, const void* W_down, void* out,
+                          const moe_aux_outputs* aux, void* const* stage_events, void* ws,
+                          size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,319 @@
+"""ctypes binding of libmoe (include/moe.h): argument marshalling only.
+
+Every function here checks shapes, dtypes, devices and contiguity on the host,
+turns tensors into device pointers and calls the C entry point of the same
+name on torch's current HIP stream.  All computation happens in the library's
+HIP kernels; there is no fallback: if libmoe.so is missing, loading fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_GATE_RAW, MOE_GATE_RENORM = 0, 1
+MOE_FILL_RANK_MAJOR, MOE_FILL_TOKEN_MAJOR = 0, 1
+MOE_CAP_ASSIGNMENTS, MOE_CAP_TOKENS = 0, 1
+MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_EXPERT_FFN, MOE_WS_LAYER = range(4)
+MOE_NUM_STAGES = 6
+STAGE_NAMES = ["route", "dispatch", "gate_up", "down", "combine", "stats"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class moe_config(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64), ("h", ctypes.c_int64), ("f", ctypes.c_int64),
+        ("E", ctypes.c_int64), ("k", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("score", ctypes.c_int32), ("gate", ctypes.c_int32),
+        ("cap_mode", ctypes.c_int32), ("fill", ctypes.c_int32), ("noisy", ctypes.c_int32),
+        ("capacity_factor", ctypes.c_double), ("min_capacity", ctypes.c_int64),
+    ]
+
+
+class moe_aux_outputs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "topk_idx", "topk_gate", "logits", "slot", "row_token", "count", "kept", "offset",
+        "prob_sum", "f", "P", "aux_loss", "maxvio", "n_dropped", "X", "Y")]
+
+
+AUX_FIELDS = [n for n, _ in moe_aux_outputs._fields_]
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mixture_experts_layer_37_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        cfgp = ctypes.POINTER(moe_config)
+        sig = {
+            "moe_status_string": (ctypes.c_char_p, [I32]),
+            "moe_capacity": (I32, [cfgp, ctypes.POINTER(I64)]),
+            "moe_max_rows": (I32, [cfgp, ctypes.POINTER(I64)]),
+            "moe_workspace_size": (I32, [cfgp, I32, ctypes.POINTER(SZ)]),
+            "moe_route": (I32, [cfgp] + [P] * 9 + [P, SZ, P]),
+            "moe_dispatch": (I32, [cfgp] + [P] * 8 + [P, SZ, P]),
+            "moe_expert_ffn": (I32, [cfgp] + [P] * 6 + [P, SZ, P]),
+            "moe_combine": (I32, [cfgp] + [P] * 5 + [P]),
+            "moe_stats": (I32, [cfgp] + [P] * 8 + [P]),
+            "moe_layer_forward": (I32, [cfgp] + [P] * 9 + [ctypes.POINTER(moe_aux_outputs), P,
+                                                         P, SZ, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+# --------------------------------------------------------------------------- config
+_DT = {"f32": MOE_F32, "bf16": MOE_BF16}
+_SC = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
+_GT = {"raw": MOE_GATE_RAW, "renorm": MOE_GATE_RENORM}
+_FL = {"rank_major": MOE_FILL_RANK_MAJOR, "token_major": MOE_FILL_TOKEN_MAJOR}
+_CP = {"assignments": MOE_CAP_ASSIGNMENTS, "tokens": MOE_CAP_TOKENS}
+
+
+def make_config(w, T: Optional[int] = None) -> moe_config:
+    """moe_config from a Workload (mixture_experts_layer_37_amd.inputs)."""
+    return moe_config(T=w.T if T is None else T, h=w.h, f=w.f, E=w.E, k=w.k,
+                      dtype=_DT[w.dtype], score=_SC[w.score], gate=_GT[w.gate],
+                      cap_mode=_CP[w.cap_mode], fill=_FL[w.fill], noisy=int(w.noisy),
+                      capacity_factor=float(w.capacity_factor),
+                      min_capacity=int(w.min_capacity))
+
+
+def capacity(cfg: moe_config) -> int:
+    v = ctypes.c_int64()
+    _check(lib().moe_capacity(ctypes.byref(cfg), ctypes.byref(v)), "moe_capacity")
+    return v.value
+
+
+def max_rows(cfg: moe_config) -> int:
+    v = ctypes.c_int64()
+    _check(lib().moe_max_rows(ctypes.byref(cfg), ctypes.byref(v)), "moe_max_rows")
+    return v.value
+
+
+def workspace_size(cfg: moe_config, entry: int) -> int:
+    v = ctypes.c_size_t()
+    _check(lib().moe_workspace_size(ctypes.byref(cfg), entry, ctypes.byref(v)),
+           "moe_workspace_size")
+    return v.value
+
+
+# --------------------------------------------------------------------------- marshalling
+def _elem_dtype(cfg) -> torch.dtype:
+    return torch.bfloat16 if cfg.dtype == MOE_BF16 else torch.float32
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, shape=None, dtype=None, min_numel=None):
+    """Device pointer of t after checking it; None gives NULL."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name}: needs at least {min_numel} elements")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ws(ws: torch.Tensor, need: int):
+    p = _ptr(ws, "ws", dtype=torch.uint8)
+    if ws.numel() < need:
+        raise ValueError(f"ws: {ws.numel()} bytes, needs {need}")
+    return p, ws.numel()
+
+
+def new_workspace(cfg: moe_config, entry: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(1, workspace_size(cfg, entry)), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------------- entry points
+def moe_route(cfg, U, W_r, b_r, W_noise, noise, topk_idx, topk_gate, logits=None,
+              prob_sum=None, ws=None, stream=None):
+    T, h, E, k = cfg.T, cfg.h, cfg.E, cfg.k
+    dt = _elem_dtype(cfg)
+    need = workspace_size(cfg, MOE_WS_ROUTE)
+    ws = new_workspace(cfg, MOE_WS_ROUTE, U.device) if ws is None else ws
+    wp, wn = _ws(ws, need)
+    args = [
+        _ptr(U, "U", (T, h), dt), _ptr(W_r, "W_r", (h, E), dt),
+        _ptr(b_r, "b_r", (E,), torch.float32),
+        _ptr(W_noise, "W_noise", (h, E), dt) if cfg.noisy else None,
+        _ptr(noise, "noise", (T, E), torch.float32) if cfg.noisy else None,
+        _ptr(topk_idx, "topk_idx", (T, k), torch.int32),
+        _ptr(topk_gate, "topk_gate", (T, k), torch.float32),
+        _ptr(logits, "logits", (T, E), torch.float32),
+        _ptr(prob_sum, "prob_sum", (E,), torch.float32),
+    ]
+    _check(lib().moe_route(ctypes.byref(cfg), *args, wp, wn, _stream(stream)), "moe_route")
+
+
+def moe_dispatch(cfg, U, topk_idx, X, row_token, slot, count, kept, offset, ws=None,
+                 stream=None):
+    T, h, E, k = cfg.T, cfg.h, cfg.E, cfg.k
+    rows = max_rows(cfg)
+    dt = _elem_dtype(cfg)
+    need = workspace_size(cfg, MOE_WS_DISPATCH)
+    ws = new_workspace(cfg, MOE_WS_DISPATCH, U.device) if ws is None else ws
+    wp, wn = _ws(ws, need)
+    args = [
+        _ptr(U, "U", (T, h), dt), _ptr(topk_idx, "topk_idx", (T, k), torch.int32),
+        _ptr(X, "X", (rows, h), dt), _ptr(row_token, "row_token", (rows,), torch.int32),
+        _ptr(slot, "slot", (T, k), torch.int32), _ptr(count, "count", (E,), torch.int32),
+        _ptr(kept, "kept", (E,), torch.int32), _ptr(offset, "offset", (E + 1,), torch.int32),
+    ]
+    _check(lib().moe_dispatch(ctypes.byref(cfg), *args, wp, wn, _stream(stream)), "moe_dispatch")
+
+
+def moe_expert_ffn(cfg, X, offset, W_gate, W_up, W_down, Y, ws=None, stream=None):
+    h, f, E = cfg.h, cfg.f, cfg.E
+    rows = max_rows(cfg)
+    dt = _elem_dtype(cfg)
+    need = workspace_size(cfg, MOE_WS_EXPERT_FFN)
+    ws = new_workspace(cfg, MOE_WS_EXPERT_FFN, X.device) if ws is None else ws
+    wp, wn = _ws(ws, need)
+    args = [
+        _ptr(X, "X", (rows, h), dt), _ptr(offset, "offset", (E + 1,), torch.int32),
+        _ptr(W_gate, "W_gate", (E, f, h), dt), _ptr(W_up, "W_up", (E, f, h), dt),
+        _ptr(W_down, "W_down", (E, h, f), dt), _ptr(Y, "Y", (rows, h), dt),
+    ]
+    _check(lib().moe_expert_ffn(ctypes.byref(cfg), *args, wp, wn, _stream(stream)),
+           "moe_expert_ffn")
+
+
+def moe_combine(cfg, U, Y, slot, topk_gate, out, stream=None):
+    T, h, k = cfg.T, cfg.h, cfg.k
+    rows = max_rows(cfg)
+    dt = _elem_dtype(cfg)
+    args = [
+        _ptr(U, "U", (T, h), dt), _ptr(Y, "Y", (rows, h), dt),
+        _ptr(slot, "slot", (T, k), torch.int32),
+        _ptr(topk_gate, "topk_gate", (T, k), torch.float32), _ptr(out, "out", (T, h), dt),
+    ]
+    _check(lib().moe_combine(ctypes.byref(cfg), *args, _stream(stream)), "moe_combine")
+
+
+def moe_stats(cfg, count, kept, prob_sum, f=None, P=None, aux_loss=None, maxvio=None,
+              n_dropped=None, stream=None):
+    E = cfg.E
+    args = [
+        _ptr(count, "count", (E,), torch.int32), _ptr(kept, "kept", (E,), torch.int32),
+        _ptr(prob_sum, "prob_sum", (E,), torch.float32), _ptr(f, "f", (E,), torch.float32),
+        _ptr(P, "P", (E,), torch.float32), _ptr(aux_loss, "aux_loss", (1,), torch.float32),
+        _ptr(maxvio, "maxvio", (1,), torch.float32),
+        _ptr(n_dropped, "n_dropped", (1,), torch.int32),
+    ]
+    _check(lib().moe_stats(ctypes.byref(cfg), *args, _stream(stream)), "moe_stats")
+
+
+_AUX_SPEC = {
+    "topk_idx": (lambda c, r: (c.T, c.k), torch.int32),
+    "topk_gate": (lambda c, r: (c.T, c.k), torch.float32),
+    "logits": (lambda c, r: (c.T, c.E), torch.float32),
+    "slot": (lambda c, r: (c.T, c.k), torch.int32),
+    "row_token": (lambda c, r: (r,), torch.int32),
+    "count": (lambda c, r: (c.E,), torch.int32),
+    "kept": (lambda c, r: (c.E,), torch.int32),
+    "offset": (lambda c, r: (c.E + 1,), torch.int32),
+    "prob_sum": (lambda c, r: (c.E,), torch.float32),
+    "f": (lambda c, r: (c.E,), torch.float32),
+    "P": (lambda c, r: (c.E,), torch.float32),
+    "aux_loss": (lambda c, r: (1,), torch.float32),
+    "maxvio": (lambda c, r: (1,), torch.float32),
+    "n_dropped": (lambda c, r: (1,), torch.int32),
+    "X": (lambda c, r: (r, c.h), None),
+    "Y": (lambda c, r: (r, c.h), None),
+}
+
+
+def alloc_aux(cfg, device="cuda", fields=None) -> dict:
+    """Allocate device tensors for the optional outputs named in `fields` (all by default)."""
+    rows = max_rows(cfg)
+    out = {}
+    for name in (AUX_FIELDS if fields is None else fields):
+        shape_fn, dt = _AUX_SPEC[name]
+        out[name] = torch.empty(shape_fn(cfg, rows), dtype=dt or _elem_dtype(cfg), device=device)
+    return out
+
+
+def moe_layer_forward(cfg, U, W_r, b_r, W_noise, noise, W_gate, W_up, W_down, out, aux=None,
+                      stage_events=None, ws=None, stream=None):
+    """The whole layer.  aux: dict of optional output tensors (see alloc_aux).
+    stage_events: list of MOE_NUM_STAGES + 1 torch.cuda.Event(enable_timing=True),
+    recorded inside the library on the same stream."""
+    T, h, f, E = cfg.T, cfg.h, cfg.f, cfg.E
+    rows = max_rows(cfg)
+    dt = _elem_dtype(cfg)
+    need = workspace_size(cfg, MOE_WS_LAYER)
+    ws = new_workspace(cfg, MOE_WS_LAYER, W_r.device) if ws is None else ws
+    wp, wn = _ws(ws, need)
+    a = moe_aux_outputs()
+    for name, t in (aux or {}).items():
+        if name not in _AUX_SPEC:
+            raise KeyError(name)
+        shape_fn, adt = _AUX_SPEC[name]
+        setattr(a, name, _ptr(t, name, shape_fn(cfg, rows), adt or dt))
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != MOE_NUM_STAGES + 1:
+            raise ValueError("stage_events needs MOE_NUM_STAGES + 1 events")
+        handles = []
+        for e in stage_events:
+            if e.cuda_event == 0:  # torch creates the HIP event lazily
+                e.record()
+            handles.append(e.cuda_event)
+        ev = (ctypes.c_void_p * len(handles))(*handles)
+    args = [
+        _ptr(U, "U", (T, h), dt), _ptr(W_r, "W_r", (h, E), dt),
+        _ptr(b_r, "b_r", (E,), torch.float32),
+        _ptr(W_noise, "W_noise", (h, E), dt) if cfg.noisy else None,
+        _ptr(noise, "noise", (T, E), torch.float32) if cfg.noisy else None,
+        _ptr(W_gate, "W_gate", (E, f, h), dt), _ptr(W_up, "W_up", (E, f, h), dt),
+        _ptr(W_down, "W_down", (E, h, f), dt), _ptr(out, "out", (T, h), dt),
+    ]
+    _check(lib().moe_layer_forward(ctypes.byref(cfg), *args, ctypes.byref(a),
+                                   ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None,
+                                   wp, wn, _stream(stream)), "moe_layer_forward")

@@ -1,0 +1,459 @@
+// Host entry points of libmoe (the C ABI declared in include/moe.h).
+//
+// Validation happens before any launch.  Capacity is computed as an exact
+// rational ceiling (page "MoE 与专家并行", section "专家容量与丢 token", eq. C;
+// top-1 form on page "Ai大模型训练教程", capacity section).  The library never
+// allocates or synchronises: every intermediate lives in the caller's
+// workspace, whose layout is planned here identically for size queries and
+// calls.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include "kernels.hpp"
+#include "moe.h"
+
+namespace moe {
+hipError_t launch_ffn_f32(const void* X, const int32_t* offset, const void* Wg, const void* Wu,
+                          const void* Wd, void* A, void* Y, int64_t rows_max, int E, int h,
+                          int f, hipStream_t s);
+}
+
+namespace {
+
+using namespace moe;
+
+constexpr int64_t kMaxE = 256, kMaxK = 8;
+
+struct Dims {
+  int64_t T, h, f, E, k, C, rows_max;
+  bool bf16;
+};
+
+int32_t check_config(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->h < 1 || c->f < 1 || c->E < 1 || c->k < 1 || c->k > c->E)
+    return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->score != MOE_SCORE_SOFTMAX && c->score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (c->gate != MOE_GATE_RAW && c->gate != MOE_GATE_RENORM) return MOE_ERR_INVALID_ARG;
+  if (c->cap_mode != MOE_CAP_ASSIGNMENTS && c->cap_mode != MOE_CAP_TOKENS)
+    return MOE_ERR_INVALID_ARG;
+  if (c->fill != MOE_FILL_RANK_MAJOR && c->fill != MOE_FILL_TOKEN_MAJOR)
+    return MOE_ERR_INVALID_ARG;
+  if (c->noisy != 0 && c->noisy != 1) return MOE_ERR_INVALID_ARG;
+  if (c->min_capacity < 0) return MOE_ERR_INVALID_ARG;
+  const double cf = c->capacity_factor;
+  if (isnan(cf) || isinf(cf)) return MOE_ERR_INVALID_ARG;
+  if (cf > 0 && (cf < 1e-6 || cf > 1e6)) return MOE_ERR_INVALID_ARG;
+  if (c->E > kMaxE || c->k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (c->dtype == MOE_BF16 && (c->h % 64 != 0 || c->f % 64 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (c->dtype == MOE_F32 && (c->h % 4 != 0 || c->f % 4 != 0)) return MOE_ERR_UNSUPPORTED;
+  // every index the kernels form stays below 2^31 elements per row block
+  const int64_t lim = (int64_t)1 << 31;
+  if (c->T * c->k >= lim || c->h >= lim / 8 || c->f >= lim / 8) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// C = ceil(cf * n / E) with cf taken at its exact binary value: cf = m * 2^ex.
+int64_t exact_capacity(const moe_config* c) {
+  int64_t C;
+  if (!(c->capacity_factor > 0)) {
+    C = c->T;
+  } else {
+    const int64_t n = (c->cap_mode == MOE_CAP_ASSIGNMENTS) ? c->T * c->k : c->T;
+    int ex = 0;
+    const double fr = frexp(c->capacity_factor, &ex);
+    uint64_t m = (uint64_t)ldexp(fr, 53);
+    ex -= 53;
+    while (m != 0 && (m & 1) == 0) {
+      m >>= 1;
+      ++ex;
+    }
+    __int128 num = (__int128)m * n, den = c->E;
+    if (ex >= 0) num <<= ex; else den <<= -ex;
+    C = (int64_t)((num + den - 1) / den);
+  }
+  return C > c->min_capacity ? C : c->min_capacity;
+}
+
+Dims dims_of(const moe_config* c) {
+  Dims d;
+  d.T = c->T;
+  d.h = c->h;
+  d.f = c->f;
+  d.E = c->E;
+  d.k = c->k;
+  d.bf16 = c->dtype == MOE_BF16;
+  const int64_t Cx = exact_capacity(c);
+  d.C = Cx < d.T ? Cx : d.T;  // no expert can receive more than T assignments
+  const int64_t a = d.T * d.k, b = d.E * d.C;
+  d.rows_max = a < b ? a : b;
+  return d;
+}
+
+size_t elem_bytes(const Dims& d) { return d.bf16 ? 2 : 4; }
+
+struct Plan {
+  size_t bytes = 0;
+  size_t add(size_t n) {
+    const size_t o = bytes;
+    bytes += (n + 255) & ~size_t(255);
+    return o;
+  }
+};
+
+struct RouteWs {
+  size_t wt, wnt, part;
+  RouteShape rs;
+};
+RouteWs plan_route(const Dims& d, int noisy, Plan& pl) {
+  RouteWs w;
+  w.rs = route_shape((int)d.T, (int)d.E, d.bf16, noisy);
+  w.wt = d.bf16 ? pl.add((size_t)w.rs.EP * d.h * 2) : 0;
+  w.wnt = (d.bf16 && noisy) ? pl.add((size_t)w.rs.EP * d.h * 2) : 0;
+  w.part = pl.add((size_t)(w.rs.nblk > 0 ? w.rs.nblk : 1) * w.rs.EP * sizeof(double));
+  return w;
+}
+
+struct DispatchWs {
+  size_t hist, base;
+};
+DispatchWs plan_dispatch(const Dims& d, Plan& pl) {
+  const int64_t nchunk = (d.T + kChunk - 1) / kChunk;
+  DispatchWs w;
+  const size_t n = (size_t)(nchunk > 0 ? nchunk : 1) * d.k * d.E * sizeof(int32_t);
+  w.hist = pl.add(n);
+  w.base = pl.add(n);
+  return w;
+}
+
+struct FfnWs {
+  size_t map1, map2, A;
+  FfnShape fs;
+};
+FfnWs plan_ffn(const Dims& d, Plan& pl) {
+  FfnWs w;
+  w.fs = ffn_shape(d.rows_max, (int)d.E, (int)d.h, (int)d.f, (int)d.T, (int)d.k, d.bf16);
+  w.map1 = pl.add((d.E + 1) * sizeof(int32_t));
+  w.map2 = pl.add((d.E + 1) * sizeof(int32_t));
+  w.A = pl.add((size_t)(d.rows_max > 0 ? d.rows_max : 1) * d.f * elem_bytes(d));
+  return w;
+}
+
+struct LayerWs {
+  RouteWs route;
+  DispatchWs disp;
+  FfnWs ffn;
+  size_t idx, gate, slot, row_token, count, kept, offset, X, Y, scal;
+};
+LayerWs plan_layer(const Dims& d, int noisy, Plan& pl) {
+  LayerWs w;
+  w.route = plan_route(d, noisy, pl);
+  w.disp = plan_dispatch(d, pl);
+  w.ffn = plan_ffn(d, pl);
+  const size_t tk = (size_t)(d.T > 0 ? d.T : 1) * d.k;
+  const size_t rows = (size_t)(d.rows_max > 0 ? d.rows_max : 1);
+  w.idx = pl.add(tk * 4);
+  w.gate = pl.add(tk * 4);
+  w.slot = pl.add(tk * 4);
+  w.row_token = pl.add(rows * 4);
+  w.count = pl.add(d.E * 4);
+  w.kept = pl.add(d.E * 4);
+  w.offset = pl.add((d.E + 1) * 4);
+  w.X = pl.add(rows * d.h * elem_bytes(d));
+  w.Y = pl.add(rows * d.h * elem_bytes(d));
+  w.scal = pl.add(64);
+  return w;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                        \
+  do {                                       \
+    const hipError_t err_ = (expr);          \
+    if (err_ != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+int32_t run_route(const Dims& d, const moe_config* c, const RouteWs& w, const void* U,
+                  const void* W_r, const float* b_r, const void* W_noise, const float* noise,
+                  int32_t* idx, float* gate, float* logits, void* ws, hipStream_t s) {
+  RouteParams p;
+  p.T = (int)d.T;
+  p.h = (int)d.h;
+  p.E = (int)d.E;
+  p.k = (int)d.k;
+  p.score = c->score;
+  p.gate = c->gate;
+  p.U = U;
+  p.b_r = b_r;
+  p.noise = c->noisy ? noise : nullptr;
+  p.topk_idx = idx;
+  p.topk_gate = gate;
+  p.logits = logits;
+  p.prob_part = at<double>(ws, w.part);
+  if (d.bf16) {
+    MOE_TRY(launch_transpose_router_w(W_r, at<void>(ws, w.wt), (int)d.h, (int)d.E, w.rs.EP, s));
+    p.Wt = at<void>(ws, w.wt);
+    p.Wnt = nullptr;
+    if (c->noisy) {
+      MOE_TRY(launch_transpose_router_w(W_noise, at<void>(ws, w.wnt), (int)d.h, (int)d.E,
+                                        w.rs.EP, s));
+      p.Wnt = at<void>(ws, w.wnt);
+    }
+  } else {
+    p.Wt = W_r;
+    p.Wnt = c->noisy ? W_noise : nullptr;
+  }
+  MOE_TRY(launch_route(w.rs, p, d.bf16, c->noisy, s));
+  return MOE_OK;
+}
+
+int32_t run_dispatch(const Dims& d, const moe_config* c, const DispatchWs& w, const void* U,
+                     const int32_t* idx, void* X, int32_t* row_token, int32_t* slot,
+                     int32_t* count, int32_t* kept, int32_t* offset, void* ws, hipStream_t s) {
+  DispatchParams p;
+  p.T = (int)d.T;
+  p.E = (int)d.E;
+  p.k = (int)d.k;
+  p.C = (int)d.C;
+  p.token_major = c->fill == MOE_FILL_TOKEN_MAJOR;
+  p.topk_idx = idx;
+  p.hist = at<int32_t>(ws, w.hist);
+  p.base = at<int32_t>(ws, w.base);
+  p.count = count;
+  p.kept = kept;
+  p.offset = offset;
+  p.slot = slot;
+  p.row_token = row_token;
+  MOE_TRY(launch_dispatch(p, s));
+  MOE_TRY(launch_permute(U, slot, X, (int)d.T, (int)d.h, (int)d.k, d.bf16, s));
+  return MOE_OK;
+}
+
+int32_t run_tile_map(const Dims& d, const FfnWs& w, const int32_t* offset, void* ws,
+                     hipStream_t s) {
+  if (!d.bf16) return MOE_OK;
+  MOE_TRY(launch_tile_map(offset, (int)d.E, w.fs.bm1, w.fs.bm2, at<int32_t>(ws, w.map1),
+                          at<int32_t>(ws, w.map2), s));
+  return MOE_OK;
+}
+
+// Expects run_tile_map to have been enqueued before.
+int32_t run_gate_up(const Dims& d, const FfnWs& w, const void* X, const int32_t* offset,
+                    const void* Wg, const void* Wu, const void* Wd, void* Y, void* ws,
+                    hipStream_t s) {
+  if (!d.bf16)
+    return hip_status(launch_ffn_f32(X, offset, Wg, Wu, Wd, at<void>(ws, w.A), Y, d.rows_max,
+                                     (int)d.E, (int)d.h, (int)d.f, s));
+  MOE_TRY(launch_gate_up(w.fs, X, offset, at<int32_t>(ws, w.map1), Wg, Wu, at<void>(ws, w.A),
+                         (int)d.E, (int)d.h, (int)d.f, 1, s));
+  return MOE_OK;
+}
+
+int32_t run_down(const Dims& d, const FfnWs& w, const int32_t* offset, const void* Wd, void* Y,
+                 void* ws, hipStream_t s) {
+  if (!d.bf16) return MOE_OK;  // the float32 path ran both products already
+  MOE_TRY(launch_down(w.fs, at<void>(ws, w.A), offset, at<int32_t>(ws, w.map2), Wd, Y, (int)d.E,
+                      (int)d.h, (int)d.f, 1, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape not supported";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP launch failed";
+    default: return "unknown moe status";
+  }
+}
+
+int32_t moe_capacity(const moe_config* cfg, int64_t* C) {
+  const int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!C) return MOE_ERR_INVALID_ARG;
+  *C = exact_capacity(cfg);
+  return MOE_OK;
+}
+
+int32_t moe_max_rows(const moe_config* cfg, int64_t* rows_max) {
+  const int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!rows_max) return MOE_ERR_INVALID_ARG;
+  *rows_max = dims_of(cfg).rows_max;
+  return MOE_OK;
+}
+
+int32_t moe_workspace_size(const moe_config* cfg, int32_t entry, size_t* bytes) {
+  const int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  const Dims d = dims_of(cfg);
+  Plan pl;
+  switch (entry) {
+    case MOE_WS_ROUTE: plan_route(d, cfg->noisy, pl); break;
+    case MOE_WS_DISPATCH: plan_dispatch(d, pl); break;
+    case MOE_WS_EXPERT_FFN: plan_ffn(d, pl); break;
+    case MOE_WS_LAYER: plan_layer(d, cfg->noisy, pl); break;
+    default: return MOE_ERR_INVALID_ARG;
+  }
+  *bytes = pl.bytes;
+  return MOE_OK;
+}
+
+int32_t moe_route(const moe_config* cfg, const void* U, const void* W_r, const float* b_r,
+                  const void* W_noise, const float* noise, int32_t* topk_idx, float* topk_gate,
+                  float* logits, float* prob_sum, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const Dims d = dims_of(cfg);
+  if (d.T > 0 && (!U || !topk_idx || !topk_gate)) return MOE_ERR_INVALID_ARG;
+  if (!W_r || !ws) return MOE_ERR_INVALID_ARG;
+  if (cfg->noisy && (!W_noise || !noise)) return MOE_ERR_INVALID_ARG;
+  Plan pl;
+  const RouteWs w = plan_route(d, cfg->noisy, pl);
+  if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_route(d, cfg, w, U, W_r, b_r, W_noise, noise, topk_idx, topk_gate, logits, ws, s);
+  if (st != MOE_OK) return st;
+  if (prob_sum)
+    return hip_status(launch_prob_reduce(at<double>(ws, w.part), w.rs.nblk, w.rs.EP, (int)d.E,
+                                         prob_sum, s));
+  return MOE_OK;
+}
+
+int32_t moe_dispatch(const moe_config* cfg, const void* U, const int32_t* topk_idx, void* X,
+                     int32_t* row_token, int32_t* slot, int32_t* count, int32_t* kept,
+                     int32_t* offset, void* ws, size_t ws_bytes, void* stream) {
+  const int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const Dims d = dims_of(cfg);
+  if (d.T > 0 && (!U || !topk_idx || !X || !row_token || !slot)) return MOE_ERR_INVALID_ARG;
+  if (!count || !kept || !offset || !ws) return MOE_ERR_INVALID_ARG;
+  Plan pl;
+  const DispatchWs w = plan_dispatch(d, pl);
+  if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
+  return run_dispatch(d, cfg, w, U, topk_idx, X, row_token, slot, count, kept, offset, ws,
+                      static_cast<hipStream_t>(stream));
+}
+
+int32_t moe_expert_ffn(const moe_config* cfg, const void* X, const int32_t* offset,
+                       const void* W_gate, const void* W_up, const void* W_down, void* Y,
+                       void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const Dims d = dims_of(cfg);
+  if (!offset || !W_gate || !W_up || !W_down || !ws) return MOE_ERR_INVALID_ARG;
+  if (d.rows_max > 0 && (!X || !Y)) return MOE_ERR_INVALID_ARG;
+  Plan pl;
+  const FfnWs w = plan_ffn(d, pl);
+  if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_tile_map(d, w, offset, ws, s);
+  if (st != MOE_OK) return st;
+  st = run_gate_up(d, w, X, offset, W_gate, W_up, W_down, Y, ws, s);
+  if (st != MOE_OK) return st;
+  return run_down(d, w, offset, W_down, Y, ws, s);
+}
+
+int32_t moe_combine(const moe_config* cfg, const void* U, const void* Y, const int32_t* slot,
+                    const float* topk_gate, void* out, void* stream) {
+  const int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const Dims d = dims_of(cfg);
+  if (d.T > 0 && (!U || !slot || !topk_gate || !out)) return MOE_ERR_INVALID_ARG;
+  if (d.rows_max > 0 && !Y) return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (out == U || out == Y)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(U, Y, slot, topk_gate, out, (int)d.T, (int)d.h, (int)d.k,
+                                   d.bf16, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_stats(const moe_config* cfg, const int32_t* count, const int32_t* kept,
+                  const float* prob_sum, float* f, float* P, float* aux_loss, float* maxvio,
+                  int32_t* n_dropped, void* stream) {
+  const int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!count || !kept || !prob_sum) return MOE_ERR_INVALID_ARG;
+  StatsParams p{(int)cfg->T, (int)cfg->E, (int)cfg->k, count, kept, nullptr, 0, 0,
+                prob_sum, f, P, aux_loss, maxvio, n_dropped};
+  return hip_status(launch_stats(p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
+                          const float* b_r, const void* W_noise, const float* noise,
+                          const void* W_gate, const void* W_up, const void* W_down, void* out,
+                          const moe_aux_outputs* aux, void* const* stage_events, void* ws,
+                          size_t ws_bytes, void* stream) {
+  int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const Dims d = dims_of(cfg);
+  if (d.T > 0 && (!U || !out)) return MOE_ERR_INVALID_ARG;
+  if (!W_r || !W_gate || !W_up || !W_down || !ws) return MOE_ERR_INVALID_ARG;
+  if (cfg->noisy && (!W_noise || !noise)) return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && out == U) return MOE_ERR_INVALID_ARG;
+  if (stage_events)
+    for (int i = 0; i <= MOE_NUM_STAGES; ++i)
+      if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
+  Plan pl;
+  const LayerWs w = plan_layer(d, cfg->noisy, pl);
+  if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
+  moe_aux_outputs o;
+  memset(&o, 0, sizeof(o));
+  if (aux) o = *aux;
+  int32_t* idx = o.topk_idx ? o.topk_idx : at<int32_t>(ws, w.idx);
+  float* gate = o.topk_gate ? o.topk_gate : at<float>(ws, w.gate);
+  int32_t* slot = o.slot ? o.slot : at<int32_t>(ws, w.slot);
+  int32_t* row_token = o.row_token ? o.row_token : at<int32_t>(ws, w.row_token);
+  int32_t* count = o.count ? o.count : at<int32_t>(ws, w.count);
+  int32_t* kept = o.kept ? o.kept : at<int32_t>(ws, w.kept);
+  int32_t* offset = o.offset ? o.offset : at<int32_t>(ws, w.offset);
+  void* X = o.X ? o.X : at<void>(ws, w.X);
+  void* Y = o.Y ? o.Y : at<void>(ws, w.Y);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> hipError_t {
+    return stage_events ? hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s)
+                        : hipSuccess;
+  };
+
+  MOE_TRY(mark(0));
+  st = run_route(d, cfg, w.route, U, W_r, b_r, W_noise, noise, idx, gate, o.logits, ws, s);
+  if (st != MOE_OK) return st;
+  MOE_TRY(mark(1));
+  st = run_dispatch(d, cfg, w.disp, U, idx, X, row_token, slot, count, kept, offset, ws, s);
+  if (st != MOE_OK) return st;
+  st = run_tile_map(d, w.ffn, offset, ws, s);
+  if (st != MOE_OK) return st;
+  MOE_TRY(mark(2));
+  st = run_gate_up(d, w.ffn, X, offset, W_gate, W_up, W_down, Y, ws, s);
+  if (st != MOE_OK) return st;
+  MOE_TRY(mark(3));
+  st = run_down(d, w.ffn, offset, W_down, Y, ws, s);
+  if (st != MOE_OK) return st;
+  MOE_TRY(mark(4));
+  MOE_TRY(launch_combine(U, Y, slot, gate, out, (int)d.T, (int)d.h, (int)d.k, d.bf16, s));
+  MOE_TRY(mark(5));
+  if (o.prob_sum)
+    MOE_TRY(launch_prob_reduce(at<double>(ws, w.route.part), w.route.rs.nblk, w.route.rs.EP,
+                               (int)d.E, o.prob_sum, s));
+  StatsParams sp{(int)d.T, (int)d.E, (int)d.k, count, kept, at<double>(ws, w.route.part),
+                 w.route.rs.nblk, w.route.rs.EP, nullptr, o.f, o.P,
+                 o.aux_loss ? o.aux_loss : at<float>(ws, w.scal),
+                 o.maxvio ? o.maxvio : at<float>(ws, w.scal) + 1,
+                 o.n_dropped ? o.n_dropped : at<int32_t>(ws, w.scal) + 2};
+  MOE_TRY(launch_stats(sp, s));
+  MOE_TRY(mark(6));
+  return MOE_OK;
+}
+
+}  // extern "C"

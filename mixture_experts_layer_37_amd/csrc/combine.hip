@@ -1,0 +1,118 @@
+// Combine with the residual, and the load-balance statistics.
+//
+// Method: page "MoE 与专家并行": the layer output h'_t = u_t + sum_i g_{i,t}
+// FFN_i(u_t) (section "从稠密 FFN 到 MoE", eq. h'_t) with dropped assignments
+// contributing nothing (section "专家容量与丢 token"); f_i, P_i and
+// L_aux = E * sum f_i P_i (section "负载均衡辅助损失：推导与梯度"); MaxVio
+// (section "无辅助损失的负载均衡").
+//
+// Combine is a weighted gather: one wave per token reads its residual row and
+// its kept expert rows (16 bytes per lane per step), accumulates in float32 in
+// rank order and writes the row once.  No atomics, so the result is
+// deterministic and each output byte is written exactly once.
+#include <limits.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+template <typename TE>
+__global__ __launch_bounds__(256) void combine_kernel(const TE* U, const TE* Y,
+                                                      const int32_t* slot, const float* gate,
+                                                      TE* out, int T, int h, int k) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  int sl[8];
+  float g[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    sl[r] = r < k ? slot[(size_t)t * k + r] : -1;
+    g[r] = r < k ? gate[(size_t)t * k + r] : 0.f;
+  }
+  constexpr int V = Elem<TE>::kPer16B;
+  const int nvec = h / V;
+  const TE* u = U + (size_t)t * h;
+  TE* o = out + (size_t)t * h;
+  for (int i = lane; i < nvec; i += 64) {
+    float acc[V], y[V];
+    Elem<TE>::unpack(ld16(u + (size_t)i * V), acc);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if (sl[r] < 0) continue;
+      Elem<TE>::unpack(ld16(Y + (size_t)sl[r] * h + (size_t)i * V), y);
+#pragma unroll
+      for (int q = 0; q < V; ++q) acc[q] = fmaf(g[r], y[q], acc[q]);
+    }
+    st16(o + (size_t)i * V, Elem<TE>::pack(acc));
+  }
+}
+
+__global__ __launch_bounds__(256) void stats_kernel(StatsParams p) {
+  __shared__ double s_fp[256];
+  __shared__ int s_max[256];
+  __shared__ int s_drop[256];
+  const int e = threadIdx.x;
+  double fp = 0.0;
+  int cnt = INT_MIN, drop = 0;
+  if (e < p.E) {
+    cnt = p.count[e];
+    drop = cnt - p.kept[e];
+    double ps = 0.0;
+    if (p.prob_part) {
+      for (int b = 0; b < p.nparts; ++b) ps += p.prob_part[(size_t)b * p.EP + e];
+    } else {
+      ps = (double)p.prob_sum[e];
+    }
+    const double f = p.T > 0 ? (double)cnt / ((double)p.T * p.k) : 0.0;
+    const double P = p.T > 0 ? ps / p.T : 0.0;
+    if (p.f) p.f[e] = (float)f;
+    if (p.P) p.P[e] = (float)P;
+    fp = f * P;
+  }
+  s_fp[e] = fp;
+  s_max[e] = cnt;
+  s_drop[e] = drop;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (e < w) {
+      s_fp[e] += s_fp[e + w];
+      s_max[e] = max(s_max[e], s_max[e + w]);
+      s_drop[e] += s_drop[e + w];
+    }
+    __syncthreads();
+  }
+  if (e == 0) {
+    const double mean = (double)p.T * p.k / p.E;
+    if (p.aux) p.aux[0] = (float)(p.E * s_fp[0]);
+    if (p.maxvio) p.maxvio[0] = p.T > 0 ? (float)((s_max[0] - mean) / mean) : 0.f;
+    if (p.n_dropped) p.n_dropped[0] = s_drop[0];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* U, const void* Y, const int32_t* slot, const float* gate,
+                          void* out, int T, int h, int k, int bf16_, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((T + 3) / 4);
+  if (bf16_)
+    hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(256), 0, s, static_cast<const bf16*>(U),
+                       static_cast<const bf16*>(Y), slot, gate, static_cast<bf16*>(out), T, h,
+                       k);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(U), static_cast<const float*>(Y), slot, gate,
+                       static_cast<float*>(out), T, h, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats(const StatsParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

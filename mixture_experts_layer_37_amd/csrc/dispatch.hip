@@ -1,0 +1,203 @@
+// Dispatch: capacity cut, fill order and the permutation of token rows into
+// per-expert contiguous blocks.
+//
+// Method: page "MoE 与专家并行", section "专家容量与丢 token": capacity C, slots
+// filled in token order with later tokens dropped (they pass only the
+// residual), and the GShard order that places every token's first choice
+// before any second choice; the rows of one expert are contiguous as in the
+// sort-and-group dataflow of section "路由器：打分、top-k、加权求和".
+//
+// The sequential definition "visit assignments in fill order, each takes the
+// next free position of its expert" is computed in three data-parallel passes
+// with integer arithmetic only, so positions are exact and deterministic:
+//  1. per 256-token chunk and rank, a histogram of experts (LDS integer
+//     counters; counts do not depend on the order of the increments);
+//  2. one workgroup scans the histograms in fill order, giving each
+//     (rank, chunk, expert) the number of earlier assignments to that expert,
+//     plus count, kept = min(count, C) and the exclusive offsets of kept;
+//  3. per chunk, each assignment adds the number of earlier assignments in its
+//     own chunk (wave ballots for lanes below it, LDS counts for waves before
+//     it); position < C keeps it at row offset[e] + position.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ int load_expert(const int32_t* idx, int t, int r, int T, int k, int E) {
+  if (t >= T) return -1;
+  const int e = idx[(size_t)t * k + r];
+  return (e >= 0 && e < E) ? e : -1;  // ids outside [0, E) are ignored
+}
+
+__global__ __launch_bounds__(256) void hist_kernel(DispatchParams p) {
+  __shared__ int cnt[8 * 256];
+  const int nchunk = gridDim.x, c = blockIdx.x;
+  for (int i = threadIdx.x; i < p.k * p.E; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  const int t = c * kChunk + threadIdx.x;
+  for (int r = 0; r < p.k; ++r) {
+    const int e = load_expert(p.topk_idx, t, r, p.T, p.k, p.E);
+    if (e >= 0) atomicAdd(&cnt[r * p.E + e], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < p.k * p.E; i += blockDim.x) {
+    const int r = i / p.E, e = i % p.E;
+    p.hist[((size_t)r * nchunk + c) * p.E + e] = cnt[i];
+  }
+}
+
+__global__ __launch_bounds__(256) void scan_kernel(DispatchParams p, int nchunk) {
+  __shared__ int kept_s[256];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < p.E) {
+    if (!p.token_major) {
+      // rank-major: (rank 0, chunk 0), (rank 0, chunk 1), ..., (rank 1, chunk 0), ...
+      for (int r = 0; r < p.k; ++r)
+        for (int c = 0; c < nchunk; ++c) {
+          const size_t i = ((size_t)r * nchunk + c) * p.E + e;
+          p.base[i] = run;
+          run += p.hist[i];
+        }
+    } else {
+      // token-major: chunks in token order; a token holds an expert at most once
+      for (int c = 0; c < nchunk; ++c) {
+        p.base[(size_t)c * p.E + e] = run;
+        for (int r = 0; r < p.k; ++r) run += p.hist[((size_t)r * nchunk + c) * p.E + e];
+      }
+    }
+    const int kp = run < p.C ? run : p.C;
+    p.count[e] = run;
+    p.kept[e] = kp;
+    kept_s[e] = kp;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int i = 0; i < p.E; ++i) {
+      p.offset[i] = acc;
+      acc += kept_s[i];
+    }
+    p.offset[p.E] = acc;
+  }
+}
+
+__global__ __launch_bounds__(256) void assign_kernel(DispatchParams p) {
+  __shared__ int wc[4][256];
+  const int nchunk = gridDim.x, c = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = c * kChunk + threadIdx.x;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // k <= 8; loops over ranks are unrolled to 8 so ex[] stays in registers
+  int ex[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) ex[r] = r < p.k ? load_expert(p.topk_idx, t, r, p.T, p.k, p.E) : -1;
+
+  if (!p.token_major) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if (r >= p.k) break;
+      for (int i = threadIdx.x; i < 4 * 256; i += blockDim.x) (&wc[0][0])[i] = 0;
+      __syncthreads();
+      const int e = ex[r];
+      const uint64_t same = match_lanes(e, e, e >= 0);
+      if (e >= 0) atomicAdd(&wc[wave][e], 1);
+      __syncthreads();
+      if (e >= 0) {
+        int pos = p.base[((size_t)r * nchunk + c) * p.E + e] + __popcll(same & below);
+        for (int w = 0; w < wave; ++w) pos += wc[w][e];
+        const int row = pos < p.C ? p.offset[e] + pos : -1;
+        p.slot[(size_t)t * p.k + r] = row;
+        if (row >= 0) p.row_token[row] = t;
+      } else if (t < p.T) {
+        p.slot[(size_t)t * p.k + r] = -1;
+      }
+      __syncthreads();
+    }
+  } else {
+    for (int i = threadIdx.x; i < 4 * 256; i += blockDim.x) (&wc[0][0])[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (ex[r] >= 0) atomicAdd(&wc[wave][ex[r]], 1);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if (r >= p.k) break;
+      const int e = ex[r];
+      // lanes below holding expert e at any rank (a token holds an expert at most once)
+      uint64_t any = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q < p.k) any |= match_lanes(e, ex[q], ex[q] >= 0);
+      if (e >= 0) {
+        int pos = p.base[(size_t)c * p.E + e] + __popcll(any & below);
+        for (int w = 0; w < wave; ++w) pos += wc[w][e];
+        const int row = pos < p.C ? p.offset[e] + pos : -1;
+        p.slot[(size_t)t * p.k + r] = row;
+        if (row >= 0) p.row_token[row] = t;
+      } else if (t < p.T) {
+        p.slot[(size_t)t * p.k + r] = -1;
+      }
+    }
+  }
+}
+
+// One wave per token: read the row once, write it to each kept slot.
+template <typename TE>
+__global__ __launch_bounds__(256) void permute_kernel(const TE* U, const int32_t* slot, TE* X,
+                                                      int T, int h, int k) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  int sl[8];
+  bool any = false;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    sl[r] = r < k ? slot[(size_t)t * k + r] : -1;
+    any |= sl[r] >= 0;
+  }
+  if (!any) return;
+  constexpr int V = Elem<TE>::kPer16B;
+  const int nvec = h / V;
+  const TE* src = U + (size_t)t * h;
+  for (int i = lane; i < nvec; i += 64) {
+    const u32x4 v = ld16(src + (size_t)i * V);
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (sl[r] >= 0) st16(X + (size_t)sl[r] * h + (size_t)i * V, v);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s) {
+  const int nchunk = (p.T + kChunk - 1) / kChunk;
+  if (nchunk > 0) {
+    hipLaunchKernelGGL(hist_kernel, dim3(nchunk), dim3(256), 0, s, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, p, nchunk);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || nchunk == 0) return err;
+  hipLaunchKernelGGL(assign_kernel, dim3(nchunk), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const void* U, const int32_t* slot, void* X, int T, int h, int k,
+                          int bf16_, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((T + 3) / 4);
+  if (bf16_)
+    hipLaunchKernelGGL(permute_kernel<bf16>, grid, dim3(256), 0, s,
+                       static_cast<const bf16*>(U), slot, static_cast<bf16*>(X), T, h, k);
+  else
+    hipLaunchKernelGGL(permute_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(U), slot, static_cast<float*>(X), T, h, k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

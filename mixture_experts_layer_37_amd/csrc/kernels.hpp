@@ -1,0 +1,97 @@
+// Host-side launchers of the MoE kernels (internal interface of libmoe).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- router
+struct RouteParams {
+  int T, h, E, k;
+  int score;  // 0 softmax, 1 sigmoid
+  int gate;   // 0 raw, 1 renorm
+  const void* U;
+  const float* b_r;
+  const float* noise;
+  const void* Wt;    // bf16: W_r transposed to [EP][h], zero rows past E; f32: W_r [h][E]
+  const void* Wnt;   // same for W_noise (noisy only)
+  int32_t* topk_idx;
+  float* topk_gate;
+  float* logits;     // optional [T][E]
+  double* prob_part; // [nblk][EP] per-block sums of the score entering P
+};
+
+struct RouteShape {
+  int EP;    // experts padded to 16 * NB (NB a power of two)
+  int NB;
+  int MW;    // 16-row blocks per wave (bf16) ; rows per block = 16 * MW
+  int RB;    // tokens per workgroup
+  int nblk;  // workgroups
+};
+
+RouteShape route_shape(int T, int E, int bf16, int noisy);
+hipError_t launch_transpose_router_w(const void* W, void* WT, int h, int E, int EP,
+                                     hipStream_t s);
+hipError_t launch_route(const RouteShape& rs, const RouteParams& p, int bf16, int noisy,
+                        hipStream_t s);
+hipError_t launch_prob_reduce(const double* part, int nblk, int EP, int E, float* prob_sum,
+                              hipStream_t s);
+
+// ---------------------------------------------------------------- dispatch
+constexpr int kChunk = 256;  // tokens per dispatch workgroup
+
+struct DispatchParams {
+  int T, E, k, C;
+  int token_major;
+  const int32_t* topk_idx;
+  int32_t* hist;   // [k][nchunk][E]
+  int32_t* base;   // [k][nchunk][E]
+  int32_t* count;  // [E]
+  int32_t* kept;   // [E]
+  int32_t* offset; // [E+1]
+  int32_t* slot;   // [T][k]
+  int32_t* row_token;
+};
+hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s);
+hipError_t launch_permute(const void* U, const int32_t* slot, void* X, int T, int h, int k,
+                          int bf16, hipStream_t s);
+
+// ---------------------------------------------------------------- experts
+struct FfnShape {
+  int bm1, bm2;     // row tile of the gate/up and the down GEMMs
+  int mt1, mt2;     // static bound on m-tiles of each GEMM
+  int nt1, nt2;     // n-tiles of each GEMM
+  int grid1, grid2; // workgroups launched (multiple of 8)
+};
+FfnShape ffn_shape(int64_t rows_max, int E, int h, int f, int T, int k, int bf16);
+hipError_t launch_tile_map(const int32_t* offset, int E, int bm1, int bm2, int32_t* map1,
+                           int32_t* map2, hipStream_t s);
+hipError_t launch_gate_up(const FfnShape& fs, const void* X, const int32_t* offset,
+                          const int32_t* map1, const void* Wg, const void* Wu, void* A, int E,
+                          int h, int f, int bf16, hipStream_t s);
+hipError_t launch_down(const FfnShape& fs, const void* A, const int32_t* offset,
+                       const int32_t* map2, const void* Wd, void* Y, int E, int h, int f,
+                       int bf16, hipStream_t s);
+
+// ---------------------------------------------------------------- combine, stats
+hipError_t launch_combine(const void* U, const void* Y, const int32_t* slot, const float* gate,
+                          void* out, int T, int h, int k, int bf16, hipStream_t s);
+
+struct StatsParams {
+  int T, E, k;
+  const int32_t* count;
+  const int32_t* kept;
+  const double* prob_part;  // [nparts][EP] (layer) or NULL
+  int nparts, EP;
+  const float* prob_sum;    // [E] (standalone) or NULL
+  float* f;
+  float* P;
+  float* aux;
+  float* maxvio;
+  int32_t* n_dropped;
+};
+hipError_t launch_stats(const StatsParams& p, hipStream_t s);
+
+}  // namespace moe

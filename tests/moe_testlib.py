@@ -1,0 +1,213 @@
+"""Shared helpers of the GPU parity tests: run the HIP path, run the oracle,
+compare them under the agreed protocol.
+
+Protocol (routing made well-posed despite float differences):
+  * the oracle routes from exactly the float32 logits the GPU used; ids, rank
+    order, counts, kept, offsets, slots, row tokens and the drop mask must be
+    identical, gates agree to 1e-6 relative;
+  * the oracle's own float64 logits agree with the GPU's to 1e-4 absolute
+    (logits are O(1)); routing from them must match on every token whose
+    selection margin exceeds that tolerance;
+  * outputs are compared per token by the norm-wise relative error
+    max_t ||x_t - x^_t|| / ||x^_t||, for out and for the MoE part out - u,
+    with tolerance 1e-4 (float32) or 2e-2 (bf16).
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+from mixture_experts_layer_37_amd import binding as B
+from mixture_experts_layer_37_amd import inputs as I
+from oracle import moe_oracle as O
+
+ORACLE_MODE = {"softmax": O.SOFTMAX, "sigmoid": O.SIGMOID, "raw": O.GATE_RAW,
+               "renorm": O.GATE_RENORM, "rank_major": O.FILL_RANK_MAJOR,
+               "token_major": O.FILL_TOKEN_MAJOR, "assignments": O.CAP_ASSIGNMENTS,
+               "tokens": O.CAP_TOKENS}
+
+LOGIT_ATOL = 1e-4
+
+
+def out_tol(w) -> float:
+    return 1e-4 if w.dtype == "f32" else 2e-2
+
+
+# Reduced versions of the five workloads: same scoring, gating, capacity and
+# distributions, sizes the float64 oracle finishes in seconds, chosen so that
+# experts span several row tiles with ragged tails and h, f are not multiples
+# of the column tiles.
+SMALL = {
+    "tiny_f32": I.WORKLOADS["tiny_f32"],
+    "mixtral_small": I.WORKLOADS["mixtral_bf16"].replace(name="mixtral_small", T=1024, h=320,
+                                                         f=448),
+    "switch_small": I.WORKLOADS["switch_bf16"].replace(name="switch_small", T=2048, h=256,
+                                                       f=512, E=32),
+    "deepseek_small": I.WORKLOADS["deepseek_v3_bf16"].replace(name="deepseek_small", T=512,
+                                                              h=448, f=192, E=64),
+    "noisy_small": I.WORKLOADS["noisy_long_bf16"].replace(name="noisy_small", T=2048, h=320,
+                                                          f=448, E=16),
+}
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    if t is None:
+        return None
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.numpy()
+
+
+def f64(t):
+    return None if t is None else to_np(t).astype(np.float64)
+
+
+def run_layer(w, x, fields=None, stage_events=None):
+    cfg = B.make_config(w)
+    dev = x["U"].device
+    aux = B.alloc_aux(cfg, dev, fields)
+    out = torch.empty((w.T, w.h), dtype=I.torch_dtype(w), device=dev)
+    B.moe_layer_forward(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], x["noise"], x["W_gate"],
+                        x["W_up"], x["W_down"], out, aux=aux, stage_events=stage_events)
+    torch.cuda.synchronize()
+    aux["out"] = out
+    return cfg, aux
+
+
+def oracle_capacity(w) -> int:
+    return O.capacity(w.T, w.E, w.k, w.capacity_factor, ORACLE_MODE[w.cap_mode],
+                      w.min_capacity)
+
+
+def check_routing_shared_logits(w, g: dict) -> dict:
+    """Oracle routing from the GPU's float32 logits; bit-exact integer outputs."""
+    C = oracle_capacity(w)
+    H = to_np(g["logits"]).astype(np.float64)
+    r = O.route(H, w.k, ORACLE_MODE[w.score], ORACLE_MODE[w.gate], C, ORACLE_MODE[w.fill])
+    np.testing.assert_array_equal(to_np(g["topk_idx"]), r["idx"], err_msg="topk_idx")
+    np.testing.assert_array_equal(to_np(g["count"]), r["count"], err_msg="count")
+    np.testing.assert_array_equal(to_np(g["kept"]), r["kept"], err_msg="kept")
+    np.testing.assert_array_equal(to_np(g["offset"]), r["offset"], err_msg="offset")
+    np.testing.assert_array_equal(to_np(g["slot"]), r["slot"], err_msg="slot")
+    rows = int(r["offset"][-1])
+    np.testing.assert_array_equal(to_np(g["row_token"])[:rows], r["row_token"], err_msg="row_token")
+    np.testing.assert_allclose(to_np(g["topk_gate"]), r["gate"], rtol=1e-6, atol=1e-7,
+                               err_msg="topk_gate")
+    if w.gate == "renorm":
+        np.testing.assert_allclose(to_np(g["topk_gate"]).astype(np.float64).sum(1), 1.0,
+                                   atol=1e-6, err_msg="gate sums")
+    return r
+
+
+def check_stats(w, g: dict, r: dict):
+    T, k = w.T, w.k
+    f_ref = (r["count"] / (T * k)).astype(np.float32)
+    np.testing.assert_array_equal(to_np(g["f"]), f_ref, err_msg="f")
+    np.testing.assert_allclose(to_np(g["P"]), r["P"], rtol=1e-5, atol=1e-9, err_msg="P")
+    np.testing.assert_allclose(to_np(g["prob_sum"]), r["prob_sum"], rtol=1e-5, atol=1e-6,
+                               err_msg="prob_sum")
+    np.testing.assert_allclose(float(to_np(g["aux_loss"])[0]), r["aux"], rtol=1e-5,
+                               err_msg="aux")
+    np.testing.assert_allclose(float(to_np(g["maxvio"])[0]), r["maxvio"], rtol=1e-6,
+                               atol=1e-6, err_msg="maxvio")
+    assert int(to_np(g["n_dropped"])[0]) == r["n_dropped"]
+
+
+def check_logits_end_to_end(w, g: dict, x_cpu: dict, tokens=None) -> dict:
+    """Oracle float64 logits vs the GPU's; routing agreement outside near-ties."""
+    tok = slice(None) if tokens is None else tokens
+    U = f64(x_cpu["U"])[tok]
+    noise = None if x_cpu["noise"] is None else f64(x_cpu["noise"])[tok]
+    H = O.router_logits(U, f64(x_cpu["W_r"]), f64(x_cpu["b_r"]), f64(x_cpu["W_noise"]), noise)
+    Hg = to_np(g["logits"]).astype(np.float64)[tok]
+    err = np.abs(H - Hg).max()
+    assert err <= LOGIT_ATOL, f"logits differ by {err}"
+    idx_o = O.select_topk(H, w.k)
+    idx_g = to_np(g["topk_idx"])[tok]
+    srt = -np.sort(-H, axis=1)
+    gaps = np.diff(-srt[:, : w.k + 1], axis=1) if w.k < w.E else np.diff(-srt, axis=1)
+    margin = np.abs(gaps).min(axis=1) if gaps.size else np.full(H.shape[0], np.inf)
+    clear = margin > 2 * LOGIT_ATOL
+    mism = (idx_o != idx_g).any(axis=1)
+    assert not (mism & clear).any(), f"{int((mism & clear).sum())} clear tokens routed differently"
+    return {"near_ties": int((~clear).sum()), "flipped": int(mism.sum()), "logit_err": float(err)}
+
+
+def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max over rows of ||got - ref|| / ||ref|| (rows with ||ref|| = 0 use 1e-6 absolute)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.size == 0:
+        return 0.0
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    zero = den == 0
+    rel = np.where(zero, num / 1e-6, num / np.where(zero, 1.0, den))
+    return float(rel.max())
+
+
+def delta_err(w, got_out, U, ref_out) -> float:
+    """Error of the MoE part out - u, allowing for the rounding of out itself.
+
+    out is stored in the layer's dtype, so out - u carries that rounding
+    (unit roundoff q = 2^-8 for bf16, 2^-24 for float32) relative to |out|,
+    which can exceed tol * |out - u| when the gates are small.  Returns
+    max_t ||d_t - d^_t|| / (||d^_t|| + q ||out^_t|| / tol): <= tol passes.
+    """
+    tol = out_tol(w)
+    q = 2.0 ** -8 if w.dtype == "bf16" else 2.0 ** -24
+    d = np.asarray(got_out, np.float64) - U
+    dr = ref_out - U
+    num = np.linalg.norm(d - dr, axis=1)
+    den = np.linalg.norm(dr, axis=1) + q * np.linalg.norm(ref_out, axis=1) / tol
+    return float((num / np.maximum(den, 1e-300)).max()) if num.size else 0.0
+
+
+def check_outputs_small(w, g: dict, x_cpu: dict, r: dict):
+    """Full oracle outputs (with the verified routing) vs the GPU outputs."""
+    U = f64(x_cpu["U"])
+    rows = int(r["offset"][-1])
+    X = U[r["row_token"]]
+    np.testing.assert_array_equal(to_np(g["X"])[:rows], to_np(x_cpu["U"])[r["row_token"]],
+                                  err_msg="X rows are copies of U rows")
+    Wg, Wu, Wd = f64(x_cpu["W_gate"]), f64(x_cpu["W_up"]), f64(x_cpu["W_down"])
+    Y = O.expert_outputs(X, r["offset"], Wg, Wu, Wd)
+    tol = out_tol(w)
+    ey = row_rel_err(to_np(g["Y"])[:rows], Y)
+    assert ey <= tol, f"Y rel err {ey}"
+    out = O.combine(U, Y, r["slot"], r["gate"])
+    eo = row_rel_err(to_np(g["out"]), out)
+    ed = delta_err(w, f64(g["out"]), U, out)
+    assert eo <= tol, f"out rel err {eo}"
+    assert ed <= tol, f"out - u rel err {ed}"
+    # fully dropped tokens return their residual bit for bit
+    full = (r["slot"] < 0).all(axis=1)
+    if full.any():
+        np.testing.assert_array_equal(to_np(g["out"])[full], to_np(x_cpu["U"])[full])
+    return {"Y": ey, "out": eo, "delta": ed}
+
+
+def sampled_expert_rows(r: dict, E: int, n_experts: int = 3, per_expert: int = 4, seed: int = 0):
+    """(expert, rows) pairs: the first, last and some middle rows of a few non-empty experts."""
+    rng = np.random.default_rng(seed)
+    nonempty = [e for e in range(E) if r["offset"][e + 1] > r["offset"][e]]
+    if not nonempty:
+        return []
+    pick = sorted(set([nonempty[0], nonempty[-1], nonempty[len(nonempty) // 2]]))[:n_experts]
+    out = []
+    for e in pick:
+        a, b = int(r["offset"][e]), int(r["offset"][e + 1])
+        rows = {a, b - 1}
+        if b - a > 2:
+            rows.update(rng.integers(a, b, size=per_expert - 2).tolist())
+        out.append((e, sorted(rows)))
+    return out
