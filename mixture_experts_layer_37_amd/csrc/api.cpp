@@ -104,7 +104,7 @@ struct Plan {
 };
 
 struct RouteWs {
-  size_t wt, wnt, part;
+  size_t wt, wnt, part, total;
   RouteShape rs;
 };
 RouteWs plan_route(const Dims& d, int noisy, Plan& pl) {
@@ -113,6 +113,7 @@ RouteWs plan_route(const Dims& d, int noisy, Plan& pl) {
   w.wt = d.bf16 ? pl.add((size_t)w.rs.EP * d.h * 2) : 0;
   w.wnt = (d.bf16 && noisy) ? pl.add((size_t)w.rs.EP * d.h * 2) : 0;
   w.part = pl.add((size_t)(w.rs.nblk > 0 ? w.rs.nblk : 1) * w.rs.EP * sizeof(double));
+  w.total = pl.add((size_t)w.rs.EP * sizeof(double));
   return w;
 }
 
@@ -132,9 +133,21 @@ struct FfnWs {
   size_t map1, map2, A;
   FfnShape fs;
 };
+// Compute units of the current device (sizes the persistent GEMM grid; a
+// host query, no synchronisation).  256 on MI355X if the query fails.
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    return 256;
+  return n;
+}
+
 FfnWs plan_ffn(const Dims& d, Plan& pl) {
   FfnWs w;
-  w.fs = ffn_shape(d.rows_max, (int)d.E, (int)d.h, (int)d.f, (int)d.T, (int)d.k, d.bf16);
+  w.fs = ffn_shape(d.rows_max, (int)d.E, (int)d.h, (int)d.f, (int)d.T, (int)d.k, d.bf16,
+                   device_cus());
   w.map1 = pl.add((d.E + 1) * sizeof(int32_t));
   w.map2 = pl.add((d.E + 1) * sizeof(int32_t));
   w.A = pl.add((size_t)(d.rows_max > 0 ? d.rows_max : 1) * d.f * elem_bytes(d));
@@ -329,7 +342,7 @@ int32_t moe_route(const moe_config* cfg, const void* U, const void* W_r, const f
   if (st != MOE_OK) return st;
   if (prob_sum)
     return hip_status(launch_prob_reduce(at<double>(ws, w.part), w.rs.nblk, w.rs.EP, (int)d.E,
-                                         prob_sum, s));
+                                         nullptr, prob_sum, s));
   return MOE_OK;
 }
 
@@ -385,7 +398,7 @@ int32_t moe_stats(const moe_config* cfg, const int32_t* count, const int32_t* ke
   const int32_t st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (!count || !kept || !prob_sum) return MOE_ERR_INVALID_ARG;
-  StatsParams p{(int)cfg->T, (int)cfg->E, (int)cfg->k, count, kept, nullptr, 0, 0,
+  StatsParams p{(int)cfg->T, (int)cfg->E, (int)cfg->k, count, kept, nullptr,
                 prob_sum, f, P, aux_loss, maxvio, n_dropped};
   return hip_status(launch_stats(p, static_cast<hipStream_t>(stream)));
 }
@@ -443,11 +456,10 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
   MOE_TRY(mark(4));
   MOE_TRY(launch_combine(U, Y, slot, gate, out, (int)d.T, (int)d.h, (int)d.k, d.bf16, s));
   MOE_TRY(mark(5));
-  if (o.prob_sum)
-    MOE_TRY(launch_prob_reduce(at<double>(ws, w.route.part), w.route.rs.nblk, w.route.rs.EP,
-                               (int)d.E, o.prob_sum, s));
-  StatsParams sp{(int)d.T, (int)d.E, (int)d.k, count, kept, at<double>(ws, w.route.part),
-                 w.route.rs.nblk, w.route.rs.EP, nullptr, o.f, o.P,
+  MOE_TRY(launch_prob_reduce(at<double>(ws, w.route.part), w.route.rs.nblk, w.route.rs.EP,
+                             (int)d.E, at<double>(ws, w.route.total), o.prob_sum, s));
+  StatsParams sp{(int)d.T, (int)d.E, (int)d.k, count, kept, at<double>(ws, w.route.total),
+                 nullptr, o.f, o.P,
                  o.aux_loss ? o.aux_loss : at<float>(ws, w.scal),
                  o.maxvio ? o.maxvio : at<float>(ws, w.scal) + 1,
                  o.n_dropped ? o.n_dropped : at<int32_t>(ws, w.scal) + 2};

@@ -61,12 +61,7 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsParams p) {
   if (e < p.E) {
     cnt = p.count[e];
     drop = cnt - p.kept[e];
-    double ps = 0.0;
-    if (p.prob_part) {
-      for (int b = 0; b < p.nparts; ++b) ps += p.prob_part[(size_t)b * p.EP + e];
-    } else {
-      ps = (double)p.prob_sum[e];
-    }
+    const double ps = p.prob_total ? p.prob_total[e] : (double)p.prob_sum[e];
     const double f = p.T > 0 ? (double)cnt / ((double)p.T * p.k) : 0.0;
     const double P = p.T > 0 ? ps / p.T : 0.0;
     if (p.f) p.f[e] = (float)f;

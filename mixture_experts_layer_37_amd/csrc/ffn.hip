@@ -11,11 +11,26 @@
 // bf16 kernels (gfx950): C[M, N] = A[M, K] W[N, K]^T with both operands
 // K-contiguous, v_mfma_f32_32x32x16_bf16, float32 accumulation.  A workgroup
 // of 4 waves (2 x 2) owns a BM x 256 output tile; each wave a (BM/2) x 128
-// block, i.e. BM/64 x 4 MFMA tiles.  K advances 64 at a time through two LDS
-// buffers (global loads for step k+1 are in flight while step k is
-// multiplied; one barrier per step).  LDS rows are 128 bytes; the 16-byte
-// chunk index is XOR-ed with (row & 7) so the 32 rows read by one MFMA
-// fragment fall on different banks.
+// block, i.e. BM/64 x 4 MFMA tiles whose accumulators live in AGPRs.
+//
+// Operand pipeline: K advances in stages of 32 through 4 LDS buffers.  Tiles
+// are copied global -> LDS by buffer loads that write LDS directly (no
+// staging registers); a buffer resource per operand bounds the reads, so rows
+// past the end of X or of a weight matrix read as zero.  Inside stage s each
+// wave runs the MFMAs of its first 16-wide K slice while reading the
+// fragments of the second, then waits for stage s+1 to land, meets the other
+// waves at a barrier (after which the buffer of stage s is free), issues the
+// copy of stage s+4 into it, and runs the second slice while reading the
+// first fragments of stage s+1.  Loads thus have three stages (about 3000
+// MFMA cycles) to arrive and no barrier leaves the matrix pipe idle.  The
+// buffers are separate LDS arrays and the loop is unrolled by 4, so the
+// compiler can tell the copy in flight from the buffer being read.
+//
+// LDS rows are 64 bytes (4 chunks of 16).  gfx950 serves a 16-byte LDS read for
+// 16 lanes per clock from 64 four-byte banks; storing logical chunk c of row r
+// at chunk c ^ ((r >> 2) & 3) makes the 16 rows of one fragment read cover all
+// banks once.
+//
 // Gate/up tile: LDS B rows 0..127 are W_gate rows n0..n0+127 and rows
 // 128..255 the W_up rows with the same indices, so each lane holds the gate
 // and the up value of one output element and the epilogue writes
@@ -23,9 +38,12 @@
 // Tile order: tiles are numbered in groups of 8 n-tiles, m-tile major inside a
 // group, and the numbering is spread over the XCDs in contiguous ranges, so
 // workgroups running together on one XCD share A rows and B tiles in its L2.
-// Ragged rows: an m-tile never crosses an expert boundary; rows past the
-// expert's end read a clamped (valid) row and are not stored.
+// Ragged rows: an m-tile never crosses an expert boundary; a tile with fewer
+// valid rows skips the MFMAs of its empty 32-row blocks and stores only valid
+// rows.
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -34,10 +52,17 @@ namespace moe {
 
 namespace {
 
-constexpr int BN = 256, BK = 64, GN = 8;
+#ifndef MOE_FFN_WAVES
+#define MOE_FFN_WAVES 8  // waves per GEMM workgroup (4 or 8)
+#endif
+
+constexpr int BN = 256, BK = 32, NSTAGE = 4, GN = 8;
+// Third dword of a raw buffer resource on gfx9-family parts (32-bit data
+// format, no swizzle); loads outside num_records bytes return zero.
+constexpr int kBufFlags = 0x00020000;
 
 struct GemmParams {
-  const bf16* A;         // [rows][K]
+  const bf16* A;         // [rows_cap][K]
   const int32_t* offset; // [E+1]
   const int32_t* tmap;   // [E+1] first m-tile of each expert
   const bf16* W0;        // gate/up: W_gate [E][N][K]; down: W_down [E][N][K]
@@ -45,66 +70,102 @@ struct GemmParams {
   bf16* C;               // [rows][Nout]
   int E, K, N, Nout;     // N: rows of each weight matrix (f or h)
   int ntiles, mtmax;
+  int rows_cap;          // rows allocated in A
 };
 
-template <int BM, bool GATEUP>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
-  constexpr int RBLK = BM / 64;      // 32-row MFMA blocks per wave
-  constexpr int ACH = BM * 8 / 256;  // 16-byte A chunks per thread per K step
-  constexpr int BCH = BN * 8 / 256;  // 16-byte B chunks per thread per K step
-  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * BK];
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  const int n = bytes > 0x7fffffffull ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kBufFlags);
+}
 
-  // ---- which tile
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int g = L / (p.mtmax * GN);
-  const int rem = L - g * p.mtmax * GN;
-  const int gw = min(GN, p.ntiles - g * GN);
-  if (gw <= 0) return;
-  const int mt = rem / gw;
-  const int nt = g * GN + rem % gw;
-  if (mt >= p.mtmax || mt >= p.tmap[p.E]) return;
-  int lo = 0, hi = p.E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.tmap[mid] <= mt) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int row0 = p.offset[e] + (mt - p.tmap[e]) * BM;
-  const int rend = p.offset[e + 1];
-  const int nvalid = min(BM, rend - row0);
+// One wave-wide 16-byte-per-lane load straight into LDS: lane i's 16 bytes
+// land at lds + 16 * i.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
+}
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without the release fence of __syncthreads(): that fence
+// would wait for every load in flight, including the LDS copies of the next
+// stages.  Callers make their own data visible first (wait_vm); the memory
+// clobber keeps the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+struct Bufs {
+  bf16 *a0, *a1, *a2, *a3, *b0, *b1, *b2, *b3;
+};
+
+template <int BM, int NW, bool GATEUP, bool PARTIAL>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, int row0,
+                                          int nvalid, const Bufs& L) {
+  constexpr int WM = NW / 2;          // waves along M (2 along N)
+  constexpr int WR = BM / WM;         // rows per wave
+  constexpr int RBLK = WR / 32;       // 32-row MFMA blocks per wave
+  constexpr int AG = BM / (16 * NW);  // 16-row A groups copied per wave per stage
+  constexpr int BG = BN / (16 * NW);  // 16-row B groups copied per wave per stage
+  constexpr int ND = AG + BG;         // copies per wave per stage
+  static_assert(AG >= 1 && BG >= 1 && RBLK >= 1, "tile shape");
+  // the wave index is uniform: keep it (and all copy addressing) in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
+  const int K = p.K;
+  const int KT = K / BK;
 
-  // ---- global -> LDS addressing
-  const bf16* aptr[ACH];
-  int alds[ACH];
-#pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int q = tid + 256 * i, r = q >> 3, c = q & 7;
-    const int gr = min(row0 + r, rend - 1);
-    aptr[i] = p.A + (size_t)gr * p.K + c * 8;
-    alds[i] = r * BK + ((c ^ (r & 7)) * 8);
+  // ---- copy sources.  Lane i of 16-row group g fills LDS row 16g + i/4,
+  // physical chunk i%4, with logical chunk (i%4) ^ ((row >> 2) & 3), which for
+  // that row is (i%4) ^ (i/16).
+  const int lrow = lane >> 2, lchunk = (lane & 3) ^ (lane >> 4);
+  const __amdgpu_buffer_rsrc_t rA =
+      make_rsrc(p.A + (size_t)row0 * K, (size_t)(p.rows_cap - row0) * K * 2);
+  __amdgpu_buffer_rsrc_t rB0, rB1;
+  if (GATEUP) {
+    const size_t n0 = (size_t)nt * 128;
+    rB0 = make_rsrc(p.W0 + ((size_t)e * p.N + n0) * K, (size_t)(p.N - n0) * K * 2);
+    rB1 = make_rsrc(p.W1 + ((size_t)e * p.N + n0) * K, (size_t)(p.N - n0) * K * 2);
+  } else {
+    const size_t n0 = (size_t)nt * BN;
+    rB0 = make_rsrc(p.W0 + ((size_t)e * p.N + n0) * K, (size_t)(p.N - n0) * K * 2);
+    rB1 = rB0;
   }
-  const bf16* bptr[BCH];
-  int blds[BCH];
+  int voA[AG], voB[BG];
 #pragma unroll
-  for (int i = 0; i < BCH; ++i) {
-    const int q = tid + 256 * i, r = q >> 3, c = q & 7;
-    const bf16* W;
-    int wr;
-    if (GATEUP) {
-      W = (r < 128) ? p.W0 : p.W1;
-      wr = nt * 128 + (r & 127);
-    } else {
-      W = p.W0;
-      wr = nt * BN + r;
-    }
-    wr = min(wr, p.N - 1);
-    bptr[i] = W + (size_t)e * p.N * p.K + (size_t)wr * p.K + c * 8;
-    blds[i] = r * BK + ((c ^ (r & 7)) * 8);
+  for (int j = 0; j < AG; ++j) voA[j] = (((wave + NW * j) * 16 + lrow) * K + lchunk * 8) * 2;
+#pragma unroll
+  for (int j = 0; j < BG; ++j) {
+    // gate/up: groups 0..7 are W_gate rows, 8..15 (j >= BG/2) the W_up rows
+    const int g = wave + NW * j;
+    const int r = GATEUP ? (16 * (g & 7) + lrow) : (16 * g + lrow);
+    voB[j] = (r * K + lchunk * 8) * 2;
   }
+  auto issue = [&](bf16* as, bf16* bs, int stage) {
+    const int kb = min(stage, KT - 1) * BK * 2;  // past the end: reload the last stage
+#pragma unroll
+    for (int j = 0; j < AG; ++j) dma16(rA, as + (wave + NW * j) * 16 * BK, voA[j] + kb);
+#pragma unroll
+    for (int j = 0; j < BG; ++j)
+      dma16((GATEUP && j >= BG / 2) ? rB1 : rB0, bs + (wave + NW * j) * 16 * BK, voB[j] + kb);
+  };
+
+  // ---- fragments: lane reads row (lane % 32) of each 32-row block, chunk
+  // 2 * slice + lane / 32
+  const int l32 = lane & 31, khalf = lane >> 5;
+  const int sw = (l32 >> 2) & 3;  // (row >> 2) & 3 of every fragment row of this lane
+  int aoff[RBLK], boff[4];
+#pragma unroll
+  for (int i = 0; i < RBLK; ++i) aoff[i] = (wm * WR + i * 32 + l32) * BK;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = GATEUP ? ((j < 2 ? 0 : 128) + wn * 64 + (j & 1) * 32 + l32)
+                         : (wn * 128 + j * 32 + l32);
+    boff[j] = r * BK;
+  }
+  int rlim = RBLK;
+  if (PARTIAL) rlim = max(0, min(RBLK, (nvalid - wm * WR + 31) / 32));
 
   floatx16 acc[RBLK][4];
 #pragma unroll
@@ -114,70 +175,79 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  u32x4 ra[ACH], rb[BCH];
-  auto gload = [&](int k0) {
+  bf16x8 fa[2][RBLK], fb[2][4];
+  auto fetch = [&](const bf16* as, const bf16* bs, int slice, int st) {
+    const int c = ((2 * slice + khalf) ^ sw) * 8;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) ra[i] = ld16(aptr[i] + k0);
+    for (int i = 0; i < RBLK; ++i)
+      if (!PARTIAL || i < rlim) fa[st][i] = *reinterpret_cast<const bf16x8*>(as + aoff[i] + c);
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) rb[i] = ld16(bptr[i] + k0);
+    for (int j = 0; j < 4; ++j) fb[st][j] = *reinterpret_cast<const bf16x8*>(bs + boff[j] + c);
   };
-  auto swrite = [&](int buf) {
+  auto mfmas = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) st16(&As[buf][alds[i]], ra[i]);
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) st16(&Bs[buf][blds[i]], rb[i]);
-  };
-
-  // fragment rows in LDS: A rows of this wave, B rows of its 4 column blocks
-  const int l32 = lane & 31, khalf = lane >> 5;
-  int arow[RBLK], brow[4];
-#pragma unroll
-  for (int i = 0; i < RBLK; ++i) arow[i] = wm * (BM / 2) + i * 32 + l32;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (GATEUP)
-      brow[j] = (j < 2 ? 0 : 128) + wn * 64 + (j & 1) * 32 + l32;
-    else
-      brow[j] = wn * 128 + j * 32 + l32;
-  }
-
-  const int KT = p.K / BK;
-  gload(0);
-  swrite(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    const bf16* as = As[cur];
-    const bf16* bs = Bs[cur];
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = 2 * kk + khalf;
-      bf16x8 af[RBLK], bfr[4];
-#pragma unroll
-      for (int i = 0; i < RBLK; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(as + arow[i] * BK + ((c ^ (arow[i] & 7)) * 8));
+    for (int i = 0; i < RBLK; ++i) {
+      if (PARTIAL && i >= rlim) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(bs + brow[j] * BK + ((c ^ (brow[j] & 7)) * 8));
-#pragma unroll
-      for (int i = 0; i < RBLK; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st][i], fb[st][j], acc[i][j],
+                                                            0, 0, 0);
     }
-    if (kt + 1 < KT) swrite(cur ^ 1);
-    __syncthreads();
+  };
+  // order for the scheduler: MFMAs interleaved with the next fragment reads
+  // (groups: 0x008 MFMA, 0x100 LDS read, 0x020 global read incl. LDS copies)
+  auto order = [&](bool copies) {
+    if (PARTIAL) return;
+    constexpr int NM = RBLK * 4, NR = RBLK + 4;
+    if (copies) __builtin_amdgcn_sched_group_barrier(0x020, ND, 0);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  // One stage held in (as, bs); (nas, nbs) holds the next one.
+  auto stage = [&](int s, bf16* as, bf16* bs, const bf16* nas, const bf16* nbs) {
+    fetch(as, bs, 1, 1);
+    mfmas(0);
+    order(false);
+    wait_vm<2 * ND>();  // stage s+1 has landed (s+2 and s+3 may be in flight)
+    barrier_only();
+    issue(as, bs, s + NSTAGE);
+    fetch(nas, nbs, 0, 0);
+    mfmas(1);
+    order(true);
+  };
+
+  issue(L.a0, L.b0, 0);
+  issue(L.a1, L.b1, 1);
+  issue(L.a2, L.b2, 2);
+  issue(L.a3, L.b3, 3);
+  wait_vm<3 * ND>();
+  barrier_only();
+  fetch(L.a0, L.b0, 0, 0);
+  int s = 0;
+  for (; s + NSTAGE <= KT; s += NSTAGE) {
+    stage(s, L.a0, L.b0, L.a1, L.b1);
+    stage(s + 1, L.a1, L.b1, L.a2, L.b2);
+    stage(s + 2, L.a2, L.b2, L.a3, L.b3);
+    stage(s + 3, L.a3, L.b3, L.a0, L.b0);
   }
+  if (s < KT) {  // K % 128 == 64: two stages left
+    stage(s, L.a0, L.b0, L.a1, L.b1);
+    stage(s + 1, L.a1, L.b1, L.a2, L.b2);
+  }
+  wait_vm<0>();  // copies past the end are still in flight
 
   // ---- epilogue.  D layout: lane holds column (lane % 32) and rows
   // 8 * (v / 4) + 4 * (lane / 32) + (v % 4), v = 0..15.
 #pragma unroll
   for (int i = 0; i < RBLK; ++i) {
+    if (PARTIAL && i >= rlim) continue;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int r = wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
-      if (r >= nvalid) continue;
+      const int r = wm * WR + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
+      if (PARTIAL && r >= nvalid) continue;
       bf16* crow = p.C + (size_t)(row0 + r) * p.Nout;
       if (GATEUP) {
 #pragma unroll
@@ -195,6 +265,49 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
         }
       }
     }
+  }
+}
+
+// Persistent grouped GEMM.  The grid holds a fixed number of workgroups (a
+// multiple of 8, about one per CU); the real number of tiles is only known on
+// the device (tmap[E] m-tiles x ntiles n-tiles).  Tiles are numbered in
+// groups of GN n-tiles, m-tile major inside a group, and split into 8
+// contiguous slices, one per XCD (workgroup i runs on XCD i % 8): each XCD gets
+// the same share of real tiles, and the workgroups running together on one
+// XCD hold neighbouring tiles, which share A row panels and weight panels in
+// that XCD's L2.
+template <int BM, int NW, bool GATEUP>
+__global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) bf16 A0[BM * BK], A1[BM * BK], A2[BM * BK],
+      A3[BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16 B0[BN * BK], B1[BN * BK], B2[BN * BK],
+      B3[BN * BK];
+  const Bufs L{A0, A1, A2, A3, B0, B1, B2, B3};
+
+  const int mtiles = p.tmap[p.E];
+  const int total = mtiles * p.ntiles;
+  const int xcd = blockIdx.x & 7, nloc = gridDim.x >> 3;
+  const int per = (total + 7) >> 3;
+  const int t_end = min(total, (xcd + 1) * per);
+  for (int t = xcd * per + (blockIdx.x >> 3); t < t_end; t += nloc) {
+    const int g = t / (mtiles * GN);
+    const int rem = t - g * mtiles * GN;
+    const int gw = min(GN, p.ntiles - g * GN);
+    const int mt = rem / gw;
+    const int nt = g * GN + rem % gw;
+    int lo = 0, hi = p.E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.tmap[mid] <= mt) lo = mid; else hi = mid;
+    }
+    const int e = lo;
+    const int row0 = p.offset[e] + (mt - p.tmap[e]) * BM;
+    const int nvalid = min(BM, p.offset[e + 1] - row0);
+    __syncthreads();  // every wave is done with the previous tile's LDS
+    if (nvalid == BM)
+      gemm_tile<BM, NW, GATEUP, false>(p, e, nt, row0, nvalid, L);
+    else
+      gemm_tile<BM, NW, GATEUP, true>(p, e, nt, row0, nvalid, L);
   }
 }
 
@@ -246,25 +359,43 @@ __global__ void tile_map_kernel(const int32_t* offset, int E, int bm1, int bm2, 
 
 int round8(int x) { return (x + 7) & ~7; }
 
+template <bool GATEUP>
+void launch_gemm(int bm, int nw, int grid, const GemmParams& p, hipStream_t s) {
+  if (bm == 256 && nw == 8)
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 8, GATEUP>), dim3(grid), dim3(512), 0, s, p);
+  else if (bm == 256)
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 4, GATEUP>), dim3(grid), dim3(256), 0, s, p);
+  else if (nw == 8)
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 8, GATEUP>), dim3(grid), dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 4, GATEUP>), dim3(grid), dim3(256), 0, s, p);
+}
+
 }  // namespace
 
-FfnShape ffn_shape(int64_t rows_max, int E, int h, int f, int T, int k, int bf16_) {
+FfnShape ffn_shape(int64_t rows_max, int E, int h, int f, int T, int k, int bf16_, int ncu) {
   FfnShape fs{};
   if (!bf16_) {
     fs.bm1 = fs.bm2 = 1;
     return fs;
   }
-  // Experts with few rows (many experts, small top-k) use 128-row tiles so
-  // less of each tile is padding.
+  // 256-row tiles unless the average expert has at most 96 rows.  With 8
+  // waves (4 along M x 2 along N) waves w and w + 4 share a SIMD, so the first
+  // two wave rows already cover all four SIMDs: a tile of an expert with
+  // 100-200 rows wastes little, and each expert's weights are streamed once
+  // per n-tile instead of once per 128-row tile.
   const double avg = E > 0 ? (double)T * k / E : 0.0;
-  fs.bm1 = avg <= 160.0 ? 128 : 256;
-  fs.bm2 = fs.bm1;
+  fs.bm1 = fs.bm2 = avg <= 96.0 ? 128 : 256;
+  fs.nw1 = fs.nw2 = MOE_FFN_WAVES;
   fs.mt1 = (int)((rows_max + (int64_t)E * (fs.bm1 - 1)) / fs.bm1);
   fs.mt2 = (int)((rows_max + (int64_t)E * (fs.bm2 - 1)) / fs.bm2);
   fs.nt1 = (f + 127) / 128;
   fs.nt2 = (h + BN - 1) / BN;
-  fs.grid1 = round8(fs.mt1 * fs.nt1);
-  fs.grid2 = round8(fs.mt2 * fs.nt2);
+  fs.rows_cap = (int)rows_max;
+  // persistent grid: one workgroup per CU (the LDS pipeline takes most of a
+  // CU), never more than the static bound on tiles, a multiple of 8
+  fs.grid1 = round8(std::min<int64_t>((int64_t)fs.mt1 * fs.nt1, ncu));
+  fs.grid2 = round8(std::min<int64_t>((int64_t)fs.mt2 * fs.nt2, ncu));
   return fs;
 }
 
@@ -284,11 +415,8 @@ hipError_t launch_gate_up(const FfnShape& fs, const void* X, const int32_t* offs
   if (fs.grid1 == 0) return hipSuccess;
   GemmParams p{static_cast<const bf16*>(X), offset, map1, static_cast<const bf16*>(Wg),
                static_cast<const bf16*>(Wu), static_cast<bf16*>(A), E, h, f, f,
-               fs.nt1, fs.mt1};
-  if (fs.bm1 == 256)
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, true>), dim3(fs.grid1), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, true>), dim3(fs.grid1), dim3(256), 0, s, p);
+               fs.nt1, fs.mt1, fs.rows_cap};
+  launch_gemm<true>(fs.bm1, fs.nw1, fs.grid1, p, s);
   return hipGetLastError();
 }
 
@@ -298,11 +426,8 @@ hipError_t launch_down(const FfnShape& fs, const void* A, const int32_t* offset,
   if (!bf16_) return hipErrorNotSupported;
   if (fs.grid2 == 0) return hipSuccess;
   GemmParams p{static_cast<const bf16*>(A), offset, map2, static_cast<const bf16*>(Wd), nullptr,
-               static_cast<bf16*>(Y), E, f, h, h, fs.nt2, fs.mt2};
-  if (fs.bm2 == 256)
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, false>), dim3(fs.grid2), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, false>), dim3(fs.grid2), dim3(256), 0, s, p);
+               static_cast<bf16*>(Y), E, f, h, h, fs.nt2, fs.mt2, fs.rows_cap};
+  launch_gemm<false>(fs.bm2, fs.nw2, fs.grid2, p, s);
   return hipGetLastError();
 }
 

@@ -36,8 +36,10 @@ hipError_t launch_transpose_router_w(const void* W, void* WT, int h, int E, int 
                                      hipStream_t s);
 hipError_t launch_route(const RouteShape& rs, const RouteParams& p, int bf16, int noisy,
                         hipStream_t s);
-hipError_t launch_prob_reduce(const double* part, int nblk, int EP, int E, float* prob_sum,
-                              hipStream_t s);
+// total[e] (double, optional) and prob_sum[e] (float, optional): sums over
+// the router's per-workgroup partials.
+hipError_t launch_prob_reduce(const double* part, int nblk, int EP, int E, double* total,
+                              float* prob_sum, hipStream_t s);
 
 // ---------------------------------------------------------------- dispatch
 constexpr int kChunk = 256;  // tokens per dispatch workgroup
@@ -61,11 +63,14 @@ hipError_t launch_permute(const void* U, const int32_t* slot, void* X, int T, in
 // ---------------------------------------------------------------- experts
 struct FfnShape {
   int bm1, bm2;     // row tile of the gate/up and the down GEMMs
+  int nw1, nw2;     // waves per workgroup of each GEMM
   int mt1, mt2;     // static bound on m-tiles of each GEMM
   int nt1, nt2;     // n-tiles of each GEMM
-  int grid1, grid2; // workgroups launched (multiple of 8)
+  int grid1, grid2; // persistent workgroups launched (multiple of 8)
+  int rows_cap;     // rows allocated in X and in the SwiGLU intermediate
 };
-FfnShape ffn_shape(int64_t rows_max, int E, int h, int f, int T, int k, int bf16);
+// ncu: compute units of the device (the persistent grid size)
+FfnShape ffn_shape(int64_t rows_max, int E, int h, int f, int T, int k, int bf16, int ncu);
 hipError_t launch_tile_map(const int32_t* offset, int E, int bm1, int bm2, int32_t* map1,
                            int32_t* map2, hipStream_t s);
 hipError_t launch_gate_up(const FfnShape& fs, const void* X, const int32_t* offset,
@@ -83,9 +88,8 @@ struct StatsParams {
   int T, E, k;
   const int32_t* count;
   const int32_t* kept;
-  const double* prob_part;  // [nparts][EP] (layer) or NULL
-  int nparts, EP;
-  const float* prob_sum;    // [E] (standalone) or NULL
+  const double* prob_total;  // [E] (layer) or NULL
+  const float* prob_sum;     // [E] (standalone) or NULL
   float* f;
   float* P;
   float* aux;

@@ -264,11 +264,23 @@ __global__ void transpose_kernel(const bf16* W, bf16* WT, int h, int E, int EP) 
   }
 }
 
-__global__ void prob_reduce_kernel(const double* part, int nblk, int EP, int E, float* out) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    double s = 0.0;
-    for (int b = 0; b < nblk; ++b) s += part[(size_t)b * EP + e];
-    out[e] = (float)s;
+// One workgroup per expert: thread j adds partials j, j + 256, ... in order,
+// then a fixed-shape tree adds the 256 sums (deterministic).
+__global__ __launch_bounds__(256) void prob_reduce_kernel(const double* part, int nblk, int EP,
+                                                          double* total, float* out) {
+  __shared__ double sh[256];
+  const int e = blockIdx.x;
+  double s = 0.0;
+  for (int b = threadIdx.x; b < nblk; b += 256) s += part[(size_t)b * EP + e];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    if (total) total[e] = sh[0];
+    if (out) out[e] = (float)sh[0];
   }
 }
 
@@ -336,9 +348,9 @@ hipError_t launch_route(const RouteShape& rs, const RouteParams& p, int bf16, in
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prob_reduce(const double* part, int nblk, int EP, int E, float* prob_sum,
-                              hipStream_t s) {
-  hipLaunchKernelGGL(prob_reduce_kernel, dim3(1), dim3(256), 0, s, part, nblk, EP, E,
+hipError_t launch_prob_reduce(const double* part, int nblk, int EP, int E, double* total,
+                              float* prob_sum, hipStream_t s) {
+  hipLaunchKernelGGL(prob_reduce_kernel, dim3(E), dim3(256), 0, s, part, nblk, EP, total,
                      prob_sum);
   return hipGetLastError();
 }
