@@ -37,7 +37,52 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes three times (for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_mixtral_bf16.txt")
+GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_37_amd", "csrc", "ffn.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the gate/up GEMM from the committed counter summary.
+
+    The summary records the sha256 of the GEMM source it was measured on; when
+    the source has changed since, the figure no longer applies and None is
+    returned.
+    """
+    import hashlib
+    if workload != "mixtral_bf16" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    with open(GEMM_SOURCE, "rb") as fh:
+        sha = hashlib.sha256(fh.read()).hexdigest()
+    if kv.get("gemm_source_sha256") != sha:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes: int):
+    import torch
+    x = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
 
 
 def cpu_baseline(w, x, g, budget_s: float) -> dict:
@@ -79,7 +124,7 @@ def cpu_baseline(w, x, g, budget_s: float) -> dict:
         t2 = time.perf_counter()
         a, b = int(r["offset"][e]), int(r["offset"][e + 1])
         # cap the rows of one expert so a single expert stays inside the budget
-        n = min(b - a, 256)
+        n = min(b - a, 1024)
         Y[a:a + n] = O.swiglu_expert(U[r["row_token"][a:a + n]], Wg, Wu, Wd)
         t3 = time.perf_counter()
         t_conv += t2 - t1
@@ -102,6 +147,9 @@ def cpu_baseline(w, x, g, budget_s: float) -> dict:
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -186,7 +234,7 @@ def main():
                    "noisy": w.noisy, "seed": args.seed},
         "roofline": {"kernel": "grouped gate/up GEMM + SwiGLU", "bound": "mfma",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None},
+                     "frac": achieved / peak, "traffic": measured_traffic(w.name)},
         "layer": {"mfma_frac_nominal": f_nom / (ms * 1e-3) / 1e12 / peak,
                   "mfma_frac_exec": f_exec / (ms * 1e-3) / 1e12 / peak,
                   "hbm_frac_alg": b_alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
