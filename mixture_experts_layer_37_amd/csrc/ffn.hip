@@ -10,26 +10,28 @@
 //
 // bf16 kernels (gfx950): C[M, N] = A[M, K] W[N, K]^T with both operands
 // K-contiguous, v_mfma_f32_32x32x16_bf16, float32 accumulation.  A workgroup
-// of 4 waves (2 x 2) owns a BM x 256 output tile; each wave a (BM/2) x 128
-// block, i.e. BM/64 x 4 MFMA tiles whose accumulators live in AGPRs.
+// of NW waves (NW/2 along M x 2 along N) owns a BM x 256 output tile; each
+// wave a (2 BM / NW) x 128 block of 32 x 32 MFMA tiles.
 //
-// Operand pipeline: K advances in stages of 32 through 4 LDS buffers.  Tiles
-// are copied global -> LDS by buffer loads that write LDS directly (no
-// staging registers); a buffer resource per operand bounds the reads, so rows
-// past the end of X or of a weight matrix read as zero.  Inside stage s each
-// wave runs the MFMAs of its first 16-wide K slice while reading the
-// fragments of the second, then waits for stage s+1 to land, meets the other
-// waves at a barrier (after which the buffer of stage s is free), issues the
-// copy of stage s+4 into it, and runs the second slice while reading the
-// first fragments of stage s+1.  Loads thus have three stages (about 3000
-// MFMA cycles) to arrive and no barrier leaves the matrix pipe idle.  The
-// buffers are separate LDS arrays and the loop is unrolled by 4, so the
-// compiler can tell the copy in flight from the buffer being read.
+// Operand pipeline.  K advances in steps of 64: a step's A tile (BM rows) and
+// B tile (256 rows) are 128 bytes per row, so every LDS-direct copy
+// instruction (16 bytes per lane) moves eight whole 128-byte lines; on this
+// part such copies sustain about twice the per-CU rate of 64-byte row pieces,
+// and the copy rate, not the matrix pipe, is what bounds a 256 x 256 tile.
+// LDS holds a ring of three A slots and two B slots (160 KB at BM = 256).
+// Step j reads A_j and B_j; between its third and fourth K slice every wave
+// waits for its copies of A_{j+1} and B_{j+1}, meets the others at one
+// barrier, and then reuses the slots of step j for B_{j+2} and A_{j+3}.
+// Copies of A thus have two steps and copies of B one step to land, with about
+// 96 KB in flight per CU.  Inside a step, each wave runs the MFMAs of one K
+// slice while reading the fragments of the next from LDS.  The slots are
+// separate LDS arrays and the loop is unrolled over the ring's period (6), so
+// the compiler can tell the copies in flight from the slots being read.
 //
-// LDS rows are 64 bytes (4 chunks of 16).  gfx950 serves a 16-byte LDS read for
-// 16 lanes per clock from 64 four-byte banks; storing logical chunk c of row r
-// at chunk c ^ ((r >> 2) & 3) makes the 16 rows of one fragment read cover all
-// banks once.
+// LDS rows are 128 bytes (8 chunks of 16).  gfx950 serves a 16-byte LDS read
+// for 16 lanes per clock from 64 four-byte banks; storing logical chunk c of
+// row r at chunk c ^ ((r >> 1) & 7) makes the 16 rows of one fragment read
+// cover all banks once.
 //
 // Gate/up tile: LDS B rows 0..127 are W_gate rows n0..n0+127 and rows
 // 128..255 the W_up rows with the same indices, so each lane holds the gate
@@ -56,7 +58,8 @@ namespace {
 #define MOE_FFN_WAVES 8  // waves per GEMM workgroup (4 or 8)
 #endif
 
-constexpr int BN = 256, BK = 32, NSTAGE = 4, GN = 8;
+constexpr int BN = 256, BK = 64, GN = 8;
+constexpr int kPeriod = 6;  // steps after which the 3 A slots and 2 B slots line up again
 // Third dword of a raw buffer resource on gfx9-family parts (32-bit data
 // format, no swizzle); loads outside num_records bytes return zero.
 constexpr int kBufFlags = 0x00020000;
@@ -79,9 +82,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, si
 }
 
 // One wave-wide 16-byte-per-lane load straight into LDS: lane i's 16 bytes
-// land at lds + 16 * i.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
+// land at lds + 16 * i.  voff: per-lane byte offset, soff: uniform byte offset.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
 }
 
 template <int N>
@@ -95,20 +98,19 @@ __device__ __forceinline__ void wait_vm() {
 // clobber keeps the compiler from moving LDS accesses across the barrier.
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
-struct Bufs {
-  bf16 *a0, *a1, *a2, *a3, *b0, *b1, *b2, *b3;
+struct Ring {
+  bf16 *a0, *a1, *a2, *b0, *b1;
 };
 
 template <int BM, int NW, bool GATEUP, bool PARTIAL>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, int row0,
-                                          int nvalid, const Bufs& L) {
-  constexpr int WM = NW / 2;          // waves along M (2 along N)
-  constexpr int WR = BM / WM;         // rows per wave
-  constexpr int RBLK = WR / 32;       // 32-row MFMA blocks per wave
-  constexpr int AG = BM / (16 * NW);  // 16-row A groups copied per wave per stage
-  constexpr int BG = BN / (16 * NW);  // 16-row B groups copied per wave per stage
-  constexpr int ND = AG + BG;         // copies per wave per stage
-  static_assert(AG >= 1 && BG >= 1 && RBLK >= 1, "tile shape");
+                                          int nvalid, const Ring& L) {
+  constexpr int WM = NW / 2;         // waves along M (2 along N)
+  constexpr int WR = BM / WM;        // rows per wave
+  constexpr int RBLK = WR / 32;      // 32-row MFMA blocks per wave
+  constexpr int AG = BM / (8 * NW);  // 8-row A groups copied per wave per step
+  constexpr int BG = BN / (8 * NW);  // 8-row B groups copied per wave per step
+  static_assert(AG >= 1 && BG >= 2 && RBLK >= 1, "tile shape");
   // the wave index is uniform: keep it (and all copy addressing) in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -116,10 +118,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
   const int K = p.K;
   const int KT = K / BK;
 
-  // ---- copy sources.  Lane i of 16-row group g fills LDS row 16g + i/4,
-  // physical chunk i%4, with logical chunk (i%4) ^ ((row >> 2) & 3), which for
-  // that row is (i%4) ^ (i/16).
-  const int lrow = lane >> 2, lchunk = (lane & 3) ^ (lane >> 4);
+  // ---- copy sources.  Lane i of 8-row group g fills LDS row 8g + i/8,
+  // physical chunk i%8, with logical chunk (i%8) ^ ((row >> 1) & 7).
+  const int lrow = lane >> 3;
   const __amdgpu_buffer_rsrc_t rA =
       make_rsrc(p.A + (size_t)row0 * K, (size_t)(p.rows_cap - row0) * K * 2);
   __amdgpu_buffer_rsrc_t rB0, rB1;
@@ -134,27 +135,35 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
   }
   int voA[AG], voB[BG];
 #pragma unroll
-  for (int j = 0; j < AG; ++j) voA[j] = (((wave + NW * j) * 16 + lrow) * K + lchunk * 8) * 2;
+  for (int j = 0; j < AG; ++j) {
+    const int r = 8 * (wave + NW * j) + lrow;
+    voA[j] = (r * K + (((lane & 7) ^ ((r >> 1) & 7)) * 8)) * 2;
+  }
 #pragma unroll
   for (int j = 0; j < BG; ++j) {
-    // gate/up: groups 0..7 are W_gate rows, 8..15 (j >= BG/2) the W_up rows
+    // gate/up: groups 0..15 are W_gate rows, 16..31 (j >= BG/2) the W_up rows
     const int g = wave + NW * j;
-    const int r = GATEUP ? (16 * (g & 7) + lrow) : (16 * g + lrow);
-    voB[j] = (r * K + lchunk * 8) * 2;
+    const int r = 8 * g + lrow;                          // LDS row
+    const int pr = GATEUP ? 8 * (g & 15) + lrow : r;     // row in the weight panel
+    voB[j] = (pr * K + (((lane & 7) ^ ((r >> 1) & 7)) * 8)) * 2;
   }
-  auto issue = [&](bf16* as, bf16* bs, int stage) {
-    const int kb = min(stage, KT - 1) * BK * 2;  // past the end: reload the last stage
+  // step j past the end reloads the last step (in bounds, never read)
+  auto issueA = [&](bf16* as, int j) {
+    const int kb = min(j, KT - 1) * BK * 2;
 #pragma unroll
-    for (int j = 0; j < AG; ++j) dma16(rA, as + (wave + NW * j) * 16 * BK, voA[j] + kb);
+    for (int q = 0; q < AG; ++q) dma16(rA, as + (wave + NW * q) * 8 * BK, voA[q], kb);
+  };
+  auto issueB = [&](bf16* bs, int j) {
+    const int kb = min(j, KT - 1) * BK * 2;
 #pragma unroll
-    for (int j = 0; j < BG; ++j)
-      dma16((GATEUP && j >= BG / 2) ? rB1 : rB0, bs + (wave + NW * j) * 16 * BK, voB[j] + kb);
+    for (int q = 0; q < BG; ++q)
+      dma16((GATEUP && q >= BG / 2) ? rB1 : rB0, bs + (wave + NW * q) * 8 * BK, voB[q], kb);
   };
 
-  // ---- fragments: lane reads row (lane % 32) of each 32-row block, chunk
-  // 2 * slice + lane / 32
+  // ---- fragments: lane reads row (lane % 32) of each 32-row block, logical
+  // chunk 2 * slice + lane / 32 of the step's 8
   const int l32 = lane & 31, khalf = lane >> 5;
-  const int sw = (l32 >> 2) & 3;  // (row >> 2) & 3 of every fragment row of this lane
+  const int sw = (l32 >> 1) & 7;  // (row >> 1) & 7 of every fragment row of this lane
   int aoff[RBLK], boff[4];
 #pragma unroll
   for (int i = 0; i < RBLK; ++i) aoff[i] = (wm * WR + i * 32 + l32) * BK;
@@ -195,48 +204,73 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
     }
   };
   // order for the scheduler: MFMAs interleaved with the next fragment reads
-  // (groups: 0x008 MFMA, 0x100 LDS read, 0x020 global read incl. LDS copies)
-  auto order = [&](bool copies) {
+  // and, after the barrier, with the copies (groups: 0x008 MFMA, 0x100 LDS
+  // read, 0x020 global read incl. LDS copies)
+  constexpr int NM = RBLK * 4, NR = RBLK + 4, NC = AG + BG;
+  constexpr int CPM = (NC + NM - 1) / NM;  // copies placed after each MFMA
+  auto order = [&]() {
     if (PARTIAL) return;
-    constexpr int NM = RBLK * 4, NR = RBLK + 4;
-    if (copies) __builtin_amdgcn_sched_group_barrier(0x020, ND, 0);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (m < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
-  // One stage held in (as, bs); (nas, nbs) holds the next one.
-  auto stage = [&](int s, bf16* as, bf16* bs, const bf16* nas, const bf16* nbs) {
+  auto order_copies = [&]() {
+    if (PARTIAL) return;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m * CPM < NC) __builtin_amdgcn_sched_group_barrier(0x020, CPM, 0);
+      if (m < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  // Step j on slots (as, bs); (nas, nbs) hold step j + 1.  On entry fa/fb[0]
+  // hold slice 0 of step j.
+  auto step = [&](int j, bf16* as, bf16* bs, const bf16* nas, const bf16* nbs) {
     fetch(as, bs, 1, 1);
     mfmas(0);
-    order(false);
-    wait_vm<2 * ND>();  // stage s+1 has landed (s+2 and s+3 may be in flight)
+    order();
+    fetch(as, bs, 2, 0);
+    mfmas(1);
+    order();
+    fetch(as, bs, 3, 1);
+    mfmas(0);
+    order();
+    // A_{j+1} and B_{j+1} have landed; only A_{j+2} may still be in flight
+    wait_vm<AG>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave is done reading (as, bs)
     barrier_only();
-    issue(as, bs, s + NSTAGE);
+    issueB(bs, j + 2);
+    issueA(as, j + 3);
     fetch(nas, nbs, 0, 0);
     mfmas(1);
-    order(true);
+    order_copies();
   };
 
-  issue(L.a0, L.b0, 0);
-  issue(L.a1, L.b1, 1);
-  issue(L.a2, L.b2, 2);
-  issue(L.a3, L.b3, 3);
-  wait_vm<3 * ND>();
+  issueA(L.a0, 0);
+  issueB(L.b0, 0);
+  issueA(L.a1, 1);
+  issueB(L.b1, 1);
+  issueA(L.a2, 2);
+  wait_vm<2 * AG + BG>();  // A_0 and B_0 have landed
   barrier_only();
   fetch(L.a0, L.b0, 0, 0);
-  int s = 0;
-  for (; s + NSTAGE <= KT; s += NSTAGE) {
-    stage(s, L.a0, L.b0, L.a1, L.b1);
-    stage(s + 1, L.a1, L.b1, L.a2, L.b2);
-    stage(s + 2, L.a2, L.b2, L.a3, L.b3);
-    stage(s + 3, L.a3, L.b3, L.a0, L.b0);
+  int j = 0;
+  for (; j + kPeriod <= KT; j += kPeriod) {
+    step(j, L.a0, L.b0, L.a1, L.b1);
+    step(j + 1, L.a1, L.b1, L.a2, L.b0);
+    step(j + 2, L.a2, L.b0, L.a0, L.b1);
+    step(j + 3, L.a0, L.b1, L.a1, L.b0);
+    step(j + 4, L.a1, L.b0, L.a2, L.b1);
+    step(j + 5, L.a2, L.b1, L.a0, L.b0);
   }
-  if (s < KT) {  // K % 128 == 64: two stages left
-    stage(s, L.a0, L.b0, L.a1, L.b1);
-    stage(s + 1, L.a1, L.b1, L.a2, L.b2);
-  }
+  const int rest = KT - j;  // 0..5 steps, starting again at slot phase 0
+  if (rest > 0) step(j, L.a0, L.b0, L.a1, L.b1);
+  if (rest > 1) step(j + 1, L.a1, L.b1, L.a2, L.b0);
+  if (rest > 2) step(j + 2, L.a2, L.b0, L.a0, L.b1);
+  if (rest > 3) step(j + 3, L.a0, L.b1, L.a1, L.b0);
+  if (rest > 4) step(j + 4, L.a1, L.b0, L.a2, L.b1);
   wait_vm<0>();  // copies past the end are still in flight
 
   // ---- epilogue.  D layout: lane holds column (lane % 32) and rows
@@ -278,11 +312,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
 // that XCD's L2.
 template <int BM, int NW, bool GATEUP>
 __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) bf16 A0[BM * BK], A1[BM * BK], A2[BM * BK],
-      A3[BM * BK];
-  __shared__ __attribute__((aligned(1024))) bf16 B0[BN * BK], B1[BN * BK], B2[BN * BK],
-      B3[BN * BK];
-  const Bufs L{A0, A1, A2, A3, B0, B1, B2, B3};
+  __shared__ __attribute__((aligned(1024))) bf16 A0[BM * BK], A1[BM * BK], A2[BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16 B0[BN * BK], B1[BN * BK];
+  const Ring L{A0, A1, A2, B0, B1};
 
   const int mtiles = p.tmap[p.E];
   const int total = mtiles * p.ntiles;
