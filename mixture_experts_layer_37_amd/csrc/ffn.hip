@@ -40,9 +40,11 @@
 // Tile order: tiles are numbered in groups of 8 n-tiles, m-tile major inside a
 // group, and the numbering is spread over the XCDs in contiguous ranges, so
 // workgroups running together on one XCD share A rows and B tiles in its L2.
-// Ragged rows: an m-tile never crosses an expert boundary; a tile with fewer
-// valid rows skips the MFMAs of its empty 32-row blocks and stores only valid
-// rows.
+// Ragged rows: an m-tile never crosses an expert boundary and only stores its
+// valid rows.  Its A buffer resource ends at its last valid row, so copies of
+// the rows past it read zero without memory traffic.  A tile at most half full
+// also skips the MFMAs of its empty 32-row blocks; a fuller one runs the
+// fully scheduled loop, which is faster than the branchy partial one.
 #include <math.h>
 
 #include <algorithm>
@@ -65,7 +67,7 @@ constexpr int kPeriod = 6;  // steps after which the 3 A slots and 2 B slots lin
 constexpr int kBufFlags = 0x00020000;
 
 struct GemmParams {
-  const bf16* A;         // [rows_cap][K]
+  const bf16* A;         // [rows][K], experts' row blocks back to back
   const int32_t* offset; // [E+1]
   const int32_t* tmap;   // [E+1] first m-tile of each expert
   const bf16* W0;        // gate/up: W_gate [E][N][K]; down: W_down [E][N][K]
@@ -73,7 +75,6 @@ struct GemmParams {
   bf16* C;               // [rows][Nout]
   int E, K, N, Nout;     // N: rows of each weight matrix (f or h)
   int ntiles, mtmax;
-  int rows_cap;          // rows allocated in A
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
@@ -121,8 +122,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
   // ---- copy sources.  Lane i of 8-row group g fills LDS row 8g + i/8,
   // physical chunk i%8, with logical chunk (i%8) ^ ((row >> 1) & 7).
   const int lrow = lane >> 3;
-  const __amdgpu_buffer_rsrc_t rA =
-      make_rsrc(p.A + (size_t)row0 * K, (size_t)(p.rows_cap - row0) * K * 2);
+  // A: only this tile's valid rows; copies of rows past them read zero
+  // without touching memory (their outputs are never stored)
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + (size_t)row0 * K, (size_t)nvalid * K * 2);
   __amdgpu_buffer_rsrc_t rB0, rB1;
   if (GATEUP) {
     const size_t n0 = (size_t)nt * 128;
@@ -281,7 +283,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = wm * WR + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
-      if (PARTIAL && r >= nvalid) continue;
+      if (r >= nvalid) continue;
       bf16* crow = p.C + (size_t)(row0 + r) * p.Nout;
       if (GATEUP) {
 #pragma unroll
@@ -336,7 +338,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(GemmParams p) {
     const int row0 = p.offset[e] + (mt - p.tmap[e]) * BM;
     const int nvalid = min(BM, p.offset[e + 1] - row0);
     __syncthreads();  // every wave is done with the previous tile's LDS
-    if (nvalid == BM)
+    // tiles more than half full run the fully scheduled loop (rows past
+    // nvalid read zero and are not stored); emptier ones skip the MFMAs of
+    // their empty 32-row blocks
+    if (2 * nvalid > BM)
       gemm_tile<BM, NW, GATEUP, false>(p, e, nt, row0, nvalid, L);
     else
       gemm_tile<BM, NW, GATEUP, true>(p, e, nt, row0, nvalid, L);
@@ -447,7 +452,7 @@ hipError_t launch_gate_up(const FfnShape& fs, const void* X, const int32_t* offs
   if (fs.grid1 == 0) return hipSuccess;
   GemmParams p{static_cast<const bf16*>(X), offset, map1, static_cast<const bf16*>(Wg),
                static_cast<const bf16*>(Wu), static_cast<bf16*>(A), E, h, f, f,
-               fs.nt1, fs.mt1, fs.rows_cap};
+               fs.nt1, fs.mt1};
   launch_gemm<true>(fs.bm1, fs.nw1, fs.grid1, p, s);
   return hipGetLastError();
 }
@@ -458,7 +463,7 @@ hipError_t launch_down(const FfnShape& fs, const void* A, const int32_t* offset,
   if (!bf16_) return hipErrorNotSupported;
   if (fs.grid2 == 0) return hipSuccess;
   GemmParams p{static_cast<const bf16*>(A), offset, map2, static_cast<const bf16*>(Wd), nullptr,
-               static_cast<bf16*>(Y), E, f, h, h, fs.nt2, fs.mt2, fs.rows_cap};
+               static_cast<bf16*>(Y), E, f, h, h, fs.nt2, fs.mt2};
   launch_gemm<false>(fs.bm2, fs.nw2, fs.grid2, p, s);
   return hipGetLastError();
 }
