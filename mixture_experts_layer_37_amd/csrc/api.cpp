@@ -130,7 +130,7 @@ DispatchWs plan_dispatch(const Dims& d, Plan& pl) {
 }
 
 struct FfnWs {
-  size_t map1, map2, A;
+  size_t map1, map2, A, part;
   FfnShape fs;
 };
 // Compute units of the current device (sizes the persistent GEMM grid; a
@@ -151,6 +151,7 @@ FfnWs plan_ffn(const Dims& d, Plan& pl) {
   w.map1 = pl.add((d.E + 1) * sizeof(int32_t));
   w.map2 = pl.add((d.E + 1) * sizeof(int32_t));
   w.A = pl.add((size_t)(d.rows_max > 0 ? d.rows_max : 1) * d.f * elem_bytes(d));
+  w.part = pl.add((size_t)w.fs.part_slots * kPartSlotBytes);
   return w;
 }
 
@@ -265,15 +266,15 @@ int32_t run_gate_up(const Dims& d, const FfnWs& w, const void* X, const int32_t*
     return hip_status(launch_ffn_f32(X, offset, Wg, Wu, Wd, at<void>(ws, w.A), Y, d.rows_max,
                                      (int)d.E, (int)d.h, (int)d.f, s));
   MOE_TRY(launch_gate_up(w.fs, X, offset, at<int32_t>(ws, w.map1), Wg, Wu, at<void>(ws, w.A),
-                         (int)d.E, (int)d.h, (int)d.f, 1, s));
+                         at<float>(ws, w.part), (int)d.E, (int)d.h, (int)d.f, 1, s));
   return MOE_OK;
 }
 
 int32_t run_down(const Dims& d, const FfnWs& w, const int32_t* offset, const void* Wd, void* Y,
                  void* ws, hipStream_t s) {
   if (!d.bf16) return MOE_OK;  // the float32 path ran both products already
-  MOE_TRY(launch_down(w.fs, at<void>(ws, w.A), offset, at<int32_t>(ws, w.map2), Wd, Y, (int)d.E,
-                      (int)d.h, (int)d.f, 1, s));
+  MOE_TRY(launch_down(w.fs, at<void>(ws, w.A), offset, at<int32_t>(ws, w.map2), Wd, Y,
+                      at<float>(ws, w.part), (int)d.E, (int)d.h, (int)d.f, 1, s));
   return MOE_OK;
 }
 

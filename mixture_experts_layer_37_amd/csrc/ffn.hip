@@ -56,9 +56,9 @@ namespace moe {
 
 namespace {
 
-#ifndef MOE_FFN_WAVES
-#define MOE_FFN_WAVES 8  // waves per GEMM workgroup (4 or 8)
-#endif
+// Waves per GEMM workgroup: 4 along M x 2 along N.  Two waves share each SIMD,
+// so one can issue MFMAs while the other waits for LDS or a barrier.
+constexpr int kWaves = 8;
 
 constexpr int BN = 256, BK = 64, GN = 8;
 constexpr int kPeriod = 6;  // steps after which the 3 A slots and 2 B slots line up again
@@ -75,7 +75,108 @@ struct GemmParams {
   bf16* C;               // [rows][Nout]
   int E, K, N, Nout;     // N: rows of each weight matrix (f or h)
   int ntiles, mtmax;
+  float* part;           // K-split partial tiles: [grid][BM * BN] float32
+  int split_max;         // most K chunks a tail tile is split into
+  int grid;              // workgroups of the GEMM launch (a multiple of 8)
 };
+
+// A K chunk of a tail tile (see gemm_bf16_kernel); ks == 1: a whole tile.
+struct KSplit {
+  int kbeg, ksteps;  // 64-wide K steps of this chunk
+  int ks;            // chunks of the tile
+  float* slot;       // where this chunk's float32 partial goes (ks > 1)
+};
+
+// Work of one XCD (workgroup i runs on XCD i % 8): a contiguous slice of the
+// tile numbering, done in rounds of nloc tiles.  When the slice is only a few
+// rounds long, the rem < nloc tiles left for the last round are each cut into
+// ks K chunks so that round keeps about nloc workgroups busy; with many
+// rounds the idle part of the last one matters little and the reduction
+// would cost more than it saves.
+constexpr int kSplitRounds = 4;  // split the tail only after at most this many full rounds
+struct XcdShare {
+  int tbeg, full, rem, ks, nloc;
+};
+__device__ __forceinline__ XcdShare xcd_share(int total, int xcd, int grid, int KT,
+                                              int split_max) {
+  XcdShare x;
+  x.nloc = grid >> 3;
+  const int per = (total + 7) >> 3;
+  x.tbeg = xcd * per;
+  const int ntile = max(0, min(total, x.tbeg + per) - x.tbeg);
+  x.full = ntile / x.nloc * x.nloc;
+  x.rem = ntile - x.full;
+  x.ks = (x.rem > 0 && x.full <= kSplitRounds * x.nloc)
+             ? max(1, min(min(split_max, x.nloc / x.rem), KT))
+             : 1;
+  return x;
+}
+
+// Tile t of the numbering: groups of GN n-tiles, m-tile major inside a group.
+struct TileAt {
+  int e, nt, row0, nvalid;
+};
+template <int BM>
+__device__ __forceinline__ TileAt tile_at(const GemmParams& p, int t, int mtiles) {
+  const int g = t / (mtiles * GN);
+  const int r = t - g * mtiles * GN;
+  const int gw = min(GN, p.ntiles - g * GN);
+  const int mt = r / gw;
+  TileAt x;
+  x.nt = g * GN + r % gw;
+  int lo = 0, hi = p.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.tmap[mid] <= mt) lo = mid; else hi = mid;
+  }
+  x.e = lo;
+  x.row0 = p.offset[lo] + (mt - p.tmap[lo]) * BM;
+  x.nvalid = min(BM, p.offset[lo + 1] - x.row0);
+  return x;
+}
+
+// Float32 partial of a K chunk, in the accumulators' own per-thread order:
+// float4 group q of thread i at slot + 4 * (q * blockDim + i).
+template <int RBLK, int NW>
+__device__ __forceinline__ float4* part_at(float* slot, int q) {
+  return reinterpret_cast<float4*>(slot) + (size_t)q * 64 * NW + threadIdx.x;
+}
+
+// Epilogue: the wave's (2 BM / NW) x 128 block.  D layout of a 32x32 MFMA
+// tile: lane holds column (lane % 32) and rows 8 * (v / 4) + 4 * (lane / 32) +
+// (v % 4), v = 0..15.  Gate/up: a = SiLU(g) * u from the gate and up halves.
+template <int BM, int NW, bool GATEUP>
+__device__ __forceinline__ void store_tile(const GemmParams& p, const floatx16 (&acc)[(2 * BM / NW) / 32][4],
+                                           int nt, int row0, int nvalid) {
+  constexpr int WR = 2 * BM / NW, RBLK = WR / 32;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, khalf = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < RBLK; ++i) {
+    if (wm * WR + i * 32 >= nvalid) continue;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = wm * WR + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
+      if (r >= nvalid) continue;
+      bf16* crow = p.C + (size_t)(row0 + r) * p.Nout;
+      if (GATEUP) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = nt * 128 + wn * 64 + j * 32 + l32;
+          const float gv = acc[i][j][v], uv = acc[i][j + 2][v];
+          const float a = gv / (1.f + __expf(-gv)) * uv;
+          if (col < p.Nout) crow[col] = f32_to_bf16(a);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = nt * BN + wn * 128 + j * 32 + l32;
+          if (col < p.Nout) crow[col] = f32_to_bf16(acc[i][j][v]);
+        }
+      }
+    }
+  }
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
   const int n = bytes > 0x7fffffffull ? 0x7fffffff : (int)bytes;
@@ -105,7 +206,7 @@ struct Ring {
 
 template <int BM, int NW, bool GATEUP, bool PARTIAL>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, int row0,
-                                          int nvalid, const Ring& L) {
+                                          int nvalid, const Ring& L, const KSplit& ksp) {
   constexpr int WM = NW / 2;         // waves along M (2 along N)
   constexpr int WR = BM / WM;        // rows per wave
   constexpr int RBLK = WR / 32;      // 32-row MFMA blocks per wave
@@ -117,7 +218,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
   const int lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int K = p.K;
-  const int KT = K / BK;
+  const int KT = ksp.ksteps;  // steps of this tile's K range, which starts at step ksp.kbeg
 
   // ---- copy sources.  Lane i of 8-row group g fills LDS row 8g + i/8,
   // physical chunk i%8, with logical chunk (i%8) ^ ((row >> 1) & 7).
@@ -151,12 +252,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
   }
   // step j past the end reloads the last step (in bounds, never read)
   auto issueA = [&](bf16* as, int j) {
-    const int kb = min(j, KT - 1) * BK * 2;
+    const int kb = (ksp.kbeg + min(j, KT - 1)) * BK * 2;
 #pragma unroll
     for (int q = 0; q < AG; ++q) dma16(rA, as + (wave + NW * q) * 8 * BK, voA[q], kb);
   };
   auto issueB = [&](bf16* bs, int j) {
-    const int kb = min(j, KT - 1) * BK * 2;
+    const int kb = (ksp.kbeg + min(j, KT - 1)) * BK * 2;
 #pragma unroll
     for (int q = 0; q < BG; ++q)
       dma16((GATEUP && q >= BG / 2) ? rB1 : rB0, bs + (wave + NW * q) * 8 * BK, voB[q], kb);
@@ -275,33 +376,19 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
   if (rest > 4) step(j + 4, L.a1, L.b0, L.a2, L.b1);
   wait_vm<0>();  // copies past the end are still in flight
 
-  // ---- epilogue.  D layout: lane holds column (lane % 32) and rows
-  // 8 * (v / 4) + 4 * (lane / 32) + (v % 4), v = 0..15.
+  if (ksp.ks > 1) {  // a K chunk of a tail tile: leave the partial to the reduction
 #pragma unroll
-  for (int i = 0; i < RBLK; ++i) {
-    if (PARTIAL && i >= rlim) continue;
+    for (int i = 0; i < RBLK; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = wm * WR + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
-      if (r >= nvalid) continue;
-      bf16* crow = p.C + (size_t)(row0 + r) * p.Nout;
-      if (GATEUP) {
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = nt * 128 + wn * 64 + j * 32 + l32;
-          const float gv = acc[i][j][v], uv = acc[i][j + 2][v];
-          const float a = gv / (1.f + __expf(-gv)) * uv;
-          if (col < p.Nout) crow[col] = f32_to_bf16(a);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = nt * BN + wn * 128 + j * 32 + l32;
-          if (col < p.Nout) crow[col] = f32_to_bf16(acc[i][j][v]);
-        }
-      }
-    }
+        for (int v4 = 0; v4 < 4; ++v4)
+          *part_at<RBLK, NW>(ksp.slot, (i * 4 + j) * 4 + v4) =
+              make_float4(acc[i][j][4 * v4], acc[i][j][4 * v4 + 1], acc[i][j][4 * v4 + 2],
+                          acc[i][j][4 * v4 + 3]);
+    return;
   }
+  store_tile<BM, NW, GATEUP>(p, acc, nt, row0, nvalid);
 }
 
 // Persistent grouped GEMM.  The grid holds a fixed number of workgroups (a
@@ -319,33 +406,69 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(GemmParams p) {
   const Ring L{A0, A1, A2, B0, B1};
 
   const int mtiles = p.tmap[p.E];
-  const int total = mtiles * p.ntiles;
-  const int xcd = blockIdx.x & 7, nloc = gridDim.x >> 3;
-  const int per = (total + 7) >> 3;
-  const int t_end = min(total, (xcd + 1) * per);
-  for (int t = xcd * per + (blockIdx.x >> 3); t < t_end; t += nloc) {
-    const int g = t / (mtiles * GN);
-    const int rem = t - g * mtiles * GN;
-    const int gw = min(GN, p.ntiles - g * GN);
-    const int mt = rem / gw;
-    const int nt = g * GN + rem % gw;
-    int lo = 0, hi = p.E;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.tmap[mid] <= mt) lo = mid; else hi = mid;
+  const int KT = p.K / BK;
+  const int xcd = blockIdx.x & 7;
+  const XcdShare xs = xcd_share(mtiles * p.ntiles, xcd, p.grid, KT, p.split_max);
+  const int units = xs.full + xs.rem * xs.ks;
+  for (int u = blockIdx.x >> 3; u < units; u += xs.nloc) {
+    int t = xs.tbeg + u;
+    KSplit ksp{0, KT, 1, nullptr};
+    if (u >= xs.full && xs.ks > 1) {
+      const int v = u - xs.full, q = v / xs.ks, kc = v - q * xs.ks;  // tail tile q, chunk kc
+      t = xs.tbeg + xs.full + q;
+      ksp.ks = xs.ks;
+      ksp.kbeg = kc * KT / xs.ks;
+      ksp.ksteps = (kc + 1) * KT / xs.ks - ksp.kbeg;
+      ksp.slot = p.part + (size_t)(xcd * xs.nloc + v) * BM * BN;
     }
-    const int e = lo;
-    const int row0 = p.offset[e] + (mt - p.tmap[e]) * BM;
-    const int nvalid = min(BM, p.offset[e + 1] - row0);
+    const TileAt ta = tile_at<BM>(p, t, mtiles);
+    const int e = ta.e, nt = ta.nt, row0 = ta.row0, nvalid = ta.nvalid;
     __syncthreads();  // every wave is done with the previous tile's LDS
     // tiles more than half full run the fully scheduled loop (rows past
     // nvalid read zero and are not stored); emptier ones skip the MFMAs of
     // their empty 32-row blocks
     if (2 * nvalid > BM)
-      gemm_tile<BM, NW, GATEUP, false>(p, e, nt, row0, nvalid, L);
+      gemm_tile<BM, NW, GATEUP, false>(p, e, nt, row0, nvalid, L, ksp);
     else
-      gemm_tile<BM, NW, GATEUP, true>(p, e, nt, row0, nvalid, L);
+      gemm_tile<BM, NW, GATEUP, true>(p, e, nt, row0, nvalid, L, ksp);
   }
+}
+
+// Sum of the K chunks of the tail tiles, in chunk order, then the same
+// epilogue as gemm_bf16_kernel.  Workgroup b handles tail tile b / 8 of XCD
+// b % 8 (if that XCD split its tail); thread i reads the partial groups that
+// thread i of the GEMM wrote.
+template <int BM, int NW, bool GATEUP>
+__global__ __launch_bounds__(64 * NW) void ksplit_reduce_kernel(GemmParams p) {
+  constexpr int RBLK = (2 * BM / NW) / 32;
+  const int mtiles = p.tmap[p.E];
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const XcdShare xs = xcd_share(mtiles * p.ntiles, xcd, p.grid, p.K / BK, p.split_max);
+  if (xs.ks <= 1 || q >= xs.rem) return;
+  const TileAt ta = tile_at<BM>(p, xs.tbeg + xs.full + q, mtiles);
+  floatx16 acc[RBLK][4];
+#pragma unroll
+  for (int i = 0; i < RBLK; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  for (int c = 0; c < xs.ks; ++c) {
+    float* slot = p.part + (size_t)(xcd * xs.nloc + q * xs.ks + c) * BM * BN;
+#pragma unroll
+    for (int i = 0; i < RBLK; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const float4 x = *part_at<RBLK, NW>(slot, (i * 4 + j) * 4 + v4);
+          acc[i][j][4 * v4] += x.x;
+          acc[i][j][4 * v4 + 1] += x.y;
+          acc[i][j][4 * v4 + 2] += x.z;
+          acc[i][j][4 * v4 + 3] += x.w;
+        }
+  }
+  store_tile<BM, NW, GATEUP>(p, acc, ta.nt, ta.row0, ta.nvalid);
 }
 
 // float32 path: one thread per output, plain dot products (small workloads).
@@ -397,15 +520,15 @@ __global__ void tile_map_kernel(const int32_t* offset, int E, int bm1, int bm2, 
 int round8(int x) { return (x + 7) & ~7; }
 
 template <bool GATEUP>
-void launch_gemm(int bm, int nw, int grid, const GemmParams& p, hipStream_t s) {
-  if (bm == 256 && nw == 8)
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 8, GATEUP>), dim3(grid), dim3(512), 0, s, p);
-  else if (bm == 256)
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 4, GATEUP>), dim3(grid), dim3(256), 0, s, p);
-  else if (nw == 8)
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 8, GATEUP>), dim3(grid), dim3(512), 0, s, p);
-  else
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 4, GATEUP>), dim3(grid), dim3(256), 0, s, p);
+void launch_gemm(int bm, const GemmParams& p, hipStream_t s) {
+  const dim3 grid(p.grid), block(64 * kWaves);
+  if (bm == 256) {
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, kWaves, GATEUP>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ksplit_reduce_kernel<256, kWaves, GATEUP>), grid, block, 0, s, p);
+  } else {
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, kWaves, GATEUP>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ksplit_reduce_kernel<128, kWaves, GATEUP>), grid, block, 0, s, p);
+  }
 }
 
 }  // namespace
@@ -423,7 +546,7 @@ FfnShape ffn_shape(int64_t rows_max, int E, int h, int f, int T, int k, int bf16
   // per n-tile instead of once per 128-row tile.
   const double avg = E > 0 ? (double)T * k / E : 0.0;
   fs.bm1 = fs.bm2 = avg <= 96.0 ? 128 : 256;
-  fs.nw1 = fs.nw2 = MOE_FFN_WAVES;
+  fs.nw1 = fs.nw2 = kWaves;
   fs.mt1 = (int)((rows_max + (int64_t)E * (fs.bm1 - 1)) / fs.bm1);
   fs.mt2 = (int)((rows_max + (int64_t)E * (fs.bm2 - 1)) / fs.bm2);
   fs.nt1 = (f + 127) / 128;
@@ -433,6 +556,10 @@ FfnShape ffn_shape(int64_t rows_max, int E, int h, int f, int T, int k, int bf16
   // CU), never more than the static bound on tiles, a multiple of 8
   fs.grid1 = round8(std::min<int64_t>((int64_t)fs.mt1 * fs.nt1, ncu));
   fs.grid2 = round8(std::min<int64_t>((int64_t)fs.mt2 * fs.nt2, ncu));
+  // tail tiles are cut into at most 4 K chunks: each chunk's float32
+  // partial (256 KB) is written and read back once by the reduction
+  fs.split_max = 4;
+  fs.part_slots = std::max(fs.grid1, fs.grid2);
   return fs;
 }
 
@@ -443,8 +570,8 @@ hipError_t launch_tile_map(const int32_t* offset, int E, int bm1, int bm2, int32
 }
 
 hipError_t launch_gate_up(const FfnShape& fs, const void* X, const int32_t* offset,
-                          const int32_t* map1, const void* Wg, const void* Wu, void* A, int E,
-                          int h, int f, int bf16_, hipStream_t s) {
+                          const int32_t* map1, const void* Wg, const void* Wu, void* A,
+                          float* part, int E, int h, int f, int bf16_, hipStream_t s) {
   if (!bf16_) {
     // rows are bounded by the caller's rows_max; launch for the static bound
     return hipErrorNotSupported;
@@ -452,19 +579,19 @@ hipError_t launch_gate_up(const FfnShape& fs, const void* X, const int32_t* offs
   if (fs.grid1 == 0) return hipSuccess;
   GemmParams p{static_cast<const bf16*>(X), offset, map1, static_cast<const bf16*>(Wg),
                static_cast<const bf16*>(Wu), static_cast<bf16*>(A), E, h, f, f,
-               fs.nt1, fs.mt1};
-  launch_gemm<true>(fs.bm1, fs.nw1, fs.grid1, p, s);
+               fs.nt1, fs.mt1, part, fs.split_max, fs.grid1};
+  launch_gemm<true>(fs.bm1, p, s);
   return hipGetLastError();
 }
 
 hipError_t launch_down(const FfnShape& fs, const void* A, const int32_t* offset,
-                       const int32_t* map2, const void* Wd, void* Y, int E, int h, int f,
-                       int bf16_, hipStream_t s) {
+                       const int32_t* map2, const void* Wd, void* Y, float* part, int E, int h,
+                       int f, int bf16_, hipStream_t s) {
   if (!bf16_) return hipErrorNotSupported;
   if (fs.grid2 == 0) return hipSuccess;
   GemmParams p{static_cast<const bf16*>(A), offset, map2, static_cast<const bf16*>(Wd), nullptr,
-               static_cast<bf16*>(Y), E, f, h, h, fs.nt2, fs.mt2};
-  launch_gemm<false>(fs.bm2, fs.nw2, fs.grid2, p, s);
+               static_cast<bf16*>(Y), E, f, h, h, fs.nt2, fs.mt2, part, fs.split_max, fs.grid2};
+  launch_gemm<false>(fs.bm2, p, s);
   return hipGetLastError();
 }
 

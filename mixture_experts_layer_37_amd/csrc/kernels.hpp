@@ -68,17 +68,22 @@ struct FfnShape {
   int nt1, nt2;     // n-tiles of each GEMM
   int grid1, grid2; // persistent workgroups launched (multiple of 8)
   int rows_cap;     // rows allocated in X and in the SwiGLU intermediate
+  int split_max;    // most K chunks of a tail tile
+  int part_slots;   // K-split partial tiles (256 x 256 float32 each), shared by the two GEMMs
 };
+constexpr size_t kPartSlotBytes = 256 * 256 * sizeof(float);
 // ncu: compute units of the device (the persistent grid size)
 FfnShape ffn_shape(int64_t rows_max, int E, int h, int f, int T, int k, int bf16, int ncu);
 hipError_t launch_tile_map(const int32_t* offset, int E, int bm1, int bm2, int32_t* map1,
                            int32_t* map2, hipStream_t s);
+// part: room for fs.part_slots K-split partial tiles (kPartSlotBytes each);
+// each GEMM is followed by the reduction of its split tail tiles
 hipError_t launch_gate_up(const FfnShape& fs, const void* X, const int32_t* offset,
-                          const int32_t* map1, const void* Wg, const void* Wu, void* A, int E,
-                          int h, int f, int bf16, hipStream_t s);
+                          const int32_t* map1, const void* Wg, const void* Wu, void* A,
+                          float* part, int E, int h, int f, int bf16, hipStream_t s);
 hipError_t launch_down(const FfnShape& fs, const void* A, const int32_t* offset,
-                       const int32_t* map2, const void* Wd, void* Y, int E, int h, int f,
-                       int bf16, hipStream_t s);
+                       const int32_t* map2, const void* Wd, void* Y, float* part, int E, int h,
+                       int f, int bf16, hipStream_t s);
 
 // ---------------------------------------------------------------- combine, stats
 hipError_t launch_combine(const void* U, const void* Y, const int32_t* slot, const float* gate,

@@ -211,3 +211,35 @@ def sampled_expert_rows(r: dict, E: int, n_experts: int = 3, per_expert: int = 4
             rows.update(rng.integers(a, b, size=per_expert - 2).tolist())
         out.append((e, sorted(rows)))
     return out
+
+
+def ksplit_chunks(w, offset, gemm: str, ncu: int) -> int:
+    """Most K chunks any XCD cuts a tail tile into, for the bf16 grouped GEMM.
+
+    Mirrors the kernel's host and device work split (tile sizes, persistent
+    grid, 8 contiguous XCD slices of nloc-wide rounds, tail split only after at
+    most 4 full rounds and into at most 4 chunks); a test uses it only to make
+    sure its shape exercises the K-split path.
+    """
+    E = w.E
+    rows = [int(offset[e + 1] - offset[e]) for e in range(E)]
+    avg = w.T * w.k / E
+    bm = 128 if avg <= 96 else 256
+    n_cols, K = (w.f, w.h) if gemm == "gate_up" else (w.h, w.f)
+    nt = (n_cols + 127) // 128 if gemm == "gate_up" else (n_cols + 255) // 256
+    C = oracle_capacity(w)
+    rows_max = min(w.T * w.k, E * min(C, w.T))
+    mt_static = (rows_max + E * (bm - 1)) // bm
+    grid = min(mt_static * nt, ncu)
+    grid = (grid + 7) // 8 * 8
+    nloc = grid // 8
+    total = sum((r + bm - 1) // bm for r in rows) * nt
+    per = (total + 7) // 8
+    best = 1
+    for x in range(8):
+        ntile = max(0, min(total, x * per + per) - x * per)
+        full = ntile // nloc * nloc
+        rem = ntile - full
+        if rem > 0 and full <= 4 * nloc:
+            best = max(best, max(1, min(4, nloc // rem, K // 64)))
+    return best

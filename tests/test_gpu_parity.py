@@ -97,6 +97,30 @@ def test_edge_cases(name):
         assert r["C"] == 40
 
 
+# Shapes whose last round of tiles is short enough that the grouped GEMM cuts
+# the tail tiles into K chunks and sums their float32 partials afterwards.
+KSPLIT = {
+    "gate_up": L.SMALL["mixtral_small"].replace(T=2204, E=1, k=1, h=512, f=4096),
+    "down": L.SMALL["mixtral_small"].replace(T=2204, E=1, k=1, h=8192, f=512),
+}
+
+
+@pytest.mark.parametrize("gemm", list(KSPLIT))
+def test_ksplit_tail(gemm):
+    w = KSPLIT[gemm]
+    L.log(f"[ksplit] {gemm} {w}")
+    x = I.make_inputs(w, seed=4, device=DEV)
+    _, g = L.run_layer(w, x)
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert L.ksplit_chunks(w, L.to_np(g["offset"]), gemm, ncu) > 1, "shape does not split"
+    xc = cpu_copy(x)
+    r = L.check_routing_shared_logits(w, g)
+    L.check_outputs_small(w, g, xc, r)
+    # the chunk sums are added in chunk order: repeated calls agree bit for bit
+    _, g2 = L.run_layer(w, x)
+    assert torch.equal(g["out"], g2["out"])
+
+
 def test_all_logits_equal_and_one_hot_load():
     # W_r = 0: every logit ties, lower index wins: experts 0..k-1 in order for
     # every token, gates 1/k; with C < T only the first C tokens are kept.
