@@ -26,6 +26,11 @@ unless another page is named):
     "负载均衡辅助损失：推导与梯度"; for sigmoid scores P uses the scores
     normalised over all experts (same section, DeepSeek-V3 paragraph).
   * MaxVio, section "无辅助损失的负载均衡".
+  * Selection-only expert bias b_i and its sign update (loss-free balancing),
+    section "无辅助损失的负载均衡", equations g'_{i,t} and e_i, b_i.
+  * Shared experts that every token passes through without the router,
+    section "细粒度专家与共享专家", equation h'_t (DeepSeek-V3 form).
+  * Group-limited (node-limited) selection, section "设备受限与节点受限路由".
 
 Readings where the pages are silent or ambiguous are listed in the design doc of the
 repository; the ones that change arithmetic are restated next to the code.
@@ -119,6 +124,65 @@ def gates(s, idx, gate: str) -> np.ndarray:
     if gate == GATE_RENORM:
         return sel / sel.sum(axis=1, keepdims=True)
     raise ValueError(gate)
+
+
+def selection_keys(s, b_sel=None) -> np.ndarray:
+    """Keys that decide which experts a token takes: s[t, i] + b_i.
+
+    Loss-free balancing adds a per-expert bias to the affinity for the top-k
+    choice only; the gates keep using s (page section "无辅助损失的负载均衡").
+    """
+    s = f64(s)
+    return s if b_sel is None else s + f64(b_sel)[None, :]
+
+
+def group_limited_mask(keys, n_groups: int, topk_groups: int, per_group: int) -> np.ndarray:
+    """Experts a token may choose under group-limited selection.
+
+    The experts form n_groups equal groups of consecutive ids (the nodes of the
+    node-limited routing).  A group scores the sum of its per_group highest
+    keys; the topk_groups best groups are kept, the lower group first among
+    equal scores; experts of the other groups are excluded (page section
+    "设备受限与节点受限路由": nodes ranked by the sum of their top K_r / M
+    affinities, at most M nodes per token).
+    """
+    keys = f64(keys)
+    T, E = keys.shape
+    assert E % n_groups == 0 and 1 <= topk_groups <= n_groups
+    gsize = E // n_groups
+    allowed = np.zeros((T, E), dtype=bool)
+    for t in range(T):
+        gscore = []
+        for g in range(n_groups):
+            members = np.sort(keys[t, g * gsize:(g + 1) * gsize])[::-1]
+            gscore.append(float(members[:per_group].sum()))
+        chosen = np.argsort(-np.asarray(gscore), kind="stable")[:topk_groups]
+        for g in chosen:
+            allowed[t, g * gsize:(g + 1) * gsize] = True
+    return allowed
+
+
+def select_topk_keys(keys, k: int, allowed=None) -> np.ndarray:
+    """The k allowed experts with the largest keys, best first; lower index first on ties."""
+    keys = f64(keys)
+    if allowed is not None:
+        keys = np.where(allowed, keys, -np.inf)
+    order = np.argsort(-keys, axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+def update_bias(b_sel, count, gamma: float) -> np.ndarray:
+    """One step of the loss-free bias update.
+
+    e_i = mean_j c_j - c_i and b_i <- b_i + gamma * sign(e_i): an overloaded
+    expert's bias drops by gamma, an underloaded one's rises by gamma, an
+    expert exactly at the mean keeps its bias (section "无辅助损失的负载均衡";
+    V3 calls gamma the bias update speed).  count is the per-expert number of
+    assignments of the batch.
+    """
+    c = f64(count)
+    e = c.mean() - c
+    return f64(b_sel) + gamma * np.sign(e)
 
 
 # --------------------------------------------------------------------------- capacity
@@ -232,11 +296,25 @@ def load_stats(s, idx, fill_result: dict, score: str) -> dict:
 
 
 # --------------------------------------------------------------------------- layer
-def route(H, k: int, score: str, gate: str, C: int, fill_order: str = FILL_RANK_MAJOR) -> dict:
-    """All routing decisions from given logits: top-k, gates, fill and statistics."""
+def route(H, k: int, score: str, gate: str, C: int, fill_order: str = FILL_RANK_MAJOR,
+          b_sel=None, n_groups: int = 1, topk_groups: int = 1) -> dict:
+    """All routing decisions from given logits: top-k, gates, fill and statistics.
+
+    Without a selection bias and groups, the top-k is taken on the logits
+    (select_topk).  With either, the choice is made on the keys s + b, among
+    the experts of the chosen groups when n_groups > 1, each group scored by
+    its k / topk_groups best keys; the gates still come from s.
+    """
     H = f64(H)
     s = scores(H, score)
-    idx = select_topk(H, k)
+    if b_sel is None and n_groups <= 1:
+        idx = select_topk(H, k)
+    else:
+        keys = selection_keys(s, b_sel)
+        allowed = None
+        if n_groups > 1:
+            allowed = group_limited_mask(keys, n_groups, topk_groups, max(1, k // topk_groups))
+        idx = select_topk_keys(keys, k, allowed)
     g = gates(s, idx, gate)
     fr = fill(idx, H.shape[1], C, fill_order)
     st = load_stats(s, idx, fr, score)
@@ -246,13 +324,17 @@ def route(H, k: int, score: str, gate: str, C: int, fill_order: str = FILL_RANK_
     return out
 
 
-def combine(U, Y, slot, gate) -> np.ndarray:
+def combine(U, Y, slot, gate, Y_shared=None) -> np.ndarray:
     """out_t = u_t + sum over kept ranks r (in rank order) of g[t, r] * Y[slot[t, r]].
 
     Dropped assignments add nothing and the remaining gates are not rescaled;
-    a token with every assignment dropped is returned as its residual u_t.
+    a token with every assignment dropped is returned as its residual u_t plus
+    the shared experts' outputs Y_shared[s, t] (none when Y_shared is None).
     """
     out = f64(U).copy()
+    if Y_shared is not None:
+        for ys in f64(Y_shared):
+            out += ys
     Y = f64(Y)
     slot = np.asarray(slot)
     g = f64(gate)
@@ -273,26 +355,41 @@ def expert_outputs(X, offset, W_gate, W_up, W_down) -> np.ndarray:
     return Y
 
 
+def shared_expert_outputs(U, Ws_gate, Ws_up, Ws_down) -> np.ndarray:
+    """FFN^(s)_i(u_t) for every shared expert i and every token t: [N_s, T, h].
+
+    Shared experts take every token with weight 1 and no router (section
+    "细粒度专家与共享专家", equation h'_t).
+    """
+    U = f64(U)
+    return np.stack([swiglu_expert(U, Ws_gate[i], Ws_up[i], Ws_down[i])
+                     for i in range(np.asarray(Ws_gate).shape[0])])
+
+
 def layer_forward(U, W_r, W_gate, W_up, W_down, *, k: int, score: str, gate: str,
                   capacity_factor: float, cap_mode: str = CAP_ASSIGNMENTS,
                   fill_order: str = FILL_RANK_MAJOR, min_capacity: int = 0,
-                  b_r=None, W_noise=None, noise=None, logits=None) -> dict:
+                  b_r=None, W_noise=None, noise=None, logits=None, b_sel=None,
+                  n_groups: int = 1, topk_groups: int = 1, Ws_gate=None, Ws_up=None,
+                  Ws_down=None) -> dict:
     """The whole layer for small inputs.
 
     logits, when given, replaces the router product (used to route from exactly
-    the logits another implementation produced).
+    the logits another implementation produced).  b_sel, n_groups/topk_groups
+    and the shared-expert weights Ws_* add the DeepSeek-V3 parts.
     """
     U = f64(U)
     T = U.shape[0]
     E = np.asarray(W_r).shape[1]
     H = router_logits(U, W_r, b_r, W_noise, noise) if logits is None else f64(logits)
     C = capacity(T, E, k, capacity_factor, cap_mode, min_capacity)
-    r = route(H, k, score, gate, C, fill_order)
+    r = route(H, k, score, gate, C, fill_order, b_sel, n_groups, topk_groups)
     X = U[r["row_token"]]
     Y = expert_outputs(X, r["offset"], W_gate, W_up, W_down)
     r["X"] = X
     r["Y"] = Y
-    r["out"] = combine(U, Y, r["slot"], r["gate"])
+    r["Y_shared"] = None if Ws_gate is None else shared_expert_outputs(U, Ws_gate, Ws_up, Ws_down)
+    r["out"] = combine(U, Y, r["slot"], r["gate"], r["Y_shared"])
     return r
 
 

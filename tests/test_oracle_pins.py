@@ -396,3 +396,115 @@ def test_gate_sums_and_dropped_count():
         np.testing.assert_allclose(res["gate"].sum(1), 1.0, rtol=1e-14)
         assert res["n_dropped"] == int((res["slot"] < 0).sum())
         assert res["n_dropped"] > 0
+
+
+# ------------------------------------------------------------- DeepSeek-V3 parts
+def test_bias_update_hand_example():
+    g = golden("v3_routing.json")["bias_update"]
+    b = O.update_bias(g["b"], g["count"], g["gamma"])
+    np.testing.assert_allclose(b, g["b_new"], rtol=0, atol=1e-15)
+
+
+def test_bias_update_moves_by_fixed_step():
+    rng = np.random.default_rng(7)
+    b = rng.normal(0, 0.01, 16)
+    count = rng.integers(0, 100, 16)
+    step = O.update_bias(b, count, 0.001) - b
+    assert set(np.round(np.abs(step) / 0.001).astype(int).tolist()) <= {0, 1}
+    # overloaded experts (count above the mean) go down, underloaded ones up
+    assert (step[count > count.mean()] < 0).all() and (step[count < count.mean()] > 0).all()
+
+
+def test_bias_selects_but_does_not_weigh():
+    g = golden("v3_routing.json")["bias_only_selects"]
+    H = np.zeros((3, g["E"]))
+    C = O.capacity(3, g["E"], g["k"], 10.0)
+    r = O.route(H, g["k"], O.SIGMOID, O.GATE_RENORM, C, b_sel=g["b"])
+    assert (r["idx"] == g["idx"]).all()
+    np.testing.assert_allclose(r["gate"], np.tile(g["gate"], (3, 1)), rtol=0, atol=1e-15)
+
+
+def test_zero_bias_and_one_group_reduce_to_plain_topk():
+    rng = np.random.default_rng(8)
+    H = rng.normal(size=(200, 32))
+    C = O.capacity(200, 32, 4, 1.25)
+    for score in (O.SOFTMAX, O.SIGMOID):
+        plain = O.route(H, 4, score, O.GATE_RENORM, C)
+        biased = O.route(H, 4, score, O.GATE_RENORM, C, b_sel=np.zeros(32))
+        grouped = O.route(H, 4, score, O.GATE_RENORM, C, b_sel=np.zeros(32), n_groups=8,
+                          topk_groups=8)
+        for r in (biased, grouped):
+            assert (r["idx"] == plain["idx"]).all()
+            np.testing.assert_array_equal(r["gate"], plain["gate"])
+            np.testing.assert_array_equal(r["slot"], plain["slot"])
+
+
+def test_large_bias_forces_an_expert():
+    rng = np.random.default_rng(9)
+    H = rng.normal(size=(100, 16))
+    b = np.zeros(16)
+    b[5] = 10.0  # sigmoid scores lie in (0, 1): expert 5's key beats every other
+    C = O.capacity(100, 16, 2, 10.0)
+    r = O.route(H, 2, O.SIGMOID, O.GATE_RENORM, C, b_sel=b)
+    assert (r["idx"][:, 0] == 5).all()
+    others = np.where(np.arange(16) == 5, -np.inf, H)
+    assert (r["idx"][:, 1] == np.argmax(others, axis=1)).all()
+    s = 1.0 / (1.0 + np.exp(-H))
+    s5, s2 = s[:, 5], s[np.arange(100), r["idx"][:, 1]]
+    np.testing.assert_allclose(r["gate"][:, 0], s5 / (s5 + s2), rtol=1e-15)
+
+
+def test_group_limited_hand_example():
+    g = golden("v3_routing.json")["group_limited"]
+    H = np.zeros((2, g["E"]))
+    C = O.capacity(2, g["E"], g["k"], 10.0)
+    for M, key in ((1, "idx_M1"), (2, "idx_M2")):
+        r = O.route(H, g["k"], O.SIGMOID, O.GATE_RENORM, C, b_sel=g["b"],
+                    n_groups=g["n_groups"], topk_groups=M)
+        assert (r["idx"] == g[key]).all(), (M, r["idx"])
+    r = O.route(H, g["k"], O.SIGMOID, O.GATE_RENORM, C, b_sel=g["b"])
+    assert (r["idx"] == g["idx_unrestricted"]).all()
+
+
+def test_group_limited_brute_force():
+    # every allowed set checked against enumeration of all group subsets
+    import itertools
+    rng = np.random.default_rng(10)
+    E, G, M, k = 12, 4, 2, 4
+    keys = rng.normal(size=(50, E))
+    allowed = O.group_limited_mask(keys, G, M, k // M)
+    gs = E // G
+    for t in range(50):
+        score = [np.sort(keys[t, g * gs:(g + 1) * gs])[::-1][:k // M].sum() for g in range(G)]
+        best = max(itertools.combinations(range(G), M),
+                   key=lambda c: (sum(score[g] for g in c), [-g for g in c]))
+        want = np.zeros(E, dtype=bool)
+        for g in best:
+            want[g * gs:(g + 1) * gs] = True
+        assert (allowed[t] == want).all()
+    idx = O.select_topk_keys(keys, k, allowed)
+    assert allowed[np.arange(50)[:, None], idx].all()
+
+
+def test_shared_expert_is_an_always_on_expert():
+    # a shared expert is an expert every token takes with gate 1 and no capacity:
+    # the sparse layer with shared experts equals the dense masked form with a
+    # column of ones for each shared expert
+    rng = np.random.default_rng(11)
+    T, h, f, E, k, Ns = 9, 6, 5, 4, 2, 2
+    U = rng.normal(size=(T, h))
+    W_r = rng.normal(size=(h, E))
+    Wg, Wu, Wd = rng.normal(size=(E, f, h)), rng.normal(size=(E, f, h)), rng.normal(size=(E, h, f))
+    Sg, Su, Sd = rng.normal(size=(Ns, f, h)), rng.normal(size=(Ns, f, h)), rng.normal(size=(Ns, h, f))
+    r = O.layer_forward(U, W_r, Wg, Wu, Wd, k=k, score=O.SIGMOID, gate=O.GATE_RENORM,
+                        capacity_factor=0.6, b_sel=rng.normal(0, 0.1, E), n_groups=2,
+                        topk_groups=1, Ws_gate=Sg, Ws_up=Su, Ws_down=Sd)
+    g_dense = np.zeros((T, E + Ns))
+    for t in range(T):
+        for rr in range(k):
+            if r["slot"][t, rr] >= 0:
+                g_dense[t, r["idx"][t, rr]] = r["gate"][t, rr]
+    g_dense[:, E:] = 1.0
+    dense = O.dense_masked_forward(U, np.concatenate([Wg, Sg]), np.concatenate([Wu, Su]),
+                                   np.concatenate([Wd, Sd]), g_dense)
+    np.testing.assert_allclose(r["out"], dense, rtol=1e-12, atol=1e-12)
