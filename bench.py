@@ -109,7 +109,9 @@ def cpu_baseline(w, x, g, budget_s: float) -> dict:
                         None if x["W_noise"] is None else f64(x["W_noise"]),
                         None if x["noise"] is None else f64(x["noise"]))
     C = O.capacity(w.T, w.E, w.k, w.capacity_factor)
-    r = O.route(H, w.k, w.score, w.gate, C, w.fill)
+    r = O.route(H, w.k, w.score, w.gate, C, w.fill,
+                None if x.get("b_sel") is None else f64(x["b_sel"]), max(1, w.n_groups),
+                max(1, w.topk_groups))
     t_route = time.perf_counter() - t0
 
     rows_total = int(r["offset"][-1])
@@ -131,18 +133,30 @@ def cpu_baseline(w, x, g, budget_s: float) -> dict:
         t_ffn += t3 - t2
         rows_done += n
         experts_done += 1
+    # shared experts: every token, timed on up to 1024 tokens and scaled
+    t_sh, n_sh = 0.0, min(w.T, 1024)
+    Ys = None
+    if w.n_shared > 0:
+        t5 = time.perf_counter()
+        Ys = np.zeros((w.n_shared, w.T, w.h))
+        for i in range(w.n_shared):
+            Ys[i, :n_sh] = O.swiglu_expert(U[:n_sh], f64(x["Ws_gate"][i]), f64(x["Ws_up"][i]),
+                                           f64(x["Ws_down"][i]))
+        t_sh = (time.perf_counter() - t5) * w.T / max(n_sh, 1)
     t4 = time.perf_counter()
-    O.combine(U, Y, r["slot"], r["gate"])
+    O.combine(U, Y, r["slot"], r["gate"], Ys)
     t_comb = time.perf_counter() - t4
-    est = (t_route + t_comb + t_conv * len(active) / experts_done
+    est = (t_route + t_comb + t_sh + t_conv * len(active) / experts_done
            + t_ffn * rows_total / max(rows_done, 1))
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": w.T / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"routing, statistics and combine on all {w.T} tokens; expert SwiGLU on "
                        f"{rows_done} of {rows_total} kept rows from {experts_done} of "
-                       f"{len(active)} active experts (float64), scaled by rows; measured "
-                       f"{t_route + t_comb + t_conv + t_ffn:.1f} s, estimated {est:.1f} s "
-                       f"per full forward")}
+                       f"{len(active)} active experts (float64), scaled by rows"
+                       + (f"; {w.n_shared} shared expert(s) on {n_sh} tokens, scaled to {w.T}"
+                          if w.n_shared else "")
+                       + f"; measured {t_route + t_comb + t_conv + t_ffn:.1f} s, estimated "
+                       f"{est:.1f} s per full forward")}
 
 
 def main():
@@ -175,7 +189,8 @@ def main():
     def step(events=None):
         B.moe_layer_forward(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], x["noise"],
                             x["W_gate"], x["W_up"], x["W_down"], out, aux=aux,
-                            stage_events=events, ws=ws)
+                            stage_events=events, ws=ws, b_sel=x["b_sel"], Ws_gate=x["Ws_gate"],
+                            Ws_up=x["Ws_up"], Ws_down=x["Ws_down"])
 
     for _ in range(args.warmup):
         step()
@@ -204,17 +219,20 @@ def main():
     n_drop = int(aux["n_dropped"].item())
     bf16 = w.dtype == "bf16"
     eb = 2 if bf16 else 4
-    # algorithmic work: 6 h f FLOPs per kept (token, expert) row; the gate/up
-    # GEMM is 4 h f of it
-    f_exec = 6.0 * w.h * w.f * kept
-    f_nom = 6.0 * w.h * w.f * w.k * w.T
-    f_gate_up = 4.0 * w.h * w.f * kept
+    # algorithmic work: 6 h f FLOPs per kept (token, expert) row, plus
+    # 6 h f_shared per token and shared expert; the gate/up stage does 4 h f
+    # (4 h f_shared) of it
+    f_sh = 6.0 * w.h * w.f_shared * w.T * w.n_shared
+    f_exec = 6.0 * w.h * w.f * kept + f_sh
+    f_nom = 6.0 * w.h * w.f * w.k * w.T + f_sh
+    f_gate_up = 4.0 * w.h * w.f * kept + f_sh * 4.0 / 6.0
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     gu_ms = stage_ms["gate_up"]
     achieved = f_gate_up / (gu_ms * 1e-3) / 1e12
     kept_per_e = aux["kept"].cpu().tolist()
     e_active = sum(1 for c in kept_per_e if c > 0)
-    b_alg = eb * (3.0 * w.h * w.f * e_active + 2.0 * w.T * w.h + w.h * w.E * (2 if w.noisy else 1))
+    b_alg = eb * (3.0 * w.h * w.f * e_active + 3.0 * w.h * w.f_shared * w.n_shared
+                  + 2.0 * w.T * w.h + w.h * w.E * (2 if w.noisy else 1))
 
     res = {
         "metric": "MoE layer fwd tokens/sec on 1 MI355X",
@@ -229,9 +247,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "T": w.T, "h": w.h, "f": w.f, "E": w.E, "k": w.k,
-                   "score": w.score, "gate": w.gate, "capacity_factor": w.capacity_factor,
-                   "noisy": w.noisy, "seed": args.seed},
+        "config": dict({"workload": w.name, "T": w.T, "h": w.h, "f": w.f, "E": w.E, "k": w.k,
+                        "score": w.score, "gate": w.gate, "capacity_factor": w.capacity_factor,
+                        "noisy": w.noisy, "seed": args.seed},
+                       **({"n_groups": w.n_groups, "topk_groups": w.topk_groups}
+                          if w.n_groups > 1 else {}),
+                       **({"n_shared": w.n_shared, "f_shared": w.f_shared}
+                          if w.n_shared else {}),
+                       **({"sel_bias_std": w.sel_bias_var ** 0.5} if w.sel_bias_var else {})),
         "roofline": {"kernel": "grouped gate/up GEMM + SwiGLU", "bound": "mfma",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": measured_traffic(w.name)},

@@ -93,6 +93,17 @@ typedef struct {
   double capacity_factor; /* > 0, finite, in [1e-6, 1e6]; <= 0 means no limit
                              (dropless: C = T)                                 */
   int64_t min_capacity;   /* C is raised to at least this (0: no floor)        */
+  /* DeepSeek-V3 parts (page "MoE 与专家并行"); all zero: a plain layer.      */
+  int64_t n_groups;     /* group-limited selection (section "设备受限与节点受限路由"):
+                           experts form n_groups equal groups of consecutive ids
+                           and a token chooses only within its topk_groups best
+                           groups.  0 or 1: no limit; else 2..64 dividing E     */
+  int64_t topk_groups;  /* 1..min(n_groups, 8, k); a group scores the sum of its
+                           k / topk_groups best selection keys; need
+                           k <= topk_groups * (E / n_groups)                    */
+  int64_t n_shared;     /* shared experts taking every token with weight 1
+                           (section "细粒度专家与共享专家", eq. h'_t), 0..16      */
+  int64_t f_shared;     /* their intermediate size (same divisibility as f)     */
 } moe_config;
 
 /* Optional outputs of moe_layer_forward.  Any NULL field is kept in the
@@ -114,6 +125,7 @@ typedef struct {
   int32_t* n_dropped;  /* [1] sum (count - kept)                              */
   void* X;             /* [rows_max, h] permuted expert inputs                */
   void* Y;             /* [rows_max, h] expert outputs                        */
+  void* Y_shared;      /* [n_shared, T, h] shared-expert outputs              */
 } moe_aux_outputs;
 
 /* Workspace sizes per entry point. */
@@ -121,7 +133,8 @@ typedef enum {
   MOE_WS_ROUTE = 0,
   MOE_WS_DISPATCH = 1,
   MOE_WS_EXPERT_FFN = 2,
-  MOE_WS_LAYER = 3
+  MOE_WS_LAYER = 3,
+  MOE_WS_SHARED_FFN = 4
 } moe_ws_entry;
 
 /* Stage boundaries recorded by moe_layer_forward when stage_events != NULL:
@@ -143,18 +156,22 @@ int32_t moe_workspace_size(const moe_config* cfg, int32_t entry, size_t* bytes);
 
 /* Router: logits, scores, top-k and gates (router section; scoring table).
  *  U [T,h], W_r [h,E]: required.  b_r [E]: optional per-expert logit bias.
+ *  b_sel [E]: optional selection-only bias (section "无辅助损失的负载均衡"):
+ *  the top-k is taken on s + b_sel while the gates keep using s.
  *  W_noise [h,E] and noise [T,E] (standard-normal draws supplied by the
  *  caller): required iff cfg->noisy.
- *  topk_idx [T,k], topk_gate [T,k]: required outputs, rank order, selection by
- *  the key (-H, expert index) on the float32 logits.
+ *  topk_idx [T,k], topk_gate [T,k]: required outputs, rank order.  Selection
+ *  is by the key (-H, expert index) on the float32 logits; with b_sel or
+ *  cfg->n_groups > 1 by (-(s + b_sel), expert index) on float32 scores,
+ *  within the chosen groups.
  *  logits [T,E]: optional output of exactly the logits used.
  *  prob_sum [E]: optional output of sum_t s (softmax) or sum_t s/sum_j s
  *  (sigmoid), the numerator of P.
  *  ws: MOE_WS_ROUTE bytes. */
 int32_t moe_route(const moe_config* cfg, const void* U, const void* W_r, const float* b_r,
-                  const void* W_noise, const float* noise, int32_t* topk_idx,
-                  float* topk_gate, float* logits, float* prob_sum, void* ws,
-                  size_t ws_bytes, void* stream);
+                  const float* b_sel, const void* W_noise, const float* noise,
+                  int32_t* topk_idx, float* topk_gate, float* logits, float* prob_sum,
+                  void* ws, size_t ws_bytes, void* stream);
 
 /* Dispatch: capacity cut and permutation (capacity section).
  *  topk_idx [T,k] in: expert ids (values outside [0,E) are undefined input).
@@ -177,11 +194,29 @@ int32_t moe_expert_ffn(const moe_config* cfg, const void* X, const int32_t* offs
                        const void* W_gate, const void* W_up, const void* W_down, void* Y,
                        void* ws, size_t ws_bytes, void* stream);
 
-/* Combine with residual (eq. h'_t): out[t] = U[t] + sum over r with
- * slot[t,r] >= 0, in rank order, of topk_gate[t,r] * Y[slot[t,r]].  Float32
- * accumulation; out has cfg->dtype and may not alias U or Y. */
+/* Shared experts (section "细粒度专家与共享专家", eq. h'_t): for every shared
+ * expert i and token t, Y_shared[i,t] = FFN^(s)_i(U[t]) with the SwiGLU of the
+ * routed experts (f_shared wide).  Ws_gate, Ws_up [n_shared, f_shared, h],
+ * Ws_down [n_shared, h, f_shared], Y_shared [n_shared, T, h] out.  Needs
+ * cfg->n_shared > 0.  ws: MOE_WS_SHARED_FFN bytes. */
+int32_t moe_shared_ffn(const moe_config* cfg, const void* U, const void* Ws_gate,
+                       const void* Ws_up, const void* Ws_down, void* Y_shared, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Combine with residual (eq. h'_t): out[t] = U[t] + sum over shared experts i
+ * of Y_shared[i,t] + sum over r with slot[t,r] >= 0, in rank order, of
+ * topk_gate[t,r] * Y[slot[t,r]].  Y_shared: NULL or [cfg->n_shared, T, h].
+ * Float32 accumulation in that order; out has cfg->dtype and may not alias
+ * U, Y or Y_shared. */
 int32_t moe_combine(const moe_config* cfg, const void* U, const void* Y, const int32_t* slot,
-                    const float* topk_gate, void* out, void* stream);
+                    const float* topk_gate, const void* Y_shared, void* out, void* stream);
+
+/* Loss-free balancing bias step (section "无辅助损失的负载均衡", equations e_i
+ * and b_i): with c = count [E] (assignments per expert, e.g. dispatch's
+ * count) and its mean, b_sel[i] += gamma * sign(mean - c[i]) in place
+ * (float32).  gamma finite and >= 0. */
+int32_t moe_update_bias(const moe_config* cfg, const int32_t* count, float* b_sel, float gamma,
+                        void* stream);
 
 /* Load-balance statistics from dispatch counts and the router's prob_sum
  * (aux-loss section; MaxVio of the loss-free section).  count, kept,
@@ -191,15 +226,21 @@ int32_t moe_stats(const moe_config* cfg, const int32_t* count, const int32_t* ke
                   const float* prob_sum, float* f, float* P, float* aux_loss, float* maxvio,
                   int32_t* n_dropped, void* stream);
 
-/* The whole layer: route, dispatch, experts, combine, statistics.
+/* The whole layer: route, dispatch, experts (and shared experts), combine,
+ * statistics.
+ *  b_sel: optional selection bias as in moe_route.  Ws_gate, Ws_up, Ws_down:
+ *  shared-expert weights as in moe_shared_ffn, required iff cfg->n_shared > 0;
+ *  their products run in the gate_up and down stages.
  *  out [T,h] required.  aux: optional outputs (struct pointer may be NULL).
  *  stage_events: NULL, or MOE_NUM_STAGES + 1 hipEvent_t handles recorded on
  *  `stream` at the stage boundaries (for timing).  ws: MOE_WS_LAYER bytes. */
 int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
-                          const float* b_r, const void* W_noise, const float* noise,
-                          const void* W_gate, const void* W_up, const void* W_down, void* out,
-                          const moe_aux_outputs* aux, void* const* stage_events, void* ws,
-                          size_t ws_bytes, void* stream);
+                          const float* b_r, const float* b_sel, const void* W_noise,
+                          const float* noise, const void* W_gate, const void* W_up,
+                          const void* W_down, const void* Ws_gate, const void* Ws_up,
+                          const void* Ws_down, void* out, const moe_aux_outputs* aux,
+                          void* const* stage_events, void* ws, size_t ws_bytes,
+                          void* stream);
 
 #ifdef __cplusplus
 }

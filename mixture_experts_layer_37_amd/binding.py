@@ -22,7 +22,7 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_GATE_RAW, MOE_GATE_RENORM = 0, 1
 MOE_FILL_RANK_MAJOR, MOE_FILL_TOKEN_MAJOR = 0, 1
 MOE_CAP_ASSIGNMENTS, MOE_CAP_TOKENS = 0, 1
-MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_EXPERT_FFN, MOE_WS_LAYER = range(4)
+MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_EXPERT_FFN, MOE_WS_LAYER, MOE_WS_SHARED_FFN = range(5)
 MOE_NUM_STAGES = 6
 STAGE_NAMES = ["route", "dispatch", "gate_up", "down", "combine", "stats"]
 
@@ -40,13 +40,15 @@ class moe_config(ctypes.Structure):
         ("dtype", ctypes.c_int32), ("score", ctypes.c_int32), ("gate", ctypes.c_int32),
         ("cap_mode", ctypes.c_int32), ("fill", ctypes.c_int32), ("noisy", ctypes.c_int32),
         ("capacity_factor", ctypes.c_double), ("min_capacity", ctypes.c_int64),
+        ("n_groups", ctypes.c_int64), ("topk_groups", ctypes.c_int64),
+        ("n_shared", ctypes.c_int64), ("f_shared", ctypes.c_int64),
     ]
 
 
 class moe_aux_outputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "topk_idx", "topk_gate", "logits", "slot", "row_token", "count", "kept", "offset",
-        "prob_sum", "f", "P", "aux_loss", "maxvio", "n_dropped", "X", "Y")]
+        "prob_sum", "f", "P", "aux_loss", "maxvio", "n_dropped", "X", "Y", "Y_shared")]
 
 
 AUX_FIELDS = [n for n, _ in moe_aux_outputs._fields_]
@@ -69,13 +71,15 @@ def lib() -> ctypes.CDLL:
             "moe_capacity": (I32, [cfgp, ctypes.POINTER(I64)]),
             "moe_max_rows": (I32, [cfgp, ctypes.POINTER(I64)]),
             "moe_workspace_size": (I32, [cfgp, I32, ctypes.POINTER(SZ)]),
-            "moe_route": (I32, [cfgp] + [P] * 9 + [P, SZ, P]),
+            "moe_route": (I32, [cfgp] + [P] * 10 + [P, SZ, P]),
             "moe_dispatch": (I32, [cfgp] + [P] * 8 + [P, SZ, P]),
             "moe_expert_ffn": (I32, [cfgp] + [P] * 6 + [P, SZ, P]),
-            "moe_combine": (I32, [cfgp] + [P] * 5 + [P]),
+            "moe_combine": (I32, [cfgp] + [P] * 6 + [P]),
+            "moe_shared_ffn": (I32, [cfgp] + [P] * 5 + [P, SZ, P]),
+            "moe_update_bias": (I32, [cfgp, P, P, ctypes.c_float, P]),
             "moe_stats": (I32, [cfgp] + [P] * 8 + [P]),
-            "moe_layer_forward": (I32, [cfgp] + [P] * 9 + [ctypes.POINTER(moe_aux_outputs), P,
-                                                         P, SZ, P]),
+            "moe_layer_forward": (I32, [cfgp] + [P] * 13 + [ctypes.POINTER(moe_aux_outputs), P,
+                                                          P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -108,7 +112,11 @@ def make_config(w, T: Optional[int] = None) -> moe_config:
                       dtype=_DT[w.dtype], score=_SC[w.score], gate=_GT[w.gate],
                       cap_mode=_CP[w.cap_mode], fill=_FL[w.fill], noisy=int(w.noisy),
                       capacity_factor=float(w.capacity_factor),
-                      min_capacity=int(w.min_capacity))
+                      min_capacity=int(w.min_capacity),
+                      n_groups=int(getattr(w, "n_groups", 0)),
+                      topk_groups=int(getattr(w, "topk_groups", 0)),
+                      n_shared=int(getattr(w, "n_shared", 0)),
+                      f_shared=int(getattr(w, "f_shared", 0)))
 
 
 def capacity(cfg: moe_config) -> int:
@@ -172,7 +180,7 @@ def new_workspace(cfg: moe_config, entry: int, device="cuda") -> torch.Tensor:
 
 # --------------------------------------------------------------------------- entry points
 def moe_route(cfg, U, W_r, b_r, W_noise, noise, topk_idx, topk_gate, logits=None,
-              prob_sum=None, ws=None, stream=None):
+              prob_sum=None, ws=None, stream=None, b_sel=None):
     T, h, E, k = cfg.T, cfg.h, cfg.E, cfg.k
     dt = _elem_dtype(cfg)
     need = workspace_size(cfg, MOE_WS_ROUTE)
@@ -180,7 +188,7 @@ def moe_route(cfg, U, W_r, b_r, W_noise, noise, topk_idx, topk_gate, logits=None
     wp, wn = _ws(ws, need)
     args = [
         _ptr(U, "U", (T, h), dt), _ptr(W_r, "W_r", (h, E), dt),
-        _ptr(b_r, "b_r", (E,), torch.float32),
+        _ptr(b_r, "b_r", (E,), torch.float32), _ptr(b_sel, "b_sel", (E,), torch.float32),
         _ptr(W_noise, "W_noise", (h, E), dt) if cfg.noisy else None,
         _ptr(noise, "noise", (T, E), torch.float32) if cfg.noisy else None,
         _ptr(topk_idx, "topk_idx", (T, k), torch.int32),
@@ -224,16 +232,39 @@ def moe_expert_ffn(cfg, X, offset, W_gate, W_up, W_down, Y, ws=None, stream=None
            "moe_expert_ffn")
 
 
-def moe_combine(cfg, U, Y, slot, topk_gate, out, stream=None):
+def moe_combine(cfg, U, Y, slot, topk_gate, out, stream=None, Y_shared=None):
     T, h, k = cfg.T, cfg.h, cfg.k
     rows = max_rows(cfg)
     dt = _elem_dtype(cfg)
     args = [
         _ptr(U, "U", (T, h), dt), _ptr(Y, "Y", (rows, h), dt),
         _ptr(slot, "slot", (T, k), torch.int32),
-        _ptr(topk_gate, "topk_gate", (T, k), torch.float32), _ptr(out, "out", (T, h), dt),
+        _ptr(topk_gate, "topk_gate", (T, k), torch.float32),
+        _ptr(Y_shared, "Y_shared", (cfg.n_shared, T, h), dt), _ptr(out, "out", (T, h), dt),
     ]
     _check(lib().moe_combine(ctypes.byref(cfg), *args, _stream(stream)), "moe_combine")
+
+
+def moe_shared_ffn(cfg, U, Ws_gate, Ws_up, Ws_down, Y_shared, ws=None, stream=None):
+    T, h, ns, fs = cfg.T, cfg.h, cfg.n_shared, cfg.f_shared
+    dt = _elem_dtype(cfg)
+    need = workspace_size(cfg, MOE_WS_SHARED_FFN)
+    ws = new_workspace(cfg, MOE_WS_SHARED_FFN, U.device) if ws is None else ws
+    wp, wn = _ws(ws, need)
+    args = [
+        _ptr(U, "U", (T, h), dt), _ptr(Ws_gate, "Ws_gate", (ns, fs, h), dt),
+        _ptr(Ws_up, "Ws_up", (ns, fs, h), dt), _ptr(Ws_down, "Ws_down", (ns, h, fs), dt),
+        _ptr(Y_shared, "Y_shared", (ns, T, h), dt),
+    ]
+    _check(lib().moe_shared_ffn(ctypes.byref(cfg), *args, wp, wn, _stream(stream)),
+           "moe_shared_ffn")
+
+
+def moe_update_bias(cfg, count, b_sel, gamma: float, stream=None):
+    E = cfg.E
+    _check(lib().moe_update_bias(ctypes.byref(cfg), _ptr(count, "count", (E,), torch.int32),
+                                 _ptr(b_sel, "b_sel", (E,), torch.float32), float(gamma),
+                                 _stream(stream)), "moe_update_bias")
 
 
 def moe_stats(cfg, count, kept, prob_sum, f=None, P=None, aux_loss=None, maxvio=None,
@@ -266,6 +297,7 @@ _AUX_SPEC = {
     "n_dropped": (lambda c, r: (1,), torch.int32),
     "X": (lambda c, r: (r, c.h), None),
     "Y": (lambda c, r: (r, c.h), None),
+    "Y_shared": (lambda c, r: (c.n_shared, c.T, c.h), None),
 }
 
 
@@ -280,11 +312,14 @@ def alloc_aux(cfg, device="cuda", fields=None) -> dict:
 
 
 def moe_layer_forward(cfg, U, W_r, b_r, W_noise, noise, W_gate, W_up, W_down, out, aux=None,
-                      stage_events=None, ws=None, stream=None):
+                      stage_events=None, ws=None, stream=None, b_sel=None, Ws_gate=None,
+                      Ws_up=None, Ws_down=None):
     """The whole layer.  aux: dict of optional output tensors (see alloc_aux).
     stage_events: list of MOE_NUM_STAGES + 1 torch.cuda.Event(enable_timing=True),
-    recorded inside the library on the same stream."""
+    recorded inside the library on the same stream.  b_sel, Ws_*: the
+    selection bias and the shared-expert weights (cfg.n_shared > 0)."""
     T, h, f, E = cfg.T, cfg.h, cfg.f, cfg.E
+    ns, fs = cfg.n_shared, cfg.f_shared
     rows = max_rows(cfg)
     dt = _elem_dtype(cfg)
     need = workspace_size(cfg, MOE_WS_LAYER)
@@ -308,11 +343,15 @@ def moe_layer_forward(cfg, U, W_r, b_r, W_noise, noise, W_gate, W_up, W_down, ou
         ev = (ctypes.c_void_p * len(handles))(*handles)
     args = [
         _ptr(U, "U", (T, h), dt), _ptr(W_r, "W_r", (h, E), dt),
-        _ptr(b_r, "b_r", (E,), torch.float32),
+        _ptr(b_r, "b_r", (E,), torch.float32), _ptr(b_sel, "b_sel", (E,), torch.float32),
         _ptr(W_noise, "W_noise", (h, E), dt) if cfg.noisy else None,
         _ptr(noise, "noise", (T, E), torch.float32) if cfg.noisy else None,
         _ptr(W_gate, "W_gate", (E, f, h), dt), _ptr(W_up, "W_up", (E, f, h), dt),
-        _ptr(W_down, "W_down", (E, h, f), dt), _ptr(out, "out", (T, h), dt),
+        _ptr(W_down, "W_down", (E, h, f), dt),
+        _ptr(Ws_gate, "Ws_gate", (ns, fs, h), dt) if ns else None,
+        _ptr(Ws_up, "Ws_up", (ns, fs, h), dt) if ns else None,
+        _ptr(Ws_down, "Ws_down", (ns, h, fs), dt) if ns else None,
+        _ptr(out, "out", (T, h), dt),
     ]
     _check(lib().moe_layer_forward(ctypes.byref(cfg), *args, ctypes.byref(a),
                                    ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None,

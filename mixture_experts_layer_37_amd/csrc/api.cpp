@@ -27,6 +27,7 @@ constexpr int64_t kMaxE = 256, kMaxK = 8;
 
 struct Dims {
   int64_t T, h, f, E, k, C, rows_max;
+  int64_t n_groups, topk_groups, ns, fs;  // group-limited selection, shared experts
   bool bf16;
 };
 
@@ -49,9 +50,29 @@ int32_t check_config(const moe_config* c) {
   if (c->E > kMaxE || c->k > kMaxK) return MOE_ERR_UNSUPPORTED;
   if (c->dtype == MOE_BF16 && (c->h % 64 != 0 || c->f % 64 != 0)) return MOE_ERR_UNSUPPORTED;
   if (c->dtype == MOE_F32 && (c->h % 4 != 0 || c->f % 4 != 0)) return MOE_ERR_UNSUPPORTED;
+  // group-limited selection
+  if (c->n_groups < 0) return MOE_ERR_INVALID_ARG;
+  if (c->n_groups > 1) {
+    if (c->n_groups > 64) return MOE_ERR_UNSUPPORTED;
+    if (c->E % c->n_groups != 0) return MOE_ERR_INVALID_ARG;
+    if (c->topk_groups < 1 || c->topk_groups > c->n_groups || c->topk_groups > c->k)
+      return MOE_ERR_INVALID_ARG;
+    if (c->topk_groups > 8) return MOE_ERR_UNSUPPORTED;
+    if (c->k > c->topk_groups * (c->E / c->n_groups)) return MOE_ERR_INVALID_ARG;
+  }
+  // shared experts
+  if (c->n_shared < 0) return MOE_ERR_INVALID_ARG;
+  if (c->n_shared > 0) {
+    if (c->n_shared > 16) return MOE_ERR_UNSUPPORTED;
+    if (c->f_shared < 1) return MOE_ERR_INVALID_ARG;
+    if (c->dtype == MOE_BF16 && c->f_shared % 64 != 0) return MOE_ERR_UNSUPPORTED;
+    if (c->dtype == MOE_F32 && c->f_shared % 4 != 0) return MOE_ERR_UNSUPPORTED;
+  }
   // every index the kernels form stays below 2^31 elements per row block
   const int64_t lim = (int64_t)1 << 31;
   if (c->T * c->k >= lim || c->h >= lim / 8 || c->f >= lim / 8) return MOE_ERR_UNSUPPORTED;
+  if (c->n_shared > 0 && (c->f_shared >= lim / 8 || c->T * c->n_shared >= lim))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -89,6 +110,10 @@ Dims dims_of(const moe_config* c) {
   d.C = Cx < d.T ? Cx : d.T;  // no expert can receive more than T assignments
   const int64_t a = d.T * d.k, b = d.E * d.C;
   d.rows_max = a < b ? a : b;
+  d.n_groups = c->n_groups > 1 ? c->n_groups : 1;
+  d.topk_groups = c->n_groups > 1 ? c->topk_groups : 1;
+  d.ns = c->n_shared;
+  d.fs = c->n_shared > 0 ? c->f_shared : 0;
   return d;
 }
 
@@ -155,10 +180,31 @@ FfnWs plan_ffn(const Dims& d, Plan& pl) {
   return w;
 }
 
+// Shared experts: one dense pass over all T rows per shared expert, through
+// the same grouped-GEMM kernels with a single "expert" (offsets {0, T}).
+struct SharedWs {
+  FfnShape fs;
+  size_t map1, map2, offs, part, A, Ys;
+};
+SharedWs plan_shared(const Dims& d, bool with_ys, Plan& pl) {
+  SharedWs w{};
+  if (d.ns == 0) return w;
+  w.fs = ffn_shape(d.T, 1, (int)d.h, (int)d.fs, (int)d.T, 1, d.bf16, device_cus());
+  w.map1 = pl.add(2 * sizeof(int32_t));
+  w.map2 = pl.add(2 * sizeof(int32_t));
+  w.offs = pl.add(2 * sizeof(int32_t));
+  w.part = pl.add((size_t)w.fs.part_slots * kPartSlotBytes);
+  const size_t T1 = (size_t)(d.T > 0 ? d.T : 1);
+  w.A = pl.add((size_t)d.ns * T1 * d.fs * elem_bytes(d));  // one intermediate per shared expert
+  w.Ys = with_ys ? pl.add((size_t)d.ns * T1 * d.h * elem_bytes(d)) : 0;
+  return w;
+}
+
 struct LayerWs {
   RouteWs route;
   DispatchWs disp;
   FfnWs ffn;
+  SharedWs sh;
   size_t idx, gate, slot, row_token, count, kept, offset, X, Y, scal;
 };
 LayerWs plan_layer(const Dims& d, int noisy, Plan& pl) {
@@ -166,6 +212,7 @@ LayerWs plan_layer(const Dims& d, int noisy, Plan& pl) {
   w.route = plan_route(d, noisy, pl);
   w.disp = plan_dispatch(d, pl);
   w.ffn = plan_ffn(d, pl);
+  w.sh = plan_shared(d, true, pl);
   const size_t tk = (size_t)(d.T > 0 ? d.T : 1) * d.k;
   const size_t rows = (size_t)(d.rows_max > 0 ? d.rows_max : 1);
   w.idx = pl.add(tk * 4);
@@ -195,8 +242,9 @@ int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP
   } while (0)
 
 int32_t run_route(const Dims& d, const moe_config* c, const RouteWs& w, const void* U,
-                  const void* W_r, const float* b_r, const void* W_noise, const float* noise,
-                  int32_t* idx, float* gate, float* logits, void* ws, hipStream_t s) {
+                  const void* W_r, const float* b_r, const float* b_sel, const void* W_noise,
+                  const float* noise, int32_t* idx, float* gate, float* logits, void* ws,
+                  hipStream_t s) {
   RouteParams p;
   p.T = (int)d.T;
   p.h = (int)d.h;
@@ -206,6 +254,9 @@ int32_t run_route(const Dims& d, const moe_config* c, const RouteWs& w, const vo
   p.gate = c->gate;
   p.U = U;
   p.b_r = b_r;
+  p.b_sel = b_sel;
+  p.n_groups = (int)d.n_groups;
+  p.topk_groups = (int)d.topk_groups;
   p.noise = c->noisy ? noise : nullptr;
   p.topk_idx = idx;
   p.topk_gate = gate;
@@ -278,6 +329,49 @@ int32_t run_down(const Dims& d, const FfnWs& w, const int32_t* offset, const voi
   return MOE_OK;
 }
 
+const char* elem_ptr(const void* base, size_t elems, const Dims& d) {
+  return static_cast<const char*>(base) + elems * elem_bytes(d);
+}
+
+// Gate/up products of every shared expert (the float32 path does the whole
+// FFN here).
+int32_t run_shared_gate_up(const Dims& d, const SharedWs& w, const void* U, const void* Wsg,
+                           const void* Wsu, const void* Wsd, void* Ys, void* ws, hipStream_t s) {
+  if (d.ns == 0 || d.T == 0) return MOE_OK;
+  int32_t* offs = at<int32_t>(ws, w.offs);
+  MOE_TRY(launch_dense_offsets((int)d.T, offs, s));
+  const size_t fh = (size_t)d.fs * d.h, th = (size_t)d.T * d.h, tf = (size_t)d.T * d.fs;
+  if (d.bf16)
+    MOE_TRY(launch_tile_map(offs, 1, w.fs.bm1, w.fs.bm2, at<int32_t>(ws, w.map1),
+                            at<int32_t>(ws, w.map2), s));
+  for (int64_t i = 0; i < d.ns; ++i) {
+    void* A = at<char>(ws, w.A) + i * tf * elem_bytes(d);
+    if (d.bf16) {
+      MOE_TRY(launch_gate_up(w.fs, U, offs, at<int32_t>(ws, w.map1), elem_ptr(Wsg, i * fh, d),
+                             elem_ptr(Wsu, i * fh, d), A, at<float>(ws, w.part), 1, (int)d.h,
+                             (int)d.fs, 1, s));
+    } else {
+      MOE_TRY(launch_ffn_f32(U, offs, elem_ptr(Wsg, i * fh, d), elem_ptr(Wsu, i * fh, d),
+                             elem_ptr(Wsd, i * fh, d), A,
+                             static_cast<char*>(Ys) + i * th * elem_bytes(d), d.T, 1, (int)d.h,
+                             (int)d.fs, s));
+    }
+  }
+  return MOE_OK;
+}
+
+int32_t run_shared_down(const Dims& d, const SharedWs& w, const void* Wsd, void* Ys, void* ws,
+                        hipStream_t s) {
+  if (d.ns == 0 || d.T == 0 || !d.bf16) return MOE_OK;
+  const size_t fh = (size_t)d.fs * d.h, th = (size_t)d.T * d.h, tf = (size_t)d.T * d.fs;
+  for (int64_t i = 0; i < d.ns; ++i)
+    MOE_TRY(launch_down(w.fs, at<char>(ws, w.A) + i * tf * elem_bytes(d), at<int32_t>(ws, w.offs),
+                        at<int32_t>(ws, w.map2), elem_ptr(Wsd, i * fh, d),
+                        static_cast<char*>(Ys) + i * th * elem_bytes(d), at<float>(ws, w.part),
+                        1, (int)d.h, (int)d.fs, 1, s));
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -320,6 +414,7 @@ int32_t moe_workspace_size(const moe_config* cfg, int32_t entry, size_t* bytes) 
     case MOE_WS_DISPATCH: plan_dispatch(d, pl); break;
     case MOE_WS_EXPERT_FFN: plan_ffn(d, pl); break;
     case MOE_WS_LAYER: plan_layer(d, cfg->noisy, pl); break;
+    case MOE_WS_SHARED_FFN: plan_shared(d, false, pl); break;
     default: return MOE_ERR_INVALID_ARG;
   }
   *bytes = pl.bytes;
@@ -327,8 +422,9 @@ int32_t moe_workspace_size(const moe_config* cfg, int32_t entry, size_t* bytes) 
 }
 
 int32_t moe_route(const moe_config* cfg, const void* U, const void* W_r, const float* b_r,
-                  const void* W_noise, const float* noise, int32_t* topk_idx, float* topk_gate,
-                  float* logits, float* prob_sum, void* ws, size_t ws_bytes, void* stream) {
+                  const float* b_sel, const void* W_noise, const float* noise,
+                  int32_t* topk_idx, float* topk_gate, float* logits, float* prob_sum,
+                  void* ws, size_t ws_bytes, void* stream) {
   int32_t st = check_config(cfg);
   if (st != MOE_OK) return st;
   const Dims d = dims_of(cfg);
@@ -339,7 +435,8 @@ int32_t moe_route(const moe_config* cfg, const void* U, const void* W_r, const f
   const RouteWs w = plan_route(d, cfg->noisy, pl);
   if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = run_route(d, cfg, w, U, W_r, b_r, W_noise, noise, topk_idx, topk_gate, logits, ws, s);
+  st = run_route(d, cfg, w, U, W_r, b_r, b_sel, W_noise, noise, topk_idx, topk_gate, logits,
+                 ws, s);
   if (st != MOE_OK) return st;
   if (prob_sum)
     return hip_status(launch_prob_reduce(at<double>(ws, w.part), w.rs.nblk, w.rs.EP, (int)d.E,
@@ -381,16 +478,46 @@ int32_t moe_expert_ffn(const moe_config* cfg, const void* X, const int32_t* offs
   return run_down(d, w, offset, W_down, Y, ws, s);
 }
 
+int32_t moe_shared_ffn(const moe_config* cfg, const void* U, const void* Ws_gate,
+                       const void* Ws_up, const void* Ws_down, void* Y_shared, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const Dims d = dims_of(cfg);
+  if (d.ns == 0) return MOE_ERR_INVALID_ARG;
+  if (!Ws_gate || !Ws_up || !Ws_down || !ws) return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (!U || !Y_shared || Y_shared == U)) return MOE_ERR_INVALID_ARG;
+  Plan pl;
+  const SharedWs w = plan_shared(d, false, pl);
+  if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_shared_gate_up(d, w, U, Ws_gate, Ws_up, Ws_down, Y_shared, ws, s);
+  if (st != MOE_OK) return st;
+  return run_shared_down(d, w, Ws_down, Y_shared, ws, s);
+}
+
 int32_t moe_combine(const moe_config* cfg, const void* U, const void* Y, const int32_t* slot,
-                    const float* topk_gate, void* out, void* stream) {
+                    const float* topk_gate, const void* Y_shared, void* out, void* stream) {
   const int32_t st = check_config(cfg);
   if (st != MOE_OK) return st;
   const Dims d = dims_of(cfg);
   if (d.T > 0 && (!U || !slot || !topk_gate || !out)) return MOE_ERR_INVALID_ARG;
   if (d.rows_max > 0 && !Y) return MOE_ERR_INVALID_ARG;
-  if (d.T > 0 && (out == U || out == Y)) return MOE_ERR_INVALID_ARG;
-  return hip_status(launch_combine(U, Y, slot, topk_gate, out, (int)d.T, (int)d.h, (int)d.k,
-                                   d.bf16, static_cast<hipStream_t>(stream)));
+  if (d.T > 0 && (out == U || out == Y || (Y_shared && out == Y_shared)))
+    return MOE_ERR_INVALID_ARG;
+  if (Y_shared && d.ns == 0) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(U, Y, slot, topk_gate, Y_shared, (int)d.ns, out, (int)d.T,
+                                   (int)d.h, (int)d.k, d.bf16,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_update_bias(const moe_config* cfg, const int32_t* count, float* b_sel, float gamma,
+                        void* stream) {
+  const int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!count || !b_sel || !(gamma >= 0.f) || isinf(gamma)) return MOE_ERR_INVALID_ARG;
+  return hip_status(
+      launch_update_bias(count, b_sel, gamma, (int)cfg->E, static_cast<hipStream_t>(stream)));
 }
 
 int32_t moe_stats(const moe_config* cfg, const int32_t* count, const int32_t* kept,
@@ -405,15 +532,18 @@ int32_t moe_stats(const moe_config* cfg, const int32_t* count, const int32_t* ke
 }
 
 int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
-                          const float* b_r, const void* W_noise, const float* noise,
-                          const void* W_gate, const void* W_up, const void* W_down, void* out,
-                          const moe_aux_outputs* aux, void* const* stage_events, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          const float* b_r, const float* b_sel, const void* W_noise,
+                          const float* noise, const void* W_gate, const void* W_up,
+                          const void* W_down, const void* Ws_gate, const void* Ws_up,
+                          const void* Ws_down, void* out, const moe_aux_outputs* aux,
+                          void* const* stage_events, void* ws, size_t ws_bytes,
+                          void* stream) {
   int32_t st = check_config(cfg);
   if (st != MOE_OK) return st;
   const Dims d = dims_of(cfg);
   if (d.T > 0 && (!U || !out)) return MOE_ERR_INVALID_ARG;
   if (!W_r || !W_gate || !W_up || !W_down || !ws) return MOE_ERR_INVALID_ARG;
+  if (d.ns > 0 && (!Ws_gate || !Ws_up || !Ws_down)) return MOE_ERR_INVALID_ARG;
   if (cfg->noisy && (!W_noise || !noise)) return MOE_ERR_INVALID_ARG;
   if (d.T > 0 && out == U) return MOE_ERR_INVALID_ARG;
   if (stage_events)
@@ -434,6 +564,7 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
   int32_t* offset = o.offset ? o.offset : at<int32_t>(ws, w.offset);
   void* X = o.X ? o.X : at<void>(ws, w.X);
   void* Y = o.Y ? o.Y : at<void>(ws, w.Y);
+  void* Ys = d.ns == 0 ? nullptr : (o.Y_shared ? o.Y_shared : at<void>(ws, w.sh.Ys));
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto mark = [&](int i) -> hipError_t {
     return stage_events ? hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s)
@@ -441,7 +572,8 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
   };
 
   MOE_TRY(mark(0));
-  st = run_route(d, cfg, w.route, U, W_r, b_r, W_noise, noise, idx, gate, o.logits, ws, s);
+  st = run_route(d, cfg, w.route, U, W_r, b_r, b_sel, W_noise, noise, idx, gate, o.logits, ws,
+                 s);
   if (st != MOE_OK) return st;
   MOE_TRY(mark(1));
   st = run_dispatch(d, cfg, w.disp, U, idx, X, row_token, slot, count, kept, offset, ws, s);
@@ -451,11 +583,16 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
   MOE_TRY(mark(2));
   st = run_gate_up(d, w.ffn, X, offset, W_gate, W_up, W_down, Y, ws, s);
   if (st != MOE_OK) return st;
+  st = run_shared_gate_up(d, w.sh, U, Ws_gate, Ws_up, Ws_down, Ys, ws, s);
+  if (st != MOE_OK) return st;
   MOE_TRY(mark(3));
   st = run_down(d, w.ffn, offset, W_down, Y, ws, s);
   if (st != MOE_OK) return st;
+  st = run_shared_down(d, w.sh, Ws_down, Ys, ws, s);
+  if (st != MOE_OK) return st;
   MOE_TRY(mark(4));
-  MOE_TRY(launch_combine(U, Y, slot, gate, out, (int)d.T, (int)d.h, (int)d.k, d.bf16, s));
+  MOE_TRY(launch_combine(U, Y, slot, gate, Ys, (int)d.ns, out, (int)d.T, (int)d.h, (int)d.k,
+                         d.bf16, s));
   MOE_TRY(mark(5));
   MOE_TRY(launch_prob_reduce(at<double>(ws, w.route.part), w.route.rs.nblk, w.route.rs.EP,
                              (int)d.E, at<double>(ws, w.route.total), o.prob_sum, s));

@@ -22,7 +22,8 @@ namespace {
 template <typename TE>
 __global__ __launch_bounds__(256) void combine_kernel(const TE* U, const TE* Y,
                                                       const int32_t* slot, const float* gate,
-                                                      TE* out, int T, int h, int k) {
+                                                      const TE* Ys, int ns, TE* out, int T, int h,
+                                                      int k) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
@@ -40,6 +41,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const TE* U, const TE* Y,
   for (int i = lane; i < nvec; i += 64) {
     float acc[V], y[V];
     Elem<TE>::unpack(ld16(u + (size_t)i * V), acc);
+    for (int q = 0; q < ns; ++q) {  // shared experts, weight 1, in order
+      Elem<TE>::unpack(ld16(Ys + ((size_t)q * T + t) * h + (size_t)i * V), y);
+#pragma unroll
+      for (int c = 0; c < V; ++c) acc[c] += y[c];
+    }
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       if (sl[r] < 0) continue;
@@ -88,20 +94,48 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsParams p) {
   }
 }
 
+// Loss-free balancing bias step (page "MoE 与专家并行", section
+// "无辅助损失的负载均衡", equations e_i and b_i): e = mean count - count[e],
+// b[e] += gamma * sign(e).  The mean is compared exactly: E * count[e]
+// against the integer total.
+__global__ __launch_bounds__(256) void update_bias_kernel(const int32_t* count, float* b,
+                                                          float gamma, int E) {
+  __shared__ long long s_tot[256];
+  const int e = threadIdx.x;
+  s_tot[e] = e < E ? (long long)count[e] : 0;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (e < w) s_tot[e] += s_tot[e + w];
+    __syncthreads();
+  }
+  if (e < E) {
+    const long long scaled = (long long)E * count[e];  // E * c_e vs the total
+    const float step = scaled < s_tot[0] ? gamma : (scaled > s_tot[0] ? -gamma : 0.f);
+    b[e] += step;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const void* U, const void* Y, const int32_t* slot, const float* gate,
-                          void* out, int T, int h, int k, int bf16_, hipStream_t s) {
+                          const void* Ys, int ns, void* out, int T, int h, int k, int bf16_,
+                          hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (!Ys) ns = 0;
   dim3 grid((T + 3) / 4);
   if (bf16_)
     hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(256), 0, s, static_cast<const bf16*>(U),
-                       static_cast<const bf16*>(Y), slot, gate, static_cast<bf16*>(out), T, h,
-                       k);
+                       static_cast<const bf16*>(Y), slot, gate, static_cast<const bf16*>(Ys),
+                       ns, static_cast<bf16*>(out), T, h, k);
   else
     hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s,
                        static_cast<const float*>(U), static_cast<const float*>(Y), slot, gate,
-                       static_cast<float*>(out), T, h, k);
+                       static_cast<const float*>(Ys), ns, static_cast<float*>(out), T, h, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_update_bias(const int32_t* count, float* b, float gamma, int E, hipStream_t s) {
+  hipLaunchKernelGGL(update_bias_kernel, dim3(1), dim3(256), 0, s, count, b, gamma, E);
   return hipGetLastError();
 }
 

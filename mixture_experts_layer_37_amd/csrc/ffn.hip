@@ -517,6 +517,15 @@ __global__ void tile_map_kernel(const int32_t* offset, int E, int bm1, int bm2, 
   m2[E] = b;
 }
 
+// Offsets of a dense pass over all T rows as one "expert" (the shared
+// experts): {0, T}.
+__global__ void dense_offsets_kernel(int T, int32_t* offset) {
+  if (threadIdx.x == 0) {
+    offset[0] = 0;
+    offset[1] = T;
+  }
+}
+
 int round8(int x) { return (x + 7) & ~7; }
 
 template <bool GATEUP>
@@ -566,6 +575,11 @@ FfnShape ffn_shape(int64_t rows_max, int E, int h, int f, int T, int k, int bf16
 hipError_t launch_tile_map(const int32_t* offset, int E, int bm1, int bm2, int32_t* map1,
                            int32_t* map2, hipStream_t s) {
   hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(64), 0, s, offset, E, bm1, bm2, map1, map2);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_offsets(int T, int32_t* offset, hipStream_t s) {
+  hipLaunchKernelGGL(dense_offsets_kernel, dim3(1), dim3(64), 0, s, T, offset);
   return hipGetLastError();
 }
 

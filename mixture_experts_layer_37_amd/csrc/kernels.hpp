@@ -14,6 +14,9 @@ struct RouteParams {
   int gate;   // 0 raw, 1 renorm
   const void* U;
   const float* b_r;
+  const float* b_sel;    // [E] selection-only bias, or NULL
+  int n_groups;          // > 1: group-limited selection over n_groups groups
+  int topk_groups;       // groups a token may use
   const float* noise;
   const void* Wt;    // bf16: W_r transposed to [EP][h], zero rows past E; f32: W_r [h][E]
   const void* Wnt;   // same for W_noise (noisy only)
@@ -76,6 +79,8 @@ constexpr size_t kPartSlotBytes = 256 * 256 * sizeof(float);
 FfnShape ffn_shape(int64_t rows_max, int E, int h, int f, int T, int k, int bf16, int ncu);
 hipError_t launch_tile_map(const int32_t* offset, int E, int bm1, int bm2, int32_t* map1,
                            int32_t* map2, hipStream_t s);
+// offset = {0, T}: all T rows as one expert (the shared experts' dense pass)
+hipError_t launch_dense_offsets(int T, int32_t* offset, hipStream_t s);
 // part: room for fs.part_slots K-split partial tiles (kPartSlotBytes each);
 // each GEMM is followed by the reduction of its split tail tiles
 hipError_t launch_gate_up(const FfnShape& fs, const void* X, const int32_t* offset,
@@ -86,8 +91,12 @@ hipError_t launch_down(const FfnShape& fs, const void* A, const int32_t* offset,
                        int f, int bf16, hipStream_t s);
 
 // ---------------------------------------------------------------- combine, stats
+// Ys: NULL or [ns][T][h] shared-expert outputs added to the residual
 hipError_t launch_combine(const void* U, const void* Y, const int32_t* slot, const float* gate,
-                          void* out, int T, int h, int k, int bf16, hipStream_t s);
+                          const void* Ys, int ns, void* out, int T, int h, int k, int bf16,
+                          hipStream_t s);
+// b[e] += gamma * sign(mean count - count[e])
+hipError_t launch_update_bias(const int32_t* count, float* b, float gamma, int E, hipStream_t s);
 
 struct StatsParams {
   int T, E, k;

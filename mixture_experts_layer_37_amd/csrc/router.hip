@@ -86,20 +86,29 @@ __device__ void route_epilogue(const float* L, const float* Ln, double (*Ps)[EP]
 #pragma unroll
       for (int j = 0; j < J; ++j) pacc[j] += (double)(s[j] / S);
     }
-    // top-k on the logits: larger value first, lower index on ties
-    bool taken[J];
+    // Selection keys.  Plain routing takes the top-k on the logits (the same
+    // order as the scores).  With a selection bias or groups the keys are the
+    // scores plus the bias (the bias decides membership only), and with
+    // groups only experts of the topk_groups best groups compete, a group
+    // scoring the sum of its k / topk_groups best keys.
+    const bool keyed = p.b_sel != nullptr || p.n_groups > 1;
+    float key[J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) taken[j] = false;
-    int my_idx = 0;
-    float my_s = 0.f, gsum = 0.f;
-    for (int r = 0; r < k; ++r) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
+    for (int j = 0; j < J; ++j) {
+      const int e = lane + 64 * j;
+      key[j] = v[j];
+      if (keyed) key[j] = e < E ? s[j] + (p.b_sel ? p.b_sel[e] : 0.f) : -INFINITY;
+    }
+    // arg-max over the keys of the experts with allow[j] set: larger key
+    // first, lower expert index on ties (wave-uniform result)
+    auto wave_argmax = [&](const bool (&allow)[J], float& bv, int& be) {
+      bv = -INFINITY;
+      be = 0x7fffffff;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int e = lane + 64 * j;
-        if (e < E && !taken[j] && (v[j] > bv || (v[j] == bv && e < be))) {
-          bv = v[j];
+        if (allow[j] && (key[j] > bv || (key[j] == bv && e < be))) {
+          bv = key[j];
           be = e;
         }
       }
@@ -112,10 +121,78 @@ __device__ void route_epilogue(const float* L, const float* Ln, double (*Ps)[EP]
           be = oe;
         }
       }
+    };
+    if (p.n_groups > 1) {
+      const int gsize = E / p.n_groups, q = k / p.topk_groups;
+      float topv[8];
+      int topg[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        topv[i] = -INFINITY;
+        topg[i] = 0x7fffffff;
+      }
+      for (int g = 0; g < p.n_groups; ++g) {
+        bool allow[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const int e = lane + 64 * j;
+          allow[j] = e >= g * gsize && e < (g + 1) * gsize;
+        }
+        float gs = 0.f;
+        for (int r = 0; r < q; ++r) {
+          float bv;
+          int be;
+          wave_argmax(allow, bv, be);
+          gs += bv;
+#pragma unroll
+          for (int j = 0; j < J; ++j)
+            if (lane + 64 * j == be) allow[j] = false;
+        }
+        // keep the topk_groups best (sum, group) pairs; an equal sum ranks
+        // after the earlier (lower) group
+        float cv = gs;
+        int cg = g;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (i < p.topk_groups && cv > topv[i]) {
+            const float tv = topv[i];
+            const int tg = topg[i];
+            topv[i] = cv;
+            topg[i] = cg;
+            cv = tv;
+            cg = tg;
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int g = (lane + 64 * j) / gsize;
+        bool in = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) in |= (i < p.topk_groups && topg[i] == g);
+        if (!in) key[j] = -INFINITY;
+      }
+    }
+    // top-k on the keys
+    bool avail[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) avail[j] = lane + 64 * j < E && (!keyed || key[j] > -INFINITY);
+    int my_idx = 0;
+    float my_s = 0.f, gsum = 0.f;
+    for (int r = 0; r < k; ++r) {
+      float bv;
+      int be;
+      wave_argmax(avail, bv, be);
 #pragma unroll
       for (int j = 0; j < J; ++j)
-        if (lane + 64 * j == be) taken[j] = true;
-      const float sv = (p.score == 0) ? expf(bv - m) / Z : 1.f / (1.f + expf(-bv));
+        if (lane + 64 * j == be) avail[j] = false;
+      // the gate uses the score of the chosen expert, never its key
+      float mine = 0.f;
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (j == (be >> 6)) mine = s[j];
+      const float sv = keyed ? __shfl(mine, be & 63, 64)
+                             : ((p.score == 0) ? expf(bv - m) / Z : 1.f / (1.f + expf(-bv)));
       gsum += sv;
       if (lane == r) {
         my_idx = be;

@@ -34,6 +34,13 @@ class Workload:
     cap_mode: str = "assignments"
     fill: str = "rank_major"
     min_capacity: int = 0
+    # DeepSeek-V3 parts (0: off): group-limited selection, shared experts and
+    # the variance of the selection-only expert bias b_sel
+    n_groups: int = 0
+    topk_groups: int = 0
+    n_shared: int = 0
+    f_shared: int = 0
+    sel_bias_var: float = 0.0
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -56,6 +63,13 @@ WORKLOADS = {
     "noisy_long_bf16": Workload("noisy_long_bf16", T=32768, h=4096, f=14336, E=64, k=2,
                                 dtype="bf16", score="softmax", gate="renorm",
                                 capacity_factor=1.0, noisy=True),
+    # the DeepSeek-V3 shape with its layer parts: 1 shared expert of the same
+    # width, node-limited selection (8 groups, at most 4 per token) and a
+    # selection bias with standard deviation 0.01
+    "deepseek_v3_full_bf16": Workload("deepseek_v3_full_bf16", T=4096, h=7168, f=2048, E=256,
+                                      k=8, dtype="bf16", score="sigmoid", gate="renorm",
+                                      capacity_factor=2.0, n_groups=8, topk_groups=4,
+                                      n_shared=1, f_shared=2048, sel_bias_var=1e-4),
 }
 
 WORKLOAD_ORDER = ["tiny_f32", "mixtral_bf16", "switch_bf16", "deepseek_v3_bf16",
@@ -78,7 +92,10 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", with_experts: bool = T
 
     Expert weights are drawn one expert at a time so that large workloads never
     hold a float32 copy of all weights.  Shapes: U [T, h]; W_r, W_noise [h, E];
-    b_r [E] fp32; noise [T, E] fp32; W_gate, W_up [E, f, h]; W_down [E, h, f].
+    b_r [E] fp32; noise [T, E] fp32; b_sel [E] fp32; W_gate, W_up [E, f, h];
+    W_down [E, h, f]; Ws_gate, Ws_up [n_shared, f_shared, h]; Ws_down
+    [n_shared, h, f_shared].  Inputs a workload does not use are None and draw
+    nothing, so adding a part never changes the other inputs.
     """
     dev = torch.device(device)
     gen = torch.Generator(device=dev)
@@ -94,6 +111,8 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", with_experts: bool = T
     else:
         x["W_noise"] = None
         x["noise"] = None
+    x["b_sel"] = (_normal((w.E,), w.sel_bias_var, gen, dev, torch.float32)
+                  if w.sel_bias_var > 0 else None)
     if with_experts:
         x["W_gate"] = torch.empty((w.E, w.f, w.h), dtype=dt, device=dev)
         x["W_up"] = torch.empty((w.E, w.f, w.h), dtype=dt, device=dev)
@@ -102,4 +121,14 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", with_experts: bool = T
             x["W_gate"][e] = _normal((w.f, w.h), 1.0 / w.h, gen, dev, dt)
             x["W_up"][e] = _normal((w.f, w.h), 1.0 / w.h, gen, dev, dt)
             x["W_down"][e] = _normal((w.h, w.f), 1.0 / w.f, gen, dev, dt)
+    x["Ws_gate"] = x["Ws_up"] = x["Ws_down"] = None
+    if with_experts and w.n_shared > 0:
+        fs = w.f_shared
+        x["Ws_gate"] = torch.empty((w.n_shared, fs, w.h), dtype=dt, device=dev)
+        x["Ws_up"] = torch.empty((w.n_shared, fs, w.h), dtype=dt, device=dev)
+        x["Ws_down"] = torch.empty((w.n_shared, w.h, fs), dtype=dt, device=dev)
+        for i in range(w.n_shared):
+            x["Ws_gate"][i] = _normal((fs, w.h), 1.0 / w.h, gen, dev, dt)
+            x["Ws_up"][i] = _normal((fs, w.h), 1.0 / w.h, gen, dev, dt)
+            x["Ws_down"][i] = _normal((w.h, fs), 1.0 / fs, gen, dev, dt)
     return x

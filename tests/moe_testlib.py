@@ -74,13 +74,64 @@ def f64(t):
 def run_layer(w, x, fields=None, stage_events=None):
     cfg = B.make_config(w)
     dev = x["U"].device
+    if fields is None:
+        fields = [n for n in B.AUX_FIELDS if n != "Y_shared" or w.n_shared > 0]
     aux = B.alloc_aux(cfg, dev, fields)
     out = torch.empty((w.T, w.h), dtype=I.torch_dtype(w), device=dev)
     B.moe_layer_forward(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], x["noise"], x["W_gate"],
-                        x["W_up"], x["W_down"], out, aux=aux, stage_events=stage_events)
+                        x["W_up"], x["W_down"], out, aux=aux, stage_events=stage_events,
+                        b_sel=x.get("b_sel"), Ws_gate=x.get("Ws_gate"), Ws_up=x.get("Ws_up"),
+                        Ws_down=x.get("Ws_down"))
     torch.cuda.synchronize()
     aux["out"] = out
     return cfg, aux
+
+
+def keyed(w) -> bool:
+    """True when selection runs on the keys s + b_sel (bias or groups), not the logits."""
+    return w.sel_bias_var > 0 or w.n_groups > 1
+
+
+# Selection keys are float32 sigmoid/softmax scores plus the bias on the GPU;
+# the oracle recomputes them in float64 from the same logits.  Their
+# difference stays far below this margin.
+KEY_MARGIN = 2e-6
+
+
+def key_margins(w, s: np.ndarray, b_sel) -> np.ndarray:
+    """Per token: the smallest gap that decides its selection under keys s + b.
+
+    Gaps between consecutive keys among the k + 1 best allowed experts, and,
+    with groups, between the topk_groups-th and the next group score.
+    """
+    keys = O.selection_keys(s, b_sel)
+    T, E = keys.shape
+    allowed = np.ones_like(keys, dtype=bool)
+    margin = np.full(T, np.inf)
+    if w.n_groups > 1:
+        q = max(1, w.k // w.topk_groups)
+        allowed = O.group_limited_mask(keys, w.n_groups, w.topk_groups, q)
+        gs = E // w.n_groups
+        gscore = -np.sort(-keys.reshape(T, w.n_groups, gs), axis=2)[:, :, :q].sum(axis=2)
+        gsorted = -np.sort(-gscore, axis=1)
+        if w.topk_groups < w.n_groups:
+            margin = np.minimum(margin, gsorted[:, w.topk_groups - 1] - gsorted[:, w.topk_groups])
+    masked = np.where(allowed, keys, -np.inf)
+    srt = -np.sort(-masked, axis=1)[:, : w.k + 1]
+    gaps = srt[:, :-1] - srt[:, 1:]
+    gaps = np.where(np.isfinite(gaps), gaps, np.inf)
+    return np.minimum(margin, gaps.min(axis=1))
+
+
+def route_given_selection(w, H, idx) -> dict:
+    """The oracle's gates, fill and statistics for a given selection idx."""
+    s = O.scores(H, ORACLE_MODE[w.score])
+    C = oracle_capacity(w)
+    fr = O.fill(idx, w.E, C, ORACLE_MODE[w.fill])
+    r = {"logits": H, "s": s, "idx": idx, "gate": O.gates(s, idx, ORACLE_MODE[w.gate])}
+    r.update(fr)
+    r.update(O.load_stats(s, idx, fr, ORACLE_MODE[w.score]))
+    return r
 
 
 def oracle_capacity(w) -> int:
@@ -88,11 +139,29 @@ def oracle_capacity(w) -> int:
                       w.min_capacity)
 
 
-def check_routing_shared_logits(w, g: dict) -> dict:
-    """Oracle routing from the GPU's float32 logits; bit-exact integer outputs."""
+def check_routing_shared_logits(w, g: dict, b_sel=None) -> dict:
+    """Oracle routing from the GPU's float32 logits; bit-exact integer outputs.
+
+    With selection keys (bias or groups), tokens whose deciding key gap is
+    below KEY_MARGIN may choose differently (the keys involve float32
+    transcendentals); they are reported, every other token must agree, and
+    the dispatch is then checked bit for bit against the oracle's fill of the
+    GPU's own selection.
+    """
     C = oracle_capacity(w)
     H = to_np(g["logits"]).astype(np.float64)
-    r = O.route(H, w.k, ORACLE_MODE[w.score], ORACLE_MODE[w.gate], C, ORACLE_MODE[w.fill])
+    b = None if b_sel is None else f64(b_sel)
+    r = O.route(H, w.k, ORACLE_MODE[w.score], ORACLE_MODE[w.gate], C, ORACLE_MODE[w.fill],
+                b, max(1, w.n_groups), max(1, w.topk_groups))
+    if keyed(w):
+        idx_g = to_np(g["topk_idx"]).astype(np.int64)
+        margin = key_margins(w, r["s"], b)
+        mism = (idx_g != r["idx"]).any(axis=1)
+        clear = margin > KEY_MARGIN
+        assert not (mism & clear).any(), f"{int((mism & clear).sum())} clear tokens differ"
+        r = route_given_selection(w, H, idx_g)
+        r["near_ties"] = int((~clear).sum())
+        r["flipped"] = int(mism.sum())
     np.testing.assert_array_equal(to_np(g["topk_idx"]), r["idx"], err_msg="topk_idx")
     np.testing.assert_array_equal(to_np(g["count"]), r["count"], err_msg="count")
     np.testing.assert_array_equal(to_np(g["kept"]), r["kept"], err_msg="kept")
@@ -131,11 +200,19 @@ def check_logits_end_to_end(w, g: dict, x_cpu: dict, tokens=None) -> dict:
     Hg = to_np(g["logits"]).astype(np.float64)[tok]
     err = np.abs(H - Hg).max()
     assert err <= LOGIT_ATOL, f"logits differ by {err}"
-    idx_o = O.select_topk(H, w.k)
     idx_g = to_np(g["topk_idx"])[tok]
-    srt = -np.sort(-H, axis=1)
-    gaps = np.diff(-srt[:, : w.k + 1], axis=1) if w.k < w.E else np.diff(-srt, axis=1)
-    margin = np.abs(gaps).min(axis=1) if gaps.size else np.full(H.shape[0], np.inf)
+    if keyed(w):
+        b = f64(x_cpu.get("b_sel"))
+        C = oracle_capacity(w)
+        idx_o = O.route(H, w.k, ORACLE_MODE[w.score], ORACLE_MODE[w.gate], C,
+                        ORACLE_MODE[w.fill], b, max(1, w.n_groups), max(1, w.topk_groups))["idx"]
+        # scores move by at most the logit error (their slope is at most 1)
+        margin = key_margins(w, O.scores(H, ORACLE_MODE[w.score]), b)
+    else:
+        idx_o = O.select_topk(H, w.k)
+        srt = -np.sort(-H, axis=1)
+        gaps = np.diff(-srt[:, : w.k + 1], axis=1) if w.k < w.E else np.diff(-srt, axis=1)
+        margin = np.abs(gaps).min(axis=1) if gaps.size else np.full(H.shape[0], np.inf)
     clear = margin > 2 * LOGIT_ATOL
     mism = (idx_o != idx_g).any(axis=1)
     assert not (mism & clear).any(), f"{int((mism & clear).sum())} clear tokens routed differently"
@@ -184,14 +261,22 @@ def check_outputs_small(w, g: dict, x_cpu: dict, r: dict):
     tol = out_tol(w)
     ey = row_rel_err(to_np(g["Y"])[:rows], Y)
     assert ey <= tol, f"Y rel err {ey}"
-    out = O.combine(U, Y, r["slot"], r["gate"])
+    Ys = None
+    if w.n_shared > 0:
+        Ys = O.shared_expert_outputs(U, f64(x_cpu["Ws_gate"]), f64(x_cpu["Ws_up"]),
+                                     f64(x_cpu["Ws_down"]))
+        if "Y_shared" in g:
+            for i in range(w.n_shared):
+                es = row_rel_err(to_np(g["Y_shared"])[i], Ys[i])
+                assert es <= tol, f"Y_shared[{i}] rel err {es}"
+    out = O.combine(U, Y, r["slot"], r["gate"], Ys)
     eo = row_rel_err(to_np(g["out"]), out)
     ed = delta_err(w, f64(g["out"]), U, out)
     assert eo <= tol, f"out rel err {eo}"
     assert ed <= tol, f"out - u rel err {ed}"
     # fully dropped tokens return their residual bit for bit
     full = (r["slot"] < 0).all(axis=1)
-    if full.any():
+    if full.any() and w.n_shared == 0:
         np.testing.assert_array_equal(to_np(g["out"])[full], to_np(x_cpu["U"])[full])
     return {"Y": ey, "out": eo, "delta": ed}
 

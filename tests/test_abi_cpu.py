@@ -87,6 +87,18 @@ def cfg_of(**kw):
     (dict(capacity_factor=float("inf")), B.MOE_ERR_INVALID_ARG),
     (dict(capacity_factor=1e-9), B.MOE_ERR_INVALID_ARG),
     (dict(min_capacity=-1), B.MOE_ERR_INVALID_ARG),
+    # group-limited selection and shared experts
+    (dict(n_groups=3, topk_groups=1), B.MOE_ERR_INVALID_ARG),      # 3 does not divide E = 8
+    (dict(n_groups=4, topk_groups=0), B.MOE_ERR_INVALID_ARG),
+    (dict(n_groups=4, topk_groups=3), B.MOE_ERR_INVALID_ARG),      # more groups than k = 2
+    (dict(n_groups=4, topk_groups=5), B.MOE_ERR_INVALID_ARG),      # more than n_groups
+    (dict(n_groups=4, topk_groups=1, k=4), B.MOE_ERR_INVALID_ARG),  # 4 > 1 group of 2
+    (dict(E=256, n_groups=128, topk_groups=1), B.MOE_ERR_UNSUPPORTED),
+    (dict(n_groups=-1), B.MOE_ERR_INVALID_ARG),
+    (dict(n_shared=1, f_shared=0), B.MOE_ERR_INVALID_ARG),
+    (dict(n_shared=1, f_shared=96), B.MOE_ERR_UNSUPPORTED),
+    (dict(n_shared=17, f_shared=64), B.MOE_ERR_UNSUPPORTED),
+    (dict(n_shared=-1), B.MOE_ERR_INVALID_ARG),
 ])
 def test_invalid_configs(kw, code):
     cfg = cfg_of(**kw)
@@ -94,7 +106,7 @@ def test_invalid_configs(kw, code):
     assert status("moe_capacity", ctypes.byref(cfg), ctypes.byref(v)) == code
     sz = ctypes.c_size_t()
     assert status("moe_workspace_size", ctypes.byref(cfg), 3, ctypes.byref(sz)) == code
-    assert status("moe_layer_forward", ctypes.byref(cfg), *([None] * 9), None, None, None, 0,
+    assert status("moe_layer_forward", ctypes.byref(cfg), *([None] * 13), None, None, None, 0,
                   None) == code
 
 
@@ -111,34 +123,58 @@ def test_bad_enums_and_null_pointers():
     assert status("moe_workspace_size", ctypes.byref(cfg), 9, ctypes.byref(sz)) == B.MOE_ERR_INVALID_ARG
     # NULL required pointers are rejected before anything is launched
     fake = ctypes.c_void_p(0x1000)
-    assert status("moe_route", ctypes.byref(cfg), None, fake, None, None, None, fake, fake,
-                  None, None, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    assert status("moe_route", ctypes.byref(cfg), None, fake, None, None, None, None, fake,
+                  fake, None, None, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
     assert status("moe_dispatch", ctypes.byref(cfg), fake, fake, fake, fake, fake, None, fake,
                   fake, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
     assert status("moe_expert_ffn", ctypes.byref(cfg), fake, fake, None, fake, fake, fake, fake,
                   1 << 30, None) == B.MOE_ERR_INVALID_ARG
-    assert status("moe_combine", ctypes.byref(cfg), fake, fake, None, fake, fake,
+    assert status("moe_combine", ctypes.byref(cfg), fake, fake, None, fake, None, fake,
                   None) == B.MOE_ERR_INVALID_ARG
-    assert status("moe_combine", ctypes.byref(cfg), fake, fake, fake, fake, fake,
+    assert status("moe_combine", ctypes.byref(cfg), fake, fake, fake, fake, None, fake,
                   None) == B.MOE_ERR_INVALID_ARG  # out aliases U
+    other = ctypes.c_void_p(0x3000)
+    assert status("moe_combine", ctypes.byref(cfg), fake, other, fake, other, other,
+                  ctypes.c_void_p(0x4000), None) == B.MOE_ERR_INVALID_ARG  # no shared experts
+    # shared experts need n_shared > 0 and their weights
+    assert status("moe_shared_ffn", ctypes.byref(cfg), fake, fake, fake, fake, other, fake,
+                  1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    scfg = cfg_of(n_shared=1, f_shared=64)
+    assert status("moe_shared_ffn", ctypes.byref(scfg), fake, None, fake, fake, other, fake,
+                  1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    assert status("moe_layer_forward", ctypes.byref(scfg), fake, fake, None, None, None, None,
+                  fake, fake, fake, None, None, None, other, None, None, fake, 1 << 30,
+                  None) == B.MOE_ERR_INVALID_ARG
+    # the bias step needs a finite, non-negative gamma
+    for gamma in (-1e-3, float("nan"), float("inf")):
+        assert status("moe_update_bias", ctypes.byref(cfg), fake, other, ctypes.c_float(gamma),
+                      None) == B.MOE_ERR_INVALID_ARG
+    assert status("moe_update_bias", ctypes.byref(cfg), None, other, ctypes.c_float(1e-3),
+                  None) == B.MOE_ERR_INVALID_ARG
     assert status("moe_stats", ctypes.byref(cfg), None, fake, fake, None, None, None, None,
                   None, None) == B.MOE_ERR_INVALID_ARG
     # noisy routing without the noise draws
     ncfg = cfg_of(noisy=True)
-    assert status("moe_route", ctypes.byref(ncfg), fake, fake, None, fake, None, fake, fake,
-                  None, None, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    assert status("moe_route", ctypes.byref(ncfg), fake, fake, None, None, fake, None, fake,
+                  fake, None, None, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
 
 
 def test_undersized_workspace_is_rejected():
     cfg = cfg_of()
     fake = ctypes.c_void_p(0x1000)
     need = B.workspace_size(cfg, B.MOE_WS_LAYER)
-    assert status("moe_layer_forward", ctypes.byref(cfg), fake, fake, None, None, None, fake,
-                  fake, fake, ctypes.c_void_p(0x2000), None, None, fake, need - 1,
-                  None) == B.MOE_ERR_WORKSPACE
+    assert status("moe_layer_forward", ctypes.byref(cfg), fake, fake, None, None, None, None,
+                  fake, fake, fake, None, None, None, ctypes.c_void_p(0x2000), None, None, fake,
+                  need - 1, None) == B.MOE_ERR_WORKSPACE
     need = B.workspace_size(cfg, B.MOE_WS_ROUTE)
-    assert status("moe_route", ctypes.byref(cfg), fake, fake, None, None, None, fake, fake,
-                  None, None, fake, need - 1, None) == B.MOE_ERR_WORKSPACE
+    assert status("moe_route", ctypes.byref(cfg), fake, fake, None, None, None, None, fake,
+                  fake, None, None, fake, need - 1, None) == B.MOE_ERR_WORKSPACE
+    scfg = cfg_of(n_shared=2, f_shared=128)
+    need = B.workspace_size(scfg, B.MOE_WS_SHARED_FFN)
+    assert need > 0
+    assert B.workspace_size(scfg, B.MOE_WS_LAYER) > B.workspace_size(cfg, B.MOE_WS_LAYER)
+    assert status("moe_shared_ffn", ctypes.byref(scfg), fake, fake, fake, fake,
+                  ctypes.c_void_p(0x2000), fake, need - 1, None) == B.MOE_ERR_WORKSPACE
 
 
 def test_status_strings():

@@ -97,6 +97,77 @@ def test_edge_cases(name):
         assert r["C"] == 40
 
 
+# DeepSeek-V3 parts on small shapes: selection bias, group-limited selection,
+# shared experts (bf16 and the float32 path), each checked completely.
+V3 = {
+    "v3_small": L.SMALL["deepseek_small"].replace(n_groups=8, topk_groups=4, n_shared=1,
+                                                  f_shared=192, sel_bias_var=1e-4),
+    "v3_bias_only": L.SMALL["deepseek_small"].replace(sel_bias_var=1e-3),
+    "v3_groups_softmax": L.SMALL["mixtral_small"].replace(n_groups=4, topk_groups=2),
+    "v3_groups_raw_drops": L.SMALL["switch_small"].replace(k=2, n_groups=4, topk_groups=1,
+                                                           sel_bias_var=1e-2),
+    "v3_shared2_bf16": L.SMALL["mixtral_small"].replace(n_shared=2, f_shared=128),
+    "v3_shared_f32": L.SMALL["tiny_f32"].replace(n_shared=2, f_shared=64, n_groups=2,
+                                                 topk_groups=1, sel_bias_var=1e-3),
+}
+
+
+@pytest.mark.parametrize("name", list(V3))
+def test_v3_parts_small(name):
+    w = V3[name]
+    L.log(f"[v3] {name} {w}")
+    x = I.make_inputs(w, seed=5, device=DEV)
+    _, g = L.run_layer(w, x)
+    xc = cpu_copy(x)
+    r = L.check_routing_shared_logits(w, g, x["b_sel"])
+    L.check_stats(w, g, r)
+    L.check_logits_end_to_end(w, g, xc)
+    L.check_outputs_small(w, g, xc, r)
+    if w.n_groups > 1:  # every token stays inside topk_groups groups
+        grp = L.to_np(g["topk_idx"]) // (w.E // w.n_groups)
+        assert max(len(set(row)) for row in grp.tolist()) <= w.topk_groups
+
+
+def test_shared_ffn_and_combine_staged():
+    w = V3["v3_small"]
+    L.log("[v3] staged shared experts and combine")
+    x = I.make_inputs(w, seed=6, device=DEV)
+    cfg, g = L.run_layer(w, x)
+    Ys = torch.empty((w.n_shared, w.T, w.h), dtype=I.torch_dtype(w), device=DEV)
+    B.moe_shared_ffn(cfg, x["U"], x["Ws_gate"], x["Ws_up"], x["Ws_down"], Ys)
+    out = torch.empty_like(g["out"])
+    B.moe_combine(cfg, x["U"], g["Y"], g["slot"], g["topk_gate"], out, Y_shared=Ys)
+    idx = torch.empty_like(g["topk_idx"])
+    gate = torch.empty_like(g["topk_gate"])
+    B.moe_route(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], x["noise"], idx, gate,
+                b_sel=x["b_sel"])
+    torch.cuda.synchronize()
+    assert torch.equal(Ys, g["Y_shared"])
+    assert torch.equal(out, g["out"])
+    assert torch.equal(idx, g["topk_idx"]) and torch.equal(gate, g["topk_gate"])
+
+
+def test_update_bias():
+    w = V3["v3_small"]
+    cfg = B.make_config(w)
+    rng = np.random.default_rng(12)
+    for trial in range(3):
+        count = rng.integers(0, 300, w.E).astype(np.int32)
+        if trial == 1:
+            count[:] = 40  # every expert at the mean: nothing moves
+        if trial == 2:
+            count[: w.E // 2] = 10
+            count[w.E // 2:] = 30  # mean 20 exactly
+        b0 = rng.normal(0, 0.01, w.E).astype(np.float32)
+        b = torch.from_numpy(b0.copy()).to(DEV)
+        B.moe_update_bias(cfg, torch.from_numpy(count).to(DEV), b, 1e-3)
+        torch.cuda.synchronize()
+        ref = O.update_bias(b0, count, 1e-3)
+        # one float32 addition of +-gamma or 0
+        want = (b0 + (ref - b0).astype(np.float32)).astype(np.float32)
+        np.testing.assert_array_equal(L.to_np(b), want)
+
+
 # Shapes whose last round of tiles is short enough that the grouped GEMM cuts
 # the tail tiles into K chunks and sums their float32 partials afterwards.
 KSPLIT = {
@@ -194,20 +265,19 @@ def test_staged_calls_match_layer(name):
 
 
 # ----------------------------------------------------------------- full-size workloads
-@pytest.mark.parametrize("name", I.WORKLOAD_ORDER)
+@pytest.mark.parametrize("name", I.WORKLOAD_ORDER + ["deepseek_v3_full_bf16"])
 def test_layer_full_size(name):
     w = I.WORKLOADS[name]
     L.log(f"[full] {name} {w}")
     x = I.make_inputs(w, seed=0, device=DEV)
     cfg, g = L.run_layer(w, x)
     L.log("  gpu done")
-    # routing on every token from the GPU's logits (bit-exact), and the
-    # oracle's own logits on every token (near-ties excepted)
-    r = L.check_routing_shared_logits(w, g)
+    # routing on every token from the GPU's logits (bit-exact; with selection
+    # keys, near-ties reported), and the oracle's own logits on every token
+    r = L.check_routing_shared_logits(w, g, x["b_sel"])
     L.check_stats(w, g, r)
-    xs = {"U": x["U"].cpu(), "W_r": x["W_r"].cpu(), "b_r": None if x["b_r"] is None else x["b_r"].cpu(),
-          "W_noise": None if x["W_noise"] is None else x["W_noise"].cpu(),
-          "noise": None if x["noise"] is None else x["noise"].cpu()}
+    xs = {n: (None if x[n] is None else x[n].cpu())
+          for n in ("U", "W_r", "b_r", "W_noise", "noise", "b_sel")}
     info = L.check_logits_end_to_end(w, g, xs)
     L.log(f"  routing ok: drops={r['n_dropped']} near_ties={info['near_ties']} "
           f"flipped={info['flipped']} logit_err={info['logit_err']:.2e}")
@@ -218,7 +288,8 @@ def test_layer_full_size(name):
     # combine on every token from the GPU's expert outputs (float64 reference)
     U = L.f64(xs["U"])
     Yg = L.f64(g["Y"][:rows])
-    out_ref = O.combine(U, Yg, r["slot"], r["gate"])
+    Ysg = L.f64(g["Y_shared"]) if w.n_shared > 0 else None
+    out_ref = O.combine(U, Yg, r["slot"], r["gate"], Ysg)
     eo = L.row_rel_err(L.to_np(g["out"]), out_ref)
     ed = L.delta_err(w, L.f64(g["out"]), U, out_ref)
     assert eo <= L.out_tol(w) and ed <= L.out_tol(w), (eo, ed)
@@ -230,4 +301,11 @@ def test_layer_full_size(name):
             ref = O.swiglu_expert(U[r["row_token"][row]][None, :], Wg, Wu, Wd)
             worst = max(worst, L.row_rel_err(Yg[row][None, :], ref))
     assert worst <= L.out_tol(w), worst
+    if w.n_shared > 0:  # shared experts on sampled tokens
+        tok = np.unique(np.r_[0, w.T - 1, np.random.default_rng(1).integers(0, w.T, 6)])
+        for i in range(w.n_shared):
+            Wg, Wu, Wd = (L.f64(x[n][i]) for n in ("Ws_gate", "Ws_up", "Ws_down"))
+            ref = O.swiglu_expert(U[tok], Wg, Wu, Wd)
+            worst = max(worst, L.row_rel_err(Ysg[i][tok], ref))
+        assert worst <= L.out_tol(w), worst
     L.log(f"  outputs ok: out={eo:.2e} delta={ed:.2e} Y(sampled)={worst:.2e}")
