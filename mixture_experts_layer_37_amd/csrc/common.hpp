@@ -102,6 +102,27 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Lanes whose value `theirs` equals `mine`, among lanes with `valid` set.
 // Values are in [0, 256).
+// Exclusive prefix sum of v over the 256 threads of a block (blockDim.x must
+// be 256; every thread calls it).  tmp: 4 ints of LDS.  *total receives the
+// sum of all 256 values.
+__device__ __forceinline__ int block_excl_scan256(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) tmp[wave] = inc;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+    if (w < wave) before += tmp[w];
+  *total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  return before + inc - v;
+}
+
 __device__ __forceinline__ uint64_t match_lanes(int mine, int theirs, bool valid) {
   uint64_t m = __ballot(valid);
 #pragma unroll

@@ -49,39 +49,46 @@ __global__ __launch_bounds__(256) void hist_kernel(DispatchParams p) {
 }
 
 __global__ __launch_bounds__(256) void scan_kernel(DispatchParams p, int nchunk) {
-  __shared__ int kept_s[256];
+  __shared__ int tmp[4];
   const int e = threadIdx.x;
   int run = 0;
   if (e < p.E) {
-    if (!p.token_major) {
-      // rank-major: (rank 0, chunk 0), (rank 0, chunk 1), ..., (rank 1, chunk 0), ...
-      for (int r = 0; r < p.k; ++r)
-        for (int c = 0; c < nchunk; ++c) {
-          const size_t i = ((size_t)r * nchunk + c) * p.E + e;
-          p.base[i] = run;
-          run += p.hist[i];
+    // Expert e's (rank, chunk) counts in fill order, 8 independent loads at a
+    // time.  rank-major: (rank 0, chunk 0), (rank 0, chunk 1), ..., (rank 1,
+    // chunk 0), ...; token-major: chunk by chunk, a token holding an expert at
+    // most once, so the base of chunk c is the total of the chunks before it.
+    const int n = p.token_major ? nchunk : p.k * nchunk;
+    for (int j0 = 0; j0 < n; j0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = j0 + q;
+        v[q] = 0;
+        if (j < n) {
+          if (!p.token_major) {
+            v[q] = p.hist[(size_t)j * p.E + e];  // j = r * nchunk + c
+          } else {
+            for (int r = 0; r < p.k; ++r) v[q] += p.hist[((size_t)r * nchunk + j) * p.E + e];
+          }
         }
-    } else {
-      // token-major: chunks in token order; a token holds an expert at most once
-      for (int c = 0; c < nchunk; ++c) {
-        p.base[(size_t)c * p.E + e] = run;
-        for (int r = 0; r < p.k; ++r) run += p.hist[((size_t)r * nchunk + c) * p.E + e];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = j0 + q;
+        if (j < n) p.base[(size_t)j * p.E + e] = run;
+        run += v[q];
       }
     }
-    const int kp = run < p.C ? run : p.C;
+  }
+  const int kp = run < p.C ? run : p.C;
+  int total;
+  const int off = block_excl_scan256(e < p.E ? kp : 0, tmp, &total);
+  if (e < p.E) {
     p.count[e] = run;
     p.kept[e] = kp;
-    kept_s[e] = kp;
+    p.offset[e] = off;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int i = 0; i < p.E; ++i) {
-      p.offset[i] = acc;
-      acc += kept_s[i];
-    }
-    p.offset[p.E] = acc;
-  }
+  if (e == 0) p.offset[p.E] = total;
 }
 
 __global__ __launch_bounds__(256) void assign_kernel(DispatchParams p) {

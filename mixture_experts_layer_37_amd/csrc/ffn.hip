@@ -502,19 +502,24 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* A, const int
   }
 }
 
-__global__ void tile_map_kernel(const int32_t* offset, int E, int bm1, int bm2, int32_t* m1,
-                                int32_t* m2) {
-  if (threadIdx.x != 0) return;
-  int a = 0, b = 0;
-  for (int e = 0; e < E; ++e) {
+// First m-tile of every expert for both GEMMs' row tiles: exclusive scans of
+// ceil(rows_e / bm) over the experts (E <= 256, one thread each).
+__global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* offset, int E, int bm1,
+                                                       int bm2, int32_t* m1, int32_t* m2) {
+  __shared__ int tmp[2][4];
+  const int e = threadIdx.x;
+  const int n = e < E ? offset[e + 1] - offset[e] : 0;
+  int t1, t2;
+  const int a = block_excl_scan256((n + bm1 - 1) / bm1, tmp[0], &t1);
+  const int b = block_excl_scan256((n + bm2 - 1) / bm2, tmp[1], &t2);
+  if (e < E) {
     m1[e] = a;
     m2[e] = b;
-    const int n = offset[e + 1] - offset[e];
-    a += (n + bm1 - 1) / bm1;
-    b += (n + bm2 - 1) / bm2;
   }
-  m1[E] = a;
-  m2[E] = b;
+  if (e == 0) {
+    m1[E] = t1;
+    m2[E] = t2;
+  }
 }
 
 // Offsets of a dense pass over all T rows as one "expert" (the shared
@@ -574,7 +579,7 @@ FfnShape ffn_shape(int64_t rows_max, int E, int h, int f, int T, int k, int bf16
 
 hipError_t launch_tile_map(const int32_t* offset, int E, int bm1, int bm2, int32_t* map1,
                            int32_t* map2, hipStream_t s) {
-  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(64), 0, s, offset, E, bm1, bm2, map1, map2);
+  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(256), 0, s, offset, E, bm1, bm2, map1, map2);
   return hipGetLastError();
 }
 
