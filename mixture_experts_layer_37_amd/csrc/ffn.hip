@@ -61,7 +61,6 @@ namespace {
 constexpr int kWaves = 8;
 
 constexpr int BN = 256, BK = 64, GN = 8;
-constexpr int kPeriod = 6;  // steps after which the 3 A slots and 2 B slots line up again
 // Third dword of a raw buffer resource on gfx9-family parts (32-bit data
 // format, no swizzle); loads outside num_records bytes return zero.
 constexpr int kBufFlags = 0x00020000;
@@ -149,7 +148,9 @@ template <int BM, int NW, bool GATEUP>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const floatx16 (&acc)[(2 * BM / NW) / 32][4],
                                            int nt, int row0, int nvalid) {
   constexpr int WR = 2 * BM / NW, RBLK = WR / 32;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));  // keeps the row addressing below out of the main loop
+  const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, khalf = lane >> 5;
 #pragma unroll
   for (int i = 0; i < RBLK; ++i) {
@@ -200,11 +201,14 @@ __device__ __forceinline__ void wait_vm() {
 // clobber keeps the compiler from moving LDS accesses across the barrier.
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
+// LDS slots of the copy pipeline: NA slots of A tiles and NB of B tiles
+// (2 or 3 each); operand X of step j is copied N_X steps ahead.
 struct Ring {
-  bf16 *a0, *a1, *a2, *b0, *b1;
+  bf16* a[3];
+  bf16* b[3];
 };
 
-template <int BM, int NW, bool GATEUP, bool PARTIAL>
+template <int BM, int NW, bool GATEUP, bool PARTIAL, int NA, int NB>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, int row0,
                                           int nvalid, const Ring& L, const KSplit& ksp) {
   constexpr int WM = NW / 2;         // waves along M (2 along N)
@@ -340,40 +344,42 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
     fetch(as, bs, 3, 1);
     mfmas(0);
     order();
-    // A_{j+1} and B_{j+1} have landed; only A_{j+2} may still be in flight
-    wait_vm<AG>();
+    // A_{j+1} and B_{j+1} have landed; copies of step j + 2 (issued last)
+    // may still be in flight
+    wait_vm<(NA == 3 ? AG : 0) + (NB == 3 ? BG : 0)>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave is done reading (as, bs)
     barrier_only();
-    issueB(bs, j + 2);
-    issueA(as, j + 3);
+    // into the slots just read: the operand copied 2 steps ahead first
+    if (NA == 2) issueA(as, j + 2);
+    issueB(bs, j + NB);
+    if (NA == 3) issueA(as, j + 3);
     fetch(nas, nbs, 0, 0);
     mfmas(1);
     order_copies();
   };
 
-  issueA(L.a0, 0);
-  issueB(L.b0, 0);
-  issueA(L.a1, 1);
-  issueB(L.b1, 1);
-  issueA(L.a2, 2);
-  wait_vm<2 * AG + BG>();  // A_0 and B_0 have landed
+  issueA(L.a[0], 0);
+  issueB(L.b[0], 0);
+  issueA(L.a[1], 1);
+  issueB(L.b[1], 1);
+  if (NA == 3) issueA(L.a[2], 2);
+  if (NB == 3) issueB(L.b[2], 2);
+  wait_vm<(NA - 1) * AG + (NB - 1) * BG>();  // A_0 and B_0 have landed
   barrier_only();
-  fetch(L.a0, L.b0, 0, 0);
+  fetch(L.a[0], L.b[0], 0, 0);
+  // the slots line up again after P steps; the loop body is unrolled over
+  // them so that every LDS address is a constant
+  constexpr int P = NA == NB ? NA : NA * NB;
   int j = 0;
-  for (; j + kPeriod <= KT; j += kPeriod) {
-    step(j, L.a0, L.b0, L.a1, L.b1);
-    step(j + 1, L.a1, L.b1, L.a2, L.b0);
-    step(j + 2, L.a2, L.b0, L.a0, L.b1);
-    step(j + 3, L.a0, L.b1, L.a1, L.b0);
-    step(j + 4, L.a1, L.b0, L.a2, L.b1);
-    step(j + 5, L.a2, L.b1, L.a0, L.b0);
+  for (; j + P <= KT; j += P) {
+#pragma unroll
+    for (int q = 0; q < P; ++q)
+      step(j + q, L.a[q % NA], L.b[q % NB], L.a[(q + 1) % NA], L.b[(q + 1) % NB]);
   }
-  const int rest = KT - j;  // 0..5 steps, starting again at slot phase 0
-  if (rest > 0) step(j, L.a0, L.b0, L.a1, L.b1);
-  if (rest > 1) step(j + 1, L.a1, L.b1, L.a2, L.b0);
-  if (rest > 2) step(j + 2, L.a2, L.b0, L.a0, L.b1);
-  if (rest > 3) step(j + 3, L.a0, L.b1, L.a1, L.b0);
-  if (rest > 4) step(j + 4, L.a1, L.b0, L.a2, L.b1);
+  const int rest = KT - j;  // 0..P-1 steps, starting again at slot phase 0
+#pragma unroll
+  for (int q = 0; q < P - 1; ++q)
+    if (q < rest) step(j + q, L.a[q % NA], L.b[q % NB], L.a[(q + 1) % NA], L.b[(q + 1) % NB]);
   wait_vm<0>();  // copies past the end are still in flight
 
   if (ksp.ks > 1) {  // a K chunk of a tail tile: leave the partial to the reduction
@@ -399,11 +405,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
 // the same share of real tiles, and the workgroups running together on one
 // XCD hold neighbouring tiles, which share A row panels and weight panels in
 // that XCD's L2.
-template <int BM, int NW, bool GATEUP>
+template <int BM, int NW, bool GATEUP, int NA, int NB>
 __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) bf16 A0[BM * BK], A1[BM * BK], A2[BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16 A0[BM * BK], A1[BM * BK];
+  __shared__ __attribute__((aligned(1024))) bf16 A2[NA == 3 ? BM * BK : 8];
   __shared__ __attribute__((aligned(1024))) bf16 B0[BN * BK], B1[BN * BK];
-  const Ring L{A0, A1, A2, B0, B1};
+  __shared__ __attribute__((aligned(1024))) bf16 B2[NB == 3 ? BN * BK : 8];
+  const Ring L{{A0, A1, A2}, {B0, B1, B2}};
 
   const int mtiles = p.tmap[p.E];
   const int KT = p.K / BK;
@@ -422,15 +430,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(GemmParams p) {
       ksp.slot = p.part + (size_t)(xcd * xs.nloc + v) * BM * BN;
     }
     const TileAt ta = tile_at<BM>(p, t, mtiles);
-    const int e = ta.e, nt = ta.nt, row0 = ta.row0, nvalid = ta.nvalid;
+    // uniform by construction; readfirstlane keeps them (and the buffer
+    // descriptors built from them) in SGPRs
+    const int e = __builtin_amdgcn_readfirstlane(ta.e);
+    const int nt = __builtin_amdgcn_readfirstlane(ta.nt);
+    const int row0 = __builtin_amdgcn_readfirstlane(ta.row0);
+    const int nvalid = __builtin_amdgcn_readfirstlane(ta.nvalid);
     __syncthreads();  // every wave is done with the previous tile's LDS
     // tiles more than half full run the fully scheduled loop (rows past
     // nvalid read zero and are not stored); emptier ones skip the MFMAs of
     // their empty 32-row blocks
     if (2 * nvalid > BM)
-      gemm_tile<BM, NW, GATEUP, false>(p, e, nt, row0, nvalid, L, ksp);
+      gemm_tile<BM, NW, GATEUP, false, NA, NB>(p, e, nt, row0, nvalid, L, ksp);
     else
-      gemm_tile<BM, NW, GATEUP, true>(p, e, nt, row0, nvalid, L, ksp);
+      gemm_tile<BM, NW, GATEUP, true, NA, NB>(p, e, nt, row0, nvalid, L, ksp);
   }
 }
 
@@ -533,14 +546,18 @@ __global__ void dense_offsets_kernel(int T, int32_t* offset) {
 
 int round8(int x) { return (x + 7) & ~7; }
 
+// Copy pipelines (LDS slots of A and B tiles): weight tiles go 3 steps ahead
+// (they come from HBM, or from L2 behind other workgroups' misses), A tiles 2
+// steps ahead in 256-row tiles (2 x 32 KB + 3 x 32 KB fill the 160 KB of LDS)
+// and 3 in 128-row tiles.
 template <bool GATEUP>
 void launch_gemm(int bm, const GemmParams& p, hipStream_t s) {
   const dim3 grid(p.grid), block(64 * kWaves);
   if (bm == 256) {
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, kWaves, GATEUP>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, kWaves, GATEUP, 2, 3>), grid, block, 0, s, p);
     hipLaunchKernelGGL((ksplit_reduce_kernel<256, kWaves, GATEUP>), grid, block, 0, s, p);
   } else {
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, kWaves, GATEUP>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, kWaves, GATEUP, 3, 3>), grid, block, 0, s, p);
     hipLaunchKernelGGL((ksplit_reduce_kernel<128, kWaves, GATEUP>), grid, block, 0, s, p);
   }
 }
