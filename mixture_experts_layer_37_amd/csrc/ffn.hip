@@ -141,9 +141,12 @@ __device__ __forceinline__ float4* part_at(float* slot, int q) {
   return reinterpret_cast<float4*>(slot) + (size_t)q * 64 * NW + threadIdx.x;
 }
 
-// Epilogue: the wave's (2 BM / NW) x 128 block.  D layout of a 32x32 MFMA
-// tile: lane holds column (lane % 32) and rows 8 * (v / 4) + 4 * (lane / 32) +
-// (v % 4), v = 0..15.  Gate/up: a = SiLU(g) * u from the gate and up halves.
+// Epilogue: the wave's (2 BM / NW) x 128 block.  The MFMAs take the weight
+// fragment as their first operand, so each 32x32 accumulator is the block's
+// transpose: lane holds output row (lane % 32) and output columns
+// 8 * g + 4 * (lane / 32) + t in acc[4 * g + t], g, t = 0..3.  Each run of 4
+// columns goes out as one 8-byte store.  Gate/up: a = SiLU(g) * u from the
+// gate and up halves, which sit in the same lane and register.
 template <int BM, int NW, bool GATEUP>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const floatx16 (&acc)[(2 * BM / NW) / 32][4],
                                            int nt, int row0, int nvalid) {
@@ -154,26 +157,27 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const floatx16 (
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, khalf = lane >> 5;
 #pragma unroll
   for (int i = 0; i < RBLK; ++i) {
-    if (wm * WR + i * 32 >= nvalid) continue;
+    const int r = wm * WR + i * 32 + l32;
+    if (r >= nvalid) continue;
+    bf16* crow = p.C + (size_t)(row0 + r) * p.Nout;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = wm * WR + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
-      if (r >= nvalid) continue;
-      bf16* crow = p.C + (size_t)(row0 + r) * p.Nout;
-      if (GATEUP) {
+    for (int j = 0; j < (GATEUP ? 2 : 4); ++j) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = nt * 128 + wn * 64 + j * 32 + l32;
-          const float gv = acc[i][j][v], uv = acc[i][j + 2][v];
-          const float a = gv / (1.f + __expf(-gv)) * uv;
-          if (col < p.Nout) crow[col] = f32_to_bf16(a);
+      for (int g = 0; g < 4; ++g) {
+        // Nout is a multiple of 4: a run is all inside or all past the end
+        const int col = (GATEUP ? nt * 128 + wn * 64 : nt * BN + wn * 128) + j * 32 + 8 * g + 4 * khalf;
+        if (col >= p.Nout) continue;
+        float y[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (GATEUP) {
+            const float gv = acc[i][j][4 * g + t], uv = acc[i][j + 2][4 * g + t];
+            y[t] = gv / (1.f + __expf(-gv)) * uv;
+          } else {
+            y[t] = acc[i][j][4 * g + t];
+          }
         }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = nt * BN + wn * 128 + j * 32 + l32;
-          if (col < p.Nout) crow[col] = f32_to_bf16(acc[i][j][v]);
-        }
+        *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
       }
     }
   }
@@ -208,7 +212,11 @@ struct Ring {
   bf16* b[3];
 };
 
-template <int BM, int NW, bool GATEUP, bool PARTIAL, int NA, int NB>
+// R: the 32-row blocks of this wave that hold valid rows (the first R of its
+// RBLK); a wave with R < RBLK skips the fragment reads and MFMAs of the others
+// (their accumulators stay zero and their rows are never stored) but issues
+// the same copies and meets the same barriers as the rest of the workgroup.
+template <int BM, int NW, bool GATEUP, int R, int NA, int NB>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, int row0,
                                           int nvalid, const Ring& L, const KSplit& ksp) {
   constexpr int WM = NW / 2;         // waves along M (2 along N)
@@ -280,8 +288,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
                          : (wn * 128 + j * 32 + l32);
     boff[j] = r * BK;
   }
-  int rlim = RBLK;
-  if (PARTIAL) rlim = max(0, min(RBLK, (nvalid - wm * WR + 31) / 32));
+  static_assert(R >= 0 && R <= RBLK, "active blocks");
 
   floatx16 acc[RBLK][4];
 #pragma unroll
@@ -295,28 +302,27 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
   auto fetch = [&](const bf16* as, const bf16* bs, int slice, int st) {
     const int c = ((2 * slice + khalf) ^ sw) * 8;
 #pragma unroll
-    for (int i = 0; i < RBLK; ++i)
-      if (!PARTIAL || i < rlim) fa[st][i] = *reinterpret_cast<const bf16x8*>(as + aoff[i] + c);
+    for (int i = 0; i < R; ++i) fa[st][i] = *reinterpret_cast<const bf16x8*>(as + aoff[i] + c);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[st][j] = *reinterpret_cast<const bf16x8*>(bs + boff[j] + c);
+    for (int j = 0; j < (R > 0 ? 4 : 0); ++j)
+      fb[st][j] = *reinterpret_cast<const bf16x8*>(bs + boff[j] + c);
   };
   auto mfmas = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < RBLK; ++i) {
-      if (PARTIAL && i >= rlim) continue;
+    for (int i = 0; i < R; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[st][i], fb[st][j], acc[i][j],
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[st][j], fa[st][i], acc[i][j],
                                                             0, 0, 0);
     }
   };
   // order for the scheduler: MFMAs interleaved with the next fragment reads
   // and, after the barrier, with the copies (groups: 0x008 MFMA, 0x100 LDS
   // read, 0x020 global read incl. LDS copies)
-  constexpr int NM = RBLK * 4, NR = RBLK + 4, NC = AG + BG;
-  constexpr int CPM = (NC + NM - 1) / NM;  // copies placed after each MFMA
+  constexpr int NM = R * 4, NR = R > 0 ? R + 4 : 0, NC = AG + BG;
+  constexpr int CPM = NM > 0 ? (NC + NM - 1) / NM : NC;  // copies placed after each MFMA
   auto order = [&]() {
-    if (PARTIAL) return;
+    if (R == 0) return;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -324,7 +330,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
     }
   };
   auto order_copies = [&]() {
-    if (PARTIAL) return;
+    if (R == 0) return;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -437,13 +443,17 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(GemmParams p) {
     const int row0 = __builtin_amdgcn_readfirstlane(ta.row0);
     const int nvalid = __builtin_amdgcn_readfirstlane(ta.nvalid);
     __syncthreads();  // every wave is done with the previous tile's LDS
-    // tiles more than half full run the fully scheduled loop (rows past
-    // nvalid read zero and are not stored); emptier ones skip the MFMAs of
-    // their empty 32-row blocks
-    if (2 * nvalid > BM)
-      gemm_tile<BM, NW, GATEUP, false, NA, NB>(p, e, nt, row0, nvalid, L, ksp);
+    // each wave runs the fully scheduled loop over its 32-row blocks that
+    // hold valid rows (rows past nvalid read zero and are not stored)
+    constexpr int RBLK = (2 * BM / NW) / 32;
+    const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >> 1;
+    const int act = min(RBLK, max(0, (nvalid - wm * (RBLK * 32) + 31) / 32));
+    if (act >= RBLK)
+      gemm_tile<BM, NW, GATEUP, RBLK, NA, NB>(p, e, nt, row0, nvalid, L, ksp);
+    else if (RBLK > 1 && act == 1)
+      gemm_tile<BM, NW, GATEUP, (RBLK > 1 ? 1 : 0), NA, NB>(p, e, nt, row0, nvalid, L, ksp);
     else
-      gemm_tile<BM, NW, GATEUP, true, NA, NB>(p, e, nt, row0, nvalid, L, ksp);
+      gemm_tile<BM, NW, GATEUP, 0, NA, NB>(p, e, nt, row0, nvalid, L, ksp);
   }
 }
 
