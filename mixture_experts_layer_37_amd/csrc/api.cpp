@@ -173,8 +173,8 @@ FfnWs plan_ffn(const Dims& d, Plan& pl) {
   FfnWs w;
   w.fs = ffn_shape(d.rows_max, (int)d.E, (int)d.h, (int)d.f, (int)d.T, (int)d.k, d.bf16,
                    device_cus());
-  w.map1 = pl.add((d.E + 1) * sizeof(int32_t));
-  w.map2 = pl.add((d.E + 1) * sizeof(int32_t));
+  w.map1 = pl.add(tile_map_bytes(d.E, w.fs.mt1));
+  w.map2 = pl.add(tile_map_bytes(d.E, w.fs.mt2));
   w.A = pl.add((size_t)(d.rows_max > 0 ? d.rows_max : 1) * d.f * elem_bytes(d));
   w.part = pl.add((size_t)w.fs.part_slots * kPartSlotBytes);
   return w;
@@ -190,8 +190,8 @@ SharedWs plan_shared(const Dims& d, bool with_ys, Plan& pl) {
   SharedWs w{};
   if (d.ns == 0) return w;
   w.fs = ffn_shape(d.T, 1, (int)d.h, (int)d.fs, (int)d.T, 1, d.bf16, device_cus());
-  w.map1 = pl.add(2 * sizeof(int32_t));
-  w.map2 = pl.add(2 * sizeof(int32_t));
+  w.map1 = pl.add(tile_map_bytes(1, w.fs.mt1));
+  w.map2 = pl.add(tile_map_bytes(1, w.fs.mt2));
   w.offs = pl.add(2 * sizeof(int32_t));
   w.part = pl.add((size_t)w.fs.part_slots * kPartSlotBytes);
   const size_t T1 = (size_t)(d.T > 0 ? d.T : 1);

@@ -68,7 +68,8 @@ constexpr int kBufFlags = 0x00020000;
 struct GemmParams {
   const bf16* A;         // [rows][K], experts' row blocks back to back
   const int32_t* offset; // [E+1]
-  const int32_t* tmap;   // [E+1] first m-tile of each expert
+  const int32_t* tmap;   // tile map: [E+1] first m-tile of each expert, then the
+                         // per-m-tile table (see tile_map_kernel)
   const bf16* W0;        // gate/up: W_gate [E][N][K]; down: W_down [E][N][K]
   const bf16* W1;        // gate/up: W_up
   bf16* C;               // [rows][Nout]
@@ -112,25 +113,26 @@ __device__ __forceinline__ XcdShare xcd_share(int total, int xcd, int grid, int 
 }
 
 // Tile t of the numbering: groups of GN n-tiles, m-tile major inside a group.
+// The m-tile's expert, first row and valid rows come from one 8-byte entry of
+// the tile map's table.
 struct TileAt {
   int e, nt, row0, nvalid;
 };
+__device__ __forceinline__ const int2* mtile_table(const int32_t* tmap, int E) {
+  return reinterpret_cast<const int2*>(tmap + ((E + 2) & ~1));
+}
 template <int BM>
 __device__ __forceinline__ TileAt tile_at(const GemmParams& p, int t, int mtiles) {
   const int g = t / (mtiles * GN);
   const int r = t - g * mtiles * GN;
   const int gw = min(GN, p.ntiles - g * GN);
   const int mt = r / gw;
+  const int2 m = mtile_table(p.tmap, p.E)[mt];
   TileAt x;
   x.nt = g * GN + r % gw;
-  int lo = 0, hi = p.E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.tmap[mid] <= mt) lo = mid; else hi = mid;
-  }
-  x.e = lo;
-  x.row0 = p.offset[lo] + (mt - p.tmap[lo]) * BM;
-  x.nvalid = min(BM, p.offset[lo + 1] - x.row0);
+  x.e = m.y & 0xffff;
+  x.row0 = m.x;
+  x.nvalid = m.y >> 16;
   return x;
 }
 
@@ -212,68 +214,102 @@ struct Ring {
   bf16* b[3];
 };
 
+// Copy sources of one unit of work (a tile, or one K chunk of a tail tile):
+// buffer resources over its valid A rows and its weight panels, and its range
+// of 64-wide K steps.  A's resource ends at the last valid row, so copies of
+// rows past it read zero without touching memory (their outputs are never
+// stored).
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t rA, rB0, rB1;
+  int kbeg, KT;
+};
+template <bool GATEUP>
+__device__ __forceinline__ TileSrc tile_src(const GemmParams& p, const TileAt& ta,
+                                            const KSplit& ksp) {
+  TileSrc s;
+  const int K = p.K;
+  s.rA = make_rsrc(p.A + (size_t)ta.row0 * K, (size_t)ta.nvalid * K * 2);
+  const size_t n0 = (size_t)ta.nt * (GATEUP ? 128 : BN);
+  s.rB0 = make_rsrc(p.W0 + ((size_t)ta.e * p.N + n0) * K, (size_t)(p.N - n0) * K * 2);
+  s.rB1 = GATEUP ? make_rsrc(p.W1 + ((size_t)ta.e * p.N + n0) * K, (size_t)(p.N - n0) * K * 2)
+                 : s.rB0;
+  s.kbeg = ksp.kbeg;
+  s.KT = ksp.ksteps;
+  return s;
+}
+
+// This wave's share of the copies of one K step.  Lane i of 8-row group g
+// fills LDS row 8g + i/8, physical chunk i%8, with logical chunk
+// (i%8) ^ ((row >> 1) & 7).  The per-lane offsets depend on K only.
+template <int BM, int NW, bool GATEUP>
+struct CopyPlan {
+  static constexpr int AG = BM / (8 * NW);  // 8-row A groups copied per wave per step
+  static constexpr int BG = BN / (8 * NW);  // 8-row B groups copied per wave per step
+  int wave;
+  int voA[AG], voB[BG];
+  __device__ __forceinline__ explicit CopyPlan(int K) {
+    // the wave index is uniform: keep it (and all copy addressing) in SGPRs
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, lrow = lane >> 3;
+#pragma unroll
+    for (int j = 0; j < AG; ++j) {
+      const int r = 8 * (wave + NW * j) + lrow;
+      voA[j] = (r * K + (((lane & 7) ^ ((r >> 1) & 7)) * 8)) * 2;
+    }
+#pragma unroll
+    for (int j = 0; j < BG; ++j) {
+      // gate/up: groups 0..15 are W_gate rows, 16..31 (j >= BG/2) the W_up rows
+      const int g = wave + NW * j;
+      const int r = 8 * g + lrow;                       // LDS row
+      const int pr = GATEUP ? 8 * (g & 15) + lrow : r;  // row in the weight panel
+      voB[j] = (pr * K + (((lane & 7) ^ ((r >> 1) & 7)) * 8)) * 2;
+    }
+  }
+  // step j past the end reloads the last step (in bounds, never read), so
+  // every step issues the same number of copies
+  __device__ __forceinline__ void issueA(const TileSrc& s, bf16* as, int j) const {
+    const int kb = (s.kbeg + min(j, s.KT - 1)) * BK * 2;
+#pragma unroll
+    for (int q = 0; q < AG; ++q) dma16(s.rA, as + (wave + NW * q) * 8 * BK, voA[q], kb);
+  }
+  __device__ __forceinline__ void issueB(const TileSrc& s, bf16* bs, int j) const {
+    const int kb = (s.kbeg + min(j, s.KT - 1)) * BK * 2;
+#pragma unroll
+    for (int q = 0; q < BG; ++q)
+      dma16((GATEUP && q >= BG / 2) ? s.rB1 : s.rB0, bs + (wave + NW * q) * 8 * BK, voB[q], kb);
+  }
+  // the first N_A A steps and N_B B steps of a unit, into slot phase 0
+  template <int NA, int NB>
+  __device__ __forceinline__ void prologue(const TileSrc& s, const Ring& L) const {
+    issueA(s, L.a[0], 0);
+    issueB(s, L.b[0], 0);
+    issueA(s, L.a[1], 1);
+    issueB(s, L.b[1], 1);
+    if (NA == 3) issueA(s, L.a[2], 2);
+    if (NB == 3) issueB(s, L.b[2], 2);
+  }
+};
+
 // R: the 32-row blocks of this wave that hold valid rows (the first R of its
 // RBLK); a wave with R < RBLK skips the fragment reads and MFMAs of the others
 // (their accumulators stay zero and their rows are never stored) but issues
 // the same copies and meets the same barriers as the rest of the workgroup.
-template <int BM, int NW, bool GATEUP, int R, int NA, int NB>
-__device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, int row0,
-                                          int nvalid, const Ring& L, const KSplit& ksp) {
+template <int BM, int NW, bool GATEUP, int R, int NA, int NB, class Next>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM, NW, GATEUP>& cp,
+                                          const TileSrc& src, const Ring& L, const TileAt& ta,
+                                          const KSplit& ksp, Next&& next) {
   constexpr int WM = NW / 2;         // waves along M (2 along N)
   constexpr int WR = BM / WM;        // rows per wave
   constexpr int RBLK = WR / 32;      // 32-row MFMA blocks per wave
-  constexpr int AG = BM / (8 * NW);  // 8-row A groups copied per wave per step
-  constexpr int BG = BN / (8 * NW);  // 8-row B groups copied per wave per step
+  constexpr int AG = CopyPlan<BM, NW, GATEUP>::AG;
+  constexpr int BG = CopyPlan<BM, NW, GATEUP>::BG;
   static_assert(AG >= 1 && BG >= 2 && RBLK >= 1, "tile shape");
-  // the wave index is uniform: keep it (and all copy addressing) in SGPRs
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = cp.wave;
   const int lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  const int K = p.K;
-  const int KT = ksp.ksteps;  // steps of this tile's K range, which starts at step ksp.kbeg
-
-  // ---- copy sources.  Lane i of 8-row group g fills LDS row 8g + i/8,
-  // physical chunk i%8, with logical chunk (i%8) ^ ((row >> 1) & 7).
-  const int lrow = lane >> 3;
-  // A: only this tile's valid rows; copies of rows past them read zero
-  // without touching memory (their outputs are never stored)
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + (size_t)row0 * K, (size_t)nvalid * K * 2);
-  __amdgpu_buffer_rsrc_t rB0, rB1;
-  if (GATEUP) {
-    const size_t n0 = (size_t)nt * 128;
-    rB0 = make_rsrc(p.W0 + ((size_t)e * p.N + n0) * K, (size_t)(p.N - n0) * K * 2);
-    rB1 = make_rsrc(p.W1 + ((size_t)e * p.N + n0) * K, (size_t)(p.N - n0) * K * 2);
-  } else {
-    const size_t n0 = (size_t)nt * BN;
-    rB0 = make_rsrc(p.W0 + ((size_t)e * p.N + n0) * K, (size_t)(p.N - n0) * K * 2);
-    rB1 = rB0;
-  }
-  int voA[AG], voB[BG];
-#pragma unroll
-  for (int j = 0; j < AG; ++j) {
-    const int r = 8 * (wave + NW * j) + lrow;
-    voA[j] = (r * K + (((lane & 7) ^ ((r >> 1) & 7)) * 8)) * 2;
-  }
-#pragma unroll
-  for (int j = 0; j < BG; ++j) {
-    // gate/up: groups 0..15 are W_gate rows, 16..31 (j >= BG/2) the W_up rows
-    const int g = wave + NW * j;
-    const int r = 8 * g + lrow;                          // LDS row
-    const int pr = GATEUP ? 8 * (g & 15) + lrow : r;     // row in the weight panel
-    voB[j] = (pr * K + (((lane & 7) ^ ((r >> 1) & 7)) * 8)) * 2;
-  }
-  // step j past the end reloads the last step (in bounds, never read)
-  auto issueA = [&](bf16* as, int j) {
-    const int kb = (ksp.kbeg + min(j, KT - 1)) * BK * 2;
-#pragma unroll
-    for (int q = 0; q < AG; ++q) dma16(rA, as + (wave + NW * q) * 8 * BK, voA[q], kb);
-  };
-  auto issueB = [&](bf16* bs, int j) {
-    const int kb = (ksp.kbeg + min(j, KT - 1)) * BK * 2;
-#pragma unroll
-    for (int q = 0; q < BG; ++q)
-      dma16((GATEUP && q >= BG / 2) ? rB1 : rB0, bs + (wave + NW * q) * 8 * BK, voB[q], kb);
-  };
+  const int KT = src.KT;
+  auto issueA = [&](bf16* as, int j) { cp.issueA(src, as, j); };
+  auto issueB = [&](bf16* bs, int j) { cp.issueB(src, bs, j); };
 
   // ---- fragments: lane reads row (lane % 32) of each 32-row block, logical
   // chunk 2 * slice + lane / 32 of the step's 8
@@ -364,14 +400,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
     order_copies();
   };
 
-  issueA(L.a[0], 0);
-  issueB(L.b[0], 0);
-  issueA(L.a[1], 1);
-  issueB(L.b[1], 1);
-  if (NA == 3) issueA(L.a[2], 2);
-  if (NB == 3) issueB(L.b[2], 2);
-  wait_vm<(NA - 1) * AG + (NB - 1) * BG>();  // A_0 and B_0 have landed
-  barrier_only();
+  // the caller issued this unit's first copies and saw them land
   fetch(L.a[0], L.b[0], 0, 0);
   // the slots line up again after P steps; the loop body is unrolled over
   // them so that every LDS address is a constant
@@ -387,6 +416,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
   for (int q = 0; q < P - 1; ++q)
     if (q < rest) step(j + q, L.a[q % NA], L.b[q % NB], L.a[(q + 1) % NA], L.b[(q + 1) % NB]);
   wait_vm<0>();  // copies past the end are still in flight
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  barrier_only();  // every wave is done with LDS
+  next();          // the next unit's first copies go out before this epilogue
 
   if (ksp.ks > 1) {  // a K chunk of a tail tile: leave the partial to the reduction
 #pragma unroll
@@ -400,7 +432,37 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int e, int nt, in
                           acc[i][j][4 * v4 + 3]);
     return;
   }
-  store_tile<BM, NW, GATEUP>(p, acc, nt, row0, nvalid);
+  store_tile<BM, NW, GATEUP>(p, acc, ta.nt, ta.row0, ta.nvalid);
+}
+
+// Unit u of an XCD's share: tile xs.tbeg + u, or (past the full rounds, when
+// the tail is split) K chunk kc of tail tile q.  Every field is uniform;
+// readfirstlane keeps them (and the buffer descriptors built from them) in
+// SGPRs.
+struct Unit {
+  TileAt ta;
+  KSplit ksp;
+};
+template <int BM>
+__device__ __forceinline__ Unit unit_at(const GemmParams& p, const XcdShare& xs, int xcd, int u,
+                                        int KT, int mtiles) {
+  Unit w;
+  int t = xs.tbeg + u;
+  w.ksp = KSplit{0, KT, 1, nullptr};
+  if (u >= xs.full && xs.ks > 1) {
+    const int v = u - xs.full, q = v / xs.ks, kc = v - q * xs.ks;  // tail tile q, chunk kc
+    t = xs.tbeg + xs.full + q;
+    w.ksp.ks = xs.ks;
+    w.ksp.kbeg = kc * KT / xs.ks;
+    w.ksp.ksteps = (kc + 1) * KT / xs.ks - w.ksp.kbeg;
+    w.ksp.slot = p.part + (size_t)(xcd * xs.nloc + v) * BM * BN;
+  }
+  const TileAt ta = tile_at<BM>(p, t, mtiles);
+  w.ta.e = __builtin_amdgcn_readfirstlane(ta.e);
+  w.ta.nt = __builtin_amdgcn_readfirstlane(ta.nt);
+  w.ta.row0 = __builtin_amdgcn_readfirstlane(ta.row0);
+  w.ta.nvalid = __builtin_amdgcn_readfirstlane(ta.nvalid);
+  return w;
 }
 
 // Persistent grouped GEMM.  The grid holds a fixed number of workgroups (a
@@ -424,36 +486,35 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(GemmParams p) {
   const int xcd = blockIdx.x & 7;
   const XcdShare xs = xcd_share(mtiles * p.ntiles, xcd, p.grid, KT, p.split_max);
   const int units = xs.full + xs.rem * xs.ks;
-  for (int u = blockIdx.x >> 3; u < units; u += xs.nloc) {
-    int t = xs.tbeg + u;
-    KSplit ksp{0, KT, 1, nullptr};
-    if (u >= xs.full && xs.ks > 1) {
-      const int v = u - xs.full, q = v / xs.ks, kc = v - q * xs.ks;  // tail tile q, chunk kc
-      t = xs.tbeg + xs.full + q;
-      ksp.ks = xs.ks;
-      ksp.kbeg = kc * KT / xs.ks;
-      ksp.ksteps = (kc + 1) * KT / xs.ks - ksp.kbeg;
-      ksp.slot = p.part + (size_t)(xcd * xs.nloc + v) * BM * BN;
-    }
-    const TileAt ta = tile_at<BM>(p, t, mtiles);
-    // uniform by construction; readfirstlane keeps them (and the buffer
-    // descriptors built from them) in SGPRs
-    const int e = __builtin_amdgcn_readfirstlane(ta.e);
-    const int nt = __builtin_amdgcn_readfirstlane(ta.nt);
-    const int row0 = __builtin_amdgcn_readfirstlane(ta.row0);
-    const int nvalid = __builtin_amdgcn_readfirstlane(ta.nvalid);
-    __syncthreads();  // every wave is done with the previous tile's LDS
+  int u = blockIdx.x >> 3;
+  if (u >= units) return;
+  const CopyPlan<BM, NW, GATEUP> cp(p.K);
+  Unit cur = unit_at<BM>(p, xs, xcd, u, KT, mtiles);
+  cp.template prologue<NA, NB>(tile_src<GATEUP>(p, cur.ta, cur.ksp), L);
+  constexpr int RBLK = (2 * BM / NW) / 32;
+  const int wm = cp.wave >> 1;
+  for (;;) {
+    wait_vm<0>();    // this unit's first copies (and the last epilogue's stores)
+    barrier_only();  // ... have landed in every wave
+    const int un = u + xs.nloc;
+    const bool more = un < units;
+    const Unit nxt = more ? unit_at<BM>(p, xs, xcd, un, KT, mtiles) : cur;
+    auto next = [&]() {
+      if (more) cp.template prologue<NA, NB>(tile_src<GATEUP>(p, nxt.ta, nxt.ksp), L);
+    };
+    const TileSrc src = tile_src<GATEUP>(p, cur.ta, cur.ksp);
     // each wave runs the fully scheduled loop over its 32-row blocks that
     // hold valid rows (rows past nvalid read zero and are not stored)
-    constexpr int RBLK = (2 * BM / NW) / 32;
-    const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >> 1;
-    const int act = min(RBLK, max(0, (nvalid - wm * (RBLK * 32) + 31) / 32));
+    const int act = min(RBLK, max(0, (cur.ta.nvalid - wm * (RBLK * 32) + 31) / 32));
     if (act >= RBLK)
-      gemm_tile<BM, NW, GATEUP, RBLK, NA, NB>(p, e, nt, row0, nvalid, L, ksp);
+      gemm_tile<BM, NW, GATEUP, RBLK, NA, NB>(p, cp, src, L, cur.ta, cur.ksp, next);
     else if (RBLK > 1 && act == 1)
-      gemm_tile<BM, NW, GATEUP, (RBLK > 1 ? 1 : 0), NA, NB>(p, e, nt, row0, nvalid, L, ksp);
+      gemm_tile<BM, NW, GATEUP, (RBLK > 1 ? 1 : 0), NA, NB>(p, cp, src, L, cur.ta, cur.ksp, next);
     else
-      gemm_tile<BM, NW, GATEUP, 0, NA, NB>(p, e, nt, row0, nvalid, L, ksp);
+      gemm_tile<BM, NW, GATEUP, 0, NA, NB>(p, cp, src, L, cur.ta, cur.ksp, next);
+    if (!more) break;
+    u = un;
+    cur = nxt;
   }
 }
 
@@ -525,8 +586,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* A, const int
   }
 }
 
-// First m-tile of every expert for both GEMMs' row tiles: exclusive scans of
-// ceil(rows_e / bm) over the experts (E <= 256, one thread each).
+// Tile maps of both GEMMs' row tiles.  Map layout: [E+1] first m-tile of
+// every expert (exclusive scan of ceil(rows_e / bm) over the experts, E <= 256,
+// one thread each), padded to an even count, then one int2 per m-tile:
+// {first row, expert | valid rows << 16}.
 __global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* offset, int E, int bm1,
                                                        int bm2, int32_t* m1, int32_t* m2) {
   __shared__ int tmp[2][4];
@@ -538,6 +601,13 @@ __global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* offset, in
   if (e < E) {
     m1[e] = a;
     m2[e] = b;
+    const int o = offset[e];
+    int2* tab1 = reinterpret_cast<int2*>(m1 + ((E + 2) & ~1));
+    int2* tab2 = reinterpret_cast<int2*>(m2 + ((E + 2) & ~1));
+    for (int q = 0; q * bm1 < n; ++q)
+      tab1[a + q] = make_int2(o + q * bm1, e | (min(bm1, n - q * bm1) << 16));
+    for (int q = 0; q * bm2 < n; ++q)
+      tab2[b + q] = make_int2(o + q * bm2, e | (min(bm2, n - q * bm2) << 16));
   }
   if (e == 0) {
     m1[E] = t1;

@@ -77,6 +77,12 @@ struct FfnShape {
 constexpr size_t kPartSlotBytes = 256 * 256 * sizeof(float);
 // ncu: compute units of the device (the persistent grid size)
 FfnShape ffn_shape(int64_t rows_max, int E, int h, int f, int T, int k, int bf16, int ncu);
+// Bytes of one GEMM's tile map: the E+1 first m-tiles of the experts padded
+// to an even count, then {first row, expert | valid rows << 16} per m-tile
+// (mt: the static bound on m-tiles).
+inline size_t tile_map_bytes(int64_t E, int mt) {
+  return (size_t)(((E + 2) & ~int64_t(1)) + 2 * (int64_t)mt) * sizeof(int32_t);
+}
 hipError_t launch_tile_map(const int32_t* offset, int E, int bm1, int bm2, int32_t* map1,
                            int32_t* map2, hipStream_t s);
 // offset = {0, T}: all T rows as one expert (the shared experts' dense pass)
