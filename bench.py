@@ -73,6 +73,34 @@ def measured_traffic(workload: str):
         return None
 
 
+def stage_bandwidth(w, stage_ms, kept, e_active, eb):
+    """Achieved bandwidth of each stage over the bytes it has to move at least.
+
+    Counted per stage (bf16: eb = 2 bytes per element): the router reads U and
+    W_r (and W_noise); dispatch reads U and writes the kept rows X; gate/up
+    reads X and the active experts' W_gate and W_up and writes the SwiGLU rows
+    A; down reads A and W_down and writes Y; combine reads U and Y and writes
+    out.  Shared experts add a dense pass over all T tokens to gate/up and
+    down.  Index and statistics arrays are left out (under 1% of any stage).
+    """
+    T, h, f, E = w.T, w.h, w.f, w.E
+    ns, fs = w.n_shared, w.f_shared
+    b = {
+        "route": eb * (T * h + h * E * (2 if w.noisy else 1)),
+        "dispatch": eb * (T * h + kept * h),
+        "gate_up": eb * (kept * h + 2 * f * h * e_active + kept * f
+                         + ns * (T * h + 2 * fs * h + T * fs)),
+        "down": eb * (kept * f + f * h * e_active + kept * h + ns * (T * fs + fs * h + T * h)),
+        "combine": eb * (T * h + kept * h + T * h + ns * T * h),
+    }
+    out = {}
+    for n, nbytes in b.items():
+        t = stage_ms.get(n, 0.0)
+        gbs = nbytes / (t * 1e-3) / 1e9 if t > 0 else 0.0
+        out[n] = {"bytes": nbytes, "GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
+
+
 def copy_calibration(nbytes: int):
     import torch
     x = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -265,6 +293,7 @@ def main():
                   "aux_loss": float(aux["aux_loss"].item()),
                   "maxvio": float(aux["maxvio"].item())},
         "stage_ms": stage_ms,
+        "stage_gbs": stage_bandwidth(w, stage_ms, kept, e_active, eb),
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
