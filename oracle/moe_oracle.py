@@ -31,6 +31,8 @@ unless another page is named):
   * Shared experts that every token passes through without the router,
     section "细粒度专家与共享专家", equation h'_t (DeepSeek-V3 form).
   * Group-limited (node-limited) selection, section "设备受限与节点受限路由".
+  * Router z-loss L_z = (1/T) sum_t (log sum_j exp H_{t,j})^2 (ST-MoE),
+    section "各家的变体", subsection "Router z-loss 与数值稳定", equation L_z.
 
 Readings where the pages are silent or ambiguous are listed in the design doc of the
 repository; the ones that change arithmetic are restated next to the code.
@@ -295,6 +297,23 @@ def load_stats(s, idx, fill_result: dict, score: str) -> dict:
             "n_dropped": n_dropped}
 
 
+def router_z_loss(H) -> float:
+    """Router z-loss: the mean over tokens of the squared log-sum-exp of the
+    token's router logits, L_z = (1/T) sum_t (log sum_j exp H_{t,j})^2.
+
+    H are the logits the scores are taken from (with the logit bias and the
+    noise term when the router has them).  The log-sum-exp is evaluated as
+    max_j H + log sum_j exp(H - max_j H), which is the same number without
+    overflow.  T = 0 gives 0.
+    """
+    H = f64(H)
+    if H.shape[0] == 0:
+        return 0.0
+    m = H.max(axis=1)
+    lse = m + np.log(np.exp(H - m[:, None]).sum(axis=1))
+    return float(np.mean(lse * lse))
+
+
 # --------------------------------------------------------------------------- layer
 def route(H, k: int, score: str, gate: str, C: int, fill_order: str = FILL_RANK_MAJOR,
           b_sel=None, n_groups: int = 1, topk_groups: int = 1) -> dict:
@@ -318,6 +337,7 @@ def route(H, k: int, score: str, gate: str, C: int, fill_order: str = FILL_RANK_
     g = gates(s, idx, gate)
     fr = fill(idx, H.shape[1], C, fill_order)
     st = load_stats(s, idx, fr, score)
+    st["z_loss"] = router_z_loss(H)
     out = {"logits": H, "s": s, "idx": idx, "gate": g}
     out.update(fr)
     out.update(st)

@@ -127,6 +127,42 @@ def test_zloss_bf16_example():
     assert abs(sb - 1.0 / 11.0) < 1e-15
 
 
+def test_router_z_loss_closed_forms():
+    # equal logits c over E experts: log-sum-exp = c + log E
+    for E, c in ((8, 0.0), (64, -3.25), (256, 17.5)):
+        H = np.full((5, E), c)
+        assert abs(O.router_z_loss(H) - (c + math.log(E)) ** 2) < 1e-12 * max(1.0, (c + math.log(E)) ** 2)
+    # logits (0, log 3): log-sum-exp = log 4 exactly
+    H = np.array([[0.0, math.log(3.0)]])
+    assert abs(O.router_z_loss(H) - math.log(4.0) ** 2) < 1e-15
+    # the mean over tokens: two tokens with log-sum-exp 1 and 3 give (1 + 9) / 2
+    H = np.array([[1.0 - math.log(2.0), 1.0 - math.log(2.0)], [3.0, -np.inf]])
+    assert abs(O.router_z_loss(H) - 5.0) < 1e-14
+    # huge logits: no overflow, the shift comes out exactly
+    H = np.array([[1000.0, 1000.0, 1000.0, 1000.0]])
+    assert abs(O.router_z_loss(H) - (1000.0 + math.log(4.0)) ** 2) < 1e-9
+    assert O.router_z_loss(np.zeros((0, 4))) == 0.0
+
+
+def test_router_z_loss_gradient_matches_page():
+    # the page gives dL_z/dH_{t,k} = (2/T) LSE(H_t) softmax(H_t)_k; central
+    # differences of the oracle's L_z must reproduce it
+    r = rng(7)
+    H = r.normal(0.0, 2.0, size=(3, 6))
+    T = H.shape[0]
+    lse = np.log(np.exp(H).sum(axis=1))
+    sm = np.exp(H - lse[:, None])
+    want = 2.0 / T * lse[:, None] * sm
+    eps = 1e-6
+    got = np.zeros_like(H)
+    for t in range(H.shape[0]):
+        for j in range(H.shape[1]):
+            Hp = H.copy(); Hp[t, j] += eps
+            Hm = H.copy(); Hm[t, j] -= eps
+            got[t, j] = (O.router_z_loss(Hp) - O.router_z_loss(Hm)) / (2 * eps)
+    np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-9)
+
+
 # ----------------------------------------------------------------- selection
 def test_topk_ties_lower_index_wins():
     H = np.zeros((5, 8))
