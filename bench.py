@@ -210,7 +210,7 @@ def main():
     x = I.make_inputs(w, seed=args.seed, device=dev)
     cfg = B.make_config(w)
     ws = B.new_workspace(cfg, B.MOE_WS_LAYER, dev)
-    aux = B.alloc_aux(cfg, dev, ["kept", "n_dropped", "aux_loss", "maxvio"])
+    aux = B.alloc_aux(cfg, dev, ["kept", "n_dropped", "aux_loss", "maxvio", "z_loss"])
     out = torch.empty((w.T, w.h), dtype=I.torch_dtype(w), device=dev)
     nst = B.MOE_NUM_STAGES
 
@@ -291,7 +291,8 @@ def main():
                   "hbm_frac_alg": b_alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                   "kept_rows": kept, "dropped": n_drop, "active_experts": e_active,
                   "aux_loss": float(aux["aux_loss"].item()),
-                  "maxvio": float(aux["maxvio"].item())},
+                  "maxvio": float(aux["maxvio"].item()),
+                  "z_loss": float(aux["z_loss"].item())},
         "stage_ms": stage_ms,
         "stage_gbs": stage_bandwidth(w, stage_ms, kept, e_active, eb),
     }

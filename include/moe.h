@@ -126,6 +126,9 @@ typedef struct {
   void* X;             /* [rows_max, h] permuted expert inputs                */
   void* Y;             /* [rows_max, h] expert outputs                        */
   void* Y_shared;      /* [n_shared, T, h] shared-expert outputs              */
+  float* z_loss;       /* [1] router z-loss: mean over tokens of the squared
+                          log-sum-exp of the logits routing used (section
+                          "各家的变体", "Router z-loss 与数值稳定", eq. L_z)   */
 } moe_aux_outputs;
 
 /* Workspace sizes per entry point. */
@@ -225,6 +228,16 @@ int32_t moe_update_bias(const moe_config* cfg, const int32_t* count, float* b_se
 int32_t moe_stats(const moe_config* cfg, const int32_t* count, const int32_t* kept,
                   const float* prob_sum, float* f, float* P, float* aux_loss, float* maxvio,
                   int32_t* n_dropped, void* stream);
+
+/* Router z-loss L_z = (1/T) sum_t (log sum_j exp logits[t,j])^2 of given
+ * float32 logits [T, E] (page "MoE 与专家并行", section "各家的变体",
+ * subsection "Router z-loss 与数值稳定", eq. L_z), written to z_loss[0] (device
+ * float).  The layer computes the same number from its own logits without
+ * materialising them (moe_aux_outputs.z_loss); this call serves the staged
+ * path.  One workgroup, a fixed summation order (deterministic).  Errors:
+ * MOE_ERR_INVALID_ARG for a NULL pointer (logits may be NULL when T = 0). */
+int32_t moe_router_z_loss(const moe_config* cfg, const float* logits, float* z_loss,
+                          void* stream);
 
 /* The whole layer: route, dispatch, experts (and shared experts), combine,
  * statistics.

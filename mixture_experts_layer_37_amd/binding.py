@@ -48,7 +48,8 @@ class moe_config(ctypes.Structure):
 class moe_aux_outputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "topk_idx", "topk_gate", "logits", "slot", "row_token", "count", "kept", "offset",
-        "prob_sum", "f", "P", "aux_loss", "maxvio", "n_dropped", "X", "Y", "Y_shared")]
+        "prob_sum", "f", "P", "aux_loss", "maxvio", "n_dropped", "X", "Y", "Y_shared",
+        "z_loss")]
 
 
 AUX_FIELDS = [n for n, _ in moe_aux_outputs._fields_]
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "moe_shared_ffn": (I32, [cfgp] + [P] * 5 + [P, SZ, P]),
             "moe_update_bias": (I32, [cfgp, P, P, ctypes.c_float, P]),
             "moe_stats": (I32, [cfgp] + [P] * 8 + [P]),
+            "moe_router_z_loss": (I32, [cfgp, P, P, P]),
             "moe_layer_forward": (I32, [cfgp] + [P] * 13 + [ctypes.POINTER(moe_aux_outputs), P,
                                                           P, SZ, P]),
         }
@@ -280,6 +282,14 @@ def moe_stats(cfg, count, kept, prob_sum, f=None, P=None, aux_loss=None, maxvio=
     _check(lib().moe_stats(ctypes.byref(cfg), *args, _stream(stream)), "moe_stats")
 
 
+def moe_router_z_loss(cfg, logits, z_loss, stream=None):
+    """z_loss[0] = mean over tokens of the squared log-sum-exp of logits [T, E]."""
+    _check(lib().moe_router_z_loss(ctypes.byref(cfg),
+                                   _ptr(logits, "logits", (cfg.T, cfg.E), torch.float32),
+                                   _ptr(z_loss, "z_loss", (1,), torch.float32),
+                                   _stream(stream)), "moe_router_z_loss")
+
+
 _AUX_SPEC = {
     "topk_idx": (lambda c, r: (c.T, c.k), torch.int32),
     "topk_gate": (lambda c, r: (c.T, c.k), torch.float32),
@@ -298,6 +308,7 @@ _AUX_SPEC = {
     "X": (lambda c, r: (r, c.h), None),
     "Y": (lambda c, r: (r, c.h), None),
     "Y_shared": (lambda c, r: (c.n_shared, c.T, c.h), None),
+    "z_loss": (lambda c, r: (1,), torch.float32),
 }
 
 

@@ -137,8 +137,9 @@ RouteWs plan_route(const Dims& d, int noisy, Plan& pl) {
   w.rs = route_shape((int)d.T, (int)d.E, d.bf16, noisy);
   w.wt = d.bf16 ? pl.add((size_t)w.rs.EP * d.h * 2) : 0;
   w.wnt = (d.bf16 && noisy) ? pl.add((size_t)w.rs.EP * d.h * 2) : 0;
-  w.part = pl.add((size_t)(w.rs.nblk > 0 ? w.rs.nblk : 1) * w.rs.EP * sizeof(double));
-  w.total = pl.add((size_t)w.rs.EP * sizeof(double));
+  // per-workgroup partials: EP score columns and one LSE^2 column
+  w.part = pl.add((size_t)(w.rs.nblk > 0 ? w.rs.nblk : 1) * (w.rs.EP + 1) * sizeof(double));
+  w.total = pl.add((size_t)(w.rs.EP + 1) * sizeof(double));
   return w;
 }
 
@@ -527,8 +528,17 @@ int32_t moe_stats(const moe_config* cfg, const int32_t* count, const int32_t* ke
   if (st != MOE_OK) return st;
   if (!count || !kept || !prob_sum) return MOE_ERR_INVALID_ARG;
   StatsParams p{(int)cfg->T, (int)cfg->E, (int)cfg->k, count, kept, nullptr,
-                prob_sum, f, P, aux_loss, maxvio, n_dropped};
+                prob_sum, f, P, aux_loss, maxvio, n_dropped, nullptr};
   return hip_status(launch_stats(p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_router_z_loss(const moe_config* cfg, const float* logits, float* z_loss,
+                          void* stream) {
+  const int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!z_loss || (cfg->T > 0 && !logits)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_z_loss(logits, (int)cfg->T, (int)cfg->E, z_loss,
+                                  static_cast<hipStream_t>(stream)));
 }
 
 int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
@@ -600,7 +610,7 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
                  nullptr, o.f, o.P,
                  o.aux_loss ? o.aux_loss : at<float>(ws, w.scal),
                  o.maxvio ? o.maxvio : at<float>(ws, w.scal) + 1,
-                 o.n_dropped ? o.n_dropped : at<int32_t>(ws, w.scal) + 2};
+                 o.n_dropped ? o.n_dropped : at<int32_t>(ws, w.scal) + 2, o.z_loss};
   MOE_TRY(launch_stats(sp, s));
   MOE_TRY(mark(6));
   return MOE_OK;

@@ -91,6 +91,8 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsParams p) {
     if (p.aux) p.aux[0] = (float)(p.E * s_fp[0]);
     if (p.maxvio) p.maxvio[0] = p.T > 0 ? (float)((s_max[0] - mean) / mean) : 0.f;
     if (p.n_dropped) p.n_dropped[0] = s_drop[0];
+    if (p.z_loss && p.prob_total)
+      p.z_loss[0] = p.T > 0 ? (float)(p.prob_total[p.E] / p.T) : 0.f;
   }
 }
 
@@ -115,7 +117,43 @@ __global__ __launch_bounds__(256) void update_bias_kernel(const int32_t* count, 
   }
 }
 
+// Router z-loss of given float32 logits [T][E] (section "各家的变体",
+// subsection "Router z-loss 与数值稳定", eq. L_z): one workgroup of 16 waves,
+// wave w takes tokens w, w + 16, ...; a token's E <= 256 logits are spread
+// over the 64 lanes, LSE = max + log sum exp(x - max) by butterfly
+// reductions; per-wave float64 sums are added in wave order.
+__global__ __launch_bounds__(1024) void z_loss_kernel(const float* logits, int T, int E,
+                                                      float* z_loss) {
+  __shared__ double s_w[16];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  double acc = 0.0;
+  for (int t = wave; t < T; t += 16) {
+    const float* row = logits + (size_t)t * E;
+    float x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = lane + 64 * j < E ? row[lane + 64 * j] : -INFINITY;
+    const float m = wave_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+    float z = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z += lane + 64 * j < E ? expf(x[j] - m) : 0.f;
+    const float lse = m + logf(wave_sum(z));
+    acc += (double)lse * (double)lse;
+  }
+  if (lane == 0) s_w[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double s = 0.0;
+    for (int w = 0; w < 16; ++w) s += s_w[w];
+    z_loss[0] = T > 0 ? (float)(s / T) : 0.f;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_z_loss(const float* logits, int T, int E, float* z_loss, hipStream_t s) {
+  hipLaunchKernelGGL(z_loss_kernel, dim3(1), dim3(1024), 0, s, logits, T, E, z_loss);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const void* U, const void* Y, const int32_t* slot, const float* gate,
                           const void* Ys, int ns, void* out, int T, int h, int k, int bf16_,

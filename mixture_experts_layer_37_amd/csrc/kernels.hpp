@@ -23,7 +23,8 @@ struct RouteParams {
   int32_t* topk_idx;
   float* topk_gate;
   float* logits;     // optional [T][E]
-  double* prob_part; // [nblk][EP] per-block sums of the score entering P
+  double* prob_part; // [nblk][EP + 1] per-block sums of the score entering P;
+                     // column EP: sum over the block's tokens of LSE(H_t)^2
 };
 
 struct RouteShape {
@@ -39,8 +40,9 @@ hipError_t launch_transpose_router_w(const void* W, void* WT, int h, int E, int 
                                      hipStream_t s);
 hipError_t launch_route(const RouteShape& rs, const RouteParams& p, int bf16, int noisy,
                         hipStream_t s);
-// total[e] (double, optional) and prob_sum[e] (float, optional): sums over
-// the router's per-workgroup partials.
+// total[e] (double, optional; E + 1 entries, the last the sum over tokens of
+// LSE(H_t)^2) and prob_sum[e] (float, optional, E entries): sums over the
+// router's per-workgroup partials.
 hipError_t launch_prob_reduce(const double* part, int nblk, int EP, int E, double* total,
                               float* prob_sum, hipStream_t s);
 
@@ -108,14 +110,17 @@ struct StatsParams {
   int T, E, k;
   const int32_t* count;
   const int32_t* kept;
-  const double* prob_total;  // [E] (layer) or NULL
+  const double* prob_total;  // [E + 1] (layer; entry E: sum of LSE^2) or NULL
   const float* prob_sum;     // [E] (standalone) or NULL
   float* f;
   float* P;
   float* aux;
   float* maxvio;
   int32_t* n_dropped;
+  float* z_loss;             // mean over tokens of LSE^2 (needs prob_total), or NULL
 };
 hipError_t launch_stats(const StatsParams& p, hipStream_t s);
+// z_loss[0] = mean over the T tokens of LSE(logits[t, :E])^2 (E <= 256).
+hipError_t launch_z_loss(const float* logits, int T, int E, float* z_loss, hipStream_t s);
 
 }  // namespace moe

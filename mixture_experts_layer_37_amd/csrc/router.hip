@@ -1,6 +1,8 @@
 // Router: logits H = U W_r (+ b_r) (+ noise * softplus(U W_noise)), scores,
 // top-k with the (-H, expert index) key, gates, and per-workgroup sums of the
-// score that enters P.
+// score that enters P and of the squared log-sum-exp of the logits (the
+// router z-loss, section "各家的变体", subsection "Router z-loss 与数值稳定",
+// equation L_z, of the same page).
 //
 // Method: page "MoE 与专家并行", section "路由器：打分、top-k、加权求和"
 // (eq. H = U W_r and the noisy-top-k eq. G(x)), the scoring table of section
@@ -31,7 +33,7 @@ __device__ __forceinline__ float softplus_f(float x) {
 // Shared epilogue.  L (and Ln) hold the [RB][EP] float32 products of this
 // workgroup's tokens.
 template <int EP, int RB, bool NOISY>
-__device__ void route_epilogue(const float* L, const float* Ln, double (*Ps)[EP],
+__device__ void route_epilogue(const float* L, const float* Ln, double (*Ps)[EP + 1],
                                const RouteParams& p, int t0) {
   constexpr int J = (EP + 63) / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -39,6 +41,7 @@ __device__ void route_epilogue(const float* L, const float* Ln, double (*Ps)[EP]
   double pacc[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) pacc[j] = 0.0;
+  double zacc = 0.0;  // sum over this wave's tokens of LSE(H_t)^2 (wave-uniform)
 
   for (int tt = wave; tt < RB; tt += 4) {
     const int t = t0 + tt;
@@ -75,6 +78,8 @@ __device__ void route_epilogue(const float* L, const float* Ln, double (*Ps)[EP]
         s[j] = s[j] / Z;
         pacc[j] += (double)s[j];
       }
+      const float lse = m + logf(Z);
+      zacc += (double)lse * (double)lse;
     } else {
       float z = 0.f;
 #pragma unroll
@@ -85,6 +90,16 @@ __device__ void route_epilogue(const float* L, const float* Ln, double (*Ps)[EP]
       S = wave_sum(z);
 #pragma unroll
       for (int j = 0; j < J; ++j) pacc[j] += (double)(s[j] / S);
+      // z-loss of the logits: log-sum-exp with the max taken out
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < J; ++j) mx = fmaxf(mx, v[j]);
+      mx = wave_max(mx);
+      float ze = 0.f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) ze += (lane + 64 * j < E) ? expf(v[j] - mx) : 0.f;
+      const float lse = mx + logf(wave_sum(ze));
+      zacc += (double)lse * (double)lse;
     }
     // Selection keys.  Plain routing takes the top-k on the logits (the same
     // order as the scores).  With a selection bias or groups the keys are the
@@ -204,15 +219,18 @@ __device__ void route_epilogue(const float* L, const float* Ln, double (*Ps)[EP]
       p.topk_gate[(size_t)t * k + lane] = (p.gate == 1) ? my_s / gsum : my_s;
     }
   }
-  // per-workgroup sums of the P score, waves added in a fixed order
+  // per-workgroup sums of the P score and (column EP) of LSE^2, waves added
+  // in a fixed order
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int e = lane + 64 * j;
     if (e < EP) Ps[wave][e] = pacc[j];
   }
+  if (lane == 0) Ps[wave][EP] = zacc;
   __syncthreads();
-  for (int e = threadIdx.x; e < EP; e += blockDim.x)
-    p.prob_part[(size_t)blockIdx.x * EP + e] = ((Ps[0][e] + Ps[1][e]) + Ps[2][e]) + Ps[3][e];
+  for (int e = threadIdx.x; e <= EP; e += blockDim.x)
+    p.prob_part[(size_t)blockIdx.x * (EP + 1) + e] =
+        ((Ps[0][e] + Ps[1][e]) + Ps[2][e]) + Ps[3][e];
 }
 
 template <int NB, int MW, bool NOISY>
@@ -220,7 +238,7 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteParams p) {
   constexpr int EP = 16 * NB, RB = 16 * MW;
   __shared__ float L[RB * EP];
   __shared__ float Ln[NOISY ? RB * EP : 1];
-  __shared__ double Ps[4][EP];
+  __shared__ double Ps[4][EP + 1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * RB;
   const int h = p.h;
@@ -304,7 +322,7 @@ __global__ __launch_bounds__(256) void route_f32_kernel(RouteParams p) {
   constexpr int EP = 16 * NB, RB = 16;
   __shared__ float L[RB * EP];
   __shared__ float Ln[NOISY ? RB * EP : 1];
-  __shared__ double Ps[4][EP];
+  __shared__ double Ps[4][EP + 1];
   const int t0 = blockIdx.x * RB;
   const float* U = static_cast<const float*>(p.U);
   const float* W = static_cast<const float*>(p.Wt);
@@ -341,14 +359,17 @@ __global__ void transpose_kernel(const bf16* W, bf16* WT, int h, int E, int EP) 
   }
 }
 
-// One workgroup per expert: thread j adds partials j, j + 256, ... in order,
-// then a fixed-shape tree adds the 256 sums (deterministic).
+// One workgroup per column (E experts, then the LSE^2 column): thread j adds
+// partials j, j + 256, ... in order, then a fixed-shape tree adds the 256
+// sums (deterministic).  Column E lands in total[E] (z-loss numerator); out
+// gets the E expert sums only.
 __global__ __launch_bounds__(256) void prob_reduce_kernel(const double* part, int nblk, int EP,
-                                                          double* total, float* out) {
+                                                          int E, double* total, float* out) {
   __shared__ double sh[256];
   const int e = blockIdx.x;
+  const int col = e < E ? e : EP;
   double s = 0.0;
-  for (int b = threadIdx.x; b < nblk; b += 256) s += part[(size_t)b * EP + e];
+  for (int b = threadIdx.x; b < nblk; b += 256) s += part[(size_t)b * (EP + 1) + col];
   sh[threadIdx.x] = s;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
@@ -357,7 +378,7 @@ __global__ __launch_bounds__(256) void prob_reduce_kernel(const double* part, in
   }
   if (threadIdx.x == 0) {
     if (total) total[e] = sh[0];
-    if (out) out[e] = (float)sh[0];
+    if (out && e < E) out[e] = (float)sh[0];
   }
 }
 
@@ -427,8 +448,9 @@ hipError_t launch_route(const RouteShape& rs, const RouteParams& p, int bf16, in
 
 hipError_t launch_prob_reduce(const double* part, int nblk, int EP, int E, double* total,
                               float* prob_sum, hipStream_t s) {
-  hipLaunchKernelGGL(prob_reduce_kernel, dim3(E), dim3(256), 0, s, part, nblk, EP, total,
-                     prob_sum);
+  // the z-loss column only when its sum has somewhere to go
+  hipLaunchKernelGGL(prob_reduce_kernel, dim3(total ? E + 1 : E), dim3(256), 0, s, part, nblk,
+                     EP, E, total, prob_sum);
   return hipGetLastError();
 }
 

@@ -131,6 +131,7 @@ def route_given_selection(w, H, idx) -> dict:
     r = {"logits": H, "s": s, "idx": idx, "gate": O.gates(s, idx, ORACLE_MODE[w.gate])}
     r.update(fr)
     r.update(O.load_stats(s, idx, fr, ORACLE_MODE[w.score]))
+    r["z_loss"] = O.router_z_loss(H)
     return r
 
 
@@ -189,6 +190,9 @@ def check_stats(w, g: dict, r: dict):
     np.testing.assert_allclose(float(to_np(g["maxvio"])[0]), r["maxvio"], rtol=1e-6,
                                atol=1e-6, err_msg="maxvio")
     assert int(to_np(g["n_dropped"])[0]) == r["n_dropped"]
+    if "z_loss" in g:  # from the same (GPU) logits: float32 log-sum-exp, float64 sums
+        np.testing.assert_allclose(float(to_np(g["z_loss"])[0]), r["z_loss"], rtol=2e-6,
+                                   atol=1e-6, err_msg="z_loss")
 
 
 def check_logits_end_to_end(w, g: dict, x_cpu: dict, tokens=None) -> dict:

@@ -153,6 +153,10 @@ def test_bad_enums_and_null_pointers():
                   None) == B.MOE_ERR_INVALID_ARG
     assert status("moe_stats", ctypes.byref(cfg), None, fake, fake, None, None, None, None,
                   None, None) == B.MOE_ERR_INVALID_ARG
+    # the z-loss helper needs its output, and logits when there are tokens
+    assert status("moe_router_z_loss", ctypes.byref(cfg), fake, None, None) == B.MOE_ERR_INVALID_ARG
+    assert status("moe_router_z_loss", ctypes.byref(cfg), None, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert status("moe_router_z_loss", None, fake, fake, None) == B.MOE_ERR_INVALID_ARG
     # noisy routing without the noise draws
     ncfg = cfg_of(noisy=True)
     assert status("moe_route", ctypes.byref(ncfg), fake, fake, None, None, fake, None, fake,

@@ -4,6 +4,8 @@ Small versions of all five workloads are checked completely; the full-size
 workloads are checked in the launch configuration the benchmark times, with
 routing compared on every token and expert outputs on sampled rows.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -211,6 +213,21 @@ def test_all_logits_equal_and_one_hot_load():
     L.check_outputs_small(w, g, xc, r)
     np.testing.assert_allclose(L.to_np(g["aux_loss"])[0], float(w.E * (r["f"] * r["P"]).sum()),
                                rtol=1e-6)
+
+
+@pytest.mark.parametrize("T,E,scale", [(1, 8, 1.0), (300, 64, 4.0), (2049, 256, 30.0), (0, 8, 1.0)])
+def test_router_z_loss_entry(T, E, scale):
+    """moe_router_z_loss on given logits (wide and large ones included) against
+    the oracle's L_z of the same float32 values."""
+    w = dataclasses.replace(I.WORKLOADS["tiny_f32"], T=T, E=E, k=2)
+    cfg = B.make_config(w)
+    g = torch.Generator().manual_seed(T + E)
+    H = (torch.randn(T, E, generator=g) * scale + 5.0).to(torch.float32)
+    z = torch.full((1,), -1.0, device=DEV)
+    B.moe_router_z_loss(cfg, H.to(DEV) if T else None, z)
+    torch.cuda.synchronize()
+    want = O.router_z_loss(H.double().numpy())
+    np.testing.assert_allclose(float(z.cpu()[0]), want, rtol=2e-6, atol=1e-7)
 
 
 def test_empty_batch():
