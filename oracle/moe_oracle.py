@@ -33,6 +33,10 @@ unless another page is named):
   * Group-limited (node-limited) selection, section "设备受限与节点受限路由".
   * Router z-loss L_z = (1/T) sum_t (log sum_j exp H_{t,j})^2 (ST-MoE),
     section "各家的变体", subsection "Router z-loss 与数值稳定", equation L_z.
+  * FP8 dispatch and FP8 up-projection with power-of-two scaling factors and
+    a BF16 combine (DeepSeek-V3), section "低精度通信".  The FP8 format is OCP
+    E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest
+    finite value 448), the one gfx950's FP8 matrix instructions read.
 
 Readings where the pages are silent or ambiguous are listed in the design doc of the
 repository; the ones that change arithmetic are restated next to the code.
@@ -314,6 +318,69 @@ def router_z_loss(H) -> float:
     return float(np.mean(lse * lse))
 
 
+# --------------------------------------------------------------------------- FP8
+FP8_E4M3_MAX = 448.0
+
+
+def fp8_e4m3_decode(code: int) -> float:
+    """Value of an OCP E4M3 byte: sign bit 7, exponent bits 6..3 (bias 7),
+    mantissa bits 2..0.  Exponent field 0 holds the subnormals m/8 * 2^-6;
+    the pattern S.1111.111 is NaN (the format has no infinities)."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def fp8_e4m3_round(x) -> np.ndarray:
+    """Round to the nearest E4M3 value, ties to the even mantissa, for
+    |x| <= 448 (the caller scales into that range).  Between 2^p and 2^(p+1)
+    the E4M3 values are spaced 2^(p-3) apart for p >= -6; below 2^-6 the
+    subnormals are spaced 2^-9 apart."""
+    x = f64(x)
+    a = np.abs(x)
+    if np.any(a > FP8_E4M3_MAX):
+        raise ValueError("value outside the E4M3 range")
+    _, p1 = np.frexp(np.where(a > 0, a, 1.0))       # a = m 2^p1, 0.5 <= m < 1: p = p1 - 1
+    spacing = np.ldexp(1.0, np.maximum(p1 - 1, -6) - 3)
+    return np.sign(x) * np.round(a / spacing) * spacing   # np.round: half to even
+
+
+def fp8_row_scale(amax: float) -> float:
+    """Power-of-two scaling factor of a row with largest magnitude amax: the
+    smallest s = 2^j with amax / s <= 448 (1 for an all-zero row)."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 1.0
+    j = math.frexp(amax)[1] - 12                      # amax / 2^j >= 2048 > 448
+    while amax / 2.0 ** j > FP8_E4M3_MAX:
+        j += 1
+    return 2.0 ** j
+
+
+def quantize_rows_fp8(X):
+    """Row-wise FP8 quantisation: s_r = fp8_row_scale(max_j |X[r, j]|) and
+    q[r] = the E4M3 rounding of X[r] / s_r.  Returns (q, s); q * s[:, None]
+    is the dequantised matrix."""
+    X = f64(X)
+    s = np.array([fp8_row_scale(np.abs(row).max() if row.size else 0.0) for row in X])
+    q = np.stack([fp8_e4m3_round(row / sr) for row, sr in zip(X, s)]) if len(X) else X.copy()
+    return q, s
+
+
+def expert_outputs_fp8(Xq, xs, offset, Wq_gate, s_gate, Wq_up, s_up, W_down) -> np.ndarray:
+    """Y rows with the up-projection in FP8: expert e computes
+    a = SiLU((x_q s_x) (W_gate,q s_gate)^T) * ((x_q s_x) (W_up,q s_up)^T) from the
+    dequantised values, then y = a W_down^T with the BF16 down weights."""
+    X = f64(Xq) * f64(xs)[:, None]
+    Wg = f64(Wq_gate) * f64(s_gate)[..., None]
+    Wu = f64(Wq_up) * f64(s_up)[..., None]
+    return expert_outputs(X, offset, Wg, Wu, W_down)
+
+
 # --------------------------------------------------------------------------- layer
 def route(H, k: int, score: str, gate: str, C: int, fill_order: str = FILL_RANK_MAJOR,
           b_sel=None, n_groups: int = 1, topk_groups: int = 1) -> dict:
@@ -391,12 +458,16 @@ def layer_forward(U, W_r, W_gate, W_up, W_down, *, k: int, score: str, gate: str
                   fill_order: str = FILL_RANK_MAJOR, min_capacity: int = 0,
                   b_r=None, W_noise=None, noise=None, logits=None, b_sel=None,
                   n_groups: int = 1, topk_groups: int = 1, Ws_gate=None, Ws_up=None,
-                  Ws_down=None) -> dict:
+                  Ws_down=None, fp8_up: bool = False) -> dict:
     """The whole layer for small inputs.
 
     logits, when given, replaces the router product (used to route from exactly
     the logits another implementation produced).  b_sel, n_groups/topk_groups
-    and the shared-expert weights Ws_* add the DeepSeek-V3 parts.
+    and the shared-expert weights Ws_* add the DeepSeek-V3 parts.  fp8_up:
+    the dispatched rows and the routed experts' W_gate and W_up are quantised
+    row-wise to FP8 (quantize_rows_fp8) and the up-projection works on the
+    dequantised values; the router, the residual, W_down, the shared experts
+    and the combine keep the inputs' own values.
     """
     U = f64(U)
     T = U.shape[0]
@@ -405,7 +476,16 @@ def layer_forward(U, W_r, W_gate, W_up, W_down, *, k: int, score: str, gate: str
     C = capacity(T, E, k, capacity_factor, cap_mode, min_capacity)
     r = route(H, k, score, gate, C, fill_order, b_sel, n_groups, topk_groups)
     X = U[r["row_token"]]
-    Y = expert_outputs(X, r["offset"], W_gate, W_up, W_down)
+    if fp8_up:
+        Xq, xs = quantize_rows_fp8(X)
+        E_, f_, h_ = np.asarray(W_gate).shape
+        Wgq, sg = quantize_rows_fp8(f64(W_gate).reshape(E_ * f_, h_))
+        Wuq, su = quantize_rows_fp8(f64(W_up).reshape(E_ * f_, h_))
+        Y = expert_outputs_fp8(Xq, xs, r["offset"], Wgq.reshape(E_, f_, h_), sg.reshape(E_, f_),
+                               Wuq.reshape(E_, f_, h_), su.reshape(E_, f_), W_down)
+        r["Xq"], r["x_scale"] = Xq, xs
+    else:
+        Y = expert_outputs(X, r["offset"], W_gate, W_up, W_down)
     r["X"] = X
     r["Y"] = Y
     r["Y_shared"] = None if Ws_gate is None else shared_expert_outputs(U, Ws_gate, Ws_up, Ws_down)

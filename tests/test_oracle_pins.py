@@ -544,3 +544,90 @@ def test_shared_expert_is_an_always_on_expert():
     dense = O.dense_masked_forward(U, np.concatenate([Wg, Sg]), np.concatenate([Wu, Su]),
                                    np.concatenate([Wd, Sd]), g_dense)
     np.testing.assert_allclose(r["out"], dense, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------- FP8
+def _torch_e4m3(x):
+    """Round-trip through torch's float8_e4m3fn (round to nearest even)."""
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).double().numpy()
+
+
+def test_fp8_decode_table_matches_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([O.fp8_e4m3_decode(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    assert O.fp8_e4m3_decode(0x7E) == 448.0 and O.fp8_e4m3_decode(0x01) == 2.0 ** -9
+    assert sum(np.isnan(got)) == 2  # S.1111.111 only
+
+
+def test_fp8_rounding_matches_torch():
+    r = rng(11)
+    vals = [r.uniform(-448, 448, 4000), r.normal(0, 1, 4000), r.normal(0, 2 ** -7, 4000),
+            np.ldexp(r.uniform(-1, 1, 2000), r.integers(-12, 9, 2000))]
+    # exact midpoints between neighbouring E4M3 values (ties go to the even mantissa)
+    grid = np.unique(np.abs([O.fp8_e4m3_decode(c) for c in range(0x7F)]))
+    mids = (grid[1:] + grid[:-1]) / 2
+    vals += [mids, -mids]
+    x = np.concatenate(vals).astype(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(O.fp8_e4m3_round(x), _torch_e4m3(x))
+    with pytest.raises(ValueError):
+        O.fp8_e4m3_round(np.array([449.0]))
+
+
+def test_fp8_row_scale_and_quantisation():
+    assert O.fp8_row_scale(448.0) == 1.0 and O.fp8_row_scale(449.0) == 2.0
+    assert O.fp8_row_scale(224.0) == 0.5 and O.fp8_row_scale(0.0) == 1.0
+    r = rng(12)
+    for amax in np.ldexp(r.uniform(0.5, 1.0, 200), r.integers(-60, 60, 200)):
+        s = O.fp8_row_scale(amax)
+        assert math.frexp(s)[0] == 0.5               # a power of two
+        assert 224.0 < amax / s <= 448.0              # the top binade, never past 448
+    X = r.normal(0, 3, (5, 64))
+    X[2] = 0.0
+    q, s = O.quantize_rows_fp8(X)
+    assert s[2] == 1.0 and not q[2].any()
+    np.testing.assert_array_equal(q, _torch_e4m3(X / s[:, None]))
+    # relative error of a normal E4M3 value is at most 2^-4
+    big = np.abs(X * 1.0) >= s[:, None] * 2.0 ** -6
+    assert np.all(np.abs(q * s[:, None] - X)[big] <= 2.0 ** -4 * np.abs(X)[big])
+    # scaling a row by a power of two scales s and leaves the codes alone
+    q2, s2 = O.quantize_rows_fp8(X * 2.0 ** 13)
+    np.testing.assert_array_equal(q2, q)
+    nz = np.arange(len(s)) != 2
+    np.testing.assert_array_equal(s2[nz], s[nz] * 2.0 ** 13)
+    assert s2[2] == 1.0  # an all-zero row keeps the scale 1
+
+
+def test_fp8_layer_equals_plain_layer_on_the_grid():
+    # inputs already on the E4M3 grid with every row's largest magnitude in
+    # (224, 448]: quantisation is the identity and the FP8 layer is the layer
+    T, h, f, E, k = 24, 16, 12, 4, 2
+    r = rng(13)
+
+    def on_grid(shape):
+        a = _torch_e4m3(r.uniform(-448, 448, shape))
+        a.reshape(-1, shape[-1])[:, 0] = 448.0
+        return a
+
+    U = on_grid((T, h))
+    W = r.normal(0, 1 / math.sqrt(h), (h, E))
+    Wg, Wu = on_grid((E, f, h)), on_grid((E, f, h))
+    Wd = r.normal(0, 1e-6, (E, h, f))
+    a = O.layer_forward(U, W, Wg, Wu, Wd, k=k, score=O.SOFTMAX, gate=O.GATE_RENORM,
+                        capacity_factor=1.0)
+    b = O.layer_forward(U, W, Wg, Wu, Wd, k=k, score=O.SOFTMAX, gate=O.GATE_RENORM,
+                        capacity_factor=1.0, fp8_up=True)
+    np.testing.assert_array_equal(b["idx"], a["idx"])
+    np.testing.assert_array_equal(b["Xq"], a["X"])
+    np.testing.assert_array_equal(b["x_scale"], 1.0)
+    np.testing.assert_allclose(b["out"], a["out"], rtol=1e-13, atol=1e-13)
+    # off the grid the FP8 layer differs, by about the E4M3 rounding
+    U2 = U * 0.3
+    c = O.layer_forward(U2, W, Wg * 0.7, Wu, Wd, k=k, score=O.SOFTMAX, gate=O.GATE_RENORM,
+                        capacity_factor=1.0, fp8_up=True)
+    d = O.layer_forward(U2, W, Wg * 0.7, Wu, Wd, k=k, score=O.SOFTMAX, gate=O.GATE_RENORM,
+                        capacity_factor=1.0)
+    rel = np.abs(c["out"] - d["out"] - (U2 - U2)).max() / np.abs(d["out"] - U2).max()
+    assert 0 < rel < 0.2
