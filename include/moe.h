@@ -255,6 +255,60 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
                           void* const* stage_events, void* ws, size_t ws_bytes,
                           void* stream);
 
+/* ---------------------------------------------------------------- FP8
+ * FP8 dispatch and FP8 up-projection (page "MoE 与专家并行", section
+ * "低精度通信": DeepSeek-V3 quantises the activations before the MoE
+ * up-projection to FP8 with power-of-two scaling factors, dispatches them at
+ * one byte per element, runs the up-projection in FP8 and keeps the combine
+ * in BF16).  Format: OCP E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; largest finite value 448).  Row-wise scales: a row with largest
+ * magnitude amax gets s = 2^j, j the smallest integer with amax / s <= 448
+ * (s = 1 for an all-zero row), and its codes are x / s rounded to the nearest
+ * E4M3 value, ties to even.  Only the routed experts' gate and up products
+ * run on FP8; the router, the residual, W_down, the shared experts and the
+ * combine keep the bf16 inputs.  Requirements of the calls below (else
+ * MOE_ERR_UNSUPPORTED): cfg->dtype == MOE_BF16 and h a multiple of 128. */
+
+/* Row-wise E4M3 codes of a bf16 matrix src [rows, cols] (device), into dst
+ * [rows, cols] bytes and scale [rows] float32 (device, caller-owned), e.g.
+ * the expert weights W_gate or W_up viewed as [E*f, h] (done once, outside
+ * the forward).  cols a multiple of 8 (else MOE_ERR_UNSUPPORTED); NULL
+ * pointers with rows > 0 or cols <= 0: MOE_ERR_INVALID_ARG. */
+int32_t moe_quantize_rows_fp8(const void* src, int64_t rows, int64_t cols, void* dst,
+                              float* scale, void* stream);
+
+/* moe_dispatch with the permuted rows in FP8: X8 [rows_max, h] bytes of E4M3
+ * codes and x_scale [rows_max] float32, the scale of each row's token (the
+ * other outputs as in moe_dispatch).  ws: MOE_WS_DISPATCH bytes. */
+int32_t moe_dispatch_fp8(const moe_config* cfg, const void* U, const int32_t* topk_idx,
+                         void* X8, float* x_scale, int32_t* row_token, int32_t* slot,
+                         int32_t* count, int32_t* kept, int32_t* offset, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* moe_expert_ffn with the up-projection on FP8: X8, x_scale from
+ * moe_dispatch_fp8; W8_gate, W8_up [E, f, h] E4M3 codes with s_gate, s_up
+ * [E, f] row scales (moe_quantize_rows_fp8 of W_gate, W_up); W_down [E, h, f]
+ * bf16.  a = SiLU(g) * u with g = sum_k X8[r,k] x_scale[r] W8_gate[e,n,k]
+ * s_gate[e,n] (float32 accumulation), rounded to bf16; Y as in
+ * moe_expert_ffn.  ws: MOE_WS_EXPERT_FFN bytes. */
+int32_t moe_expert_ffn_fp8(const moe_config* cfg, const void* X8, const float* x_scale,
+                           const int32_t* offset, const void* W8_gate, const float* s_gate,
+                           const void* W8_up, const float* s_up, const void* W_down, void* Y,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* moe_layer_forward with the FP8 dispatch and up-projection: W8_gate, s_gate,
+ * W8_up, s_up as in moe_expert_ffn_fp8 replace W_gate and W_up; every other
+ * argument as in moe_layer_forward, except that aux->X is not written (the
+ * FP8 rows stay in the workspace; moe_dispatch_fp8 returns them).
+ * ws: MOE_WS_LAYER bytes. */
+int32_t moe_layer_forward_fp8(const moe_config* cfg, const void* U, const void* W_r,
+                              const float* b_r, const float* b_sel, const void* W_noise,
+                              const float* noise, const void* W8_gate, const float* s_gate,
+                              const void* W8_up, const float* s_up, const void* W_down,
+                              const void* Ws_gate, const void* Ws_up, const void* Ws_down,
+                              void* out, const moe_aux_outputs* aux, void* const* stage_events,
+                              void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

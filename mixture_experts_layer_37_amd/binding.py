@@ -82,6 +82,11 @@ def lib() -> ctypes.CDLL:
             "moe_router_z_loss": (I32, [cfgp, P, P, P]),
             "moe_layer_forward": (I32, [cfgp] + [P] * 13 + [ctypes.POINTER(moe_aux_outputs), P,
                                                           P, SZ, P]),
+            "moe_layer_forward_fp8": (I32, [cfgp] + [P] * 15 + [ctypes.POINTER(moe_aux_outputs),
+                                                              P, P, SZ, P]),
+            "moe_quantize_rows_fp8": (I32, [P, I64, I64, P, P, P]),
+            "moe_dispatch_fp8": (I32, [cfgp] + [P] * 9 + [P, SZ, P]),
+            "moe_expert_ffn_fp8": (I32, [cfgp] + [P] * 9 + [P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -322,13 +327,10 @@ def alloc_aux(cfg, device="cuda", fields=None) -> dict:
     return out
 
 
-def moe_layer_forward(cfg, U, W_r, b_r, W_noise, noise, W_gate, W_up, W_down, out, aux=None,
-                      stage_events=None, ws=None, stream=None, b_sel=None, Ws_gate=None,
-                      Ws_up=None, Ws_down=None):
-    """The whole layer.  aux: dict of optional output tensors (see alloc_aux).
-    stage_events: list of MOE_NUM_STAGES + 1 torch.cuda.Event(enable_timing=True),
-    recorded inside the library on the same stream.  b_sel, Ws_*: the
-    selection bias and the shared-expert weights (cfg.n_shared > 0)."""
+def _layer_call(fn_name, cfg, U, W_r, b_r, W_noise, noise, weights, W_down, out, aux,
+                stage_events, ws, stream, b_sel, Ws_gate, Ws_up, Ws_down):
+    """Argument marshalling shared by moe_layer_forward and moe_layer_forward_fp8;
+    weights: the already checked pointers that stand between noise and W_down."""
     T, h, f, E = cfg.T, cfg.h, cfg.f, cfg.E
     ns, fs = cfg.n_shared, cfg.f_shared
     rows = max_rows(cfg)
@@ -357,13 +359,95 @@ def moe_layer_forward(cfg, U, W_r, b_r, W_noise, noise, W_gate, W_up, W_down, ou
         _ptr(b_r, "b_r", (E,), torch.float32), _ptr(b_sel, "b_sel", (E,), torch.float32),
         _ptr(W_noise, "W_noise", (h, E), dt) if cfg.noisy else None,
         _ptr(noise, "noise", (T, E), torch.float32) if cfg.noisy else None,
-        _ptr(W_gate, "W_gate", (E, f, h), dt), _ptr(W_up, "W_up", (E, f, h), dt),
+        *weights,
         _ptr(W_down, "W_down", (E, h, f), dt),
         _ptr(Ws_gate, "Ws_gate", (ns, fs, h), dt) if ns else None,
         _ptr(Ws_up, "Ws_up", (ns, fs, h), dt) if ns else None,
         _ptr(Ws_down, "Ws_down", (ns, h, fs), dt) if ns else None,
         _ptr(out, "out", (T, h), dt),
     ]
-    _check(lib().moe_layer_forward(ctypes.byref(cfg), *args, ctypes.byref(a),
+    _check(getattr(lib(), fn_name)(ctypes.byref(cfg), *args, ctypes.byref(a),
                                    ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None,
-                                   wp, wn, _stream(stream)), "moe_layer_forward")
+                                   wp, wn, _stream(stream)), fn_name)
+
+
+def moe_layer_forward(cfg, U, W_r, b_r, W_noise, noise, W_gate, W_up, W_down, out, aux=None,
+                      stage_events=None, ws=None, stream=None, b_sel=None, Ws_gate=None,
+                      Ws_up=None, Ws_down=None):
+    """The whole layer.  aux: dict of optional output tensors (see alloc_aux).
+    stage_events: list of MOE_NUM_STAGES + 1 torch.cuda.Event(enable_timing=True),
+    recorded inside the library on the same stream.  b_sel, Ws_*: the
+    selection bias and the shared-expert weights (cfg.n_shared > 0)."""
+    E, f, h, dt = cfg.E, cfg.f, cfg.h, _elem_dtype(cfg)
+    weights = [_ptr(W_gate, "W_gate", (E, f, h), dt), _ptr(W_up, "W_up", (E, f, h), dt)]
+    _layer_call("moe_layer_forward", cfg, U, W_r, b_r, W_noise, noise, weights, W_down, out, aux,
+                stage_events, ws, stream, b_sel, Ws_gate, Ws_up, Ws_down)
+
+
+def moe_layer_forward_fp8(cfg, U, W_r, b_r, W_noise, noise, W8_gate, s_gate, W8_up, s_up,
+                          W_down, out, aux=None, stage_events=None, ws=None, stream=None,
+                          b_sel=None, Ws_gate=None, Ws_up=None, Ws_down=None):
+    """The layer with the FP8 dispatch and up-projection: W8_* are E4M3 codes
+    (uint8 [E, f, h]) with row scales s_* (float32 [E, f]) from
+    moe_quantize_rows_fp8; everything else as in moe_layer_forward."""
+    E, f, h = cfg.E, cfg.f, cfg.h
+    weights = [_ptr(W8_gate, "W8_gate", (E, f, h), torch.uint8),
+               _ptr(s_gate, "s_gate", (E, f), torch.float32),
+               _ptr(W8_up, "W8_up", (E, f, h), torch.uint8),
+               _ptr(s_up, "s_up", (E, f), torch.float32)]
+    _layer_call("moe_layer_forward_fp8", cfg, U, W_r, b_r, W_noise, noise, weights, W_down, out,
+                aux, stage_events, ws, stream, b_sel, Ws_gate, Ws_up, Ws_down)
+
+
+def moe_quantize_rows_fp8(src, dst=None, scale=None, stream=None):
+    """Row-wise E4M3 codes (uint8, shape of src) and power-of-two scales
+    (float32, src.shape[:-1]) of a bf16 tensor src [..., cols]."""
+    if src.dtype != torch.bfloat16:
+        raise ValueError("src: expected bfloat16")
+    cols = src.shape[-1]
+    rows = src.numel() // cols if cols else 0
+    dst = torch.empty(src.shape, dtype=torch.uint8, device=src.device) if dst is None else dst
+    scale = (torch.empty(src.shape[:-1], dtype=torch.float32, device=src.device)
+             if scale is None else scale)
+    _check(lib().moe_quantize_rows_fp8(_ptr(src, "src", tuple(src.shape), torch.bfloat16), rows,
+                                       cols, _ptr(dst, "dst", tuple(src.shape), torch.uint8),
+                                       _ptr(scale, "scale", tuple(src.shape[:-1]), torch.float32),
+                                       _stream(stream)), "moe_quantize_rows_fp8")
+    return dst, scale
+
+
+def moe_dispatch_fp8(cfg, U, topk_idx, X8, x_scale, row_token, slot, count, kept, offset,
+                     ws=None, stream=None):
+    T, h, E, k = cfg.T, cfg.h, cfg.E, cfg.k
+    rows = max_rows(cfg)
+    need = workspace_size(cfg, MOE_WS_DISPATCH)
+    ws = new_workspace(cfg, MOE_WS_DISPATCH, U.device) if ws is None else ws
+    wp, wn = _ws(ws, need)
+    args = [
+        _ptr(U, "U", (T, h), torch.bfloat16), _ptr(topk_idx, "topk_idx", (T, k), torch.int32),
+        _ptr(X8, "X8", (rows, h), torch.uint8), _ptr(x_scale, "x_scale", (rows,), torch.float32),
+        _ptr(row_token, "row_token", (rows,), torch.int32),
+        _ptr(slot, "slot", (T, k), torch.int32), _ptr(count, "count", (E,), torch.int32),
+        _ptr(kept, "kept", (E,), torch.int32), _ptr(offset, "offset", (E + 1,), torch.int32),
+    ]
+    _check(lib().moe_dispatch_fp8(ctypes.byref(cfg), *args, wp, wn, _stream(stream)),
+           "moe_dispatch_fp8")
+
+
+def moe_expert_ffn_fp8(cfg, X8, x_scale, offset, W8_gate, s_gate, W8_up, s_up, W_down, Y,
+                       ws=None, stream=None):
+    h, f, E = cfg.h, cfg.f, cfg.E
+    rows = max_rows(cfg)
+    need = workspace_size(cfg, MOE_WS_EXPERT_FFN)
+    ws = new_workspace(cfg, MOE_WS_EXPERT_FFN, X8.device) if ws is None else ws
+    wp, wn = _ws(ws, need)
+    args = [
+        _ptr(X8, "X8", (rows, h), torch.uint8), _ptr(x_scale, "x_scale", (rows,), torch.float32),
+        _ptr(offset, "offset", (E + 1,), torch.int32),
+        _ptr(W8_gate, "W8_gate", (E, f, h), torch.uint8),
+        _ptr(s_gate, "s_gate", (E, f), torch.float32),
+        _ptr(W8_up, "W8_up", (E, f, h), torch.uint8), _ptr(s_up, "s_up", (E, f), torch.float32),
+        _ptr(W_down, "W_down", (E, h, f), torch.bfloat16), _ptr(Y, "Y", (rows, h), torch.bfloat16),
+    ]
+    _check(lib().moe_expert_ffn_fp8(ctypes.byref(cfg), *args, wp, wn, _stream(stream)),
+           "moe_expert_ffn_fp8")

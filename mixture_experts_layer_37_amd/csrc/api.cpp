@@ -206,7 +206,7 @@ struct LayerWs {
   DispatchWs disp;
   FfnWs ffn;
   SharedWs sh;
-  size_t idx, gate, slot, row_token, count, kept, offset, X, Y, scal;
+  size_t idx, gate, slot, row_token, count, kept, offset, X, Y, xs, scal;
 };
 LayerWs plan_layer(const Dims& d, int noisy, Plan& pl) {
   LayerWs w;
@@ -223,8 +223,9 @@ LayerWs plan_layer(const Dims& d, int noisy, Plan& pl) {
   w.count = pl.add(d.E * 4);
   w.kept = pl.add(d.E * 4);
   w.offset = pl.add((d.E + 1) * 4);
-  w.X = pl.add(rows * d.h * elem_bytes(d));
+  w.X = pl.add(rows * d.h * elem_bytes(d));  // also holds the FP8 rows (rows * h bytes)
   w.Y = pl.add(rows * d.h * elem_bytes(d));
+  w.xs = pl.add(rows * 4);                     // FP8 row scales
   w.scal = pl.add(64);
   return w;
 }
@@ -280,9 +281,11 @@ int32_t run_route(const Dims& d, const moe_config* c, const RouteWs& w, const vo
   return MOE_OK;
 }
 
+// xs != NULL: FP8 dispatch (X receives E4M3 codes, xs the row scales).
 int32_t run_dispatch(const Dims& d, const moe_config* c, const DispatchWs& w, const void* U,
                      const int32_t* idx, void* X, int32_t* row_token, int32_t* slot,
-                     int32_t* count, int32_t* kept, int32_t* offset, void* ws, hipStream_t s) {
+                     int32_t* count, int32_t* kept, int32_t* offset, void* ws, hipStream_t s,
+                     float* xs = nullptr) {
   DispatchParams p;
   p.T = (int)d.T;
   p.E = (int)d.E;
@@ -298,7 +301,18 @@ int32_t run_dispatch(const Dims& d, const moe_config* c, const DispatchWs& w, co
   p.slot = slot;
   p.row_token = row_token;
   MOE_TRY(launch_dispatch(p, s));
-  MOE_TRY(launch_permute(U, slot, X, (int)d.T, (int)d.h, (int)d.k, d.bf16, s));
+  if (xs)
+    MOE_TRY(launch_permute_fp8(U, slot, X, xs, (int)d.T, (int)d.h, (int)d.k, s));
+  else
+    MOE_TRY(launch_permute(U, slot, X, (int)d.T, (int)d.h, (int)d.k, d.bf16, s));
+  return MOE_OK;
+}
+
+// The FP8 path takes bf16 inputs and K steps of 128 FP8 elements.
+int32_t check_fp8(const moe_config* cfg) {
+  const int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16 || cfg->h % 128 != 0) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -310,10 +324,27 @@ int32_t run_tile_map(const Dims& d, const FfnWs& w, const int32_t* offset, void*
   return MOE_OK;
 }
 
-// Expects run_tile_map to have been enqueued before.
+// FP8 operands of the up-projection: E4M3 weights with their row scales, and
+// the scales of the dispatched rows.
+struct Fp8Up {
+  const void* Wg;
+  const float* sg;
+  const void* Wu;
+  const float* su;
+  const float* xs;
+};
+
+// Expects run_tile_map to have been enqueued before.  f8 != NULL: X holds
+// E4M3 rows and the gate/up GEMM runs on FP8.
 int32_t run_gate_up(const Dims& d, const FfnWs& w, const void* X, const int32_t* offset,
                     const void* Wg, const void* Wu, const void* Wd, void* Y, void* ws,
-                    hipStream_t s) {
+                    hipStream_t s, const Fp8Up* f8 = nullptr) {
+  if (f8) {
+    MOE_TRY(launch_gate_up_fp8(w.fs, X, f8->xs, offset, at<int32_t>(ws, w.map1), f8->Wg, f8->sg,
+                               f8->Wu, f8->su, at<void>(ws, w.A), at<float>(ws, w.part),
+                               (int)d.E, (int)d.h, (int)d.f, s));
+    return MOE_OK;
+  }
   if (!d.bf16)
     return hip_status(launch_ffn_f32(X, offset, Wg, Wu, Wd, at<void>(ws, w.A), Y, d.rows_max,
                                      (int)d.E, (int)d.h, (int)d.f, s));
@@ -541,14 +572,19 @@ int32_t moe_router_z_loss(const moe_config* cfg, const float* logits, float* z_l
                                   static_cast<hipStream_t>(stream)));
 }
 
-int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
-                          const float* b_r, const float* b_sel, const void* W_noise,
-                          const float* noise, const void* W_gate, const void* W_up,
-                          const void* W_down, const void* Ws_gate, const void* Ws_up,
-                          const void* Ws_down, void* out, const moe_aux_outputs* aux,
-                          void* const* stage_events, void* ws, size_t ws_bytes,
-                          void* stream) {
-  int32_t st = check_config(cfg);
+}  // extern "C"
+
+namespace {
+
+// The layer; f8 != NULL runs the FP8 dispatch and up-projection (its weights
+// replace W_gate and W_up).
+int32_t layer_impl(const moe_config* cfg, const void* U, const void* W_r, const float* b_r,
+                   const float* b_sel, const void* W_noise, const float* noise,
+                   const void* W_gate, const void* W_up, const void* W_down, const void* Ws_gate,
+                   const void* Ws_up, const void* Ws_down, void* out, const moe_aux_outputs* aux,
+                   void* const* stage_events, void* ws, size_t ws_bytes, void* stream,
+                   Fp8Up* f8) {
+  int32_t st = f8 ? check_fp8(cfg) : check_config(cfg);
   if (st != MOE_OK) return st;
   const Dims d = dims_of(cfg);
   if (d.T > 0 && (!U || !out)) return MOE_ERR_INVALID_ARG;
@@ -572,8 +608,11 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
   int32_t* count = o.count ? o.count : at<int32_t>(ws, w.count);
   int32_t* kept = o.kept ? o.kept : at<int32_t>(ws, w.kept);
   int32_t* offset = o.offset ? o.offset : at<int32_t>(ws, w.offset);
-  void* X = o.X ? o.X : at<void>(ws, w.X);
+  // the FP8 rows stay in the workspace (aux X is typed for the input dtype)
+  void* X = (o.X && !f8) ? o.X : at<void>(ws, w.X);
   void* Y = o.Y ? o.Y : at<void>(ws, w.Y);
+  float* xs = f8 ? at<float>(ws, w.xs) : nullptr;
+  if (f8) f8->xs = xs;
   void* Ys = d.ns == 0 ? nullptr : (o.Y_shared ? o.Y_shared : at<void>(ws, w.sh.Ys));
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto mark = [&](int i) -> hipError_t {
@@ -586,12 +625,12 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
                  s);
   if (st != MOE_OK) return st;
   MOE_TRY(mark(1));
-  st = run_dispatch(d, cfg, w.disp, U, idx, X, row_token, slot, count, kept, offset, ws, s);
+  st = run_dispatch(d, cfg, w.disp, U, idx, X, row_token, slot, count, kept, offset, ws, s, xs);
   if (st != MOE_OK) return st;
   st = run_tile_map(d, w.ffn, offset, ws, s);
   if (st != MOE_OK) return st;
   MOE_TRY(mark(2));
-  st = run_gate_up(d, w.ffn, X, offset, W_gate, W_up, W_down, Y, ws, s);
+  st = run_gate_up(d, w.ffn, X, offset, W_gate, W_up, W_down, Y, ws, s, f8);
   if (st != MOE_OK) return st;
   st = run_shared_gate_up(d, w.sh, U, Ws_gate, Ws_up, Ws_down, Ys, ws, s);
   if (st != MOE_OK) return st;
@@ -614,6 +653,82 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
   MOE_TRY(launch_stats(sp, s));
   MOE_TRY(mark(6));
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
+                          const float* b_r, const float* b_sel, const void* W_noise,
+                          const float* noise, const void* W_gate, const void* W_up,
+                          const void* W_down, const void* Ws_gate, const void* Ws_up,
+                          const void* Ws_down, void* out, const moe_aux_outputs* aux,
+                          void* const* stage_events, void* ws, size_t ws_bytes,
+                          void* stream) {
+  return layer_impl(cfg, U, W_r, b_r, b_sel, W_noise, noise, W_gate, W_up, W_down, Ws_gate,
+                    Ws_up, Ws_down, out, aux, stage_events, ws, ws_bytes, stream, nullptr);
+}
+
+int32_t moe_layer_forward_fp8(const moe_config* cfg, const void* U, const void* W_r,
+                              const float* b_r, const float* b_sel, const void* W_noise,
+                              const float* noise, const void* W8_gate, const float* s_gate,
+                              const void* W8_up, const float* s_up, const void* W_down,
+                              const void* Ws_gate, const void* Ws_up, const void* Ws_down,
+                              void* out, const moe_aux_outputs* aux, void* const* stage_events,
+                              void* ws, size_t ws_bytes, void* stream) {
+  if (!s_gate || !s_up) return MOE_ERR_INVALID_ARG;
+  Fp8Up f8{W8_gate, s_gate, W8_up, s_up, nullptr};
+  return layer_impl(cfg, U, W_r, b_r, b_sel, W_noise, noise, W8_gate, W8_up, W_down, Ws_gate,
+                    Ws_up, Ws_down, out, aux, stage_events, ws, ws_bytes, stream, &f8);
+}
+
+int32_t moe_quantize_rows_fp8(const void* src, int64_t rows, int64_t cols, void* dst,
+                              float* scale, void* stream) {
+  if (rows < 0 || cols <= 0 || cols > (int64_t)1 << 30) return MOE_ERR_INVALID_ARG;
+  if (cols % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows > 0 && (!src || !dst || !scale)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_rows_fp8(src, rows, (int)cols, dst, scale,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_dispatch_fp8(const moe_config* cfg, const void* U, const int32_t* topk_idx,
+                         void* X8, float* x_scale, int32_t* row_token, int32_t* slot,
+                         int32_t* count, int32_t* kept, int32_t* offset, void* ws,
+                         size_t ws_bytes, void* stream) {
+  const int32_t st = check_fp8(cfg);
+  if (st != MOE_OK) return st;
+  const Dims d = dims_of(cfg);
+  if (d.T > 0 && (!U || !topk_idx || !X8 || !x_scale || !row_token || !slot))
+    return MOE_ERR_INVALID_ARG;
+  if (!count || !kept || !offset || !ws) return MOE_ERR_INVALID_ARG;
+  Plan pl;
+  const DispatchWs w = plan_dispatch(d, pl);
+  if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
+  return run_dispatch(d, cfg, w, U, topk_idx, X8, row_token, slot, count, kept, offset, ws,
+                      static_cast<hipStream_t>(stream), x_scale);
+}
+
+int32_t moe_expert_ffn_fp8(const moe_config* cfg, const void* X8, const float* x_scale,
+                           const int32_t* offset, const void* W8_gate, const float* s_gate,
+                           const void* W8_up, const float* s_up, const void* W_down, void* Y,
+                           void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_fp8(cfg);
+  if (st != MOE_OK) return st;
+  const Dims d = dims_of(cfg);
+  if (!offset || !W8_gate || !s_gate || !W8_up || !s_up || !W_down || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (d.rows_max > 0 && (!X8 || !x_scale || !Y)) return MOE_ERR_INVALID_ARG;
+  Plan pl;
+  const FfnWs w = plan_ffn(d, pl);
+  if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_tile_map(d, w, offset, ws, s);
+  if (st != MOE_OK) return st;
+  const Fp8Up f8{W8_gate, s_gate, W8_up, s_up, x_scale};
+  st = run_gate_up(d, w, X8, offset, W8_gate, W8_up, W_down, Y, ws, s, &f8);
+  if (st != MOE_OK) return st;
+  return run_down(d, w, offset, W_down, Y, ws, s);
 }
 
 }  // extern "C"

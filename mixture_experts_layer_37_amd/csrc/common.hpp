@@ -89,6 +89,30 @@ __device__ __forceinline__ void st16(void* p, const u32x4& v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// FP8 rows (page "MoE 与专家并行", section "低精度通信": activations quantised
+// to FP8 with power-of-two scaling factors).  Format OCP E4M3, largest finite
+// value 448 = 0.875 * 2^9.  A row with largest magnitude amax gets the scale
+// 2^j with j the smallest integer such that amax / 2^j <= 448 (j = 0 for an
+// all-zero row): with amax = m 2^p, 0.5 <= m < 1, that is p - 9 when
+// m <= 0.875 and p - 8 otherwise.
+__device__ __forceinline__ int fp8_scale_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int p;
+  const float m = frexpf(amax, &p);
+  return m > 0.875f ? p - 8 : p - 9;
+}
+// Eight values times 2^-j (exact), each rounded to the nearest E4M3 value with
+// ties to even (the conversion instruction in the default rounding mode), as
+// eight bytes in element order.
+__device__ __forceinline__ uint2 to_fp8x8(const float* v, int j) {
+  int lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[0], -j), ldexpf(v[1], -j), lo, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[2], -j), ldexpf(v[3], -j), lo, true);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4], -j), ldexpf(v[5], -j), hi, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[6], -j), ldexpf(v[7], -j), hi, true);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

@@ -178,7 +178,90 @@ __global__ __launch_bounds__(256) void permute_kernel(const TE* U, const int32_t
   }
 }
 
+// FP8 dispatch: one wave per token reads its row, takes the largest magnitude,
+// and writes the row's E4M3 codes and power-of-two scale to each kept slot.
+__global__ __launch_bounds__(256) void permute_fp8_kernel(const bf16* U, const int32_t* slot,
+                                                          uint8_t* X8, float* xs, int T, int h,
+                                                          int k) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  int sl[8];
+  bool any = false;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    sl[r] = r < k ? slot[(size_t)t * k + r] : -1;
+    any |= sl[r] >= 0;
+  }
+  if (!any) return;
+  const int nvec = h / 8;
+  const bf16* src = U + (size_t)t * h;
+  float amax = 0.f;
+  for (int i = lane; i < nvec; i += 64) {
+    float v[8];
+    Elem<bf16>::unpack(ld16(src + (size_t)i * 8), v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+  }
+  const int j = fp8_scale_exp(wave_max(amax));
+  for (int i = lane; i < nvec; i += 64) {
+    float v[8];
+    Elem<bf16>::unpack(ld16(src + (size_t)i * 8), v);
+    const uint2 q = to_fp8x8(v, j);
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (sl[r] >= 0) *reinterpret_cast<uint2*>(X8 + (size_t)sl[r] * h + (size_t)i * 8) = q;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (sl[r] >= 0) xs[sl[r]] = ldexpf(1.f, j);
+  }
+}
+
+// Row-wise FP8 quantisation of a bf16 matrix (weights): one wave per row.
+__global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const bf16* src, int64_t rows,
+                                                                int cols, uint8_t* dst,
+                                                                float* scale) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+  if (r >= rows) return;
+  const bf16* row = src + (size_t)r * cols;
+  const int nvec = cols / 8;
+  float amax = 0.f;
+  for (int i = lane; i < nvec; i += 64) {
+    float v[8];
+    Elem<bf16>::unpack(ld16(row + (size_t)i * 8), v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+  }
+  const int j = fp8_scale_exp(wave_max(amax));
+  for (int i = lane; i < nvec; i += 64) {
+    float v[8];
+    Elem<bf16>::unpack(ld16(row + (size_t)i * 8), v);
+    *reinterpret_cast<uint2*>(dst + (size_t)r * cols + (size_t)i * 8) = to_fp8x8(v, j);
+  }
+  if (lane == 0) scale[r] = ldexpf(1.f, j);
+}
+
 }  // namespace
+
+hipError_t launch_permute_fp8(const void* U, const int32_t* slot, void* X8, float* xs, int T,
+                              int h, int k, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(permute_fp8_kernel, dim3((T + 3) / 4), dim3(256), 0, s,
+                     static_cast<const bf16*>(U), slot, static_cast<uint8_t*>(X8), xs, T, h, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows_fp8(const void* src, int64_t rows, int cols, void* dst,
+                                    float* scale, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_rows_fp8_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+                     static_cast<const bf16*>(src), rows, cols, static_cast<uint8_t*>(dst),
+                     scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s) {
   const int nchunk = (p.T + kChunk - 1) / kChunk;

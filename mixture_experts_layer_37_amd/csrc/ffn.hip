@@ -8,46 +8,46 @@
 // row counts and offsets, with gate and up merged into one GEMM, the SiLU
 // product in its epilogue, and a second GEMM for down.
 //
-// bf16 kernels (gfx950): C[M, N] = A[M, K] W[N, K]^T with both operands
-// K-contiguous, v_mfma_f32_32x32x16_bf16, float32 accumulation.  A workgroup
-// of NW waves (NW/2 along M x 2 along N) owns a BM x 256 output tile; each
-// wave a (2 BM / NW) x 128 block of 32 x 32 MFMA tiles.
+// Kernels (gfx950): C[M, N] = A[M, K] W[N, K]^T with both operands
+// K-contiguous and float32 accumulation, on v_mfma_f32_32x32x16_bf16 for bf16
+// operands, or on v_mfma_f32_32x32x64_f8f6f4 for the FP8 (E4M3) up-projection
+// of section "低精度通信" (DeepSeek-V3: activations quantised to FP8 with
+// power-of-two scales before dispatch, FP8 up-projection, BF16 combine).  A
+// workgroup of NW waves (NW/2 along M x 2 along N) owns a BM x 256 output
+// tile; each wave a (2 BM / NW) x 128 block of 32 x 32 MFMA tiles.
 //
-// Operand pipeline.  K advances in steps of 64: a step's A tile (BM rows) and
-// B tile (256 rows) are 128 bytes per row, so every LDS-direct copy
-// instruction (16 bytes per lane) moves eight whole 128-byte lines; on this
-// part such copies sustain about twice the per-CU rate of 64-byte row pieces,
-// and the copy rate, not the matrix pipe, is what bounds a 256 x 256 tile.
-// LDS holds a ring of three A slots and two B slots (160 KB at BM = 256).
-// Step j reads A_j and B_j; between its third and fourth K slice every wave
-// waits for its copies of A_{j+1} and B_{j+1}, meets the others at one
-// barrier, and then reuses the slots of step j for B_{j+2} and A_{j+3}.
-// Copies of A thus have two steps and copies of B one step to land, with about
-// 96 KB in flight per CU.  Inside a step, each wave runs the MFMAs of one K
-// slice while reading the fragments of the next from LDS.  The slots are
-// separate LDS arrays and the loop is unrolled over the ring's period (6), so
-// the compiler can tell the copies in flight from the slots being read.
+// Operand pipeline.  K advances in steps of 128 bytes per row (64 bf16 or
+// 128 FP8 elements), so every LDS-direct copy instruction (16 bytes per lane)
+// moves eight whole 128-byte lines; on this part such copies sustain about
+// twice the per-CU rate of 64-byte row pieces.  LDS holds a ring of N_A A
+// slots and N_B B slots (2 + 3 at BM = 256, 3 + 3 at BM = 128).  Step j reads
+// A_j and B_j; before its last K slice every wave waits for its copies of
+// A_{j+1} and B_{j+1}, meets the others at one barrier, and then reuses the
+// slots of step j for A_{j+N_A} and B_{j+N_B}.  Inside a step, each wave runs
+// the MFMAs of one K slice while reading the fragments of the next from LDS.
+// The slots are separate LDS arrays and the loop is unrolled over the ring's
+// period, so the compiler can tell the copies in flight from the slots being
+// read.
 //
 // LDS rows are 128 bytes (8 chunks of 16).  gfx950 serves a 16-byte LDS read
 // for 16 lanes per clock from 64 four-byte banks; storing logical chunk c of
 // row r at chunk c ^ ((r >> 1) & 7) makes the 16 rows of one fragment read
-// cover all banks once.
+// cover all banks once.  A bf16 fragment is one chunk per lane, an FP8
+// fragment two.
 //
 // Gate/up tile: LDS B rows 0..127 are W_gate rows n0..n0+127 and rows
 // 128..255 the W_up rows with the same indices, so each lane holds the gate
 // and the up value of one output element and the epilogue writes
-// a = SiLU(g) * u (rounded to bf16) directly.
-// Tile order: tiles are numbered in groups of 8 n-tiles, m-tile major inside a
-// group, and the numbering is spread over the XCDs in contiguous ranges, so
-// workgroups running together on one XCD share A rows and B tiles in its L2.
+// a = SiLU(g) * u (rounded to bf16) directly; with FP8 operands g and u are
+// first multiplied by the row scale of A and the row scales of W_gate / W_up.
 // Ragged rows: an m-tile never crosses an expert boundary and only stores its
 // valid rows.  Its A buffer resource ends at its last valid row, so copies of
-// the rows past it read zero without memory traffic.  A tile at most half full
-// also skips the MFMAs of its empty 32-row blocks; a fuller one runs the
-// fully scheduled loop, which is faster than the branchy partial one.
+// the rows past it read zero without memory traffic, and each wave skips the
+// MFMAs of its 32-row blocks without valid rows.
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -61,18 +61,31 @@ namespace {
 constexpr int kWaves = 8;
 
 constexpr int BN = 256, BK = 64, GN = 8;
+// Operand element types: every K step moves 128 bytes of each row, i.e. 64
+// bf16 or 128 FP8 elements, in 4 or 2 MFMA K slices.
+typedef int v8i __attribute__((ext_vector_type(8)));
+template <bool F8>
+struct Elt {
+  static constexpr int kBytes = F8 ? 1 : 2;    // bytes per element
+  static constexpr int kStep = 128 / kBytes;   // K elements per step
+  static constexpr int kSlices = F8 ? 2 : 4;   // MFMA K slices per step
+  using Frag = std::conditional_t<F8, v8i, bf16x8>;
+};
 // Third dword of a raw buffer resource on gfx9-family parts (32-bit data
 // format, no swizzle); loads outside num_records bytes return zero.
 constexpr int kBufFlags = 0x00020000;
 
 struct GemmParams {
-  const bf16* A;         // [rows][K], experts' row blocks back to back
+  const void* A;         // [rows][K], experts' row blocks back to back (bf16 or FP8)
   const int32_t* offset; // [E+1]
   const int32_t* tmap;   // tile map: [E+1] first m-tile of each expert, then the
                          // per-m-tile table (see tile_map_kernel)
-  const bf16* W0;        // gate/up: W_gate [E][N][K]; down: W_down [E][N][K]
-  const bf16* W1;        // gate/up: W_up
+  const void* W0;        // gate/up: W_gate [E][N][K]; down: W_down [E][N][K]
+  const void* W1;        // gate/up: W_up
   bf16* C;               // [rows][Nout]
+  const float* sa;       // FP8: [rows] power-of-two scale of each A row
+  const float* sw0;      // FP8: [E][N] scale of each W0 row
+  const float* sw1;      // FP8: [E][N] scale of each W1 row
   int E, K, N, Nout;     // N: rows of each weight matrix (f or h)
   int ntiles, mtmax;
   float* part;           // K-split partial tiles: [grid][BM * BN] float32
@@ -82,7 +95,7 @@ struct GemmParams {
 
 // A K chunk of a tail tile (see gemm_bf16_kernel); ks == 1: a whole tile.
 struct KSplit {
-  int kbeg, ksteps;  // 64-wide K steps of this chunk
+  int kbeg, ksteps;  // 128-byte K steps of this chunk
   int ks;            // chunks of the tile
   float* slot;       // where this chunk's float32 partial goes (ks > 1)
 };
@@ -149,10 +162,11 @@ __device__ __forceinline__ float4* part_at(float* slot, int q) {
 // 8 * g + 4 * (lane / 32) + t in acc[4 * g + t], g, t = 0..3.  Each run of 4
 // columns goes out as one 8-byte store.  Gate/up: a = SiLU(g) * u from the
 // gate and up halves, which sit in the same lane and register.
-template <int BM, int NW, bool GATEUP>
+template <int BM, int NW, bool GATEUP, bool F8>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const floatx16 (&acc)[(2 * BM / NW) / 32][4],
-                                           int nt, int row0, int nvalid) {
+                                           const TileAt& ta) {
   constexpr int WR = 2 * BM / NW, RBLK = WR / 32;
+  const int nt = ta.nt, row0 = ta.row0, nvalid = ta.nvalid;
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));  // keeps the row addressing below out of the main loop
   const int wave = tid >> 6, lane = tid & 63;
@@ -162,6 +176,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const floatx16 (
     const int r = wm * WR + i * 32 + l32;
     if (r >= nvalid) continue;
     bf16* crow = p.C + (size_t)(row0 + r) * p.Nout;
+    const float sa = F8 ? p.sa[row0 + r] : 1.f;
 #pragma unroll
     for (int j = 0; j < (GATEUP ? 2 : 4); ++j) {
 #pragma unroll
@@ -169,11 +184,17 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const floatx16 (
         // Nout is a multiple of 4: a run is all inside or all past the end
         const int col = (GATEUP ? nt * 128 + wn * 64 : nt * BN + wn * 128) + j * 32 + 8 * g + 4 * khalf;
         if (col >= p.Nout) continue;
-        float y[4];
+        float y[4], sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
+        if (F8) {  // power-of-two scales: the products below are exact
+          const float4 a = *reinterpret_cast<const float4*>(p.sw0 + (size_t)ta.e * p.N + col);
+          const float4 b = *reinterpret_cast<const float4*>(p.sw1 + (size_t)ta.e * p.N + col);
+          sg[0] = sa * a.x; sg[1] = sa * a.y; sg[2] = sa * a.z; sg[3] = sa * a.w;
+          su[0] = sa * b.x; su[1] = sa * b.y; su[2] = sa * b.z; su[3] = sa * b.w;
+        }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           if (GATEUP) {
-            const float gv = acc[i][j][4 * g + t], uv = acc[i][j + 2][4 * g + t];
+            const float gv = acc[i][j][4 * g + t] * sg[t], uv = acc[i][j + 2][4 * g + t] * su[t];
             y[t] = gv / (1.f + __expf(-gv)) * uv;
           } else {
             y[t] = acc[i][j][4 * g + t];
@@ -216,22 +237,25 @@ struct Ring {
 
 // Copy sources of one unit of work (a tile, or one K chunk of a tail tile):
 // buffer resources over its valid A rows and its weight panels, and its range
-// of 64-wide K steps.  A's resource ends at the last valid row, so copies of
+// of K steps.  A's resource ends at the last valid row, so copies of
 // rows past it read zero without touching memory (their outputs are never
 // stored).
 struct TileSrc {
   __amdgpu_buffer_rsrc_t rA, rB0, rB1;
   int kbeg, KT;
 };
-template <bool GATEUP>
+template <bool GATEUP, bool F8>
 __device__ __forceinline__ TileSrc tile_src(const GemmParams& p, const TileAt& ta,
                                             const KSplit& ksp) {
   TileSrc s;
-  const int K = p.K;
-  s.rA = make_rsrc(p.A + (size_t)ta.row0 * K, (size_t)ta.nvalid * K * 2);
+  const size_t rb = (size_t)p.K * Elt<F8>::kBytes;  // bytes per row
+  const char* A = static_cast<const char*>(p.A);
+  s.rA = make_rsrc(A + (size_t)ta.row0 * rb, (size_t)ta.nvalid * rb);
   const size_t n0 = (size_t)ta.nt * (GATEUP ? 128 : BN);
-  s.rB0 = make_rsrc(p.W0 + ((size_t)ta.e * p.N + n0) * K, (size_t)(p.N - n0) * K * 2);
-  s.rB1 = GATEUP ? make_rsrc(p.W1 + ((size_t)ta.e * p.N + n0) * K, (size_t)(p.N - n0) * K * 2)
+  const char* W0 = static_cast<const char*>(p.W0);
+  const char* W1 = static_cast<const char*>(p.W1);
+  s.rB0 = make_rsrc(W0 + ((size_t)ta.e * p.N + n0) * rb, (size_t)(p.N - n0) * rb);
+  s.rB1 = GATEUP ? make_rsrc(W1 + ((size_t)ta.e * p.N + n0) * rb, (size_t)(p.N - n0) * rb)
                  : s.rB0;
   s.kbeg = ksp.kbeg;
   s.KT = ksp.ksteps;
@@ -241,7 +265,7 @@ __device__ __forceinline__ TileSrc tile_src(const GemmParams& p, const TileAt& t
 // This wave's share of the copies of one K step.  Lane i of 8-row group g
 // fills LDS row 8g + i/8, physical chunk i%8, with logical chunk
 // (i%8) ^ ((row >> 1) & 7).  The per-lane offsets depend on K only.
-template <int BM, int NW, bool GATEUP>
+template <int BM, int NW, bool GATEUP, bool F8>
 struct CopyPlan {
   static constexpr int AG = BM / (8 * NW);  // 8-row A groups copied per wave per step
   static constexpr int BG = BN / (8 * NW);  // 8-row B groups copied per wave per step
@@ -254,7 +278,7 @@ struct CopyPlan {
 #pragma unroll
     for (int j = 0; j < AG; ++j) {
       const int r = 8 * (wave + NW * j) + lrow;
-      voA[j] = (r * K + (((lane & 7) ^ ((r >> 1) & 7)) * 8)) * 2;
+      voA[j] = r * K * Elt<F8>::kBytes + (((lane & 7) ^ ((r >> 1) & 7)) * 16);
     }
 #pragma unroll
     for (int j = 0; j < BG; ++j) {
@@ -262,18 +286,18 @@ struct CopyPlan {
       const int g = wave + NW * j;
       const int r = 8 * g + lrow;                       // LDS row
       const int pr = GATEUP ? 8 * (g & 15) + lrow : r;  // row in the weight panel
-      voB[j] = (pr * K + (((lane & 7) ^ ((r >> 1) & 7)) * 8)) * 2;
+      voB[j] = pr * K * Elt<F8>::kBytes + (((lane & 7) ^ ((r >> 1) & 7)) * 16);
     }
   }
   // step j past the end reloads the last step (in bounds, never read), so
   // every step issues the same number of copies
   __device__ __forceinline__ void issueA(const TileSrc& s, bf16* as, int j) const {
-    const int kb = (s.kbeg + min(j, s.KT - 1)) * BK * 2;
+    const int kb = (s.kbeg + min(j, s.KT - 1)) * 128;
 #pragma unroll
     for (int q = 0; q < AG; ++q) dma16(s.rA, as + (wave + NW * q) * 8 * BK, voA[q], kb);
   }
   __device__ __forceinline__ void issueB(const TileSrc& s, bf16* bs, int j) const {
-    const int kb = (s.kbeg + min(j, s.KT - 1)) * BK * 2;
+    const int kb = (s.kbeg + min(j, s.KT - 1)) * 128;
 #pragma unroll
     for (int q = 0; q < BG; ++q)
       dma16((GATEUP && q >= BG / 2) ? s.rB1 : s.rB0, bs + (wave + NW * q) * 8 * BK, voB[q], kb);
@@ -294,15 +318,18 @@ struct CopyPlan {
 // RBLK); a wave with R < RBLK skips the fragment reads and MFMAs of the others
 // (their accumulators stay zero and their rows are never stored) but issues
 // the same copies and meets the same barriers as the rest of the workgroup.
-template <int BM, int NW, bool GATEUP, int R, int NA, int NB, class Next>
-__device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM, NW, GATEUP>& cp,
+template <int BM, int NW, bool GATEUP, bool F8, int R, int NA, int NB, class Next>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM, NW, GATEUP, F8>& cp,
                                           const TileSrc& src, const Ring& L, const TileAt& ta,
                                           const KSplit& ksp, Next&& next) {
   constexpr int WM = NW / 2;         // waves along M (2 along N)
   constexpr int WR = BM / WM;        // rows per wave
   constexpr int RBLK = WR / 32;      // 32-row MFMA blocks per wave
-  constexpr int AG = CopyPlan<BM, NW, GATEUP>::AG;
-  constexpr int BG = CopyPlan<BM, NW, GATEUP>::BG;
+  constexpr int AG = CopyPlan<BM, NW, GATEUP, F8>::AG;
+  constexpr int BG = CopyPlan<BM, NW, GATEUP, F8>::BG;
+  constexpr int NSL = Elt<F8>::kSlices;  // MFMA K slices per step
+  constexpr int FC = F8 ? 2 : 1;         // 16-byte chunks per fragment and lane
+  using Frag = typename Elt<F8>::Frag;
   static_assert(AG >= 1 && BG >= 2 && RBLK >= 1, "tile shape");
   const int wave = cp.wave;
   const int lane = threadIdx.x & 63;
@@ -312,17 +339,19 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM
   auto issueB = [&](bf16* bs, int j) { cp.issueB(src, bs, j); };
 
   // ---- fragments: lane reads row (lane % 32) of each 32-row block, logical
-  // chunk 2 * slice + lane / 32 of the step's 8
+  // chunks FC * (2 * slice + lane / 32) + 0..FC-1 of the step's 8.  The A and
+  // B fragments of a slice cover the same K elements in the same lane and
+  // byte positions, which is all the MFMA's dot products need.
   const int l32 = lane & 31, khalf = lane >> 5;
   const int sw = (l32 >> 1) & 7;  // (row >> 1) & 7 of every fragment row of this lane
-  int aoff[RBLK], boff[4];
+  int aoff[RBLK], boff[4];  // byte offsets of this lane's rows in a slot
 #pragma unroll
-  for (int i = 0; i < RBLK; ++i) aoff[i] = (wm * WR + i * 32 + l32) * BK;
+  for (int i = 0; i < RBLK; ++i) aoff[i] = (wm * WR + i * 32 + l32) * 128;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = GATEUP ? ((j < 2 ? 0 : 128) + wn * 64 + (j & 1) * 32 + l32)
                          : (wn * 128 + j * 32 + l32);
-    boff[j] = r * BK;
+    boff[j] = r * 128;
   }
   static_assert(R >= 0 && R <= RBLK, "active blocks");
 
@@ -334,35 +363,52 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  bf16x8 fa[2][RBLK], fb[2][4];
+  Frag fa[2][RBLK], fb[2][4];
+  // one fragment: FC chunks of 16 bytes of a row, at physical chunks c ^ sw
+  auto frag = [&](const bf16* slot, int off, int c0) {
+    const char* row = reinterpret_cast<const char*>(slot) + off;
+    if constexpr (F8) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(row + ((c0 ^ sw) * 16));
+      const u32x4 y = *reinterpret_cast<const u32x4*>(row + (((c0 + 1) ^ sw) * 16));
+      return Frag{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
+                  (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+    } else {
+      return *reinterpret_cast<const Frag*>(row + ((c0 ^ sw) * 16));
+    }
+  };
   auto fetch = [&](const bf16* as, const bf16* bs, int slice, int st) {
-    const int c = ((2 * slice + khalf) ^ sw) * 8;
+    const int c0 = FC * (2 * slice + khalf);
 #pragma unroll
-    for (int i = 0; i < R; ++i) fa[st][i] = *reinterpret_cast<const bf16x8*>(as + aoff[i] + c);
+    for (int i = 0; i < R; ++i) fa[st][i] = frag(as, aoff[i], c0);
 #pragma unroll
-    for (int j = 0; j < (R > 0 ? 4 : 0); ++j)
-      fb[st][j] = *reinterpret_cast<const bf16x8*>(bs + boff[j] + c);
+    for (int j = 0; j < (R > 0 ? 4 : 0); ++j) fb[st][j] = frag(bs, boff[j], c0);
   };
   auto mfmas = [&](int st) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[st][j], fa[st][i], acc[i][j],
-                                                            0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (F8)  // format codes 0, 0: both operands E4M3; no block scales
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fb[st][j], fa[st][i], acc[i][j], 0, 0, 0, 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[st][j], fa[st][i], acc[i][j],
+                                                              0, 0, 0);
+      }
     }
   };
   // order for the scheduler: MFMAs interleaved with the next fragment reads
   // and, after the barrier, with the copies (groups: 0x008 MFMA, 0x100 LDS
   // read, 0x020 global read incl. LDS copies)
-  constexpr int NM = R * 4, NR = R > 0 ? R + 4 : 0, NC = AG + BG;
+  constexpr int NM = R * 4, NR = R > 0 ? (R + 4) * FC : 0, NC = AG + BG;
   constexpr int CPM = NM > 0 ? (NC + NM - 1) / NM : NC;  // copies placed after each MFMA
+  constexpr int RPM = NM > 0 ? (NR + NM - 1) / NM : NR;  // LDS reads placed after each MFMA
   auto order = [&]() {
     if (R == 0) return;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (m < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (m * RPM < NR) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
     }
   };
   auto order_copies = [&]() {
@@ -371,21 +417,18 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM
     for (int m = 0; m < NM; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (m * CPM < NC) __builtin_amdgcn_sched_group_barrier(0x020, CPM, 0);
-      if (m < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (m * RPM < NR) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
     }
   };
   // Step j on slots (as, bs); (nas, nbs) hold step j + 1.  On entry fa/fb[0]
   // hold slice 0 of step j.
   auto step = [&](int j, bf16* as, bf16* bs, const bf16* nas, const bf16* nbs) {
-    fetch(as, bs, 1, 1);
-    mfmas(0);
-    order();
-    fetch(as, bs, 2, 0);
-    mfmas(1);
-    order();
-    fetch(as, bs, 3, 1);
-    mfmas(0);
-    order();
+#pragma unroll
+    for (int sl = 0; sl + 1 < NSL; ++sl) {
+      fetch(as, bs, sl + 1, (sl + 1) & 1);
+      mfmas(sl & 1);
+      order();
+    }
     // A_{j+1} and B_{j+1} have landed; copies of step j + 2 (issued last)
     // may still be in flight
     wait_vm<(NA == 3 ? AG : 0) + (NB == 3 ? BG : 0)>();
@@ -396,7 +439,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM
     issueB(bs, j + NB);
     if (NA == 3) issueA(as, j + 3);
     fetch(nas, nbs, 0, 0);
-    mfmas(1);
+    mfmas((NSL - 1) & 1);
     order_copies();
   };
 
@@ -432,7 +475,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM
                           acc[i][j][4 * v4 + 3]);
     return;
   }
-  store_tile<BM, NW, GATEUP>(p, acc, ta.nt, ta.row0, ta.nvalid);
+  store_tile<BM, NW, GATEUP, F8>(p, acc, ta);
 }
 
 // Unit u of an XCD's share: tile xs.tbeg + u, or (past the full rounds, when
@@ -473,24 +516,18 @@ __device__ __forceinline__ Unit unit_at(const GemmParams& p, const XcdShare& xs,
 // the same share of real tiles, and the workgroups running together on one
 // XCD hold neighbouring tiles, which share A row panels and weight panels in
 // that XCD's L2.
-template <int BM, int NW, bool GATEUP, int NA, int NB>
-__global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) bf16 A0[BM * BK], A1[BM * BK];
-  __shared__ __attribute__((aligned(1024))) bf16 A2[NA == 3 ? BM * BK : 8];
-  __shared__ __attribute__((aligned(1024))) bf16 B0[BN * BK], B1[BN * BK];
-  __shared__ __attribute__((aligned(1024))) bf16 B2[NB == 3 ? BN * BK : 8];
-  const Ring L{{A0, A1, A2}, {B0, B1, B2}};
-
+template <int BM, int NW, bool GATEUP, bool F8, int NA, int NB>
+__device__ __forceinline__ void grouped_gemm(const GemmParams& p, const Ring& L) {
   const int mtiles = p.tmap[p.E];
-  const int KT = p.K / BK;
+  const int KT = p.K / Elt<F8>::kStep;
   const int xcd = blockIdx.x & 7;
   const XcdShare xs = xcd_share(mtiles * p.ntiles, xcd, p.grid, KT, p.split_max);
   const int units = xs.full + xs.rem * xs.ks;
   int u = blockIdx.x >> 3;
   if (u >= units) return;
-  const CopyPlan<BM, NW, GATEUP> cp(p.K);
+  const CopyPlan<BM, NW, GATEUP, F8> cp(p.K);
   Unit cur = unit_at<BM>(p, xs, xcd, u, KT, mtiles);
-  cp.template prologue<NA, NB>(tile_src<GATEUP>(p, cur.ta, cur.ksp), L);
+  cp.template prologue<NA, NB>(tile_src<GATEUP, F8>(p, cur.ta, cur.ksp), L);
   constexpr int RBLK = (2 * BM / NW) / 32;
   const int wm = cp.wave >> 1;
   for (;;) {
@@ -500,34 +537,57 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(GemmParams p) {
     const bool more = un < units;
     const Unit nxt = more ? unit_at<BM>(p, xs, xcd, un, KT, mtiles) : cur;
     auto next = [&]() {
-      if (more) cp.template prologue<NA, NB>(tile_src<GATEUP>(p, nxt.ta, nxt.ksp), L);
+      if (more) cp.template prologue<NA, NB>(tile_src<GATEUP, F8>(p, nxt.ta, nxt.ksp), L);
     };
-    const TileSrc src = tile_src<GATEUP>(p, cur.ta, cur.ksp);
+    const TileSrc src = tile_src<GATEUP, F8>(p, cur.ta, cur.ksp);
     // each wave runs the fully scheduled loop over its 32-row blocks that
     // hold valid rows (rows past nvalid read zero and are not stored)
     const int act = min(RBLK, max(0, (cur.ta.nvalid - wm * (RBLK * 32) + 31) / 32));
     if (act >= RBLK)
-      gemm_tile<BM, NW, GATEUP, RBLK, NA, NB>(p, cp, src, L, cur.ta, cur.ksp, next);
+      gemm_tile<BM, NW, GATEUP, F8, RBLK, NA, NB>(p, cp, src, L, cur.ta, cur.ksp, next);
     else if (RBLK > 1 && act == 1)
-      gemm_tile<BM, NW, GATEUP, (RBLK > 1 ? 1 : 0), NA, NB>(p, cp, src, L, cur.ta, cur.ksp, next);
+      gemm_tile<BM, NW, GATEUP, F8, (RBLK > 1 ? 1 : 0), NA, NB>(p, cp, src, L, cur.ta, cur.ksp,
+                                                               next);
     else
-      gemm_tile<BM, NW, GATEUP, 0, NA, NB>(p, cp, src, L, cur.ta, cur.ksp, next);
+      gemm_tile<BM, NW, GATEUP, F8, 0, NA, NB>(p, cp, src, L, cur.ta, cur.ksp, next);
     if (!more) break;
     u = un;
     cur = nxt;
   }
 }
 
+// LDS ring of the copy pipeline: 128-byte rows, BM-row A slots, 256-row B slots.
+#define MOE_GEMM_LDS_RING                                                         \
+  __shared__ __attribute__((aligned(1024))) bf16 A0[BM * BK], A1[BM * BK];        \
+  __shared__ __attribute__((aligned(1024))) bf16 A2[NA == 3 ? BM * BK : 8];       \
+  __shared__ __attribute__((aligned(1024))) bf16 B0[BN * BK], B1[BN * BK];        \
+  __shared__ __attribute__((aligned(1024))) bf16 B2[NB == 3 ? BN * BK : 8];       \
+  const Ring L{{A0, A1, A2}, {B0, B1, B2}};
+
+template <int BM, int NW, bool GATEUP, int NA, int NB>
+__global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(GemmParams p) {
+  MOE_GEMM_LDS_RING
+  grouped_gemm<BM, NW, GATEUP, false, NA, NB>(p, L);
+}
+
+// The gate/up GEMM on FP8 (E4M3) rows and weights with power-of-two row scales.
+template <int BM, int NW, int NA, int NB>
+__global__ __launch_bounds__(64 * NW) void gemm_fp8_kernel(GemmParams p) {
+  MOE_GEMM_LDS_RING
+  grouped_gemm<BM, NW, true, true, NA, NB>(p, L);
+}
+
 // Sum of the K chunks of the tail tiles, in chunk order, then the same
 // epilogue as gemm_bf16_kernel.  Workgroup b handles tail tile b / 8 of XCD
 // b % 8 (if that XCD split its tail); thread i reads the partial groups that
 // thread i of the GEMM wrote.
-template <int BM, int NW, bool GATEUP>
+template <int BM, int NW, bool GATEUP, bool F8>
 __global__ __launch_bounds__(64 * NW) void ksplit_reduce_kernel(GemmParams p) {
   constexpr int RBLK = (2 * BM / NW) / 32;
   const int mtiles = p.tmap[p.E];
   const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
-  const XcdShare xs = xcd_share(mtiles * p.ntiles, xcd, p.grid, p.K / BK, p.split_max);
+  const XcdShare xs =
+      xcd_share(mtiles * p.ntiles, xcd, p.grid, p.K / Elt<F8>::kStep, p.split_max);
   if (xs.ks <= 1 || q >= xs.rem) return;
   const TileAt ta = tile_at<BM>(p, xs.tbeg + xs.full + q, mtiles);
   floatx16 acc[RBLK][4];
@@ -552,7 +612,7 @@ __global__ __launch_bounds__(64 * NW) void ksplit_reduce_kernel(GemmParams p) {
           acc[i][j][4 * v4 + 3] += x.w;
         }
   }
-  store_tile<BM, NW, GATEUP>(p, acc, ta.nt, ta.row0, ta.nvalid);
+  store_tile<BM, NW, GATEUP, F8>(p, acc, ta);
 }
 
 // float32 path: one thread per output, plain dot products (small workloads).
@@ -635,10 +695,21 @@ void launch_gemm(int bm, const GemmParams& p, hipStream_t s) {
   const dim3 grid(p.grid), block(64 * kWaves);
   if (bm == 256) {
     hipLaunchKernelGGL((gemm_bf16_kernel<256, kWaves, GATEUP, 2, 3>), grid, block, 0, s, p);
-    hipLaunchKernelGGL((ksplit_reduce_kernel<256, kWaves, GATEUP>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ksplit_reduce_kernel<256, kWaves, GATEUP, false>), grid, block, 0, s, p);
   } else {
     hipLaunchKernelGGL((gemm_bf16_kernel<128, kWaves, GATEUP, 3, 3>), grid, block, 0, s, p);
-    hipLaunchKernelGGL((ksplit_reduce_kernel<128, kWaves, GATEUP>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ksplit_reduce_kernel<128, kWaves, GATEUP, false>), grid, block, 0, s, p);
+  }
+}
+
+void launch_gemm_fp8(int bm, const GemmParams& p, hipStream_t s) {
+  const dim3 grid(p.grid), block(64 * kWaves);
+  if (bm == 256) {
+    hipLaunchKernelGGL((gemm_fp8_kernel<256, kWaves, 2, 3>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ksplit_reduce_kernel<256, kWaves, true, true>), grid, block, 0, s, p);
+  } else {
+    hipLaunchKernelGGL((gemm_fp8_kernel<128, kWaves, 3, 3>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ksplit_reduce_kernel<128, kWaves, true, true>), grid, block, 0, s, p);
   }
 }
 
@@ -693,10 +764,20 @@ hipError_t launch_gate_up(const FfnShape& fs, const void* X, const int32_t* offs
     return hipErrorNotSupported;
   }
   if (fs.grid1 == 0) return hipSuccess;
-  GemmParams p{static_cast<const bf16*>(X), offset, map1, static_cast<const bf16*>(Wg),
-               static_cast<const bf16*>(Wu), static_cast<bf16*>(A), E, h, f, f,
-               fs.nt1, fs.mt1, part, fs.split_max, fs.grid1};
+  GemmParams p{X, offset, map1, Wg, Wu, static_cast<bf16*>(A), nullptr, nullptr, nullptr,
+               E, h, f, f, fs.nt1, fs.mt1, part, fs.split_max, fs.grid1};
   launch_gemm<true>(fs.bm1, p, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up_fp8(const FfnShape& fs, const void* X8, const float* x_scale,
+                              const int32_t* offset, const int32_t* map1, const void* Wg8,
+                              const float* s_gate, const void* Wu8, const float* s_up, void* A,
+                              float* part, int E, int h, int f, hipStream_t s) {
+  if (fs.grid1 == 0) return hipSuccess;
+  GemmParams p{X8, offset, map1, Wg8, Wu8, static_cast<bf16*>(A), x_scale, s_gate, s_up,
+               E, h, f, f, fs.nt1, fs.mt1, part, fs.split_max, fs.grid1};
+  launch_gemm_fp8(fs.bm1, p, s);
   return hipGetLastError();
 }
 
@@ -705,8 +786,8 @@ hipError_t launch_down(const FfnShape& fs, const void* A, const int32_t* offset,
                        int f, int bf16_, hipStream_t s) {
   if (!bf16_) return hipErrorNotSupported;
   if (fs.grid2 == 0) return hipSuccess;
-  GemmParams p{static_cast<const bf16*>(A), offset, map2, static_cast<const bf16*>(Wd), nullptr,
-               static_cast<bf16*>(Y), E, f, h, h, fs.nt2, fs.mt2, part, fs.split_max, fs.grid2};
+  GemmParams p{A, offset, map2, Wd, nullptr, static_cast<bf16*>(Y), nullptr, nullptr, nullptr,
+               E, f, h, h, fs.nt2, fs.mt2, part, fs.split_max, fs.grid2};
   launch_gemm<false>(fs.bm2, p, s);
   return hipGetLastError();
 }

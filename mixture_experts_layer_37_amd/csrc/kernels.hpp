@@ -62,6 +62,14 @@ struct DispatchParams {
   int32_t* row_token;
 };
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s);
+// FP8 dispatch (E4M3 codes of each kept row, with its power-of-two scale);
+// bf16 U, h a multiple of 8.
+hipError_t launch_permute_fp8(const void* U, const int32_t* slot, void* X8, float* xs, int T,
+                              int h, int k, hipStream_t s);
+// Row-wise E4M3 codes and power-of-two scales of a bf16 [rows][cols] matrix
+// (cols a multiple of 8).
+hipError_t launch_quantize_rows_fp8(const void* src, int64_t rows, int cols, void* dst,
+                                    float* scale, hipStream_t s);
 hipError_t launch_permute(const void* U, const int32_t* slot, void* X, int T, int h, int k,
                           int bf16, hipStream_t s);
 
@@ -94,6 +102,13 @@ hipError_t launch_dense_offsets(int T, int32_t* offset, hipStream_t s);
 hipError_t launch_gate_up(const FfnShape& fs, const void* X, const int32_t* offset,
                           const int32_t* map1, const void* Wg, const void* Wu, void* A,
                           float* part, int E, int h, int f, int bf16, hipStream_t s);
+// The gate/up GEMM with FP8 (E4M3) operands: X8 [rows][h] codes with
+// x_scale [rows], Wg8 / Wu8 [E][f][h] codes with s_gate / s_up [E][f]
+// (power-of-two scales); h a multiple of 128.  Writes A [rows][f] bf16.
+hipError_t launch_gate_up_fp8(const FfnShape& fs, const void* X8, const float* x_scale,
+                              const int32_t* offset, const int32_t* map1, const void* Wg8,
+                              const float* s_gate, const void* Wu8, const float* s_up, void* A,
+                              float* part, int E, int h, int f, hipStream_t s);
 hipError_t launch_down(const FfnShape& fs, const void* A, const int32_t* offset,
                        const int32_t* map2, const void* Wd, void* Y, float* part, int E, int h,
                        int f, int bf16, hipStream_t s);

@@ -41,6 +41,9 @@ class Workload:
     n_shared: int = 0
     f_shared: int = 0
     sel_bias_var: float = 0.0
+    # FP8 dispatch and up-projection (E4M3, power-of-two row scales); the
+    # inputs stay bf16 and the weights are quantised once before the forward
+    fp8_up: bool = False
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -70,6 +73,9 @@ WORKLOADS = {
                                       k=8, dtype="bf16", score="sigmoid", gate="renorm",
                                       capacity_factor=2.0, n_groups=8, topk_groups=4,
                                       n_shared=1, f_shared=2048, sel_bias_var=1e-4),
+    # the Mixtral shape with the FP8 dispatch and up-projection
+    "mixtral_fp8": Workload("mixtral_fp8", T=4096, h=4096, f=14336, E=8, k=2, dtype="bf16",
+                            score="softmax", gate="renorm", capacity_factor=1.25, fp8_up=True),
 }
 
 WORKLOAD_ORDER = ["tiny_f32", "mixtral_bf16", "switch_bf16", "deepseek_v3_bf16",

@@ -71,17 +71,32 @@ def f64(t):
     return None if t is None else to_np(t).astype(np.float64)
 
 
+def fp8_weights(x):
+    """E4M3 codes and row scales of the routed experts' W_gate and W_up (made
+    once with the library's quantiser and kept in x)."""
+    if "W8_gate" not in x:
+        x["W8_gate"], x["s_gate"] = B.moe_quantize_rows_fp8(x["W_gate"])
+        x["W8_up"], x["s_up"] = B.moe_quantize_rows_fp8(x["W_up"])
+    return x["W8_gate"], x["s_gate"], x["W8_up"], x["s_up"]
+
+
 def run_layer(w, x, fields=None, stage_events=None):
     cfg = B.make_config(w)
     dev = x["U"].device
     if fields is None:
-        fields = [n for n in B.AUX_FIELDS if n != "Y_shared" or w.n_shared > 0]
+        fields = [n for n in B.AUX_FIELDS if (n != "Y_shared" or w.n_shared > 0)
+                  and (n != "X" or not w.fp8_up)]
     aux = B.alloc_aux(cfg, dev, fields)
     out = torch.empty((w.T, w.h), dtype=I.torch_dtype(w), device=dev)
-    B.moe_layer_forward(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], x["noise"], x["W_gate"],
-                        x["W_up"], x["W_down"], out, aux=aux, stage_events=stage_events,
-                        b_sel=x.get("b_sel"), Ws_gate=x.get("Ws_gate"), Ws_up=x.get("Ws_up"),
-                        Ws_down=x.get("Ws_down"))
+    common = dict(aux=aux, stage_events=stage_events, b_sel=x.get("b_sel"),
+                  Ws_gate=x.get("Ws_gate"), Ws_up=x.get("Ws_up"), Ws_down=x.get("Ws_down"))
+    if w.fp8_up:
+        W8g, sg, W8u, su = fp8_weights(x)
+        B.moe_layer_forward_fp8(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], x["noise"], W8g,
+                                sg, W8u, su, x["W_down"], out, **common)
+    else:
+        B.moe_layer_forward(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], x["noise"],
+                            x["W_gate"], x["W_up"], x["W_down"], out, **common)
     torch.cuda.synchronize()
     aux["out"] = out
     return cfg, aux
