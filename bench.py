@@ -20,6 +20,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
@@ -85,11 +86,12 @@ def stage_bandwidth(w, stage_ms, kept, e_active, eb):
     """
     T, h, f, E = w.T, w.h, w.f, w.E
     ns, fs = w.n_shared, w.f_shared
+    e8 = 1 if w.fp8_up else eb  # bytes of a dispatched row element and of W_gate / W_up
     b = {
         "route": eb * (T * h + h * E * (2 if w.noisy else 1)),
-        "dispatch": eb * (T * h + kept * h),
-        "gate_up": eb * (kept * h + 2 * f * h * e_active + kept * f
-                         + ns * (T * h + 2 * fs * h + T * fs)),
+        "dispatch": eb * T * h + e8 * kept * h,
+        "gate_up": (e8 * (kept * h + 2 * f * h * e_active) + eb * kept * f
+                    + eb * ns * (T * h + 2 * fs * h + T * fs)),
         "down": eb * (kept * f + f * h * e_active + kept * h + ns * (T * fs + fs * h + T * h)),
         "combine": eb * (T * h + kept * h + T * h + ns * T * h),
     }
@@ -117,7 +119,8 @@ def cpu_baseline(w, x, g, budget_s: float) -> dict:
     """The float64 oracle, as it is, on a bounded sample of the same workload.
 
     Routing (router product, scores, top-k, capacity fill, statistics) runs on
-    all T tokens.  The expert products run on whole experts taken in order
+    all T tokens.  With the FP8 up-projection the sampled rows and the sampled
+    experts' W_gate and W_up are quantised first (part of the timed work).  The expert products run on whole experts taken in order
     until the time budget is used (each expert's weights converted to float64
     plus its SwiGLU over its rows); combine runs on all tokens.  The time of the
     expert part is scaled by (all kept rows / sampled rows) plus the weight
@@ -151,11 +154,19 @@ def cpu_baseline(w, x, g, budget_s: float) -> dict:
             break
         t1 = time.perf_counter()
         Wg, Wu, Wd = f64(x["W_gate"][e]), f64(x["W_up"][e]), f64(x["W_down"][e])
+        if w.fp8_up:
+            qg, sg = O.quantize_rows_fp8(Wg)
+            qu, su = O.quantize_rows_fp8(Wu)
+            Wg, Wu = qg * sg[:, None], qu * su[:, None]
         t2 = time.perf_counter()
         a, b = int(r["offset"][e]), int(r["offset"][e + 1])
         # cap the rows of one expert so a single expert stays inside the budget
         n = min(b - a, 1024)
-        Y[a:a + n] = O.swiglu_expert(U[r["row_token"][a:a + n]], Wg, Wu, Wd)
+        Xe = U[r["row_token"][a:a + n]]
+        if w.fp8_up:
+            qx, sx = O.quantize_rows_fp8(Xe)
+            Xe = qx * sx[:, None]
+        Y[a:a + n] = O.swiglu_expert(Xe, Wg, Wu, Wd)
         t3 = time.perf_counter()
         t_conv += t2 - t1
         t_ffn += t3 - t2
@@ -214,11 +225,20 @@ def main():
     out = torch.empty((w.T, w.h), dtype=I.torch_dtype(w), device=dev)
     nst = B.MOE_NUM_STAGES
 
+    if w.fp8_up:
+        # the FP8 weights are prepared once, like a model load (not timed)
+        W8g, sg = B.moe_quantize_rows_fp8(x["W_gate"])
+        W8u, su = B.moe_quantize_rows_fp8(x["W_up"])
+
     def step(events=None):
-        B.moe_layer_forward(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], x["noise"],
-                            x["W_gate"], x["W_up"], x["W_down"], out, aux=aux,
-                            stage_events=events, ws=ws, b_sel=x["b_sel"], Ws_gate=x["Ws_gate"],
-                            Ws_up=x["Ws_up"], Ws_down=x["Ws_down"])
+        common = dict(aux=aux, stage_events=events, ws=ws, b_sel=x["b_sel"],
+                      Ws_gate=x["Ws_gate"], Ws_up=x["Ws_up"], Ws_down=x["Ws_down"])
+        if w.fp8_up:
+            B.moe_layer_forward_fp8(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], x["noise"],
+                                    W8g, sg, W8u, su, x["W_down"], out, **common)
+        else:
+            B.moe_layer_forward(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], x["noise"],
+                                x["W_gate"], x["W_up"], x["W_down"], out, **common)
 
     for _ in range(args.warmup):
         step()
@@ -255,12 +275,16 @@ def main():
     f_nom = 6.0 * w.h * w.f * w.k * w.T + f_sh
     f_gate_up = 4.0 * w.h * w.f * kept + f_sh * 4.0 / 6.0
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    peak_gu = PEAK_FP8_TFLOPS if w.fp8_up else peak  # the gate/up GEMM's own dtype
     gu_ms = stage_ms["gate_up"]
     achieved = f_gate_up / (gu_ms * 1e-3) / 1e12
     kept_per_e = aux["kept"].cpu().tolist()
     e_active = sum(1 for c in kept_per_e if c > 0)
-    b_alg = eb * (3.0 * w.h * w.f * e_active + 3.0 * w.h * w.f_shared * w.n_shared
-                  + 2.0 * w.T * w.h + w.h * w.E * (2 if w.noisy else 1))
+    # W_gate and W_up are read as one byte per element on the FP8 path
+    ew = 1 if w.fp8_up else eb
+    b_alg = (ew * 2.0 * w.h * w.f * e_active + eb * w.h * w.f * e_active
+             + eb * (3.0 * w.h * w.f_shared * w.n_shared + 2.0 * w.T * w.h
+                     + w.h * w.E * (2 if w.noisy else 1)))
 
     res = {
         "metric": "MoE layer fwd tokens/sec on 1 MI355X",
@@ -273,7 +297,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if bf16 else "f32",
+        # FP8: E4M3 operands in the gate/up GEMM, bf16 everywhere else
+        "dtype": ("fp8+bf16" if w.fp8_up else "bf16") if bf16 else "f32",
         "data": "synthetic",
         "config": dict({"workload": w.name, "T": w.T, "h": w.h, "f": w.f, "E": w.E, "k": w.k,
                         "score": w.score, "gate": w.gate, "capacity_factor": w.capacity_factor,
@@ -282,10 +307,11 @@ def main():
                           if w.n_groups > 1 else {}),
                        **({"n_shared": w.n_shared, "f_shared": w.f_shared}
                           if w.n_shared else {}),
-                       **({"sel_bias_std": w.sel_bias_var ** 0.5} if w.sel_bias_var else {})),
+                       **({"sel_bias_std": w.sel_bias_var ** 0.5} if w.sel_bias_var else {}),
+                       **({"fp8_up": True} if w.fp8_up else {})),
         "roofline": {"kernel": "grouped gate/up GEMM + SwiGLU", "bound": "mfma",
-                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": measured_traffic(w.name)},
+                     "achieved": achieved, "peak": peak_gu, "unit": "TFLOP/s",
+                     "frac": achieved / peak_gu, "traffic": measured_traffic(w.name)},
         "layer": {"mfma_frac_nominal": f_nom / (ms * 1e-3) / 1e12 / peak,
                   "mfma_frac_exec": f_exec / (ms * 1e-3) / 1e12 / peak,
                   "hbm_frac_alg": b_alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
