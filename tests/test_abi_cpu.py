@@ -153,6 +153,25 @@ def test_bad_enums_and_null_pointers():
                   None) == B.MOE_ERR_INVALID_ARG
     assert status("moe_stats", ctypes.byref(cfg), None, fake, fake, None, None, None, None,
                   None, None) == B.MOE_ERR_INVALID_ARG
+    # FP8 calls: bf16 and h a multiple of 128 only; their scale pointers are required
+    fcfg = cfg_of(h=384)
+    assert status("moe_dispatch_fp8", ctypes.byref(cfg_of(h=320)), fake, fake, fake, fake, fake,
+                  fake, fake, fake, fake, fake, 1 << 30, None) == B.MOE_ERR_UNSUPPORTED
+    f32cfg = B.make_config(I.WORKLOADS["tiny_f32"])
+    assert status("moe_dispatch_fp8", ctypes.byref(f32cfg), fake, fake, fake, fake, fake, fake,
+                  fake, fake, fake, fake, 1 << 30, None) == B.MOE_ERR_UNSUPPORTED
+    assert status("moe_dispatch_fp8", ctypes.byref(fcfg), fake, fake, fake, None, fake, fake,
+                  fake, fake, fake, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    assert status("moe_expert_ffn_fp8", ctypes.byref(fcfg), fake, fake, fake, fake, None, fake,
+                  fake, fake, fake, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    assert status("moe_layer_forward_fp8", ctypes.byref(fcfg), fake, fake, None, None, None, None,
+                  fake, fake, fake, None, fake, None, None, None, other, None, None, fake,
+                  1 << 30, None) == B.MOE_ERR_INVALID_ARG  # s_up missing
+    assert status("moe_quantize_rows_fp8", fake, 4, 12, fake, fake, None) == B.MOE_ERR_UNSUPPORTED
+    assert status("moe_quantize_rows_fp8", fake, 4, 0, fake, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert status("moe_quantize_rows_fp8", fake, -1, 16, fake, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert status("moe_quantize_rows_fp8", None, 4, 16, fake, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert status("moe_quantize_rows_fp8", None, 0, 16, None, None, None) == B.MOE_OK
     # the z-loss helper needs its output, and logits when there are tokens
     assert status("moe_router_z_loss", ctypes.byref(cfg), fake, None, None) == B.MOE_ERR_INVALID_ARG
     assert status("moe_router_z_loss", ctypes.byref(cfg), None, fake, None) == B.MOE_ERR_INVALID_ARG
