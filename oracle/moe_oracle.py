@@ -33,6 +33,14 @@ unless another page is named):
   * Group-limited (node-limited) selection, section "设备受限与节点受限路由".
   * Router z-loss L_z = (1/T) sum_t (log sum_j exp H_{t,j})^2 (ST-MoE),
     section "各家的变体", subsection "Router z-loss 与数值稳定", equation L_z.
+  * Backward pass: the gradient reaching the gates is the inner product of
+    the upstream gradient with the expert's output, carried on through the
+    score function to the logits, W_r and u_t (section "路由器：打分、top-k、
+    加权求和", equation dL/dg); the load-balance term's logit gradient
+    (section "负载均衡辅助损失：推导与梯度", the equations for softmax and, with
+    s' = s / sum s, for sigmoid scores); the expert products backward as
+    grouped products for inputs and weights (section "专家计算：padding、
+    block-sparse 与 grouped GEMM", last paragraph).
   * FP8 dispatch and FP8 up-projection with power-of-two scaling factors and
     a BF16 combine (DeepSeek-V3), section "低精度通信".  The FP8 format is OCP
     E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest
@@ -379,6 +387,115 @@ def expert_outputs_fp8(Xq, xs, offset, Wq_gate, s_gate, Wq_up, s_up, W_down) -> 
     Wg = f64(Wq_gate) * f64(s_gate)[..., None]
     Wu = f64(Wq_up) * f64(s_up)[..., None]
     return expert_outputs(X, offset, Wg, Wu, W_down)
+
+
+# --------------------------------------------------------------------------- backward
+def dsilu(v: np.ndarray) -> np.ndarray:
+    """d/dv (v sigmoid(v)) = sigmoid(v) (1 + v (1 - sigmoid(v)))."""
+    sg = 1.0 / (1.0 + np.exp(-f64(v)))
+    return sg * (1.0 + v * (1.0 - sg))
+
+
+def aux_logit_grad(s, f, score: str) -> np.ndarray:
+    """d/dH[t, k] of sum_i f_i P_i with f held constant (it has no gradient),
+    times T: s_k (f_k - sum_i f_i s_i) for softmax scores, and
+    s'_k (1 - s_k) (f_k - sum_i f_i s'_i) with s' = s / sum_j s for sigmoid
+    scores.  The layer's aux = E sum f P and P averages over the T tokens, so
+    its gradient is (E / T) times this."""
+    s, f = f64(s), f64(f)
+    if score == SOFTMAX:
+        return s * (f[None, :] - (s * f[None, :]).sum(axis=1, keepdims=True))
+    if score == SIGMOID:
+        sp = s / s.sum(axis=1, keepdims=True)
+        return sp * (1.0 - s) * (f[None, :] - (sp * f[None, :]).sum(axis=1, keepdims=True))
+    raise ValueError(score)
+
+
+def z_loss_logit_grad(H) -> np.ndarray:
+    """dL_z/dH[t, k] = (2 / T) LSE(H_t) softmax(H_t)_k."""
+    H = f64(H)
+    T = H.shape[0]
+    m = H.max(axis=1, keepdims=True)
+    e = np.exp(H - m)
+    lse = m[:, 0] + np.log(e.sum(axis=1))
+    return 2.0 / T * lse[:, None] * e / e.sum(axis=1, keepdims=True)
+
+
+def layer_backward(U, W_r, W_gate, W_up, W_down, fwd: dict, dOut, *, score: str, gate: str,
+                   alpha: float = 0.0, c_z: float = 0.0) -> dict:
+    """Gradients of L = <dOut, out> + alpha * aux + c_z * L_z for the routing
+    in fwd (a layer_forward result).  The top-k choice, the capacity cut and
+    the load fractions f are piecewise constant and carry no gradient; a
+    dropped assignment adds nothing to out, but its score still enters the
+    renormalisation of the token's other gates.  Every expert product is
+    recomputed from the inputs.  Returns dU, dW_r, db_r, dW_gate, dW_up,
+    dW_down, and the intermediate dgate [T, k] and dH [T, E].
+    """
+    U, W_r, dOut = f64(U), f64(W_r), f64(dOut)
+    Wg, Wu, Wd = f64(W_gate), f64(W_up), f64(W_down)
+    T, h = U.shape
+    E = W_r.shape[1]
+    idx, g, slot = np.asarray(fwd["idx"]), f64(fwd["gate"]), np.asarray(fwd["slot"])
+    off, row_token = np.asarray(fwd["offset"]), np.asarray(fwd["row_token"])
+    k = idx.shape[1]
+    rows = int(off[-1])
+    # experts, recomputed
+    X = U[row_token]
+    Y = np.zeros((rows, h))
+    dY = np.zeros((rows, h))
+    dgate = np.zeros((T, k))
+    G, Up = np.zeros((rows, Wg.shape[1])), np.zeros((rows, Wg.shape[1]))
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        G[a:b], Up[a:b] = X[a:b] @ Wg[e].T, X[a:b] @ Wu[e].T
+        Y[a:b] = (silu(G[a:b]) * Up[a:b]) @ Wd[e].T
+    # combine: out_t = u_t + sum_r g[t, r] Y[slot[t, r]]
+    for t in range(T):
+        for r in range(k):
+            if slot[t, r] >= 0:
+                dY[slot[t, r]] += g[t, r] * dOut[t]
+                dgate[t, r] = dOut[t] @ Y[slot[t, r]]
+    dWg, dWu, dWd = np.zeros_like(Wg), np.zeros_like(Wu), np.zeros_like(Wd)
+    dX = np.zeros((rows, h))
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        A = silu(G[a:b]) * Up[a:b]
+        dA = dY[a:b] @ Wd[e]
+        dWd[e] = dY[a:b].T @ A
+        dG = dA * Up[a:b] * dsilu(G[a:b])
+        dUp = dA * silu(G[a:b])
+        dWg[e] = dG.T @ X[a:b]
+        dWu[e] = dUp.T @ X[a:b]
+        dX[a:b] = dG @ Wg[e] + dUp @ Wu[e]
+    dU = dOut.copy()
+    for row in range(rows):
+        dU[row_token[row]] += dX[row]
+    # gates -> scores -> logits
+    H = f64(fwd["logits"])
+    s = scores(H, score)
+    ds = np.zeros((T, E))
+    for t in range(T):
+        sel = idx[t]
+        if gate == GATE_RAW:
+            ds[t, sel] += dgate[t]
+        elif gate == GATE_RENORM:
+            S = s[t, sel].sum()
+            ds[t, sel] += (dgate[t] - (dgate[t] * g[t]).sum()) / S
+        else:
+            raise ValueError(gate)
+    if score == SOFTMAX:
+        dH = s * (ds - (ds * s).sum(axis=1, keepdims=True))
+    elif score == SIGMOID:
+        dH = ds * s * (1.0 - s)
+    else:
+        raise ValueError(score)
+    if alpha:
+        dH += alpha * E / T * aux_logit_grad(s, fwd["f"], score)
+    if c_z:
+        dH += c_z * z_loss_logit_grad(H)
+    dU += dH @ W_r.T
+    return {"dU": dU, "dW_r": U.T @ dH, "db_r": dH.sum(axis=0), "dW_gate": dWg, "dW_up": dWu,
+            "dW_down": dWd, "dgate": dgate, "dH": dH}
 
 
 # --------------------------------------------------------------------------- layer

@@ -631,3 +631,81 @@ def test_fp8_layer_equals_plain_layer_on_the_grid():
                         capacity_factor=1.0)
     rel = np.abs(c["out"] - d["out"] - (U2 - U2)).max() / np.abs(d["out"] - U2).max()
     assert 0 < rel < 0.2
+
+
+# ------------------------------------------------------------------ backward
+def test_aux_gradient_worked_example():
+    g = golden("aux_gradient.json")
+    s = np.array([g["s"]])
+    H = np.log(s)  # softmax(log s) = s
+    np.testing.assert_allclose(O.scores(H, O.SOFTMAX), s, rtol=1e-15)
+    assert abs(float(np.dot(g["f"], g["s"])) - g["weighted_mean_load"]) < 1e-15
+    np.testing.assert_allclose(O.aux_logit_grad(O.scores(H, O.SOFTMAX), g["f"], O.SOFTMAX)[0],
+                               g["grad"], rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("score", [O.SOFTMAX, O.SIGMOID])
+def test_aux_gradient_finite_differences(score):
+    # sum_i f_i P_i with f held constant, P from the oracle's own statistics
+    r = rng(21)
+    T, E, k = 5, 6, 2
+    H = r.normal(0, 1.5, (T, E))
+    f = r.dirichlet(np.ones(E))
+
+    def fp(Hx):
+        s = O.scores(Hx, score)
+        idx = O.select_topk(Hx, k)
+        fr = O.fill(idx, E, T * k)
+        return float(np.dot(f, O.load_stats(s, idx, fr, score)["P"]))
+
+    eps = 1e-6
+    fd = np.zeros_like(H)
+    for t in range(T):
+        for j in range(E):
+            Hp, Hm = H.copy(), H.copy()
+            Hp[t, j] += eps
+            Hm[t, j] -= eps
+            fd[t, j] = (fp(Hp) - fp(Hm)) / (2 * eps)
+    np.testing.assert_allclose(fd, O.aux_logit_grad(O.scores(H, score), f, score) / T,
+                               rtol=1e-6, atol=1e-10)
+
+
+@pytest.mark.parametrize("score,gate,cf", [(O.SOFTMAX, O.GATE_RENORM, 0.6),
+                                           (O.SIGMOID, O.GATE_RENORM, 1.0),
+                                           (O.SOFTMAX, O.GATE_RAW, 0.6)])
+def test_layer_backward_finite_differences(score, gate, cf):
+    # L = <dOut, out> + alpha aux + c_z L_z; routing and the capacity cut are
+    # piecewise constant, so central differences of the forward oracle must
+    # match every gradient of layer_backward on generic inputs
+    T, h, f, E, k = 7, 4, 3, 3, 2
+    r = rng(22)
+    U = r.normal(0, 1, (T, h))
+    W_r = r.normal(0, 0.8, (h, E))
+    b_r = r.normal(0, 0.3, E)
+    Wg, Wu = r.normal(0, 0.6, (E, f, h)), r.normal(0, 0.6, (E, f, h))
+    Wd = r.normal(0, 0.6, (E, h, f))
+    dOut = r.normal(0, 1, (T, h))
+    alpha, c_z = 0.3, 0.05
+    kw = dict(k=k, score=score, gate=gate, capacity_factor=cf)
+
+    def loss(U_, W_r_, b_r_, Wg_, Wu_, Wd_):
+        o = O.layer_forward(U_, W_r_, Wg_, Wu_, Wd_, b_r=b_r_, **kw)
+        return float(np.sum(dOut * o["out"])) + alpha * o["aux"] + c_z * o["z_loss"]
+
+    fwd = O.layer_forward(U, W_r, Wg, Wu, Wd, b_r=b_r, **kw)
+    if cf < 1:
+        assert fwd["n_dropped"] > 0
+    bw = O.layer_backward(U, W_r, Wg, Wu, Wd, fwd, dOut, score=score, gate=gate, alpha=alpha,
+                          c_z=c_z)
+    args = [U, W_r, b_r, Wg, Wu, Wd]
+    names = ["dU", "dW_r", "db_r", "dW_gate", "dW_up", "dW_down"]
+    eps = 1e-6
+    for i, name in enumerate(names):
+        fd = np.zeros_like(args[i])
+        for j in np.ndindex(args[i].shape):
+            ap = [a.copy() for a in args]
+            am = [a.copy() for a in args]
+            ap[i][j] += eps
+            am[i][j] -= eps
+            fd[j] = (loss(*ap) - loss(*am)) / (2 * eps)
+        np.testing.assert_allclose(bw[name], fd, rtol=1e-5, atol=1e-7, err_msg=name)
