@@ -137,7 +137,8 @@ typedef enum {
   MOE_WS_DISPATCH = 1,
   MOE_WS_EXPERT_FFN = 2,
   MOE_WS_LAYER = 3,
-  MOE_WS_SHARED_FFN = 4
+  MOE_WS_SHARED_FFN = 4,
+  MOE_WS_BACKWARD = 5
 } moe_ws_entry;
 
 /* Stage boundaries recorded by moe_layer_forward when stage_events != NULL:
@@ -254,6 +255,34 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
                           const void* Ws_down, void* out, const moe_aux_outputs* aux,
                           void* const* stage_events, void* ws, size_t ws_bytes,
                           void* stream);
+
+/* ---------------------------------------------------------------- backward
+ * Gradients of L = <dOut, out> + alpha * aux_loss + c_z * z_loss with respect
+ * to U, W_r, b_r, W_gate, W_up and W_down, for the routing a moe_layer_forward
+ * call chose (page "MoE 与专家并行": the gates' gradient is the inner product
+ * of the upstream gradient with the expert's output and flows on through the
+ * score function, section "路由器：打分、top-k、加权求和", eq. dL/dg; the
+ * load-balance term's logit gradient, section "负载均衡辅助损失：推导与梯度"; the
+ * z-loss's, section "各家的变体"; the experts as grouped products for inputs
+ * and weights, section "专家计算：padding、block-sparse 与 grouped GEMM").  The
+ * top-k choice, the capacity cut and the load fractions f carry no gradient.
+ *  Inputs: U, W_r, W_gate, W_up, W_down as given to the forward; from its
+ *  outputs (moe_aux_outputs) logits [T,E], topk_idx, topk_gate, slot [T,k],
+ *  count [E], offset [E+1]; dOut [T,h] the upstream gradient.  alpha and c_z
+ *  scale aux_loss and z_loss (finite; 0 leaves a term out).  The experts are
+ *  recomputed from U (no activations are kept by the forward).
+ *  Outputs: dU [T,h] and dW_gate, dW_up [E,f,h], dW_down [E,h,f] in bf16;
+ *  dW_r [h,E] and db_r [E] (nullable) in float32.
+ *  Supported: cfg->dtype == MOE_BF16, not noisy, no shared experts (else
+ *  MOE_ERR_UNSUPPORTED); the routing may come from a selection bias or
+ *  groups.  ws: MOE_WS_BACKWARD bytes. */
+int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r,
+                           const void* W_gate, const void* W_up, const void* W_down,
+                           const float* logits, const int32_t* topk_idx, const float* topk_gate,
+                           const int32_t* slot, const int32_t* count, const int32_t* offset,
+                           const void* dOut, float alpha, float c_z, void* dU, float* dW_r,
+                           float* db_r, void* dW_gate, void* dW_up, void* dW_down, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- FP8
  * FP8 dispatch and FP8 up-projection (page "MoE 与专家并行", section

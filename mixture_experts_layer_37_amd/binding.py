@@ -22,7 +22,8 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_GATE_RAW, MOE_GATE_RENORM = 0, 1
 MOE_FILL_RANK_MAJOR, MOE_FILL_TOKEN_MAJOR = 0, 1
 MOE_CAP_ASSIGNMENTS, MOE_CAP_TOKENS = 0, 1
-MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_EXPERT_FFN, MOE_WS_LAYER, MOE_WS_SHARED_FFN = range(5)
+(MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_EXPERT_FFN, MOE_WS_LAYER, MOE_WS_SHARED_FFN,
+ MOE_WS_BACKWARD) = range(6)
 MOE_NUM_STAGES = 6
 STAGE_NAMES = ["route", "dispatch", "gate_up", "down", "combine", "stats"]
 
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
             "moe_layer_forward_fp8": (I32, [cfgp] + [P] * 15 + [ctypes.POINTER(moe_aux_outputs),
                                                               P, P, SZ, P]),
             "moe_quantize_rows_fp8": (I32, [P, I64, I64, P, P, P]),
+            "moe_layer_backward": (I32, [cfgp] + [P] * 12 + [ctypes.c_float, ctypes.c_float]
+                                   + [P] * 6 + [P, SZ, P]),
             "moe_dispatch_fp8": (I32, [cfgp] + [P] * 9 + [P, SZ, P]),
             "moe_expert_ffn_fp8": (I32, [cfgp] + [P] * 9 + [P, SZ, P]),
         }
@@ -397,6 +400,34 @@ def moe_layer_forward_fp8(cfg, U, W_r, b_r, W_noise, noise, W8_gate, s_gate, W8_
                _ptr(s_up, "s_up", (E, f), torch.float32)]
     _layer_call("moe_layer_forward_fp8", cfg, U, W_r, b_r, W_noise, noise, weights, W_down, out,
                 aux, stage_events, ws, stream, b_sel, Ws_gate, Ws_up, Ws_down)
+
+
+def moe_layer_backward(cfg, U, W_r, W_gate, W_up, W_down, logits, topk_idx, topk_gate, slot,
+                       count, offset, dOut, dU, dW_r, dW_gate, dW_up, dW_down, db_r=None,
+                       alpha=0.0, c_z=0.0, ws=None, stream=None):
+    """Gradients of <dOut, out> + alpha aux_loss + c_z z_loss for the routing of a
+    forward (logits ... offset from its aux outputs).  dU, dW_gate, dW_up,
+    dW_down bf16; dW_r [h, E] and db_r [E] float32."""
+    T, h, f, E, k = cfg.T, cfg.h, cfg.f, cfg.E, cfg.k
+    bf = torch.bfloat16
+    need = workspace_size(cfg, MOE_WS_BACKWARD)
+    ws = new_workspace(cfg, MOE_WS_BACKWARD, W_r.device) if ws is None else ws
+    wp, wn = _ws(ws, need)
+    args = [
+        _ptr(U, "U", (T, h), bf), _ptr(W_r, "W_r", (h, E), bf),
+        _ptr(W_gate, "W_gate", (E, f, h), bf), _ptr(W_up, "W_up", (E, f, h), bf),
+        _ptr(W_down, "W_down", (E, h, f), bf), _ptr(logits, "logits", (T, E), torch.float32),
+        _ptr(topk_idx, "topk_idx", (T, k), torch.int32),
+        _ptr(topk_gate, "topk_gate", (T, k), torch.float32),
+        _ptr(slot, "slot", (T, k), torch.int32), _ptr(count, "count", (E,), torch.int32),
+        _ptr(offset, "offset", (E + 1,), torch.int32), _ptr(dOut, "dOut", (T, h), bf),
+        ctypes.c_float(alpha), ctypes.c_float(c_z),
+        _ptr(dU, "dU", (T, h), bf), _ptr(dW_r, "dW_r", (h, E), torch.float32),
+        _ptr(db_r, "db_r", (E,), torch.float32), _ptr(dW_gate, "dW_gate", (E, f, h), bf),
+        _ptr(dW_up, "dW_up", (E, f, h), bf), _ptr(dW_down, "dW_down", (E, h, f), bf),
+    ]
+    _check(lib().moe_layer_backward(ctypes.byref(cfg), *args, wp, wn, _stream(stream)),
+           "moe_layer_backward")
 
 
 def moe_quantize_rows_fp8(src, dst=None, scale=None, stream=None):

@@ -8,6 +8,8 @@
 // calls.
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <algorithm>
 #include <string.h>
 
 #include "kernels.hpp"
@@ -230,6 +232,47 @@ LayerWs plan_layer(const Dims& d, int noisy, Plan& pl) {
   return w;
 }
 
+// Backward workspace: recomputed expert activations, their gradients, the
+// transposed weights, and the activations transposed into the zero-padded
+// per-expert K layout of the weight-gradient products (pitch Kp).
+struct BackwardWs {
+  FfnWs ffn;  // tile maps, A (the SwiGLU rows), K-split partials
+  FfnShape fsA, fsX;  // shapes of the dA (N = f, K = h) and dX (N = h, K = 2f) products
+  int Kp;
+  size_t X, GU, Y, dY, dA, dGU, dX, WdT, WguT, dYT, AT, dGUT, XT, kofs, dgate, dH, part;
+};
+BackwardWs plan_backward(const Dims& d, Plan& pl) {
+  BackwardWs w;
+  w.ffn = plan_ffn(d, pl);
+  const int ncu = device_cus();
+  w.fsA = ffn_shape(d.rows_max, (int)d.E, (int)d.f, (int)d.h, (int)d.T, (int)d.k, 1, ncu);
+  w.fsX = ffn_shape(d.rows_max, (int)d.E, (int)d.h, (int)(2 * d.f), (int)d.T, (int)d.k, 1, ncu);
+  const size_t rows = (size_t)(d.rows_max > 0 ? d.rows_max : 1);
+  w.Kp = (int)(((d.rows_max + 63) / 64) * 64 + 64 * d.E);
+  const size_t kp = (size_t)w.Kp;
+  const size_t T1 = (size_t)(d.T > 0 ? d.T : 1);
+  w.X = pl.add(rows * d.h * 2);
+  w.GU = pl.add(rows * 2 * d.f * 2);
+  w.Y = pl.add(rows * d.h * 2);
+  w.dY = pl.add(rows * d.h * 2);
+  w.dA = pl.add(rows * d.f * 2);
+  w.dGU = pl.add(rows * 2 * d.f * 2);
+  w.dX = pl.add(rows * d.h * 2);
+  w.WdT = pl.add((size_t)d.E * d.f * d.h * 2);
+  w.WguT = pl.add((size_t)d.E * d.h * 2 * d.f * 2);
+  w.dYT = pl.add((size_t)d.h * kp * 2);
+  w.AT = pl.add((size_t)d.f * kp * 2);
+  w.dGUT = pl.add((size_t)2 * d.f * kp * 2);
+  w.XT = pl.add((size_t)d.h * kp * 2);
+  w.kofs = pl.add((d.E + 1) * 4);
+  w.dgate = pl.add(T1 * d.k * 4);
+  w.dH = pl.add(T1 * d.E * 4);
+  // K-split partials for the largest grid of the three row-grouped products
+  const int slots = std::max(w.ffn.fs.part_slots, std::max(w.fsA.part_slots, w.fsX.part_slots));
+  w.part = pl.add((size_t)slots * kPartSlotBytes);
+  return w;
+}
+
 template <typename P>
 P* at(void* ws, size_t off) {
   return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
@@ -447,6 +490,7 @@ int32_t moe_workspace_size(const moe_config* cfg, int32_t entry, size_t* bytes) 
     case MOE_WS_EXPERT_FFN: plan_ffn(d, pl); break;
     case MOE_WS_LAYER: plan_layer(d, cfg->noisy, pl); break;
     case MOE_WS_SHARED_FFN: plan_shared(d, false, pl); break;
+    case MOE_WS_BACKWARD: plan_backward(d, pl); break;
     default: return MOE_ERR_INVALID_ARG;
   }
   *bytes = pl.bytes;
@@ -681,6 +725,82 @@ int32_t moe_layer_forward_fp8(const moe_config* cfg, const void* U, const void* 
   Fp8Up f8{W8_gate, s_gate, W8_up, s_up, nullptr};
   return layer_impl(cfg, U, W_r, b_r, b_sel, W_noise, noise, W8_gate, W8_up, W_down, Ws_gate,
                     Ws_up, Ws_down, out, aux, stage_events, ws, ws_bytes, stream, &f8);
+}
+
+int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r,
+                           const void* W_gate, const void* W_up, const void* W_down,
+                           const float* logits, const int32_t* topk_idx, const float* topk_gate,
+                           const int32_t* slot, const int32_t* count, const int32_t* offset,
+                           const void* dOut, float alpha, float c_z, void* dU, float* dW_r,
+                           float* db_r, void* dW_gate, void* dW_up, void* dW_down, void* ws,
+                           size_t ws_bytes, void* stream) {
+  int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16 || cfg->noisy || cfg->n_shared > 0) return MOE_ERR_UNSUPPORTED;
+  const Dims d = dims_of(cfg);
+  if (!W_r || !W_gate || !W_up || !W_down || !count || !offset || !dW_r || !dW_gate ||
+      !dW_up || !dW_down || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (!U || !logits || !topk_idx || !topk_gate || !slot || !dOut || !dU))
+    return MOE_ERR_INVALID_ARG;
+  if (!isfinite(alpha) || !isfinite(c_z)) return MOE_ERR_INVALID_ARG;
+  Plan pl;
+  const BackwardWs w = plan_backward(d, pl);
+  if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int E = (int)d.E, h = (int)d.h, f = (int)d.f, T = (int)d.T, k = (int)d.k;
+  const int ncu = device_cus();
+  void* X = at<void>(ws, w.X);
+  void* A = at<void>(ws, w.ffn.A);
+  void* GU = at<void>(ws, w.GU);
+  void* Y = at<void>(ws, w.Y);
+  void* dY = at<void>(ws, w.dY);
+  void* dA = at<void>(ws, w.dA);
+  void* dGU = at<void>(ws, w.dGU);
+  void* dX = at<void>(ws, w.dX);
+  int32_t* kofs = at<int32_t>(ws, w.kofs);
+  float* dgate = at<float>(ws, w.dgate);
+  float* dH = at<float>(ws, w.dH);
+  float* part = at<float>(ws, w.part);
+  const int32_t* map = at<int32_t>(ws, w.ffn.map1);  // every product uses the same row tiles
+  // 1. recompute the experts: X, then A = SiLU(g) u with g, u kept, then Y
+  st = run_tile_map(d, w.ffn, offset, ws, s);
+  if (st != MOE_OK) return st;
+  MOE_TRY(launch_permute(U, slot, X, T, h, k, 1, s));
+  MOE_TRY(launch_gate_up_save(w.ffn.fs, X, offset, map, W_gate, W_up, A, GU, part, E, h, f, s));
+  MOE_TRY(launch_down(w.ffn.fs, A, offset, at<int32_t>(ws, w.ffn.map2), W_down, Y, part, E, h,
+                      f, 1, s));
+  // 2. combine: dY rows and the gates' gradient
+  MOE_TRY(launch_combine_bwd(dOut, Y, slot, topk_gate, dY, dgate, T, h, k, s));
+  // 3. dA = dY W_down (B = W_down^T, [E][f][h]); SwiGLU backward; dX = [dg du] [W_gate; W_up]
+  MOE_TRY(launch_transpose_batched(W_down, h, f, (size_t)h * f, at<void>(ws, w.WdT), h, 0,
+                                   (size_t)f * h, E, s));
+  MOE_TRY(launch_down(w.fsA, dY, offset, map, at<void>(ws, w.WdT), dA, part, E, f, h, 1, s));
+  MOE_TRY(launch_swiglu_bwd(dA, GU, offset, E, d.rows_max, f, dGU, s));
+  MOE_TRY(launch_transpose_batched(W_gate, f, h, (size_t)f * h, at<void>(ws, w.WguT), 2 * f, 0,
+                                   (size_t)h * 2 * f, E, s));
+  MOE_TRY(launch_transpose_batched(W_up, f, h, (size_t)f * h, at<void>(ws, w.WguT), 2 * f, f,
+                                   (size_t)h * 2 * f, E, s));
+  MOE_TRY(launch_down(w.fsX, dGU, offset, map, at<void>(ws, w.WguT), dX, part, E, h, 2 * f, 1,
+                      s));
+  // 4. weight gradients: sums over each expert's rows of outer products
+  MOE_TRY(launch_kofs(offset, E, kofs, s));
+  MOE_TRY(launch_transpose_pad(dY, offset, kofs, E, h, at<void>(ws, w.dYT), w.Kp, s));
+  MOE_TRY(launch_transpose_pad(A, offset, kofs, E, f, at<void>(ws, w.AT), w.Kp, s));
+  MOE_TRY(launch_transpose_pad(dGU, offset, kofs, E, 2 * f, at<void>(ws, w.dGUT), w.Kp, s));
+  MOE_TRY(launch_transpose_pad(X, offset, kofs, E, h, at<void>(ws, w.XT), w.Kp, s));
+  MOE_TRY(launch_wgrad(at<void>(ws, w.dYT), at<void>(ws, w.AT), kofs, dW_down, E, h, f, w.Kp,
+                       ncu, s));
+  MOE_TRY(launch_wgrad(at<void>(ws, w.dGUT), at<void>(ws, w.XT), kofs, dW_gate, E, f, h, w.Kp,
+                       ncu, s));
+  MOE_TRY(launch_wgrad(at<char>(ws, w.dGUT) + (size_t)f * w.Kp * 2, at<void>(ws, w.XT), kofs,
+                       dW_up, E, f, h, w.Kp, ncu, s));
+  // 5. router: dH, then dU and dW_r, db_r
+  MOE_TRY(launch_router_bwd(logits, topk_idx, topk_gate, dgate, count, T, E, k, cfg->score,
+                            cfg->gate == MOE_GATE_RENORM, alpha, c_z, dH, s));
+  MOE_TRY(launch_grad_input(dOut, dX, slot, dH, W_r, dU, T, h, E, k, s));
+  MOE_TRY(launch_dwr(U, dH, dW_r, db_r, T, h, E, s));
+  return MOE_OK;
 }
 
 int32_t moe_quantize_rows_fp8(const void* src, int64_t rows, int64_t cols, void* dst,

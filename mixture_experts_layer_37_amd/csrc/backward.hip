@@ -1,0 +1,424 @@
+// Backward pass of the layer: gradients of L = <dOut, out> + alpha aux +
+// c_z L_z with respect to U, W_r, b_r and the experts' W_gate, W_up, W_down,
+// for the routing the forward chose (top-k and the capacity cut carry no
+// gradient).
+//
+// Method: page "MoE 与专家并行".  The gradient reaching a gate is the inner
+// product of the upstream gradient with that expert's output, and it flows on
+// through the score function to the logits, W_r and u_t (section
+// "路由器：打分、top-k、加权求和", equation dL/dg).  The load-balance term's
+// logit gradient is s_k (f_k - sum_i f_i s_i) per token (softmax scores), and
+// s'_k (1 - s_k) (f_k - sum_i f_i s'_i) with s' = s / sum_j s (sigmoid), times
+// E / T for aux = E sum f P (section "负载均衡辅助损失：推导与梯度").  The
+// z-loss's is (2 / T) LSE softmax (section "各家的变体", "Router z-loss").  The
+// expert products run backward as grouped products for the inputs and for the
+// weights (section "专家计算：padding、block-sparse 与 grouped GEMM").
+//
+// This file holds the element-wise, reduction and layout kernels; the grouped
+// products are the GEMM kernels of ffn.hip.
+#include <math.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+// Combine backward, one wave per token: dY[slot] = g dOut_t for every kept
+// rank, and dgate[t, r] = dOut_t . Y[slot] (0 for a dropped rank).
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16* dOut, const bf16* Y,
+                                                          const int32_t* slot, const float* gate,
+                                                          bf16* dY, float* dgate, int T, int h,
+                                                          int k) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const int nvec = h / 8;
+  const bf16* d = dOut + (size_t)t * h;
+  for (int r = 0; r < k; ++r) {
+    const int row = slot[(size_t)t * k + r];
+    float acc = 0.f;
+    if (row >= 0) {
+      const float g = gate[(size_t)t * k + r];
+      const bf16* y = Y + (size_t)row * h;
+      bf16* dy = dY + (size_t)row * h;
+      for (int i = lane; i < nvec; i += 64) {
+        float a[8], b[8];
+        Elem<bf16>::unpack(ld16(d + (size_t)i * 8), a);
+        Elem<bf16>::unpack(ld16(y + (size_t)i * 8), b);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          acc = fmaf(a[q], b[q], acc);
+          a[q] *= g;
+        }
+        st16(dy + (size_t)i * 8, Elem<bf16>::pack(a));
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) dgate[(size_t)t * k + r] = acc;
+  }
+}
+
+// SwiGLU backward: a = SiLU(g) u gives dg = da u SiLU'(g) and du = da SiLU(g),
+// with SiLU'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))).  GU and dGU hold
+// [rows][2f] (g or dg in columns 0..f-1, u or du after); rows past offset[E]
+// are left alone.  Eight elements per thread.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const bf16* dA, const bf16* GU,
+                                                         const int32_t* offset, int E, int f,
+                                                         bf16* dGU) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per = f / 8;
+  const int64_t row = i / per;
+  if (row >= offset[E]) return;
+  const int c = (int)(i - row * per) * 8;
+  float da[8], g[8], u[8], dg[8], du[8];
+  Elem<bf16>::unpack(ld16(dA + row * f + c), da);
+  Elem<bf16>::unpack(ld16(GU + row * 2 * f + c), g);
+  Elem<bf16>::unpack(ld16(GU + row * 2 * f + f + c), u);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float sg = 1.f / (1.f + expf(-g[q]));
+    du[q] = da[q] * g[q] * sg;
+    dg[q] = da[q] * u[q] * sg * (1.f + g[q] * (1.f - sg));
+  }
+  st16(dGU + row * 2 * f + c, Elem<bf16>::pack(dg));
+  st16(dGU + row * 2 * f + f + c, Elem<bf16>::pack(du));
+}
+
+// Batched transpose through LDS: for each of `batches` matrices,
+// dst[c][c0 + r] = src[r][c] (src [R][C] with batch stride sb, dst rows of
+// ld elements with batch stride db).  64 x 64 tiles, 256 threads.
+__global__ __launch_bounds__(256) void transpose_batched_kernel(const bf16* src, int R, int C,
+                                                                size_t sb, bf16* dst, int ld,
+                                                                int c0, size_t db) {
+  __shared__ bf16 tile[64][66];
+  const int b = blockIdx.z;
+  const int r0 = blockIdx.y * 64, cc0 = blockIdx.x * 64;
+  const bf16* s = src + b * sb;
+  bf16* d = dst + b * db;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = cc0 + tx;
+    tile[i][tx] = (r < R && c < C) ? s[(size_t)r * C + c] : bf16(0);
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = cc0 + i, r = r0 + tx;
+    if (c < C && r < R) d[(size_t)c * ld + c0 + r] = tile[tx][i];
+  }
+}
+
+// Per-expert offsets of the zero-padded K layout of the weight gradients:
+// kofs[e] = sum over earlier experts of their rows rounded up to 64.
+__global__ __launch_bounds__(256) void kofs_kernel(const int32_t* offset, int E, int32_t* kofs) {
+  __shared__ int tmp[4];
+  const int e = threadIdx.x;
+  const int n = e < E ? offset[e + 1] - offset[e] : 0;
+  int tot;
+  const int a = block_excl_scan256((n + 63) & ~63, tmp, &tot);
+  if (e < E) kofs[e] = a;
+  if (e == 0) kofs[E] = tot;
+}
+
+// Transpose of row-grouped activations into the padded K layout:
+// dst[c][kofs[e] + i] = src[offset[e] + i][c] for the expert's rows i, and 0
+// up to kofs[e + 1].  A 64-wide block of K lies inside one expert.
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const bf16* src, const int32_t* offset,
+                                                            const int32_t* kofs, int E, int C,
+                                                            bf16* dst, int ld) {
+  __shared__ bf16 tile[64][66];
+  const int k0 = blockIdx.y * 64, cc0 = blockIdx.x * 64;
+  if (k0 >= kofs[E]) return;
+  int lo = 0, hi = E;  // expert e with kofs[e] <= k0 < kofs[e + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (kofs[mid] <= k0) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int n = offset[e + 1] - offset[e];
+  const int i0 = k0 - kofs[e];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int ii = i0 + i, c = cc0 + tx;
+    tile[i][tx] = (ii < n && c < C) ? src[(size_t)(offset[e] + ii) * C + c] : bf16(0);
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = cc0 + i;
+    if (c < C) dst[(size_t)c * ld + k0 + tx] = tile[tx][i];
+  }
+}
+
+// Router backward, one wave per token: scores from the float32 logits, the
+// gates' gradient back to the scores (raw: ds = dg; renormalised over the
+// selected set S: ds_j = (dg_j - sum_i dg_i g_i) / sum_S s), then to the
+// logits (softmax: s (ds - <ds, s>); sigmoid: ds s (1 - s)), plus alpha times
+// the aux-loss gradient and c_z times the z-loss gradient.  E <= 256.
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float* logits, const int32_t* idx,
+                                                         const float* gate, const float* dgate,
+                                                         const int32_t* count, int T, int E,
+                                                         int k, int score, int renorm,
+                                                         float alpha, float c_z, float* dH) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  float x[4], s[4], ds[4], fr[4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    x[j] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+    fr[j] = e < E ? (float)count[e] / ((float)T * k) : 0.f;
+    m = fmaxf(m, x[j]);
+  }
+  m = wave_max(m);
+  float z = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    const float ex = e < E ? expf(x[j] - m) : 0.f;
+    s[j] = ex;  // softmax numerators for now
+    z += ex;
+  }
+  z = wave_sum(z);
+  const float lse = m + logf(z);
+  float sm[4];  // softmax of the logits (for the z-loss term)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sm[j] = s[j] / z;
+    s[j] = score == 0 ? sm[j] : ((lane + 64 * j < E) ? 1.f / (1.f + expf(-x[j])) : 0.f);
+    ds[j] = 0.f;
+  }
+  // gates -> scores over the selected experts
+  float ssel = 0.f, dgg = 0.f;
+  for (int r = 0; r < k; ++r) {
+    const int e = idx[(size_t)t * k + r];
+    float se = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j == e) se = s[j];
+    ssel += __shfl(se, e & 63, 64);
+    dgg += dgate[(size_t)t * k + r] * gate[(size_t)t * k + r];
+  }
+  for (int r = 0; r < k; ++r) {
+    const int e = idx[(size_t)t * k + r];
+    const float dg = dgate[(size_t)t * k + r];
+    const float v = renorm ? (dg - dgg) / ssel : dg;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j == e) ds[j] += v;
+  }
+  float dh[4];
+  if (score == 0) {
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dot += ds[j] * s[j];
+    dot = wave_sum(dot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dh[j] = s[j] * (ds[j] - dot);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dh[j] = ds[j] * s[j] * (1.f - s[j]);
+  }
+  if (alpha != 0.f) {
+    float ssum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ssum += s[j];
+    ssum = wave_sum(ssum);
+    float fw = 0.f;  // sum_i f_i s_i (softmax) or sum_i f_i s'_i (sigmoid)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fw += fr[j] * (score == 0 ? s[j] : s[j] / ssum);
+    fw = wave_sum(fw);
+    const float c = alpha * (float)E / (float)T;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dh[j] += score == 0 ? c * s[j] * (fr[j] - fw)
+                          : c * (s[j] / ssum) * (1.f - s[j]) * (fr[j] - fw);
+  }
+  if (c_z != 0.f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dh[j] += c_z * 2.f / (float)T * lse * sm[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    if (e < E) dH[(size_t)t * E + e] = dh[j];
+  }
+}
+
+// dU = dOut + sum over kept ranks of dX[slot] + dH W_r^T, for 16 tokens per
+// workgroup: their dH rows sit in LDS and each W_r row is read once per
+// workgroup.  Thread j handles columns j, j + 256, ...
+constexpr int kGiTok = 16;
+__global__ __launch_bounds__(256) void grad_input_kernel(const bf16* dOut, const bf16* dX,
+                                                         const int32_t* slot, const float* dH,
+                                                         const bf16* W_r, bf16* dU, int T, int h,
+                                                         int E, int k) {
+  __shared__ float sdh[kGiTok][256];
+  __shared__ int ssl[kGiTok][8];
+  const int t0 = blockIdx.x * kGiTok;
+  for (int i = threadIdx.x; i < kGiTok * 256; i += 256) {
+    const int tt = i / 256, e = i % 256, t = t0 + tt;
+    sdh[tt][e] = (t < T && e < E) ? dH[(size_t)t * E + e] : 0.f;
+  }
+  if (threadIdx.x < kGiTok * 8) {
+    const int tt = threadIdx.x / 8, r = threadIdx.x % 8, t = t0 + tt;
+    ssl[tt][r] = (t < T && r < k) ? slot[(size_t)t * k + r] : -1;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < h; j += 256) {
+    float acc[kGiTok];
+#pragma unroll
+    for (int tt = 0; tt < kGiTok; ++tt) acc[tt] = 0.f;
+    const bf16* w = W_r + (size_t)j * E;
+    int e = 0;
+    if ((E & 7) == 0) {  // rows are 16-byte aligned: 8 weights per load
+      for (; e < E; e += 8) {
+        float we[8];
+        Elem<bf16>::unpack(ld16(w + e), we);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int tt = 0; tt < kGiTok; ++tt) acc[tt] = fmaf(sdh[tt][e + q], we[q], acc[tt]);
+      }
+    }
+    for (; e < E; ++e) {
+      const float we = bf16_to_f32(w[e]);
+#pragma unroll
+      for (int tt = 0; tt < kGiTok; ++tt) acc[tt] = fmaf(sdh[tt][e], we, acc[tt]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < kGiTok; ++tt) {
+      const int t = t0 + tt;
+      if (t >= T) break;
+      float v = bf16_to_f32(dOut[(size_t)t * h + j]) + acc[tt];
+      for (int r = 0; r < k; ++r)
+        if (ssl[tt][r] >= 0) v += bf16_to_f32(dX[(size_t)ssl[tt][r] * h + j]);
+      dU[(size_t)t * h + j] = f32_to_bf16(v);
+    }
+  }
+}
+
+// dW_r[j][e] = sum_t U[t][j] dH[t][e] (float32): workgroup b takes 64 rows j
+// and every e, and walks the tokens in chunks of 32 staged in LDS.  db_r[e] =
+// sum_t dH[t][e] comes from workgroup 0 (tokens in order).
+__global__ __launch_bounds__(256) void dwr_kernel(const bf16* U, const float* dH, float* dWr,
+                                                  float* db, int T, int h, int E) {
+  __shared__ float su[32][64];
+  __shared__ float sd[32][256];
+  const int j0 = blockIdx.x * 64;
+  const int nout = 64 * E;  // outputs of this workgroup, id = jj * E + e
+  float acc[64];            // at most 64 * 256 / 256 per thread
+  const int per = (nout + 255) / 256;
+#pragma unroll
+  for (int q = 0; q < 64; ++q) acc[q] = 0.f;
+  for (int tb = 0; tb < T; tb += 32) {
+    for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+      const int tt = i / 64, jj = i % 64, t = tb + tt, j = j0 + jj;
+      su[tt][jj] = (t < T && j < h) ? bf16_to_f32(U[(size_t)t * h + j]) : 0.f;
+    }
+    for (int i = threadIdx.x; i < 32 * 256; i += 256) {
+      const int tt = i / 256, e = i % 256, t = tb + tt;
+      sd[tt][e] = (t < T && e < E) ? dH[(size_t)t * E + e] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 64; ++q) {  // unrolled: acc stays in registers
+      const int o = threadIdx.x + 256 * q;
+      if (q >= per || o >= nout) break;
+      const int jj = o / E, e = o % E;
+      float a = acc[q];
+#pragma unroll 8
+      for (int tt = 0; tt < 32; ++tt) a = fmaf(su[tt][jj], sd[tt][e], a);
+      acc[q] = a;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < 64; ++q) {
+    const int o = threadIdx.x + 256 * q;
+    if (q >= per || o >= nout) break;
+    const int jj = o / E, e = o % E, j = j0 + jj;
+    if (j < h) dWr[(size_t)j * E + e] = acc[q];
+  }
+  if (db && blockIdx.x == 0 && threadIdx.x < E) {
+    float s = 0.f;
+    for (int t = 0; t < T; ++t) s += dH[(size_t)t * E + threadIdx.x];
+    db[threadIdx.x] = s;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine_bwd(const void* dOut, const void* Y, const int32_t* slot,
+                              const float* gate, void* dY, float* dgate, int T, int h, int k,
+                              hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_bwd_kernel, dim3((T + 3) / 4), dim3(256), 0, s,
+                     static_cast<const bf16*>(dOut), static_cast<const bf16*>(Y), slot, gate,
+                     static_cast<bf16*>(dY), dgate, T, h, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const void* dA, const void* GU, const int32_t* offset, int E,
+                             int64_t rows_max, int f, void* dGU, hipStream_t s) {
+  const int64_t n = rows_max * (f / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const bf16*>(dA), static_cast<const bf16*>(GU), offset, E, f,
+                     static_cast<bf16*>(dGU));
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_batched(const void* src, int R, int C, size_t sb, void* dst, int ld,
+                                    int c0, size_t db, int batches, hipStream_t s) {
+  if (batches == 0 || R == 0 || C == 0) return hipSuccess;
+  dim3 grid((C + 63) / 64, (R + 63) / 64, batches);
+  hipLaunchKernelGGL(transpose_batched_kernel, grid, dim3(256), 0, s,
+                     static_cast<const bf16*>(src), R, C, sb, static_cast<bf16*>(dst), ld, c0, db);
+  return hipGetLastError();
+}
+
+hipError_t launch_kofs(const int32_t* offset, int E, int32_t* kofs, hipStream_t s) {
+  hipLaunchKernelGGL(kofs_kernel, dim3(1), dim3(256), 0, s, offset, E, kofs);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_pad(const void* src, const int32_t* offset, const int32_t* kofs,
+                                int E, int C, void* dst, int ld, hipStream_t s) {
+  if (C == 0 || ld == 0) return hipSuccess;
+  dim3 grid((C + 63) / 64, ld / 64);
+  hipLaunchKernelGGL(transpose_pad_kernel, grid, dim3(256), 0, s, static_cast<const bf16*>(src),
+                     offset, kofs, E, C, static_cast<bf16*>(dst), ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const float* gate,
+                             const float* dgate, const int32_t* count, int T, int E, int k,
+                             int score, int renorm, float alpha, float c_z, float* dH,
+                             hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(router_bwd_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, idx, gate,
+                     dgate, count, T, E, k, score, renorm, alpha, c_z, dH);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_input(const void* dOut, const void* dX, const int32_t* slot,
+                             const float* dH, const void* W_r, void* dU, int T, int h, int E,
+                             int k, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(grad_input_kernel, dim3((T + kGiTok - 1) / kGiTok), dim3(256), 0, s,
+                     static_cast<const bf16*>(dOut), static_cast<const bf16*>(dX), slot, dH,
+                     static_cast<const bf16*>(W_r), static_cast<bf16*>(dU), T, h, E, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_dwr(const void* U, const float* dH, float* dWr, float* db, int T, int h, int E,
+                      hipStream_t s) {
+  hipLaunchKernelGGL(dwr_kernel, dim3((h + 63) / 64), dim3(256), 0, s,
+                     static_cast<const bf16*>(U), dH, dWr, db, T, h, E);
+  return hipGetLastError();
+}
+
+}  // namespace moe

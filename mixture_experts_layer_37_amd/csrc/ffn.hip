@@ -91,6 +91,13 @@ struct GemmParams {
   float* part;           // K-split partial tiles: [grid][BM * BN] float32
   int split_max;         // most K chunks a tail tile is split into
   int grid;              // workgroups of the GEMM launch (a multiple of 8)
+  bf16* C2 = nullptr;    // gate/up: also store the pre-activations g and u,
+                         // [rows][2 Nout] (g in columns 0..Nout-1, u after)
+  // weight gradients (gemm_wgrad_kernel): C_e[M][N] = A[:, K_e] B[:, K_e]^T
+  // for each expert e, A [M][K] and B [N][K] with K the row pitch and
+  // K_e = kofs[e] .. kofs[e+1]-1 (multiples of 64, zero-padded)
+  const int32_t* kofs = nullptr;
+  int M = 0;
 };
 
 // A K chunk of a tail tile (see gemm_bf16_kernel); ks == 1: a whole tile.
@@ -191,16 +198,26 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const floatx16 (
           sg[0] = sa * a.x; sg[1] = sa * a.y; sg[2] = sa * a.z; sg[3] = sa * a.w;
           su[0] = sa * b.x; su[1] = sa * b.y; su[2] = sa * b.z; su[3] = sa * b.w;
         }
+        float gp[4], up[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           if (GATEUP) {
             const float gv = acc[i][j][4 * g + t] * sg[t], uv = acc[i][j + 2][4 * g + t] * su[t];
             y[t] = gv / (1.f + __expf(-gv)) * uv;
+            gp[t] = gv;
+            up[t] = uv;
           } else {
             y[t] = acc[i][j][4 * g + t];
           }
         }
         *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+        if (GATEUP && p.C2) {
+          bf16* prow = p.C2 + (size_t)(row0 + r) * 2 * p.Nout;
+          *reinterpret_cast<uint2*>(prow + col) =
+              make_uint2(pack_bf16x2(gp[0], gp[1]), pack_bf16x2(gp[2], gp[3]));
+          *reinterpret_cast<uint2*>(prow + p.Nout + col) =
+              make_uint2(pack_bf16x2(up[0], up[1]), pack_bf16x2(up[2], up[3]));
+        }
       }
     }
   }
@@ -577,6 +594,83 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_kernel(GemmParams p) {
   grouped_gemm<BM, NW, true, true, NA, NB>(p, L);
 }
 
+// Weight gradients of the expert products (section "专家计算：padding、
+// block-sparse 与 grouped GEMM": the backward is a grouped product for the
+// inputs and one for the weights): C_e = A[:, K_e] B[:, K_e]^T, the sum over
+// expert e's rows.  A [M][K] and B [N][K] are the transposed activations with
+// each expert's rows padded with zeros to a multiple of 64 (kofs), so every K
+// step lies inside one expert.  Tiles (e, m-tile, n-tile) in e-major order,
+// round-robin over the persistent grid; the main loop and the cross-tile
+// prefetch are those of the row-grouped GEMM.  An expert without rows gets one
+// K step of zeros (its buffer resource is empty), i.e. C_e = 0.
+__device__ __forceinline__ Unit wgrad_unit(const GemmParams& p, int t, int mt_n, int nt_n) {
+  Unit w;
+  const int per = mt_n * nt_n;
+  const int e = t / per, r = t - e * per, mt = r / nt_n;
+  w.ta.e = __builtin_amdgcn_readfirstlane(e);
+  w.ta.nt = __builtin_amdgcn_readfirstlane(r - mt * nt_n);
+  w.ta.row0 = __builtin_amdgcn_readfirstlane(mt * 256);  // row in A (and in C_e)
+  w.ta.nvalid = __builtin_amdgcn_readfirstlane(min(256, p.M - mt * 256));
+  const int k0 = p.kofs[w.ta.e] / BK, k1 = p.kofs[w.ta.e + 1] / BK;
+  w.ksp = KSplit{__builtin_amdgcn_readfirstlane(k0), __builtin_amdgcn_readfirstlane(max(1, k1 - k0)),
+                 1, nullptr};
+  w.ksp.ks = k1 > k0 ? 1 : 0;  // 0 marks an expert without rows
+  return w;
+}
+__device__ __forceinline__ TileSrc wgrad_src(const GemmParams& p, const Unit& w) {
+  TileSrc s;
+  const size_t rb = (size_t)p.K * 2;
+  const char* A = static_cast<const char*>(p.A);
+  const char* B = static_cast<const char*>(p.W0);
+  const size_t n0 = (size_t)w.ta.nt * BN;
+  const bool empty = w.ksp.ks == 0;
+  s.rA = make_rsrc(A + (size_t)w.ta.row0 * rb, empty ? 0 : (size_t)w.ta.nvalid * rb);
+  s.rB0 = make_rsrc(B + n0 * rb, empty ? 0 : (size_t)(p.N - n0) * rb);
+  s.rB1 = s.rB0;
+  s.kbeg = w.ksp.kbeg;
+  s.KT = w.ksp.ksteps;
+  return s;
+}
+template <int NA, int NB>
+__global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_kernel(GemmParams p) {
+  constexpr int BM = 256, NW = kWaves;
+  MOE_GEMM_LDS_RING
+  const int mt_n = (p.M + BM - 1) / BM, nt_n = (p.N + BN - 1) / BN;
+  const int units = p.E * mt_n * nt_n;
+  int u = blockIdx.x;
+  if (u >= units) return;
+  const CopyPlan<BM, NW, false, false> cp(p.K);
+  Unit cur = wgrad_unit(p, u, mt_n, nt_n);
+  cp.template prologue<NA, NB>(wgrad_src(p, cur), L);
+  constexpr int RBLK = (2 * BM / NW) / 32;
+  const int wm = cp.wave >> 1;
+  for (;;) {
+    wait_vm<0>();
+    barrier_only();
+    const int un = u + (int)gridDim.x;
+    const bool more = un < units;
+    const Unit nxt = more ? wgrad_unit(p, un, mt_n, nt_n) : cur;
+    auto next = [&]() {
+      if (more) cp.template prologue<NA, NB>(wgrad_src(p, nxt), L);
+    };
+    const TileSrc src = wgrad_src(p, cur);
+    // C_e is row block e of a [E * M][N] matrix
+    Unit out = cur;
+    out.ta.row0 = cur.ta.e * p.M + cur.ta.row0;
+    out.ksp.ks = 1;
+    const int act = min(RBLK, max(0, (cur.ta.nvalid - wm * (RBLK * 32) + 31) / 32));
+    if (act >= RBLK)
+      gemm_tile<BM, NW, false, false, RBLK, NA, NB>(p, cp, src, L, out.ta, out.ksp, next);
+    else if (act == 1)
+      gemm_tile<BM, NW, false, false, 1, NA, NB>(p, cp, src, L, out.ta, out.ksp, next);
+    else
+      gemm_tile<BM, NW, false, false, 0, NA, NB>(p, cp, src, L, out.ta, out.ksp, next);
+    if (!more) break;
+    u = un;
+    cur = nxt;
+  }
+}
+
 // Sum of the K chunks of the tail tiles, in chunk order, then the same
 // epilogue as gemm_bf16_kernel.  Workgroup b handles tail tile b / 8 of XCD
 // b % 8 (if that XCD split its tail); thread i reads the partial groups that
@@ -778,6 +872,30 @@ hipError_t launch_gate_up_fp8(const FfnShape& fs, const void* X8, const float* x
   GemmParams p{X8, offset, map1, Wg8, Wu8, static_cast<bf16*>(A), x_scale, s_gate, s_up,
                E, h, f, f, fs.nt1, fs.mt1, part, fs.split_max, fs.grid1};
   launch_gemm_fp8(fs.bm1, p, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up_save(const FfnShape& fs, const void* X, const int32_t* offset,
+                               const int32_t* map1, const void* Wg, const void* Wu, void* A,
+                               void* GU, float* part, int E, int h, int f, hipStream_t s) {
+  if (fs.grid1 == 0) return hipSuccess;
+  GemmParams p{X, offset, map1, Wg, Wu, static_cast<bf16*>(A), nullptr, nullptr, nullptr,
+               E, h, f, f, fs.nt1, fs.mt1, part, fs.split_max, fs.grid1};
+  p.C2 = static_cast<bf16*>(GU);
+  launch_gemm<true>(fs.bm1, p, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad(const void* A, const void* B, const int32_t* kofs, void* C, int E, int M,
+                        int N, int Kp, int ncu, hipStream_t s) {
+  const int units = E * ((M + 255) / 256) * ((N + BN - 1) / BN);
+  if (units == 0) return hipSuccess;
+  GemmParams p{A, nullptr, nullptr, B, nullptr, static_cast<bf16*>(C), nullptr, nullptr, nullptr,
+               E, Kp, N, N, 0, 0, nullptr, 1, 0};
+  p.kofs = kofs;
+  p.M = M;
+  const int grid = std::min(units, ncu);
+  hipLaunchKernelGGL((gemm_wgrad_kernel<2, 3>), dim3(grid), dim3(64 * kWaves), 0, s, p);
   return hipGetLastError();
 }
 

@@ -214,3 +214,29 @@ def test_binding_rejects_bad_tensors_before_calling():
         B._ptr(U, "U", (64, 4096), torch.bfloat16)
     with pytest.raises(TypeError):
         B._ptr([1, 2], "U")
+
+
+def test_backward_argument_checks():
+    fake, other = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)
+    cfg = cfg_of()
+
+    def bwd(c, *, alpha=0.0, c_z=0.0, U=fake, dW_r=other, dU=other, ws_bytes=1 << 40):
+        return status("moe_layer_backward", ctypes.byref(c), U, fake, fake, fake, fake, fake,
+                      fake, fake, fake, fake, fake, fake, alpha, c_z, dU, dW_r, None, other,
+                      other, other, fake, ws_bytes, None)
+
+    # bf16 only, and neither noisy routing nor shared experts
+    assert bwd(B.make_config(I.WORKLOADS["tiny_f32"])) == B.MOE_ERR_UNSUPPORTED
+    assert bwd(cfg_of(noisy=True)) == B.MOE_ERR_UNSUPPORTED
+    assert bwd(cfg_of(n_shared=1, f_shared=64)) == B.MOE_ERR_UNSUPPORTED
+    # missing pointers and non-finite loss weights
+    assert bwd(cfg, U=None) == B.MOE_ERR_INVALID_ARG
+    assert bwd(cfg, dU=None) == B.MOE_ERR_INVALID_ARG
+    assert bwd(cfg, dW_r=None) == B.MOE_ERR_INVALID_ARG
+    for v in (float("nan"), float("inf")):
+        assert bwd(cfg, alpha=v) == B.MOE_ERR_INVALID_ARG
+        assert bwd(cfg, c_z=v) == B.MOE_ERR_INVALID_ARG
+    # the workspace has its own size
+    need = B.workspace_size(cfg, B.MOE_WS_BACKWARD)
+    assert need > B.workspace_size(cfg, B.MOE_WS_LAYER)
+    assert bwd(cfg, ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE
