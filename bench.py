@@ -2,10 +2,12 @@
 
 One step = one moe_layer_forward (router, dispatch, grouped SwiGLU experts,
 combine, statistics) over one batch of seeded synthetic tokens whose inputs
-are resident in HBM.  Prints one JSON line on stdout; progress goes to stderr.
+are resident in HBM; with --backward, one forward followed by one
+moe_layer_backward (a training step of the layer, upstream gradient seeded).
+Prints one JSON line on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--cpu-baseline-seconds S | --no-cpu-baseline]
+                    [--backward] [--cpu-baseline-seconds S | --no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -36,6 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_bf16")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--backward", action="store_true",
+                    help="time forward + backward (bf16, not noisy, no shared experts)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -221,7 +225,21 @@ def main():
     x = I.make_inputs(w, seed=args.seed, device=dev)
     cfg = B.make_config(w)
     ws = B.new_workspace(cfg, B.MOE_WS_LAYER, dev)
-    aux = B.alloc_aux(cfg, dev, ["kept", "n_dropped", "aux_loss", "maxvio", "z_loss"])
+    fields = ["kept", "n_dropped", "aux_loss", "maxvio", "z_loss"]
+    if args.backward:
+        if w.dtype != "bf16" or w.noisy or w.n_shared or w.fp8_up:
+            print("--backward needs a bf16 workload without noise, shared experts or FP8",
+                  file=sys.stderr)
+            sys.exit(2)
+        fields += ["logits", "topk_idx", "topk_gate", "slot", "count", "offset"]
+        bws = B.new_workspace(cfg, B.MOE_WS_BACKWARD, dev)
+        gen = torch.Generator(device=dev).manual_seed(args.seed + 1)
+        dOut = torch.randn((w.T, w.h), generator=gen, device=dev).to(torch.bfloat16)
+        grads = {"dU": torch.empty_like(x["U"]), "dW_r": torch.empty((w.h, w.E), device=dev),
+                 "db_r": torch.empty((w.E,), device=dev),
+                 "dW_gate": torch.empty_like(x["W_gate"]), "dW_up": torch.empty_like(x["W_up"]),
+                 "dW_down": torch.empty_like(x["W_down"])}
+    aux = B.alloc_aux(cfg, dev, fields)
     out = torch.empty((w.T, w.h), dtype=I.torch_dtype(w), device=dev)
     nst = B.MOE_NUM_STAGES
 
@@ -231,7 +249,7 @@ def main():
         W8u, su = B.moe_quantize_rows_fp8(x["W_up"])
 
     def step(events=None):
-        common = dict(aux=aux, stage_events=events, ws=ws, b_sel=x["b_sel"],
+        common = dict(aux=aux, stage_events=None if events is None else events[:nst + 1], ws=ws, b_sel=x["b_sel"],
                       Ws_gate=x["Ws_gate"], Ws_up=x["Ws_up"], Ws_down=x["Ws_down"])
         if w.fp8_up:
             B.moe_layer_forward_fp8(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], x["noise"],
@@ -239,11 +257,20 @@ def main():
         else:
             B.moe_layer_forward(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], x["noise"],
                                 x["W_gate"], x["W_up"], x["W_down"], out, **common)
+        if args.backward:
+            B.moe_layer_backward(cfg, x["U"], x["W_r"], x["W_gate"], x["W_up"], x["W_down"],
+                                 aux["logits"], aux["topk_idx"], aux["topk_gate"], aux["slot"],
+                                 aux["count"], aux["offset"], dOut, grads["dU"], grads["dW_r"],
+                                 grads["dW_gate"], grads["dW_up"], grads["dW_down"],
+                                 db_r=grads["db_r"], alpha=0.01, c_z=1e-3, ws=bws)
+            if events is not None:
+                events[-1].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
+    n_ev = nst + 1 + (1 if args.backward else 0)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
               for _ in range(args.steps)]
     for evs in events:  # create the HIP events outside the timed region
         for e in evs:
@@ -261,6 +288,8 @@ def main():
         for j, n in enumerate(B.STAGE_NAMES):
             stage_ms[n] += evs[j].elapsed_time(evs[j + 1]) / args.steps
     ms = elapsed * 1e3 / args.steps
+    bwd_ms = (sum(evs[nst].elapsed_time(evs[nst + 1]) for evs in events) / args.steps
+              if args.backward else None)
     tokens_per_s = w.T * args.steps / elapsed
 
     kept = int(aux["kept"].sum().item())
@@ -287,7 +316,8 @@ def main():
                      + w.h * w.E * (2 if w.noisy else 1)))
 
     res = {
-        "metric": "MoE layer fwd tokens/sec on 1 MI355X",
+        "metric": ("MoE layer fwd+bwd tokens/sec on 1 MI355X" if args.backward
+                   else "MoE layer fwd tokens/sec on 1 MI355X"),
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -322,7 +352,15 @@ def main():
         "stage_ms": stage_ms,
         "stage_gbs": stage_bandwidth(w, stage_ms, kept, e_active, eb),
     }
-    if not args.no_cpu_baseline:
+    if args.backward:
+        # the backward's products: dgrad 6 h f and wgrad 6 h f per kept row
+        # (useful), plus 6 h f of recomputed forward (executed)
+        res["backward"] = {"ms": bwd_ms, "forward_ms": ms - bwd_ms,
+                           "mfma_frac_useful": 12.0 * w.h * w.f * kept / (bwd_ms * 1e-3) / 1e12
+                           / PEAK_BF16_TFLOPS,
+                           "mfma_frac_exec": 18.0 * w.h * w.f * kept / (bwd_ms * 1e-3) / 1e12
+                           / PEAK_BF16_TFLOPS}
+    if not args.no_cpu_baseline and not args.backward:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(w, x, aux, args.cpu_baseline_seconds)
     print(json.dumps(res), flush=True)

@@ -239,7 +239,7 @@ struct BackwardWs {
   FfnWs ffn;  // tile maps, A (the SwiGLU rows), K-split partials
   FfnShape fsA, fsX;  // shapes of the dA (N = f, K = h) and dX (N = h, K = 2f) products
   int Kp;
-  size_t X, GU, Y, dY, dA, dGU, dX, WdT, WguT, dYT, AT, dGUT, XT, kofs, dgate, dH, part;
+  size_t X, GU, Y, dY, dA, dGU, dX, dYT, AT, dGUT, XT, kofs, dgate, dH, part, dwr;
 };
 BackwardWs plan_backward(const Dims& d, Plan& pl) {
   BackwardWs w;
@@ -258,8 +258,6 @@ BackwardWs plan_backward(const Dims& d, Plan& pl) {
   w.dA = pl.add(rows * d.f * 2);
   w.dGU = pl.add(rows * 2 * d.f * 2);
   w.dX = pl.add(rows * d.h * 2);
-  w.WdT = pl.add((size_t)d.E * d.f * d.h * 2);
-  w.WguT = pl.add((size_t)d.E * d.h * 2 * d.f * 2);
   w.dYT = pl.add((size_t)d.h * kp * 2);
   w.AT = pl.add((size_t)d.f * kp * 2);
   w.dGUT = pl.add((size_t)2 * d.f * kp * 2);
@@ -270,6 +268,7 @@ BackwardWs plan_backward(const Dims& d, Plan& pl) {
   // K-split partials for the largest grid of the three row-grouped products
   const int slots = std::max(w.ffn.fs.part_slots, std::max(w.fsA.part_slots, w.fsX.part_slots));
   w.part = pl.add((size_t)slots * kPartSlotBytes);
+  w.dwr = pl.add(dwr_part_bytes(d.T, (int)d.h, (int)d.E));
   return w;
 }
 
@@ -772,17 +771,11 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
                       f, 1, s));
   // 2. combine: dY rows and the gates' gradient
   MOE_TRY(launch_combine_bwd(dOut, Y, slot, topk_gate, dY, dgate, T, h, k, s));
-  // 3. dA = dY W_down (B = W_down^T, [E][f][h]); SwiGLU backward; dX = [dg du] [W_gate; W_up]
-  MOE_TRY(launch_transpose_batched(W_down, h, f, (size_t)h * f, at<void>(ws, w.WdT), h, 0,
-                                   (size_t)f * h, E, s));
-  MOE_TRY(launch_down(w.fsA, dY, offset, map, at<void>(ws, w.WdT), dA, part, E, f, h, 1, s));
+  // 3. dA = dY W_down[e]; SwiGLU backward; dX = [dg du] [W_gate[e]; W_up[e]]: products
+  // with the weights read as stored, [K][N]
+  MOE_TRY(launch_dgrad(w.fsA, dY, offset, map, W_down, W_down, h, dA, part, E, f, h, s));
   MOE_TRY(launch_swiglu_bwd(dA, GU, offset, E, d.rows_max, f, dGU, s));
-  MOE_TRY(launch_transpose_batched(W_gate, f, h, (size_t)f * h, at<void>(ws, w.WguT), 2 * f, 0,
-                                   (size_t)h * 2 * f, E, s));
-  MOE_TRY(launch_transpose_batched(W_up, f, h, (size_t)f * h, at<void>(ws, w.WguT), 2 * f, f,
-                                   (size_t)h * 2 * f, E, s));
-  MOE_TRY(launch_down(w.fsX, dGU, offset, map, at<void>(ws, w.WguT), dX, part, E, h, 2 * f, 1,
-                      s));
+  MOE_TRY(launch_dgrad(w.fsX, dGU, offset, map, W_gate, W_up, f, dX, part, E, h, 2 * f, s));
   // 4. weight gradients: sums over each expert's rows of outer products
   MOE_TRY(launch_kofs(offset, E, kofs, s));
   MOE_TRY(launch_transpose_pad(dY, offset, kofs, E, h, at<void>(ws, w.dYT), w.Kp, s));
@@ -799,7 +792,7 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
   MOE_TRY(launch_router_bwd(logits, topk_idx, topk_gate, dgate, count, T, E, k, cfg->score,
                             cfg->gate == MOE_GATE_RENORM, alpha, c_z, dH, s));
   MOE_TRY(launch_grad_input(dOut, dX, slot, dH, W_r, dU, T, h, E, k, s));
-  MOE_TRY(launch_dwr(U, dH, dW_r, db_r, T, h, E, s));
+  MOE_TRY(launch_dwr(U, dH, dW_r, db_r, at<float>(ws, w.dwr), T, h, E, s));
   return MOE_OK;
 }
 

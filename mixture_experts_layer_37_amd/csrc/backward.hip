@@ -18,6 +18,8 @@
 // products are the GEMM kernels of ffn.hip.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -84,29 +86,6 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const bf16* dA, const b
   }
   st16(dGU + row * 2 * f + c, Elem<bf16>::pack(dg));
   st16(dGU + row * 2 * f + f + c, Elem<bf16>::pack(du));
-}
-
-// Batched transpose through LDS: for each of `batches` matrices,
-// dst[c][c0 + r] = src[r][c] (src [R][C] with batch stride sb, dst rows of
-// ld elements with batch stride db).  64 x 64 tiles, 256 threads.
-__global__ __launch_bounds__(256) void transpose_batched_kernel(const bf16* src, int R, int C,
-                                                                size_t sb, bf16* dst, int ld,
-                                                                int c0, size_t db) {
-  __shared__ bf16 tile[64][66];
-  const int b = blockIdx.z;
-  const int r0 = blockIdx.y * 64, cc0 = blockIdx.x * 64;
-  const bf16* s = src + b * sb;
-  bf16* d = dst + b * db;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int r = r0 + i, c = cc0 + tx;
-    tile[i][tx] = (r < R && c < C) ? s[(size_t)r * C + c] : bf16(0);
-  }
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = cc0 + i, r = r0 + tx;
-    if (c < C && r < R) d[(size_t)c * ld + c0 + r] = tile[tx][i];
-  }
 }
 
 // Per-expert offsets of the zero-padded K layout of the weight gradients:
@@ -247,105 +226,156 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* logits, co
   }
 }
 
-// dU = dOut + sum over kept ranks of dX[slot] + dH W_r^T, for 16 tokens per
-// workgroup: their dH rows sit in LDS and each W_r row is read once per
-// workgroup.  Thread j handles columns j, j + 256, ...
-constexpr int kGiTok = 16;
+// dU = dOut + sum over kept ranks of dX[slot] + dH W_r^T.  A workgroup
+// takes 64 tokens x 128 columns j (a thread 4 tokens x 8 consecutive columns,
+// so dOut, dX and dU move 16 bytes at a time); the product over the experts
+// runs in chunks of 32 with dH^T and W_r^T staged in LDS as float32.
+constexpr int kGiT = 64, kGiJ = 128, kGiK = 32;
+
 __global__ __launch_bounds__(256) void grad_input_kernel(const bf16* dOut, const bf16* dX,
                                                          const int32_t* slot, const float* dH,
                                                          const bf16* W_r, bf16* dU, int T, int h,
                                                          int E, int k) {
-  __shared__ float sdh[kGiTok][256];
-  __shared__ int ssl[kGiTok][8];
-  const int t0 = blockIdx.x * kGiTok;
-  for (int i = threadIdx.x; i < kGiTok * 256; i += 256) {
-    const int tt = i / 256, e = i % 256, t = t0 + tt;
-    sdh[tt][e] = (t < T && e < E) ? dH[(size_t)t * E + e] : 0.f;
+  __shared__ __align__(16) float sh[kGiK][kGiT];  // sh[e][t] = dH[t0 + t][e0 + e]
+  __shared__ __align__(16) float sw[kGiK][kGiJ];  // sw[e][j] = W_r[j0 + j][e0 + e]
+  const int t0 = blockIdx.x * kGiT, j0 = blockIdx.y * kGiJ;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[i][q] = 0.f;
+  for (int e0 = 0; e0 < E; e0 += kGiK) {
+    const int kc = min(kGiK, E - e0);
+    for (int i = threadIdx.x; i < kGiT * kGiK; i += 256) {
+      const int tt = i / kGiK, ee = i % kGiK, t = t0 + tt, e = e0 + ee;
+      sh[ee][tt] = (t < T && ee < kc) ? dH[(size_t)t * E + e] : 0.f;
+    }
+    for (int i = threadIdx.x; i < kGiJ * kGiK; i += 256) {
+      const int jj = i / kGiK, ee = i % kGiK, j = j0 + jj;
+      sw[ee][jj] = (j < h && ee < kc) ? bf16_to_f32(W_r[(size_t)j * E + e0 + ee]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int ee = 0; ee < kc; ++ee) {
+      const float4 a = *reinterpret_cast<const float4*>(&sh[ee][ty * 4]);
+      const float4 b0 = *reinterpret_cast<const float4*>(&sw[ee][tx * 8]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&sw[ee][tx * 8 + 4]);
+      const float av[4] = {a.x, a.y, a.z, a.w};
+      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[i][q] = fmaf(av[i], bv[q], acc[i][q]);
+    }
+    __syncthreads();
   }
-  if (threadIdx.x < kGiTok * 8) {
-    const int tt = threadIdx.x / 8, r = threadIdx.x % 8, t = t0 + tt;
-    ssl[tt][r] = (t < T && r < k) ? slot[(size_t)t * k + r] : -1;
+  const int j = j0 + tx * 8;
+  if (j >= h) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + ty * 4 + i;
+    if (t >= T) break;
+    float v[8], x[8];
+    Elem<bf16>::unpack(ld16(dOut + (size_t)t * h + j), v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] += acc[i][q];
+    for (int r = 0; r < k; ++r) {
+      const int row = slot[(size_t)t * k + r];
+      if (row < 0) continue;
+      Elem<bf16>::unpack(ld16(dX + (size_t)row * h + j), x);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] += x[q];
+    }
+    st16(dU + (size_t)t * h + j, Elem<bf16>::pack(v));
   }
-  __syncthreads();
-  for (int j = threadIdx.x; j < h; j += 256) {
-    float acc[kGiTok];
+}
+
+// dW_r[j][e] = sum_t U[t][j] dH[t][e] and db_r[e] = sum_t dH[t][e] in
+// float32, computed as one product in which U has an extra column of ones
+// (j = h).  Workgroup (jt, et, s) takes TJ x TE outputs over the tokens of
+// split s, stages 16 tokens of U and dH at a time in LDS as float32, and a
+// thread accumulates 4 x 4 outputs; the splits' partials part[s][j][e] are
+// summed in split order by dwr_reduce_kernel (deterministic).
+template <int TE>
+__global__ __launch_bounds__(256) void dwr_part_kernel(const bf16* U, const float* dH,
+                                                       float* part, int T, int h, int E,
+                                                       int tchunk) {
+  constexpr int NE = TE / 4, NJ = 256 / NE, TJ = 4 * NJ, KC = 16;
+  __shared__ __align__(16) float su[KC][TJ];
+  __shared__ __align__(16) float sd[KC][TE];
+  const int j0 = blockIdx.x * TJ, e0 = blockIdx.y * TE;
+  const int tb = blockIdx.z * tchunk, tend = min(T, tb + tchunk);
+  const int tx = threadIdx.x % NE, ty = threadIdx.x / NE;
+  float acc[4][4];
 #pragma unroll
-    for (int tt = 0; tt < kGiTok; ++tt) acc[tt] = 0.f;
-    const bf16* w = W_r + (size_t)j * E;
-    int e = 0;
-    if ((E & 7) == 0) {  // rows are 16-byte aligned: 8 weights per load
-      for (; e < E; e += 8) {
-        float we[8];
-        Elem<bf16>::unpack(ld16(w + e), we);
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < 4; ++q) acc[i][q] = 0.f;
+  const bool vec_e = (E & 3) == 0;
+  for (int t0 = tb; t0 < tend; t0 += KC) {
+    for (int i = threadIdx.x; i < KC * (TJ / 8); i += 256) {
+      const int tt = i / (TJ / 8), jj = (i % (TJ / 8)) * 8, t = t0 + tt, j = j0 + jj;
+      float v[8];
+      if (t < tend && j < h) {  // h is a multiple of 8
+        Elem<bf16>::unpack(ld16(U + (size_t)t * h + j), v);
+      } else {
 #pragma unroll
-          for (int tt = 0; tt < kGiTok; ++tt) acc[tt] = fmaf(sdh[tt][e + q], we[q], acc[tt]);
+        for (int q = 0; q < 8; ++q) v[q] = (t < tend && j + q == h) ? 1.f : 0.f;
       }
+      *reinterpret_cast<float4*>(&su[tt][jj]) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(&su[tt][jj + 4]) = make_float4(v[4], v[5], v[6], v[7]);
     }
-    for (; e < E; ++e) {
-      const float we = bf16_to_f32(w[e]);
-#pragma unroll
-      for (int tt = 0; tt < kGiTok; ++tt) acc[tt] = fmaf(sdh[tt][e], we, acc[tt]);
+    for (int i = threadIdx.x; i < KC * NE; i += 256) {
+      const int tt = i / NE, ee = (i % NE) * 4, t = t0 + tt, e = e0 + ee;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < tend) {
+        const float* src = dH + (size_t)t * E + e;
+        if (vec_e && e + 4 <= E) {
+          v = *reinterpret_cast<const float4*>(src);
+        } else {
+          v.x = e < E ? src[0] : 0.f;
+          v.y = e + 1 < E ? src[1] : 0.f;
+          v.z = e + 2 < E ? src[2] : 0.f;
+          v.w = e + 3 < E ? src[3] : 0.f;
+        }
+      }
+      *reinterpret_cast<float4*>(&sd[tt][ee]) = v;
     }
+    __syncthreads();
 #pragma unroll
-    for (int tt = 0; tt < kGiTok; ++tt) {
-      const int t = t0 + tt;
-      if (t >= T) break;
-      float v = bf16_to_f32(dOut[(size_t)t * h + j]) + acc[tt];
-      for (int r = 0; r < k; ++r)
-        if (ssl[tt][r] >= 0) v += bf16_to_f32(dX[(size_t)ssl[tt][r] * h + j]);
-      dU[(size_t)t * h + j] = f32_to_bf16(v);
+    for (int tt = 0; tt < KC; ++tt) {
+      const float4 a = *reinterpret_cast<const float4*>(&su[tt][ty * 4]);
+      const float4 b = *reinterpret_cast<const float4*>(&sd[tt][tx * 4]);
+      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q] = fmaf(av[i], bv[q], acc[i][q]);
+    }
+    __syncthreads();
+  }
+  float* P = part + (size_t)blockIdx.z * (size_t)(h + 1) * E;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = j0 + ty * 4 + i;
+    if (j > h) break;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = e0 + tx * 4 + q;
+      if (e < E) P[(size_t)j * E + e] = acc[i][q];
     }
   }
 }
 
-// dW_r[j][e] = sum_t U[t][j] dH[t][e] (float32): workgroup b takes 64 rows j
-// and every e, and walks the tokens in chunks of 32 staged in LDS.  db_r[e] =
-// sum_t dH[t][e] comes from workgroup 0 (tokens in order).
-__global__ __launch_bounds__(256) void dwr_kernel(const bf16* U, const float* dH, float* dWr,
-                                                  float* db, int T, int h, int E) {
-  __shared__ float su[32][64];
-  __shared__ float sd[32][256];
-  const int j0 = blockIdx.x * 64;
-  const int nout = 64 * E;  // outputs of this workgroup, id = jj * E + e
-  float acc[64];            // at most 64 * 256 / 256 per thread
-  const int per = (nout + 255) / 256;
-#pragma unroll
-  for (int q = 0; q < 64; ++q) acc[q] = 0.f;
-  for (int tb = 0; tb < T; tb += 32) {
-    for (int i = threadIdx.x; i < 32 * 64; i += 256) {
-      const int tt = i / 64, jj = i % 64, t = tb + tt, j = j0 + jj;
-      su[tt][jj] = (t < T && j < h) ? bf16_to_f32(U[(size_t)t * h + j]) : 0.f;
-    }
-    for (int i = threadIdx.x; i < 32 * 256; i += 256) {
-      const int tt = i / 256, e = i % 256, t = tb + tt;
-      sd[tt][e] = (t < T && e < E) ? dH[(size_t)t * E + e] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 64; ++q) {  // unrolled: acc stays in registers
-      const int o = threadIdx.x + 256 * q;
-      if (q >= per || o >= nout) break;
-      const int jj = o / E, e = o % E;
-      float a = acc[q];
-#pragma unroll 8
-      for (int tt = 0; tt < 32; ++tt) a = fmaf(su[tt][jj], sd[tt][e], a);
-      acc[q] = a;
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int q = 0; q < 64; ++q) {
-    const int o = threadIdx.x + 256 * q;
-    if (q >= per || o >= nout) break;
-    const int jj = o / E, e = o % E, j = j0 + jj;
-    if (j < h) dWr[(size_t)j * E + e] = acc[q];
-  }
-  if (db && blockIdx.x == 0 && threadIdx.x < E) {
+__global__ __launch_bounds__(256) void dwr_reduce_kernel(const float* part, int nsplit, int h,
+                                                         int E, float* dWr, float* db) {
+  const size_t n = (size_t)(h + 1) * E;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
     float s = 0.f;
-    for (int t = 0; t < T; ++t) s += dH[(size_t)t * E + threadIdx.x];
-    db[threadIdx.x] = s;
+    for (int sp = 0; sp < nsplit; ++sp) s += part[(size_t)sp * n + i];
+    if (i < (size_t)h * E) dWr[i] = s;
+    else if (db) db[i - (size_t)h * E] = s;
   }
 }
 
@@ -368,15 +398,6 @@ hipError_t launch_swiglu_bwd(const void* dA, const void* GU, const int32_t* offs
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      static_cast<const bf16*>(dA), static_cast<const bf16*>(GU), offset, E, f,
                      static_cast<bf16*>(dGU));
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_batched(const void* src, int R, int C, size_t sb, void* dst, int ld,
-                                    int c0, size_t db, int batches, hipStream_t s) {
-  if (batches == 0 || R == 0 || C == 0) return hipSuccess;
-  dim3 grid((C + 63) / 64, (R + 63) / 64, batches);
-  hipLaunchKernelGGL(transpose_batched_kernel, grid, dim3(256), 0, s,
-                     static_cast<const bf16*>(src), R, C, sb, static_cast<bf16*>(dst), ld, c0, db);
   return hipGetLastError();
 }
 
@@ -408,16 +429,41 @@ hipError_t launch_grad_input(const void* dOut, const void* dX, const int32_t* sl
                              const float* dH, const void* W_r, void* dU, int T, int h, int E,
                              int k, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(grad_input_kernel, dim3((T + kGiTok - 1) / kGiTok), dim3(256), 0, s,
-                     static_cast<const bf16*>(dOut), static_cast<const bf16*>(dX), slot, dH,
-                     static_cast<const bf16*>(W_r), static_cast<bf16*>(dU), T, h, E, k);
+  hipLaunchKernelGGL(grad_input_kernel, dim3((T + kGiT - 1) / kGiT, (h + kGiJ - 1) / kGiJ),
+                     dim3(256), 0, s, static_cast<const bf16*>(dOut),
+                     static_cast<const bf16*>(dX), slot, dH, static_cast<const bf16*>(W_r),
+                     static_cast<bf16*>(dU), T, h, E, k);
   return hipGetLastError();
 }
 
-hipError_t launch_dwr(const void* U, const float* dH, float* dWr, float* db, int T, int h, int E,
-                      hipStream_t s) {
-  hipLaunchKernelGGL(dwr_kernel, dim3((h + 63) / 64), dim3(256), 0, s,
-                     static_cast<const bf16*>(U), dH, dWr, db, T, h, E);
+hipError_t launch_dwr(const void* U, const float* dH, float* dWr, float* db, float* part, int T,
+                      int h, int E, hipStream_t s) {
+  const DwrPlan p = dwr_plan(T, h, E);
+  const dim3 grid(p.jt, p.et, p.nsplit);
+  const bf16* u = static_cast<const bf16*>(U);
+  switch (p.te) {
+    case 8:
+      hipLaunchKernelGGL(dwr_part_kernel<8>, grid, dim3(256), 0, s, u, dH, part, T, h, E,
+                         p.tchunk);
+      break;
+    case 16:
+      hipLaunchKernelGGL(dwr_part_kernel<16>, grid, dim3(256), 0, s, u, dH, part, T, h, E,
+                         p.tchunk);
+      break;
+    case 32:
+      hipLaunchKernelGGL(dwr_part_kernel<32>, grid, dim3(256), 0, s, u, dH, part, T, h, E,
+                         p.tchunk);
+      break;
+    default:
+      hipLaunchKernelGGL(dwr_part_kernel<64>, grid, dim3(256), 0, s, u, dH, part, T, h, E,
+                         p.tchunk);
+      break;
+  }
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const size_t n = (size_t)(h + 1) * E;
+  const unsigned nb = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(dwr_reduce_kernel, dim3(nb), dim3(256), 0, s, part, p.nsplit, h, E, dWr, db);
   return hipGetLastError();
 }
 

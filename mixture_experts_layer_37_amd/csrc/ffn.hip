@@ -98,6 +98,9 @@ struct GemmParams {
   // K_e = kofs[e] .. kofs[e+1]-1 (multiples of 64, zero-padded)
   const int32_t* kofs = nullptr;
   int M = 0;
+  // BT kernels (weights stored [K][N]): W0 holds K rows 0..K0-1 of each
+  // expert's [K][N] operand and W1 the rest ([E][K0][N] and [E][K-K0][N])
+  int K0 = 0;
 };
 
 // A K chunk of a tail tile (see gemm_bf16_kernel); ks == 1: a whole tile.
@@ -260,11 +263,26 @@ struct Ring {
 struct TileSrc {
   __amdgpu_buffer_rsrc_t rA, rB0, rB1;
   int kbeg, KT;
+  int kt0;  // BT: K steps taken from W0 (the later ones come from W1)
 };
-template <bool GATEUP, bool F8>
+template <bool GATEUP, bool F8, bool BT = false>
 __device__ __forceinline__ TileSrc tile_src(const GemmParams& p, const TileAt& ta,
                                             const KSplit& ksp) {
   TileSrc s;
+  if constexpr (BT) {  // weights [K][N]: the panel is columns n0.. of K rows
+    const size_t pitch = (size_t)p.N * 2, nb = (size_t)ta.nt * BN * 2;
+    const char* A = static_cast<const char*>(p.A);
+    s.rA = make_rsrc(A + (size_t)ta.row0 * p.K * 2, (size_t)ta.nvalid * p.K * 2);
+    const char* W0 = static_cast<const char*>(p.W0);
+    const char* W1 = static_cast<const char*>(p.W1);
+    const size_t b0 = (size_t)p.K0 * pitch, b1 = (size_t)(p.K - p.K0) * pitch;
+    s.rB0 = make_rsrc(W0 + (size_t)ta.e * b0 + nb, b0 - nb);
+    s.rB1 = p.K > p.K0 ? make_rsrc(W1 + (size_t)ta.e * b1 + nb, b1 - nb) : s.rB0;
+    s.kbeg = ksp.kbeg;
+    s.KT = ksp.ksteps;
+    s.kt0 = p.K0 / BK;
+    return s;
+  }
   const size_t rb = (size_t)p.K * Elt<F8>::kBytes;  // bytes per row
   const char* A = static_cast<const char*>(p.A);
   s.rA = make_rsrc(A + (size_t)ta.row0 * rb, (size_t)ta.nvalid * rb);
@@ -282,13 +300,23 @@ __device__ __forceinline__ TileSrc tile_src(const GemmParams& p, const TileAt& t
 // This wave's share of the copies of one K step.  Lane i of 8-row group g
 // fills LDS row 8g + i/8, physical chunk i%8, with logical chunk
 // (i%8) ^ ((row >> 1) & 7).  The per-lane offsets depend on K only.
-template <int BM, int NW, bool GATEUP, bool F8>
+//
+// BT: the weight operand is stored [K][N] (N contiguous).  Its K step is then
+// 64 rows of the tile's 256 columns, 512 bytes each, kept in that layout:
+// copy instruction q of a wave fills k-rows 2 (wave + NW q) and the next,
+// lane i physical chunk i % 32 of row 2 (wave + NW q) + i / 32 with logical
+// chunk (i % 32) ^ trswz(row); fragments are read with the transposing LDS
+// load (see gemm_tile).
+__device__ __forceinline__ constexpr int trswz(int kr) { return (kr & 3) << 2; }
+
+template <int BM, int NW, bool GATEUP, bool F8, bool BT = false>
 struct CopyPlan {
   static constexpr int AG = BM / (8 * NW);  // 8-row A groups copied per wave per step
   static constexpr int BG = BN / (8 * NW);  // 8-row B groups copied per wave per step
   int wave;
   int voA[AG], voB[BG];
-  __device__ __forceinline__ explicit CopyPlan(int K) {
+  int bstep;  // BT: bytes of one K step of the weight panel (64 rows)
+  __device__ __forceinline__ explicit CopyPlan(int K, int N = 0) {
     // the wave index is uniform: keep it (and all copy addressing) in SGPRs
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, lrow = lane >> 3;
@@ -299,12 +327,18 @@ struct CopyPlan {
     }
 #pragma unroll
     for (int j = 0; j < BG; ++j) {
-      // gate/up: groups 0..15 are W_gate rows, 16..31 (j >= BG/2) the W_up rows
-      const int g = wave + NW * j;
-      const int r = 8 * g + lrow;                       // LDS row
-      const int pr = GATEUP ? 8 * (g & 15) + lrow : r;  // row in the weight panel
-      voB[j] = pr * K * Elt<F8>::kBytes + (((lane & 7) ^ ((r >> 1) & 7)) * 16);
+      if constexpr (BT) {
+        const int kr = 2 * (wave + NW * j) + (lane >> 5);
+        voB[j] = kr * N * 2 + (((lane & 31) ^ trswz(kr)) * 16);
+      } else {
+        // gate/up: groups 0..15 are W_gate rows, 16..31 (j >= BG/2) the W_up rows
+        const int g = wave + NW * j;
+        const int r = 8 * g + lrow;                       // LDS row
+        const int pr = GATEUP ? 8 * (g & 15) + lrow : r;  // row in the weight panel
+        voB[j] = pr * K * Elt<F8>::kBytes + (((lane & 7) ^ ((r >> 1) & 7)) * 16);
+      }
     }
+    bstep = BK * N * 2;
   }
   // step j past the end reloads the last step (in bounds, never read), so
   // every step issues the same number of copies
@@ -314,6 +348,15 @@ struct CopyPlan {
     for (int q = 0; q < AG; ++q) dma16(s.rA, as + (wave + NW * q) * 8 * BK, voA[q], kb);
   }
   __device__ __forceinline__ void issueB(const TileSrc& s, bf16* bs, int j) const {
+    if constexpr (BT) {
+      const int st = s.kbeg + min(j, s.KT - 1);
+      const bool second = st >= s.kt0;
+      const int kb = (second ? st - s.kt0 : st) * bstep;
+#pragma unroll
+      for (int q = 0; q < BG; ++q)
+        dma16(second ? s.rB1 : s.rB0, bs + (wave + NW * q) * 8 * BK, voB[q], kb);
+      return;
+    }
     const int kb = (s.kbeg + min(j, s.KT - 1)) * 128;
 #pragma unroll
     for (int q = 0; q < BG; ++q)
@@ -335,15 +378,15 @@ struct CopyPlan {
 // RBLK); a wave with R < RBLK skips the fragment reads and MFMAs of the others
 // (their accumulators stay zero and their rows are never stored) but issues
 // the same copies and meets the same barriers as the rest of the workgroup.
-template <int BM, int NW, bool GATEUP, bool F8, int R, int NA, int NB, class Next>
-__device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM, NW, GATEUP, F8>& cp,
+template <int BM, int NW, bool GATEUP, bool F8, int R, int NA, int NB, bool BT, class Next>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM, NW, GATEUP, F8, BT>& cp,
                                           const TileSrc& src, const Ring& L, const TileAt& ta,
                                           const KSplit& ksp, Next&& next) {
   constexpr int WM = NW / 2;         // waves along M (2 along N)
   constexpr int WR = BM / WM;        // rows per wave
   constexpr int RBLK = WR / 32;      // 32-row MFMA blocks per wave
-  constexpr int AG = CopyPlan<BM, NW, GATEUP, F8>::AG;
-  constexpr int BG = CopyPlan<BM, NW, GATEUP, F8>::BG;
+  constexpr int AG = CopyPlan<BM, NW, GATEUP, F8, BT>::AG;
+  constexpr int BG = CopyPlan<BM, NW, GATEUP, F8, BT>::BG;
   constexpr int NSL = Elt<F8>::kSlices;  // MFMA K slices per step
   constexpr int FC = F8 ? 2 : 1;         // 16-byte chunks per fragment and lane
   using Frag = typename Elt<F8>::Frag;
@@ -366,9 +409,22 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM
   for (int i = 0; i < RBLK; ++i) aoff[i] = (wm * WR + i * 32 + l32) * 128;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int r = GATEUP ? ((j < 2 ? 0 : 128) + wn * 64 + (j & 1) * 32 + l32)
-                         : (wn * 128 + j * 32 + l32);
-    boff[j] = r * 128;
+    if constexpr (BT) {
+      // transposing read: within each 16-lane group, lane i gets element i % 4
+      // of the 8 bytes that lanes 4 q + i / 4 (q = 0..3) address.  Lane
+      // 4 q + m of a group addresses k-row q (+ 4 for the second half) of the
+      // slice's 8 and columns 4 (m % 4) .. +3 of its 16, so lane i receives
+      // column i of the group's 16 at 4 consecutive k: the fragment of column
+      // l32 at k = 16 slice + 8 khalf + 0..7, like the A fragment.
+      const int l16 = lane & 15, qk = l16 >> 2;
+      const int kr = 8 * khalf + qk;  // + 16 slice + 4 half, multiples of 4
+      const int c = (wn * 128 + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (l16 & 3)) >> 3;
+      boff[j] = kr * (BN * 2) + ((c ^ trswz(kr)) * 16) + 8 * (l16 & 1);
+    } else {
+      const int r = GATEUP ? ((j < 2 ? 0 : 128) + wn * 64 + (j & 1) * 32 + l32)
+                           : (wn * 128 + j * 32 + l32);
+      boff[j] = r * 128;
+    }
   }
   static_assert(R >= 0 && R <= RBLK, "active blocks");
 
@@ -393,12 +449,27 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM
       return *reinterpret_cast<const Frag*>(row + ((c0 ^ sw) * 16));
     }
   };
+  // BT fragment: two transposing 8-byte reads, k-rows 16 slice + (0..3, 4..7)
+  auto fragT = [&](const bf16* slot, int off, int slice) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const char* q = reinterpret_cast<const char*>(slot) + off + slice * (16 * BN * 2);
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(q));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(q + 4 * BN * 2));
+    const v4s v[2] = {lo, hi};
+    bf16x8 r;
+    __builtin_memcpy(&r, v, 16);
+    return r;
+  };
   auto fetch = [&](const bf16* as, const bf16* bs, int slice, int st) {
     const int c0 = FC * (2 * slice + khalf);
 #pragma unroll
     for (int i = 0; i < R; ++i) fa[st][i] = frag(as, aoff[i], c0);
 #pragma unroll
-    for (int j = 0; j < (R > 0 ? 4 : 0); ++j) fb[st][j] = frag(bs, boff[j], c0);
+    for (int j = 0; j < (R > 0 ? 4 : 0); ++j) {
+      if constexpr (BT) fb[st][j] = fragT(bs, boff[j], slice);
+      else fb[st][j] = frag(bs, boff[j], c0);
+    }
   };
   auto mfmas = [&](int st) {
 #pragma unroll
@@ -417,7 +488,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM
   // order for the scheduler: MFMAs interleaved with the next fragment reads
   // and, after the barrier, with the copies (groups: 0x008 MFMA, 0x100 LDS
   // read, 0x020 global read incl. LDS copies)
-  constexpr int NM = R * 4, NR = R > 0 ? (R + 4) * FC : 0, NC = AG + BG;
+  constexpr int NM = R * 4, NR = R > 0 ? R * FC + 4 * (BT ? 2 : FC) : 0, NC = AG + BG;
   constexpr int CPM = NM > 0 ? (NC + NM - 1) / NM : NC;  // copies placed after each MFMA
   constexpr int RPM = NM > 0 ? (NR + NM - 1) / NM : NR;  // LDS reads placed after each MFMA
   auto order = [&]() {
@@ -533,7 +604,7 @@ __device__ __forceinline__ Unit unit_at(const GemmParams& p, const XcdShare& xs,
 // the same share of real tiles, and the workgroups running together on one
 // XCD hold neighbouring tiles, which share A row panels and weight panels in
 // that XCD's L2.
-template <int BM, int NW, bool GATEUP, bool F8, int NA, int NB>
+template <int BM, int NW, bool GATEUP, bool F8, int NA, int NB, bool BT = false>
 __device__ __forceinline__ void grouped_gemm(const GemmParams& p, const Ring& L) {
   const int mtiles = p.tmap[p.E];
   const int KT = p.K / Elt<F8>::kStep;
@@ -542,9 +613,9 @@ __device__ __forceinline__ void grouped_gemm(const GemmParams& p, const Ring& L)
   const int units = xs.full + xs.rem * xs.ks;
   int u = blockIdx.x >> 3;
   if (u >= units) return;
-  const CopyPlan<BM, NW, GATEUP, F8> cp(p.K);
+  const CopyPlan<BM, NW, GATEUP, F8, BT> cp(p.K, p.N);
   Unit cur = unit_at<BM>(p, xs, xcd, u, KT, mtiles);
-  cp.template prologue<NA, NB>(tile_src<GATEUP, F8>(p, cur.ta, cur.ksp), L);
+  cp.template prologue<NA, NB>(tile_src<GATEUP, F8, BT>(p, cur.ta, cur.ksp), L);
   constexpr int RBLK = (2 * BM / NW) / 32;
   const int wm = cp.wave >> 1;
   for (;;) {
@@ -554,19 +625,19 @@ __device__ __forceinline__ void grouped_gemm(const GemmParams& p, const Ring& L)
     const bool more = un < units;
     const Unit nxt = more ? unit_at<BM>(p, xs, xcd, un, KT, mtiles) : cur;
     auto next = [&]() {
-      if (more) cp.template prologue<NA, NB>(tile_src<GATEUP, F8>(p, nxt.ta, nxt.ksp), L);
+      if (more) cp.template prologue<NA, NB>(tile_src<GATEUP, F8, BT>(p, nxt.ta, nxt.ksp), L);
     };
-    const TileSrc src = tile_src<GATEUP, F8>(p, cur.ta, cur.ksp);
+    const TileSrc src = tile_src<GATEUP, F8, BT>(p, cur.ta, cur.ksp);
     // each wave runs the fully scheduled loop over its 32-row blocks that
     // hold valid rows (rows past nvalid read zero and are not stored)
     const int act = min(RBLK, max(0, (cur.ta.nvalid - wm * (RBLK * 32) + 31) / 32));
     if (act >= RBLK)
-      gemm_tile<BM, NW, GATEUP, F8, RBLK, NA, NB>(p, cp, src, L, cur.ta, cur.ksp, next);
+      gemm_tile<BM, NW, GATEUP, F8, RBLK, NA, NB, BT>(p, cp, src, L, cur.ta, cur.ksp, next);
     else if (RBLK > 1 && act == 1)
-      gemm_tile<BM, NW, GATEUP, F8, (RBLK > 1 ? 1 : 0), NA, NB>(p, cp, src, L, cur.ta, cur.ksp,
-                                                               next);
+      gemm_tile<BM, NW, GATEUP, F8, (RBLK > 1 ? 1 : 0), NA, NB, BT>(p, cp, src, L, cur.ta,
+                                                                   cur.ksp, next);
     else
-      gemm_tile<BM, NW, GATEUP, F8, 0, NA, NB>(p, cp, src, L, cur.ta, cur.ksp, next);
+      gemm_tile<BM, NW, GATEUP, F8, 0, NA, NB, BT>(p, cp, src, L, cur.ta, cur.ksp, next);
     if (!more) break;
     u = un;
     cur = nxt;
@@ -585,6 +656,14 @@ template <int BM, int NW, bool GATEUP, int NA, int NB>
 __global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(GemmParams p) {
   MOE_GEMM_LDS_RING
   grouped_gemm<BM, NW, GATEUP, false, NA, NB>(p, L);
+}
+
+// The row-grouped product with the weights stored [K][N] (input gradients:
+// dA = dY W_down[e] and dX = [dG | dU] [W_gate[e]; W_up[e]]).
+template <int BM, int NW, int NA, int NB>
+__global__ __launch_bounds__(64 * NW) void gemm_bt_kernel(GemmParams p) {
+  MOE_GEMM_LDS_RING
+  grouped_gemm<BM, NW, false, false, NA, NB, true>(p, L);
 }
 
 // The gate/up GEMM on FP8 (E4M3) rows and weights with power-of-two row scales.
@@ -639,7 +718,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_kernel(GemmParams p) {
   const int units = p.E * mt_n * nt_n;
   int u = blockIdx.x;
   if (u >= units) return;
-  const CopyPlan<BM, NW, false, false> cp(p.K);
+  const CopyPlan<BM, NW, false, false> cp(p.K, p.N);
   Unit cur = wgrad_unit(p, u, mt_n, nt_n);
   cp.template prologue<NA, NB>(wgrad_src(p, cur), L);
   constexpr int RBLK = (2 * BM / NW) / 32;
@@ -660,11 +739,11 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_kernel(GemmParams p) {
     out.ksp.ks = 1;
     const int act = min(RBLK, max(0, (cur.ta.nvalid - wm * (RBLK * 32) + 31) / 32));
     if (act >= RBLK)
-      gemm_tile<BM, NW, false, false, RBLK, NA, NB>(p, cp, src, L, out.ta, out.ksp, next);
+      gemm_tile<BM, NW, false, false, RBLK, NA, NB, false>(p, cp, src, L, out.ta, out.ksp, next);
     else if (act == 1)
-      gemm_tile<BM, NW, false, false, 1, NA, NB>(p, cp, src, L, out.ta, out.ksp, next);
+      gemm_tile<BM, NW, false, false, 1, NA, NB, false>(p, cp, src, L, out.ta, out.ksp, next);
     else
-      gemm_tile<BM, NW, false, false, 0, NA, NB>(p, cp, src, L, out.ta, out.ksp, next);
+      gemm_tile<BM, NW, false, false, 0, NA, NB, false>(p, cp, src, L, out.ta, out.ksp, next);
     if (!more) break;
     u = un;
     cur = nxt;
@@ -796,6 +875,17 @@ void launch_gemm(int bm, const GemmParams& p, hipStream_t s) {
   }
 }
 
+void launch_gemm_bt(int bm, const GemmParams& p, hipStream_t s) {
+  const dim3 grid(p.grid), block(64 * kWaves);
+  if (bm == 256) {
+    hipLaunchKernelGGL((gemm_bt_kernel<256, kWaves, 2, 3>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ksplit_reduce_kernel<256, kWaves, false, false>), grid, block, 0, s, p);
+  } else {
+    hipLaunchKernelGGL((gemm_bt_kernel<128, kWaves, 3, 3>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ksplit_reduce_kernel<128, kWaves, false, false>), grid, block, 0, s, p);
+  }
+}
+
 void launch_gemm_fp8(int bm, const GemmParams& p, hipStream_t s) {
   const dim3 grid(p.grid), block(64 * kWaves);
   if (bm == 256) {
@@ -907,6 +997,17 @@ hipError_t launch_down(const FfnShape& fs, const void* A, const int32_t* offset,
   GemmParams p{A, offset, map2, Wd, nullptr, static_cast<bf16*>(Y), nullptr, nullptr, nullptr,
                E, f, h, h, fs.nt2, fs.mt2, part, fs.split_max, fs.grid2};
   launch_gemm<false>(fs.bm2, p, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dgrad(const FfnShape& fs, const void* A, const int32_t* offset,
+                        const int32_t* map2, const void* W0, const void* W1, int K0, void* C,
+                        float* part, int E, int N, int K, hipStream_t s) {
+  if (fs.grid2 == 0) return hipSuccess;
+  GemmParams p{A, offset, map2, W0, W1, static_cast<bf16*>(C), nullptr, nullptr, nullptr,
+               E, K, N, N, fs.nt2, fs.mt2, part, fs.split_max, fs.grid2};
+  p.K0 = K0;
+  launch_gemm_bt(fs.bm2, p, s);
   return hipGetLastError();
 }
 

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace moe {
 
 // ---------------------------------------------------------------- router
@@ -109,6 +111,13 @@ hipError_t launch_gate_up_fp8(const FfnShape& fs, const void* X8, const float* x
                               const int32_t* offset, const int32_t* map1, const void* Wg8,
                               const float* s_gate, const void* Wu8, const float* s_up, void* A,
                               float* part, int E, int h, int f, hipStream_t s);
+// Row-grouped product with the weights stored [K][N]: C[rows][N] = A[rows][K]
+// B_e with B_e rows 0..K0-1 from W0 [E][K0][N] and the rest from W1
+// [E][K-K0][N] (K0 and K multiples of 64); tiles and grid of fs's second
+// product (bm2, nt2 = N / 256 tiles, grid2).
+hipError_t launch_dgrad(const FfnShape& fs, const void* A, const int32_t* offset,
+                        const int32_t* map2, const void* W0, const void* W1, int K0, void* C,
+                        float* part, int E, int N, int K, hipStream_t s);
 hipError_t launch_down(const FfnShape& fs, const void* A, const int32_t* offset,
                        const int32_t* map2, const void* Wd, void* Y, float* part, int E, int h,
                        int f, int bf16, hipStream_t s);
@@ -152,8 +161,6 @@ hipError_t launch_combine_bwd(const void* dOut, const void* Y, const int32_t* sl
                               hipStream_t s);
 hipError_t launch_swiglu_bwd(const void* dA, const void* GU, const int32_t* offset, int E,
                              int64_t rows_max, int f, void* dGU, hipStream_t s);
-hipError_t launch_transpose_batched(const void* src, int R, int C, size_t sb, void* dst, int ld,
-                                    int c0, size_t db, int batches, hipStream_t s);
 hipError_t launch_kofs(const int32_t* offset, int E, int32_t* kofs, hipStream_t s);
 hipError_t launch_transpose_pad(const void* src, const int32_t* offset, const int32_t* kofs,
                                 int E, int C, void* dst, int ld, hipStream_t s);
@@ -164,7 +171,30 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const floa
 hipError_t launch_grad_input(const void* dOut, const void* dX, const int32_t* slot,
                              const float* dH, const void* W_r, void* dU, int T, int h, int E,
                              int k, hipStream_t s);
-hipError_t launch_dwr(const void* U, const float* dH, float* dWr, float* db, int T, int h, int E,
-                      hipStream_t s);
+// dW_r = U^T dH, db_r = column sums of dH: TE experts x TJ rows of U per
+// workgroup, the tokens cut into nsplit chunks of tchunk (a multiple of 16)
+// whose float32 partials [nsplit][h + 1][E] are summed afterwards.
+struct DwrPlan {
+  int te, tj, jt, et, nsplit, tchunk;
+};
+inline DwrPlan dwr_plan(int64_t T, int h, int E) {
+  DwrPlan p;
+  p.te = E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64;
+  p.tj = 4 * (256 / (p.te / 4));
+  p.jt = (h + 1 + p.tj - 1) / p.tj;
+  p.et = (E + p.te - 1) / p.te;
+  const int64_t tiles = (int64_t)p.jt * p.et;
+  const int64_t want = (2048 + tiles - 1) / tiles;  // about 2048 workgroups
+  int64_t chunk = (T + want - 1) / want;
+  chunk = std::max<int64_t>(32, (chunk + 15) / 16 * 16);
+  p.tchunk = (int)chunk;
+  p.nsplit = T > 0 ? (int)((T + chunk - 1) / chunk) : 1;
+  return p;
+}
+inline size_t dwr_part_bytes(int64_t T, int h, int E) {
+  return (size_t)dwr_plan(T, h, E).nsplit * (size_t)(h + 1) * E * 4;
+}
+hipError_t launch_dwr(const void* U, const float* dH, float* dWr, float* db, float* part, int T,
+                      int h, int E, hipStream_t s);
 
 }  // namespace moe
