@@ -232,14 +232,13 @@ LayerWs plan_layer(const Dims& d, int noisy, Plan& pl) {
   return w;
 }
 
-// Backward workspace: recomputed expert activations, their gradients, the
-// transposed weights, and the activations transposed into the zero-padded
-// per-expert K layout of the weight-gradient products (pitch Kp).
+// Backward workspace: the recomputed expert activations (X, g and u, A, Y),
+// their gradients, the router's logit gradient and the float32 partials of
+// the split products.  Every product reads its operands as stored.
 struct BackwardWs {
   FfnWs ffn;  // tile maps, A (the SwiGLU rows), K-split partials
   FfnShape fsA, fsX;  // shapes of the dA (N = f, K = h) and dX (N = h, K = 2f) products
-  int Kp;
-  size_t X, GU, Y, dY, dA, dGU, dX, dYT, AT, dGUT, XT, kofs, dgate, dH, part, dwr;
+  size_t X, GU, Y, dY, dA, dGU, dX, dgate, dH, part, dwr;
 };
 BackwardWs plan_backward(const Dims& d, Plan& pl) {
   BackwardWs w;
@@ -248,8 +247,6 @@ BackwardWs plan_backward(const Dims& d, Plan& pl) {
   w.fsA = ffn_shape(d.rows_max, (int)d.E, (int)d.f, (int)d.h, (int)d.T, (int)d.k, 1, ncu);
   w.fsX = ffn_shape(d.rows_max, (int)d.E, (int)d.h, (int)(2 * d.f), (int)d.T, (int)d.k, 1, ncu);
   const size_t rows = (size_t)(d.rows_max > 0 ? d.rows_max : 1);
-  w.Kp = (int)(((d.rows_max + 63) / 64) * 64 + 64 * d.E);
-  const size_t kp = (size_t)w.Kp;
   const size_t T1 = (size_t)(d.T > 0 ? d.T : 1);
   w.X = pl.add(rows * d.h * 2);
   w.GU = pl.add(rows * 2 * d.f * 2);
@@ -258,11 +255,6 @@ BackwardWs plan_backward(const Dims& d, Plan& pl) {
   w.dA = pl.add(rows * d.f * 2);
   w.dGU = pl.add(rows * 2 * d.f * 2);
   w.dX = pl.add(rows * d.h * 2);
-  w.dYT = pl.add((size_t)d.h * kp * 2);
-  w.AT = pl.add((size_t)d.f * kp * 2);
-  w.dGUT = pl.add((size_t)2 * d.f * kp * 2);
-  w.XT = pl.add((size_t)d.h * kp * 2);
-  w.kofs = pl.add((d.E + 1) * 4);
   w.dgate = pl.add(T1 * d.k * 4);
   w.dH = pl.add(T1 * d.E * 4);
   // K-split partials for the largest grid of the three row-grouped products
@@ -757,7 +749,6 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
   void* dA = at<void>(ws, w.dA);
   void* dGU = at<void>(ws, w.dGU);
   void* dX = at<void>(ws, w.dX);
-  int32_t* kofs = at<int32_t>(ws, w.kofs);
   float* dgate = at<float>(ws, w.dgate);
   float* dH = at<float>(ws, w.dH);
   float* part = at<float>(ws, w.part);
@@ -776,18 +767,12 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
   MOE_TRY(launch_dgrad(w.fsA, dY, offset, map, W_down, W_down, h, dA, part, E, f, h, s));
   MOE_TRY(launch_swiglu_bwd(dA, GU, offset, E, d.rows_max, f, dGU, s));
   MOE_TRY(launch_dgrad(w.fsX, dGU, offset, map, W_gate, W_up, f, dX, part, E, h, 2 * f, s));
-  // 4. weight gradients: sums over each expert's rows of outer products
-  MOE_TRY(launch_kofs(offset, E, kofs, s));
-  MOE_TRY(launch_transpose_pad(dY, offset, kofs, E, h, at<void>(ws, w.dYT), w.Kp, s));
-  MOE_TRY(launch_transpose_pad(A, offset, kofs, E, f, at<void>(ws, w.AT), w.Kp, s));
-  MOE_TRY(launch_transpose_pad(dGU, offset, kofs, E, 2 * f, at<void>(ws, w.dGUT), w.Kp, s));
-  MOE_TRY(launch_transpose_pad(X, offset, kofs, E, h, at<void>(ws, w.XT), w.Kp, s));
-  MOE_TRY(launch_wgrad(at<void>(ws, w.dYT), at<void>(ws, w.AT), kofs, dW_down, E, h, f, w.Kp,
-                       ncu, s));
-  MOE_TRY(launch_wgrad(at<void>(ws, w.dGUT), at<void>(ws, w.XT), kofs, dW_gate, E, f, h, w.Kp,
-                       ncu, s));
-  MOE_TRY(launch_wgrad(at<char>(ws, w.dGUT) + (size_t)f * w.Kp * 2, at<void>(ws, w.XT), kofs,
-                       dW_up, E, f, h, w.Kp, ncu, s));
+  // 4. weight gradients: sums over each expert's rows of outer products, the
+  // row-major activations read as stored
+  MOE_TRY(launch_wgrad(dY, h, A, f, offset, dW_down, E, h, f, ncu, s));
+  MOE_TRY(launch_wgrad(dGU, 2 * f, X, h, offset, dW_gate, E, f, h, ncu, s));
+  MOE_TRY(launch_wgrad(static_cast<char*>(dGU) + (size_t)f * 2, 2 * f, X, h, offset, dW_up, E, f,
+                       h, ncu, s));
   // 5. router: dH, then dU and dW_r, db_r
   MOE_TRY(launch_router_bwd(logits, topk_idx, topk_gate, dgate, count, T, E, k, cfg->score,
                             cfg->gate == MOE_GATE_RENORM, alpha, c_z, dH, s));

@@ -88,47 +88,6 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const bf16* dA, const b
   st16(dGU + row * 2 * f + f + c, Elem<bf16>::pack(du));
 }
 
-// Per-expert offsets of the zero-padded K layout of the weight gradients:
-// kofs[e] = sum over earlier experts of their rows rounded up to 64.
-__global__ __launch_bounds__(256) void kofs_kernel(const int32_t* offset, int E, int32_t* kofs) {
-  __shared__ int tmp[4];
-  const int e = threadIdx.x;
-  const int n = e < E ? offset[e + 1] - offset[e] : 0;
-  int tot;
-  const int a = block_excl_scan256((n + 63) & ~63, tmp, &tot);
-  if (e < E) kofs[e] = a;
-  if (e == 0) kofs[E] = tot;
-}
-
-// Transpose of row-grouped activations into the padded K layout:
-// dst[c][kofs[e] + i] = src[offset[e] + i][c] for the expert's rows i, and 0
-// up to kofs[e + 1].  A 64-wide block of K lies inside one expert.
-__global__ __launch_bounds__(256) void transpose_pad_kernel(const bf16* src, const int32_t* offset,
-                                                            const int32_t* kofs, int E, int C,
-                                                            bf16* dst, int ld) {
-  __shared__ bf16 tile[64][66];
-  const int k0 = blockIdx.y * 64, cc0 = blockIdx.x * 64;
-  if (k0 >= kofs[E]) return;
-  int lo = 0, hi = E;  // expert e with kofs[e] <= k0 < kofs[e + 1]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (kofs[mid] <= k0) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int n = offset[e + 1] - offset[e];
-  const int i0 = k0 - kofs[e];
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int ii = i0 + i, c = cc0 + tx;
-    tile[i][tx] = (ii < n && c < C) ? src[(size_t)(offset[e] + ii) * C + c] : bf16(0);
-  }
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = cc0 + i;
-    if (c < C) dst[(size_t)c * ld + k0 + tx] = tile[tx][i];
-  }
-}
-
 // Router backward, one wave per token: scores from the float32 logits, the
 // gates' gradient back to the scores (raw: ds = dg; renormalised over the
 // selected set S: ds_j = (dg_j - sum_i dg_i g_i) / sum_S s), then to the
@@ -398,20 +357,6 @@ hipError_t launch_swiglu_bwd(const void* dA, const void* GU, const int32_t* offs
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      static_cast<const bf16*>(dA), static_cast<const bf16*>(GU), offset, E, f,
                      static_cast<bf16*>(dGU));
-  return hipGetLastError();
-}
-
-hipError_t launch_kofs(const int32_t* offset, int E, int32_t* kofs, hipStream_t s) {
-  hipLaunchKernelGGL(kofs_kernel, dim3(1), dim3(256), 0, s, offset, E, kofs);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_pad(const void* src, const int32_t* offset, const int32_t* kofs,
-                                int E, int C, void* dst, int ld, hipStream_t s) {
-  if (C == 0 || ld == 0) return hipSuccess;
-  dim3 grid((C + 63) / 64, ld / 64);
-  hipLaunchKernelGGL(transpose_pad_kernel, grid, dim3(256), 0, s, static_cast<const bf16*>(src),
-                     offset, kofs, E, C, static_cast<bf16*>(dst), ld);
   return hipGetLastError();
 }
 

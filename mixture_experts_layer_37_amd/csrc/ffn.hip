@@ -93,10 +93,8 @@ struct GemmParams {
   int grid;              // workgroups of the GEMM launch (a multiple of 8)
   bf16* C2 = nullptr;    // gate/up: also store the pre-activations g and u,
                          // [rows][2 Nout] (g in columns 0..Nout-1, u after)
-  // weight gradients (gemm_wgrad_kernel): C_e[M][N] = A[:, K_e] B[:, K_e]^T
-  // for each expert e, A [M][K] and B [N][K] with K the row pitch and
-  // K_e = kofs[e] .. kofs[e+1]-1 (multiples of 64, zero-padded)
-  const int32_t* kofs = nullptr;
+  // weight gradients (gemm_wgrad_kernel): M columns of A per expert (K is
+  // then A's row pitch and Nout B's)
   int M = 0;
   // BT kernels (weights stored [K][N]): W0 holds K rows 0..K0-1 of each
   // expert's [K][N] operand and W1 the rest ([E][K0][N] and [E][K-K0][N])
@@ -309,22 +307,34 @@ __device__ __forceinline__ TileSrc tile_src(const GemmParams& p, const TileAt& t
 // load (see gemm_tile).
 __device__ __forceinline__ constexpr int trswz(int kr) { return (kr & 3) << 2; }
 
-template <int BM, int NW, bool GATEUP, bool F8, bool BT = false>
+//
+// AT: the same for the A operand, stored [K][M] (weight gradients), its K
+// step 64 rows of the tile's BM columns.
+template <int BM, int NW, bool GATEUP, bool F8, bool BT = false, bool AT = false>
 struct CopyPlan {
   static constexpr int AG = BM / (8 * NW);  // 8-row A groups copied per wave per step
   static constexpr int BG = BN / (8 * NW);  // 8-row B groups copied per wave per step
   int wave;
   int voA[AG], voB[BG];
-  int bstep;  // BT: bytes of one K step of the weight panel (64 rows)
-  __device__ __forceinline__ explicit CopyPlan(int K, int N = 0) {
+  int astep, bstep;  // AT / BT: bytes of one K step (64 rows) of A / of the weight panel
+  // K: row length of the K-contiguous operands; N, M: row lengths (elements)
+  // of a [K][N] weight operand (BT) and a [K][M] A operand (AT)
+  __device__ __forceinline__ explicit CopyPlan(int K, int N = 0, int M = 0) {
     // the wave index is uniform: keep it (and all copy addressing) in SGPRs
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, lrow = lane >> 3;
 #pragma unroll
     for (int j = 0; j < AG; ++j) {
-      const int r = 8 * (wave + NW * j) + lrow;
-      voA[j] = r * K * Elt<F8>::kBytes + (((lane & 7) ^ ((r >> 1) & 7)) * 16);
+      if constexpr (AT) {  // BM / 8 chunks per k-row
+        constexpr int CPR = BM / 8, RPI = 64 / CPR;  // chunks per row, rows per copy
+        const int kr = RPI * (wave + NW * j) + lane / CPR;
+        voA[j] = kr * M * 2 + (((lane % CPR) ^ trswz(kr)) * 16);
+      } else {
+        const int r = 8 * (wave + NW * j) + lrow;
+        voA[j] = r * K * Elt<F8>::kBytes + (((lane & 7) ^ ((r >> 1) & 7)) * 16);
+      }
     }
+    astep = BK * M * 2;
 #pragma unroll
     for (int j = 0; j < BG; ++j) {
       if constexpr (BT) {
@@ -343,7 +353,7 @@ struct CopyPlan {
   // step j past the end reloads the last step (in bounds, never read), so
   // every step issues the same number of copies
   __device__ __forceinline__ void issueA(const TileSrc& s, bf16* as, int j) const {
-    const int kb = (s.kbeg + min(j, s.KT - 1)) * 128;
+    const int kb = (s.kbeg + min(j, s.KT - 1)) * (AT ? astep : 128);
 #pragma unroll
     for (int q = 0; q < AG; ++q) dma16(s.rA, as + (wave + NW * q) * 8 * BK, voA[q], kb);
   }
@@ -378,15 +388,17 @@ struct CopyPlan {
 // RBLK); a wave with R < RBLK skips the fragment reads and MFMAs of the others
 // (their accumulators stay zero and their rows are never stored) but issues
 // the same copies and meets the same barriers as the rest of the workgroup.
-template <int BM, int NW, bool GATEUP, bool F8, int R, int NA, int NB, bool BT, class Next>
-__device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM, NW, GATEUP, F8, BT>& cp,
+template <int BM, int NW, bool GATEUP, bool F8, int R, int NA, int NB, bool BT, bool AT,
+          class Next>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p,
+                                          const CopyPlan<BM, NW, GATEUP, F8, BT, AT>& cp,
                                           const TileSrc& src, const Ring& L, const TileAt& ta,
                                           const KSplit& ksp, Next&& next) {
   constexpr int WM = NW / 2;         // waves along M (2 along N)
   constexpr int WR = BM / WM;        // rows per wave
   constexpr int RBLK = WR / 32;      // 32-row MFMA blocks per wave
-  constexpr int AG = CopyPlan<BM, NW, GATEUP, F8, BT>::AG;
-  constexpr int BG = CopyPlan<BM, NW, GATEUP, F8, BT>::BG;
+  constexpr int AG = CopyPlan<BM, NW, GATEUP, F8, BT, AT>::AG;
+  constexpr int BG = CopyPlan<BM, NW, GATEUP, F8, BT, AT>::BG;
   constexpr int NSL = Elt<F8>::kSlices;  // MFMA K slices per step
   constexpr int FC = F8 ? 2 : 1;         // 16-byte chunks per fragment and lane
   using Frag = typename Elt<F8>::Frag;
@@ -405,21 +417,21 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM
   const int l32 = lane & 31, khalf = lane >> 5;
   const int sw = (l32 >> 1) & 7;  // (row >> 1) & 7 of every fragment row of this lane
   int aoff[RBLK], boff[4];  // byte offsets of this lane's rows in a slot
+  // transposing read (see below): lane 4 q + m of each 16-lane group
+  // addresses k-row q of the slice's 8 (+ 4 for the second half) and columns
+  // 4 (m % 4) .. +3 of its 16; width: the tile's columns
+  auto tr_off = [&](int width, int x0) {
+    const int l16 = lane & 15, kr = 8 * khalf + (l16 >> 2);
+    const int c = (x0 + 16 * ((lane >> 4) & 1) + 4 * (l16 & 3)) >> 3;
+    return kr * (width * 2) + ((c ^ trswz(kr)) * 16) + 8 * (l16 & 1);
+  };
 #pragma unroll
-  for (int i = 0; i < RBLK; ++i) aoff[i] = (wm * WR + i * 32 + l32) * 128;
+  for (int i = 0; i < RBLK; ++i)
+    aoff[i] = AT ? tr_off(BM, wm * WR + i * 32) : (wm * WR + i * 32 + l32) * 128;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if constexpr (BT) {
-      // transposing read: within each 16-lane group, lane i gets element i % 4
-      // of the 8 bytes that lanes 4 q + i / 4 (q = 0..3) address.  Lane
-      // 4 q + m of a group addresses k-row q (+ 4 for the second half) of the
-      // slice's 8 and columns 4 (m % 4) .. +3 of its 16, so lane i receives
-      // column i of the group's 16 at 4 consecutive k: the fragment of column
-      // l32 at k = 16 slice + 8 khalf + 0..7, like the A fragment.
-      const int l16 = lane & 15, qk = l16 >> 2;
-      const int kr = 8 * khalf + qk;  // + 16 slice + 4 half, multiples of 4
-      const int c = (wn * 128 + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (l16 & 3)) >> 3;
-      boff[j] = kr * (BN * 2) + ((c ^ trswz(kr)) * 16) + 8 * (l16 & 1);
+      boff[j] = tr_off(BN, wn * 128 + j * 32);
     } else {
       const int r = GATEUP ? ((j < 2 ? 0 : 128) + wn * 64 + (j & 1) * 32 + l32)
                            : (wn * 128 + j * 32 + l32);
@@ -449,13 +461,19 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM
       return *reinterpret_cast<const Frag*>(row + ((c0 ^ sw) * 16));
     }
   };
-  // BT fragment: two transposing 8-byte reads, k-rows 16 slice + (0..3, 4..7)
-  auto fragT = [&](const bf16* slot, int off, int slice) {
+  // Fragment of an operand stored [K][columns] (AT, BT): two transposing
+  // 8-byte reads (ds_read_b64_tr_b16) of k-rows 16 slice + 8 khalf + (0..3,
+  // 4..7).  Within each 16-lane group, lane i gets element i % 4 of the 8
+  // bytes that lanes 4 q + i / 4 (q = 0..3) address; with the addresses of
+  // tr_off, lane i receives column i of the group's 16 at 4 consecutive k,
+  // so the lane holds column l32 at k = 16 slice + 8 khalf + 0..7, as a
+  // K-contiguous fragment does.
+  auto fragT = [&](const bf16* slot, int off, int slice, int width) {
     typedef short v4s __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) v4s lds_v4s;
-    const char* q = reinterpret_cast<const char*>(slot) + off + slice * (16 * BN * 2);
+    const char* q = reinterpret_cast<const char*>(slot) + off + slice * (16 * width * 2);
     const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(q));
-    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(q + 4 * BN * 2));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(q + 4 * width * 2));
     const v4s v[2] = {lo, hi};
     bf16x8 r;
     __builtin_memcpy(&r, v, 16);
@@ -464,10 +482,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM
   auto fetch = [&](const bf16* as, const bf16* bs, int slice, int st) {
     const int c0 = FC * (2 * slice + khalf);
 #pragma unroll
-    for (int i = 0; i < R; ++i) fa[st][i] = frag(as, aoff[i], c0);
+    for (int i = 0; i < R; ++i) {
+      if constexpr (AT) fa[st][i] = fragT(as, aoff[i], slice, BM);
+      else fa[st][i] = frag(as, aoff[i], c0);
+    }
 #pragma unroll
     for (int j = 0; j < (R > 0 ? 4 : 0); ++j) {
-      if constexpr (BT) fb[st][j] = fragT(bs, boff[j], slice);
+      if constexpr (BT) fb[st][j] = fragT(bs, boff[j], slice, BN);
       else fb[st][j] = frag(bs, boff[j], c0);
     }
   };
@@ -488,7 +509,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const CopyPlan<BM
   // order for the scheduler: MFMAs interleaved with the next fragment reads
   // and, after the barrier, with the copies (groups: 0x008 MFMA, 0x100 LDS
   // read, 0x020 global read incl. LDS copies)
-  constexpr int NM = R * 4, NR = R > 0 ? R * FC + 4 * (BT ? 2 : FC) : 0, NC = AG + BG;
+  constexpr int NM = R * 4, NR = R > 0 ? R * (AT ? 2 : FC) + 4 * (BT ? 2 : FC) : 0;
+  constexpr int NC = AG + BG;
   constexpr int CPM = NM > 0 ? (NC + NM - 1) / NM : NC;  // copies placed after each MFMA
   constexpr int RPM = NM > 0 ? (NR + NM - 1) / NM : NR;  // LDS reads placed after each MFMA
   auto order = [&]() {
@@ -613,7 +635,7 @@ __device__ __forceinline__ void grouped_gemm(const GemmParams& p, const Ring& L)
   const int units = xs.full + xs.rem * xs.ks;
   int u = blockIdx.x >> 3;
   if (u >= units) return;
-  const CopyPlan<BM, NW, GATEUP, F8, BT> cp(p.K, p.N);
+  const CopyPlan<BM, NW, GATEUP, F8, BT, false> cp(p.K, p.N);
   Unit cur = unit_at<BM>(p, xs, xcd, u, KT, mtiles);
   cp.template prologue<NA, NB>(tile_src<GATEUP, F8, BT>(p, cur.ta, cur.ksp), L);
   constexpr int RBLK = (2 * BM / NW) / 32;
@@ -632,12 +654,13 @@ __device__ __forceinline__ void grouped_gemm(const GemmParams& p, const Ring& L)
     // hold valid rows (rows past nvalid read zero and are not stored)
     const int act = min(RBLK, max(0, (cur.ta.nvalid - wm * (RBLK * 32) + 31) / 32));
     if (act >= RBLK)
-      gemm_tile<BM, NW, GATEUP, F8, RBLK, NA, NB, BT>(p, cp, src, L, cur.ta, cur.ksp, next);
+      gemm_tile<BM, NW, GATEUP, F8, RBLK, NA, NB, BT, false>(p, cp, src, L, cur.ta, cur.ksp,
+                                                             next);
     else if (RBLK > 1 && act == 1)
-      gemm_tile<BM, NW, GATEUP, F8, (RBLK > 1 ? 1 : 0), NA, NB, BT>(p, cp, src, L, cur.ta,
-                                                                   cur.ksp, next);
+      gemm_tile<BM, NW, GATEUP, F8, (RBLK > 1 ? 1 : 0), NA, NB, BT, false>(p, cp, src, L, cur.ta,
+                                                                          cur.ksp, next);
     else
-      gemm_tile<BM, NW, GATEUP, F8, 0, NA, NB, BT>(p, cp, src, L, cur.ta, cur.ksp, next);
+      gemm_tile<BM, NW, GATEUP, F8, 0, NA, NB, BT, false>(p, cp, src, L, cur.ta, cur.ksp, next);
     if (!more) break;
     u = un;
     cur = nxt;
@@ -675,39 +698,43 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_kernel(GemmParams p) {
 
 // Weight gradients of the expert products (section "专家计算：padding、
 // block-sparse 与 grouped GEMM": the backward is a grouped product for the
-// inputs and one for the weights): C_e = A[:, K_e] B[:, K_e]^T, the sum over
-// expert e's rows.  A [M][K] and B [N][K] are the transposed activations with
-// each expert's rows padded with zeros to a multiple of 64 (kofs), so every K
-// step lies inside one expert.  Tiles (e, m-tile, n-tile) in e-major order,
-// round-robin over the persistent grid; the main loop and the cross-tile
-// prefetch are those of the row-grouped GEMM.  An expert without rows gets one
-// K step of zeros (its buffer resource is empty), i.e. C_e = 0.
+// inputs and one for the weights): C_e[M][N] = sum over expert e's rows r of
+// A[r][m] B[r][n], with A [rows][lda] and B [rows][ldb] the row-major
+// activations (columns 0..M-1 of A, 0..N-1 of B).  Both operands are read as
+// stored ([K][columns], the AT and BT copies and transposing fragment reads),
+// K being expert e's rows offset[e] .. offset[e+1]-1: the buffer resources
+// end at the expert's last row, so the ragged last K step reads zeros.
+// Tiles (e, m-tile, n-tile) in e-major order, round-robin over the
+// persistent grid; the main loop and the cross-tile prefetch are those of the
+// row-grouped GEMM.  An expert without rows gets one K step of zeros (its
+// buffer resources are empty), i.e. C_e = 0.
 __device__ __forceinline__ Unit wgrad_unit(const GemmParams& p, int t, int mt_n, int nt_n) {
   Unit w;
   const int per = mt_n * nt_n;
   const int e = t / per, r = t - e * per, mt = r / nt_n;
   w.ta.e = __builtin_amdgcn_readfirstlane(e);
   w.ta.nt = __builtin_amdgcn_readfirstlane(r - mt * nt_n);
-  w.ta.row0 = __builtin_amdgcn_readfirstlane(mt * 256);  // row in A (and in C_e)
+  w.ta.row0 = __builtin_amdgcn_readfirstlane(mt * 256);  // first column m of A (row of C_e)
   w.ta.nvalid = __builtin_amdgcn_readfirstlane(min(256, p.M - mt * 256));
-  const int k0 = p.kofs[w.ta.e] / BK, k1 = p.kofs[w.ta.e + 1] / BK;
-  w.ksp = KSplit{__builtin_amdgcn_readfirstlane(k0), __builtin_amdgcn_readfirstlane(max(1, k1 - k0)),
-                 1, nullptr};
-  w.ksp.ks = k1 > k0 ? 1 : 0;  // 0 marks an expert without rows
+  const int r0 = p.offset[w.ta.e], n = p.offset[w.ta.e + 1] - r0;
+  w.ksp = KSplit{__builtin_amdgcn_readfirstlane(r0),
+                 __builtin_amdgcn_readfirstlane(max(1, (n + BK - 1) / BK)), 1, nullptr};
+  w.ksp.ks = __builtin_amdgcn_readfirstlane(n);  // rows of the expert (0: none)
   return w;
 }
 __device__ __forceinline__ TileSrc wgrad_src(const GemmParams& p, const Unit& w) {
   TileSrc s;
-  const size_t rb = (size_t)p.K * 2;
+  const size_t pa = (size_t)p.K * 2, pb = (size_t)p.Nout * 2;  // row pitches of A and B
+  const size_t r0 = (size_t)w.ksp.kbeg, n = (size_t)w.ksp.ks;
+  const size_t ma = (size_t)w.ta.row0 * 2, nb = (size_t)w.ta.nt * BN * 2;
   const char* A = static_cast<const char*>(p.A);
   const char* B = static_cast<const char*>(p.W0);
-  const size_t n0 = (size_t)w.ta.nt * BN;
-  const bool empty = w.ksp.ks == 0;
-  s.rA = make_rsrc(A + (size_t)w.ta.row0 * rb, empty ? 0 : (size_t)w.ta.nvalid * rb);
-  s.rB0 = make_rsrc(B + n0 * rb, empty ? 0 : (size_t)(p.N - n0) * rb);
+  s.rA = make_rsrc(A + r0 * pa + ma, n > 0 ? n * pa - ma : 0);
+  s.rB0 = make_rsrc(B + r0 * pb + nb, n > 0 ? n * pb - nb : 0);
   s.rB1 = s.rB0;
-  s.kbeg = w.ksp.kbeg;
+  s.kbeg = 0;
   s.KT = w.ksp.ksteps;
+  s.kt0 = 1 << 30;  // one panel
   return s;
 }
 template <int NA, int NB>
@@ -718,7 +745,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_kernel(GemmParams p) {
   const int units = p.E * mt_n * nt_n;
   int u = blockIdx.x;
   if (u >= units) return;
-  const CopyPlan<BM, NW, false, false> cp(p.K, p.N);
+  // A [rows][K = lda], B [rows][Nout = ldb]
+  const CopyPlan<BM, NW, false, false, true, true> cp(0, p.Nout, p.K);
   Unit cur = wgrad_unit(p, u, mt_n, nt_n);
   cp.template prologue<NA, NB>(wgrad_src(p, cur), L);
   constexpr int RBLK = (2 * BM / NW) / 32;
@@ -733,17 +761,22 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_kernel(GemmParams p) {
       if (more) cp.template prologue<NA, NB>(wgrad_src(p, nxt), L);
     };
     const TileSrc src = wgrad_src(p, cur);
-    // C_e is row block e of a [E * M][N] matrix
+    // C_e is row block e of a [E * M][N] matrix (row pitch N)
+    GemmParams q = p;
+    q.Nout = p.N;
     Unit out = cur;
     out.ta.row0 = cur.ta.e * p.M + cur.ta.row0;
-    out.ksp.ks = 1;
+    out.ksp = KSplit{0, cur.ksp.ksteps, 1, nullptr};
     const int act = min(RBLK, max(0, (cur.ta.nvalid - wm * (RBLK * 32) + 31) / 32));
     if (act >= RBLK)
-      gemm_tile<BM, NW, false, false, RBLK, NA, NB, false>(p, cp, src, L, out.ta, out.ksp, next);
+      gemm_tile<BM, NW, false, false, RBLK, NA, NB, true, true>(q, cp, src, L, out.ta, out.ksp,
+                                                                next);
     else if (act == 1)
-      gemm_tile<BM, NW, false, false, 1, NA, NB, false>(p, cp, src, L, out.ta, out.ksp, next);
+      gemm_tile<BM, NW, false, false, 1, NA, NB, true, true>(q, cp, src, L, out.ta, out.ksp,
+                                                             next);
     else
-      gemm_tile<BM, NW, false, false, 0, NA, NB, false>(p, cp, src, L, out.ta, out.ksp, next);
+      gemm_tile<BM, NW, false, false, 0, NA, NB, true, true>(q, cp, src, L, out.ta, out.ksp,
+                                                             next);
     if (!more) break;
     u = un;
     cur = nxt;
@@ -976,13 +1009,13 @@ hipError_t launch_gate_up_save(const FfnShape& fs, const void* X, const int32_t*
   return hipGetLastError();
 }
 
-hipError_t launch_wgrad(const void* A, const void* B, const int32_t* kofs, void* C, int E, int M,
-                        int N, int Kp, int ncu, hipStream_t s) {
+hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const int32_t* offset,
+                        void* C, int E, int M, int N, int ncu, hipStream_t s) {
   const int units = E * ((M + 255) / 256) * ((N + BN - 1) / BN);
   if (units == 0) return hipSuccess;
-  GemmParams p{A, nullptr, nullptr, B, nullptr, static_cast<bf16*>(C), nullptr, nullptr, nullptr,
-               E, Kp, N, N, 0, 0, nullptr, 1, 0};
-  p.kofs = kofs;
+  // K: A's row pitch, Nout: B's row pitch (the epilogue writes rows of N)
+  GemmParams p{A, offset, nullptr, B, nullptr, static_cast<bf16*>(C), nullptr, nullptr, nullptr,
+               E, lda, N, ldb, 0, 0, nullptr, 1, 0};
   p.M = M;
   const int grid = std::min(units, ncu);
   hipLaunchKernelGGL((gemm_wgrad_kernel<2, 3>), dim3(grid), dim3(64 * kWaves), 0, s, p);

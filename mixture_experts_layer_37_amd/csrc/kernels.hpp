@@ -152,18 +152,16 @@ hipError_t launch_z_loss(const float* logits, int T, int E, float* z_loss, hipSt
 hipError_t launch_gate_up_save(const FfnShape& fs, const void* X, const int32_t* offset,
                                const int32_t* map1, const void* Wg, const void* Wu, void* A,
                                void* GU, float* part, int E, int h, int f, hipStream_t s);
-// C_e = A[:, K_e] B[:, K_e]^T per expert (weight gradients), A [M][Kp],
-// B [N][Kp] bf16 with the zero-padded per-expert K ranges kofs; C [E][M][N].
-hipError_t launch_wgrad(const void* A, const void* B, const int32_t* kofs, void* C, int E, int M,
-                        int N, int Kp, int ncu, hipStream_t s);
+// Weight gradients: C_e[m][n] = sum over expert e's rows r (offset[e] ..
+// offset[e+1]-1) of A[r][m] B[r][n], A [rows][lda] (columns 0..M-1) and B
+// [rows][ldb] (columns 0..N-1) bf16 row-major; C [E][M][N].
+hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const int32_t* offset,
+                        void* C, int E, int M, int N, int ncu, hipStream_t s);
 hipError_t launch_combine_bwd(const void* dOut, const void* Y, const int32_t* slot,
                               const float* gate, void* dY, float* dgate, int T, int h, int k,
                               hipStream_t s);
 hipError_t launch_swiglu_bwd(const void* dA, const void* GU, const int32_t* offset, int E,
                              int64_t rows_max, int f, void* dGU, hipStream_t s);
-hipError_t launch_kofs(const int32_t* offset, int E, int32_t* kofs, hipStream_t s);
-hipError_t launch_transpose_pad(const void* src, const int32_t* offset, const int32_t* kofs,
-                                int E, int C, void* dst, int ld, hipStream_t s);
 hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const float* gate,
                              const float* dgate, const int32_t* count, int T, int E, int k,
                              int score, int renorm, float alpha, float c_z, float* dH,
