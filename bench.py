@@ -3,7 +3,8 @@
 One step = one moe_layer_forward (router, dispatch, grouped SwiGLU experts,
 combine, statistics) over one batch of seeded synthetic tokens whose inputs
 are resident in HBM; with --backward, one forward followed by one
-moe_layer_backward (a training step of the layer, upstream gradient seeded).
+moe_layer_backward (a training step of the layer, upstream gradient seeded; the
+forward keeps the expert activations for it unless --recompute).
 Prints one JSON line on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -40,6 +41,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--backward", action="store_true",
                     help="time forward + backward (bf16, not noisy, no shared experts)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="with --backward: the forward keeps no activations and the backward "
+                         "recomputes them")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -232,6 +236,8 @@ def main():
                   file=sys.stderr)
             sys.exit(2)
         fields += ["logits", "topk_idx", "topk_gate", "slot", "count", "offset"]
+        if not args.recompute:  # the forward keeps X, g | u, a and Y for the backward
+            fields += list(B.SAVED_FIELDS)
         bws = B.new_workspace(cfg, B.MOE_WS_BACKWARD, dev)
         gen = torch.Generator(device=dev).manual_seed(args.seed + 1)
         dOut = torch.randn((w.T, w.h), generator=gen, device=dev).to(torch.bfloat16)
@@ -262,7 +268,9 @@ def main():
                                  aux["logits"], aux["topk_idx"], aux["topk_gate"], aux["slot"],
                                  aux["count"], aux["offset"], dOut, grads["dU"], grads["dW_r"],
                                  grads["dW_gate"], grads["dW_up"], grads["dW_down"],
-                                 db_r=grads["db_r"], alpha=0.01, c_z=1e-3, ws=bws)
+                                 db_r=grads["db_r"], alpha=0.01, c_z=1e-3, ws=bws,
+                                 saved=(None if args.recompute
+                                        else {n: aux[n] for n in B.SAVED_FIELDS}))
             if events is not None:
                 events[-1].record()
 
@@ -354,12 +362,13 @@ def main():
     }
     if args.backward:
         # the backward's products: dgrad 6 h f and wgrad 6 h f per kept row
-        # (useful), plus 6 h f of recomputed forward (executed)
+        # (useful), plus 6 h f of recomputed forward when it recomputes
         res["backward"] = {"ms": bwd_ms, "forward_ms": ms - bwd_ms,
+                           "activations": "recomputed" if args.recompute else "kept by the forward",
                            "mfma_frac_useful": 12.0 * w.h * w.f * kept / (bwd_ms * 1e-3) / 1e12
                            / PEAK_BF16_TFLOPS,
-                           "mfma_frac_exec": 18.0 * w.h * w.f * kept / (bwd_ms * 1e-3) / 1e12
-                           / PEAK_BF16_TFLOPS}
+                           "mfma_frac_exec": (18.0 if args.recompute else 12.0) * w.h * w.f
+                           * kept / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     if not args.no_cpu_baseline and not args.backward:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(w, x, aux, args.cpu_baseline_seconds)

@@ -129,6 +129,10 @@ typedef struct {
   float* z_loss;       /* [1] router z-loss: mean over tokens of the squared
                           log-sum-exp of the logits routing used (section
                           "各家的变体", "Router z-loss 与数值稳定", eq. L_z)   */
+  void* GU;            /* [rows_max, 2f] bf16 gate and up pre-activations g, u
+                          (g in columns 0..f-1, u in f..2f-1); bf16 layers
+                          without FP8 only (else MOE_ERR_UNSUPPORTED)          */
+  void* A;             /* [rows_max, f] SwiGLU products a = SiLU(g) u         */
 } moe_aux_outputs;
 
 /* Workspace sizes per entry point. */
@@ -269,8 +273,11 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
  *  Inputs: U, W_r, W_gate, W_up, W_down as given to the forward; from its
  *  outputs (moe_aux_outputs) logits [T,E], topk_idx, topk_gate, slot [T,k],
  *  count [E], offset [E+1]; dOut [T,h] the upstream gradient.  alpha and c_z
- *  scale aux_loss and z_loss (finite; 0 leaves a term out).  The experts are
- *  recomputed from U (no activations are kept by the forward).
+ *  scale aux_loss and z_loss (finite; 0 leaves a term out).
+ *  saved: NULL, and the experts are recomputed from U with the forward's
+ *  kernels (the same values bit for bit); or the forward's aux outputs with
+ *  X, GU, A and Y all set (every other field is ignored), which the backward
+ *  then reads instead (MOE_ERR_INVALID_ARG if one of the four is NULL).
  *  Outputs: dU [T,h] and dW_gate, dW_up [E,f,h], dW_down [E,h,f] in bf16;
  *  dW_r [h,E] and db_r [E] (nullable) in float32.
  *  Supported: cfg->dtype == MOE_BF16, not noisy, no shared experts (else
@@ -281,8 +288,9 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
                            const float* logits, const int32_t* topk_idx, const float* topk_gate,
                            const int32_t* slot, const int32_t* count, const int32_t* offset,
                            const void* dOut, float alpha, float c_z, void* dU, float* dW_r,
-                           float* db_r, void* dW_gate, void* dW_up, void* dW_down, void* ws,
-                           size_t ws_bytes, void* stream);
+                           float* db_r, void* dW_gate, void* dW_up, void* dW_down,
+                           const moe_aux_outputs* saved, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /* ---------------------------------------------------------------- FP8
  * FP8 dispatch and FP8 up-projection (page "MoE 与专家并行", section

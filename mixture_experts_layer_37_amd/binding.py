@@ -50,7 +50,7 @@ class moe_aux_outputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "topk_idx", "topk_gate", "logits", "slot", "row_token", "count", "kept", "offset",
         "prob_sum", "f", "P", "aux_loss", "maxvio", "n_dropped", "X", "Y", "Y_shared",
-        "z_loss")]
+        "z_loss", "GU", "A")]
 
 
 AUX_FIELDS = [n for n, _ in moe_aux_outputs._fields_]
@@ -87,7 +87,7 @@ def lib() -> ctypes.CDLL:
                                                               P, P, SZ, P]),
             "moe_quantize_rows_fp8": (I32, [P, I64, I64, P, P, P]),
             "moe_layer_backward": (I32, [cfgp] + [P] * 12 + [ctypes.c_float, ctypes.c_float]
-                                   + [P] * 6 + [P, SZ, P]),
+                                   + [P] * 7 + [P, SZ, P]),
             "moe_dispatch_fp8": (I32, [cfgp] + [P] * 9 + [P, SZ, P]),
             "moe_expert_ffn_fp8": (I32, [cfgp] + [P] * 9 + [P, SZ, P]),
         }
@@ -317,7 +317,12 @@ _AUX_SPEC = {
     "Y": (lambda c, r: (r, c.h), None),
     "Y_shared": (lambda c, r: (c.n_shared, c.T, c.h), None),
     "z_loss": (lambda c, r: (1,), torch.float32),
+    "GU": (lambda c, r: (r, 2 * c.f), None),
+    "A": (lambda c, r: (r, c.f), None),
 }
+
+# the forward's outputs that moe_layer_backward can take instead of recomputing
+SAVED_FIELDS = ("X", "GU", "A", "Y")
 
 
 def alloc_aux(cfg, device="cuda", fields=None) -> dict:
@@ -404,10 +409,11 @@ def moe_layer_forward_fp8(cfg, U, W_r, b_r, W_noise, noise, W8_gate, s_gate, W8_
 
 def moe_layer_backward(cfg, U, W_r, W_gate, W_up, W_down, logits, topk_idx, topk_gate, slot,
                        count, offset, dOut, dU, dW_r, dW_gate, dW_up, dW_down, db_r=None,
-                       alpha=0.0, c_z=0.0, ws=None, stream=None):
+                       alpha=0.0, c_z=0.0, saved=None, ws=None, stream=None):
     """Gradients of <dOut, out> + alpha aux_loss + c_z z_loss for the routing of a
     forward (logits ... offset from its aux outputs).  dU, dW_gate, dW_up,
-    dW_down bf16; dW_r [h, E] and db_r [E] float32."""
+    dW_down bf16; dW_r [h, E] and db_r [E] float32.  saved: None (the experts
+    are recomputed) or a dict with the forward's aux outputs X, GU, A and Y."""
     T, h, f, E, k = cfg.T, cfg.h, cfg.f, cfg.E, cfg.k
     bf = torch.bfloat16
     need = workspace_size(cfg, MOE_WS_BACKWARD)
@@ -426,8 +432,16 @@ def moe_layer_backward(cfg, U, W_r, W_gate, W_up, W_down, logits, topk_idx, topk
         _ptr(db_r, "db_r", (E,), torch.float32), _ptr(dW_gate, "dW_gate", (E, f, h), bf),
         _ptr(dW_up, "dW_up", (E, f, h), bf), _ptr(dW_down, "dW_down", (E, h, f), bf),
     ]
-    _check(lib().moe_layer_backward(ctypes.byref(cfg), *args, wp, wn, _stream(stream)),
-           "moe_layer_backward")
+    sv = None
+    if saved is not None:
+        sv = moe_aux_outputs()
+        rows = max_rows(cfg)
+        for name in SAVED_FIELDS:
+            shape_fn, _ = _AUX_SPEC[name]
+            setattr(sv, name, _ptr(saved[name], name, shape_fn(cfg, rows), bf))
+    _check(lib().moe_layer_backward(ctypes.byref(cfg), *args,
+                                    ctypes.byref(sv) if sv is not None else None, wp, wn,
+                                    _stream(stream)), "moe_layer_backward")
 
 
 def moe_quantize_rows_fp8(src, dst=None, scale=None, stream=None):

@@ -369,28 +369,35 @@ struct Fp8Up {
 };
 
 // Expects run_tile_map to have been enqueued before.  f8 != NULL: X holds
-// E4M3 rows and the gate/up GEMM runs on FP8.
+// E4M3 rows and the gate/up GEMM runs on FP8.  A: where the SwiGLU products go
+// (NULL: the workspace); GU: also keep the pre-activations g, u (bf16 only).
 int32_t run_gate_up(const Dims& d, const FfnWs& w, const void* X, const int32_t* offset,
                     const void* Wg, const void* Wu, const void* Wd, void* Y, void* ws,
-                    hipStream_t s, const Fp8Up* f8 = nullptr) {
+                    hipStream_t s, const Fp8Up* f8 = nullptr, void* A = nullptr,
+                    void* GU = nullptr) {
+  if (!A) A = at<void>(ws, w.A);
   if (f8) {
     MOE_TRY(launch_gate_up_fp8(w.fs, X, f8->xs, offset, at<int32_t>(ws, w.map1), f8->Wg, f8->sg,
-                               f8->Wu, f8->su, at<void>(ws, w.A), at<float>(ws, w.part),
-                               (int)d.E, (int)d.h, (int)d.f, s));
+                               f8->Wu, f8->su, A, at<float>(ws, w.part), (int)d.E, (int)d.h,
+                               (int)d.f, s));
     return MOE_OK;
   }
   if (!d.bf16)
-    return hip_status(launch_ffn_f32(X, offset, Wg, Wu, Wd, at<void>(ws, w.A), Y, d.rows_max,
-                                     (int)d.E, (int)d.h, (int)d.f, s));
-  MOE_TRY(launch_gate_up(w.fs, X, offset, at<int32_t>(ws, w.map1), Wg, Wu, at<void>(ws, w.A),
-                         at<float>(ws, w.part), (int)d.E, (int)d.h, (int)d.f, 1, s));
+    return hip_status(launch_ffn_f32(X, offset, Wg, Wu, Wd, A, Y, d.rows_max, (int)d.E,
+                                     (int)d.h, (int)d.f, s));
+  if (GU)
+    MOE_TRY(launch_gate_up_save(w.fs, X, offset, at<int32_t>(ws, w.map1), Wg, Wu, A, GU,
+                                at<float>(ws, w.part), (int)d.E, (int)d.h, (int)d.f, s));
+  else
+    MOE_TRY(launch_gate_up(w.fs, X, offset, at<int32_t>(ws, w.map1), Wg, Wu, A,
+                           at<float>(ws, w.part), (int)d.E, (int)d.h, (int)d.f, 1, s));
   return MOE_OK;
 }
 
 int32_t run_down(const Dims& d, const FfnWs& w, const int32_t* offset, const void* Wd, void* Y,
-                 void* ws, hipStream_t s) {
+                 void* ws, hipStream_t s, const void* A = nullptr) {
   if (!d.bf16) return MOE_OK;  // the float32 path ran both products already
-  MOE_TRY(launch_down(w.fs, at<void>(ws, w.A), offset, at<int32_t>(ws, w.map2), Wd, Y,
+  MOE_TRY(launch_down(w.fs, A ? A : at<void>(ws, w.A), offset, at<int32_t>(ws, w.map2), Wd, Y,
                       at<float>(ws, w.part), (int)d.E, (int)d.h, (int)d.f, 1, s));
   return MOE_OK;
 }
@@ -627,6 +634,7 @@ int32_t layer_impl(const moe_config* cfg, const void* U, const void* W_r, const 
   if (d.ns > 0 && (!Ws_gate || !Ws_up || !Ws_down)) return MOE_ERR_INVALID_ARG;
   if (cfg->noisy && (!W_noise || !noise)) return MOE_ERR_INVALID_ARG;
   if (d.T > 0 && out == U) return MOE_ERR_INVALID_ARG;
+  if (aux && aux->GU && (!d.bf16 || f8)) return MOE_ERR_UNSUPPORTED;
   if (stage_events)
     for (int i = 0; i <= MOE_NUM_STAGES; ++i)
       if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
@@ -665,12 +673,12 @@ int32_t layer_impl(const moe_config* cfg, const void* U, const void* W_r, const 
   st = run_tile_map(d, w.ffn, offset, ws, s);
   if (st != MOE_OK) return st;
   MOE_TRY(mark(2));
-  st = run_gate_up(d, w.ffn, X, offset, W_gate, W_up, W_down, Y, ws, s, f8);
+  st = run_gate_up(d, w.ffn, X, offset, W_gate, W_up, W_down, Y, ws, s, f8, o.A, o.GU);
   if (st != MOE_OK) return st;
   st = run_shared_gate_up(d, w.sh, U, Ws_gate, Ws_up, Ws_down, Ys, ws, s);
   if (st != MOE_OK) return st;
   MOE_TRY(mark(3));
-  st = run_down(d, w.ffn, offset, W_down, Y, ws, s);
+  st = run_down(d, w.ffn, offset, W_down, Y, ws, s, o.A);
   if (st != MOE_OK) return st;
   st = run_shared_down(d, w.sh, Ws_down, Ys, ws, s);
   if (st != MOE_OK) return st;
@@ -723,8 +731,9 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
                            const float* logits, const int32_t* topk_idx, const float* topk_gate,
                            const int32_t* slot, const int32_t* count, const int32_t* offset,
                            const void* dOut, float alpha, float c_z, void* dU, float* dW_r,
-                           float* db_r, void* dW_gate, void* dW_up, void* dW_down, void* ws,
-                           size_t ws_bytes, void* stream) {
+                           float* db_r, void* dW_gate, void* dW_up, void* dW_down,
+                           const moe_aux_outputs* saved, void* ws, size_t ws_bytes,
+                           void* stream) {
   int32_t st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (cfg->dtype != MOE_BF16 || cfg->noisy || cfg->n_shared > 0) return MOE_ERR_UNSUPPORTED;
@@ -735,16 +744,17 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
   if (d.T > 0 && (!U || !logits || !topk_idx || !topk_gate || !slot || !dOut || !dU))
     return MOE_ERR_INVALID_ARG;
   if (!isfinite(alpha) || !isfinite(c_z)) return MOE_ERR_INVALID_ARG;
+  if (saved && (!saved->X || !saved->GU || !saved->A || !saved->Y)) return MOE_ERR_INVALID_ARG;
   Plan pl;
   const BackwardWs w = plan_backward(d, pl);
   if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int E = (int)d.E, h = (int)d.h, f = (int)d.f, T = (int)d.T, k = (int)d.k;
   const int ncu = device_cus();
-  void* X = at<void>(ws, w.X);
-  void* A = at<void>(ws, w.ffn.A);
-  void* GU = at<void>(ws, w.GU);
-  void* Y = at<void>(ws, w.Y);
+  void* X = saved ? saved->X : at<void>(ws, w.X);
+  void* A = saved ? saved->A : at<void>(ws, w.ffn.A);
+  void* GU = saved ? saved->GU : at<void>(ws, w.GU);
+  void* Y = saved ? saved->Y : at<void>(ws, w.Y);
   void* dY = at<void>(ws, w.dY);
   void* dA = at<void>(ws, w.dA);
   void* dGU = at<void>(ws, w.dGU);
@@ -753,13 +763,17 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
   float* dH = at<float>(ws, w.dH);
   float* part = at<float>(ws, w.part);
   const int32_t* map = at<int32_t>(ws, w.ffn.map1);  // every product uses the same row tiles
-  // 1. recompute the experts: X, then A = SiLU(g) u with g, u kept, then Y
+  // 1. the experts' activations: kept by the forward, or recomputed (X, then
+  // A = SiLU(g) u with g, u kept, then Y)
   st = run_tile_map(d, w.ffn, offset, ws, s);
   if (st != MOE_OK) return st;
-  MOE_TRY(launch_permute(U, slot, X, T, h, k, 1, s));
-  MOE_TRY(launch_gate_up_save(w.ffn.fs, X, offset, map, W_gate, W_up, A, GU, part, E, h, f, s));
-  MOE_TRY(launch_down(w.ffn.fs, A, offset, at<int32_t>(ws, w.ffn.map2), W_down, Y, part, E, h,
-                      f, 1, s));
+  if (!saved) {
+    MOE_TRY(launch_permute(U, slot, X, T, h, k, 1, s));
+    MOE_TRY(launch_gate_up_save(w.ffn.fs, X, offset, map, W_gate, W_up, A, GU, part, E, h, f,
+                                s));
+    MOE_TRY(launch_down(w.ffn.fs, A, offset, at<int32_t>(ws, w.ffn.map2), W_down, Y, part, E, h,
+                        f, 1, s));
+  }
   // 2. combine: dY rows and the gates' gradient
   MOE_TRY(launch_combine_bwd(dOut, Y, slot, topk_gate, dY, dgate, T, h, k, s));
   // 3. dA = dY W_down[e]; SwiGLU backward; dX = [dg du] [W_gate[e]; W_up[e]]: products

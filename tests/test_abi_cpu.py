@@ -220,10 +220,11 @@ def test_backward_argument_checks():
     fake, other = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)
     cfg = cfg_of()
 
-    def bwd(c, *, alpha=0.0, c_z=0.0, U=fake, dW_r=other, dU=other, ws_bytes=1 << 40):
+    def bwd(c, *, alpha=0.0, c_z=0.0, U=fake, dW_r=other, dU=other, ws_bytes=1 << 40,
+            saved=None):
         return status("moe_layer_backward", ctypes.byref(c), U, fake, fake, fake, fake, fake,
                       fake, fake, fake, fake, fake, fake, alpha, c_z, dU, dW_r, None, other,
-                      other, other, fake, ws_bytes, None)
+                      other, other, saved, fake, ws_bytes, None)
 
     # bf16 only, and neither noisy routing nor shared experts
     assert bwd(B.make_config(I.WORKLOADS["tiny_f32"])) == B.MOE_ERR_UNSUPPORTED
@@ -236,6 +237,17 @@ def test_backward_argument_checks():
     for v in (float("nan"), float("inf")):
         assert bwd(cfg, alpha=v) == B.MOE_ERR_INVALID_ARG
         assert bwd(cfg, c_z=v) == B.MOE_ERR_INVALID_ARG
+    # saved activations come as all four of X, GU, A, Y
+    sv = B.moe_aux_outputs()
+    sv.X = sv.GU = sv.A = 0x3000
+    assert bwd(cfg, saved=ctypes.byref(sv)) == B.MOE_ERR_INVALID_ARG  # Y missing
+    # keeping g, u in the forward needs a bf16 layer without FP8
+    a = B.moe_aux_outputs()
+    a.GU = 0x3000
+    f32cfg = B.make_config(I.WORKLOADS["tiny_f32"])
+    assert status("moe_layer_forward", ctypes.byref(f32cfg), fake, fake, None, None, None, None,
+                  fake, fake, fake, None, None, None, other, ctypes.byref(a), None, fake,
+                  1 << 40, None) == B.MOE_ERR_UNSUPPORTED
     # the workspace has its own size
     need = B.workspace_size(cfg, B.MOE_WS_BACKWARD)
     assert need > B.workspace_size(cfg, B.MOE_WS_LAYER)

@@ -40,7 +40,7 @@ def rel(got, ref):
     return np.linalg.norm(got - ref) / (n if n > 0 else 1.0)
 
 
-def run_backward(w, x, g, dOut, alpha, c_z):
+def run_backward(w, x, g, dOut, alpha, c_z, saved=None):
     cfg = B.make_config(w)
     T, h, f, E = w.T, w.h, w.f, w.E
     out = {"dU": torch.empty((T, h), dtype=torch.bfloat16, device=DEV),
@@ -52,7 +52,7 @@ def run_backward(w, x, g, dOut, alpha, c_z):
     B.moe_layer_backward(cfg, x["U"], x["W_r"], x["W_gate"], x["W_up"], x["W_down"], g["logits"],
                          g["topk_idx"], g["topk_gate"], g["slot"], g["count"], g["offset"], dOut,
                          out["dU"], out["dW_r"], out["dW_gate"], out["dW_up"], out["dW_down"],
-                         db_r=out["db_r"], alpha=alpha, c_z=c_z)
+                         db_r=out["db_r"], alpha=alpha, c_z=c_z, saved=saved)
     torch.cuda.synchronize()
     return out
 
@@ -96,6 +96,30 @@ def test_backward(name):
     L.log(f"  errs {errs}")
     for n, v in errs.items():
         assert v <= TOL, (n, v)
+
+
+@pytest.mark.parametrize("name", ["mixtral_drops", "switch_small", "v3_keyed"])
+def test_saved_activations_equal_recompute(name):
+    # the forward keeps X, g | u, a and Y; the backward reading them gives the
+    # same gradients bit for bit as recomputing them, and keeping them leaves
+    # the forward's own outputs unchanged
+    w = BWD[name]
+    x = I.make_inputs(w, seed=1, device=DEV)
+    cfg, g2 = L.run_layer(w, x)
+    plain = [n for n in g2 if n != "out"]
+    cfg, g = L.run_layer(w, x, fields=plain + ["GU", "A"])
+    rows = int(g["offset"][-1])  # row-indexed outputs are defined up to offset[E]
+    for n in plain + ["out"]:
+        if n in ("row_token", "X", "Y"):
+            assert torch.equal(g[n][:rows], g2[n][:rows]), n
+        else:
+            assert torch.equal(g[n], g2[n]), n
+    gen = torch.Generator(device=DEV).manual_seed(9)
+    dOut = torch.randn((w.T, w.h), generator=gen, device=DEV).to(torch.bfloat16)
+    ref = run_backward(w, x, g, dOut, 0.01, 1e-3)
+    got = run_backward(w, x, g, dOut, 0.01, 1e-3, saved={n: g[n] for n in B.SAVED_FIELDS})
+    for n in ref:
+        assert torch.equal(got[n], ref[n]), n
 
 
 def test_backward_alpha_and_z_terms_only():
