@@ -422,7 +422,8 @@ def z_loss_logit_grad(H) -> np.ndarray:
 
 
 def layer_backward(U, W_r, W_gate, W_up, W_down, fwd: dict, dOut, *, score: str, gate: str,
-                   alpha: float = 0.0, c_z: float = 0.0) -> dict:
+                   alpha: float = 0.0, c_z: float = 0.0, W_noise=None, noise=None,
+                   Ws_gate=None, Ws_up=None, Ws_down=None) -> dict:
     """Gradients of L = <dOut, out> + alpha * aux + c_z * L_z for the routing
     in fwd (a layer_forward result).  The top-k choice, the capacity cut and
     the load fractions f are piecewise constant and carry no gradient; a
@@ -430,6 +431,11 @@ def layer_backward(U, W_r, W_gate, W_up, W_down, fwd: dict, dOut, *, score: str,
     renormalisation of the token's other gates.  Every expert product is
     recomputed from the inputs.  Returns dU, dW_r, db_r, dW_gate, dW_up,
     dW_down, and the intermediate dgate [T, k] and dH [T, E].
+
+    Noisy routing (W_noise, noise): the logits' term noise * softplus(U W_noise)
+    passes dH on through softplus' = sigmoid to W_noise and U (dW_noise).
+    Shared experts (Ws_*): each adds SwiGLU(u) with weight 1 to every token,
+    so its output gradient is dOut itself (dWs_gate, dWs_up, dWs_down).
     """
     U, W_r, dOut = f64(U), f64(W_r), f64(dOut)
     Wg, Wu, Wd = f64(W_gate), f64(W_up), f64(W_down)
@@ -494,8 +500,28 @@ def layer_backward(U, W_r, W_gate, W_up, W_down, fwd: dict, dOut, *, score: str,
     if c_z:
         dH += c_z * z_loss_logit_grad(H)
     dU += dH @ W_r.T
-    return {"dU": dU, "dW_r": U.T @ dH, "db_r": dH.sum(axis=0), "dW_gate": dWg, "dW_up": dWu,
-            "dW_down": dWd, "dgate": dgate, "dH": dH}
+    out = {"dU": dU, "dW_r": U.T @ dH, "db_r": dH.sum(axis=0), "dW_gate": dWg, "dW_up": dWu,
+           "dW_down": dWd, "dgate": dgate, "dH": dH}
+    if W_noise is not None:
+        Wn = f64(W_noise)
+        Z = U @ Wn
+        dZ = dH * f64(noise) / (1.0 + np.exp(-Z))
+        out["dW_noise"] = U.T @ dZ
+        dU += dZ @ Wn.T
+    if Ws_gate is not None:
+        Sg, Su, Sd = f64(Ws_gate), f64(Ws_up), f64(Ws_down)
+        out["dWs_gate"], out["dWs_up"] = np.zeros_like(Sg), np.zeros_like(Su)
+        out["dWs_down"] = np.zeros_like(Sd)
+        for i in range(Sg.shape[0]):
+            G, Up = U @ Sg[i].T, U @ Su[i].T
+            dA = dOut @ Sd[i]
+            out["dWs_down"][i] = dOut.T @ (silu(G) * Up)
+            dG = dA * Up * dsilu(G)
+            dUp = dA * silu(G)
+            out["dWs_gate"][i] = dG.T @ U
+            out["dWs_up"][i] = dUp.T @ U
+            dU += dG @ Sg[i] + dUp @ Su[i]
+    return out
 
 
 # --------------------------------------------------------------------------- layer

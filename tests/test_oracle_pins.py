@@ -709,3 +709,52 @@ def test_layer_backward_finite_differences(score, gate, cf):
             am[i][j] -= eps
             fd[j] = (loss(*ap) - loss(*am)) / (2 * eps)
         np.testing.assert_allclose(bw[name], fd, rtol=1e-5, atol=1e-7, err_msg=name)
+
+
+@pytest.mark.parametrize("part", ["noisy", "shared", "v3"])
+def test_layer_backward_finite_differences_parts(part):
+    # the noisy router's softplus branch, shared experts, and the V3 routing
+    # (selection bias, groups) with a shared expert: central differences of
+    # the forward oracle against layer_backward
+    T, h, f, E, k = 6, 4, 3, 4, 2
+    r = rng(23)
+    U = r.normal(0, 1, (T, h))
+    W_r = r.normal(0, 0.8, (h, E))
+    Wg, Wu = r.normal(0, 0.6, (E, f, h)), r.normal(0, 0.6, (E, f, h))
+    Wd = r.normal(0, 0.6, (E, h, f))
+    dOut = r.normal(0, 1, (T, h))
+    alpha, c_z = 0.3, 0.05
+    score = O.SIGMOID if part == "v3" else O.SOFTMAX
+    kw = dict(k=k, score=score, gate=O.GATE_RENORM, capacity_factor=0.8)
+    extra, names = {}, ["dU", "dW_r", "dW_gate", "dW_up", "dW_down"]
+    if part == "noisy":
+        extra = {"W_noise": r.normal(0, 0.8, (h, E)), "noise": r.normal(0, 1, (T, E))}
+        names.append("dW_noise")
+    if part in ("shared", "v3"):
+        extra = {"Ws_gate": r.normal(0, 0.6, (2, 2, h)), "Ws_up": r.normal(0, 0.6, (2, 2, h)),
+                 "Ws_down": r.normal(0, 0.6, (2, h, 2))}
+        names += ["dWs_gate", "dWs_up", "dWs_down"]
+    if part == "v3":
+        kw.update(b_sel=r.normal(0, 0.3, E), n_groups=2, topk_groups=1)
+    keys = ["U", "W_r", "W_gate", "W_up", "W_down"] + [n for n in extra if n != "noise"]
+    base = dict(U=U, W_r=W_r, W_gate=Wg, W_up=Wu, W_down=Wd, **extra)
+
+    def loss(v):
+        o = O.layer_forward(v["U"], v["W_r"], v["W_gate"], v["W_up"], v["W_down"], **kw,
+                            **{n: v[n] for n in extra})
+        return float(np.sum(dOut * o["out"])) + alpha * o["aux"] + c_z * o["z_loss"]
+
+    fwd = O.layer_forward(U, W_r, Wg, Wu, Wd, **kw, **extra)
+    assert fwd["n_dropped"] > 0
+    bw = O.layer_backward(U, W_r, Wg, Wu, Wd, fwd, dOut, score=score, gate=O.GATE_RENORM,
+                          alpha=alpha, c_z=c_z, **extra)
+    eps = 1e-6
+    for key, name in zip(keys, names):
+        fd = np.zeros_like(base[key])
+        for j in np.ndindex(base[key].shape):
+            vp = {n: a.copy() for n, a in base.items()}
+            vm = {n: a.copy() for n, a in base.items()}
+            vp[key][j] += eps
+            vm[key][j] -= eps
+            fd[j] = (loss(vp) - loss(vm)) / (2 * eps)
+        np.testing.assert_allclose(bw[name], fd, rtol=1e-5, atol=1e-7, err_msg=name)
