@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--workload", default="mixtral_bf16")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--backward", action="store_true",
-                    help="time forward + backward (bf16, not noisy, no shared experts)")
+                    help="time forward + backward (bf16 workloads without FP8)")
     ap.add_argument("--recompute", action="store_true",
                     help="with --backward: the forward keeps no activations and the backward "
                          "recomputes them")
@@ -231,9 +231,8 @@ def main():
     ws = B.new_workspace(cfg, B.MOE_WS_LAYER, dev)
     fields = ["kept", "n_dropped", "aux_loss", "maxvio", "z_loss"]
     if args.backward:
-        if w.dtype != "bf16" or w.noisy or w.n_shared or w.fp8_up:
-            print("--backward needs a bf16 workload without noise, shared experts or FP8",
-                  file=sys.stderr)
+        if w.dtype != "bf16" or w.fp8_up:
+            print("--backward needs a bf16 workload without FP8", file=sys.stderr)
             sys.exit(2)
         fields += ["logits", "topk_idx", "topk_gate", "slot", "count", "offset"]
         if not args.recompute:  # the forward keeps X, g | u, a and Y for the backward
@@ -245,6 +244,15 @@ def main():
                  "db_r": torch.empty((w.E,), device=dev),
                  "dW_gate": torch.empty_like(x["W_gate"]), "dW_up": torch.empty_like(x["W_up"]),
                  "dW_down": torch.empty_like(x["W_down"])}
+        extra = {}
+        if w.noisy:
+            extra = {"W_noise": x["W_noise"], "noise": x["noise"],
+                     "dW_noise": torch.empty((w.h, w.E), device=dev)}
+        if w.n_shared:
+            extra.update(Ws_gate=x["Ws_gate"], Ws_up=x["Ws_up"], Ws_down=x["Ws_down"],
+                         dWs_gate=torch.empty_like(x["Ws_gate"]),
+                         dWs_up=torch.empty_like(x["Ws_up"]),
+                         dWs_down=torch.empty_like(x["Ws_down"]))
     aux = B.alloc_aux(cfg, dev, fields)
     out = torch.empty((w.T, w.h), dtype=I.torch_dtype(w), device=dev)
     nst = B.MOE_NUM_STAGES
@@ -270,7 +278,7 @@ def main():
                                  grads["dW_gate"], grads["dW_up"], grads["dW_down"],
                                  db_r=grads["db_r"], alpha=0.01, c_z=1e-3, ws=bws,
                                  saved=(None if args.recompute
-                                        else {n: aux[n] for n in B.SAVED_FIELDS}))
+                                        else {n: aux[n] for n in B.SAVED_FIELDS}), **extra)
             if events is not None:
                 events[-1].record()
 
@@ -361,14 +369,17 @@ def main():
         "stage_gbs": stage_bandwidth(w, stage_ms, kept, e_active, eb),
     }
     if args.backward:
-        # the backward's products: dgrad 6 h f and wgrad 6 h f per kept row
-        # (useful), plus 6 h f of recomputed forward when it recomputes
+        # the backward's products: dgrad 6 h f and wgrad 6 h f per kept row and
+        # per token and shared expert (useful); executed adds the recomputed
+        # forward products (6 h f per kept row when recomputing, and the shared
+        # experts' gate/up, 4 h f_shared per token, always)
+        sh = w.h * w.f_shared * w.T * w.n_shared
+        useful = 12.0 * w.h * w.f * kept + 12.0 * sh
+        executed = useful + (6.0 * w.h * w.f * kept if args.recompute else 0.0) + 4.0 * sh
         res["backward"] = {"ms": bwd_ms, "forward_ms": ms - bwd_ms,
                            "activations": "recomputed" if args.recompute else "kept by the forward",
-                           "mfma_frac_useful": 12.0 * w.h * w.f * kept / (bwd_ms * 1e-3) / 1e12
-                           / PEAK_BF16_TFLOPS,
-                           "mfma_frac_exec": (18.0 if args.recompute else 12.0) * w.h * w.f
-                           * kept / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+                           "mfma_frac_useful": useful / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                           "mfma_frac_exec": executed / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     if not args.no_cpu_baseline and not args.backward:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(w, x, aux, args.cpu_baseline_seconds)

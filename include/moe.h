@@ -261,36 +261,62 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
                           void* stream);
 
 /* ---------------------------------------------------------------- backward
- * Gradients of L = <dOut, out> + alpha * aux_loss + c_z * z_loss with respect
- * to U, W_r, b_r, W_gate, W_up and W_down, for the routing a moe_layer_forward
- * call chose (page "MoE 与专家并行": the gates' gradient is the inner product
- * of the upstream gradient with the expert's output and flows on through the
- * score function, section "路由器：打分、top-k、加权求和", eq. dL/dg; the
- * load-balance term's logit gradient, section "负载均衡辅助损失：推导与梯度"; the
- * z-loss's, section "各家的变体"; the experts as grouped products for inputs
- * and weights, section "专家计算：padding、block-sparse 与 grouped GEMM").  The
- * top-k choice, the capacity cut and the load fractions f carry no gradient.
+ * The parts of the backward that only some layers have (each group NULL when
+ * the layer lacks the part):
+ *  noisy routing (cfg->noisy): W_noise [h,E] and noise [T,E] as given to the
+ *  forward; dW_noise [h,E] float32 out.  The logits' term
+ *  noise * softplus(U W_noise) passes the logit gradient on through
+ *  softplus' = sigmoid (page "MoE 与专家并行", router section, eq. G(x)).
+ *  shared experts (cfg->n_shared > 0): Ws_gate, Ws_up [n_shared,f_shared,h],
+ *  Ws_down [n_shared,h,f_shared] as given to the forward; dWs_gate, dWs_up,
+ *  dWs_down of the same shapes, bf16, out.  Each takes every token with
+ *  weight 1 (section "细粒度专家与共享专家", eq. h'_t), so its output gradient
+ *  is dOut itself. */
+typedef struct {
+  const void* W_noise;
+  const float* noise;
+  float* dW_noise;
+  const void* Ws_gate;
+  const void* Ws_up;
+  const void* Ws_down;
+  void* dWs_gate;
+  void* dWs_up;
+  void* dWs_down;
+} moe_backward_extras;
+
+/* Gradients of L = <dOut, out> + alpha * aux_loss + c_z * z_loss with respect
+ * to U, W_r, b_r, W_gate, W_up and W_down (and W_noise, the shared experts'
+ * weights), for the routing a moe_layer_forward call chose (page
+ * "MoE 与专家并行": the gates' gradient is the inner product of the upstream
+ * gradient with the expert's output and flows on through the score function,
+ * section "路由器：打分、top-k、加权求和", eq. dL/dg; the load-balance term's logit
+ * gradient, section "负载均衡辅助损失：推导与梯度"; the z-loss's, section
+ * "各家的变体"; the experts as grouped products for inputs and weights, section
+ * "专家计算：padding、block-sparse 与 grouped GEMM").  The top-k choice, the
+ * capacity cut and the load fractions f carry no gradient.
  *  Inputs: U, W_r, W_gate, W_up, W_down as given to the forward; from its
  *  outputs (moe_aux_outputs) logits [T,E], topk_idx, topk_gate, slot [T,k],
  *  count [E], offset [E+1]; dOut [T,h] the upstream gradient.  alpha and c_z
  *  scale aux_loss and z_loss (finite; 0 leaves a term out).
- *  saved: NULL, and the experts are recomputed from U with the forward's
- *  kernels (the same values bit for bit); or the forward's aux outputs with
- *  X, GU, A and Y all set (every other field is ignored), which the backward
- *  then reads instead (MOE_ERR_INVALID_ARG if one of the four is NULL).
+ *  saved: NULL, and the routed experts are recomputed from U with the
+ *  forward's kernels (the same values bit for bit); or the forward's aux
+ *  outputs with X, GU, A and Y all set (every other field is ignored), which
+ *  the backward then reads instead (MOE_ERR_INVALID_ARG if one of the four is
+ *  NULL).  Shared experts are always recomputed.
+ *  extra: required (with every pointer of the part) for noisy layers and
+ *  layers with shared experts, else may be NULL.
  *  Outputs: dU [T,h] and dW_gate, dW_up [E,f,h], dW_down [E,h,f] in bf16;
  *  dW_r [h,E] and db_r [E] (nullable) in float32.
- *  Supported: cfg->dtype == MOE_BF16, not noisy, no shared experts (else
- *  MOE_ERR_UNSUPPORTED); the routing may come from a selection bias or
- *  groups.  ws: MOE_WS_BACKWARD bytes. */
+ *  Supported: cfg->dtype == MOE_BF16 (else MOE_ERR_UNSUPPORTED); the routing
+ *  may come from a selection bias or groups.  ws: MOE_WS_BACKWARD bytes. */
 int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r,
                            const void* W_gate, const void* W_up, const void* W_down,
                            const float* logits, const int32_t* topk_idx, const float* topk_gate,
                            const int32_t* slot, const int32_t* count, const int32_t* offset,
                            const void* dOut, float alpha, float c_z, void* dU, float* dW_r,
                            float* db_r, void* dW_gate, void* dW_up, void* dW_down,
-                           const moe_aux_outputs* saved, void* ws, size_t ws_bytes,
-                           void* stream);
+                           const moe_aux_outputs* saved, const moe_backward_extras* extra,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- FP8
  * FP8 dispatch and FP8 up-projection (page "MoE 与专家并行", section

@@ -55,6 +55,12 @@ class moe_aux_outputs(ctypes.Structure):
 
 AUX_FIELDS = [n for n, _ in moe_aux_outputs._fields_]
 
+
+class moe_backward_extras(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "W_noise", "noise", "dW_noise", "Ws_gate", "Ws_up", "Ws_down", "dWs_gate", "dWs_up",
+        "dWs_down")]
+
 _lib = None
 
 
@@ -87,7 +93,7 @@ def lib() -> ctypes.CDLL:
                                                               P, P, SZ, P]),
             "moe_quantize_rows_fp8": (I32, [P, I64, I64, P, P, P]),
             "moe_layer_backward": (I32, [cfgp] + [P] * 12 + [ctypes.c_float, ctypes.c_float]
-                                   + [P] * 7 + [P, SZ, P]),
+                                   + [P] * 8 + [P, SZ, P]),
             "moe_dispatch_fp8": (I32, [cfgp] + [P] * 9 + [P, SZ, P]),
             "moe_expert_ffn_fp8": (I32, [cfgp] + [P] * 9 + [P, SZ, P]),
         }
@@ -409,11 +415,15 @@ def moe_layer_forward_fp8(cfg, U, W_r, b_r, W_noise, noise, W8_gate, s_gate, W8_
 
 def moe_layer_backward(cfg, U, W_r, W_gate, W_up, W_down, logits, topk_idx, topk_gate, slot,
                        count, offset, dOut, dU, dW_r, dW_gate, dW_up, dW_down, db_r=None,
-                       alpha=0.0, c_z=0.0, saved=None, ws=None, stream=None):
+                       alpha=0.0, c_z=0.0, saved=None, W_noise=None, noise=None, dW_noise=None,
+                       Ws_gate=None, Ws_up=None, Ws_down=None, dWs_gate=None, dWs_up=None,
+                       dWs_down=None, ws=None, stream=None):
     """Gradients of <dOut, out> + alpha aux_loss + c_z z_loss for the routing of a
     forward (logits ... offset from its aux outputs).  dU, dW_gate, dW_up,
     dW_down bf16; dW_r [h, E] and db_r [E] float32.  saved: None (the experts
-    are recomputed) or a dict with the forward's aux outputs X, GU, A and Y."""
+    are recomputed) or a dict with the forward's aux outputs X, GU, A and Y.
+    Noisy layers: W_noise, noise as in the forward, dW_noise [h, E] float32.
+    Shared experts: Ws_* as in the forward, dWs_* of the same shapes (bf16)."""
     T, h, f, E, k = cfg.T, cfg.h, cfg.f, cfg.E, cfg.k
     bf = torch.bfloat16
     need = workspace_size(cfg, MOE_WS_BACKWARD)
@@ -439,8 +449,24 @@ def moe_layer_backward(cfg, U, W_r, W_gate, W_up, W_down, logits, topk_idx, topk
         for name in SAVED_FIELDS:
             shape_fn, _ = _AUX_SPEC[name]
             setattr(sv, name, _ptr(saved[name], name, shape_fn(cfg, rows), bf))
+    ex = None
+    if cfg.noisy or cfg.n_shared:
+        ex = moe_backward_extras()
+        ns, fs = cfg.n_shared, cfg.f_shared
+        if cfg.noisy:
+            ex.W_noise = _ptr(W_noise, "W_noise", (h, E), bf)
+            ex.noise = _ptr(noise, "noise", (T, E), torch.float32)
+            ex.dW_noise = _ptr(dW_noise, "dW_noise", (h, E), torch.float32)
+        if ns:
+            ex.Ws_gate = _ptr(Ws_gate, "Ws_gate", (ns, fs, h), bf)
+            ex.Ws_up = _ptr(Ws_up, "Ws_up", (ns, fs, h), bf)
+            ex.Ws_down = _ptr(Ws_down, "Ws_down", (ns, h, fs), bf)
+            ex.dWs_gate = _ptr(dWs_gate, "dWs_gate", (ns, fs, h), bf)
+            ex.dWs_up = _ptr(dWs_up, "dWs_up", (ns, fs, h), bf)
+            ex.dWs_down = _ptr(dWs_down, "dWs_down", (ns, h, fs), bf)
     _check(lib().moe_layer_backward(ctypes.byref(cfg), *args,
-                                    ctypes.byref(sv) if sv is not None else None, wp, wn,
+                                    ctypes.byref(sv) if sv is not None else None,
+                                    ctypes.byref(ex) if ex is not None else None, wp, wn,
                                     _stream(stream)), "moe_layer_backward")
 
 

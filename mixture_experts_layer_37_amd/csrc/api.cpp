@@ -239,6 +239,12 @@ struct BackwardWs {
   FfnWs ffn;  // tile maps, A (the SwiGLU rows), K-split partials
   FfnShape fsA, fsX;  // shapes of the dA (N = f, K = h) and dX (N = h, K = 2f) products
   size_t X, GU, Y, dY, dA, dGU, dX, dgate, dH, part, dwr;
+  size_t dZ;  // noisy routing: [T, E] float32
+  // shared experts: the dense pass's shapes, maps and rows ({0, T}), one
+  // expert's g | u, dA and dG | dU at a time, every expert's a and dX
+  SharedWs sh;
+  FfnShape shA, shX;
+  size_t sGU, sdA, sdGU, sdX;
 };
 BackwardWs plan_backward(const Dims& d, Plan& pl) {
   BackwardWs w;
@@ -257,8 +263,20 @@ BackwardWs plan_backward(const Dims& d, Plan& pl) {
   w.dX = pl.add(rows * d.h * 2);
   w.dgate = pl.add(T1 * d.k * 4);
   w.dH = pl.add(T1 * d.E * 4);
-  // K-split partials for the largest grid of the three row-grouped products
-  const int slots = std::max(w.ffn.fs.part_slots, std::max(w.fsA.part_slots, w.fsX.part_slots));
+  w.dZ = pl.add(T1 * d.E * 4);
+  w.sh = plan_shared(d, false, pl);
+  int slots = std::max(w.ffn.fs.part_slots, std::max(w.fsA.part_slots, w.fsX.part_slots));
+  if (d.ns > 0) {
+    w.shA = ffn_shape(d.T, 1, (int)d.fs, (int)d.h, (int)d.T, 1, 1, ncu);
+    w.shX = ffn_shape(d.T, 1, (int)d.h, (int)(2 * d.fs), (int)d.T, 1, 1, ncu);
+    w.sGU = pl.add(T1 * 2 * d.fs * 2);
+    w.sdA = pl.add(T1 * d.fs * 2);
+    w.sdGU = pl.add(T1 * 2 * d.fs * 2);
+    w.sdX = pl.add((size_t)d.ns * T1 * d.h * 2);
+    slots = std::max(slots, std::max(w.sh.fs.part_slots,
+                                     std::max(w.shA.part_slots, w.shX.part_slots)));
+  }
+  // K-split partials for the largest grid of the row-grouped products
   w.part = pl.add((size_t)slots * kPartSlotBytes);
   w.dwr = pl.add(dwr_part_bytes(d.T, (int)d.h, (int)d.E));
   return w;
@@ -732,11 +750,18 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
                            const int32_t* slot, const int32_t* count, const int32_t* offset,
                            const void* dOut, float alpha, float c_z, void* dU, float* dW_r,
                            float* db_r, void* dW_gate, void* dW_up, void* dW_down,
-                           const moe_aux_outputs* saved, void* ws, size_t ws_bytes,
-                           void* stream) {
+                           const moe_aux_outputs* saved, const moe_backward_extras* extra,
+                           void* ws, size_t ws_bytes, void* stream) {
   int32_t st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (cfg->dtype != MOE_BF16 || cfg->noisy || cfg->n_shared > 0) return MOE_ERR_UNSUPPORTED;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (cfg->noisy && (!extra || !extra->W_noise || !extra->dW_noise ||
+                     (cfg->T > 0 && !extra->noise)))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->n_shared > 0 &&
+      (!extra || !extra->Ws_gate || !extra->Ws_up || !extra->Ws_down || !extra->dWs_gate ||
+       !extra->dWs_up || !extra->dWs_down))
+    return MOE_ERR_INVALID_ARG;
   const Dims d = dims_of(cfg);
   if (!W_r || !W_gate || !W_up || !W_down || !count || !offset || !dW_r || !dW_gate ||
       !dW_up || !dW_down || !ws)
@@ -787,11 +812,52 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
   MOE_TRY(launch_wgrad(dGU, 2 * f, X, h, offset, dW_gate, E, f, h, ncu, s));
   MOE_TRY(launch_wgrad(static_cast<char*>(dGU) + (size_t)f * 2, 2 * f, X, h, offset, dW_up, E, f,
                        h, ncu, s));
-  // 5. router: dH, then dU and dW_r, db_r
+  // 5. shared experts (every token, weight 1): recomputed g | u and a, then
+  // the same products with offsets {0, T}
+  const int ns = (int)d.ns, fsh = (int)d.fs;
+  void* sdX = ns > 0 ? at<void>(ws, w.sdX) : nullptr;
+  if (ns > 0) {  // with T = 0 the weight gradients come out zero
+    int32_t* offs = at<int32_t>(ws, w.sh.offs);
+    const int32_t* smap = at<int32_t>(ws, w.sh.map1);  // bm1 == bm2 for one expert of T rows
+    MOE_TRY(launch_dense_offsets(T, offs, s));
+    MOE_TRY(launch_tile_map(offs, 1, w.sh.fs.bm1, w.sh.fs.bm2, at<int32_t>(ws, w.sh.map1),
+                            at<int32_t>(ws, w.sh.map2), s));
+    void* sGU = at<void>(ws, w.sGU);
+    void* sdA = at<void>(ws, w.sdA);
+    void* sdGU = at<void>(ws, w.sdGU);
+    const size_t fh = (size_t)fsh * h, tf = (size_t)T * fsh, th = (size_t)T * h;
+    for (int i = 0; i < ns; ++i) {
+      const char* Wsg = static_cast<const char*>(extra->Ws_gate) + i * fh * 2;
+      const char* Wsu = static_cast<const char*>(extra->Ws_up) + i * fh * 2;
+      const char* Wsd = static_cast<const char*>(extra->Ws_down) + i * fh * 2;
+      char* sA = at<char>(ws, w.sh.A) + i * tf * 2;
+      char* dXi = static_cast<char*>(sdX) + i * th * 2;
+      MOE_TRY(launch_gate_up_save(w.sh.fs, U, offs, smap, Wsg, Wsu, sA, sGU, part, 1, h, fsh,
+                                  s));
+      MOE_TRY(launch_dgrad(w.shA, dOut, offs, smap, Wsd, Wsd, h, sdA, part, 1, fsh, h, s));
+      MOE_TRY(launch_swiglu_bwd(sdA, sGU, offs, 1, T, fsh, sdGU, s));
+      MOE_TRY(launch_dgrad(w.shX, sdGU, offs, smap, Wsg, Wsu, fsh, dXi, part, 1, h, 2 * fsh, s));
+      MOE_TRY(launch_wgrad(dOut, h, sA, fsh, offs, static_cast<char*>(extra->dWs_down) + i * fh * 2,
+                           1, h, fsh, ncu, s));
+      MOE_TRY(launch_wgrad(sdGU, 2 * fsh, U, h, offs,
+                           static_cast<char*>(extra->dWs_gate) + i * fh * 2, 1, fsh, h, ncu, s));
+      MOE_TRY(launch_wgrad(static_cast<char*>(sdGU) + (size_t)fsh * 2, 2 * fsh, U, h, offs,
+                           static_cast<char*>(extra->dWs_up) + i * fh * 2, 1, fsh, h, ncu, s));
+    }
+  }
+  // 6. router: dH (and dZ for the noise term), then dU and dW_r, db_r (dW_noise)
   MOE_TRY(launch_router_bwd(logits, topk_idx, topk_gate, dgate, count, T, E, k, cfg->score,
                             cfg->gate == MOE_GATE_RENORM, alpha, c_z, dH, s));
-  MOE_TRY(launch_grad_input(dOut, dX, slot, dH, W_r, dU, T, h, E, k, s));
+  float* dZ = nullptr;
+  if (cfg->noisy) {
+    dZ = at<float>(ws, w.dZ);
+    MOE_TRY(launch_noise_grad(U, extra->W_noise, dH, extra->noise, dZ, T, h, E, s));
+  }
+  MOE_TRY(launch_grad_input(dOut, dX, slot, dH, W_r, dZ, cfg->noisy ? extra->W_noise : nullptr,
+                            sdX, T > 0 ? ns : 0, dU, T, h, E, k, s));
   MOE_TRY(launch_dwr(U, dH, dW_r, db_r, at<float>(ws, w.dwr), T, h, E, s));
+  if (cfg->noisy)
+    MOE_TRY(launch_dwr(U, dZ, extra->dW_noise, nullptr, at<float>(ws, w.dwr), T, h, E, s));
   return MOE_OK;
 }
 

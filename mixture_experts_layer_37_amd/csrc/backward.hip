@@ -185,16 +185,19 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* logits, co
   }
 }
 
-// dU = dOut + sum over kept ranks of dX[slot] + dH W_r^T.  A workgroup
-// takes 64 tokens x 128 columns j (a thread 4 tokens x 8 consecutive columns,
-// so dOut, dX and dU move 16 bytes at a time); the product over the experts
-// runs in chunks of 32 with dH^T and W_r^T staged in LDS as float32.
+// dU = dOut + sum over kept ranks of dX[slot] + dH W_r^T (+ dZ W_noise^T
+// for noisy routing, + the shared experts' dXs[i]).  A workgroup takes 64
+// tokens x 128 columns j (a thread 4 tokens x 8 consecutive columns, so dOut,
+// dX and dU move 16 bytes at a time); the products over the experts run in
+// chunks of 32 with dH^T and W_r^T staged in LDS as float32.
 constexpr int kGiT = 64, kGiJ = 128, kGiK = 32;
 
 __global__ __launch_bounds__(256) void grad_input_kernel(const bf16* dOut, const bf16* dX,
                                                          const int32_t* slot, const float* dH,
-                                                         const bf16* W_r, bf16* dU, int T, int h,
-                                                         int E, int k) {
+                                                         const bf16* W_r, const float* dZ,
+                                                         const bf16* W_n, const bf16* dXs,
+                                                         int ns, bf16* dU, int T, int h, int E,
+                                                         int k) {
   __shared__ __align__(16) float sh[kGiK][kGiT];  // sh[e][t] = dH[t0 + t][e0 + e]
   __shared__ __align__(16) float sw[kGiK][kGiJ];  // sw[e][j] = W_r[j0 + j][e0 + e]
   const int t0 = blockIdx.x * kGiT, j0 = blockIdx.y * kGiJ;
@@ -204,15 +207,21 @@ __global__ __launch_bounds__(256) void grad_input_kernel(const bf16* dOut, const
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[i][q] = 0.f;
-  for (int e0 = 0; e0 < E; e0 += kGiK) {
-    const int kc = min(kGiK, E - e0);
+  // the experts of (dH, W_r), then those of (dZ, W_noise), kGiK at a time
+  const int chunks = (E + kGiK - 1) / kGiK;
+  for (int c = 0; c < (dZ ? 2 * chunks : chunks); ++c) {
+    const bool second = c >= chunks;
+    const float* D = second ? dZ : dH;
+    const bf16* W = second ? W_n : W_r;
+    const int eb = (second ? c - chunks : c) * kGiK;
+    const int kc = min(kGiK, E - eb);
     for (int i = threadIdx.x; i < kGiT * kGiK; i += 256) {
-      const int tt = i / kGiK, ee = i % kGiK, t = t0 + tt, e = e0 + ee;
-      sh[ee][tt] = (t < T && ee < kc) ? dH[(size_t)t * E + e] : 0.f;
+      const int tt = i / kGiK, ee = i % kGiK, t = t0 + tt, e = eb + ee;
+      sh[ee][tt] = (t < T && ee < kc) ? D[(size_t)t * E + e] : 0.f;
     }
     for (int i = threadIdx.x; i < kGiJ * kGiK; i += 256) {
       const int jj = i / kGiK, ee = i % kGiK, j = j0 + jj;
-      sw[ee][jj] = (j < h && ee < kc) ? bf16_to_f32(W_r[(size_t)j * E + e0 + ee]) : 0.f;
+      sw[ee][jj] = (j < h && ee < kc) ? bf16_to_f32(W[(size_t)j * E + eb + ee]) : 0.f;
     }
     __syncthreads();
 #pragma unroll 4
@@ -246,7 +255,73 @@ __global__ __launch_bounds__(256) void grad_input_kernel(const bf16* dOut, const
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] += x[q];
     }
+    for (int i2 = 0; i2 < ns; ++i2) {
+      Elem<bf16>::unpack(ld16(dXs + ((size_t)i2 * T + t) * h + j), x);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] += x[q];
+    }
     st16(dU + (size_t)t * h + j, Elem<bf16>::pack(v));
+  }
+}
+
+// Noisy routing: the logits hold noise * softplus(Z) with Z = U W_noise, so
+// dZ = dH * noise * sigmoid(Z) (softplus' = sigmoid; page "MoE 与专家并行",
+// router section, eq. G(x)).  Z is recomputed in float32: a workgroup takes
+// 64 tokens x 64 experts, stages 32 columns of U (transposed) and of W_noise
+// at a time in LDS, and a thread accumulates 4 tokens x 4 experts.
+__global__ __launch_bounds__(256) void noise_grad_kernel(const bf16* U, const bf16* W_n,
+                                                         const float* dH, const float* noise,
+                                                         float* dZ, int T, int h, int E) {
+  __shared__ __align__(16) float su[32][64];  // su[j][t] = U[t0 + t][j0 + j]
+  __shared__ __align__(16) float sw[32][64];  // sw[j][e] = W_noise[j0 + j][e0 + e]
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;  // 4 experts, 4 tokens
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[i][q] = 0.f;
+  for (int j0 = 0; j0 < h; j0 += 32) {  // h is a multiple of 64
+    {
+      const int tt = threadIdx.x >> 2, jj = (threadIdx.x & 3) * 8, t = t0 + tt;
+      float v[8];
+      if (t < T) {
+        Elem<bf16>::unpack(ld16(U + (size_t)t * h + j0 + jj), v);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) su[jj + q][tt] = v[q];
+    }
+    for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+      const int jj = i >> 6, ee = i & 63, e = e0 + ee;
+      sw[jj][ee] = e < E ? bf16_to_f32(W_n[(size_t)(j0 + jj) * E + e]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int jj = 0; jj < 32; ++jj) {
+      const float4 a = *reinterpret_cast<const float4*>(&su[jj][ty * 4]);
+      const float4 b = *reinterpret_cast<const float4*>(&sw[jj][tx * 4]);
+      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q] = fmaf(av[i], bv[q], acc[i][q]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + ty * 4 + i;
+    if (t >= T) break;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = e0 + tx * 4 + q;
+      if (e >= E) break;
+      const size_t o = (size_t)t * E + e;
+      dZ[o] = dH[o] * noise[o] / (1.f + __expf(-acc[i][q]));
+    }
   }
 }
 
@@ -371,13 +446,24 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const floa
 }
 
 hipError_t launch_grad_input(const void* dOut, const void* dX, const int32_t* slot,
-                             const float* dH, const void* W_r, void* dU, int T, int h, int E,
-                             int k, hipStream_t s) {
+                             const float* dH, const void* W_r, const float* dZ,
+                             const void* W_noise, const void* dXs, int ns, void* dU, int T, int h,
+                             int E, int k, hipStream_t s) {
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(grad_input_kernel, dim3((T + kGiT - 1) / kGiT, (h + kGiJ - 1) / kGiJ),
                      dim3(256), 0, s, static_cast<const bf16*>(dOut),
-                     static_cast<const bf16*>(dX), slot, dH, static_cast<const bf16*>(W_r),
+                     static_cast<const bf16*>(dX), slot, dH, static_cast<const bf16*>(W_r), dZ,
+                     static_cast<const bf16*>(W_noise), static_cast<const bf16*>(dXs), ns,
                      static_cast<bf16*>(dU), T, h, E, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_noise_grad(const void* U, const void* W_noise, const float* dH,
+                             const float* noise, float* dZ, int T, int h, int E, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(noise_grad_kernel, dim3((T + 63) / 64, (E + 63) / 64), dim3(256), 0, s,
+                     static_cast<const bf16*>(U), static_cast<const bf16*>(W_noise), dH, noise,
+                     dZ, T, h, E);
   return hipGetLastError();
 }
 

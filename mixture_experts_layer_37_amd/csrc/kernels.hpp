@@ -166,9 +166,15 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const floa
                              const float* dgate, const int32_t* count, int T, int E, int k,
                              int score, int renorm, float alpha, float c_z, float* dH,
                              hipStream_t s);
+// dU = dOut + sum_r dX[slot] + dH W_r^T (+ dZ W_noise^T when dZ is set)
+// (+ sum over the ns shared experts of dXs[i], dXs [ns][T][h]).
 hipError_t launch_grad_input(const void* dOut, const void* dX, const int32_t* slot,
-                             const float* dH, const void* W_r, void* dU, int T, int h, int E,
-                             int k, hipStream_t s);
+                             const float* dH, const void* W_r, const float* dZ,
+                             const void* W_noise, const void* dXs, int ns, void* dU, int T, int h,
+                             int E, int k, hipStream_t s);
+// dZ = dH * noise * sigmoid(U W_noise), [T][E] float32.
+hipError_t launch_noise_grad(const void* U, const void* W_noise, const float* dH,
+                             const float* noise, float* dZ, int T, int h, int E, hipStream_t s);
 // dW_r = U^T dH, db_r = column sums of dH: TE experts x TJ rows of U per
 // workgroup, the tokens cut into nsplit chunks of tchunk (a multiple of 16)
 // whose float32 partials [nsplit][h + 1][E] are summed afterwards.

@@ -221,15 +221,23 @@ def test_backward_argument_checks():
     cfg = cfg_of()
 
     def bwd(c, *, alpha=0.0, c_z=0.0, U=fake, dW_r=other, dU=other, ws_bytes=1 << 40,
-            saved=None):
+            saved=None, extra=None):
         return status("moe_layer_backward", ctypes.byref(c), U, fake, fake, fake, fake, fake,
                       fake, fake, fake, fake, fake, fake, alpha, c_z, dU, dW_r, None, other,
-                      other, other, saved, fake, ws_bytes, None)
+                      other, other, saved, extra, fake, ws_bytes, None)
 
-    # bf16 only, and neither noisy routing nor shared experts
+    # bf16 only
     assert bwd(B.make_config(I.WORKLOADS["tiny_f32"])) == B.MOE_ERR_UNSUPPORTED
-    assert bwd(cfg_of(noisy=True)) == B.MOE_ERR_UNSUPPORTED
-    assert bwd(cfg_of(n_shared=1, f_shared=64)) == B.MOE_ERR_UNSUPPORTED
+    # noisy routing and shared experts need their parts of the extras
+    ex = B.moe_backward_extras()
+    assert bwd(cfg_of(noisy=True)) == B.MOE_ERR_INVALID_ARG
+    assert bwd(cfg_of(noisy=True), extra=ctypes.byref(ex)) == B.MOE_ERR_INVALID_ARG
+    ex.W_noise, ex.noise = 0x3000, 0x3000
+    assert bwd(cfg_of(noisy=True), extra=ctypes.byref(ex)) == B.MOE_ERR_INVALID_ARG  # dW_noise
+    scfg = cfg_of(n_shared=1, f_shared=64)
+    assert bwd(scfg) == B.MOE_ERR_INVALID_ARG
+    ex.Ws_gate = ex.Ws_up = ex.Ws_down = ex.dWs_gate = ex.dWs_up = 0x3000
+    assert bwd(scfg, extra=ctypes.byref(ex)) == B.MOE_ERR_INVALID_ARG  # dWs_down missing
     # missing pointers and non-finite loss weights
     assert bwd(cfg, U=None) == B.MOE_ERR_INVALID_ARG
     assert bwd(cfg, dU=None) == B.MOE_ERR_INVALID_ARG

@@ -43,6 +43,16 @@ def rel(got, ref):
 def run_backward(w, x, g, dOut, alpha, c_z, saved=None):
     cfg = B.make_config(w)
     T, h, f, E = w.T, w.h, w.f, w.E
+    extra = {}
+    if w.noisy:
+        extra = {"W_noise": x["W_noise"], "noise": x["noise"],
+                 "dW_noise": torch.empty((h, E), dtype=torch.float32, device=DEV)}
+    if w.n_shared:
+        ns, fs = w.n_shared, w.f_shared
+        extra.update(Ws_gate=x["Ws_gate"], Ws_up=x["Ws_up"], Ws_down=x["Ws_down"],
+                     dWs_gate=torch.empty((ns, fs, h), dtype=torch.bfloat16, device=DEV),
+                     dWs_up=torch.empty((ns, fs, h), dtype=torch.bfloat16, device=DEV),
+                     dWs_down=torch.empty((ns, h, fs), dtype=torch.bfloat16, device=DEV))
     out = {"dU": torch.empty((T, h), dtype=torch.bfloat16, device=DEV),
            "dW_r": torch.empty((h, E), dtype=torch.float32, device=DEV),
            "db_r": torch.empty((E,), dtype=torch.float32, device=DEV),
@@ -52,8 +62,9 @@ def run_backward(w, x, g, dOut, alpha, c_z, saved=None):
     B.moe_layer_backward(cfg, x["U"], x["W_r"], x["W_gate"], x["W_up"], x["W_down"], g["logits"],
                          g["topk_idx"], g["topk_gate"], g["slot"], g["count"], g["offset"], dOut,
                          out["dU"], out["dW_r"], out["dW_gate"], out["dW_up"], out["dW_down"],
-                         db_r=out["db_r"], alpha=alpha, c_z=c_z, saved=saved)
+                         db_r=out["db_r"], alpha=alpha, c_z=c_z, saved=saved, **extra)
     torch.cuda.synchronize()
+    out.update({n: t for n, t in extra.items() if n.startswith("d")})
     return out
 
 
@@ -285,3 +296,53 @@ def test_full_size_input_and_router_gradients(full_cases):
     L.log(f"  errs {errs}")
     for n, v in errs.items():
         assert v <= TOL, (n, v)
+
+
+EXTRA = {
+    "noisy_small": L.SMALL["noisy_small"],
+    "shared2": L.SMALL["mixtral_small"].replace(name="shared2", n_shared=2, f_shared=128,
+                                                capacity_factor=0.8),
+    "v3_full_small": L.SMALL["deepseek_small"].replace(name="v3_full_small", n_groups=8,
+                                                       topk_groups=4, sel_bias_var=1e-4,
+                                                       n_shared=1, f_shared=192),
+}
+
+
+@pytest.mark.parametrize("name", list(EXTRA))
+def test_backward_noisy_and_shared(name):
+    w = EXTRA[name]
+    L.log(f"[bwd extra] {name} {w}")
+    x = I.make_inputs(w, seed=3, device=DEV)
+    cfg, g = L.run_layer(w, x)
+    gen = torch.Generator(device=DEV).manual_seed(10)
+    dOut = torch.randn((w.T, w.h), generator=gen, device=DEV).to(torch.bfloat16)
+    alpha, c_z = 0.01, 1e-3
+    got = run_backward(w, x, g, dOut, alpha, c_z)
+    kw = {}
+    if w.noisy:
+        kw.update(W_noise=L.f64(x["W_noise"]), noise=L.f64(x["noise"]))
+    if w.n_shared:
+        kw.update(Ws_gate=L.f64(x["Ws_gate"]), Ws_up=L.f64(x["Ws_up"]),
+                  Ws_down=L.f64(x["Ws_down"]))
+    ref = O.layer_backward(L.f64(x["U"]), L.f64(x["W_r"]), L.f64(x["W_gate"]), L.f64(x["W_up"]),
+                           L.f64(x["W_down"]), oracle_routing(w, g), L.f64(dOut),
+                           score=L.ORACLE_MODE[w.score], gate=L.ORACLE_MODE[w.gate],
+                           alpha=alpha, c_z=c_z, **kw)
+    names = ["dU", "dW_r", "db_r", "dW_gate", "dW_up", "dW_down"]
+    names += ["dW_noise"] if w.noisy else []
+    names += ["dWs_gate", "dWs_up", "dWs_down"] if w.n_shared else []
+    errs = {n: rel(L.f64(got[n]), ref[n]) for n in names}
+    L.log(f"  errs {errs}")
+    for n, v in errs.items():
+        assert v <= TOL, (n, v)
+
+
+def test_backward_empty_batch_with_shared_experts():
+    # T = 0: every weight gradient is exactly zero
+    w = EXTRA["v3_full_small"].replace(name="v3_empty", T=0)
+    x = I.make_inputs(w, seed=3, device=DEV)
+    cfg, g = L.run_layer(w, x)
+    dOut = torch.zeros((0, w.h), dtype=torch.bfloat16, device=DEV)
+    got = run_backward(w, x, g, dOut, 0.01, 1e-3)
+    for n in ("dW_r", "db_r", "dW_gate", "dW_up", "dW_down", "dWs_gate", "dWs_up", "dWs_down"):
+        assert not got[n].any(), n
