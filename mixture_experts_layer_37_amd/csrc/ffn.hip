@@ -253,6 +253,57 @@ struct Ring {
   bf16* b[3];
 };
 
+// Epilogue through LDS (weight gradients, whose tiles have few K steps and
+// whose 256 x 256 outputs are the bulk of the kernel's traffic).  After the K
+// loop the ring is idle: its slots A0, A1, B0, B1 hold the tile's rows 0-63,
+// 64-127, 128-191, 192-255 as bf16, 512 bytes a row, 16-byte chunk c of row r
+// at c ^ (r mod 32) (the 32 rows a wave writes at once then fall into
+// different banks).  Each wave then stores 32 whole rows, two per
+// instruction, 16 bytes per lane, so every store covers full cache lines.
+template <int BM, int NW>
+__device__ __forceinline__ void store_tile_staged(const GemmParams& p,
+                                                  const floatx16 (&acc)[(2 * BM / NW) / 32][4],
+                                                  const TileAt& ta, const Ring& L) {
+  static_assert(BM == 256 && NW == 8, "staged epilogue: 256 x 256 tiles, 8 waves");
+  constexpr int RBLK = 2;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, kh = lane >> 5;
+  char* const slot[4] = {reinterpret_cast<char*>(L.a[0]), reinterpret_cast<char*>(L.a[1]),
+                         reinterpret_cast<char*>(L.b[0]), reinterpret_cast<char*>(L.b[1])};
+  char* const mine = slot[wm];  // rows wm * 64 .. + 63
+#pragma unroll
+  for (int i = 0; i < RBLK; ++i) {
+    const int r = i * 32 + l32;  // row within the slot; r mod 32 = l32
+    char* rowp = mine + r * 512;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = wn * 16 + j * 4 + g;  // logical chunk: columns 8c .. 8c + 7
+        *reinterpret_cast<uint2*>(rowp + ((c ^ l32) * 16) + 8 * kh) =
+            make_uint2(pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                       pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
+      }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  barrier_only();
+  // wave w stores rows 32 w .. 32 w + 31 (in slot w / 2)
+  const char* src = slot[wm];
+  const int col = ta.nt * BN + l32 * 8;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int rr = (wave & 1) * 32 + 2 * q + kh;  // row within the slot
+    const int r = wm * 64 + rr;                   // row within the tile
+    const uint4 v = *reinterpret_cast<const uint4*>(src + rr * 512 + ((l32 ^ (rr & 31)) * 16));
+    if (r < ta.nvalid && col < p.Nout)
+      *reinterpret_cast<uint4*>(p.C + (size_t)(ta.row0 + r) * p.Nout + col) = v;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  barrier_only();  // the slots are free for the next unit's copies
+}
+
 // Copy sources of one unit of work (a tile, or one K chunk of a tail tile):
 // buffer resources over its valid A rows and its weight panels, and its range
 // of K steps.  A's resource ends at the last valid row, so copies of
@@ -261,7 +312,9 @@ struct Ring {
 struct TileSrc {
   __amdgpu_buffer_rsrc_t rA, rB0, rB1;
   int kbeg, KT;
-  int kt0;  // BT: K steps taken from W0 (the later ones come from W1)
+  int kt0;   // BT: K steps taken from W0 (the later ones come from W1)
+  int klast; // copies of steps past the end reload step klast (in bounds,
+             // never read), so that every step issues the same copies
 };
 template <bool GATEUP, bool F8, bool BT = false>
 __device__ __forceinline__ TileSrc tile_src(const GemmParams& p, const TileAt& ta,
@@ -279,6 +332,7 @@ __device__ __forceinline__ TileSrc tile_src(const GemmParams& p, const TileAt& t
     s.kbeg = ksp.kbeg;
     s.KT = ksp.ksteps;
     s.kt0 = p.K0 / BK;
+    s.klast = s.KT - 1;
     return s;
   }
   const size_t rb = (size_t)p.K * Elt<F8>::kBytes;  // bytes per row
@@ -292,6 +346,7 @@ __device__ __forceinline__ TileSrc tile_src(const GemmParams& p, const TileAt& t
                  : s.rB0;
   s.kbeg = ksp.kbeg;
   s.KT = ksp.ksteps;
+  s.klast = s.KT - 1;
   return s;
 }
 
@@ -353,13 +408,13 @@ struct CopyPlan {
   // step j past the end reloads the last step (in bounds, never read), so
   // every step issues the same number of copies
   __device__ __forceinline__ void issueA(const TileSrc& s, bf16* as, int j) const {
-    const int kb = (s.kbeg + min(j, s.KT - 1)) * (AT ? astep : 128);
+    const int kb = (s.kbeg + min(j, s.klast)) * (AT ? astep : 128);
 #pragma unroll
     for (int q = 0; q < AG; ++q) dma16(s.rA, as + (wave + NW * q) * 8 * BK, voA[q], kb);
   }
   __device__ __forceinline__ void issueB(const TileSrc& s, bf16* bs, int j) const {
     if constexpr (BT) {
-      const int st = s.kbeg + min(j, s.KT - 1);
+      const int st = s.kbeg + min(j, s.klast);
       const bool second = st >= s.kt0;
       const int kb = (second ? st - s.kt0 : st) * bstep;
 #pragma unroll
@@ -367,7 +422,7 @@ struct CopyPlan {
         dma16(second ? s.rB1 : s.rB0, bs + (wave + NW * q) * 8 * BK, voB[q], kb);
       return;
     }
-    const int kb = (s.kbeg + min(j, s.KT - 1)) * 128;
+    const int kb = (s.kbeg + min(j, s.klast)) * 128;
 #pragma unroll
     for (int q = 0; q < BG; ++q)
       dma16((GATEUP && q >= BG / 2) ? s.rB1 : s.rB0, bs + (wave + NW * q) * 8 * BK, voB[q], kb);
@@ -389,7 +444,7 @@ struct CopyPlan {
 // (their accumulators stay zero and their rows are never stored) but issues
 // the same copies and meets the same barriers as the rest of the workgroup.
 template <int BM, int NW, bool GATEUP, bool F8, int R, int NA, int NB, bool BT, bool AT,
-          class Next>
+          bool STAGED, class Next>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p,
                                           const CopyPlan<BM, NW, GATEUP, F8, BT, AT>& cp,
                                           const TileSrc& src, const Ring& L, const TileAt& ta,
@@ -571,7 +626,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p,
   wait_vm<0>();  // copies past the end are still in flight
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   barrier_only();  // every wave is done with LDS
-  next();          // the next unit's first copies go out before this epilogue
+  if constexpr (STAGED) {  // the epilogue uses the ring; the next copies follow it
+    store_tile_staged<BM, NW>(p, acc, ta, L);
+    next();
+    return;
+  }
+  next();  // the next unit's first copies go out before this epilogue
 
   if (ksp.ks > 1) {  // a K chunk of a tail tile: leave the partial to the reduction
 #pragma unroll
@@ -654,13 +714,14 @@ __device__ __forceinline__ void grouped_gemm(const GemmParams& p, const Ring& L)
     // hold valid rows (rows past nvalid read zero and are not stored)
     const int act = min(RBLK, max(0, (cur.ta.nvalid - wm * (RBLK * 32) + 31) / 32));
     if (act >= RBLK)
-      gemm_tile<BM, NW, GATEUP, F8, RBLK, NA, NB, BT, false>(p, cp, src, L, cur.ta, cur.ksp,
-                                                             next);
+      gemm_tile<BM, NW, GATEUP, F8, RBLK, NA, NB, BT, false, false>(p, cp, src, L, cur.ta,
+                                                                    cur.ksp, next);
     else if (RBLK > 1 && act == 1)
-      gemm_tile<BM, NW, GATEUP, F8, (RBLK > 1 ? 1 : 0), NA, NB, BT, false>(p, cp, src, L, cur.ta,
-                                                                          cur.ksp, next);
+      gemm_tile<BM, NW, GATEUP, F8, (RBLK > 1 ? 1 : 0), NA, NB, BT, false, false>(
+          p, cp, src, L, cur.ta, cur.ksp, next);
     else
-      gemm_tile<BM, NW, GATEUP, F8, 0, NA, NB, BT, false>(p, cp, src, L, cur.ta, cur.ksp, next);
+      gemm_tile<BM, NW, GATEUP, F8, 0, NA, NB, BT, false, false>(p, cp, src, L, cur.ta, cur.ksp,
+                                                                 next);
     if (!more) break;
     u = un;
     cur = nxt;
@@ -735,6 +796,9 @@ __device__ __forceinline__ TileSrc wgrad_src(const GemmParams& p, const Unit& w)
   s.kbeg = 0;
   s.KT = w.ksp.ksteps;
   s.kt0 = 1 << 30;  // one panel
+  // past the expert's last row both resources read zeros without touching
+  // memory, so the copies past the end are left unclamped
+  s.klast = 1 << 30;
   return s;
 }
 template <int NA, int NB>
@@ -743,8 +807,21 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_kernel(GemmParams p) {
   MOE_GEMM_LDS_RING
   const int mt_n = (p.M + BM - 1) / BM, nt_n = (p.N + BN - 1) / BN;
   const int units = p.E * mt_n * nt_n;
-  int u = blockIdx.x;
-  if (u >= units) return;
+  // with a grid of whole XCDs (workgroup i runs on XCD i % 8), each XCD takes
+  // a contiguous slice of the tiles, so the tiles of one expert, which share
+  // its row panels, run in one L2; otherwise round-robin
+  int u, uend, ustep;
+  if ((gridDim.x & 7) == 0) {
+    const int per = (units + 7) >> 3, xcd = blockIdx.x & 7;
+    u = xcd * per + (blockIdx.x >> 3);
+    uend = min(units, xcd * per + per);
+    ustep = gridDim.x >> 3;
+  } else {
+    u = blockIdx.x;
+    uend = units;
+    ustep = gridDim.x;
+  }
+  if (u >= uend) return;
   // A [rows][K = lda], B [rows][Nout = ldb]
   const CopyPlan<BM, NW, false, false, true, true> cp(0, p.Nout, p.K);
   Unit cur = wgrad_unit(p, u, mt_n, nt_n);
@@ -754,8 +831,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_kernel(GemmParams p) {
   for (;;) {
     wait_vm<0>();
     barrier_only();
-    const int un = u + (int)gridDim.x;
-    const bool more = un < units;
+    const int un = u + ustep;
+    const bool more = un < uend;
     const Unit nxt = more ? wgrad_unit(p, un, mt_n, nt_n) : cur;
     auto next = [&]() {
       if (more) cp.template prologue<NA, NB>(wgrad_src(p, nxt), L);
@@ -769,13 +846,13 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_kernel(GemmParams p) {
     out.ksp = KSplit{0, cur.ksp.ksteps, 1, nullptr};
     const int act = min(RBLK, max(0, (cur.ta.nvalid - wm * (RBLK * 32) + 31) / 32));
     if (act >= RBLK)
-      gemm_tile<BM, NW, false, false, RBLK, NA, NB, true, true>(q, cp, src, L, out.ta, out.ksp,
+      gemm_tile<BM, NW, false, false, RBLK, NA, NB, true, true, true>(q, cp, src, L, out.ta, out.ksp,
                                                                 next);
     else if (act == 1)
-      gemm_tile<BM, NW, false, false, 1, NA, NB, true, true>(q, cp, src, L, out.ta, out.ksp,
+      gemm_tile<BM, NW, false, false, 1, NA, NB, true, true, true>(q, cp, src, L, out.ta, out.ksp,
                                                              next);
     else
-      gemm_tile<BM, NW, false, false, 0, NA, NB, true, true>(q, cp, src, L, out.ta, out.ksp,
+      gemm_tile<BM, NW, false, false, 0, NA, NB, true, true, true>(q, cp, src, L, out.ta, out.ksp,
                                                              next);
     if (!more) break;
     u = un;
