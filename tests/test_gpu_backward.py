@@ -31,6 +31,9 @@ BWD = {
     "v3_keyed": L.SMALL["deepseek_small"].replace(name="v3_keyed", n_groups=8, topk_groups=4,
                                                   sel_bias_var=1e-4),
     "medium": I.WORKLOADS["mixtral_bf16"].replace(name="medium", T=2048, h=1024, f=2048),
+    # T not a multiple of any tile, E not a multiple of 4, drops
+    "ragged": I.WORKLOADS["mixtral_bf16"].replace(name="ragged", T=1000, h=192, f=320, E=6,
+                                                  capacity_factor=0.9),
 }
 
 
@@ -305,6 +308,9 @@ EXTRA = {
     "v3_full_small": L.SMALL["deepseek_small"].replace(name="v3_full_small", n_groups=8,
                                                        topk_groups=4, sel_bias_var=1e-4,
                                                        n_shared=1, f_shared=192),
+    "ragged_noisy_shared": L.SMALL["noisy_small"].replace(name="ragged_noisy_shared", T=777,
+                                                          h=192, f=192, E=6, n_shared=1,
+                                                          f_shared=64),
 }
 
 
