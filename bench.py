@@ -304,6 +304,10 @@ def main():
         for j, n in enumerate(B.STAGE_NAMES):
             stage_ms[n] += evs[j].elapsed_time(evs[j + 1]) / args.steps
     ms = elapsed * 1e3 / args.steps
+    # per-step times from the events around each step (the first and last
+    # stage boundaries, and the backward's end with --backward)
+    step_ms = sorted(evs[0].elapsed_time(evs[-1]) for evs in events)
+    ms_median = (step_ms[(len(step_ms) - 1) // 2] + step_ms[len(step_ms) // 2]) / 2
     bwd_ms = (sum(evs[nst].elapsed_time(evs[nst + 1]) for evs in events) / args.steps
               if args.backward else None)
     tokens_per_s = w.T * args.steps / elapsed
@@ -340,6 +344,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_median": ms_median,
+        "ms_min": step_ms[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
