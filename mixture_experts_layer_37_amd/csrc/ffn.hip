@@ -765,10 +765,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_kernel(GemmParams p) {
 // stored ([K][columns], the AT and BT copies and transposing fragment reads),
 // K being expert e's rows offset[e] .. offset[e+1]-1: the buffer resources
 // end at the expert's last row, so the ragged last K step reads zeros.
-// Tiles (e, m-tile, n-tile) in e-major order, round-robin over the
-// persistent grid; the main loop and the cross-tile prefetch are those of the
-// row-grouped GEMM.  An expert without rows gets one K step of zeros (its
-// buffer resources are empty), i.e. C_e = 0.
+// Tiles (e, m-tile, n-tile) in that order (n fastest), each XCD taking a
+// contiguous slice of them; the main loop is that of the row-grouped GEMM and
+// the epilogue goes through LDS (store_tile_staged), after which the next
+// tile's first copies go out.  An expert without rows gets one K step of
+// zeros (its buffer resources are empty), i.e. C_e = 0.
 __device__ __forceinline__ Unit wgrad_unit(const GemmParams& p, int t, int mt_n, int nt_n) {
   Unit w;
   const int per = mt_n * nt_n;
