@@ -770,11 +770,13 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
     return MOE_ERR_INVALID_ARG;
   if (!isfinite(alpha) || !isfinite(c_z)) return MOE_ERR_INVALID_ARG;
   if (saved && (!saved->X || !saved->GU || !saved->A || !saved->Y)) return MOE_ERR_INVALID_ARG;
-  // the weight-gradient products address an expert's rows with 32-bit byte
-  // offsets (rows of up to 2 f or h elements, plus the ring's steps past the end)
+  // the weight-gradient products address one expert's rows (at most
+  // min(C, T), a token taking an expert once; T for a shared expert) with
+  // 32-bit byte offsets: rows of up to 2 f or h elements, plus the ring's
+  // steps past the end
   {
     const int64_t pitch = 2 * std::max<int64_t>(2 * d.f, std::max<int64_t>(d.h, 2 * d.fs));
-    const int64_t rows = std::max<int64_t>(d.rows_max, d.ns > 0 ? d.T : 0) + 3 * 64;
+    const int64_t rows = std::max<int64_t>(std::min(d.C, d.T), d.ns > 0 ? d.T : 0) + 3 * 64;
     if (rows * pitch > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   }
   Plan pl;

@@ -215,7 +215,8 @@ def oracle_routing(w, g, tokens=None):
             "logits": fwd["logits"][tokens], "f": fwd["f"]}
 
 
-FULL = ["mixtral_bf16", "deepseek_v3_bf16", "switch_bf16"]
+FULL = ["mixtral_bf16", "deepseek_v3_bf16", "switch_bf16", "noisy_long_bf16",
+        "deepseek_v3_full_bf16"]
 
 
 @pytest.fixture(scope="module")
@@ -246,10 +247,17 @@ def test_full_size_weight_gradients(full_cases, name):
     J = np.unique(np.concatenate([[0, w.f - 1], rng.choice(w.f, 14, replace=False)]))
     Jt = torch.as_tensor(J, device=DEV)
     sub = lambda t, dim: L.f64(t.index_select(dim, Jt))
+    # the shared experts (output gradient dOut) restrict the same way
+    shared = {}
+    if w.n_shared:
+        Js = torch.as_tensor(J[J < w.f_shared], device=DEV)
+        ssub = lambda t, dim: L.f64(t.index_select(dim, Js))
+        shared = dict(Ws_gate=ssub(x["Ws_gate"], 1), Ws_up=ssub(x["Ws_up"], 1),
+                      Ws_down=ssub(x["Ws_down"], 2))
     ref = O.layer_backward(L.f64(x["U"]), L.f64(x["W_r"]), sub(x["W_gate"], 1),
                            sub(x["W_up"], 1), sub(x["W_down"], 2), oracle_routing(w, g),
                            L.f64(dOut), score=L.ORACLE_MODE[w.score],
-                           gate=L.ORACLE_MODE[w.gate])
+                           gate=L.ORACLE_MODE[w.gate], **shared)
     kept = L.to_np(g["kept"])
     for n, dim in (("dW_gate", 1), ("dW_up", 1), ("dW_down", 2)):
         G = sub(got[n], dim)
@@ -257,6 +265,12 @@ def test_full_size_weight_gradients(full_cases, name):
         assert all(not G[e].any() for e in range(w.E) if kept[e] == 0), n
         L.log(f"  {n} worst expert rel {worst:.3e}")
         assert worst <= TOL, (n, worst)
+    if w.n_shared:
+        for n, dim in (("dWs_gate", 1), ("dWs_up", 1), ("dWs_down", 2)):
+            G = L.f64(got[n].index_select(dim, Js))
+            worst = max(rel(G[i], ref[n][i]) for i in range(w.n_shared))
+            L.log(f"  {n} rel {worst:.3e}")
+            assert worst <= TOL, (n, worst)
 
 
 def test_full_size_input_and_router_gradients(full_cases):
