@@ -308,7 +308,10 @@ typedef struct {
  *  Outputs: dU [T,h] and dW_gate, dW_up [E,f,h], dW_down [E,h,f] in bf16;
  *  dW_r [h,E] and db_r [E] (nullable) in float32.
  *  Supported: cfg->dtype == MOE_BF16 (else MOE_ERR_UNSUPPORTED); the routing
- *  may come from a selection bias or groups.  ws: MOE_WS_BACKWARD bytes. */
+ *  may come from a selection bias or groups.  One expert's rows (at most
+ *  min(C, T); T for a shared expert), plus 192, times 2 max(2 f, h, 2 f_shared)
+ *  bytes must stay below 2^31 (else MOE_ERR_UNSUPPORTED).
+ *  ws: MOE_WS_BACKWARD bytes. */
 int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r,
                            const void* W_gate, const void* W_up, const void* W_down,
                            const float* logits, const int32_t* topk_idx, const float* topk_gate,

@@ -256,6 +256,9 @@ def test_backward_argument_checks():
     assert status("moe_layer_forward", ctypes.byref(f32cfg), fake, fake, None, None, None, None,
                   fake, fake, fake, None, None, None, other, ctypes.byref(a), None, fake,
                   1 << 40, None) == B.MOE_ERR_UNSUPPORTED
+    # one expert's rows must be addressable with 32-bit byte offsets
+    big = B.make_config(I.WORKLOADS["mixtral_bf16"].replace(T=200000, h=64, f=65536, E=2, k=1))
+    assert bwd(big) == B.MOE_ERR_UNSUPPORTED
     # the workspace has its own size
     need = B.workspace_size(cfg, B.MOE_WS_BACKWARD)
     assert need > B.workspace_size(cfg, B.MOE_WS_LAYER)
