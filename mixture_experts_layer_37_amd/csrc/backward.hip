@@ -14,8 +14,13 @@
 // expert products run backward as grouped products for the inputs and for the
 // weights (section "专家计算：padding、block-sparse 与 grouped GEMM").
 //
-// This file holds the element-wise, reduction and layout kernels; the grouped
-// products are the GEMM kernels of ffn.hip.
+// Noisy routing adds the softplus branch of the router's noise term (router
+// section, eq. G(x)); shared experts take dOut as their output gradient
+// (section "细粒度专家与共享专家").
+//
+// This file holds the element-wise kernels, the router's backward and the
+// small float32 products (dU, dW_r, the noise term); the grouped products are
+// the GEMM kernels of ffn.hip.
 #include <math.h>
 
 #include <algorithm>
