@@ -34,6 +34,15 @@ BWD = {
     # T not a multiple of any tile, E not a multiple of 4, drops
     "ragged": I.WORKLOADS["mixtral_bf16"].replace(name="ragged", T=1000, h=192, f=320, E=6,
                                                   capacity_factor=0.9),
+    # degenerate routing: every expert selected, one expert, dropless, and
+    # most assignments dropped (their scores still renormalise the kept gates)
+    "k_eq_E": I.WORKLOADS["mixtral_bf16"].replace(name="k_eq_E", T=512, h=128, f=192, E=4, k=4),
+    "one_expert": I.WORKLOADS["mixtral_bf16"].replace(name="one_expert", T=300, h=128, f=128,
+                                                      E=1, k=1),
+    "dropless": I.WORKLOADS["deepseek_v3_bf16"].replace(name="dropless", T=512, h=256, f=192,
+                                                        E=32, capacity_factor=0.0),
+    "heavy_drops": I.WORKLOADS["mixtral_bf16"].replace(name="heavy_drops", T=1024, h=192, f=256,
+                                                       capacity_factor=0.05),
 }
 
 
