@@ -142,7 +142,9 @@ typedef enum {
   MOE_WS_EXPERT_FFN = 2,
   MOE_WS_LAYER = 3,
   MOE_WS_SHARED_FFN = 4,
-  MOE_WS_BACKWARD = 5
+  MOE_WS_BACKWARD = 5,
+  MOE_WS_EXPERT_FFN_BACKWARD = 6,
+  MOE_WS_ROUTER_BACKWARD = 7
 } moe_ws_entry;
 
 /* Stage boundaries recorded by moe_layer_forward when stage_events != NULL:
@@ -320,6 +322,51 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
                            float* db_r, void* dW_gate, void* dW_up, void* dW_down,
                            const moe_aux_outputs* saved, const moe_backward_extras* extra,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* Staged backward: the three parts of moe_layer_backward as separate calls
+ * (for instance with the expert rows exchanged between GPUs in between).
+ * Run in this order they give exactly the layer call's results.  bf16 only
+ * (else MOE_ERR_UNSUPPORTED).
+ *
+ * moe_combine_backward: through the weighted sum (page "MoE 与专家并行",
+ * section "路由器：打分、top-k、加权求和", eq. dL/dg): dY[slot[t,r]] =
+ * topk_gate[t,r] dOut_t for every kept rank (rows of dY that no token keeps
+ * are left untouched) and dgate[t,r] = dOut_t . Y[slot[t,r]] (0 when
+ * dropped).  dOut [T,h], Y and dY [rows_max,h] bf16; slot, topk_gate [T,k];
+ * dgate [T,k] float32.  No workspace. */
+int32_t moe_combine_backward(const moe_config* cfg, const void* dOut, const void* Y,
+                             const int32_t* slot, const float* topk_gate, void* dY, float* dgate,
+                             void* stream);
+
+/* moe_expert_ffn_backward: the experts' grouped products backward (section
+ * "专家计算：padding、block-sparse 与 grouped GEMM") for the rows X [rows_max,h]
+ * of offset [E+1] and their output gradients dY [rows_max,h]: dX [rows_max,h]
+ * (rows past offset[E] untouched), dW_gate, dW_up [E,f,h], dW_down [E,h,f]
+ * (an expert without rows gets zeros), all bf16.  GU [rows_max,2f] and A
+ * [rows_max,f]: the forward's kept g | u and a (moe_aux_outputs), or both
+ * NULL to recompute them from X.  A shared expert is one expert of all T
+ * rows: cfg with E = k = 1 and a capacity of T, X = U, offset {0, T},
+ * dY = dOut.  Errors as moe_layer_backward.  ws: MOE_WS_EXPERT_FFN_BACKWARD. */
+int32_t moe_expert_ffn_backward(const moe_config* cfg, const void* X, const int32_t* offset,
+                                const void* W_gate, const void* W_up, const void* W_down,
+                                const void* dY, const void* GU, const void* A, void* dX,
+                                void* dW_gate, void* dW_up, void* dW_down, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* moe_router_backward: from the gates' gradient dgate [T,k] to the logits
+ * (scores, renormalisation, plus alpha times the load-balance term and c_z
+ * times the z-loss term, as in moe_layer_backward) and on to
+ * dU = dOut + sum over kept ranks of dX[slot] + dH W_r^T, dW_r = U^T dH and
+ * db_r (nullable) = column sums of dH.  dOut is the gradient that reaches u_t
+ * directly (the residual; add the shared experts' input gradients to it);
+ * dX [rows_max,h] the experts' input gradients.  extra: the noise part
+ * (W_noise, noise, dW_noise) for noisy layers.  ws: MOE_WS_ROUTER_BACKWARD. */
+int32_t moe_router_backward(const moe_config* cfg, const void* U, const void* W_r,
+                            const float* logits, const int32_t* topk_idx, const float* topk_gate,
+                            const int32_t* slot, const int32_t* count, const float* dgate,
+                            const void* dOut, const void* dX, float alpha, float c_z,
+                            const moe_backward_extras* extra, void* dU, float* dW_r,
+                            float* db_r, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- FP8
  * FP8 dispatch and FP8 up-projection (page "MoE 与专家并行", section

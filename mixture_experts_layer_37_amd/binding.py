@@ -23,7 +23,7 @@ MOE_GATE_RAW, MOE_GATE_RENORM = 0, 1
 MOE_FILL_RANK_MAJOR, MOE_FILL_TOKEN_MAJOR = 0, 1
 MOE_CAP_ASSIGNMENTS, MOE_CAP_TOKENS = 0, 1
 (MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_EXPERT_FFN, MOE_WS_LAYER, MOE_WS_SHARED_FFN,
- MOE_WS_BACKWARD) = range(6)
+ MOE_WS_BACKWARD, MOE_WS_EXPERT_FFN_BACKWARD, MOE_WS_ROUTER_BACKWARD) = range(8)
 MOE_NUM_STAGES = 6
 STAGE_NAMES = ["route", "dispatch", "gate_up", "down", "combine", "stats"]
 
@@ -92,6 +92,10 @@ def lib() -> ctypes.CDLL:
             "moe_layer_forward_fp8": (I32, [cfgp] + [P] * 15 + [ctypes.POINTER(moe_aux_outputs),
                                                               P, P, SZ, P]),
             "moe_quantize_rows_fp8": (I32, [P, I64, I64, P, P, P]),
+            "moe_combine_backward": (I32, [cfgp] + [P] * 6 + [P]),
+            "moe_expert_ffn_backward": (I32, [cfgp] + [P] * 12 + [P, SZ, P]),
+            "moe_router_backward": (I32, [cfgp] + [P] * 10 + [ctypes.c_float, ctypes.c_float]
+                                    + [P] * 4 + [P, SZ, P]),
             "moe_layer_backward": (I32, [cfgp] + [P] * 12 + [ctypes.c_float, ctypes.c_float]
                                    + [P] * 8 + [P, SZ, P]),
             "moe_dispatch_fp8": (I32, [cfgp] + [P] * 9 + [P, SZ, P]),
@@ -468,6 +472,67 @@ def moe_layer_backward(cfg, U, W_r, W_gate, W_up, W_down, logits, topk_idx, topk
                                     ctypes.byref(sv) if sv is not None else None,
                                     ctypes.byref(ex) if ex is not None else None, wp, wn,
                                     _stream(stream)), "moe_layer_backward")
+
+
+def moe_combine_backward(cfg, dOut, Y, slot, topk_gate, dY, dgate, stream=None):
+    """dY[slot] = gate * dOut for every kept rank, dgate = dOut . Y[slot]."""
+    T, h, k = cfg.T, cfg.h, cfg.k
+    rows, bf = max_rows(cfg), torch.bfloat16
+    _check(lib().moe_combine_backward(
+        ctypes.byref(cfg), _ptr(dOut, "dOut", (T, h), bf), _ptr(Y, "Y", (rows, h), bf),
+        _ptr(slot, "slot", (T, k), torch.int32),
+        _ptr(topk_gate, "topk_gate", (T, k), torch.float32), _ptr(dY, "dY", (rows, h), bf),
+        _ptr(dgate, "dgate", (T, k), torch.float32), _stream(stream)), "moe_combine_backward")
+
+
+def moe_expert_ffn_backward(cfg, X, offset, W_gate, W_up, W_down, dY, dX, dW_gate, dW_up,
+                            dW_down, GU=None, A=None, ws=None, stream=None):
+    """The experts' products backward for rows X and output gradients dY: dX rows and
+    the weight gradients.  GU, A: the forward's kept g | u and a, or None to
+    recompute them."""
+    h, f, E = cfg.h, cfg.f, cfg.E
+    rows, bf = max_rows(cfg), torch.bfloat16
+    need = workspace_size(cfg, MOE_WS_EXPERT_FFN_BACKWARD)
+    ws = new_workspace(cfg, MOE_WS_EXPERT_FFN_BACKWARD, W_gate.device) if ws is None else ws
+    wp, wn = _ws(ws, need)
+    _check(lib().moe_expert_ffn_backward(
+        ctypes.byref(cfg), _ptr(X, "X", (rows, h), bf),
+        _ptr(offset, "offset", (E + 1,), torch.int32), _ptr(W_gate, "W_gate", (E, f, h), bf),
+        _ptr(W_up, "W_up", (E, f, h), bf), _ptr(W_down, "W_down", (E, h, f), bf),
+        _ptr(dY, "dY", (rows, h), bf), _ptr(GU, "GU", (rows, 2 * f), bf),
+        _ptr(A, "A", (rows, f), bf), _ptr(dX, "dX", (rows, h), bf),
+        _ptr(dW_gate, "dW_gate", (E, f, h), bf), _ptr(dW_up, "dW_up", (E, f, h), bf),
+        _ptr(dW_down, "dW_down", (E, h, f), bf), wp, wn, _stream(stream)),
+        "moe_expert_ffn_backward")
+
+
+def moe_router_backward(cfg, U, W_r, logits, topk_idx, topk_gate, slot, count, dgate, dOut, dX,
+                        dU, dW_r, db_r=None, alpha=0.0, c_z=0.0, W_noise=None, noise=None,
+                        dW_noise=None, ws=None, stream=None):
+    """dH from the gates' gradient (and the aux and z terms), then
+    dU = dOut + sum dX[slot] + dH W_r^T, dW_r, db_r (dW_noise for noisy layers)."""
+    T, h, E, k = cfg.T, cfg.h, cfg.E, cfg.k
+    rows, bf = max_rows(cfg), torch.bfloat16
+    need = workspace_size(cfg, MOE_WS_ROUTER_BACKWARD)
+    ws = new_workspace(cfg, MOE_WS_ROUTER_BACKWARD, W_r.device) if ws is None else ws
+    wp, wn = _ws(ws, need)
+    ex = None
+    if cfg.noisy:
+        ex = moe_backward_extras()
+        ex.W_noise = _ptr(W_noise, "W_noise", (h, E), bf)
+        ex.noise = _ptr(noise, "noise", (T, E), torch.float32)
+        ex.dW_noise = _ptr(dW_noise, "dW_noise", (h, E), torch.float32)
+    _check(lib().moe_router_backward(
+        ctypes.byref(cfg), _ptr(U, "U", (T, h), bf), _ptr(W_r, "W_r", (h, E), bf),
+        _ptr(logits, "logits", (T, E), torch.float32),
+        _ptr(topk_idx, "topk_idx", (T, k), torch.int32),
+        _ptr(topk_gate, "topk_gate", (T, k), torch.float32),
+        _ptr(slot, "slot", (T, k), torch.int32), _ptr(count, "count", (E,), torch.int32),
+        _ptr(dgate, "dgate", (T, k), torch.float32), _ptr(dOut, "dOut", (T, h), bf),
+        _ptr(dX, "dX", (rows, h), bf), ctypes.c_float(alpha), ctypes.c_float(c_z),
+        ctypes.byref(ex) if ex is not None else None, _ptr(dU, "dU", (T, h), bf),
+        _ptr(dW_r, "dW_r", (h, E), torch.float32), _ptr(db_r, "db_r", (E,), torch.float32),
+        wp, wn, _stream(stream)), "moe_router_backward")
 
 
 def moe_quantize_rows_fp8(src, dst=None, scale=None, stream=None):

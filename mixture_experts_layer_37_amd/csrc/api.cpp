@@ -232,40 +232,65 @@ LayerWs plan_layer(const Dims& d, int noisy, Plan& pl) {
   return w;
 }
 
-// Backward workspace: the recomputed expert activations (X, g and u, A, Y),
-// their gradients, the router's logit gradient and the float32 partials of
-// the split products.  Every product reads its operands as stored.
-struct BackwardWs {
-  FfnWs ffn;  // tile maps, A (the SwiGLU rows), K-split partials
+// Backward workspaces.  Every product reads its operands as stored.
+// The expert products' backward: tile maps, g | u and a (when recomputed),
+// dA, dG | dU and the K-split partials of the largest product (min_slots
+// partial tiles at least).
+struct FfnBwdWs {
+  FfnWs ffn;          // tile maps and a (ffn.A); ffn.part is this part
   FfnShape fsA, fsX;  // shapes of the dA (N = f, K = h) and dX (N = h, K = 2f) products
-  size_t X, GU, Y, dY, dA, dGU, dX, dgate, dH, part, dwr;
-  size_t dZ;  // noisy routing: [T, E] float32
-  // shared experts: the dense pass's shapes, maps and rows ({0, T}), one
-  // expert's g | u, dA and dG | dU at a time, every expert's a and dX
+  size_t GU, dA, dGU;
+};
+FfnBwdWs plan_ffn_backward(const Dims& d, Plan& pl, int min_slots = 0) {
+  FfnBwdWs w;
+  const int ncu = device_cus();
+  w.ffn.fs = ffn_shape(d.rows_max, (int)d.E, (int)d.h, (int)d.f, (int)d.T, (int)d.k, 1, ncu);
+  w.fsA = ffn_shape(d.rows_max, (int)d.E, (int)d.f, (int)d.h, (int)d.T, (int)d.k, 1, ncu);
+  w.fsX = ffn_shape(d.rows_max, (int)d.E, (int)d.h, (int)(2 * d.f), (int)d.T, (int)d.k, 1, ncu);
+  const size_t rows = (size_t)(d.rows_max > 0 ? d.rows_max : 1);
+  w.ffn.map1 = pl.add(tile_map_bytes(d.E, w.ffn.fs.mt1));
+  w.ffn.map2 = pl.add(tile_map_bytes(d.E, w.ffn.fs.mt2));
+  w.ffn.A = pl.add(rows * d.f * 2);
+  w.GU = pl.add(rows * 2 * d.f * 2);
+  w.dA = pl.add(rows * d.f * 2);
+  w.dGU = pl.add(rows * 2 * d.f * 2);
+  const int slots = std::max(std::max(min_slots, w.ffn.fs.part_slots),
+                             std::max(w.fsA.part_slots, w.fsX.part_slots));
+  w.ffn.part = pl.add((size_t)slots * kPartSlotBytes);
+  return w;
+}
+
+// The router's backward: dH, dZ (noisy routing) and the dW_r partials.
+struct RouterBwdWs {
+  size_t dH, dZ, dwr;
+};
+RouterBwdWs plan_router_backward(const Dims& d, Plan& pl) {
+  RouterBwdWs w;
+  const size_t T1 = (size_t)(d.T > 0 ? d.T : 1);
+  w.dH = pl.add(T1 * d.E * 4);
+  w.dZ = pl.add(T1 * d.E * 4);
+  w.dwr = pl.add(dwr_part_bytes(d.T, (int)d.h, (int)d.E));
+  return w;
+}
+
+// The whole layer: the two above, the recomputed X and Y, dY, dX and the
+// gates' gradient, and the shared experts' dense pass (one expert of T rows:
+// its maps and rows {0, T}, one expert's g | u, dA and dG | dU at a time,
+// every expert's a and dX).
+struct BackwardWs {
+  FfnBwdWs fb;
+  RouterBwdWs rb;
+  size_t X, Y, dY, dX, dgate;
   SharedWs sh;
   FfnShape shA, shX;
   size_t sGU, sdA, sdGU, sdX;
 };
 BackwardWs plan_backward(const Dims& d, Plan& pl) {
   BackwardWs w;
-  w.ffn = plan_ffn(d, pl);
   const int ncu = device_cus();
-  w.fsA = ffn_shape(d.rows_max, (int)d.E, (int)d.f, (int)d.h, (int)d.T, (int)d.k, 1, ncu);
-  w.fsX = ffn_shape(d.rows_max, (int)d.E, (int)d.h, (int)(2 * d.f), (int)d.T, (int)d.k, 1, ncu);
-  const size_t rows = (size_t)(d.rows_max > 0 ? d.rows_max : 1);
-  const size_t T1 = (size_t)(d.T > 0 ? d.T : 1);
-  w.X = pl.add(rows * d.h * 2);
-  w.GU = pl.add(rows * 2 * d.f * 2);
-  w.Y = pl.add(rows * d.h * 2);
-  w.dY = pl.add(rows * d.h * 2);
-  w.dA = pl.add(rows * d.f * 2);
-  w.dGU = pl.add(rows * 2 * d.f * 2);
-  w.dX = pl.add(rows * d.h * 2);
-  w.dgate = pl.add(T1 * d.k * 4);
-  w.dH = pl.add(T1 * d.E * 4);
-  w.dZ = pl.add(T1 * d.E * 4);
   w.sh = plan_shared(d, false, pl);
-  int slots = std::max(w.ffn.fs.part_slots, std::max(w.fsA.part_slots, w.fsX.part_slots));
+  int sh_slots = 0;
+  const size_t T1 = (size_t)(d.T > 0 ? d.T : 1);
   if (d.ns > 0) {
     w.shA = ffn_shape(d.T, 1, (int)d.fs, (int)d.h, (int)d.T, 1, 1, ncu);
     w.shX = ffn_shape(d.T, 1, (int)d.h, (int)(2 * d.fs), (int)d.T, 1, 1, ncu);
@@ -273,13 +298,27 @@ BackwardWs plan_backward(const Dims& d, Plan& pl) {
     w.sdA = pl.add(T1 * d.fs * 2);
     w.sdGU = pl.add(T1 * 2 * d.fs * 2);
     w.sdX = pl.add((size_t)d.ns * T1 * d.h * 2);
-    slots = std::max(slots, std::max(w.sh.fs.part_slots,
-                                     std::max(w.shA.part_slots, w.shX.part_slots)));
+    sh_slots = std::max(w.sh.fs.part_slots, std::max(w.shA.part_slots, w.shX.part_slots));
   }
-  // K-split partials for the largest grid of the row-grouped products
-  w.part = pl.add((size_t)slots * kPartSlotBytes);
-  w.dwr = pl.add(dwr_part_bytes(d.T, (int)d.h, (int)d.E));
+  w.fb = plan_ffn_backward(d, pl, sh_slots);
+  w.rb = plan_router_backward(d, pl);
+  const size_t rows = (size_t)(d.rows_max > 0 ? d.rows_max : 1);
+  w.X = pl.add(rows * d.h * 2);
+  w.Y = pl.add(rows * d.h * 2);
+  w.dY = pl.add(rows * d.h * 2);
+  w.dX = pl.add(rows * d.h * 2);
+  w.dgate = pl.add(T1 * d.k * 4);
   return w;
+}
+
+// One expert's rows (at most min(C, T), a token taking an expert once; T for
+// a shared expert) are addressed with 32-bit byte offsets by the
+// weight-gradient products: rows of up to 2 f or h elements, plus the ring's
+// steps past the end.
+bool backward_offsets_fit(const Dims& d) {
+  const int64_t pitch = 2 * std::max<int64_t>(2 * d.f, std::max<int64_t>(d.h, 2 * d.fs));
+  const int64_t rows = std::max<int64_t>(std::min(d.C, d.T), d.ns > 0 ? d.T : 0) + 3 * 64;
+  return rows * pitch <= 0x7fffffffLL;
 }
 
 template <typename P>
@@ -507,6 +546,8 @@ int32_t moe_workspace_size(const moe_config* cfg, int32_t entry, size_t* bytes) 
     case MOE_WS_LAYER: plan_layer(d, cfg->noisy, pl); break;
     case MOE_WS_SHARED_FFN: plan_shared(d, false, pl); break;
     case MOE_WS_BACKWARD: plan_backward(d, pl); break;
+    case MOE_WS_EXPERT_FFN_BACKWARD: plan_ffn_backward(d, pl); break;
+    case MOE_WS_ROUTER_BACKWARD: plan_router_backward(d, pl); break;
     default: return MOE_ERR_INVALID_ARG;
   }
   *bytes = pl.bytes;
@@ -744,6 +785,151 @@ int32_t moe_layer_forward_fp8(const moe_config* cfg, const void* U, const void* 
                     Ws_up, Ws_down, out, aux, stage_events, ws, ws_bytes, stream, &f8);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Steps of the backward shared by the layer call and the staged calls.
+
+// The expert products backward for dY rows (tile maps already built in
+// w.ffn): dA = dY W_down[e], SwiGLU backward from g | u, dX = [dg du]
+// [W_gate[e]; W_up[e]], then the weight gradients from dY, a, dG | dU and X.
+int32_t run_ffn_backward(const Dims& d, const FfnBwdWs& w, void* ws, const void* X,
+                         const void* GU, const void* A, const void* dY, const int32_t* offset,
+                         const void* Wg, const void* Wu, const void* Wd, void* dX, void* dWg,
+                         void* dWu, void* dWd, hipStream_t s) {
+  const int E = (int)d.E, h = (int)d.h, f = (int)d.f, ncu = device_cus();
+  const int32_t* map = at<int32_t>(ws, w.ffn.map1);  // every product uses the same row tiles
+  float* part = at<float>(ws, w.ffn.part);
+  void* dA = at<void>(ws, w.dA);
+  void* dGU = at<void>(ws, w.dGU);
+  MOE_TRY(launch_dgrad(w.fsA, dY, offset, map, Wd, Wd, h, dA, part, E, f, h, s));
+  MOE_TRY(launch_swiglu_bwd(dA, GU, offset, E, d.rows_max, f, dGU, s));
+  MOE_TRY(launch_dgrad(w.fsX, dGU, offset, map, Wg, Wu, f, dX, part, E, h, 2 * f, s));
+  MOE_TRY(launch_wgrad(dY, h, A, f, offset, dWd, E, h, f, ncu, s));
+  MOE_TRY(launch_wgrad(dGU, 2 * f, X, h, offset, dWg, E, f, h, ncu, s));
+  MOE_TRY(launch_wgrad(static_cast<const char*>(dGU) + (size_t)f * 2, 2 * f, X, h, offset, dWu,
+                       E, f, h, ncu, s));
+  return MOE_OK;
+}
+
+// g | u and a recomputed from X (tile maps already built in w.ffn).
+int32_t run_ffn_recompute(const Dims& d, const FfnBwdWs& w, void* ws, const void* X,
+                          const int32_t* offset, const void* Wg, const void* Wu, void* GU,
+                          void* A, hipStream_t s) {
+  MOE_TRY(launch_gate_up_save(w.ffn.fs, X, offset, at<int32_t>(ws, w.ffn.map1), Wg, Wu, A, GU,
+                              at<float>(ws, w.ffn.part), (int)d.E, (int)d.h, (int)d.f, s));
+  return MOE_OK;
+}
+
+// The router's backward and the input gradient: dH from the gates' gradient
+// and the aux and z terms (dZ for the noise term), then
+// dU = dOut + sum_r dX[slot] + dH W_r^T (+ dZ W_noise^T) (+ the shared experts'
+// dXs), dW_r, db_r (dW_noise).
+int32_t run_router_backward(const moe_config* cfg, const Dims& d, const RouterBwdWs& w, void* ws,
+                            const void* U, const void* W_r, const float* logits,
+                            const int32_t* topk_idx, const float* topk_gate,
+                            const int32_t* slot, const int32_t* count, const float* dgate,
+                            const void* dOut, const void* dX, const void* dXs, int ns,
+                            float alpha, float c_z, const moe_backward_extras* extra, void* dU,
+                            float* dW_r, float* db_r, hipStream_t s) {
+  const int E = (int)d.E, h = (int)d.h, T = (int)d.T, k = (int)d.k;
+  float* dH = at<float>(ws, w.dH);
+  MOE_TRY(launch_router_bwd(logits, topk_idx, topk_gate, dgate, count, T, E, k, cfg->score,
+                            cfg->gate == MOE_GATE_RENORM, alpha, c_z, dH, s));
+  float* dZ = nullptr;
+  if (cfg->noisy) {
+    dZ = at<float>(ws, w.dZ);
+    MOE_TRY(launch_noise_grad(U, extra->W_noise, dH, extra->noise, dZ, T, h, E, s));
+  }
+  MOE_TRY(launch_grad_input(dOut, dX, slot, dH, W_r, dZ, cfg->noisy ? extra->W_noise : nullptr,
+                            dXs, T > 0 ? ns : 0, dU, T, h, E, k, s));
+  MOE_TRY(launch_dwr(U, dH, dW_r, db_r, at<float>(ws, w.dwr), T, h, E, s));
+  if (cfg->noisy)
+    MOE_TRY(launch_dwr(U, dZ, extra->dW_noise, nullptr, at<float>(ws, w.dwr), T, h, E, s));
+  return MOE_OK;
+}
+
+int32_t check_noise_extras(const moe_config* cfg, const moe_backward_extras* extra) {
+  if (cfg->noisy && (!extra || !extra->W_noise || !extra->dW_noise ||
+                     (cfg->T > 0 && !extra->noise)))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_combine_backward(const moe_config* cfg, const void* dOut, const void* Y,
+                             const int32_t* slot, const float* topk_gate, void* dY, float* dgate,
+                             void* stream) {
+  const int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (cfg->T > 0 && (!dOut || !Y || !slot || !topk_gate || !dY || !dgate))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine_bwd(dOut, Y, slot, topk_gate, dY, dgate, (int)cfg->T,
+                                       (int)cfg->h, (int)cfg->k,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_expert_ffn_backward(const moe_config* cfg, const void* X, const int32_t* offset,
+                                const void* W_gate, const void* W_up, const void* W_down,
+                                const void* dY, const void* GU, const void* A, void* dX,
+                                void* dW_gate, void* dW_up, void* dW_down, void* ws,
+                                size_t ws_bytes, void* stream) {
+  const int32_t st0 = check_config(cfg);
+  if (st0 != MOE_OK) return st0;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const Dims d = dims_of(cfg);
+  if (!offset || !W_gate || !W_up || !W_down || !dW_gate || !dW_up || !dW_down || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (d.rows_max > 0 && (!X || !dY || !dX)) return MOE_ERR_INVALID_ARG;
+  if ((GU == nullptr) != (A == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!backward_offsets_fit(d)) return MOE_ERR_UNSUPPORTED;
+  Plan pl;
+  const FfnBwdWs w = plan_ffn_backward(d, pl);
+  if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t st = run_tile_map(d, w.ffn, offset, ws, s);
+  if (st != MOE_OK) return st;
+  if (!GU) {
+    GU = at<void>(ws, w.GU);
+    A = at<void>(ws, w.ffn.A);
+    st = run_ffn_recompute(d, w, ws, X, offset, W_gate, W_up, const_cast<void*>(GU),
+                           const_cast<void*>(A), s);
+    if (st != MOE_OK) return st;
+  }
+  return run_ffn_backward(d, w, ws, X, GU, A, dY, offset, W_gate, W_up, W_down, dX, dW_gate,
+                          dW_up, dW_down, s);
+}
+
+int32_t moe_router_backward(const moe_config* cfg, const void* U, const void* W_r,
+                            const float* logits, const int32_t* topk_idx, const float* topk_gate,
+                            const int32_t* slot, const int32_t* count, const float* dgate,
+                            const void* dOut, const void* dX, float alpha, float c_z,
+                            const moe_backward_extras* extra, void* dU, float* dW_r,
+                            float* db_r, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  st = check_noise_extras(cfg, extra);
+  if (st != MOE_OK) return st;
+  const Dims d = dims_of(cfg);
+  if (!W_r || !count || !dW_r || !ws) return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (!U || !logits || !topk_idx || !topk_gate || !slot || !dgate || !dOut || !dX ||
+                  !dU))
+    return MOE_ERR_INVALID_ARG;
+  if (!isfinite(alpha) || !isfinite(c_z)) return MOE_ERR_INVALID_ARG;
+  Plan pl;
+  const RouterBwdWs w = plan_router_backward(d, pl);
+  if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
+  return run_router_backward(cfg, d, w, ws, U, W_r, logits, topk_idx, topk_gate, slot, count,
+                             dgate, dOut, dX, nullptr, 0, alpha, c_z, extra, dU, dW_r, db_r,
+                             static_cast<hipStream_t>(stream));
+}
+
 int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r,
                            const void* W_gate, const void* W_up, const void* W_down,
                            const float* logits, const int32_t* topk_idx, const float* topk_gate,
@@ -755,9 +941,8 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
   int32_t st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (cfg->noisy && (!extra || !extra->W_noise || !extra->dW_noise ||
-                     (cfg->T > 0 && !extra->noise)))
-    return MOE_ERR_INVALID_ARG;
+  st = check_noise_extras(cfg, extra);
+  if (st != MOE_OK) return st;
   if (cfg->n_shared > 0 &&
       (!extra || !extra->Ws_gate || !extra->Ws_up || !extra->Ws_down || !extra->dWs_gate ||
        !extra->dWs_up || !extra->dWs_down))
@@ -770,15 +955,7 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
     return MOE_ERR_INVALID_ARG;
   if (!isfinite(alpha) || !isfinite(c_z)) return MOE_ERR_INVALID_ARG;
   if (saved && (!saved->X || !saved->GU || !saved->A || !saved->Y)) return MOE_ERR_INVALID_ARG;
-  // the weight-gradient products address one expert's rows (at most
-  // min(C, T), a token taking an expert once; T for a shared expert) with
-  // 32-bit byte offsets: rows of up to 2 f or h elements, plus the ring's
-  // steps past the end
-  {
-    const int64_t pitch = 2 * std::max<int64_t>(2 * d.f, std::max<int64_t>(d.h, 2 * d.fs));
-    const int64_t rows = std::max<int64_t>(std::min(d.C, d.T), d.ns > 0 ? d.T : 0) + 3 * 64;
-    if (rows * pitch > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-  }
+  if (!backward_offsets_fit(d)) return MOE_ERR_UNSUPPORTED;
   Plan pl;
   const BackwardWs w = plan_backward(d, pl);
   if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
@@ -786,42 +963,31 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
   const int E = (int)d.E, h = (int)d.h, f = (int)d.f, T = (int)d.T, k = (int)d.k;
   const int ncu = device_cus();
   void* X = saved ? saved->X : at<void>(ws, w.X);
-  void* A = saved ? saved->A : at<void>(ws, w.ffn.A);
-  void* GU = saved ? saved->GU : at<void>(ws, w.GU);
+  void* A = saved ? saved->A : at<void>(ws, w.fb.ffn.A);
+  void* GU = saved ? saved->GU : at<void>(ws, w.fb.GU);
   void* Y = saved ? saved->Y : at<void>(ws, w.Y);
   void* dY = at<void>(ws, w.dY);
-  void* dA = at<void>(ws, w.dA);
-  void* dGU = at<void>(ws, w.dGU);
   void* dX = at<void>(ws, w.dX);
   float* dgate = at<float>(ws, w.dgate);
-  float* dH = at<float>(ws, w.dH);
-  float* part = at<float>(ws, w.part);
-  const int32_t* map = at<int32_t>(ws, w.ffn.map1);  // every product uses the same row tiles
+  float* part = at<float>(ws, w.fb.ffn.part);
   // 1. the experts' activations: kept by the forward, or recomputed (X, then
   // A = SiLU(g) u with g, u kept, then Y)
-  st = run_tile_map(d, w.ffn, offset, ws, s);
+  st = run_tile_map(d, w.fb.ffn, offset, ws, s);
   if (st != MOE_OK) return st;
   if (!saved) {
     MOE_TRY(launch_permute(U, slot, X, T, h, k, 1, s));
-    MOE_TRY(launch_gate_up_save(w.ffn.fs, X, offset, map, W_gate, W_up, A, GU, part, E, h, f,
-                                s));
-    MOE_TRY(launch_down(w.ffn.fs, A, offset, at<int32_t>(ws, w.ffn.map2), W_down, Y, part, E, h,
-                        f, 1, s));
+    st = run_ffn_recompute(d, w.fb, ws, X, offset, W_gate, W_up, GU, A, s);
+    if (st != MOE_OK) return st;
+    MOE_TRY(launch_down(w.fb.ffn.fs, A, offset, at<int32_t>(ws, w.fb.ffn.map2), W_down, Y, part,
+                        E, h, f, 1, s));
   }
   // 2. combine: dY rows and the gates' gradient
   MOE_TRY(launch_combine_bwd(dOut, Y, slot, topk_gate, dY, dgate, T, h, k, s));
-  // 3. dA = dY W_down[e]; SwiGLU backward; dX = [dg du] [W_gate[e]; W_up[e]]: products
-  // with the weights read as stored, [K][N]
-  MOE_TRY(launch_dgrad(w.fsA, dY, offset, map, W_down, W_down, h, dA, part, E, f, h, s));
-  MOE_TRY(launch_swiglu_bwd(dA, GU, offset, E, d.rows_max, f, dGU, s));
-  MOE_TRY(launch_dgrad(w.fsX, dGU, offset, map, W_gate, W_up, f, dX, part, E, h, 2 * f, s));
-  // 4. weight gradients: sums over each expert's rows of outer products, the
-  // row-major activations read as stored
-  MOE_TRY(launch_wgrad(dY, h, A, f, offset, dW_down, E, h, f, ncu, s));
-  MOE_TRY(launch_wgrad(dGU, 2 * f, X, h, offset, dW_gate, E, f, h, ncu, s));
-  MOE_TRY(launch_wgrad(static_cast<char*>(dGU) + (size_t)f * 2, 2 * f, X, h, offset, dW_up, E, f,
-                       h, ncu, s));
-  // 5. shared experts (every token, weight 1): recomputed g | u and a, then
+  // 3. the expert products backward
+  st = run_ffn_backward(d, w.fb, ws, X, GU, A, dY, offset, W_gate, W_up, W_down, dX, dW_gate,
+                        dW_up, dW_down, s);
+  if (st != MOE_OK) return st;
+  // 4. shared experts (every token, weight 1): recomputed g | u and a, then
   // the same products with offsets {0, T}
   const int ns = (int)d.ns, fsh = (int)d.fs;
   void* sdX = ns > 0 ? at<void>(ws, w.sdX) : nullptr;
@@ -854,20 +1020,9 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
                            static_cast<char*>(extra->dWs_up) + i * fh * 2, 1, fsh, h, ncu, s));
     }
   }
-  // 6. router: dH (and dZ for the noise term), then dU and dW_r, db_r (dW_noise)
-  MOE_TRY(launch_router_bwd(logits, topk_idx, topk_gate, dgate, count, T, E, k, cfg->score,
-                            cfg->gate == MOE_GATE_RENORM, alpha, c_z, dH, s));
-  float* dZ = nullptr;
-  if (cfg->noisy) {
-    dZ = at<float>(ws, w.dZ);
-    MOE_TRY(launch_noise_grad(U, extra->W_noise, dH, extra->noise, dZ, T, h, E, s));
-  }
-  MOE_TRY(launch_grad_input(dOut, dX, slot, dH, W_r, dZ, cfg->noisy ? extra->W_noise : nullptr,
-                            sdX, T > 0 ? ns : 0, dU, T, h, E, k, s));
-  MOE_TRY(launch_dwr(U, dH, dW_r, db_r, at<float>(ws, w.dwr), T, h, E, s));
-  if (cfg->noisy)
-    MOE_TRY(launch_dwr(U, dZ, extra->dW_noise, nullptr, at<float>(ws, w.dwr), T, h, E, s));
-  return MOE_OK;
+  // 5. router: dH (and dZ for the noise term), then dU and dW_r, db_r (dW_noise)
+  return run_router_backward(cfg, d, w.rb, ws, U, W_r, logits, topk_idx, topk_gate, slot, count,
+                             dgate, dOut, dX, sdX, ns, alpha, c_z, extra, dU, dW_r, db_r, s);
 }
 
 int32_t moe_quantize_rows_fp8(const void* src, int64_t rows, int64_t cols, void* dst,

@@ -263,3 +263,32 @@ def test_backward_argument_checks():
     need = B.workspace_size(cfg, B.MOE_WS_BACKWARD)
     assert need > B.workspace_size(cfg, B.MOE_WS_LAYER)
     assert bwd(cfg, ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE
+
+
+def test_staged_backward_argument_checks():
+    fake, other = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)
+    cfg = cfg_of()
+    f32cfg = B.make_config(I.WORKLOADS["tiny_f32"])
+    # combine backward: bf16 only, every pointer required when T > 0
+    assert status("moe_combine_backward", ctypes.byref(f32cfg), fake, fake, fake, fake, other,
+                  other, None) == B.MOE_ERR_UNSUPPORTED
+    assert status("moe_combine_backward", ctypes.byref(cfg), fake, fake, fake, fake, None, other,
+                  None) == B.MOE_ERR_INVALID_ARG
+
+    def ffn(c, GU=None, A=None, ws_bytes=1 << 40):
+        return status("moe_expert_ffn_backward", ctypes.byref(c), fake, fake, fake, fake, fake,
+                      fake, GU, A, other, other, other, other, fake, ws_bytes, None)
+    assert ffn(f32cfg) == B.MOE_ERR_UNSUPPORTED
+    assert ffn(cfg, GU=fake) == B.MOE_ERR_INVALID_ARG  # g | u without a
+    need = B.workspace_size(cfg, B.MOE_WS_EXPERT_FFN_BACKWARD)
+    assert 0 < need < B.workspace_size(cfg, B.MOE_WS_BACKWARD)
+    assert ffn(cfg, ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE
+
+    def router(c, extra=None, alpha=0.0, ws_bytes=1 << 40):
+        return status("moe_router_backward", ctypes.byref(c), fake, fake, fake, fake, fake, fake,
+                      fake, fake, fake, fake, alpha, 0.0, extra, other, other, None, fake,
+                      ws_bytes, None)
+    assert router(cfg_of(noisy=True)) == B.MOE_ERR_INVALID_ARG  # the noise part is required
+    assert router(cfg, alpha=float("nan")) == B.MOE_ERR_INVALID_ARG
+    need = B.workspace_size(cfg, B.MOE_WS_ROUTER_BACKWARD)
+    assert router(cfg, ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE

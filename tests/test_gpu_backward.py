@@ -375,3 +375,60 @@ def test_backward_empty_batch_with_shared_experts():
     got = run_backward(w, x, g, dOut, 0.01, 1e-3)
     for n in ("dW_r", "db_r", "dW_gate", "dW_up", "dW_down", "dWs_gate", "dWs_up", "dWs_down"):
         assert not got[n].any(), n
+
+
+@pytest.mark.parametrize("name,saved", [("mixtral_drops", False), ("mixtral_drops", True),
+                                        ("noisy_small", False), ("v3_full_small", False)])
+def test_staged_backward_equals_layer(name, saved):
+    # combine backward, the experts' backward and the router backward called
+    # one by one give the layer call's gradients bit for bit; only with shared
+    # experts dU differs, since the caller adds their input gradients to dOut
+    # in bf16 first, one more rounding (compared at the bf16 bar)
+    w = {**BWD, **EXTRA}[name]
+    x = I.make_inputs(w, seed=6, device=DEV)
+    fields = ["logits", "topk_idx", "topk_gate", "slot", "count", "kept", "offset", "X", "Y"]
+    cfg, g = L.run_layer(w, x, fields=fields + (["GU", "A"] if saved else []))
+    gen = torch.Generator(device=DEV).manual_seed(12)
+    dOut = torch.randn((w.T, w.h), generator=gen, device=DEV).to(torch.bfloat16)
+    alpha, c_z = 0.01, 1e-3
+    ref = run_backward(w, x, g, dOut, alpha, c_z)
+    rows, bf = B.max_rows(cfg), torch.bfloat16
+    dY = torch.empty((rows, w.h), dtype=bf, device=DEV)
+    dgate = torch.empty((w.T, w.k), dtype=torch.float32, device=DEV)
+    B.moe_combine_backward(cfg, dOut, g["Y"], g["slot"], g["topk_gate"], dY, dgate)
+    dX = torch.empty((rows, w.h), dtype=bf, device=DEV)
+    got = {n: torch.empty_like(ref[n]) for n in ("dU", "dW_r", "db_r", "dW_gate", "dW_up",
+                                                  "dW_down")}
+    B.moe_expert_ffn_backward(cfg, g["X"], g["offset"], x["W_gate"], x["W_up"], x["W_down"], dY,
+                              dX, got["dW_gate"], got["dW_up"], got["dW_down"],
+                              GU=g["GU"] if saved else None, A=g["A"] if saved else None)
+    d_res = dOut
+    if w.n_shared:
+        cfg_s = B.make_config(w.replace(E=1, k=1, f=w.f_shared, n_shared=0, f_shared=0,
+                                        n_groups=0, topk_groups=0, sel_bias_var=0.0,
+                                        capacity_factor=0.0))
+        offs = torch.tensor([0, w.T], dtype=torch.int32, device=DEV)
+        acc = dOut.float()
+        for n in ("dWs_gate", "dWs_up", "dWs_down"):
+            got[n] = torch.empty_like(ref[n])
+        for i in range(w.n_shared):
+            dXs = torch.empty((w.T, w.h), dtype=bf, device=DEV)
+            B.moe_expert_ffn_backward(cfg_s, x["U"], offs, x["Ws_gate"][i:i + 1],
+                                      x["Ws_up"][i:i + 1], x["Ws_down"][i:i + 1], dOut, dXs,
+                                      got["dWs_gate"][i:i + 1], got["dWs_up"][i:i + 1],
+                                      got["dWs_down"][i:i + 1])
+            acc += dXs.float()
+        d_res = acc.to(bf)
+    noise = {}
+    if w.noisy:
+        got["dW_noise"] = torch.empty_like(ref["dW_noise"])
+        noise = dict(W_noise=x["W_noise"], noise=x["noise"], dW_noise=got["dW_noise"])
+    B.moe_router_backward(cfg, x["U"], x["W_r"], g["logits"], g["topk_idx"], g["topk_gate"],
+                          g["slot"], g["count"], dgate, d_res, dX, got["dU"], got["dW_r"],
+                          db_r=got["db_r"], alpha=alpha, c_z=c_z, **noise)
+    torch.cuda.synchronize()
+    for n in got:
+        if w.n_shared and n == "dU":
+            assert rel(L.f64(got[n]), L.f64(ref[n])) <= TOL, n
+        else:
+            assert torch.equal(got[n], ref[n]), n
