@@ -432,3 +432,26 @@ def test_staged_backward_equals_layer(name, saved):
             assert rel(L.f64(got[n]), L.f64(ref[n])) <= TOL, n
         else:
             assert torch.equal(got[n], ref[n]), n
+
+
+def test_backward_deterministic_and_stream_ordered():
+    # no atomics and fixed-order partial sums: repeated runs agree bit for bit,
+    # also on other streams with their own workspaces
+    w = EXTRA["v3_full_small"]
+    x = I.make_inputs(w, seed=8, device=DEV)
+    cfg, g = L.run_layer(w, x)
+    gen = torch.Generator(device=DEV).manual_seed(13)
+    dOut = torch.randn((w.T, w.h), generator=gen, device=DEV).to(torch.bfloat16)
+    ref = run_backward(w, x, g, dOut, 0.01, 1e-3)
+    again = run_backward(w, x, g, dOut, 0.01, 1e-3)
+    for n in ref:
+        assert torch.equal(ref[n], again[n]), n
+    outs = []
+    for _ in range(2):
+        st = torch.cuda.Stream()
+        with torch.cuda.stream(st):
+            outs.append(run_backward(w, x, g, dOut, 0.01, 1e-3))
+    torch.cuda.synchronize()
+    for o in outs:
+        for n in ref:
+            assert torch.equal(ref[n], o[n]), n
