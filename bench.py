@@ -123,6 +123,18 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), for the baseline's record."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, x, g, budget_s: float) -> dict:
     """The float64 oracle, as it is, on a bounded sample of the same workload.
 
@@ -197,6 +209,7 @@ def cpu_baseline(w, x, g, budget_s: float) -> dict:
            + t_ffn * rows_total / max(rows_done, 1))
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": w.T / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": (f"routing, statistics and combine on all {w.T} tokens; expert SwiGLU on "
                        f"{rows_done} of {rows_total} kept rows from {experts_done} of "
                        f"{len(active)} active experts (float64), scaled by rows"
