@@ -421,9 +421,54 @@ def z_loss_logit_grad(H) -> np.ndarray:
     return 2.0 / T * lse[:, None] * e / e.sum(axis=1, keepdims=True)
 
 
+def expert_backward(X, offset, W_gate, W_up, W_down, dY):
+    """The experts' products backward for rows X of the experts in offset and
+    their output gradients dY: a = SiLU(g) u with g = X W_gate^T, u = X W_up^T
+    recomputed; dA = dY W_down, dg = dA u SiLU'(g), du = dA SiLU(g); returns
+    dX = dg W_gate + du W_up and dW_gate = dg^T X, dW_up = du^T X,
+    dW_down = dY^T a, expert by expert (zeros for an expert without rows)."""
+    X, dY = f64(X), f64(dY)
+    Wg, Wu, Wd = f64(W_gate), f64(W_up), f64(W_down)
+    off = np.asarray(offset)
+    dX = np.zeros(X.shape)
+    dWg, dWu, dWd = np.zeros_like(Wg), np.zeros_like(Wu), np.zeros_like(Wd)
+    for e in range(Wg.shape[0]):
+        a, b = int(off[e]), int(off[e + 1])
+        G, Up = X[a:b] @ Wg[e].T, X[a:b] @ Wu[e].T
+        A = silu(G) * Up
+        dA = dY[a:b] @ Wd[e]
+        dWd[e] = dY[a:b].T @ A
+        dG = dA * Up * dsilu(G)
+        dUp = dA * silu(G)
+        dWg[e] = dG.T @ X[a:b]
+        dWu[e] = dUp.T @ X[a:b]
+        dX[a:b] = dG @ Wg[e] + dUp @ Wu[e]
+    return dX, dWg, dWu, dWd
+
+
+def expert_backward_fp8(X, offset, W_gate, W_up, W_down, dYq, dY_scale):
+    """expert_backward with the output gradients given as FP8 rows (codes dYq
+    and power-of-two row scales, section "低精度通信": the activation
+    gradients before the down-projection are quantised like the activations
+    before the up-projection).  The experts use the dequantised rows
+    dY = dYq * dY_scale throughout; the down-projection's input gradient
+    dA = dY W_down[e] runs against W_down[e] quantised per output column (its
+    transpose quantised row-wise), so each scale factors out of a dot
+    product."""
+    dY = f64(dYq) * f64(dY_scale)[:, None]
+    Wd = f64(W_down)
+    E, h, f = Wd.shape
+    WdT = np.transpose(Wd, (0, 2, 1)).reshape(E * f, h)
+    WdTq, sdT = quantize_rows_fp8(WdT)
+    Wd_q = np.transpose((WdTq * sdT[:, None]).reshape(E, f, h), (0, 2, 1))
+    # dA = dY W_down from the FP8 operands; dW_down = dY^T a does not involve
+    # W_down
+    return expert_backward(X, offset, W_gate, W_up, Wd_q, dY)
+
+
 def layer_backward(U, W_r, W_gate, W_up, W_down, fwd: dict, dOut, *, score: str, gate: str,
                    alpha: float = 0.0, c_z: float = 0.0, W_noise=None, noise=None,
-                   Ws_gate=None, Ws_up=None, Ws_down=None) -> dict:
+                   Ws_gate=None, Ws_up=None, Ws_down=None, fp8_down_grad: bool = False) -> dict:
     """Gradients of L = <dOut, out> + alpha * aux + c_z * L_z for the routing
     in fwd (a layer_forward result).  The top-k choice, the capacity cut and
     the load fractions f are piecewise constant and carry no gradient; a
@@ -436,6 +481,13 @@ def layer_backward(U, W_r, W_gate, W_up, W_down, fwd: dict, dOut, *, score: str,
     passes dH on through softplus' = sigmoid to W_noise and U (dW_noise).
     Shared experts (Ws_*): each adds SwiGLU(u) with weight 1 to every token,
     so its output gradient is dOut itself (dWs_gate, dWs_up, dWs_down).
+
+    fp8_down_grad: the experts' output gradients dY are quantised row-wise to
+    FP8 before they reach the experts (as the activations are before the
+    up-projection), and the experts work on the dequantised rows: the
+    down-projection's input gradient dA = dY W_down against W_down quantised
+    per output column (rows of W_down^T), and dW_down = dY^T a (see
+    expert_backward_fp8).  Also returns dYq and dY_scale.
     """
     U, W_r, dOut = f64(U), f64(W_r), f64(dOut)
     Wg, Wu, Wd = f64(W_gate), f64(W_up), f64(W_down)
@@ -461,18 +513,13 @@ def layer_backward(U, W_r, W_gate, W_up, W_down, fwd: dict, dOut, *, score: str,
             if slot[t, r] >= 0:
                 dY[slot[t, r]] += g[t, r] * dOut[t]
                 dgate[t, r] = dOut[t] @ Y[slot[t, r]]
-    dWg, dWu, dWd = np.zeros_like(Wg), np.zeros_like(Wu), np.zeros_like(Wd)
-    dX = np.zeros((rows, h))
-    for e in range(E):
-        a, b = int(off[e]), int(off[e + 1])
-        A = silu(G[a:b]) * Up[a:b]
-        dA = dY[a:b] @ Wd[e]
-        dWd[e] = dY[a:b].T @ A
-        dG = dA * Up[a:b] * dsilu(G[a:b])
-        dUp = dA * silu(G[a:b])
-        dWg[e] = dG.T @ X[a:b]
-        dWu[e] = dUp.T @ X[a:b]
-        dX[a:b] = dG @ Wg[e] + dUp @ Wu[e]
+    fp8 = {}
+    if fp8_down_grad:
+        dYq, sy = quantize_rows_fp8(dY)
+        fp8 = {"dYq": dYq, "dY_scale": sy}
+        dX, dWg, dWu, dWd = expert_backward_fp8(X, off, Wg, Wu, Wd, dYq, sy)
+    else:
+        dX, dWg, dWu, dWd = expert_backward(X, off, Wg, Wu, Wd, dY)
     dU = dOut.copy()
     for row in range(rows):
         dU[row_token[row]] += dX[row]
@@ -501,7 +548,7 @@ def layer_backward(U, W_r, W_gate, W_up, W_down, fwd: dict, dOut, *, score: str,
         dH += c_z * z_loss_logit_grad(H)
     dU += dH @ W_r.T
     out = {"dU": dU, "dW_r": U.T @ dH, "db_r": dH.sum(axis=0), "dW_gate": dWg, "dW_up": dWu,
-           "dW_down": dWd, "dgate": dgate, "dH": dH}
+           "dW_down": dWd, "dgate": dgate, "dH": dH, **fp8}
     if W_noise is not None:
         Wn = f64(W_noise)
         Z = U @ Wn

@@ -758,3 +758,49 @@ def test_layer_backward_finite_differences_parts(part):
             vm[key][j] -= eps
             fd[j] = (loss(vp) - loss(vm)) / (2 * eps)
         np.testing.assert_allclose(bw[name], fd, rtol=1e-5, atol=1e-7, err_msg=name)
+
+
+def test_fp8_backward_exact_on_the_grid():
+    # one expert (gate 1, so dY = dOut) with dOut and W_down on the E4M3 grid:
+    # quantising them is exact, and the FP8 backward equals the plain one
+    r = rng(24)
+    T, h, f = 9, 16, 8
+    grid = np.array([O.fp8_e4m3_decode(c) for c in range(256)])
+    grid = grid[np.isfinite(grid) & (np.abs(grid) <= 8) & (np.abs(grid) >= 0.25)]
+    U = r.normal(0, 1, (T, h))
+    W_r = r.normal(0, 1, (h, 1))
+    Wg, Wu = r.normal(0, 0.5, (1, f, h)), r.normal(0, 0.5, (1, f, h))
+    Wd = r.choice(grid, (1, h, f)) / 8
+    dOut = r.choice(grid, (T, h))
+    kw = dict(k=1, score=O.SOFTMAX, gate=O.GATE_RENORM, capacity_factor=0.0)
+    fwd = O.layer_forward(U, W_r, Wg, Wu, Wd, **kw)
+    a = O.layer_backward(U, W_r, Wg, Wu, Wd, fwd, dOut, score=O.SOFTMAX, gate=O.GATE_RENORM)
+    b = O.layer_backward(U, W_r, Wg, Wu, Wd, fwd, dOut, score=O.SOFTMAX, gate=O.GATE_RENORM,
+                         fp8_down_grad=True)
+    np.testing.assert_array_equal(b["dYq"] * b["dY_scale"][:, None], dOut)
+    for n in ("dU", "dW_r", "dW_gate", "dW_up", "dW_down"):
+        np.testing.assert_array_equal(a[n], b[n], err_msg=n)
+
+
+def test_fp8_backward_within_the_rounding_bound():
+    # generic inputs: dY rounds to E4M3 (relative error <= 2^-4 on normals),
+    # so dW_down moves by about that much and the input-side gradients by a
+    # few times that; a dropped or mis-scaled term would move them by O(1)
+    r = rng(25)
+    T, h, f, E, k = 40, 16, 12, 4, 2
+    U = r.normal(0, 1, (T, h))
+    W_r = r.normal(0, 0.5, (h, E))
+    Wg, Wu = r.normal(0, 0.5, (E, f, h)), r.normal(0, 0.5, (E, f, h))
+    Wd = r.normal(0, 0.5, (E, h, f))
+    dOut = r.normal(0, 1, (T, h))
+    kw = dict(k=k, score=O.SOFTMAX, gate=O.GATE_RENORM, capacity_factor=1.0)
+    fwd = O.layer_forward(U, W_r, Wg, Wu, Wd, **kw)
+    a = O.layer_backward(U, W_r, Wg, Wu, Wd, fwd, dOut, score=O.SOFTMAX, gate=O.GATE_RENORM)
+    b = O.layer_backward(U, W_r, Wg, Wu, Wd, fwd, dOut, score=O.SOFTMAX, gate=O.GATE_RENORM,
+                         fp8_down_grad=True)
+    rel = lambda n: np.linalg.norm(b[n] - a[n]) / np.linalg.norm(a[n])
+    assert 0 < rel("dW_down") < 2 ** -4
+    for n in ("dW_gate", "dW_up", "dU"):
+        assert 0 < rel(n) < 2 ** -2, (n, rel(n))
+    # the router's gradient does not see the experts' input gradients
+    np.testing.assert_array_equal(a["dW_r"], b["dW_r"])
