@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--backward", action="store_true",
                     help="time forward + backward (bf16 workloads without FP8)")
+    ap.add_argument("--fp8-grad", action="store_true",
+                    help="with --backward: the experts' output gradients in FP8 (W_down^T "
+                         "quantised once before the timed loop)")
     ap.add_argument("--recompute", action="store_true",
                     help="with --backward: the forward keeps no activations and the backward "
                          "recomputes them")
@@ -261,6 +264,9 @@ def main():
         if w.noisy:
             extra = {"W_noise": x["W_noise"], "noise": x["noise"],
                      "dW_noise": torch.empty((w.h, w.E), device=dev)}
+        if args.fp8_grad:  # a one-time weight preparation, like a model load
+            WdT8, sdT = B.moe_quantize_rows_fp8(x["W_down"].transpose(1, 2).contiguous())
+            extra.update(W_downT8=WdT8, s_downT=sdT)
         if w.n_shared:
             extra.update(Ws_gate=x["Ws_gate"], Ws_up=x["Ws_up"], Ws_down=x["Ws_down"],
                          dWs_gate=torch.empty_like(x["Ws_gate"]),
@@ -397,6 +403,7 @@ def main():
         executed = useful + (6.0 * w.h * w.f * kept if args.recompute else 0.0) + 4.0 * sh
         res["backward"] = {"ms": bwd_ms, "forward_ms": ms - bwd_ms,
                            "activations": "recomputed" if args.recompute else "kept by the forward",
+                           "output_gradients": "fp8" if args.fp8_grad else "bf16",
                            "mfma_frac_useful": useful / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                            "mfma_frac_exec": executed / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     if not args.no_cpu_baseline and not args.backward:

@@ -273,7 +273,15 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
  *  Ws_down [n_shared,h,f_shared] as given to the forward; dWs_gate, dWs_up,
  *  dWs_down of the same shapes, bf16, out.  Each takes every token with
  *  weight 1 (section "细粒度专家与共享专家", eq. h'_t), so its output gradient
- *  is dOut itself. */
+ *  is dOut itself.
+ *  FP8 output gradients (section "低精度通信": the activation gradients
+ *  before the down-projection are quantised like the activations before the
+ *  up-projection): W_downT8 [E,f,h] E4M3 codes and s_downT [E,f] power-of-two
+ *  scales of W_down transposed, quantised row-wise (moe_quantize_rows_fp8 on
+ *  W_down^T, a one-time step); when set, the experts' output gradients are
+ *  quantised row-wise to E4M3, dA = dY W_down runs on FP8 operands, and
+ *  every other use of dY takes the dequantised rows.  Needs h a multiple of
+ *  128 (else MOE_ERR_UNSUPPORTED). */
 typedef struct {
   const void* W_noise;
   const float* noise;
@@ -284,6 +292,8 @@ typedef struct {
   void* dWs_gate;
   void* dWs_up;
   void* dWs_down;
+  const void* W_downT8;
+  const float* s_downT;
 } moe_backward_extras;
 
 /* Gradients of L = <dOut, out> + alpha * aux_loss + c_z * z_loss with respect
@@ -352,6 +362,19 @@ int32_t moe_expert_ffn_backward(const moe_config* cfg, const void* X, const int3
                                 const void* dY, const void* GU, const void* A, void* dX,
                                 void* dW_gate, void* dW_up, void* dW_down, void* ws,
                                 size_t ws_bytes, void* stream);
+
+/* The same with the output gradients as FP8 rows (section "低精度通信"): dY8
+ * [rows_max,h] E4M3 codes and dY_scale [rows_max] power-of-two row scales
+ * (moe_quantize_rows_fp8 of the dY rows), W_downT8 / s_downT as in
+ * moe_backward_extras.  dA = dY W_down runs on the FP8 operands; dW_down and
+ * the rest use the dequantised rows.  Needs h a multiple of 128 (else
+ * MOE_ERR_UNSUPPORTED).  ws: MOE_WS_EXPERT_FFN_BACKWARD. */
+int32_t moe_expert_ffn_backward_fp8(const moe_config* cfg, const void* X, const int32_t* offset,
+                                    const void* W_gate, const void* W_up, const void* W_downT8,
+                                    const float* s_downT, const void* dY8,
+                                    const float* dY_scale, const void* GU, const void* A,
+                                    void* dX, void* dW_gate, void* dW_up, void* dW_down,
+                                    void* ws, size_t ws_bytes, void* stream);
 
 /* moe_router_backward: from the gates' gradient dgate [T,k] to the logits
  * (scores, renormalisation, plus alpha times the load-balance term and c_z

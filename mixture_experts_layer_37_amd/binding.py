@@ -59,7 +59,7 @@ AUX_FIELDS = [n for n, _ in moe_aux_outputs._fields_]
 class moe_backward_extras(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "W_noise", "noise", "dW_noise", "Ws_gate", "Ws_up", "Ws_down", "dWs_gate", "dWs_up",
-        "dWs_down")]
+        "dWs_down", "W_downT8", "s_downT")]
 
 _lib = None
 
@@ -94,6 +94,7 @@ def lib() -> ctypes.CDLL:
             "moe_quantize_rows_fp8": (I32, [P, I64, I64, P, P, P]),
             "moe_combine_backward": (I32, [cfgp] + [P] * 6 + [P]),
             "moe_expert_ffn_backward": (I32, [cfgp] + [P] * 12 + [P, SZ, P]),
+            "moe_expert_ffn_backward_fp8": (I32, [cfgp] + [P] * 14 + [P, SZ, P]),
             "moe_router_backward": (I32, [cfgp] + [P] * 10 + [ctypes.c_float, ctypes.c_float]
                                     + [P] * 4 + [P, SZ, P]),
             "moe_layer_backward": (I32, [cfgp] + [P] * 12 + [ctypes.c_float, ctypes.c_float]
@@ -421,13 +422,15 @@ def moe_layer_backward(cfg, U, W_r, W_gate, W_up, W_down, logits, topk_idx, topk
                        count, offset, dOut, dU, dW_r, dW_gate, dW_up, dW_down, db_r=None,
                        alpha=0.0, c_z=0.0, saved=None, W_noise=None, noise=None, dW_noise=None,
                        Ws_gate=None, Ws_up=None, Ws_down=None, dWs_gate=None, dWs_up=None,
-                       dWs_down=None, ws=None, stream=None):
+                       dWs_down=None, W_downT8=None, s_downT=None, ws=None, stream=None):
     """Gradients of <dOut, out> + alpha aux_loss + c_z z_loss for the routing of a
     forward (logits ... offset from its aux outputs).  dU, dW_gate, dW_up,
     dW_down bf16; dW_r [h, E] and db_r [E] float32.  saved: None (the experts
     are recomputed) or a dict with the forward's aux outputs X, GU, A and Y.
     Noisy layers: W_noise, noise as in the forward, dW_noise [h, E] float32.
-    Shared experts: Ws_* as in the forward, dWs_* of the same shapes (bf16)."""
+    Shared experts: Ws_* as in the forward, dWs_* of the same shapes (bf16).
+    FP8 output gradients: W_downT8 [E, f, h] uint8 and s_downT [E, f], the
+    row-wise E4M3 quantisation of W_down transposed."""
     T, h, f, E, k = cfg.T, cfg.h, cfg.f, cfg.E, cfg.k
     bf = torch.bfloat16
     need = workspace_size(cfg, MOE_WS_BACKWARD)
@@ -454,8 +457,11 @@ def moe_layer_backward(cfg, U, W_r, W_gate, W_up, W_down, logits, topk_idx, topk
             shape_fn, _ = _AUX_SPEC[name]
             setattr(sv, name, _ptr(saved[name], name, shape_fn(cfg, rows), bf))
     ex = None
-    if cfg.noisy or cfg.n_shared:
+    if cfg.noisy or cfg.n_shared or W_downT8 is not None:
         ex = moe_backward_extras()
+        if W_downT8 is not None:
+            ex.W_downT8 = _ptr(W_downT8, "W_downT8", (E, f, h), torch.uint8)
+            ex.s_downT = _ptr(s_downT, "s_downT", (E, f), torch.float32)
         ns, fs = cfg.n_shared, cfg.f_shared
         if cfg.noisy:
             ex.W_noise = _ptr(W_noise, "W_noise", (h, E), bf)
@@ -504,6 +510,30 @@ def moe_expert_ffn_backward(cfg, X, offset, W_gate, W_up, W_down, dY, dX, dW_gat
         _ptr(dW_gate, "dW_gate", (E, f, h), bf), _ptr(dW_up, "dW_up", (E, f, h), bf),
         _ptr(dW_down, "dW_down", (E, h, f), bf), wp, wn, _stream(stream)),
         "moe_expert_ffn_backward")
+
+
+def moe_expert_ffn_backward_fp8(cfg, X, offset, W_gate, W_up, W_downT8, s_downT, dY8, dY_scale,
+                                dX, dW_gate, dW_up, dW_down, GU=None, A=None, ws=None,
+                                stream=None):
+    """moe_expert_ffn_backward with the output gradients as FP8 rows (dY8 uint8
+    [rows_max, h], dY_scale [rows_max]) and W_down^T quantised row-wise
+    (W_downT8 [E, f, h], s_downT [E, f])."""
+    h, f, E = cfg.h, cfg.f, cfg.E
+    rows, bf = max_rows(cfg), torch.bfloat16
+    need = workspace_size(cfg, MOE_WS_EXPERT_FFN_BACKWARD)
+    ws = new_workspace(cfg, MOE_WS_EXPERT_FFN_BACKWARD, W_gate.device) if ws is None else ws
+    wp, wn = _ws(ws, need)
+    _check(lib().moe_expert_ffn_backward_fp8(
+        ctypes.byref(cfg), _ptr(X, "X", (rows, h), bf),
+        _ptr(offset, "offset", (E + 1,), torch.int32), _ptr(W_gate, "W_gate", (E, f, h), bf),
+        _ptr(W_up, "W_up", (E, f, h), bf), _ptr(W_downT8, "W_downT8", (E, f, h), torch.uint8),
+        _ptr(s_downT, "s_downT", (E, f), torch.float32),
+        _ptr(dY8, "dY8", (rows, h), torch.uint8),
+        _ptr(dY_scale, "dY_scale", (rows,), torch.float32), _ptr(GU, "GU", (rows, 2 * f), bf),
+        _ptr(A, "A", (rows, f), bf), _ptr(dX, "dX", (rows, h), bf),
+        _ptr(dW_gate, "dW_gate", (E, f, h), bf), _ptr(dW_up, "dW_up", (E, f, h), bf),
+        _ptr(dW_down, "dW_down", (E, h, f), bf), wp, wn, _stream(stream)),
+        "moe_expert_ffn_backward_fp8")
 
 
 def moe_router_backward(cfg, U, W_r, logits, topk_idx, topk_gate, slot, count, dgate, dOut, dX,

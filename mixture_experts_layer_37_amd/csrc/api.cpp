@@ -240,6 +240,7 @@ struct FfnBwdWs {
   FfnWs ffn;          // tile maps and a (ffn.A); ffn.part is this part
   FfnShape fsA, fsX;  // shapes of the dA (N = f, K = h) and dX (N = h, K = 2f) products
   size_t GU, dA, dGU;
+  size_t dY8, sy, dYd;  // FP8 output gradients: codes, row scales, dequantised rows
 };
 FfnBwdWs plan_ffn_backward(const Dims& d, Plan& pl, int min_slots = 0) {
   FfnBwdWs w;
@@ -254,6 +255,9 @@ FfnBwdWs plan_ffn_backward(const Dims& d, Plan& pl, int min_slots = 0) {
   w.GU = pl.add(rows * 2 * d.f * 2);
   w.dA = pl.add(rows * d.f * 2);
   w.dGU = pl.add(rows * 2 * d.f * 2);
+  w.dY8 = pl.add(rows * d.h);
+  w.sy = pl.add(rows * 4);
+  w.dYd = pl.add(rows * d.h * 2);
   const int slots = std::max(std::max(min_slots, w.ffn.fs.part_slots),
                              std::max(w.fsA.part_slots, w.fsX.part_slots));
   w.ffn.part = pl.add((size_t)slots * kPartSlotBytes);
@@ -791,19 +795,33 @@ namespace {
 
 // Steps of the backward shared by the layer call and the staged calls.
 
+// FP8 output gradients for the dA product: the dY rows' codes and scales,
+// and W_down^T's.
+struct Fp8Grad {
+  const void* dY8;
+  const float* sy;
+  const void* WdT8;
+  const float* sdT;
+};
+
 // The expert products backward for dY rows (tile maps already built in
-// w.ffn): dA = dY W_down[e], SwiGLU backward from g | u, dX = [dg du]
+// w.ffn): dA = dY W_down[e] (on FP8 operands when f8 is set, dY then being
+// the dequantised rows), SwiGLU backward from g | u, dX = [dg du]
 // [W_gate[e]; W_up[e]], then the weight gradients from dY, a, dG | dU and X.
 int32_t run_ffn_backward(const Dims& d, const FfnBwdWs& w, void* ws, const void* X,
                          const void* GU, const void* A, const void* dY, const int32_t* offset,
                          const void* Wg, const void* Wu, const void* Wd, void* dX, void* dWg,
-                         void* dWu, void* dWd, hipStream_t s) {
+                         void* dWu, void* dWd, hipStream_t s, const Fp8Grad* f8 = nullptr) {
   const int E = (int)d.E, h = (int)d.h, f = (int)d.f, ncu = device_cus();
   const int32_t* map = at<int32_t>(ws, w.ffn.map1);  // every product uses the same row tiles
   float* part = at<float>(ws, w.ffn.part);
   void* dA = at<void>(ws, w.dA);
   void* dGU = at<void>(ws, w.dGU);
-  MOE_TRY(launch_dgrad(w.fsA, dY, offset, map, Wd, Wd, h, dA, part, E, f, h, s));
+  if (f8)
+    MOE_TRY(launch_dgrad_fp8(w.fsA, f8->dY8, f8->sy, offset, map, f8->WdT8, f8->sdT, dA, part, E,
+                             f, h, s));
+  else
+    MOE_TRY(launch_dgrad(w.fsA, dY, offset, map, Wd, Wd, h, dA, part, E, f, h, s));
   MOE_TRY(launch_swiglu_bwd(dA, GU, offset, E, d.rows_max, f, dGU, s));
   MOE_TRY(launch_dgrad(w.fsX, dGU, offset, map, Wg, Wu, f, dX, part, E, h, 2 * f, s));
   MOE_TRY(launch_wgrad(dY, h, A, f, offset, dWd, E, h, f, ncu, s));
@@ -857,6 +875,16 @@ int32_t check_noise_extras(const moe_config* cfg, const moe_backward_extras* ext
   return MOE_OK;
 }
 
+// dY rows to FP8 codes and scales, then back to bf16 in place (the values
+// every other use of dY takes).
+int32_t quantize_grad_rows(const Dims& d, const FfnBwdWs& w, void* ws, void* dY, hipStream_t s) {
+  MOE_TRY(launch_quantize_rows_fp8(dY, d.rows_max, (int)d.h, at<void>(ws, w.dY8),
+                                   at<float>(ws, w.sy), s));
+  MOE_TRY(launch_dequant_rows_fp8(at<void>(ws, w.dY8), at<float>(ws, w.sy), d.rows_max,
+                                  (int)d.h, dY, s));
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -903,6 +931,41 @@ int32_t moe_expert_ffn_backward(const moe_config* cfg, const void* X, const int3
   }
   return run_ffn_backward(d, w, ws, X, GU, A, dY, offset, W_gate, W_up, W_down, dX, dW_gate,
                           dW_up, dW_down, s);
+}
+
+int32_t moe_expert_ffn_backward_fp8(const moe_config* cfg, const void* X, const int32_t* offset,
+                                    const void* W_gate, const void* W_up, const void* W_downT8,
+                                    const float* s_downT, const void* dY8,
+                                    const float* dY_scale, const void* GU, const void* A,
+                                    void* dX, void* dW_gate, void* dW_up, void* dW_down,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  const int32_t st0 = check_fp8(cfg);
+  if (st0 != MOE_OK) return st0;
+  const Dims d = dims_of(cfg);
+  if (!offset || !W_gate || !W_up || !W_downT8 || !s_downT || !dW_gate || !dW_up || !dW_down ||
+      !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (d.rows_max > 0 && (!X || !dY8 || !dY_scale || !dX)) return MOE_ERR_INVALID_ARG;
+  if ((GU == nullptr) != (A == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!backward_offsets_fit(d)) return MOE_ERR_UNSUPPORTED;
+  Plan pl;
+  const FfnBwdWs w = plan_ffn_backward(d, pl);
+  if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t st = run_tile_map(d, w.ffn, offset, ws, s);
+  if (st != MOE_OK) return st;
+  if (!GU) {
+    GU = at<void>(ws, w.GU);
+    A = at<void>(ws, w.ffn.A);
+    st = run_ffn_recompute(d, w, ws, X, offset, W_gate, W_up, const_cast<void*>(GU),
+                           const_cast<void*>(A), s);
+    if (st != MOE_OK) return st;
+  }
+  void* dYd = at<void>(ws, w.dYd);
+  MOE_TRY(launch_dequant_rows_fp8(dY8, dY_scale, d.rows_max, (int)d.h, dYd, s));
+  const Fp8Grad f8{dY8, dY_scale, W_downT8, s_downT};
+  return run_ffn_backward(d, w, ws, X, GU, A, dYd, offset, W_gate, W_up, nullptr, dX, dW_gate,
+                          dW_up, dW_down, s, &f8);
 }
 
 int32_t moe_router_backward(const moe_config* cfg, const void* U, const void* W_r,
@@ -955,6 +1018,12 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
     return MOE_ERR_INVALID_ARG;
   if (!isfinite(alpha) || !isfinite(c_z)) return MOE_ERR_INVALID_ARG;
   if (saved && (!saved->X || !saved->GU || !saved->A || !saved->Y)) return MOE_ERR_INVALID_ARG;
+  const bool fp8g = extra && extra->W_downT8;
+  if (fp8g) {
+    if (!extra->s_downT) return MOE_ERR_INVALID_ARG;
+    st = check_fp8(cfg);
+    if (st != MOE_OK) return st;
+  }
   if (!backward_offsets_fit(d)) return MOE_ERR_UNSUPPORTED;
   Plan pl;
   const BackwardWs w = plan_backward(d, pl);
@@ -983,9 +1052,17 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
   }
   // 2. combine: dY rows and the gates' gradient
   MOE_TRY(launch_combine_bwd(dOut, Y, slot, topk_gate, dY, dgate, T, h, k, s));
-  // 3. the expert products backward
+  // 3. the expert products backward (FP8 output gradients: quantised rows,
+  // dequantised in place for every other use)
+  Fp8Grad f8{};
+  if (fp8g) {
+    st = quantize_grad_rows(d, w.fb, ws, dY, s);
+    if (st != MOE_OK) return st;
+    f8 = Fp8Grad{at<void>(ws, w.fb.dY8), at<float>(ws, w.fb.sy), extra->W_downT8,
+                 extra->s_downT};
+  }
   st = run_ffn_backward(d, w.fb, ws, X, GU, A, dY, offset, W_gate, W_up, W_down, dX, dW_gate,
-                        dW_up, dW_down, s);
+                        dW_up, dW_down, s, fp8g ? &f8 : nullptr);
   if (st != MOE_OK) return st;
   // 4. shared experts (every token, weight 1): recomputed g | u and a, then
   // the same products with offsets {0, T}

@@ -244,7 +244,39 @@ __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const bf16* src,
   if (lane == 0) scale[r] = ldexpf(1.f, j);
 }
 
+// FP8 rows back to bf16: codes times the row's power-of-two scale.  Exact,
+// since an E4M3 value has 4 significant bits and the scale only moves the
+// exponent.  Eight elements per thread.
+__global__ __launch_bounds__(256) void dequant_rows_fp8_kernel(const uint8_t* q,
+                                                               const float* scale, int64_t rows,
+                                                               int cols, bf16* out) {
+  const int per = cols / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = i / per;
+  if (r >= rows) return;
+  const int c = (int)(i - r * per) * 8;
+  const uint2 w = *reinterpret_cast<const uint2*>(q + (size_t)r * cols + c);
+  const float sc = scale[r];
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+  const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+  const f2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+  const f2 e = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+  const float v[8] = {a.x * sc, a.y * sc, b.x * sc, b.y * sc, d.x * sc, d.y * sc, e.x * sc,
+                      e.y * sc};
+  st16(out + (size_t)r * cols + c, Elem<bf16>::pack(v));
+}
+
 }  // namespace
+
+hipError_t launch_dequant_rows_fp8(const void* q, const float* scale, int64_t rows, int cols,
+                                   void* out, hipStream_t s) {
+  const int64_t n = rows * (cols / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant_rows_fp8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(q), scale, rows, cols, static_cast<bf16*>(out));
+  return hipGetLastError();
+}
 
 hipError_t launch_permute_fp8(const void* U, const int32_t* slot, void* X8, float* xs, int T,
                               int h, int k, hipStream_t s) {

@@ -195,9 +195,11 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const floatx16 (
         float y[4], sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
         if (F8) {  // power-of-two scales: the products below are exact
           const float4 a = *reinterpret_cast<const float4*>(p.sw0 + (size_t)ta.e * p.N + col);
-          const float4 b = *reinterpret_cast<const float4*>(p.sw1 + (size_t)ta.e * p.N + col);
           sg[0] = sa * a.x; sg[1] = sa * a.y; sg[2] = sa * a.z; sg[3] = sa * a.w;
-          su[0] = sa * b.x; su[1] = sa * b.y; su[2] = sa * b.z; su[3] = sa * b.w;
+          if (GATEUP) {
+            const float4 b = *reinterpret_cast<const float4*>(p.sw1 + (size_t)ta.e * p.N + col);
+            su[0] = sa * b.x; su[1] = sa * b.y; su[2] = sa * b.z; su[3] = sa * b.w;
+          }
         }
         float gp[4], up[4];
 #pragma unroll
@@ -208,7 +210,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const floatx16 (
             gp[t] = gv;
             up[t] = uv;
           } else {
-            y[t] = acc[i][j][4 * g + t];
+            y[t] = acc[i][j][4 * g + t] * sg[t];  // sg = 1 for bf16 operands
           }
         }
         *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
@@ -750,11 +752,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_bt_kernel(GemmParams p) {
   grouped_gemm<BM, NW, false, false, NA, NB, true>(p, L);
 }
 
-// The gate/up GEMM on FP8 (E4M3) rows and weights with power-of-two row scales.
-template <int BM, int NW, int NA, int NB>
+// The gate/up GEMM on FP8 (E4M3) rows and weights with power-of-two row
+// scales (GATEUP), or a plain product of them (the experts' backward: the
+// output gradients' rows against W_down^T, each output scaled by its row's
+// and its column's factor).
+template <int BM, int NW, bool GATEUP, int NA, int NB>
 __global__ __launch_bounds__(64 * NW) void gemm_fp8_kernel(GemmParams p) {
   MOE_GEMM_LDS_RING
-  grouped_gemm<BM, NW, true, true, NA, NB>(p, L);
+  grouped_gemm<BM, NW, GATEUP, true, NA, NB>(p, L);
 }
 
 // Weight gradients of the expert products (section "专家计算：padding、
@@ -997,14 +1002,15 @@ void launch_gemm_bt(int bm, const GemmParams& p, hipStream_t s) {
   }
 }
 
+template <bool GATEUP>
 void launch_gemm_fp8(int bm, const GemmParams& p, hipStream_t s) {
   const dim3 grid(p.grid), block(64 * kWaves);
   if (bm == 256) {
-    hipLaunchKernelGGL((gemm_fp8_kernel<256, kWaves, 2, 3>), grid, block, 0, s, p);
-    hipLaunchKernelGGL((ksplit_reduce_kernel<256, kWaves, true, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gemm_fp8_kernel<256, kWaves, GATEUP, 2, 3>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ksplit_reduce_kernel<256, kWaves, GATEUP, true>), grid, block, 0, s, p);
   } else {
-    hipLaunchKernelGGL((gemm_fp8_kernel<128, kWaves, 3, 3>), grid, block, 0, s, p);
-    hipLaunchKernelGGL((ksplit_reduce_kernel<128, kWaves, true, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gemm_fp8_kernel<128, kWaves, GATEUP, 3, 3>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ksplit_reduce_kernel<128, kWaves, GATEUP, true>), grid, block, 0, s, p);
   }
 }
 
@@ -1072,7 +1078,7 @@ hipError_t launch_gate_up_fp8(const FfnShape& fs, const void* X8, const float* x
   if (fs.grid1 == 0) return hipSuccess;
   GemmParams p{X8, offset, map1, Wg8, Wu8, static_cast<bf16*>(A), x_scale, s_gate, s_up,
                E, h, f, f, fs.nt1, fs.mt1, part, fs.split_max, fs.grid1};
-  launch_gemm_fp8(fs.bm1, p, s);
+  launch_gemm_fp8<true>(fs.bm1, p, s);
   return hipGetLastError();
 }
 
@@ -1119,6 +1125,17 @@ hipError_t launch_dgrad(const FfnShape& fs, const void* A, const int32_t* offset
                E, K, N, N, fs.nt2, fs.mt2, part, fs.split_max, fs.grid2};
   p.K0 = K0;
   launch_gemm_bt(fs.bm2, p, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dgrad_fp8(const FfnShape& fs, const void* A8, const float* sa,
+                            const int32_t* offset, const int32_t* map2, const void* W8,
+                            const float* sw, void* C, float* part, int E, int N, int K,
+                            hipStream_t s) {
+  if (fs.grid2 == 0) return hipSuccess;
+  GemmParams p{A8, offset, map2, W8, nullptr, static_cast<bf16*>(C), sa, sw, nullptr,
+               E, K, N, N, fs.nt2, fs.mt2, part, fs.split_max, fs.grid2};
+  launch_gemm_fp8<false>(fs.bm2, p, s);
   return hipGetLastError();
 }
 

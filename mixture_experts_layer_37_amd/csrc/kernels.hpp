@@ -155,6 +155,17 @@ hipError_t launch_gate_up_save(const FfnShape& fs, const void* X, const int32_t*
 // Weight gradients: C_e[m][n] = sum over expert e's rows r (offset[e] ..
 // offset[e+1]-1) of A[r][m] B[r][n], A [rows][lda] (columns 0..M-1) and B
 // [rows][ldb] (columns 0..N-1) bf16 row-major; C [E][M][N].
+// FP8 rows (codes, power-of-two row scales) back to bf16, exactly; cols a
+// multiple of 8.
+hipError_t launch_dequant_rows_fp8(const void* q, const float* scale, int64_t rows, int cols,
+                                   void* out, hipStream_t s);
+// FP8 product for the experts' backward: C[rows][N] = (A8 rows x sa) (W8_e rows
+// x sw)^T with A8 [rows][K] and W8 [E][N][K] codes, sw [E][N]; tiles and grid
+// of fs's second product.
+hipError_t launch_dgrad_fp8(const FfnShape& fs, const void* A8, const float* sa,
+                            const int32_t* offset, const int32_t* map2, const void* W8,
+                            const float* sw, void* C, float* part, int E, int N, int K,
+                            hipStream_t s);
 hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const int32_t* offset,
                         void* C, int E, int M, int N, int ncu, hipStream_t s);
 hipError_t launch_combine_bwd(const void* dOut, const void* Y, const int32_t* slot,

@@ -292,3 +292,26 @@ def test_staged_backward_argument_checks():
     assert router(cfg, alpha=float("nan")) == B.MOE_ERR_INVALID_ARG
     need = B.workspace_size(cfg, B.MOE_WS_ROUTER_BACKWARD)
     assert router(cfg, ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE
+
+
+def test_fp8_gradient_argument_checks():
+    fake, other = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)
+
+    def ffn8(c, sdT=fake, dYs=fake):
+        return status("moe_expert_ffn_backward_fp8", ctypes.byref(c), fake, fake, fake, fake,
+                      fake, sdT, fake, dYs, None, None, other, other, other, other, fake,
+                      1 << 40, None)
+    assert ffn8(cfg_of(h=320)) == B.MOE_ERR_UNSUPPORTED  # h a multiple of 128
+    assert ffn8(cfg_of(h=384), sdT=None) == B.MOE_ERR_INVALID_ARG
+    assert ffn8(cfg_of(h=384), dYs=None) == B.MOE_ERR_INVALID_ARG
+    # the layer call: codes without scales, and h not a multiple of 128
+    ex = B.moe_backward_extras()
+    ex.W_downT8 = 0x3000
+
+    def bwd(c):
+        return status("moe_layer_backward", ctypes.byref(c), fake, fake, fake, fake, fake, fake,
+                      fake, fake, fake, fake, fake, fake, 0.0, 0.0, other, other, None, other,
+                      other, other, None, ctypes.byref(ex), fake, 1 << 40, None)
+    assert bwd(cfg_of(h=384)) == B.MOE_ERR_INVALID_ARG
+    ex.s_downT = 0x3000
+    assert bwd(cfg_of(h=320)) == B.MOE_ERR_UNSUPPORTED

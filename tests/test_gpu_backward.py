@@ -455,3 +455,73 @@ def test_backward_deterministic_and_stream_ordered():
     for o in outs:
         for n in ref:
             assert torch.equal(ref[n], o[n]), n
+
+
+# --------------------------------------------------------------------------- FP8 gradients
+FP8_DECODE = np.array([O.fp8_e4m3_decode(c) for c in range(256)])
+
+
+def fp8_down_weights(x):
+    """W_down^T quantised row-wise: codes [E, f, h] and scales [E, f]."""
+    return B.moe_quantize_rows_fp8(x["W_down"].transpose(1, 2).contiguous())
+
+
+@pytest.mark.parametrize("name", ["fp8_grad_small", "fp8_grad_v3"])
+def test_fp8_output_gradients(name):
+    # the experts' output gradients as FP8 rows: codes bit for bit against the
+    # oracle's quantisation of the GPU's own dY rows, the staged call against
+    # the oracle's expert_backward_fp8, and the layer call equal to the staged
+    # path bit for bit and close to the oracle's layer_backward with FP8
+    # gradients
+    w = {"fp8_grad_small": L.SMALL["mixtral_small"].replace(name=name, h=256, f=384,
+                                                           capacity_factor=0.8),
+         "fp8_grad_v3": L.SMALL["deepseek_small"].replace(name=name, h=384, f=192)}[name]
+    x = I.make_inputs(w, seed=9, device=DEV)
+    fields = ["logits", "topk_idx", "topk_gate", "slot", "row_token", "count", "kept", "offset",
+              "X", "Y"]
+    cfg, g = L.run_layer(w, x, fields=fields)
+    gen = torch.Generator(device=DEV).manual_seed(14)
+    dOut = torch.randn((w.T, w.h), generator=gen, device=DEV).to(torch.bfloat16)
+    WdT8, sdT = fp8_down_weights(x)
+    rows_max, bf = B.max_rows(cfg), torch.bfloat16
+    offset = L.to_np(g["offset"]).astype(np.int64)
+    rows = int(offset[-1])
+    # staged: combine backward, quantise the dY rows, the experts' FP8 backward
+    dY = torch.zeros((rows_max, w.h), dtype=bf, device=DEV)
+    dgate = torch.empty((w.T, w.k), dtype=torch.float32, device=DEV)
+    B.moe_combine_backward(cfg, dOut, g["Y"], g["slot"], g["topk_gate"], dY, dgate)
+    dY8, sy = B.moe_quantize_rows_fp8(dY)
+    dX = torch.empty((rows_max, w.h), dtype=bf, device=DEV)
+    st = {n: torch.empty_like(x[m]) for n, m in (("dW_gate", "W_gate"), ("dW_up", "W_up"),
+                                                 ("dW_down", "W_down"))}
+    B.moe_expert_ffn_backward_fp8(cfg, g["X"], g["offset"], x["W_gate"], x["W_up"], WdT8, sdT,
+                                  dY8, sy, dX, st["dW_gate"], st["dW_up"], st["dW_down"])
+    torch.cuda.synchronize()
+    q_ref, s_ref = O.quantize_rows_fp8(L.f64(dY[:rows]))
+    q_got = FP8_DECODE[L.to_np(dY8[:rows]).astype(np.int64)]
+    np.testing.assert_array_equal(q_got, q_ref)
+    np.testing.assert_array_equal(L.f64(sy[:rows]), s_ref)
+    eX, eWg, eWu, eWd = O.expert_backward_fp8(L.f64(g["X"][:rows]), offset, L.f64(x["W_gate"]),
+                                              L.f64(x["W_up"]), L.f64(x["W_down"]), q_ref, s_ref)
+    assert rel(L.f64(dX[:rows]), eX) <= TOL
+    for n, ref in (("dW_gate", eWg), ("dW_up", eWu), ("dW_down", eWd)):
+        assert rel(L.f64(st[n]), ref) <= TOL, n
+    # the layer call
+    out = {"dU": torch.empty_like(x["U"]),
+           "dW_r": torch.empty((w.h, w.E), dtype=torch.float32, device=DEV),
+           "db_r": torch.empty((w.E,), dtype=torch.float32, device=DEV),
+           "dW_gate": torch.empty_like(x["W_gate"]), "dW_up": torch.empty_like(x["W_up"]),
+           "dW_down": torch.empty_like(x["W_down"])}
+    B.moe_layer_backward(cfg, x["U"], x["W_r"], x["W_gate"], x["W_up"], x["W_down"], g["logits"],
+                         g["topk_idx"], g["topk_gate"], g["slot"], g["count"], g["offset"], dOut,
+                         out["dU"], out["dW_r"], out["dW_gate"], out["dW_up"], out["dW_down"],
+                         db_r=out["db_r"], alpha=0.01, c_z=1e-3, W_downT8=WdT8, s_downT=sdT)
+    torch.cuda.synchronize()
+    for n in ("dW_gate", "dW_up", "dW_down"):
+        assert torch.equal(out[n], st[n]), n
+    ref = O.layer_backward(L.f64(x["U"]), L.f64(x["W_r"]), L.f64(x["W_gate"]), L.f64(x["W_up"]),
+                           L.f64(x["W_down"]), oracle_routing(w, g), L.f64(dOut),
+                           score=L.ORACLE_MODE[w.score], gate=L.ORACLE_MODE[w.gate],
+                           alpha=0.01, c_z=1e-3, fp8_down_grad=True)
+    for n in out:
+        assert rel(L.f64(out[n]), ref[n]) <= TOL, n
