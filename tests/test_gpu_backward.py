@@ -245,13 +245,28 @@ def full_case(full_cases, name):
     return full_cases[name]
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_weight_gradients(full_cases, name):
+@pytest.mark.parametrize("name,fp8", [(n, False) for n in FULL] + [("mixtral_bf16", True)])
+def test_full_size_weight_gradients(full_cases, name, fp8):
+    # fp8: the experts' output gradients as FP8 rows; W_down's per-column
+    # scales are column-local and the dY rows do not depend on the weights,
+    # so the restriction to J stays exact
     w, x, g = full_case(full_cases, name)
-    L.log(f"[bwd full wgrad] {name}")
+    L.log(f"[bwd full wgrad] {name}{' fp8 gradients' if fp8 else ''}")
     gen = torch.Generator(device=DEV).manual_seed(7)
     dOut = torch.randn((w.T, w.h), generator=gen, device=DEV).to(torch.bfloat16)
-    got = run_backward(w, x, g, dOut, 0.01, 1e-3)
+    if fp8:
+        WdT8, sdT = fp8_down_weights(x)
+        got = {n: torch.empty_like(x[m]) for n, m in (("dW_gate", "W_gate"), ("dW_up", "W_up"),
+                                                      ("dW_down", "W_down"), ("dU", "U"))}
+        got["dW_r"] = torch.empty((w.h, w.E), dtype=torch.float32, device=DEV)
+        B.moe_layer_backward(B.make_config(w), x["U"], x["W_r"], x["W_gate"], x["W_up"],
+                             x["W_down"], g["logits"], g["topk_idx"], g["topk_gate"], g["slot"],
+                             g["count"], g["offset"], dOut, got["dU"], got["dW_r"],
+                             got["dW_gate"], got["dW_up"], got["dW_down"], alpha=0.01, c_z=1e-3,
+                             W_downT8=WdT8, s_downT=sdT)
+        torch.cuda.synchronize()
+    else:
+        got = run_backward(w, x, g, dOut, 0.01, 1e-3)
     rng = np.random.default_rng(1)
     J = np.unique(np.concatenate([[0, w.f - 1], rng.choice(w.f, 14, replace=False)]))
     Jt = torch.as_tensor(J, device=DEV)
@@ -266,7 +281,7 @@ def test_full_size_weight_gradients(full_cases, name):
     ref = O.layer_backward(L.f64(x["U"]), L.f64(x["W_r"]), sub(x["W_gate"], 1),
                            sub(x["W_up"], 1), sub(x["W_down"], 2), oracle_routing(w, g),
                            L.f64(dOut), score=L.ORACLE_MODE[w.score],
-                           gate=L.ORACLE_MODE[w.gate], **shared)
+                           gate=L.ORACLE_MODE[w.gate], fp8_down_grad=fp8, **shared)
     kept = L.to_np(g["kept"])
     for n, dim in (("dW_gate", 1), ("dW_up", 1), ("dW_down", 2)):
         G = sub(got[n], dim)
