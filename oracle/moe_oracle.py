@@ -421,6 +421,14 @@ def z_loss_logit_grad(H) -> np.ndarray:
     return 2.0 / T * lse[:, None] * e / e.sum(axis=1, keepdims=True)
 
 
+def round_bf16(x) -> np.ndarray:
+    """float32 values rounded to bfloat16 (8 significant bits), to nearest,
+    ties to even, as float64."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def expert_backward(X, offset, W_gate, W_up, W_down, dY):
     """The experts' products backward for rows X of the experts in offset and
     their output gradients dY: a = SiLU(g) u with g = X W_gate^T, u = X W_up^T
@@ -482,9 +490,10 @@ def layer_backward(U, W_r, W_gate, W_up, W_down, fwd: dict, dOut, *, score: str,
     Shared experts (Ws_*): each adds SwiGLU(u) with weight 1 to every token,
     so its output gradient is dOut itself (dWs_gate, dWs_up, dWs_down).
 
-    fp8_down_grad: the experts' output gradients dY are quantised row-wise to
-    FP8 before they reach the experts (as the activations are before the
-    up-projection), and the experts work on the dequantised rows: the
+    fp8_down_grad: the experts' output gradients dY, as the layer stores them
+    (bf16), are quantised row-wise to FP8 before they reach the experts (as
+    the activations are before the up-projection), and the experts work on
+    the dequantised rows: the
     down-projection's input gradient dA = dY W_down against W_down quantised
     per output column (rows of W_down^T), and dW_down = dY^T a (see
     expert_backward_fp8).  Also returns dYq and dY_scale.
@@ -515,7 +524,9 @@ def layer_backward(U, W_r, W_gate, W_up, W_down, fwd: dict, dOut, *, score: str,
                 dgate[t, r] = dOut[t] @ Y[slot[t, r]]
     fp8 = {}
     if fp8_down_grad:
-        dYq, sy = quantize_rows_fp8(dY)
+        # quantised as the layer stores dY: g dOut rounded to float32, then to
+        # bf16 (the decision on each code is taken in the layer's precision)
+        dYq, sy = quantize_rows_fp8(round_bf16(dY.astype(np.float32)))
         fp8 = {"dYq": dYq, "dY_scale": sy}
         dX, dWg, dWu, dWd = expert_backward_fp8(X, off, Wg, Wu, Wd, dYq, sy)
     else:

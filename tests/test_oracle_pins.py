@@ -804,3 +804,18 @@ def test_fp8_backward_within_the_rounding_bound():
         assert 0 < rel(n) < 2 ** -2, (n, rel(n))
     # the router's gradient does not see the experts' input gradients
     np.testing.assert_array_equal(a["dW_r"], b["dW_r"])
+
+
+def test_round_bf16():
+    # against torch's conversion, ties to even, on random values and exact
+    # midpoints between neighbouring bf16 values
+    import torch
+    r = rng(26)
+    # midpoints: a bf16 value's bits with only the half-ulp bit set below them
+    hi = r.integers(0x0080, 0x7F00, 4000, dtype=np.uint32) << 16
+    sign = r.integers(0, 2, 4000, dtype=np.uint32) << 31
+    mid = (hi | sign | 0x8000).view(np.float32)
+    x = np.concatenate([(r.normal(0, 1, 5000) * np.exp2(r.integers(-20, 20, 5000)))
+                        .astype(np.float32), mid])
+    want = torch.from_numpy(x).to(torch.bfloat16).float().numpy().astype(np.float64)
+    np.testing.assert_array_equal(O.round_bf16(x), want)
