@@ -824,10 +824,11 @@ int32_t run_ffn_backward(const Dims& d, const FfnBwdWs& w, void* ws, const void*
     MOE_TRY(launch_dgrad(w.fsA, dY, offset, map, Wd, Wd, h, dA, part, E, f, h, s));
   MOE_TRY(launch_swiglu_bwd(dA, GU, offset, E, d.rows_max, f, dGU, s));
   MOE_TRY(launch_dgrad(w.fsX, dGU, offset, map, Wg, Wu, f, dX, part, E, h, 2 * f, s));
-  MOE_TRY(launch_wgrad(dY, h, A, f, offset, dWd, E, h, f, ncu, s));
-  MOE_TRY(launch_wgrad(dGU, 2 * f, X, h, offset, dWg, E, f, h, ncu, s));
+  const int64_t rows = d.rows_max;
+  MOE_TRY(launch_wgrad(dY, h, A, f, offset, dWd, E, h, f, rows, ncu, s));
+  MOE_TRY(launch_wgrad(dGU, 2 * f, X, h, offset, dWg, E, f, h, rows, ncu, s));
   MOE_TRY(launch_wgrad(static_cast<const char*>(dGU) + (size_t)f * 2, 2 * f, X, h, offset, dWu,
-                       E, f, h, ncu, s));
+                       E, f, h, rows, ncu, s));
   return MOE_OK;
 }
 
@@ -1090,11 +1091,11 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
       MOE_TRY(launch_swiglu_bwd(sdA, sGU, offs, 1, T, fsh, sdGU, s));
       MOE_TRY(launch_dgrad(w.shX, sdGU, offs, smap, Wsg, Wsu, fsh, dXi, part, 1, h, 2 * fsh, s));
       MOE_TRY(launch_wgrad(dOut, h, sA, fsh, offs, static_cast<char*>(extra->dWs_down) + i * fh * 2,
-                           1, h, fsh, ncu, s));
+                           1, h, fsh, T, ncu, s));
       MOE_TRY(launch_wgrad(sdGU, 2 * fsh, U, h, offs,
-                           static_cast<char*>(extra->dWs_gate) + i * fh * 2, 1, fsh, h, ncu, s));
+                           static_cast<char*>(extra->dWs_gate) + i * fh * 2, 1, fsh, h, T, ncu, s));
       MOE_TRY(launch_wgrad(static_cast<char*>(sdGU) + (size_t)fsh * 2, 2 * fsh, U, h, offs,
-                           static_cast<char*>(extra->dWs_up) + i * fh * 2, 1, fsh, h, ncu, s));
+                           static_cast<char*>(extra->dWs_up) + i * fh * 2, 1, fsh, h, T, ncu, s));
     }
   }
   // 5. router: dH (and dZ for the noise term), then dU and dW_r, db_r (dW_noise)

@@ -866,6 +866,271 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_kernel(GemmParams p) {
   }
 }
 
+// Weight gradients as one stream of K steps per workgroup.  The workgroup's
+// tiles (the same XCD slices as gemm_wgrad_kernel) run their K steps back to
+// back through the copy ring, A two steps ahead and B three, so the copies of
+// a tile's first steps are in flight while the previous tile computes, which
+// matters when experts have few rows and tiles only one or two K steps.  Each
+// tile's epilogue stores straight from the accumulators with buffer stores,
+// after the copies issued in its last step: every lane issues exactly
+// kWgStores of them (the expert's output resource ends at its last row, and a
+// column past N is sent past the resource's end), so the next step's wait
+// can leave them in flight.  Vector memory loads and stores complete in issue
+// order on this family: vmcnt <= BG + kWgStores there still covers every copy
+// that step needs.  Requires M N 2 < 2^31 - 256 and N a multiple of 8
+// (checked by the launcher).
+// s_waitcnt through the builtin rather than inline asm, so that the
+// compiler's own wait insertion sees it and knows which copies have landed
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8;
+// the counters not waited on are left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm_seen() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0_seen() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+constexpr int kWgStores = 16;  // 2 row blocks x 4 column blocks x 2 runs of 8 columns
+constexpr int kPastEnd = 0x7ffffff0;  // a byte offset past every output resource
+// A copy cursor: plain integers (uniform, kept in SGPRs); the buffer
+// resources are rebuilt from them at each copy.
+struct WgCursor {
+  int u, j, KT;  // tile of the share, its K step, its K steps
+  int r0, n;     // the expert's first row and its rows (0: none, or past the share)
+  int m0, nt;    // the tile's first column of A (row of C_e) and its n-tile
+  int e;         // the expert
+};
+__device__ __forceinline__ void wg_load(const GemmParams& p, WgCursor& c, int uend, int mt_n,
+                                        int nt_n) {
+  c.j = 0;
+  if (c.u < uend) {
+    // the same numbering as wgrad_unit; the offsets are read through the
+    // constant address space, i.e. with scalar loads, which do not wait on
+    // the copies and stores in flight as a vector load would
+    typedef __attribute__((address_space(4))) const int32_t cint;
+    const int per = mt_n * nt_n;
+    const int e = c.u / per, r = c.u - e * per, mt = r / nt_n;
+    cint* off = (cint*)p.offset;
+    c.r0 = off[e];
+    c.n = off[e + 1] - c.r0;
+    c.KT = max(1, (c.n + BK - 1) / BK);
+    c.m0 = mt * 256;
+    c.nt = r - mt * nt_n;
+    c.e = e;
+  } else {  // past the share: copies from an empty resource read zeros
+    c.KT = 1;
+    c.r0 = c.n = c.m0 = c.nt = c.e = 0;
+  }
+}
+template <int NA, int NB>
+__global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_stream_kernel(GemmParams p) {
+  static_assert(NA == 2 && NB == 3, "ring of 2 A and 3 B slots");
+  constexpr int BM = 256, NW = kWaves, WR = 2 * BM / NW, RBLK = WR / 32;
+  MOE_GEMM_LDS_RING
+  const int mt_n = (p.M + BM - 1) / BM, nt_n = (p.N + BN - 1) / BN;
+  const int units = p.E * mt_n * nt_n;
+  int u, uend, ustep;
+  if ((gridDim.x & 7) == 0) {
+    const int per = (units + 7) >> 3, xcd = blockIdx.x & 7;
+    u = xcd * per + (blockIdx.x >> 3);
+    uend = min(units, xcd * per + per);
+    ustep = gridDim.x >> 3;
+  } else {
+    u = blockIdx.x;
+    uend = units;
+    ustep = gridDim.x;
+  }
+  if (u >= uend) return;
+  using CP = CopyPlan<BM, NW, false, false, true, true>;
+  constexpr int AG = CP::AG, BG = CP::BG;
+  const CP cp(0, p.Nout, p.K);  // A [rows][K = lda], B [rows][Nout = ldb]
+  // copy cursors: A runs two stream steps ahead of the compute, B three
+  WgCursor ca, cb;
+  ca.u = cb.u = u;
+  wg_load(p, ca, uend, mt_n, nt_n);
+  wg_load(p, cb, uend, mt_n, nt_n);
+  auto advance = [&](WgCursor& c) __attribute__((always_inline)) {
+    if (++c.j == c.KT) {
+      c.u += ustep;
+      wg_load(p, c, uend, mt_n, nt_n);
+    }
+  };
+  // the same copies as CopyPlan::issueA / issueB over the resources of
+  // wgrad_src: A [rows][K = lda] from column m0, B [rows][Nout = ldb] from
+  // column BN nt, both over the expert's rows r0 .. r0 + n - 1
+  auto copyA = [&](bf16* as) __attribute__((always_inline)) {
+    const size_t pa = (size_t)p.K * 2, ma = (size_t)ca.m0 * 2;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(
+        static_cast<const char*>(p.A) + (size_t)ca.r0 * pa + ma, ca.n > 0 ? ca.n * pa - ma : 0);
+#pragma unroll
+    for (int q = 0; q < AG; ++q) dma16(r, as + (cp.wave + NW * q) * 8 * BK, cp.voA[q], ca.j * cp.astep);
+    advance(ca);
+  };
+  auto copyB = [&](bf16* bs) __attribute__((always_inline)) {
+    const size_t pb = (size_t)p.Nout * 2, nb = (size_t)cb.nt * BN * 2;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(
+        static_cast<const char*>(p.W0) + (size_t)cb.r0 * pb + nb, cb.n > 0 ? cb.n * pb - nb : 0);
+#pragma unroll
+    for (int q = 0; q < BG; ++q) dma16(r, bs + (cp.wave + NW * q) * 8 * BK, cp.voB[q], cb.j * cp.bstep);
+    advance(cb);
+  };
+  copyA(L.a[0]);
+  copyB(L.b[0]);
+  copyA(L.a[1]);
+  copyB(L.b[1]);
+  copyB(L.b[2]);
+
+  const int wave = cp.wave, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, khalf = lane >> 5;
+  // transposing fragment reads, as in gemm_tile (AT and BT operands)
+  auto tr_off = [&](int width, int x0) {
+    const int l16 = lane & 15, kr = 8 * khalf + (l16 >> 2);
+    const int c = (x0 + 16 * ((lane >> 4) & 1) + 4 * (l16 & 3)) >> 3;
+    return kr * (width * 2) + ((c ^ trswz(kr)) * 16) + 8 * (l16 & 1);
+  };
+  int aoff[RBLK], boff[4];
+#pragma unroll
+  for (int i = 0; i < RBLK; ++i) aoff[i] = tr_off(BM, wm * WR + i * 32);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) boff[j] = tr_off(BN, wn * 128 + j * 32);
+  auto fragT = [&](const bf16* slot, int off, int slice, int width) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const char* q = reinterpret_cast<const char*>(slot) + off + slice * (16 * width * 2);
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(q));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(q + 4 * width * 2));
+    const v4s v[2] = {lo, hi};
+    bf16x8 r;
+    __builtin_memcpy(&r, v, 16);
+    return r;
+  };
+  floatx16 acc[RBLK][4];
+  auto zero = [&]() {
+#pragma unroll
+    for (int i = 0; i < RBLK; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  };
+  zero();
+  bf16x8 fa[2][RBLK], fb[2][4];
+  auto fetch = [&](const bf16* as, const bf16* bs, int slice, int st) {
+#pragma unroll
+    for (int i = 0; i < RBLK; ++i) fa[st][i] = fragT(as, aoff[i], slice, BM);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[st][j] = fragT(bs, boff[j], slice, BN);
+  };
+  auto mfmas = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < RBLK; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[st][j], fa[st][i], acc[i][j], 0, 0, 0);
+  };
+  constexpr int NSL = Elt<false>::kSlices;
+  constexpr int NM = RBLK * 4, NR = RBLK * 2 + 4 * 2, NC = AG + BG;
+  constexpr int CPM = (NC + NM - 1) / NM, RPM = (NR + NM - 1) / NM;
+  auto order = [&]() {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m * RPM < NR) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+    }
+  };
+  auto order_copies = [&]() {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m * CPM < NC) __builtin_amdgcn_sched_group_barrier(0x020, CPM, 0);
+      if (m * RPM < NR) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+    }
+  };
+  // the tile being computed
+  WgCursor cc;
+  cc.u = u;
+  wg_load(p, cc, uend, mt_n, nt_n);
+  // epilogue: lane holds row l32 of each 32 x 32 block and columns
+  // 8 g + 4 khalf + 0..3 (see store_tile).  The two lanes of a row swap
+  // halves (v_permlane32_swap exchanges lanes 32..63 of its first operand
+  // with lanes 0..31 of its second), after which lane (l32, khalf) holds
+  // columns 16 h + 8 khalf + 0..7 for h = 0, 1 and stores each run of 8 as
+  // one 16-byte store.  C_e is row block e of [E M][N].
+  auto store = [&]() __attribute__((always_inline)) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const size_t r0 = (size_t)cc.e * p.M + cc.m0;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + r0 * p.N, (size_t)(p.M - cc.m0) * p.N * 2);
+#pragma unroll
+    for (int i = 0; i < RBLK; ++i) {
+      const int rb = (wm * WR + i * 32 + l32) * p.N * 2;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const floatx16& a = acc[i][j];
+          // runs g = 2 h (x) and 2 h + 1 (y) of this lane, 4 columns each
+          const unsigned x0 = pack_bf16x2(a[8 * h], a[8 * h + 1]);
+          const unsigned x1 = pack_bf16x2(a[8 * h + 2], a[8 * h + 3]);
+          const unsigned y0 = pack_bf16x2(a[8 * h + 4], a[8 * h + 5]);
+          const unsigned y1 = pack_bf16x2(a[8 * h + 6], a[8 * h + 7]);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+          const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+          const int col = cc.nt * BN + wn * 128 + j * 32 + 16 * h + 8 * khalf;
+          const int off = col < p.N ? rb + col * 2 : kPastEnd;
+          __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
+        }
+    }
+  };
+  bool stored = false;  // the previous step issued a tile's stores
+  // one stream step on slots (as, bs); (nas, nbs) hold the next step.  On
+  // entry fa/fb[0] hold slice 0 of this step.  Returns whether work remains.
+  auto step = [&](bf16* as, bf16* bs, const bf16* nas, const bf16* nbs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sl = 0; sl + 1 < NSL; ++sl) {
+      fetch(as, bs, sl + 1, (sl + 1) & 1);
+      mfmas(sl & 1);
+      order();
+    }
+    // the next step's A and B have landed; B three steps ahead (issued
+    // last) and the stores of a tile that ended at the previous step may
+    // still be in flight
+    if (stored) wait_vm_seen<BG + kWgStores>();
+    else wait_vm_seen<BG>();
+    wait_lgkm0_seen();  // this wave is done reading (as, bs)
+    barrier_only();
+    copyA(as);
+    copyB(bs);
+    fetch(nas, nbs, 0, 0);
+    mfmas((NSL - 1) & 1);
+    order_copies();
+    stored = false;
+    if (++cc.j < cc.KT) return true;
+    store();
+    asm volatile("" ::: "memory");
+    zero();
+    stored = true;
+    cc.u += ustep;
+    if (cc.u >= uend) return false;
+    wg_load(p, cc, uend, mt_n, nt_n);
+    return true;
+  };
+  wait_vm_seen<0>();
+  barrier_only();
+  fetch(L.a[0], L.b[0], 0, 0);
+  // the slots line up again every 6 steps: the body is unrolled over them so
+  // that every LDS address is a constant (the compiler then sees which slot
+  // each copy in flight writes, and waits for none of them before reading
+  // another)
+  for (bool live = true; live;) {
+#pragma unroll
+    for (int q = 0; q < 6; ++q)
+      if (live) live = step(L.a[q % 2], L.b[q % 3], L.a[(q + 1) % 2], L.b[(q + 1) % 3]);
+  }
+  wait_vm_seen<0>();  // copies past the share, and the last stores
+}
+
 // Sum of the K chunks of the tail tiles, in chunk order, then the same
 // epilogue as gemm_bf16_kernel.  Workgroup b handles tail tile b / 8 of XCD
 // b % 8 (if that XCD split its tail); thread i reads the partial groups that
@@ -1094,7 +1359,7 @@ hipError_t launch_gate_up_save(const FfnShape& fs, const void* X, const int32_t*
 }
 
 hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const int32_t* offset,
-                        void* C, int E, int M, int N, int ncu, hipStream_t s) {
+                        void* C, int E, int M, int N, int64_t rows, int ncu, hipStream_t s) {
   const int units = E * ((M + 255) / 256) * ((N + BN - 1) / BN);
   if (units == 0) return hipSuccess;
   // K: A's row pitch, Nout: B's row pitch (the epilogue writes rows of N)
@@ -1102,7 +1367,13 @@ hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const in
                E, lda, N, ldb, 0, 0, nullptr, 1, 0};
   p.M = M;
   const int grid = std::min(units, ncu);
-  hipLaunchKernelGGL((gemm_wgrad_kernel<2, 3>), dim3(grid), dim3(64 * kWaves), 0, s, p);
+  // short tiles gain from the stream (DeepSeek-V3 shape, 128 rows an expert:
+  // 20% faster); with long ones the staged epilogue of gemm_wgrad_kernel
+  // wins slightly (Mixtral shape, 1024 rows an expert: 2.6%)
+  if (rows <= 512 * (int64_t)E && (size_t)M * N * 2 < (size_t)kPastEnd - 256 && N % 8 == 0)
+    hipLaunchKernelGGL((gemm_wgrad_stream_kernel<2, 3>), dim3(grid), dim3(64 * kWaves), 0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_wgrad_kernel<2, 3>), dim3(grid), dim3(64 * kWaves), 0, s, p);
   return hipGetLastError();
 }
 

@@ -166,8 +166,11 @@ hipError_t launch_dgrad_fp8(const FfnShape& fs, const void* A8, const float* sa,
                             const int32_t* offset, const int32_t* map2, const void* W8,
                             const float* sw, void* C, float* part, int E, int N, int K,
                             hipStream_t s);
+// rows: a bound on the experts' rows in total; with at most 512 per expert on
+// average (tiles of at most 8 K steps) the tiles run as one stream of K steps
+// per workgroup (gemm_wgrad_stream_kernel).
 hipError_t launch_wgrad(const void* A, int lda, const void* B, int ldb, const int32_t* offset,
-                        void* C, int E, int M, int N, int ncu, hipStream_t s);
+                        void* C, int E, int M, int N, int64_t rows, int ncu, hipStream_t s);
 hipError_t launch_combine_bwd(const void* dOut, const void* Y, const int32_t* slot,
                               const float* gate, void* dY, float* dgate, int T, int h, int k,
                               hipStream_t s);
