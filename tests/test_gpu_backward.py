@@ -43,6 +43,10 @@ BWD = {
                                                         E=32, capacity_factor=0.0),
     "heavy_drops": I.WORKLOADS["mixtral_bf16"].replace(name="heavy_drops", T=1024, h=192, f=256,
                                                        capacity_factor=0.05),
+    # 6 tokens, 16 experts, k = 1: at least 10 experts get no rows, and their
+    # weight gradients must be written as exact zeros
+    "idle_experts": I.WORKLOADS["mixtral_bf16"].replace(name="idle_experts", T=6, h=128, f=192,
+                                                        E=16, k=1),
 }
 
 
@@ -107,6 +111,8 @@ def test_backward(name):
         errs[n] = rel(L.f64(got[n]), ref[n])
     # weight gradients expert by expert; an expert without rows gets zeros
     kept = L.to_np(g["kept"])
+    if name == "idle_experts":
+        assert (kept == 0).sum() >= 10, kept
     for n in ("dW_gate", "dW_up", "dW_down"):
         G = L.f64(got[n])
         worst = 0.0
