@@ -120,10 +120,18 @@ def copy_calibration(nbytes: int):
     y = torch.empty_like(x)
     x.fill_(1)
     torch.cuda.synchronize()
-    for _ in range(3):
+    # events around each copy (no extra launches, so the counter scaling is
+    # unchanged); each copy reads and writes nbytes
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    for i in range(3):
         y.copy_(x)
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3,
+                      "ms": ms, "read_plus_write_GBps": 2 * nbytes / (min(ms) * 1e-3) / 1e9}),
+          flush=True)
 
 
 def cpu_model() -> str:
