@@ -866,19 +866,6 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_kernel(GemmParams p) {
   }
 }
 
-// Weight gradients as one stream of K steps per workgroup.  The workgroup's
-// tiles (the same XCD slices as gemm_wgrad_kernel) run their K steps back to
-// back through the copy ring, A two steps ahead and B three, so the copies of
-// a tile's first steps are in flight while the previous tile computes, which
-// matters when experts have few rows and tiles only one or two K steps.  Each
-// tile's epilogue stores straight from the accumulators with buffer stores,
-// after the copies issued in its last step: every lane issues exactly
-// kWgStores of them (the expert's output resource ends at its last row, and a
-// column past N is sent past the resource's end), so the next step's wait
-// can leave them in flight.  Vector memory loads and stores complete in issue
-// order on this family: vmcnt <= BG + kWgStores there still covers every copy
-// that step needs.  Requires M N 2 < 2^31 - 256 and N a multiple of 8
-// (checked by the launcher).
 // s_waitcnt through the builtin rather than inline asm, so that the
 // compiler's own wait insertion sees it and knows which copies have landed
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8;
@@ -923,6 +910,19 @@ __device__ __forceinline__ void wg_load(const GemmParams& p, WgCursor& c, int ue
     c.r0 = c.n = c.m0 = c.nt = c.e = 0;
   }
 }
+// Weight gradients as one stream of K steps per workgroup.  The workgroup's
+// tiles (the same XCD slices as gemm_wgrad_kernel) run their K steps back to
+// back through the copy ring, A two steps ahead and B three, so the copies of
+// a tile's first steps are in flight while the previous tile computes, which
+// matters when experts have few rows and tiles only one or two K steps.  Each
+// tile's epilogue stores straight from the accumulators with buffer stores,
+// after the copies issued in its last step: every lane issues exactly
+// kWgStores of them (the expert's output resource ends at its last row, and a
+// column past N is sent past the resource's end), so the next step's wait
+// can leave them in flight.  Vector memory loads and stores complete in issue
+// order on this family: vmcnt <= BG + kWgStores there still covers every copy
+// that step needs.  Requires M N 2 < 2^31 - 256 and N a multiple of 8
+// (checked by the launcher).
 template <int NA, int NB>
 __global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_stream_kernel(GemmParams p) {
   static_assert(NA == 2 && NB == 3, "ring of 2 A and 3 B slots");
