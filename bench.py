@@ -167,9 +167,10 @@ def cpu_baseline(w, x, g, budget_s: float) -> dict:
 
     t0 = time.perf_counter()
     U = f64(x["U"])
+    # the noisy router's draws from the oracle's own counter-based generator
+    noise = O.philox_normals(w.T, w.E, w.rng_seed, w.rng_offset) if w.noisy else None
     H = O.router_logits(U, f64(x["W_r"]), None if x["b_r"] is None else f64(x["b_r"]),
-                        None if x["W_noise"] is None else f64(x["W_noise"]),
-                        None if x["noise"] is None else f64(x["noise"]))
+                        None if x["W_noise"] is None else f64(x["W_noise"]), noise)
     C = O.capacity(w.T, w.E, w.k, w.capacity_factor)
     r = O.route(H, w.k, w.score, w.gate, C, w.fill,
                 None if x.get("b_sel") is None else f64(x["b_sel"]), max(1, w.n_groups),
@@ -270,8 +271,7 @@ def main():
                  "dW_down": torch.empty_like(x["W_down"])}
         extra = {}
         if w.noisy:
-            extra = {"W_noise": x["W_noise"], "noise": x["noise"],
-                     "dW_noise": torch.empty((w.h, w.E), device=dev)}
+            extra = {"W_noise": x["W_noise"], "dW_noise": torch.empty((w.h, w.E), device=dev)}
         if args.fp8_grad:  # a one-time weight preparation, like a model load
             WdT8, sdT = B.moe_quantize_rows_fp8(x["W_down"].transpose(1, 2).contiguous())
             extra.update(W_downT8=WdT8, s_downT=sdT)
@@ -293,10 +293,10 @@ def main():
         common = dict(aux=aux, stage_events=None if events is None else events[:nst + 1], ws=ws, b_sel=x["b_sel"],
                       Ws_gate=x["Ws_gate"], Ws_up=x["Ws_up"], Ws_down=x["Ws_down"])
         if w.fp8_up:
-            B.moe_layer_forward_fp8(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], x["noise"],
+            B.moe_layer_forward_fp8(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"],
                                     W8g, sg, W8u, su, x["W_down"], out, **common)
         else:
-            B.moe_layer_forward(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], x["noise"],
+            B.moe_layer_forward(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"],
                                 x["W_gate"], x["W_up"], x["W_down"], out, **common)
         if args.backward:
             B.moe_layer_backward(cfg, x["U"], x["W_r"], x["W_gate"], x["W_up"], x["W_down"],

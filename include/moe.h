@@ -3,7 +3,7 @@
  * on one gfx950 GPU (MI355X).
  *
  * The layer (page "MoE 与专家并行", hs-black.github.io/posts/scaling-moe):
- *   logits  H = U W_r (+ b_r) (+ noise * softplus(U W_noise))
+ *   logits  H = U W_r (+ b_r) (+ z * softplus(U W_noise), z ~ N(0,1))
  *                      section "路由器：打分、top-k、加权求和", eq. H and G(x)
  *   scores  softmax or sigmoid; top-k; gates raw or renormalised
  *                      section "softmax 门控还是 sigmoid 门控", table
@@ -83,13 +83,15 @@ typedef struct {
   int64_t f;      /* expert intermediate size (d_e)                            */
   int64_t E;      /* experts, 1..256                                           */
   int64_t k;      /* experts per token, 1..min(E, 8)                           */
-  int32_t dtype;  /* moe_dtype.  BF16 needs h % 64 == 0 and f % 64 == 0;
-                     F32 needs h % 4 == 0 and f % 4 == 0 (else UNSUPPORTED)     */
+  int32_t dtype;  /* moe_dtype.  BF16 needs h % 64 == 0 and f % 64 == 0, one
+                     expert matrix below 2 GiB (h * max(f, f_shared) * 2 < 2^31)
+                     and h, f, f_shared below 2^22; F32 needs h % 4 == 0 and
+                     f % 4 == 0 (else UNSUPPORTED)                             */
   int32_t score;  /* moe_score                                                 */
   int32_t gate;   /* moe_gate                                                  */
   int32_t cap_mode; /* moe_cap                                                 */
   int32_t fill;   /* moe_fill                                                  */
-  int32_t noisy;  /* 1: add noise * softplus(U W_noise) to the logits          */
+  int32_t noisy;  /* 1: add z * softplus(U W_noise) to the logits (z below)  */
   double capacity_factor; /* > 0, finite, in [1e-6, 1e6]; <= 0 means no limit
                              (dropless: C = T)                                 */
   int64_t min_capacity;   /* C is raised to at least this (0: no floor)        */
@@ -104,6 +106,20 @@ typedef struct {
   int64_t n_shared;     /* shared experts taking every token with weight 1
                            (section "细粒度专家与共享专家", eq. h'_t), 0..16      */
   int64_t f_shared;     /* their intermediate size (same divisibility as f)     */
+  /* Noisy routing (noisy = 1; section "路由器：打分、top-k、加权求和", eq.
+   * G(x)): the standard-normal factor z[t,i] of token t and expert i is drawn
+   * by the library from a counter-based generator, Philox-4x64-10 (Salmon,
+   * Moraes, Dror and Shaw, SC'11) with key (seed, 0) and counter
+   * (t*E + i + rng_offset mod 2^64, 0, 0, 0), mapped to N(0,1) by the
+   * Box-Muller transform of the block's first two words w0, w1:
+   * u1 = (w0 >> 11) * 2^-53 + 2^-53, u2 = (w1 >> 11) * 2^-53,
+   * z = sqrt(-2 ln u1) cos(2 pi u2), evaluated in double precision and rounded
+   * to float32.  The same (seed, rng_offset) give the same draws on every
+   * call and launch shape; a caller that wants fresh noise per step advances
+   * rng_offset by at least T*E.  The backward draws them again from the
+   * same fields, so it must get the forward's config.                       */
+  uint64_t seed;
+  uint64_t rng_offset;
 } moe_config;
 
 /* Optional outputs of moe_layer_forward.  Any NULL field is kept in the
@@ -133,6 +149,8 @@ typedef struct {
                           (g in columns 0..f-1, u in f..2f-1); bf16 layers
                           without FP8 only (else MOE_ERR_UNSUPPORTED)          */
   void* A;             /* [rows_max, f] SwiGLU products a = SiLU(g) u         */
+  float* noise;        /* [T, E] the standard-normal draws z of a noisy layer
+                          (see moe_config.seed); ignored when cfg->noisy = 0 */
 } moe_aux_outputs;
 
 /* Workspace sizes per entry point. */
@@ -168,8 +186,9 @@ int32_t moe_workspace_size(const moe_config* cfg, int32_t entry, size_t* bytes);
  *  U [T,h], W_r [h,E]: required.  b_r [E]: optional per-expert logit bias.
  *  b_sel [E]: optional selection-only bias (section "无辅助损失的负载均衡"):
  *  the top-k is taken on s + b_sel while the gates keep using s.
- *  W_noise [h,E] and noise [T,E] (standard-normal draws supplied by the
- *  caller): required iff cfg->noisy.
+ *  W_noise [h,E]: required iff cfg->noisy; the logits then get
+ *  z * softplus(U W_noise) with z drawn from cfg->seed and cfg->rng_offset
+ *  (see moe_config).  noise_out [T,E]: optional output of those draws.
  *  topk_idx [T,k], topk_gate [T,k]: required outputs, rank order.  Selection
  *  is by the key (-H, expert index) on the float32 logits; with b_sel or
  *  cfg->n_groups > 1 by (-(s + b_sel), expert index) on float32 scores,
@@ -179,12 +198,14 @@ int32_t moe_workspace_size(const moe_config* cfg, int32_t entry, size_t* bytes);
  *  (sigmoid), the numerator of P.
  *  ws: MOE_WS_ROUTE bytes. */
 int32_t moe_route(const moe_config* cfg, const void* U, const void* W_r, const float* b_r,
-                  const float* b_sel, const void* W_noise, const float* noise,
+                  const float* b_sel, const void* W_noise, float* noise_out,
                   int32_t* topk_idx, float* topk_gate, float* logits, float* prob_sum,
                   void* ws, size_t ws_bytes, void* stream);
 
 /* Dispatch: capacity cut and permutation (capacity section).
  *  topk_idx [T,k] in: expert ids (values outside [0,E) are undefined input).
+ *  A token may name one expert at several ranks (each is one assignment,
+ *  placed in fill order like any other).
  *  count [E], kept [E], offset [E+1], slot [T,k], row_token [rows_max]: outputs
  *  (count is before the cut; offset is the exclusive scan of kept; rows of
  *  expert e are offset[e]..offset[e+1]-1 in fill order).
@@ -248,7 +269,8 @@ int32_t moe_router_z_loss(const moe_config* cfg, const float* logits, float* z_l
 
 /* The whole layer: route, dispatch, experts (and shared experts), combine,
  * statistics.
- *  b_sel: optional selection bias as in moe_route.  Ws_gate, Ws_up, Ws_down:
+ *  b_r, b_sel, W_noise: as in moe_route (aux->noise receives the draws).
+ *  Ws_gate, Ws_up, Ws_down:
  *  shared-expert weights as in moe_shared_ffn, required iff cfg->n_shared > 0;
  *  their products run in the gate_up and down stages.
  *  out [T,h] required.  aux: optional outputs (struct pointer may be NULL).
@@ -256,7 +278,7 @@ int32_t moe_router_z_loss(const moe_config* cfg, const float* logits, float* z_l
  *  `stream` at the stage boundaries (for timing).  ws: MOE_WS_LAYER bytes. */
 int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
                           const float* b_r, const float* b_sel, const void* W_noise,
-                          const float* noise, const void* W_gate, const void* W_up,
+                          const void* W_gate, const void* W_up,
                           const void* W_down, const void* Ws_gate, const void* Ws_up,
                           const void* Ws_down, void* out, const moe_aux_outputs* aux,
                           void* const* stage_events, void* ws, size_t ws_bytes,
@@ -265,10 +287,11 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
 /* ---------------------------------------------------------------- backward
  * The parts of the backward that only some layers have (each group NULL when
  * the layer lacks the part):
- *  noisy routing (cfg->noisy): W_noise [h,E] and noise [T,E] as given to the
- *  forward; dW_noise [h,E] float32 out.  The logits' term
- *  noise * softplus(U W_noise) passes the logit gradient on through
- *  softplus' = sigmoid (page "MoE 与专家并行", router section, eq. G(x)).
+ *  noisy routing (cfg->noisy): W_noise [h,E] as given to the forward;
+ *  dW_noise [h,E] float32 out.  The logits' term z * softplus(U W_noise)
+ *  passes the logit gradient on through softplus' = sigmoid (page
+ *  "MoE 与专家并行", router section, eq. G(x)); z is drawn again from
+ *  cfg->seed and cfg->rng_offset, which must be the forward's.
  *  shared experts (cfg->n_shared > 0): Ws_gate, Ws_up [n_shared,f_shared,h],
  *  Ws_down [n_shared,h,f_shared] as given to the forward; dWs_gate, dWs_up,
  *  dWs_down of the same shapes, bf16, out.  Each takes every token with
@@ -284,7 +307,6 @@ int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
  *  128 (else MOE_ERR_UNSUPPORTED). */
 typedef struct {
   const void* W_noise;
-  const float* noise;
   float* dW_noise;
   const void* Ws_gate;
   const void* Ws_up;
@@ -383,7 +405,7 @@ int32_t moe_expert_ffn_backward_fp8(const moe_config* cfg, const void* X, const 
  * db_r (nullable) = column sums of dH.  dOut is the gradient that reaches u_t
  * directly (the residual; add the shared experts' input gradients to it);
  * dX [rows_max,h] the experts' input gradients.  extra: the noise part
- * (W_noise, noise, dW_noise) for noisy layers.  ws: MOE_WS_ROUTER_BACKWARD. */
+ * (W_noise, dW_noise) for noisy layers.  ws: MOE_WS_ROUTER_BACKWARD. */
 int32_t moe_router_backward(const moe_config* cfg, const void* U, const void* W_r,
                             const float* logits, const int32_t* topk_idx, const float* topk_gate,
                             const int32_t* slot, const int32_t* count, const float* dgate,
@@ -439,7 +461,7 @@ int32_t moe_expert_ffn_fp8(const moe_config* cfg, const void* X8, const float* x
  * ws: MOE_WS_LAYER bytes. */
 int32_t moe_layer_forward_fp8(const moe_config* cfg, const void* U, const void* W_r,
                               const float* b_r, const float* b_sel, const void* W_noise,
-                              const float* noise, const void* W8_gate, const float* s_gate,
+                              const void* W8_gate, const float* s_gate,
                               const void* W8_up, const float* s_up, const void* W_down,
                               const void* Ws_gate, const void* Ws_up, const void* Ws_down,
                               void* out, const moe_aux_outputs* aux, void* const* stage_events,

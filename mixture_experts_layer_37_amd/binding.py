@@ -13,6 +13,8 @@ from typing import Optional
 
 import torch
 
+from . import debug as _debug
+
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
@@ -43,6 +45,7 @@ class moe_config(ctypes.Structure):
         ("capacity_factor", ctypes.c_double), ("min_capacity", ctypes.c_int64),
         ("n_groups", ctypes.c_int64), ("topk_groups", ctypes.c_int64),
         ("n_shared", ctypes.c_int64), ("f_shared", ctypes.c_int64),
+        ("seed", ctypes.c_uint64), ("rng_offset", ctypes.c_uint64),
     ]
 
 
@@ -50,7 +53,7 @@ class moe_aux_outputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "topk_idx", "topk_gate", "logits", "slot", "row_token", "count", "kept", "offset",
         "prob_sum", "f", "P", "aux_loss", "maxvio", "n_dropped", "X", "Y", "Y_shared",
-        "z_loss", "GU", "A")]
+        "z_loss", "GU", "A", "noise")]
 
 
 AUX_FIELDS = [n for n, _ in moe_aux_outputs._fields_]
@@ -58,7 +61,7 @@ AUX_FIELDS = [n for n, _ in moe_aux_outputs._fields_]
 
 class moe_backward_extras(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "W_noise", "noise", "dW_noise", "Ws_gate", "Ws_up", "Ws_down", "dWs_gate", "dWs_up",
+        "W_noise", "dW_noise", "Ws_gate", "Ws_up", "Ws_down", "dWs_gate", "dWs_up",
         "dWs_down", "W_downT8", "s_downT")]
 
 _lib = None
@@ -87,9 +90,9 @@ def lib() -> ctypes.CDLL:
             "moe_update_bias": (I32, [cfgp, P, P, ctypes.c_float, P]),
             "moe_stats": (I32, [cfgp] + [P] * 8 + [P]),
             "moe_router_z_loss": (I32, [cfgp, P, P, P]),
-            "moe_layer_forward": (I32, [cfgp] + [P] * 13 + [ctypes.POINTER(moe_aux_outputs), P,
+            "moe_layer_forward": (I32, [cfgp] + [P] * 12 + [ctypes.POINTER(moe_aux_outputs), P,
                                                           P, SZ, P]),
-            "moe_layer_forward_fp8": (I32, [cfgp] + [P] * 15 + [ctypes.POINTER(moe_aux_outputs),
+            "moe_layer_forward_fp8": (I32, [cfgp] + [P] * 14 + [ctypes.POINTER(moe_aux_outputs),
                                                               P, P, SZ, P]),
             "moe_quantize_rows_fp8": (I32, [P, I64, I64, P, P, P]),
             "moe_combine_backward": (I32, [cfgp] + [P] * 6 + [P]),
@@ -128,7 +131,8 @@ _CP = {"assignments": MOE_CAP_ASSIGNMENTS, "tokens": MOE_CAP_TOKENS}
 
 
 def make_config(w, T: Optional[int] = None) -> moe_config:
-    """moe_config from a Workload (mixture_experts_layer_37_amd.inputs)."""
+    """moe_config from a Workload (mixture_experts_layer_37_amd.inputs); the
+    noisy router's draws use the workload's rng_seed and rng_offset."""
     return moe_config(T=w.T if T is None else T, h=w.h, f=w.f, E=w.E, k=w.k,
                       dtype=_DT[w.dtype], score=_SC[w.score], gate=_GT[w.gate],
                       cap_mode=_CP[w.cap_mode], fill=_FL[w.fill], noisy=int(w.noisy),
@@ -137,7 +141,9 @@ def make_config(w, T: Optional[int] = None) -> moe_config:
                       n_groups=int(getattr(w, "n_groups", 0)),
                       topk_groups=int(getattr(w, "topk_groups", 0)),
                       n_shared=int(getattr(w, "n_shared", 0)),
-                      f_shared=int(getattr(w, "f_shared", 0)))
+                      f_shared=int(getattr(w, "f_shared", 0)),
+                      seed=int(getattr(w, "rng_seed", 0)),
+                      rng_offset=int(getattr(w, "rng_offset", 0)))
 
 
 def capacity(cfg: moe_config) -> int:
@@ -200,8 +206,10 @@ def new_workspace(cfg: moe_config, entry: int, device="cuda") -> torch.Tensor:
 
 
 # --------------------------------------------------------------------------- entry points
-def moe_route(cfg, U, W_r, b_r, W_noise, noise, topk_idx, topk_gate, logits=None,
-              prob_sum=None, ws=None, stream=None, b_sel=None):
+def moe_route(cfg, U, W_r, b_r, W_noise, topk_idx, topk_gate, logits=None,
+              prob_sum=None, ws=None, stream=None, b_sel=None, noise_out=None):
+    """Router outputs; noise_out [T, E] float32 (noisy layers, optional): the
+    standard-normal draws the library made from cfg.seed and cfg.rng_offset."""
     T, h, E, k = cfg.T, cfg.h, cfg.E, cfg.k
     dt = _elem_dtype(cfg)
     need = workspace_size(cfg, MOE_WS_ROUTE)
@@ -211,7 +219,7 @@ def moe_route(cfg, U, W_r, b_r, W_noise, noise, topk_idx, topk_gate, logits=None
         _ptr(U, "U", (T, h), dt), _ptr(W_r, "W_r", (h, E), dt),
         _ptr(b_r, "b_r", (E,), torch.float32), _ptr(b_sel, "b_sel", (E,), torch.float32),
         _ptr(W_noise, "W_noise", (h, E), dt) if cfg.noisy else None,
-        _ptr(noise, "noise", (T, E), torch.float32) if cfg.noisy else None,
+        _ptr(noise_out, "noise_out", (T, E), torch.float32) if cfg.noisy else None,
         _ptr(topk_idx, "topk_idx", (T, k), torch.int32),
         _ptr(topk_gate, "topk_gate", (T, k), torch.float32),
         _ptr(logits, "logits", (T, E), torch.float32),
@@ -235,6 +243,15 @@ def moe_dispatch(cfg, U, topk_idx, X, row_token, slot, count, kept, offset, ws=N
         _ptr(kept, "kept", (E,), torch.int32), _ptr(offset, "offset", (E + 1,), torch.int32),
     ]
     _check(lib().moe_dispatch(ctypes.byref(cfg), *args, wp, wn, _stream(stream)), "moe_dispatch")
+    if _debug.enabled():
+        _debug_check(cfg, topk_idx, slot, row_token, count, kept, offset, stream)
+
+
+def _debug_check(cfg, topk_idx, slot, row_token, count, kept, offset, stream):
+    """MOE_DEBUG=1: wait for the stream, download the maps and validate them."""
+    (torch.cuda.current_stream() if stream is None else stream).synchronize()
+    _debug.check_dispatch_maps(*(t.cpu().numpy() for t in (topk_idx, slot, row_token, count,
+                                                            kept, offset)), capacity(cfg))
 
 
 def moe_expert_ffn(cfg, X, offset, W_gate, W_up, W_down, Y, ws=None, stream=None):
@@ -330,6 +347,7 @@ _AUX_SPEC = {
     "z_loss": (lambda c, r: (1,), torch.float32),
     "GU": (lambda c, r: (r, 2 * c.f), None),
     "A": (lambda c, r: (r, c.f), None),
+    "noise": (lambda c, r: (c.T, c.E), torch.float32),
 }
 
 # the forward's outputs that moe_layer_backward can take instead of recomputing
@@ -346,10 +364,10 @@ def alloc_aux(cfg, device="cuda", fields=None) -> dict:
     return out
 
 
-def _layer_call(fn_name, cfg, U, W_r, b_r, W_noise, noise, weights, W_down, out, aux,
+def _layer_call(fn_name, cfg, U, W_r, b_r, W_noise, weights, W_down, out, aux,
                 stage_events, ws, stream, b_sel, Ws_gate, Ws_up, Ws_down):
     """Argument marshalling shared by moe_layer_forward and moe_layer_forward_fp8;
-    weights: the already checked pointers that stand between noise and W_down."""
+    weights: the already checked pointers that stand between W_noise and W_down."""
     T, h, f, E = cfg.T, cfg.h, cfg.f, cfg.E
     ns, fs = cfg.n_shared, cfg.f_shared
     rows = max_rows(cfg)
@@ -377,7 +395,6 @@ def _layer_call(fn_name, cfg, U, W_r, b_r, W_noise, noise, weights, W_down, out,
         _ptr(U, "U", (T, h), dt), _ptr(W_r, "W_r", (h, E), dt),
         _ptr(b_r, "b_r", (E,), torch.float32), _ptr(b_sel, "b_sel", (E,), torch.float32),
         _ptr(W_noise, "W_noise", (h, E), dt) if cfg.noisy else None,
-        _ptr(noise, "noise", (T, E), torch.float32) if cfg.noisy else None,
         *weights,
         _ptr(W_down, "W_down", (E, h, f), dt),
         _ptr(Ws_gate, "Ws_gate", (ns, fs, h), dt) if ns else None,
@@ -388,9 +405,12 @@ def _layer_call(fn_name, cfg, U, W_r, b_r, W_noise, noise, weights, W_down, out,
     _check(getattr(lib(), fn_name)(ctypes.byref(cfg), *args, ctypes.byref(a),
                                    ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None,
                                    wp, wn, _stream(stream)), fn_name)
+    maps = ("topk_idx", "slot", "row_token", "count", "kept", "offset")
+    if _debug.enabled() and aux and all(aux.get(n) is not None for n in maps):
+        _debug_check(cfg, *(aux[n] for n in maps), stream)
 
 
-def moe_layer_forward(cfg, U, W_r, b_r, W_noise, noise, W_gate, W_up, W_down, out, aux=None,
+def moe_layer_forward(cfg, U, W_r, b_r, W_noise, W_gate, W_up, W_down, out, aux=None,
                       stage_events=None, ws=None, stream=None, b_sel=None, Ws_gate=None,
                       Ws_up=None, Ws_down=None):
     """The whole layer.  aux: dict of optional output tensors (see alloc_aux).
@@ -399,11 +419,11 @@ def moe_layer_forward(cfg, U, W_r, b_r, W_noise, noise, W_gate, W_up, W_down, ou
     selection bias and the shared-expert weights (cfg.n_shared > 0)."""
     E, f, h, dt = cfg.E, cfg.f, cfg.h, _elem_dtype(cfg)
     weights = [_ptr(W_gate, "W_gate", (E, f, h), dt), _ptr(W_up, "W_up", (E, f, h), dt)]
-    _layer_call("moe_layer_forward", cfg, U, W_r, b_r, W_noise, noise, weights, W_down, out, aux,
+    _layer_call("moe_layer_forward", cfg, U, W_r, b_r, W_noise, weights, W_down, out, aux,
                 stage_events, ws, stream, b_sel, Ws_gate, Ws_up, Ws_down)
 
 
-def moe_layer_forward_fp8(cfg, U, W_r, b_r, W_noise, noise, W8_gate, s_gate, W8_up, s_up,
+def moe_layer_forward_fp8(cfg, U, W_r, b_r, W_noise, W8_gate, s_gate, W8_up, s_up,
                           W_down, out, aux=None, stage_events=None, ws=None, stream=None,
                           b_sel=None, Ws_gate=None, Ws_up=None, Ws_down=None):
     """The layer with the FP8 dispatch and up-projection: W8_* are E4M3 codes
@@ -414,20 +434,21 @@ def moe_layer_forward_fp8(cfg, U, W_r, b_r, W_noise, noise, W8_gate, s_gate, W8_
                _ptr(s_gate, "s_gate", (E, f), torch.float32),
                _ptr(W8_up, "W8_up", (E, f, h), torch.uint8),
                _ptr(s_up, "s_up", (E, f), torch.float32)]
-    _layer_call("moe_layer_forward_fp8", cfg, U, W_r, b_r, W_noise, noise, weights, W_down, out,
+    _layer_call("moe_layer_forward_fp8", cfg, U, W_r, b_r, W_noise, weights, W_down, out,
                 aux, stage_events, ws, stream, b_sel, Ws_gate, Ws_up, Ws_down)
 
 
 def moe_layer_backward(cfg, U, W_r, W_gate, W_up, W_down, logits, topk_idx, topk_gate, slot,
                        count, offset, dOut, dU, dW_r, dW_gate, dW_up, dW_down, db_r=None,
-                       alpha=0.0, c_z=0.0, saved=None, W_noise=None, noise=None, dW_noise=None,
+                       alpha=0.0, c_z=0.0, saved=None, W_noise=None, dW_noise=None,
                        Ws_gate=None, Ws_up=None, Ws_down=None, dWs_gate=None, dWs_up=None,
                        dWs_down=None, W_downT8=None, s_downT=None, ws=None, stream=None):
     """Gradients of <dOut, out> + alpha aux_loss + c_z z_loss for the routing of a
     forward (logits ... offset from its aux outputs).  dU, dW_gate, dW_up,
     dW_down bf16; dW_r [h, E] and db_r [E] float32.  saved: None (the experts
     are recomputed) or a dict with the forward's aux outputs X, GU, A and Y.
-    Noisy layers: W_noise, noise as in the forward, dW_noise [h, E] float32.
+    Noisy layers: W_noise as in the forward (the draws come again from cfg's seed
+    and rng_offset), dW_noise [h, E] float32.
     Shared experts: Ws_* as in the forward, dWs_* of the same shapes (bf16).
     FP8 output gradients: W_downT8 [E, f, h] uint8 and s_downT [E, f], the
     row-wise E4M3 quantisation of W_down transposed."""
@@ -465,7 +486,6 @@ def moe_layer_backward(cfg, U, W_r, W_gate, W_up, W_down, logits, topk_idx, topk
         ns, fs = cfg.n_shared, cfg.f_shared
         if cfg.noisy:
             ex.W_noise = _ptr(W_noise, "W_noise", (h, E), bf)
-            ex.noise = _ptr(noise, "noise", (T, E), torch.float32)
             ex.dW_noise = _ptr(dW_noise, "dW_noise", (h, E), torch.float32)
         if ns:
             ex.Ws_gate = _ptr(Ws_gate, "Ws_gate", (ns, fs, h), bf)
@@ -537,7 +557,7 @@ def moe_expert_ffn_backward_fp8(cfg, X, offset, W_gate, W_up, W_downT8, s_downT,
 
 
 def moe_router_backward(cfg, U, W_r, logits, topk_idx, topk_gate, slot, count, dgate, dOut, dX,
-                        dU, dW_r, db_r=None, alpha=0.0, c_z=0.0, W_noise=None, noise=None,
+                        dU, dW_r, db_r=None, alpha=0.0, c_z=0.0, W_noise=None,
                         dW_noise=None, ws=None, stream=None):
     """dH from the gates' gradient (and the aux and z terms), then
     dU = dOut + sum dX[slot] + dH W_r^T, dW_r, db_r (dW_noise for noisy layers)."""
@@ -550,7 +570,6 @@ def moe_router_backward(cfg, U, W_r, logits, topk_idx, topk_gate, slot, count, d
     if cfg.noisy:
         ex = moe_backward_extras()
         ex.W_noise = _ptr(W_noise, "W_noise", (h, E), bf)
-        ex.noise = _ptr(noise, "noise", (T, E), torch.float32)
         ex.dW_noise = _ptr(dW_noise, "dW_noise", (h, E), torch.float32)
     _check(lib().moe_router_backward(
         ctypes.byref(cfg), _ptr(U, "U", (T, h), bf), _ptr(W_r, "W_r", (h, E), bf),
@@ -598,6 +617,8 @@ def moe_dispatch_fp8(cfg, U, topk_idx, X8, x_scale, row_token, slot, count, kept
     ]
     _check(lib().moe_dispatch_fp8(ctypes.byref(cfg), *args, wp, wn, _stream(stream)),
            "moe_dispatch_fp8")
+    if _debug.enabled():
+        _debug_check(cfg, topk_idx, slot, row_token, count, kept, offset, stream)
 
 
 def moe_expert_ffn_fp8(cfg, X8, x_scale, offset, W8_gate, s_gate, W8_up, s_up, W_down, Y,

@@ -75,6 +75,15 @@ int32_t check_config(const moe_config* c) {
   if (c->T * c->k >= lim || c->h >= lim / 8 || c->f >= lim / 8) return MOE_ERR_UNSUPPORTED;
   if (c->n_shared > 0 && (c->f_shared >= lim / 8 || c->T * c->n_shared >= lim))
     return MOE_ERR_UNSUPPORTED;
+  if (c->dtype == MOE_BF16) {
+    // The grouped GEMMs address one expert's weight matrix (h x f elements)
+    // through a buffer resource of at most 2^31 - 1 bytes and their per-lane
+    // copy offsets (row < 256 of a tile, times a row of K = h or f elements)
+    // as 32-bit integers.
+    const int64_t fmax = std::max(c->f, c->n_shared > 0 ? c->f_shared : 0);
+    if (c->h * fmax * 2 >= lim) return MOE_ERR_UNSUPPORTED;
+    if (256 * std::max(c->h, fmax) * 2 >= lim) return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 
@@ -340,7 +349,7 @@ int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP
 
 int32_t run_route(const Dims& d, const moe_config* c, const RouteWs& w, const void* U,
                   const void* W_r, const float* b_r, const float* b_sel, const void* W_noise,
-                  const float* noise, int32_t* idx, float* gate, float* logits, void* ws,
+                  float* noise_out, int32_t* idx, float* gate, float* logits, void* ws,
                   hipStream_t s) {
   RouteParams p;
   p.T = (int)d.T;
@@ -354,7 +363,9 @@ int32_t run_route(const Dims& d, const moe_config* c, const RouteWs& w, const vo
   p.b_sel = b_sel;
   p.n_groups = (int)d.n_groups;
   p.topk_groups = (int)d.topk_groups;
-  p.noise = c->noisy ? noise : nullptr;
+  p.seed = c->seed;
+  p.rng_offset = c->rng_offset;
+  p.noise_out = c->noisy ? noise_out : nullptr;
   p.topk_idx = idx;
   p.topk_gate = gate;
   p.logits = logits;
@@ -559,7 +570,7 @@ int32_t moe_workspace_size(const moe_config* cfg, int32_t entry, size_t* bytes) 
 }
 
 int32_t moe_route(const moe_config* cfg, const void* U, const void* W_r, const float* b_r,
-                  const float* b_sel, const void* W_noise, const float* noise,
+                  const float* b_sel, const void* W_noise, float* noise_out,
                   int32_t* topk_idx, float* topk_gate, float* logits, float* prob_sum,
                   void* ws, size_t ws_bytes, void* stream) {
   int32_t st = check_config(cfg);
@@ -567,12 +578,12 @@ int32_t moe_route(const moe_config* cfg, const void* U, const void* W_r, const f
   const Dims d = dims_of(cfg);
   if (d.T > 0 && (!U || !topk_idx || !topk_gate)) return MOE_ERR_INVALID_ARG;
   if (!W_r || !ws) return MOE_ERR_INVALID_ARG;
-  if (cfg->noisy && (!W_noise || !noise)) return MOE_ERR_INVALID_ARG;
+  if (cfg->noisy && !W_noise) return MOE_ERR_INVALID_ARG;
   Plan pl;
   const RouteWs w = plan_route(d, cfg->noisy, pl);
   if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = run_route(d, cfg, w, U, W_r, b_r, b_sel, W_noise, noise, topk_idx, topk_gate, logits,
+  st = run_route(d, cfg, w, U, W_r, b_r, b_sel, W_noise, noise_out, topk_idx, topk_gate, logits,
                  ws, s);
   if (st != MOE_OK) return st;
   if (prob_sum)
@@ -684,9 +695,8 @@ namespace {
 // The layer; f8 != NULL runs the FP8 dispatch and up-projection (its weights
 // replace W_gate and W_up).
 int32_t layer_impl(const moe_config* cfg, const void* U, const void* W_r, const float* b_r,
-                   const float* b_sel, const void* W_noise, const float* noise,
-                   const void* W_gate, const void* W_up, const void* W_down, const void* Ws_gate,
-                   const void* Ws_up, const void* Ws_down, void* out, const moe_aux_outputs* aux,
+                   const float* b_sel, const void* W_noise, const void* W_gate,
+                   const void* W_up, const void* W_down, const void* Ws_gate, const void* Ws_up, const void* Ws_down, void* out, const moe_aux_outputs* aux,
                    void* const* stage_events, void* ws, size_t ws_bytes, void* stream,
                    Fp8Up* f8) {
   int32_t st = f8 ? check_fp8(cfg) : check_config(cfg);
@@ -695,7 +705,7 @@ int32_t layer_impl(const moe_config* cfg, const void* U, const void* W_r, const 
   if (d.T > 0 && (!U || !out)) return MOE_ERR_INVALID_ARG;
   if (!W_r || !W_gate || !W_up || !W_down || !ws) return MOE_ERR_INVALID_ARG;
   if (d.ns > 0 && (!Ws_gate || !Ws_up || !Ws_down)) return MOE_ERR_INVALID_ARG;
-  if (cfg->noisy && (!W_noise || !noise)) return MOE_ERR_INVALID_ARG;
+  if (cfg->noisy && !W_noise) return MOE_ERR_INVALID_ARG;
   if (d.T > 0 && out == U) return MOE_ERR_INVALID_ARG;
   if (aux && aux->GU && (!d.bf16 || f8)) return MOE_ERR_UNSUPPORTED;
   if (stage_events)
@@ -727,8 +737,8 @@ int32_t layer_impl(const moe_config* cfg, const void* U, const void* W_r, const 
   };
 
   MOE_TRY(mark(0));
-  st = run_route(d, cfg, w.route, U, W_r, b_r, b_sel, W_noise, noise, idx, gate, o.logits, ws,
-                 s);
+  st = run_route(d, cfg, w.route, U, W_r, b_r, b_sel, W_noise, o.noise, idx, gate, o.logits,
+                 ws, s);
   if (st != MOE_OK) return st;
   MOE_TRY(mark(1));
   st = run_dispatch(d, cfg, w.disp, U, idx, X, row_token, slot, count, kept, offset, ws, s, xs);
@@ -767,25 +777,25 @@ extern "C" {
 
 int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
                           const float* b_r, const float* b_sel, const void* W_noise,
-                          const float* noise, const void* W_gate, const void* W_up,
+                          const void* W_gate, const void* W_up,
                           const void* W_down, const void* Ws_gate, const void* Ws_up,
                           const void* Ws_down, void* out, const moe_aux_outputs* aux,
                           void* const* stage_events, void* ws, size_t ws_bytes,
                           void* stream) {
-  return layer_impl(cfg, U, W_r, b_r, b_sel, W_noise, noise, W_gate, W_up, W_down, Ws_gate,
+  return layer_impl(cfg, U, W_r, b_r, b_sel, W_noise, W_gate, W_up, W_down, Ws_gate,
                     Ws_up, Ws_down, out, aux, stage_events, ws, ws_bytes, stream, nullptr);
 }
 
 int32_t moe_layer_forward_fp8(const moe_config* cfg, const void* U, const void* W_r,
                               const float* b_r, const float* b_sel, const void* W_noise,
-                              const float* noise, const void* W8_gate, const float* s_gate,
+                              const void* W8_gate, const float* s_gate,
                               const void* W8_up, const float* s_up, const void* W_down,
                               const void* Ws_gate, const void* Ws_up, const void* Ws_down,
                               void* out, const moe_aux_outputs* aux, void* const* stage_events,
                               void* ws, size_t ws_bytes, void* stream) {
   if (!s_gate || !s_up) return MOE_ERR_INVALID_ARG;
   Fp8Up f8{W8_gate, s_gate, W8_up, s_up, nullptr};
-  return layer_impl(cfg, U, W_r, b_r, b_sel, W_noise, noise, W8_gate, W8_up, W_down, Ws_gate,
+  return layer_impl(cfg, U, W_r, b_r, b_sel, W_noise, W8_gate, W8_up, W_down, Ws_gate,
                     Ws_up, Ws_down, out, aux, stage_events, ws, ws_bytes, stream, &f8);
 }
 
@@ -859,7 +869,8 @@ int32_t run_router_backward(const moe_config* cfg, const Dims& d, const RouterBw
   float* dZ = nullptr;
   if (cfg->noisy) {
     dZ = at<float>(ws, w.dZ);
-    MOE_TRY(launch_noise_grad(U, extra->W_noise, dH, extra->noise, dZ, T, h, E, s));
+    MOE_TRY(launch_noise_grad(U, extra->W_noise, dH, cfg->seed, cfg->rng_offset, dZ, T, h, E,
+                              s));
   }
   MOE_TRY(launch_grad_input(dOut, dX, slot, dH, W_r, dZ, cfg->noisy ? extra->W_noise : nullptr,
                             dXs, T > 0 ? ns : 0, dU, T, h, E, k, s));
@@ -870,9 +881,7 @@ int32_t run_router_backward(const moe_config* cfg, const Dims& d, const RouterBw
 }
 
 int32_t check_noise_extras(const moe_config* cfg, const moe_backward_extras* extra) {
-  if (cfg->noisy && (!extra || !extra->W_noise || !extra->dW_noise ||
-                     (cfg->T > 0 && !extra->noise)))
-    return MOE_ERR_INVALID_ARG;
+  if (cfg->noisy && (!extra || !extra->W_noise || !extra->dW_noise)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 

@@ -269,14 +269,16 @@ __global__ __launch_bounds__(256) void grad_input_kernel(const bf16* dOut, const
   }
 }
 
-// Noisy routing: the logits hold noise * softplus(Z) with Z = U W_noise, so
-// dZ = dH * noise * sigmoid(Z) (softplus' = sigmoid; page "MoE 与专家并行",
-// router section, eq. G(x)).  Z is recomputed in float32: a workgroup takes
+// Noisy routing: the logits hold z * softplus(Z) with Z = U W_noise, so
+// dZ = dH * z * sigmoid(Z) (softplus' = sigmoid; page "MoE 与专家并行",
+// router section, eq. G(x)); z, the forward's standard-normal draw of the
+// pair, is drawn again from its counter.  Z is recomputed in float32: a workgroup takes
 // 64 tokens x 64 experts, stages 32 columns of U (transposed) and of W_noise
 // at a time in LDS, and a thread accumulates 4 tokens x 4 experts.
 __global__ __launch_bounds__(256) void noise_grad_kernel(const bf16* U, const bf16* W_n,
-                                                         const float* dH, const float* noise,
-                                                         float* dZ, int T, int h, int E) {
+                                                         const float* dH, uint64_t seed,
+                                                         uint64_t rng_offset, float* dZ, int T,
+                                                         int h, int E) {
   __shared__ __align__(16) float su[32][64];  // su[j][t] = U[t0 + t][j0 + j]
   __shared__ __align__(16) float sw[32][64];  // sw[j][e] = W_noise[j0 + j][e0 + e]
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
@@ -325,7 +327,8 @@ __global__ __launch_bounds__(256) void noise_grad_kernel(const bf16* U, const bf
       const int e = e0 + tx * 4 + q;
       if (e >= E) break;
       const size_t o = (size_t)t * E + e;
-      dZ[o] = dH[o] * noise[o] / (1.f + __expf(-acc[i][q]));
+      const float z = (float)philox_normal(seed, (uint64_t)o + rng_offset);
+      dZ[o] = dH[o] * z / (1.f + __expf(-acc[i][q]));
     }
   }
 }
@@ -464,11 +467,12 @@ hipError_t launch_grad_input(const void* dOut, const void* dX, const int32_t* sl
 }
 
 hipError_t launch_noise_grad(const void* U, const void* W_noise, const float* dH,
-                             const float* noise, float* dZ, int T, int h, int E, hipStream_t s) {
+                             uint64_t seed, uint64_t rng_offset, float* dZ, int T, int h, int E,
+                             hipStream_t s) {
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(noise_grad_kernel, dim3((T + 63) / 64, (E + 63) / 64), dim3(256), 0, s,
-                     static_cast<const bf16*>(U), static_cast<const bf16*>(W_noise), dH, noise,
-                     dZ, T, h, E);
+                     static_cast<const bf16*>(U), static_cast<const bf16*>(W_noise), dH, seed,
+                     rng_offset, dZ, T, h, E);
   return hipGetLastError();
 }
 

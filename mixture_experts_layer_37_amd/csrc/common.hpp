@@ -113,6 +113,37 @@ __device__ __forceinline__ uint2 to_fp8x8(const float* v, int j) {
   return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
+// Standard-normal draw of the noisy router (page "MoE 与专家并行", section
+// "路由器：打分、top-k、加权求和", eq. G(x): an N(0, 1) factor per token and
+// expert) from a counter-based generator, so each (token, expert) pair has
+// its own draw whatever the launch shape: Philox-4x64 with 10 rounds (Salmon,
+// Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3",
+// SC'11), key (seed, 0) and counter (n, 0, 0, 0).  A round takes the two
+// 128-bit products M0 x0 and M1 x2 and maps (x0, x1, x2, x3) to
+// (hi(M1 x2) ^ x1 ^ k0, lo(M1 x2), hi(M0 x0) ^ x3 ^ k1, lo(M0 x0)); the key
+// then grows by the two Weyl increments.  The draw is the Box-Muller
+// transform of u1 = (w0 / 2^11 + 1) 2^-53 in (0, 1] and u2 = (w1 / 2^11)
+// 2^-53 in [0, 1) from the block's first two words, in double precision.
+__device__ __forceinline__ double philox_normal(uint64_t seed, uint64_t n) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+  uint64_t x0 = n, x1 = 0, x2 = 0, x3 = 0, k0 = seed, k1 = 0;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(M0, x0), lo0 = M0 * x0;
+    const uint64_t hi1 = __umul64hi(M1, x2), lo1 = M1 * x2;
+    x0 = hi1 ^ x1 ^ k0;
+    x1 = lo1;
+    x2 = hi0 ^ x3 ^ k1;
+    x3 = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+  const double u1 = (double)((x0 >> 11) + 1) * 0x1p-53;
+  const double u2 = (double)(x1 >> 11) * 0x1p-53;
+  return sqrt(-2.0 * log(u1)) * cos(2.0 * M_PI * u2);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

@@ -134,13 +134,18 @@ __global__ __launch_bounds__(256) void assign_kernel(DispatchParams p) {
     for (int r = 0; r < 8; ++r) {
       if (r >= p.k) break;
       const int e = ex[r];
-      // lanes below holding expert e at any rank (a token holds an expert at most once)
-      uint64_t any = 0;
+      // earlier assignments to expert e in this wave: every rank of the lanes
+      // below that holds e, then this token's own lower ranks that hold e (a
+      // caller's topk_idx may name one expert twice for a token)
+      int lower = 0;
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        if (q < p.k) any |= match_lanes(e, ex[q], ex[q] >= 0);
+        if (q < p.k) lower += __popcll(match_lanes(e, ex[q], ex[q] >= 0) & below);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q < r && ex[q] == e) ++lower;
       if (e >= 0) {
-        int pos = p.base[(size_t)c * p.E + e] + __popcll(any & below);
+        int pos = p.base[(size_t)c * p.E + e] + lower;
         for (int w = 0; w < wave; ++w) pos += wc[w][e];
         const int row = pos < p.C ? p.offset[e] + pos : -1;
         p.slot[(size_t)t * p.k + r] = row;

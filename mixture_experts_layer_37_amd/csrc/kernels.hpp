@@ -19,7 +19,9 @@ struct RouteParams {
   const float* b_sel;    // [E] selection-only bias, or NULL
   int n_groups;          // > 1: group-limited selection over n_groups groups
   int topk_groups;       // groups a token may use
-  const float* noise;
+  uint64_t seed;        // noisy routing: key of the draws' generator
+  uint64_t rng_offset;  // ... and the counter of token 0, expert 0
+  float* noise_out;     // optional [T][E]: the standard-normal draws used
   const void* Wt;    // bf16: W_r transposed to [EP][h], zero rows past E; f32: W_r [h][E]
   const void* Wnt;   // same for W_noise (noisy only)
   int32_t* topk_idx;
@@ -188,7 +190,8 @@ hipError_t launch_grad_input(const void* dOut, const void* dX, const int32_t* sl
                              int E, int k, hipStream_t s);
 // dZ = dH * noise * sigmoid(U W_noise), [T][E] float32.
 hipError_t launch_noise_grad(const void* U, const void* W_noise, const float* dH,
-                             const float* noise, float* dZ, int T, int h, int E, hipStream_t s);
+                             uint64_t seed, uint64_t rng_offset, float* dZ, int T, int h, int E,
+                             hipStream_t s);
 // dW_r = U^T dH, db_r = column sums of dH: TE experts x TJ rows of U per
 // workgroup, the tokens cut into nsplit chunks of tchunk (a multiple of 16)
 // whose float32 partials [nsplit][h + 1][E] are summed afterwards.

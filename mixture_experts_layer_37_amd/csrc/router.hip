@@ -1,4 +1,5 @@
-// Router: logits H = U W_r (+ b_r) (+ noise * softplus(U W_noise)), scores,
+// Router: logits H = U W_r (+ b_r) (+ z * softplus(U W_noise), z the
+// counter-based standard-normal draw of each token and expert), scores,
 // top-k with the (-H, expert index) key, gates, and per-workgroup sums of the
 // score that enters P and of the squared log-sum-exp of the logits (the
 // router z-loss, section "各家的变体", subsection "Router z-loss 与数值稳定",
@@ -54,7 +55,12 @@ __device__ void route_epilogue(const float* L, const float* Ln, double (*Ps)[EP 
       if (e < E) {
         x = L[tt * EP + e];
         if (p.b_r) x += p.b_r[e];
-        if (NOISY) x += p.noise[(size_t)t * E + e] * softplus_f(Ln[tt * EP + e]);
+        if (NOISY) {
+          // the draw of pair (t, e): counter t * E + e + rng_offset (mod 2^64)
+          const float z = (float)philox_normal(p.seed, (uint64_t)t * E + e + p.rng_offset);
+          if (p.noise_out) p.noise_out[(size_t)t * E + e] = z;
+          x += z * softplus_f(Ln[tt * EP + e]);
+        }
         if (p.logits) p.logits[(size_t)t * E + e] = x;
       }
       v[j] = x;

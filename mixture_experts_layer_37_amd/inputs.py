@@ -2,12 +2,15 @@
 
 This module only describes shapes and draws random numbers; it holds none of
 the layer's arithmetic.  Both the GPU path and the CPU oracle are fed from it.
+The noisy router's standard-normal draws are not inputs: the library makes
+them from the workload's rng_seed and rng_offset, and the oracle makes the
+same ones from its own implementation of the same counter-based generator.
 
 Distributions follow the workload descriptions: U ~ N(0, 1); router and
 gate/up weights ~ N(0, 1/h); down weights ~ N(0, 1/f); the Switch-style
 workload adds a per-expert logit bias ~ N(0, 1.5); the noisy workload adds a
-noise-router weight ~ N(0, 1/h) and one standard-normal draw per
-(token, expert).  The second parameter of N(., .) is a variance.
+noise-router weight ~ N(0, 1/h).  The second parameter of N(., .) is a
+variance.
 """
 from __future__ import annotations
 
@@ -44,6 +47,9 @@ class Workload:
     # FP8 dispatch and up-projection (E4M3, power-of-two row scales); the
     # inputs stay bf16 and the weights are quantised once before the forward
     fp8_up: bool = False
+    # noisy routing: key and counter offset of the standard-normal draws
+    rng_seed: int = 0
+    rng_offset: int = 0
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -98,7 +104,7 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", with_experts: bool = T
 
     Expert weights are drawn one expert at a time so that large workloads never
     hold a float32 copy of all weights.  Shapes: U [T, h]; W_r, W_noise [h, E];
-    b_r [E] fp32; noise [T, E] fp32; b_sel [E] fp32; W_gate, W_up [E, f, h];
+    b_r [E] fp32; b_sel [E] fp32; W_gate, W_up [E, f, h];
     W_down [E, h, f]; Ws_gate, Ws_up [n_shared, f_shared, h]; Ws_down
     [n_shared, h, f_shared].  Inputs a workload does not use are None and draw
     nothing, so adding a part never changes the other inputs.
@@ -111,12 +117,7 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", with_experts: bool = T
     x["U"] = _normal((w.T, w.h), 1.0, gen, dev, dt)
     x["W_r"] = _normal((w.h, w.E), 1.0 / w.h, gen, dev, dt)
     x["b_r"] = _normal((w.E,), w.bias_var, gen, dev, torch.float32) if w.bias_var > 0 else None
-    if w.noisy:
-        x["W_noise"] = _normal((w.h, w.E), 1.0 / w.h, gen, dev, dt)
-        x["noise"] = _normal((w.T, w.E), 1.0, gen, dev, torch.float32)
-    else:
-        x["W_noise"] = None
-        x["noise"] = None
+    x["W_noise"] = _normal((w.h, w.E), 1.0 / w.h, gen, dev, dt) if w.noisy else None
     x["b_sel"] = (_normal((w.E,), w.sel_bias_var, gen, dev, torch.float32)
                   if w.sel_bias_var > 0 else None)
     if with_experts:

@@ -15,7 +15,9 @@ unless another page is named):
   * SwiGLU expert, section "从稠密 FFN 到 MoE", equation FFN(u).
   * Layer output with residual, same section, equation h'_t = u_t + sum g FFN.
   * Router logits H = U W_r, section "路由器：打分、top-k、加权求和".
-  * Noisy top-k logits, same section, equation G(x) (Shazeer 2017).
+  * Noisy top-k logits, same section, equation G(x) (Shazeer 2017); the
+    standard-normal draws from Philox-4x64-10 (Salmon et al., SC'11) and the
+    Box-Muller transform, one counter per (token, expert).
   * Scoring/gating variants, section "softmax 门控还是 sigmoid 门控", table.
   * Capacity C = ceil(CF * T * k / E) and token-order fill with drops,
     section "专家容量与丢 token", equation C and its figure; the GShard fill
@@ -87,7 +89,7 @@ def router_logits(U, W_r, b_r=None, W_noise=None, noise=None) -> np.ndarray:
     b_r, when given, is a per-expert bias added to every token's logits.
     W_noise/noise, when given, add the noisy top-k term
     noise[t, i] * softplus((U W_noise)[t, i]) (eq. G(x)); noise holds the
-    standard-normal draws, supplied by the caller.
+    standard-normal draws (philox_normals below gives the layer's).
     """
     U = f64(U)
     H = U @ f64(W_r)
@@ -98,6 +100,76 @@ def router_logits(U, W_r, b_r=None, W_noise=None, noise=None) -> np.ndarray:
             raise ValueError("noisy routing needs the standard-normal draws")
         H = H + f64(noise) * softplus(U @ f64(W_noise))
     return H
+
+
+# --------------------------------------------------------------------------- noise
+# The noisy router's standard-normal draws (router section, eq. G(x): the
+# N(0, 1) factor of each token's and expert's noise term).  The page leaves
+# the generator open; here every (token t, expert i) pair has its own draw
+# from a counter-based generator, so the draws do not depend on how the work
+# is split.  Generator: Philox-4x64 with 10 rounds (Salmon, Moraes, Dror and
+# Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11), the 64-bit,
+# four-word member of the Philox family, with its published multipliers and
+# key increments.  Key (seed, 0); counter (t * E + i + rng_offset mod 2^64,
+# 0, 0, 0).  Normal: the Box-Muller transform of two uniforms taken from the
+# block's first two words, the first one in (0, 1] so its logarithm is finite.
+PHILOX_M = (0xD2E7470EE14C6C93, 0xCA5A826395121157)   # round multipliers
+PHILOX_W = (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)   # key increments per round
+PHILOX_ROUNDS = 10
+_MASK64 = (1 << 64) - 1
+
+
+def _mulhilo64(a: int, x: np.ndarray):
+    """High and low 64-bit words of the 128-bit product a * x (x uint64 array).
+
+    The product is formed from 32-bit halves, each partial product exact in
+    uint64: a x = aH xH 2^64 + (aH xL + aL xH) 2^32 + aL xL.
+    """
+    m32 = np.uint64(0xFFFFFFFF)
+    s32 = np.uint64(32)
+    aL, aH = np.uint64(a & 0xFFFFFFFF), np.uint64(a >> 32)
+    xL, xH = x & m32, x >> s32
+    ll, lh, hl, hh = aL * xL, aL * xH, aH * xL, aH * xH
+    mid = (ll >> s32) + (lh & m32) + (hl & m32)
+    hi = hh + (lh >> s32) + (hl >> s32) + (mid >> s32)
+    lo = (mid << s32) | (ll & m32)
+    return hi, lo
+
+
+def philox4x64_10(counter, key):
+    """Philox-4x64-10 blocks.  counter: four uint64 arrays (words 0..3, of one
+    shape), key: two Python ints.  Returns the four output words.
+
+    One round maps (x0, x1, x2, x3) under key (k0, k1) to
+    (hi(M1 x2) ^ x1 ^ k0, lo(M1 x2), hi(M0 x0) ^ x3 ^ k1, lo(M0 x0)), where
+    hi and lo are the two 64-bit halves of a 128-bit product; the key grows
+    by (W0, W1) after every round.
+    """
+    x0, x1, x2, x3 = (np.asarray(c, dtype=np.uint64) for c in counter)
+    k0, k1 = int(key[0]) & _MASK64, int(key[1]) & _MASK64
+    for _ in range(PHILOX_ROUNDS):
+        h0, l0 = _mulhilo64(PHILOX_M[0], x0)
+        h1, l1 = _mulhilo64(PHILOX_M[1], x2)
+        x0, x1, x2, x3 = h1 ^ x1 ^ np.uint64(k0), l1, h0 ^ x3 ^ np.uint64(k1), l0
+        k0 = (k0 + PHILOX_W[0]) & _MASK64
+        k1 = (k1 + PHILOX_W[1]) & _MASK64
+    return x0, x1, x2, x3
+
+
+def philox_normals(T: int, E: int, seed: int, rng_offset: int = 0) -> np.ndarray:
+    """The standard-normal draw z[t, i] of every token t < T and expert i < E.
+
+    Counter n = t * E + i + rng_offset (mod 2^64) in word 0, key (seed, 0).
+    With w0, w1 the block's first two words: u1 = (floor(w0 / 2^11) + 1) 2^-53
+    in (0, 1], u2 = floor(w1 / 2^11) 2^-53 in [0, 1), and
+    z = sqrt(-2 ln u1) cos(2 pi u2) (Box-Muller).
+    """
+    n = (np.arange(T * E, dtype=np.uint64) + np.uint64(int(rng_offset) & _MASK64)).reshape(T, E)
+    zero = np.zeros_like(n)
+    w0, w1, _, _ = philox4x64_10((n, zero, zero, zero), (seed, 0))
+    u1 = ((w0 >> np.uint64(11)).astype(np.float64) + 1.0) * 2.0 ** -53
+    u2 = (w1 >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
+    return np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)
 
 
 def scores(H, score: str) -> np.ndarray:

@@ -106,8 +106,35 @@ def test_invalid_configs(kw, code):
     assert status("moe_capacity", ctypes.byref(cfg), ctypes.byref(v)) == code
     sz = ctypes.c_size_t()
     assert status("moe_workspace_size", ctypes.byref(cfg), 3, ctypes.byref(sz)) == code
-    assert status("moe_layer_forward", ctypes.byref(cfg), *([None] * 13), None, None, None, 0,
+    assert status("moe_layer_forward", ctypes.byref(cfg), *([None] * 12), None, None, None, 0,
                   None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    # one expert matrix of 2^31 bytes or more (h * f * 2), routed or shared
+    (dict(h=16384, f=65536), B.MOE_ERR_UNSUPPORTED),
+    (dict(h=32768, f=32768), B.MOE_ERR_UNSUPPORTED),
+    (dict(h=4096, f=4096, n_shared=1, f_shared=262144), B.MOE_ERR_UNSUPPORTED),
+    # a row of 2^22 elements: 256 rows of a tile overflow a 32-bit copy offset
+    (dict(h=64, f=1 << 22), B.MOE_ERR_UNSUPPORTED),
+    (dict(h=1 << 22, f=64), B.MOE_ERR_UNSUPPORTED),
+    # just below both limits
+    (dict(h=16384, f=65536 - 64), B.MOE_OK),
+    (dict(h=64, f=(1 << 22) - 64), B.MOE_OK),
+])
+def test_32bit_buffer_limits(kw, code):
+    """The bf16 grouped GEMMs address an expert's weight matrix through a
+    buffer resource of at most 2^31 - 1 bytes and per-lane copy offsets as
+    32-bit integers: larger shapes are refused before anything runs."""
+    cfg = cfg_of(**kw)
+    v = ctypes.c_int64()
+    assert status("moe_capacity", ctypes.byref(cfg), ctypes.byref(v)) == code
+    sz = ctypes.c_size_t()
+    assert status("moe_workspace_size", ctypes.byref(cfg), B.MOE_WS_EXPERT_FFN,
+                  ctypes.byref(sz)) == code
+    # the float32 path has no buffer resources
+    f32 = B.make_config(I.WORKLOADS["tiny_f32"].replace(T=64, **kw))
+    assert status("moe_capacity", ctypes.byref(f32), ctypes.byref(v)) == B.MOE_OK
 
 
 def test_bad_enums_and_null_pointers():
@@ -142,7 +169,7 @@ def test_bad_enums_and_null_pointers():
     scfg = cfg_of(n_shared=1, f_shared=64)
     assert status("moe_shared_ffn", ctypes.byref(scfg), fake, None, fake, fake, other, fake,
                   1 << 30, None) == B.MOE_ERR_INVALID_ARG
-    assert status("moe_layer_forward", ctypes.byref(scfg), fake, fake, None, None, None, None,
+    assert status("moe_layer_forward", ctypes.byref(scfg), fake, fake, None, None, None,
                   fake, fake, fake, None, None, None, other, None, None, fake, 1 << 30,
                   None) == B.MOE_ERR_INVALID_ARG
     # the bias step needs a finite, non-negative gamma
@@ -164,7 +191,7 @@ def test_bad_enums_and_null_pointers():
                   fake, fake, fake, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
     assert status("moe_expert_ffn_fp8", ctypes.byref(fcfg), fake, fake, fake, fake, None, fake,
                   fake, fake, fake, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
-    assert status("moe_layer_forward_fp8", ctypes.byref(fcfg), fake, fake, None, None, None, None,
+    assert status("moe_layer_forward_fp8", ctypes.byref(fcfg), fake, fake, None, None, None,
                   fake, fake, fake, None, fake, None, None, None, other, None, None, fake,
                   1 << 30, None) == B.MOE_ERR_INVALID_ARG  # s_up missing
     assert status("moe_quantize_rows_fp8", fake, 4, 12, fake, fake, None) == B.MOE_ERR_UNSUPPORTED
@@ -176,17 +203,20 @@ def test_bad_enums_and_null_pointers():
     assert status("moe_router_z_loss", ctypes.byref(cfg), fake, None, None) == B.MOE_ERR_INVALID_ARG
     assert status("moe_router_z_loss", ctypes.byref(cfg), None, fake, None) == B.MOE_ERR_INVALID_ARG
     assert status("moe_router_z_loss", None, fake, fake, None) == B.MOE_ERR_INVALID_ARG
-    # noisy routing without the noise draws
+    # noisy routing without W_noise (the draws' output is optional)
     ncfg = cfg_of(noisy=True)
-    assert status("moe_route", ctypes.byref(ncfg), fake, fake, None, None, fake, None, fake,
+    assert status("moe_route", ctypes.byref(ncfg), fake, fake, None, None, None, fake, fake,
                   fake, None, None, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    assert status("moe_layer_forward", ctypes.byref(ncfg), fake, fake, None, None, None, fake,
+                  fake, fake, None, None, None, other, None, None, fake, 1 << 40,
+                  None) == B.MOE_ERR_INVALID_ARG
 
 
 def test_undersized_workspace_is_rejected():
     cfg = cfg_of()
     fake = ctypes.c_void_p(0x1000)
     need = B.workspace_size(cfg, B.MOE_WS_LAYER)
-    assert status("moe_layer_forward", ctypes.byref(cfg), fake, fake, None, None, None, None,
+    assert status("moe_layer_forward", ctypes.byref(cfg), fake, fake, None, None, None,
                   fake, fake, fake, None, None, None, ctypes.c_void_p(0x2000), None, None, fake,
                   need - 1, None) == B.MOE_ERR_WORKSPACE
     need = B.workspace_size(cfg, B.MOE_WS_ROUTE)
@@ -232,7 +262,7 @@ def test_backward_argument_checks():
     ex = B.moe_backward_extras()
     assert bwd(cfg_of(noisy=True)) == B.MOE_ERR_INVALID_ARG
     assert bwd(cfg_of(noisy=True), extra=ctypes.byref(ex)) == B.MOE_ERR_INVALID_ARG
-    ex.W_noise, ex.noise = 0x3000, 0x3000
+    ex.W_noise = 0x3000
     assert bwd(cfg_of(noisy=True), extra=ctypes.byref(ex)) == B.MOE_ERR_INVALID_ARG  # dW_noise
     scfg = cfg_of(n_shared=1, f_shared=64)
     assert bwd(scfg) == B.MOE_ERR_INVALID_ARG
@@ -253,7 +283,7 @@ def test_backward_argument_checks():
     a = B.moe_aux_outputs()
     a.GU = 0x3000
     f32cfg = B.make_config(I.WORKLOADS["tiny_f32"])
-    assert status("moe_layer_forward", ctypes.byref(f32cfg), fake, fake, None, None, None, None,
+    assert status("moe_layer_forward", ctypes.byref(f32cfg), fake, fake, None, None, None,
                   fake, fake, fake, None, None, None, other, ctypes.byref(a), None, fake,
                   1 << 40, None) == B.MOE_ERR_UNSUPPORTED
     # one expert's rows must be addressable with 32-bit byte offsets
@@ -315,3 +345,40 @@ def test_fp8_gradient_argument_checks():
     assert bwd(cfg_of(h=384)) == B.MOE_ERR_INVALID_ARG
     ex.s_downT = 0x3000
     assert bwd(cfg_of(h=320)) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_debug_map_checker():
+    """The MOE_DEBUG host check accepts the oracle's fill and refuses each
+    kind of corrupted map."""
+    import numpy as np
+    from mixture_experts_layer_37_amd import debug as D
+    rng = np.random.default_rng(3)
+    T, E, k, C = 50, 6, 2, 12
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+    fr = O.fill(idx, E, C)
+    rows_max = T * k
+    row_token = np.full(rows_max, -7, dtype=np.int64)
+    row_token[:len(fr["row_token"])] = fr["row_token"]
+    good = dict(topk_idx=idx, slot=fr["slot"], row_token=row_token, count=fr["count"],
+                kept=fr["kept"], offset=fr["offset"], C=C)
+    D.check_dispatch_maps(**good)
+    assert fr["kept"].sum() < fr["count"].sum()  # drops happen
+
+    def bad(**kw):
+        m = {n: (v.copy() if hasattr(v, "copy") else v) for n, v in good.items()}
+        for n, f in kw.items():
+            f(m[n])
+        with pytest.raises(D.DispatchMapError):
+            D.check_dispatch_maps(**m)
+
+    kept_slot = np.argwhere(fr["slot"] >= 0)[0]
+    other = np.argwhere(fr["slot"] >= 0)[5]
+
+    def dup(s):
+        s[tuple(kept_slot)] = s[tuple(other)]
+    bad(slot=dup)                                                   # two owners of a row
+    bad(slot=lambda s: s.__setitem__(tuple(kept_slot), rows_max))   # out of range
+    bad(row_token=lambda r: r.__setitem__(0, (r[0] + 1) % T))       # wrong token
+    bad(offset=lambda o: o.__setitem__(2, o[2] + 1))                # not the scan
+    bad(kept=lambda kk: kk.__setitem__(0, kk[0] - 1))               # not min(count, C)
+    bad(count=lambda c: c.__setitem__(1, c[1] + 1))                 # not the histogram

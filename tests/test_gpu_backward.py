@@ -14,6 +14,14 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 TOL = 2e-2  # bf16 activations and weight gradients, float32 accumulation
+# Element and row bounds of the expert weight gradients (elements against
+# |x^| + the expert's rms, rows of normal size against their norm): each is a
+# sum over the expert's rows of products whose factors went through up to five
+# bf16 roundings (dY, g, u, dA, dG / dU, a); the same chain evaluated on the
+# CPU reaches 2-3.5% per element and 3% per row on the small shapes
+# (tests/test_tolerance_derivation.py), so both bounds are 5%.  Each expert's
+# whole gradient stays within TOL.
+WGRAD_ELEM_TOL = 5e-2
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -50,10 +58,30 @@ BWD = {
 }
 
 
-def rel(got, ref):
+def close(got, ref, name, tol=TOL):
+    """Group by group and element by element (moe_testlib.check_close): dU
+    and dX per token; each expert's weight gradient matrix ([E, f, h] or
+    [E, h, f]) as one group, so each element is held to tol (|x^| + rms of its
+    expert's gradient); dW_r and dW_noise per expert (their columns); db_r as
+    one group.  A group the oracle gives as exactly zero (an expert without
+    rows) must be exactly zero.
+
+    Rows of an expert's weight gradient are held to WGRAD_ELEM_TOL, and only
+    rows whose norm is at least a quarter of the expert's typical row norm: with
+    g and u stored in bf16 (the forward's kept activations, or the same values
+    recomputed), SiLU'(g), which crosses zero near g = -1.28, carries an
+    absolute error of about 2^-9 |g| |SiLU''|, so the rows of hidden units
+    whose SiLU'(g) nearly vanishes on every row of the expert (experts with
+    one or two rows) are small and have a large relative error, while their
+    error against the expert's scale stays near 2^-9 (the element bound
+    covers them)."""
     got, ref = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
-    n = np.linalg.norm(ref)
-    return np.linalg.norm(got - ref) / (n if n > 0 else 1.0)
+    if name.startswith("dW_r") or name.startswith("dW_noise"):
+        got, ref = got.T, ref.T
+    wgrad = ref.ndim == 3 and name.startswith("dW")
+    return L.check_close(got, ref, tol, name, group_axes=2 if wgrad else 1,
+                         elem_tol=WGRAD_ELEM_TOL if wgrad else tol,
+                         row_tol=WGRAD_ELEM_TOL if wgrad else tol)
 
 
 def run_backward(w, x, g, dOut, alpha, c_z, saved=None):
@@ -61,7 +89,7 @@ def run_backward(w, x, g, dOut, alpha, c_z, saved=None):
     T, h, f, E = w.T, w.h, w.f, w.E
     extra = {}
     if w.noisy:
-        extra = {"W_noise": x["W_noise"], "noise": x["noise"],
+        extra = {"W_noise": x["W_noise"],
                  "dW_noise": torch.empty((h, E), dtype=torch.float32, device=DEV)}
     if w.n_shared:
         ns, fs = w.n_shared, w.f_shared
@@ -106,25 +134,15 @@ def test_backward(name):
                            L.f64(x["W_down"]), fwd, L.f64(dOut),
                            score=L.ORACLE_MODE[w.score], gate=L.ORACLE_MODE[w.gate],
                            alpha=alpha, c_z=c_z)
-    errs = {}
-    for n in ("dU", "dW_r", "db_r"):
-        errs[n] = rel(L.f64(got[n]), ref[n])
-    # weight gradients expert by expert; an expert without rows gets zeros
+    # every gradient row by row; an expert without rows gets exact zeros
     kept = L.to_np(g["kept"])
     if name == "idle_experts":
         assert (kept == 0).sum() >= 10, kept
     for n in ("dW_gate", "dW_up", "dW_down"):
-        G = L.f64(got[n])
-        worst = 0.0
-        for e in range(w.E):
-            if kept[e] == 0:
-                assert not G[e].any(), (n, e)
-            else:
-                worst = max(worst, rel(G[e], ref[n][e]))
-        errs[n] = worst
+        assert all(not got[n][e].any() for e in range(w.E) if kept[e] == 0), n
+    errs = {n: close(L.f64(got[n]), ref[n], n)
+            for n in ("dU", "dW_r", "db_r", "dW_gate", "dW_up", "dW_down")}
     L.log(f"  errs {errs}")
-    for n, v in errs.items():
-        assert v <= TOL, (n, v)
 
 
 @pytest.mark.parametrize("name", ["mixtral_drops", "switch_small", "v3_keyed"])
@@ -165,9 +183,9 @@ def test_backward_alpha_and_z_terms_only():
     s = O.scores(H, O.SOFTMAX)
     f = L.to_np(g["count"]).astype(np.float64) / (w.T * w.k)
     dH = 0.5 * w.E / w.T * O.aux_logit_grad(s, f, O.SOFTMAX) + 0.25 * O.z_loss_logit_grad(H)
-    assert rel(L.f64(got["dW_r"]), L.f64(x["U"]).T @ dH) < 1e-4
-    assert rel(L.f64(got["db_r"]), dH.sum(axis=0)) < 1e-4
-    assert rel(L.f64(got["dU"]), dH @ L.f64(x["W_r"]).T) < TOL
+    close(L.f64(got["dW_r"]), L.f64(x["U"]).T @ dH, "dW_r", tol=1e-4)
+    close(L.f64(got["db_r"]), dH.sum(axis=0), "db_r", tol=1e-4)
+    close(L.f64(got["dU"]), dH @ L.f64(x["W_r"]).T, "dU")
 
 
 def test_backward_256_experts():
@@ -183,7 +201,7 @@ def test_backward_256_experts():
                            L.f64(x["W_down"]), fwd, L.f64(dOut), score=L.ORACLE_MODE[w.score],
                            gate=L.ORACLE_MODE[w.gate], alpha=0.01, c_z=1e-3)
     for n in ("dU", "dW_r", "db_r", "dW_gate", "dW_up", "dW_down"):
-        assert rel(L.f64(got[n]), ref[n]) <= TOL, n
+        close(L.f64(got[n]), ref[n], n)
 
 
 # --------------------------------------------------------------------------- full sizes
@@ -291,16 +309,15 @@ def test_full_size_weight_gradients(full_cases, name, fp8):
     kept = L.to_np(g["kept"])
     for n, dim in (("dW_gate", 1), ("dW_up", 1), ("dW_down", 2)):
         G = sub(got[n], dim)
-        worst = max(rel(G[e], ref[n][e]) for e in range(w.E) if kept[e] > 0)
         assert all(not G[e].any() for e in range(w.E) if kept[e] == 0), n
-        L.log(f"  {n} worst expert rel {worst:.3e}")
-        assert worst <= TOL, (n, worst)
+        # each expert's sampled hidden units form one group
+        err = close(G, ref[n], n)
+        L.log(f"  {n} worst {err}")
     if w.n_shared:
         for n, dim in (("dWs_gate", 1), ("dWs_up", 1), ("dWs_down", 2)):
             G = L.f64(got[n].index_select(dim, Js))
-            worst = max(rel(G[i], ref[n][i]) for i in range(w.n_shared))
-            L.log(f"  {n} rel {worst:.3e}")
-            assert worst <= TOL, (n, worst)
+            err = close(G, ref[n], n)
+            L.log(f"  {n} worst {err}")
 
 
 def test_full_size_input_and_router_gradients(full_cases):
@@ -336,13 +353,10 @@ def test_full_size_input_and_router_gradients(full_cases):
                             alpha=alpha * fR, c_z=c_z * fR, **mode)
     dU = np.zeros((w.T, w.h))
     dU[S], dU[R] = refS["dU"], refR["dU"]
-    errs = {"dU": rel(L.f64(got["dU"]), dU),
-            "dU[S]": rel(L.f64(got["dU"][St]), refS["dU"]),
-            "dW_r": rel(L.f64(got["dW_r"]), refS["dW_r"] + refR["dW_r"]),
-            "db_r": rel(L.f64(got["db_r"]), refS["db_r"] + refR["db_r"])}
+    errs = {"dU": close(L.f64(got["dU"]), dU, "dU"),
+            "dW_r": close(L.f64(got["dW_r"]), refS["dW_r"] + refR["dW_r"], "dW_r"),
+            "db_r": close(L.f64(got["db_r"]), refS["db_r"] + refR["db_r"], "db_r")}
     L.log(f"  errs {errs}")
-    for n, v in errs.items():
-        assert v <= TOL, (n, v)
 
 
 EXTRA = {
@@ -370,7 +384,7 @@ def test_backward_noisy_and_shared(name):
     got = run_backward(w, x, g, dOut, alpha, c_z)
     kw = {}
     if w.noisy:
-        kw.update(W_noise=L.f64(x["W_noise"]), noise=L.f64(x["noise"]))
+        kw.update(W_noise=L.f64(x["W_noise"]), noise=L.oracle_noise(w))
     if w.n_shared:
         kw.update(Ws_gate=L.f64(x["Ws_gate"]), Ws_up=L.f64(x["Ws_up"]),
                   Ws_down=L.f64(x["Ws_down"]))
@@ -381,10 +395,8 @@ def test_backward_noisy_and_shared(name):
     names = ["dU", "dW_r", "db_r", "dW_gate", "dW_up", "dW_down"]
     names += ["dW_noise"] if w.noisy else []
     names += ["dWs_gate", "dWs_up", "dWs_down"] if w.n_shared else []
-    errs = {n: rel(L.f64(got[n]), ref[n]) for n in names}
+    errs = {n: close(L.f64(got[n]), ref[n], n) for n in names}
     L.log(f"  errs {errs}")
-    for n, v in errs.items():
-        assert v <= TOL, (n, v)
 
 
 def test_backward_empty_batch_with_shared_experts():
@@ -443,14 +455,14 @@ def test_staged_backward_equals_layer(name, saved):
     noise = {}
     if w.noisy:
         got["dW_noise"] = torch.empty_like(ref["dW_noise"])
-        noise = dict(W_noise=x["W_noise"], noise=x["noise"], dW_noise=got["dW_noise"])
+        noise = dict(W_noise=x["W_noise"], dW_noise=got["dW_noise"])
     B.moe_router_backward(cfg, x["U"], x["W_r"], g["logits"], g["topk_idx"], g["topk_gate"],
                           g["slot"], g["count"], dgate, d_res, dX, got["dU"], got["dW_r"],
                           db_r=got["db_r"], alpha=alpha, c_z=c_z, **noise)
     torch.cuda.synchronize()
     for n in got:
         if w.n_shared and n == "dU":
-            assert rel(L.f64(got[n]), L.f64(ref[n])) <= TOL, n
+            close(L.f64(got[n]), L.f64(ref[n]), n)
         else:
             assert torch.equal(got[n], ref[n]), n
 
@@ -524,9 +536,9 @@ def test_fp8_output_gradients(name):
     np.testing.assert_array_equal(L.f64(sy[:rows]), s_ref)
     eX, eWg, eWu, eWd = O.expert_backward_fp8(L.f64(g["X"][:rows]), offset, L.f64(x["W_gate"]),
                                               L.f64(x["W_up"]), L.f64(x["W_down"]), q_ref, s_ref)
-    assert rel(L.f64(dX[:rows]), eX) <= TOL
+    close(L.f64(dX[:rows]), eX, "dX")
     for n, ref in (("dW_gate", eWg), ("dW_up", eWu), ("dW_down", eWd)):
-        assert rel(L.f64(st[n]), ref) <= TOL, n
+        close(L.f64(st[n]), ref, n)
     # the layer call
     out = {"dU": torch.empty_like(x["U"]),
            "dW_r": torch.empty((w.h, w.E), dtype=torch.float32, device=DEV),
@@ -545,4 +557,4 @@ def test_fp8_output_gradients(name):
                            score=L.ORACLE_MODE[w.score], gate=L.ORACLE_MODE[w.gate],
                            alpha=0.01, c_z=1e-3, fp8_down_grad=True)
     for n in out:
-        assert rel(L.f64(out[n]), ref[n]) <= TOL, n
+        close(L.f64(out[n]), ref[n], n)

@@ -121,16 +121,14 @@ def test_fp8_layer_small(name):
                           Ws_down=None if w.n_shared == 0 else L.f64(x["Ws_down"]), fp8_up=True)
     if not L.keyed(w):  # keyed routing is checked against the GPU's own selection above
         np.testing.assert_array_equal(ref["idx"], L.to_np(g["topk_idx"]))
-        eo = L.row_rel_err(L.to_np(g["out"]), ref["out"])
-        ed = L.delta_err(w, L.f64(g["out"]), U, ref["out"])
-        assert eo <= L.out_tol(w) and ed <= L.out_tol(w), (eo, ed)
-    ey = L.row_rel_err(L.to_np(g["Y"][:rows]), O.expert_outputs_fp8(
+        L.check_close(L.to_np(g["out"]), ref["out"], L.out_tol(w), "out")
+        L.check_delta(w, L.f64(g["out"]), U, ref["out"])
+    ey = L.check_close(L.to_np(g["Y"][:rows]), O.expert_outputs_fp8(
         qo, so, r["offset"], qg.reshape(w.E, w.f, w.h), sgo.reshape(w.E, w.f),
         *[a.reshape(*s) for a, s in zip(O.quantize_rows_fp8(L.f64(x["W_up"]).reshape(-1, w.h)),
                                         [(w.E, w.f, w.h), (w.E, w.f)])],
-        L.f64(x["W_down"])))
-    assert ey <= L.out_tol(w), ey
-    L.log(f"  drops={r['n_dropped']} Y err={ey:.2e}")
+        L.f64(x["W_down"])), L.out_tol(w), "Y")
+    L.log(f"  drops={r['n_dropped']} Y err={ey}")
 
 
 @pytest.mark.parametrize("name", ["mixtral_fp8_small", "deepseek_fp8_small"])
@@ -167,18 +165,21 @@ def test_fp8_full_size_mixtral():
     np.testing.assert_array_equal(d["x_scale"][:rows].cpu().double().numpy(), so)
     W8g, sg, W8u, su = L.fp8_weights(x)
     Yg = L.f64(g["Y"][:rows])
+    # every row of the expert with the most rows, sampled rows of others
+    kept = L.to_np(g["kept"])
+    e_big = int(np.argmax(kept))
+    picks = [(e_big, list(range(int(r["offset"][e_big]), int(r["offset"][e_big + 1]))))]
+    picks += [(e, rws) for e, rws in L.sampled_expert_rows(r, w.E) if e != e_big]
     worst = 0.0
-    for e, rws in L.sampled_expert_rows(r, w.E):
+    for e, rws in picks:
         Wg = decode(W8g[e]) * sg[e].cpu().double().numpy()[:, None]
         Wu = decode(W8u[e]) * su[e].cpu().double().numpy()[:, None]
         Wd = L.f64(x["W_down"][e])
-        for row in rws:
-            xr = (qo[row] * so[row])[None, :]
-            ref = O.swiglu_expert(xr, Wg, Wu, Wd)
-            worst = max(worst, L.row_rel_err(Yg[row][None, :], ref))
-    assert worst <= L.out_tol(w), worst
+        xr = qo[rws] * so[rws][:, None]
+        ref = O.swiglu_expert(xr, Wg, Wu, Wd)
+        worst = max(worst, L.check_close(Yg[rws], ref, L.out_tol(w), f"Y of expert {e}")["elem"])
     # combine on every token from the GPU's expert outputs
     out_ref = O.combine(U, Yg, r["slot"], r["gate"])
-    eo = L.row_rel_err(L.to_np(g["out"]), out_ref)
-    assert eo <= L.out_tol(w), eo
-    L.log(f"  fp8 full ok: Y(sampled)={worst:.2e} out={eo:.2e}")
+    eo = L.check_close(L.to_np(g["out"]), out_ref, L.out_tol(w), "out")
+    L.check_delta(w, L.f64(g["out"]), U, out_ref)
+    L.log(f"  fp8 full ok: Y(expert {e_big} whole, sampled others)={worst:.2e} out={eo}")

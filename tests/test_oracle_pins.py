@@ -232,6 +232,71 @@ def test_router_vs_library_with_bias_and_noise():
     assert O.softplus(np.array([-800.0]))[0] == 0.0
 
 
+# ----------------------------------------------------------------- noise generator
+def _words(n: int, count: int):
+    return [np.array([(n >> (64 * j)) & ((1 << 64) - 1)], dtype=np.uint64) for j in range(count)]
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_philox_known_answers_vs_numpy(case):
+    """The integer stream against numpy's own Philox-4x64-10 (an independent
+    implementation in C).  numpy's bit generator increments its 256-bit counter
+    before each block, so Philox(counter=c, key=k) starts with the block of
+    counter c + 1."""
+    r = np.random.default_rng(100 + case)
+    if case == 0:
+        c, k = 0, 0
+    elif case == 1:
+        c, k = (1 << 64) - 2, 7          # the +1 reaches 2^64 - 1, no carry
+    elif case == 2:
+        c, k = (1 << 64) - 1, 12345      # the +1 carries into word 1
+    else:
+        c = int.from_bytes(r.bytes(32), "little") >> (case % 3)
+        k = int.from_bytes(r.bytes(16), "little")
+    bg = np.random.Philox(counter=c, key=k)
+    want = [int(v) for v in bg.random_raw(8)]
+    got = []
+    for blk in (1, 2):
+        n = (c + blk) % (1 << 256)
+        words = O.philox4x64_10(_words(n, 4), (k & ((1 << 64) - 1), k >> 64))
+        got += [int(w[0]) for w in words]
+    assert got == want
+
+
+def test_philox_normals_take_one_counter_per_pair():
+    """z[t, i] depends only on seed and t * E + i + rng_offset, so shifting the
+    offset by E moves every draw up by one token, and any single pair can be
+    drawn alone."""
+    T, E, seed = 9, 7, 0xDEADBEEF
+    z = O.philox_normals(T, E, seed, rng_offset=5)
+    z2 = O.philox_normals(T, E, seed, rng_offset=5 + E)
+    np.testing.assert_array_equal(z[1:], z2[:-1])
+    for t, i in [(0, 0), (3, 4), (8, 6)]:
+        assert O.philox_normals(1, 1, seed, t * E + i + 5)[0, 0] == z[t, i]
+    # the counter wraps modulo 2^64
+    top = O.philox_normals(1, 2, seed, (1 << 64) - 1)
+    assert top[0, 1] == O.philox_normals(1, 1, seed, 0)[0, 0]
+    # another seed gives other draws
+    assert not np.array_equal(z, O.philox_normals(T, E, seed + 1, 5))
+
+
+def test_philox_normals_are_standard_normal():
+    """Moments of n = 2^18 draws (mean within 4 sigma / sqrt(n), variance
+    within 1%), no correlation between neighbouring counters, and a
+    Kolmogorov-Smirnov test against the normal distribution."""
+    from scipy import stats
+    z = O.philox_normals(4096, 64, seed=0)
+    n = z.size
+    assert abs(z.mean()) < 4.0 / math.sqrt(n)
+    assert abs(z.var() - 1.0) < 0.01
+    assert abs(stats.kurtosis(z.ravel())) < 0.05
+    flat = z.ravel()
+    assert abs(np.corrcoef(flat[:-1], flat[1:])[0, 1]) < 4.0 / math.sqrt(n)
+    assert stats.kstest(flat, "norm").pvalue > 1e-3
+    # Box-Muller bounds: |z| <= sqrt(-2 ln 2^-53)
+    assert np.abs(z).max() <= math.sqrt(2.0 * 53 * math.log(2.0))
+
+
 # ----------------------------------------------------------------- fill
 def brute_positions(idx, order):
     """Position of each assignment = number of earlier assignments (in fill order) to its expert."""
@@ -819,3 +884,34 @@ def test_round_bf16():
                         .astype(np.float32), mid])
     want = torch.from_numpy(x).to(torch.bfloat16).float().numpy().astype(np.float64)
     np.testing.assert_array_equal(O.round_bf16(x), want)
+
+
+def test_fp8_gradient_codes_of_stored_rows_within_one_step():
+    """layer_backward(fp8_down_grad=True) quantises dY as the layer stores it:
+    the float32 products g * dOut rounded to bf16.  This is the one place the
+    oracle follows a storage rounding of the layer (elsewhere it stays in
+    float64), so that both sides take each E4M3 decision on the same value.
+    The choice moves little: the bf16 rounding shifts a value by at most 2^-9
+    of itself, far below an E4M3 step (2^-4 of it at least), so the stored
+    rows' dequantised codes and the exact products' differ by at most one
+    step of the coarser of the two grids, also where the rounding moves a
+    row's largest magnitude across a power-of-two scale boundary."""
+    r = rng(31)
+    dY = r.normal(0, 1, (200, 96)) * np.exp2(r.integers(-20, 20, (200, 1)))
+    # rows whose largest magnitude sits just above 448 * 2^j: the exact row
+    # takes the scale 2^(j+1), the bf16 row (rounded down to 448 * 2^j) 2^j
+    for i, j in enumerate(range(-6, 6)):
+        dY[i] = r.uniform(-1, 1, 96) * 300.0 * 2.0 ** j
+        dY[i, 5] = 448.0 * (1 + 2.0 ** -10) * 2.0 ** j
+    stored = O.round_bf16(dY.astype(np.float32))
+    q_x, s_x = O.quantize_rows_fp8(dY)
+    q_b, s_b = O.quantize_rows_fp8(stored)
+    assert (s_b[:12] * 2 == s_x[:12]).all()    # the boundary rows change scale
+    a, b = q_x * s_x[:, None], q_b * s_b[:, None]
+
+    def step(q, s):  # E4M3 spacing at |q| (scaled units), times the row scale
+        _, p1 = np.frexp(np.where(q != 0, np.abs(q), 1.0))
+        return np.ldexp(1.0, np.maximum(p1 - 1, -6) - 3) * s[:, None]
+
+    assert (np.abs(a - b) <= np.maximum(step(q_x, s_x), step(q_b, s_b))).all()
+    assert (a[12:] == b[12:]).mean() > 0.9    # away from the boundary most codes agree
