@@ -216,6 +216,20 @@ int32_t moe_dispatch(const moe_config* cfg, const void* U, const int32_t* topk_i
                      int32_t* kept, int32_t* offset, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* moe_dispatch for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same outputs, bit for bit, with the histograms and scan bases in a fixed
+ * 4 MiB device array of the library (one per GPU, held until the process
+ * ends) instead of a caller workspace.  It calls no allocator.  Shapes whose
+ * dispatch workspace (moe_workspace_size, MOE_WS_DISPATCH) exceeds 4 MiB,
+ * i.e. roughly T * k * E > 2^27, return MOE_ERR_WORKSPACE before anything
+ * is launched.  Every call on one GPU uses that GPU's array: calls that
+ * overlap in time on one GPU (other streams, other threads) race and must
+ * be ordered by the caller. */
+int32_t moe_dispatch_noalloc(const moe_config* cfg, const void* U, const int32_t* topk_idx,
+                             void* X, int32_t* row_token, int32_t* slot, int32_t* count,
+                             int32_t* kept, int32_t* offset, void* stream);
+
 /* Grouped SwiGLU experts (FFN eq.; grouped-GEMM option of the expert-compute
  * section): for every expert e and row r in offset[e]..offset[e+1]-1,
  * Y[r] = W_down[e] (SiLU(W_gate[e] X[r]) * W_up[e] X[r]).  Accumulation is

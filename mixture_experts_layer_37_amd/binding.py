@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
             "moe_workspace_size": (I32, [cfgp, I32, ctypes.POINTER(SZ)]),
             "moe_route": (I32, [cfgp] + [P] * 10 + [P, SZ, P]),
             "moe_dispatch": (I32, [cfgp] + [P] * 8 + [P, SZ, P]),
+            "moe_dispatch_noalloc": (I32, [cfgp] + [P] * 8 + [P]),
             "moe_expert_ffn": (I32, [cfgp] + [P] * 6 + [P, SZ, P]),
             "moe_combine": (I32, [cfgp] + [P] * 6 + [P]),
             "moe_shared_ffn": (I32, [cfgp] + [P] * 5 + [P, SZ, P]),
@@ -252,6 +253,23 @@ def _debug_check(cfg, topk_idx, slot, row_token, count, kept, offset, stream):
     (torch.cuda.current_stream() if stream is None else stream).synchronize()
     _debug.check_dispatch_maps(*(t.cpu().numpy() for t in (topk_idx, slot, row_token, count,
                                                             kept, offset)), capacity(cfg))
+
+
+def moe_dispatch_noalloc(cfg, U, topk_idx, X, row_token, slot, count, kept, offset,
+                         stream=None):
+    """moe_dispatch without a workspace: its scratch is the library's fixed
+    device array (calls overlapping on one GPU race)."""
+    T, h, E, k = cfg.T, cfg.h, cfg.E, cfg.k
+    rows = max_rows(cfg)
+    dt = _elem_dtype(cfg)
+    args = [
+        _ptr(U, "U", (T, h), dt), _ptr(topk_idx, "topk_idx", (T, k), torch.int32),
+        _ptr(X, "X", (rows, h), dt), _ptr(row_token, "row_token", (rows,), torch.int32),
+        _ptr(slot, "slot", (T, k), torch.int32), _ptr(count, "count", (E,), torch.int32),
+        _ptr(kept, "kept", (E,), torch.int32), _ptr(offset, "offset", (E + 1,), torch.int32),
+    ]
+    _check(lib().moe_dispatch_noalloc(ctypes.byref(cfg), *args, _stream(stream)),
+           "moe_dispatch_noalloc")
 
 
 def moe_expert_ffn(cfg, X, offset, W_gate, W_up, W_down, Y, ws=None, stream=None):

@@ -607,6 +607,23 @@ int32_t moe_dispatch(const moe_config* cfg, const void* U, const int32_t* topk_i
                       static_cast<hipStream_t>(stream));
 }
 
+int32_t moe_dispatch_noalloc(const moe_config* cfg, const void* U, const int32_t* topk_idx,
+                             void* X, int32_t* row_token, int32_t* slot, int32_t* count,
+                             int32_t* kept, int32_t* offset, void* stream) {
+  const int32_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const Dims d = dims_of(cfg);
+  if (d.T > 0 && (!U || !topk_idx || !X || !row_token || !slot)) return MOE_ERR_INVALID_ARG;
+  if (!count || !kept || !offset) return MOE_ERR_INVALID_ARG;
+  Plan pl;
+  const DispatchWs w = plan_dispatch(d, pl);
+  if (pl.bytes > kDispatchScratchBytes) return MOE_ERR_WORKSPACE;
+  int32_t* scratch = nullptr;
+  MOE_TRY(dispatch_scratch(&scratch));
+  return run_dispatch(d, cfg, w, U, topk_idx, X, row_token, slot, count, kept, offset, scratch,
+                      static_cast<hipStream_t>(stream));
+}
+
 int32_t moe_expert_ffn(const moe_config* cfg, const void* X, const int32_t* offset,
                        const void* W_gate, const void* W_up, const void* W_down, void* Y,
                        void* ws, size_t ws_bytes, void* stream) {

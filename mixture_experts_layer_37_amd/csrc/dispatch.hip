@@ -18,12 +18,23 @@
 //  3. per chunk, each assignment adds the number of earlier assignments in its
 //     own chunk (wave ballots for lanes below it, LDS counts for waves before
 //     it); position < C keeps it at row offset[e] + position.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
 namespace {
+
+// Scratch of moe_dispatch_noalloc: the per-chunk histograms and bases of
+// hist_kernel / scan_kernel, in a fixed device array instead of a caller
+// workspace.  Every entry they read is written by the same call first, so
+// nothing needs clearing between calls.
+__device__ __align__(256) int32_t scratch[kDispatchScratchBytes / sizeof(int32_t)];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+int32_t* scratch_ptr[kMaxDevices] = {};
 
 __device__ __forceinline__ int load_expert(const int32_t* idx, int t, int r, int T, int k, int E) {
   if (t >= T) return -1;
@@ -298,6 +309,25 @@ hipError_t launch_quantize_rows_fp8(const void* src, int64_t rows, int cols, voi
                      static_cast<const bf16*>(src), rows, cols, static_cast<uint8_t*>(dst),
                      scale);
   return hipGetLastError();
+}
+
+// The device address of this device's copy of `scratch`, looked up once per
+// device (with that device current) and kept: the array's name in host code
+// is not a device address.
+hipError_t dispatch_scratch(int32_t** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    scratch_ptr[dev] = static_cast<int32_t*>(ptr);
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s) {

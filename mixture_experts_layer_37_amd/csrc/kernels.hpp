@@ -66,6 +66,10 @@ struct DispatchParams {
   int32_t* row_token;
 };
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s);
+// Bytes of the fixed device array behind moe_dispatch_noalloc, and its
+// address on the current device (looked up once per device).
+constexpr size_t kDispatchScratchBytes = size_t(4) << 20;
+hipError_t dispatch_scratch(int32_t** out);
 // FP8 dispatch (E4M3 codes of each kept row, with its power-of-two scale);
 // bf16 U, h a multiple of 8.
 hipError_t launch_permute_fp8(const void* U, const int32_t* slot, void* X8, float* xs, int T,
