@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--read-calibration", type=int, default=0, metavar="BYTES",
+                    help="only time the library's read-stream kernel over BYTES bytes "
+                         "(the read rate a plain stream reaches on this device) and exit")
     return ap.parse_args()
 
 
@@ -131,6 +134,37 @@ def copy_calibration(nbytes: int):
     ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3,
                       "ms": ms, "read_plus_write_GBps": 2 * nbytes / (min(ms) * 1e-3) / 1e9}),
+          flush=True)
+
+
+def read_calibration(nbytes: int):
+    """The read rate of a plain stream of 16-byte loads (moe_stream_read) over
+    nbytes of device memory, for several grid sizes; the best is the yardstick
+    for the weight-read-bound workloads."""
+    import torch
+
+    from mixture_experts_layer_37_amd import binding as B
+    nbytes -= nbytes % 16
+    x = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    x.fill_(3)
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(64 * ncu, dtype=torch.int32, device="cuda")
+    res = {}
+    for per_cu in (2, 4, 8, 16, 32, 64):
+        blocks = per_cu * ncu
+        B.moe_stream_read(x, sink, blocks)  # warm-up
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev[0].record()
+        for i in range(5):
+            B.moe_stream_read(x, sink, blocks)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        ms = min(ev[i].elapsed_time(ev[i + 1]) for i in range(5))
+        res[str(blocks)] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    best = max(res.values())
+    print(json.dumps({"read_calibration_bytes": nbytes, "read_GBps_by_grid": res,
+                      "read_GBps_best": best, "hbm_frac_of_peak": round(best / PEAK_HBM_GBS, 4)}),
           flush=True)
 
 
@@ -235,6 +269,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.read_calibration:
+        read_calibration(args.read_calibration)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

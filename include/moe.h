@@ -172,6 +172,15 @@ enum { MOE_NUM_STAGES = 6 }; /* route, dispatch, gate_up, down, combine, stats *
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_string(int32_t status);
 
+/* Measurement yardstick, not part of the layer: reads `bytes` bytes (a
+ * multiple of 16) of device memory at src once with 16-byte loads and writes
+ * one XOR word per workgroup to sink[0 .. blocks-1] (device), so that the
+ * read rate of the HBM-bound workloads can be compared with a plain read
+ * stream on the same device.  Errors: MOE_ERR_INVALID_ARG for a size not a
+ * multiple of 16, blocks outside 1..2^20, or NULL pointers with bytes > 0. */
+int32_t moe_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
+                        void* stream);
+
 /* Capacity C of cfg, on the host, as an exact rational ceiling (the double
  * capacity_factor is taken at its exact binary value).  Pure; no GPU use. */
 int32_t moe_capacity(const moe_config* cfg, int64_t* C);

@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
             "moe_route": (I32, [cfgp] + [P] * 10 + [P, SZ, P]),
             "moe_dispatch": (I32, [cfgp] + [P] * 8 + [P, SZ, P]),
             "moe_dispatch_noalloc": (I32, [cfgp] + [P] * 8 + [P]),
+            "moe_stream_read": (I32, [P, SZ, P, I32, P]),
             "moe_expert_ffn": (I32, [cfgp] + [P] * 6 + [P, SZ, P]),
             "moe_combine": (I32, [cfgp] + [P] * 6 + [P]),
             "moe_shared_ffn": (I32, [cfgp] + [P] * 5 + [P, SZ, P]),
@@ -253,6 +254,14 @@ def _debug_check(cfg, topk_idx, slot, row_token, count, kept, offset, stream):
     (torch.cuda.current_stream() if stream is None else stream).synchronize()
     _debug.check_dispatch_maps(*(t.cpu().numpy() for t in (topk_idx, slot, row_token, count,
                                                             kept, offset)), capacity(cfg))
+
+
+def moe_stream_read(src, sink, blocks: int, stream=None):
+    """One read pass over the bytes of src (a uint8 GPU tensor, size a
+    multiple of 16); sink: int32 GPU tensor of at least `blocks` words."""
+    _check(lib().moe_stream_read(_ptr(src, "src", dtype=torch.uint8), src.numel(),
+                                 _ptr(sink, "sink", dtype=torch.int32, min_numel=blocks),
+                                 int(blocks), _stream(stream)), "moe_stream_read")
 
 
 def moe_dispatch_noalloc(cfg, U, topk_idx, X, row_token, slot, count, kept, offset,

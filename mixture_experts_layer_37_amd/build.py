@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libmoe.so")
-SOURCES = ["api.cpp", "router.hip", "dispatch.hip", "ffn.hip", "combine.hip", "backward.hip"]
+SOURCES = ["api.cpp", "router.hip", "dispatch.hip", "ffn.hip", "combine.hip", "backward.hip",
+           "stream.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -532,6 +532,13 @@ const char* moe_status_string(int32_t status) {
   }
 }
 
+int32_t moe_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
+                        void* stream) {
+  if (bytes % 16 != 0 || blocks <= 0 || blocks > (1 << 20)) return MOE_ERR_INVALID_ARG;
+  if (bytes > 0 && (!src || !sink)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_stream_read(src, bytes, sink, blocks, static_cast<hipStream_t>(stream)));
+}
+
 int32_t moe_capacity(const moe_config* cfg, int64_t* C) {
   const int32_t st = check_config(cfg);
   if (st != MOE_OK) return st;

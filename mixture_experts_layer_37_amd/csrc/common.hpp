@@ -20,17 +20,16 @@ __device__ __forceinline__ float bf16_to_f32(bf16 v) {
   return __uint_as_float(uint32_t(v) << 16);
 }
 
-// Round to nearest even; NaN stays NaN.
-__device__ __forceinline__ bf16 f32_to_bf16(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return bf16(u >> 16);
-}
-
+// Round to nearest even (NaN stays NaN), with gfx950's v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  const bf16x2_t b = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &b, 4);
+  return u;
 }
+__device__ __forceinline__ bf16 f32_to_bf16(float x) { return bf16(pack_bf16x2(x, 0.f)); }
 
 // Element traits: how 16 bytes unpack into floats.
 template <typename T>

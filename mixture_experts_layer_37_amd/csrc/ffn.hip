@@ -205,8 +205,11 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const floatx16 (
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           if (GATEUP) {
+            // SiLU(g) u = g u / (1 + e^-g), with the hardware reciprocal
+            // (1 ulp) instead of a correctly rounded division: the product is
+            // rounded to bf16 next
             const float gv = acc[i][j][4 * g + t] * sg[t], uv = acc[i][j + 2][4 * g + t] * su[t];
-            y[t] = gv / (1.f + __expf(-gv)) * uv;
+            y[t] = gv * uv * __builtin_amdgcn_rcpf(1.f + __expf(-gv));
             gp[t] = gv;
             up[t] = uv;
           } else {

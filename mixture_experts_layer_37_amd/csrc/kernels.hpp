@@ -50,6 +50,12 @@ hipError_t launch_route(const RouteShape& rs, const RouteParams& p, int bf16, in
 hipError_t launch_prob_reduce(const double* part, int nblk, int EP, int E, double* total,
                               float* prob_sum, hipStream_t s);
 
+// ---------------------------------------------------------------- yardstick
+// One pass of 16-byte loads over bytes (a multiple of 16) of src; sink gets one
+// word per workgroup (blocks of them).
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks,
+                              hipStream_t s);
+
 // ---------------------------------------------------------------- dispatch
 constexpr int kChunk = 256;  // tokens per dispatch workgroup
 
