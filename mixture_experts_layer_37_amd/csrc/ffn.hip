@@ -27,7 +27,9 @@
 // the MFMAs of one K slice while reading the fragments of the next from LDS.
 // The slots are separate LDS arrays and the loop is unrolled over the ring's
 // period, so the compiler can tell the copies in flight from the slots being
-// read.
+// read.  The forward bf16 products (gemm_chain_kernel) keep the ring running
+// from one tile to the next: the copies past a tile's last step fetch the
+// next tile's first steps; the FP8 and backward products refill it per tile.
 //
 // LDS rows are 128 bytes (8 chunks of 16).  gfx950 serves a 16-byte LDS read
 // for 16 lanes per clock from 64 four-byte banks; storing logical chunk c of
@@ -101,7 +103,7 @@ struct GemmParams {
   int K0 = 0;
 };
 
-// A K chunk of a tail tile (see gemm_bf16_kernel); ks == 1: a whole tile.
+// A K chunk of a tail tile (see xcd_share); ks == 1: a whole tile.
 struct KSplit {
   int kbeg, ksteps;  // 128-byte K steps of this chunk
   int ks;            // chunks of the tile
@@ -691,14 +693,12 @@ __device__ __forceinline__ Unit unit_at(const GemmParams& p, const XcdShare& xs,
 // the same share of real tiles, and the workgroups running together on one
 // XCD hold neighbouring tiles, which share A row panels and weight panels in
 // that XCD's L2.
+// Units u, u + nloc, ... below `units` of this workgroup's share, one at a
+// time: each unit's first copies go out before the previous one's epilogue.
 template <int BM, int NW, bool GATEUP, bool F8, int NA, int NB, bool BT = false>
-__device__ __forceinline__ void grouped_gemm(const GemmParams& p, const Ring& L) {
-  const int mtiles = p.tmap[p.E];
-  const int KT = p.K / Elt<F8>::kStep;
-  const int xcd = blockIdx.x & 7;
-  const XcdShare xs = xcd_share(mtiles * p.ntiles, xcd, p.grid, KT, p.split_max);
-  const int units = xs.full + xs.rem * xs.ks;
-  int u = blockIdx.x >> 3;
+__device__ __forceinline__ void grouped_units(const GemmParams& p, const Ring& L,
+                                              const XcdShare& xs, int xcd, int KT, int mtiles,
+                                              int u, int units) {
   if (u >= units) return;
   const CopyPlan<BM, NW, GATEUP, F8, BT, false> cp(p.K, p.N);
   Unit cur = unit_at<BM>(p, xs, xcd, u, KT, mtiles);
@@ -733,6 +733,16 @@ __device__ __forceinline__ void grouped_gemm(const GemmParams& p, const Ring& L)
   }
 }
 
+template <int BM, int NW, bool GATEUP, bool F8, int NA, int NB, bool BT = false>
+__device__ __forceinline__ void grouped_gemm(const GemmParams& p, const Ring& L) {
+  const int mtiles = p.tmap[p.E];
+  const int KT = p.K / Elt<F8>::kStep;
+  const int xcd = blockIdx.x & 7;
+  const XcdShare xs = xcd_share(mtiles * p.ntiles, xcd, p.grid, KT, p.split_max);
+  grouped_units<BM, NW, GATEUP, F8, NA, NB, BT>(p, L, xs, xcd, KT, mtiles, blockIdx.x >> 3,
+                                                xs.full + xs.rem * xs.ks);
+}
+
 // LDS ring of the copy pipeline: 128-byte rows, BM-row A slots, 256-row B slots.
 #define MOE_GEMM_LDS_RING                                                         \
   __shared__ __attribute__((aligned(1024))) bf16 A0[BM * BK], A1[BM * BK];        \
@@ -740,12 +750,6 @@ __device__ __forceinline__ void grouped_gemm(const GemmParams& p, const Ring& L)
   __shared__ __attribute__((aligned(1024))) bf16 B0[BN * BK], B1[BN * BK];        \
   __shared__ __attribute__((aligned(1024))) bf16 B2[NB == 3 ? BN * BK : 8];       \
   const Ring L{{A0, A1, A2}, {B0, B1, B2}};
-
-template <int BM, int NW, bool GATEUP, int NA, int NB>
-__global__ __launch_bounds__(64 * NW) void gemm_bf16_kernel(GemmParams p) {
-  MOE_GEMM_LDS_RING
-  grouped_gemm<BM, NW, GATEUP, false, NA, NB>(p, L);
-}
 
 // The row-grouped product with the weights stored [K][N] (input gradients:
 // dA = dY W_down[e] and dX = [dG | dU] [W_gate[e]; W_up[e]]).
@@ -1134,8 +1138,361 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_stream_kernel(GemmPara
   wait_vm_seen<0>();  // copies past the share, and the last stores
 }
 
+// Forward grouped GEMM with the copy ring running across units (bf16).  The
+// workgroup's units are those of grouped_gemm (the same XCD slices, rounds
+// and K chunks of a split tail round), one at a time as there, but the copies
+// that would run past a unit's last K step fetch the next unit's first steps
+// instead: the next unit starts with its first NA + NB stages already in
+// flight, no wave waits for the ring to drain between units, and the
+// epilogue's stores overlap those copies.  The ring's slots therefore start a
+// unit at the phase where the previous one left them: unit i starts at slot
+// phase (sum of the earlier units' K steps) mod P.  Each unit's steps run with
+// its slots rotated to phase 0 and passed as restrict parameters, together
+// with the operands: the compiler then tags each copy (its buffer resource is
+// based on an operand parameter) and each fragment read with its slot, and
+// its own wait insertion makes a read wait only for copies into that slot.
+//
+// Epilogue: straight from the accumulators after the unit's last copies, with
+// the same number of stores in every lane whatever the unit (rows past the
+// unit's valid rows and columns past Nout fall outside the output resource
+// and are dropped), so that the next unit's first wait can leave exactly
+// those stores and the newest copies in flight (vector memory operations
+// complete in issue order on this family).
+struct FwUnit {
+  int u;                          // unit of the workgroup's share
+  int kbeg, KT, ks;               // first K step, K steps, K chunks of the tile (1: whole)
+  int e, nt, row0, nvalid, live;  // the tile (live = 0: past the share)
+};
+__device__ __forceinline__ FwUnit fw_unit(const GemmParams& p, const XcdShare& xs, int units,
+                                          int mtiles, int KT, int u) {
+  typedef __attribute__((address_space(4))) const int32_t cint;
+  FwUnit c;
+  c.u = u;
+  c.kbeg = 0;
+  c.KT = KT;
+  c.ks = 1;
+  c.e = c.nt = c.row0 = c.nvalid = c.live = 0;
+  if (u >= units) return c;  // copies from empty resources read zeros
+  int t = xs.tbeg + u;
+  if (u >= xs.full && xs.ks > 1) {  // K chunk kc of tail tile q (as unit_at)
+    const int v = u - xs.full, q = v / xs.ks, kc = v - q * xs.ks;
+    t = xs.tbeg + xs.full + q;
+    c.ks = xs.ks;
+    c.kbeg = kc * KT / xs.ks;
+    c.KT = (kc + 1) * KT / xs.ks - c.kbeg;
+  }
+  // tile t of the numbering of tile_at, read with scalar loads
+  const int g = t / (mtiles * GN);
+  const int r = t - g * mtiles * GN;
+  const int gw = min(GN, p.ntiles - g * GN);
+  const int mt = r / gw;
+  const cint* tab = (cint*)p.tmap + ((p.E + 2) & ~1);
+  const int m0 = tab[2 * mt], m1 = tab[2 * mt + 1];
+  c.nt = g * GN + r % gw;
+  c.e = m1 & 0xffff;
+  c.row0 = m0;
+  c.nvalid = m1 >> 16;
+  c.live = 1;
+  return c;
+}
+
+template <int BM, int NA, int NB, bool GATEUP, bool SAVE>
+__global__ __launch_bounds__(64 * kWaves) void gemm_chain_kernel(GemmParams p) {
+  constexpr int NW = kWaves, WR = 2 * BM / NW, RBLK = WR / 32;
+  constexpr int P = NA == NB ? NA : NA * NB;  // the slots line up again after P steps
+  static_assert(RBLK >= 1 && (NA == 2 || NA == 3) && NB == 3, "ring");
+  static_assert(GATEUP || !SAVE, "pre-activations are a gate/up output");
+  MOE_GEMM_LDS_RING
+  typedef __attribute__((address_space(4))) const int32_t cint;
+  const int mtiles = ((cint*)p.tmap)[p.E];
+  const int KT = p.K / BK;
+  const int xcd = blockIdx.x & 7;
+  const XcdShare xs = xcd_share(mtiles * p.ntiles, xcd, p.grid, KT, p.split_max);
+  const int units = xs.full + xs.rem * xs.ks;
+  if ((int)(blockIdx.x >> 3) >= units) return;
+  using CP = CopyPlan<BM, NW, GATEUP, false>;
+  constexpr int AG = CP::AG, BG = CP::BG;
+  const CP cp(p.K, p.N);
+  const int wave = cp.wave, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, khalf = lane >> 5;
+  const int sw = (l32 >> 1) & 7;  // (row >> 1) & 7 of every fragment row of this lane
+  const size_t rb = (size_t)p.K * 2;  // bytes per row of A and of the weights
+  int aoff[RBLK], boff[4];
+#pragma unroll
+  for (int i = 0; i < RBLK; ++i) aoff[i] = (wm * WR + i * 32 + l32) * 128;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = GATEUP ? ((j < 2 ? 0 : 128) + wn * 64 + (j & 1) * 32 + l32)
+                         : (wn * 128 + j * 32 + l32);
+    boff[j] = r * 128;
+  }
+  bf16x8 fa[2][RBLK], fb[2][4];
+  auto frag = [&](const bf16* slot, int off, int c0) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(slot) + off +
+                                            ((c0 ^ sw) * 16));
+  };
+  // all the fragments of a slice (the next unit's slice 0 is read whatever
+  // its rows)
+  auto fetch = [&](const bf16* as, const bf16* bs, int slice, int st) __attribute__((always_inline)) {
+    const int c0 = 2 * slice + khalf;
+#pragma unroll
+    for (int i = 0; i < RBLK; ++i) fa[st][i] = frag(as, aoff[i], c0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[st][j] = frag(bs, boff[j], c0);
+  };
+  // buffer resources of a unit's A rows and weight panels
+  auto srcA = [&](const char* Ag, const FwUnit& c) __attribute__((always_inline)) {
+    return make_rsrc(Ag + (size_t)c.row0 * rb, (size_t)c.nvalid * rb);
+  };
+  auto srcB = [&](const char* W, const FwUnit& c) __attribute__((always_inline)) {
+    const size_t n0 = (size_t)c.nt * (GATEUP ? 128 : BN);
+    return make_rsrc(W + ((size_t)c.e * p.N + n0) * rb, c.live ? (size_t)(p.N - n0) * rb : 0);
+  };
+  auto copyA = [&](__amdgpu_buffer_rsrc_t r, bf16* as, int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < AG; ++q) dma16(r, as + (wave + NW * q) * 8 * BK, cp.voA[q], kb);
+  };
+  auto copyB = [&](__amdgpu_buffer_rsrc_t r0, __amdgpu_buffer_rsrc_t r1, bf16* bs, int kb)
+                   __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < BG; ++q)
+      dma16((GATEUP && q >= BG / 2) ? r1 : r0, bs + (wave + NW * q) * 8 * BK, cp.voB[q], kb);
+  };
+
+  constexpr int NSL = Elt<false>::kSlices;
+  constexpr int kWaitBase = BG + (NA == 3 ? AG : 0);
+  const char* const pA = static_cast<const char*>(p.A);
+  const char* const pW0 = static_cast<const char*>(p.W0);
+  const char* const pW1 = static_cast<const char*>(p.W1 ? p.W1 : p.W0);
+
+  // One unit: its K steps on slots rotated so that its step 0 is in a0 / b0.
+  // On entry fa/fb[0] hold slice 0 of step 0, and the copies of the unit's
+  // steps 0 .. NA-1 (A) and 0 .. NB-1 (B) are in flight, followed by the
+  // previous unit's epilogue stores.  R: this wave's 32-row
+  // blocks with valid rows (RBLK or none: a wave with some valid rows runs
+  // all its blocks).
+  auto unit = [&](auto Rc, bf16* __restrict__ a0, bf16* __restrict__ a1, bf16* __restrict__ a2,
+                  bf16* __restrict__ b0, bf16* __restrict__ b1, bf16* __restrict__ b2,
+                  const char* __restrict__ Ag, const char* __restrict__ Wg,
+                  const char* __restrict__ Wu, const FwUnit& cur, const FwUnit& nxt)
+                  __attribute__((always_inline)) {
+    constexpr int R = decltype(Rc)::value;
+    bf16* const A[3] = {a0, a1, a2};
+    bf16* const B[3] = {b0, b1, b2};
+    const __amdgpu_buffer_rsrc_t rA = srcA(Ag, cur), rB0 = srcB(Wg, cur), rB1 = srcB(Wu, cur);
+    const __amdgpu_buffer_rsrc_t nA = srcA(Ag, nxt), nB0 = srcB(Wg, nxt), nB1 = srcB(Wu, nxt);
+    const int KTu = cur.KT;
+    floatx16 acc[RBLK][4];
+#pragma unroll
+    for (int i = 0; i < RBLK; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    auto mfmas = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[st][j], fa[st][i], acc[i][j], 0, 0, 0);
+    };
+    constexpr int NM = R * 4, NR = RBLK + 4, NC = AG + BG;
+    constexpr int CPM = NM > 0 ? (NC + NM - 1) / NM : NC, RPM = NM > 0 ? (NR + NM - 1) / NM : NR;
+    auto order = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (m * RPM < NR) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+      }
+    };
+    auto order_copies = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (m * CPM < NC) __builtin_amdgcn_sched_group_barrier(0x020, CPM, 0);
+        if (m * RPM < NR) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+      }
+    };
+    // step j on slots (as, bs); (nas, nbs) hold step j + 1 (or the next
+    // unit's step 0)
+    auto step = [&](int j, bf16* as, bf16* bs, const bf16* nas, const bf16* nbs)
+                    __attribute__((always_inline)) {
+      if (R > 0) {
+#pragma unroll
+        for (int sl = 0; sl + 1 < NSL; ++sl) {
+          fetch(as, bs, sl + 1, (sl + 1) & 1);
+          mfmas(sl & 1);
+          order();
+        }
+      }
+      // step j + 1's A and B have landed; the copies issued in the previous
+      // step for later steps may still be in flight (at a unit's step 0 this
+      // also retires the previous unit's epilogue stores and its last B
+      // copies: one early wait per unit, for one wait count that the
+      // compiler's own wait insertion can follow everywhere)
+      wait_vm_seen<kWaitBase>();
+      wait_lgkm0_seen();  // this wave is done reading (as, bs)
+      barrier_only();
+      // into the slots just read: A for step j + NA and B for step j + NB,
+      // of this unit or, past its end, of the next one
+      const int sa = j + NA, sb = j + NB;
+      const bool na = sa >= KTu, nb = sb >= KTu;
+      const __amdgpu_buffer_rsrc_t ra = na ? nA : rA;
+      const __amdgpu_buffer_rsrc_t rb0 = nb ? nB0 : rB0, rb1 = nb ? nB1 : rB1;
+      const int ka = (na ? nxt.kbeg + sa - KTu : cur.kbeg + sa) * 128;
+      const int kb = (nb ? nxt.kbeg + sb - KTu : cur.kbeg + sb) * 128;
+      if (NA == 2) copyA(ra, as, ka);
+      copyB(rb0, rb1, bs, kb);
+      if (NA == 3) copyA(ra, as, ka);
+      fetch(nas, nbs, 0, 0);
+      if (R > 0) {
+        mfmas((NSL - 1) & 1);
+        order_copies();
+      } else {  // the fragment reads before this step's copies
+        __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, NC, 0);
+      }
+    };
+    int j = 0;
+    for (; j + P <= KTu; j += P) {
+#pragma unroll
+      for (int q = 0; q < P; ++q)
+        step(j + q, A[q % NA], B[q % NB], A[(q + 1) % NA], B[(q + 1) % NB]);
+    }
+    const int rest = KTu - j;  // 0 .. P-1 steps, starting again at slot phase 0
+#pragma unroll
+    for (int q = 0; q < P - 1; ++q)
+      if (q < rest) step(j + q, A[q % NA], B[q % NB], A[(q + 1) % NA], B[(q + 1) % NB]);
+
+    // epilogue
+    if (cur.ks > 1) {  // a K chunk of a tail tile: its float32 partial
+      float* slot = p.part + (size_t)(xcd * xs.nloc + (cur.u - xs.full)) * BM * BN;
+#pragma unroll
+      for (int i = 0; i < RBLK; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4)
+            *part_at<RBLK, NW>(slot, (i * 4 + jj) * 4 + v4) =
+                make_float4(acc[i][jj][4 * v4], acc[i][jj][4 * v4 + 1], acc[i][jj][4 * v4 + 2],
+                            acc[i][jj][4 * v4 + 3]);
+      return;
+    }
+    // lane holds row l32 of each 32 x 32 block and columns 8 g + 4 khalf +
+    // 0..3 (see store_tile).  The two lanes of a row swap halves
+    // (v_permlane32_swap), after which lane (l32, khalf) holds columns
+    // 16 h + 8 khalf + 0..7 of the block for h = 0, 1 and stores each run of 8
+    // with one 16-byte store.  Gate/up: a = SiLU(g) u, and with SAVE also g
+    // and u into C2.
+    auto pack8 = [&](const float* x, const float* y) __attribute__((always_inline)) {
+      const auto s0 = __builtin_amdgcn_permlane32_swap(pack_bf16x2(x[0], x[1]),
+                                                       pack_bf16x2(y[0], y[1]), false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(pack_bf16x2(x[2], x[3]),
+                                                       pack_bf16x2(y[2], y[3]), false, false);
+      const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+      return v;
+    };
+    const int pitch = p.Nout * 2;
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(p.C + (size_t)cur.row0 * p.Nout, (size_t)cur.nvalid * pitch);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(SAVE ? p.C2 + (size_t)cur.row0 * 2 * p.Nout : p.C,
+                                                SAVE ? (size_t)cur.nvalid * 2 * pitch : 0);
+#pragma unroll
+    for (int i = 0; i < RBLK; ++i) {
+      const int r = wm * WR + i * 32 + l32;
+#pragma unroll
+      for (int jj = 0; jj < (GATEUP ? 2 : 4); ++jj)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int col = (GATEUP ? cur.nt * 128 + wn * 64 : cur.nt * BN + wn * 128) + jj * 32 +
+                          16 * h + 8 * khalf;
+          const bool in = col < p.Nout;
+          // runs 2 h (x) and 2 h + 1 (y) of this lane's columns
+          float x[4], y[4], gx[4], gy[4], ux[4], uy[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            gx[t] = acc[i][jj][8 * h + t];
+            gy[t] = acc[i][jj][8 * h + 4 + t];
+            if (GATEUP) {  // SiLU(g) u with the hardware reciprocal, as in store_tile
+              ux[t] = acc[i][jj + 2][8 * h + t];
+              uy[t] = acc[i][jj + 2][8 * h + 4 + t];
+              x[t] = gx[t] * ux[t] * __builtin_amdgcn_rcpf(1.f + __expf(-gx[t]));
+              y[t] = gy[t] * uy[t] * __builtin_amdgcn_rcpf(1.f + __expf(-gy[t]));
+            } else {
+              x[t] = gx[t];
+              y[t] = gy[t];
+            }
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(pack8(x, y), rc,
+                                                 in ? r * pitch + col * 2 : kPastEnd, 0, 0);
+          if (SAVE) {
+            const int ro = r * 2 * pitch;
+            __builtin_amdgcn_raw_buffer_store_b128(pack8(gx, gy), rs,
+                                                   in ? ro + col * 2 : kPastEnd, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(pack8(ux, uy), rs,
+                                                   in ? ro + pitch + col * 2 : kPastEnd, 0, 0);
+          }
+        }
+    }
+  };
+  // the first unit's first copies, into slot phase 0 (its own restrict scope)
+  FwUnit cur = fw_unit(p, xs, units, mtiles, KT, blockIdx.x >> 3);
+  auto prologue = [&](bf16* __restrict__ a0, bf16* __restrict__ a1, bf16* __restrict__ a2,
+                      bf16* __restrict__ b0, bf16* __restrict__ b1, bf16* __restrict__ b2,
+                      const char* __restrict__ Ag, const char* __restrict__ Wg,
+                      const char* __restrict__ Wu) __attribute__((always_inline)) {
+    // steps past a short unit's end copy its last step again (in bounds,
+    // never read): the next unit then starts from a full prologue
+    const __amdgpu_buffer_rsrc_t rA = srcA(Ag, cur), rB0 = srcB(Wg, cur), rB1 = srcB(Wu, cur);
+    bf16* const A[3] = {a0, a1, a2};
+    bf16* const B[3] = {b0, b1, b2};
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      const int k = (cur.kbeg + min(s, cur.KT - 1)) * 128;
+      if (s < NA) copyA(rA, A[s], k);
+      copyB(rB0, rB1, B[s], k);
+    }
+    wait_vm_seen<0>();
+    barrier_only();
+    fetch(a0, b0, 0, 0);
+  };
+  // (with 2 A slots the third A parameter repeats slot 0 and is never used)
+  prologue(L.a[0], L.a[1], L.a[NA == 3 ? 2 : 0], L.b[0], L.b[1], L.b[2], pA, pW0, pW1);
+  int ph = 0;
+  for (;;) {
+    const FwUnit nxt = fw_unit(p, xs, units, mtiles, KT, cur.u + xs.nloc);
+    // rotate the slots so that this unit's step 0 is in slot 0 (selects
+    // among the slots, so that only the ring's own slots are referenced)
+    auto rotA = [&](int k) __attribute__((always_inline)) {
+      if (NA == 2) return (k & 1) ? L.a[1] : L.a[0];
+      const int m = k % 3;
+      return m == 0 ? L.a[0] : (m == 1 ? L.a[1] : L.a[2]);
+    };
+    auto rotB = [&](int k) __attribute__((always_inline)) {
+      const int m = k % 3;
+      return m == 0 ? L.b[0] : (m == 1 ? L.b[1] : L.b[2]);
+    };
+    bf16* const A0 = rotA(ph);
+    bf16* const A1 = rotA(ph + 1);
+    bf16* const A2 = rotA(ph + 2);
+    bf16* const B0r = rotB(ph);
+    bf16* const B1r = rotB(ph + 1);
+    bf16* const B2r = rotB(ph + 2);
+    if (wm * WR < cur.nvalid)
+      unit(std::integral_constant<int, RBLK>{}, A0, A1, A2, B0r, B1r, B2r, pA, pW0, pW1, cur,
+           nxt);
+    else
+      unit(std::integral_constant<int, 0>{}, A0, A1, A2, B0r, B1r, B2r, pA, pW0, pW1, cur, nxt);
+    if (!nxt.live) break;
+    ph = (ph + cur.KT) % P;
+    cur = nxt;
+  }
+  wait_vm_seen<0>();  // copies past the share, and the last stores
+}
+
 // Sum of the K chunks of the tail tiles, in chunk order, then the same
-// epilogue as gemm_bf16_kernel.  Workgroup b handles tail tile b / 8 of XCD
+// epilogue as the GEMM kernels.  Workgroup b handles tail tile b / 8 of XCD
 // b % 8 (if that XCD split its tail); thread i reads the partial groups that
 // thread i of the GEMM wrote.
 template <int BM, int NW, bool GATEUP, bool F8>
@@ -1250,11 +1607,18 @@ int round8(int x) { return (x + 7) & ~7; }
 template <bool GATEUP>
 void launch_gemm(int bm, const GemmParams& p, hipStream_t s) {
   const dim3 grid(p.grid), block(64 * kWaves);
+  const bool save = GATEUP && p.C2;
   if (bm == 256) {
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, kWaves, GATEUP, 2, 3>), grid, block, 0, s, p);
+    if (save)
+      hipLaunchKernelGGL((gemm_chain_kernel<256, 2, 3, GATEUP, GATEUP>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((gemm_chain_kernel<256, 2, 3, GATEUP, false>), grid, block, 0, s, p);
     hipLaunchKernelGGL((ksplit_reduce_kernel<256, kWaves, GATEUP, false>), grid, block, 0, s, p);
   } else {
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, kWaves, GATEUP, 3, 3>), grid, block, 0, s, p);
+    if (save)
+      hipLaunchKernelGGL((gemm_chain_kernel<128, 3, 3, GATEUP, GATEUP>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((gemm_chain_kernel<128, 3, 3, GATEUP, false>), grid, block, 0, s, p);
     hipLaunchKernelGGL((ksplit_reduce_kernel<128, kWaves, GATEUP, false>), grid, block, 0, s, p);
   }
 }
