@@ -1138,6 +1138,73 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_stream_kernel(GemmPara
   wait_vm_seen<0>();  // copies past the share, and the last stores
 }
 
+// Epilogue of one wave's (2 BM / NW) x 128 block with 16-byte stores, the
+// same number in every lane whatever the tile (rows past the tile's nvalid
+// valid rows and columns past Nout fall outside the output resource and are
+// dropped).  The accumulators are transposed blocks as in store_tile: lane
+// holds row l32 of each 32 x 32 block and columns 8 g + 4 khalf + 0..3.  The
+// two lanes of a row swap halves (v_permlane32_swap exchanges lanes 32..63 of
+// its first operand with lanes 0..31 of its second), after which lane
+// (l32, khalf) holds columns 16 h + 8 khalf + 0..7 of the block for h = 0, 1.
+// Gate/up: a = SiLU(g) u, and with SAVE also g and u into C2.  Stores per
+// lane: RBLK * (GATEUP ? 2 : 4) * 2, three times that with SAVE.
+template <int BM, int NW, bool GATEUP, bool SAVE>
+__device__ __forceinline__ void store_tile16(const GemmParams& p,
+                                             const floatx16 (&acc)[(2 * BM / NW) / 32][4],
+                                             int row0, int nvalid, int nt, int wave, int lane) {
+  constexpr int WR = 2 * BM / NW, RBLK = WR / 32;
+  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, khalf = lane >> 5;
+  auto pack8 = [&](const float* x, const float* y) __attribute__((always_inline)) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(pack_bf16x2(x[0], x[1]),
+                                                     pack_bf16x2(y[0], y[1]), false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(pack_bf16x2(x[2], x[3]),
+                                                     pack_bf16x2(y[2], y[3]), false, false);
+    const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+    return v;
+  };
+  const int pitch = p.Nout * 2;
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + (size_t)row0 * p.Nout, (size_t)nvalid * pitch);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(SAVE ? p.C2 + (size_t)row0 * 2 * p.Nout : p.C,
+                                              SAVE ? (size_t)nvalid * 2 * pitch : 0);
+#pragma unroll
+  for (int i = 0; i < RBLK; ++i) {
+    const int r = wm * WR + i * 32 + l32;
+#pragma unroll
+    for (int j = 0; j < (GATEUP ? 2 : 4); ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int col = (GATEUP ? nt * 128 + wn * 64 : nt * BN + wn * 128) + j * 32 + 16 * h +
+                        8 * khalf;
+        const bool in = col < p.Nout;
+        // runs 2 h (x) and 2 h + 1 (y) of this lane's columns
+        float x[4], y[4], gx[4], gy[4], ux[4], uy[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          gx[t] = acc[i][j][8 * h + t];
+          gy[t] = acc[i][j][8 * h + 4 + t];
+          if (GATEUP) {  // SiLU(g) u with the hardware reciprocal, as in store_tile
+            ux[t] = acc[i][j + 2][8 * h + t];
+            uy[t] = acc[i][j + 2][8 * h + 4 + t];
+            x[t] = gx[t] * ux[t] * __builtin_amdgcn_rcpf(1.f + __expf(-gx[t]));
+            y[t] = gy[t] * uy[t] * __builtin_amdgcn_rcpf(1.f + __expf(-gy[t]));
+          } else {
+            x[t] = gx[t];
+            y[t] = gy[t];
+          }
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(pack8(x, y), rc, in ? r * pitch + col * 2 : kPastEnd,
+                                               0, 0);
+        if (SAVE) {
+          const int ro = r * 2 * pitch;
+          __builtin_amdgcn_raw_buffer_store_b128(pack8(gx, gy), rs, in ? ro + col * 2 : kPastEnd,
+                                                 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(pack8(ux, uy), rs,
+                                                 in ? ro + pitch + col * 2 : kPastEnd, 0, 0);
+        }
+      }
+  }
+}
+
 // Forward grouped GEMM with the copy ring running across units (bf16).  The
 // workgroup's units are those of grouped_gemm (the same XCD slices, rounds
 // and K chunks of a split tail round), one at a time as there, but the copies
@@ -1379,62 +1446,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_chain_kernel(GemmParams p) {
                             acc[i][jj][4 * v4 + 3]);
       return;
     }
-    // lane holds row l32 of each 32 x 32 block and columns 8 g + 4 khalf +
-    // 0..3 (see store_tile).  The two lanes of a row swap halves
-    // (v_permlane32_swap), after which lane (l32, khalf) holds columns
-    // 16 h + 8 khalf + 0..7 of the block for h = 0, 1 and stores each run of 8
-    // with one 16-byte store.  Gate/up: a = SiLU(g) u, and with SAVE also g
-    // and u into C2.
-    auto pack8 = [&](const float* x, const float* y) __attribute__((always_inline)) {
-      const auto s0 = __builtin_amdgcn_permlane32_swap(pack_bf16x2(x[0], x[1]),
-                                                       pack_bf16x2(y[0], y[1]), false, false);
-      const auto s1 = __builtin_amdgcn_permlane32_swap(pack_bf16x2(x[2], x[3]),
-                                                       pack_bf16x2(y[2], y[3]), false, false);
-      const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
-      return v;
-    };
-    const int pitch = p.Nout * 2;
-    const __amdgpu_buffer_rsrc_t rc =
-        make_rsrc(p.C + (size_t)cur.row0 * p.Nout, (size_t)cur.nvalid * pitch);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(SAVE ? p.C2 + (size_t)cur.row0 * 2 * p.Nout : p.C,
-                                                SAVE ? (size_t)cur.nvalid * 2 * pitch : 0);
-#pragma unroll
-    for (int i = 0; i < RBLK; ++i) {
-      const int r = wm * WR + i * 32 + l32;
-#pragma unroll
-      for (int jj = 0; jj < (GATEUP ? 2 : 4); ++jj)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int col = (GATEUP ? cur.nt * 128 + wn * 64 : cur.nt * BN + wn * 128) + jj * 32 +
-                          16 * h + 8 * khalf;
-          const bool in = col < p.Nout;
-          // runs 2 h (x) and 2 h + 1 (y) of this lane's columns
-          float x[4], y[4], gx[4], gy[4], ux[4], uy[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            gx[t] = acc[i][jj][8 * h + t];
-            gy[t] = acc[i][jj][8 * h + 4 + t];
-            if (GATEUP) {  // SiLU(g) u with the hardware reciprocal, as in store_tile
-              ux[t] = acc[i][jj + 2][8 * h + t];
-              uy[t] = acc[i][jj + 2][8 * h + 4 + t];
-              x[t] = gx[t] * ux[t] * __builtin_amdgcn_rcpf(1.f + __expf(-gx[t]));
-              y[t] = gy[t] * uy[t] * __builtin_amdgcn_rcpf(1.f + __expf(-gy[t]));
-            } else {
-              x[t] = gx[t];
-              y[t] = gy[t];
-            }
-          }
-          __builtin_amdgcn_raw_buffer_store_b128(pack8(x, y), rc,
-                                                 in ? r * pitch + col * 2 : kPastEnd, 0, 0);
-          if (SAVE) {
-            const int ro = r * 2 * pitch;
-            __builtin_amdgcn_raw_buffer_store_b128(pack8(gx, gy), rs,
-                                                   in ? ro + col * 2 : kPastEnd, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(pack8(ux, uy), rs,
-                                                   in ? ro + pitch + col * 2 : kPastEnd, 0, 0);
-          }
-        }
-    }
+    store_tile16<BM, NW, GATEUP, SAVE>(p, acc, cur.row0, cur.nvalid, cur.nt, wave, lane);
   };
   // the first unit's first copies, into slot phase 0 (its own restrict scope)
   FwUnit cur = fw_unit(p, xs, units, mtiles, KT, blockIdx.x >> 3);
@@ -1529,6 +1541,46 @@ __global__ __launch_bounds__(64 * NW) void ksplit_reduce_kernel(GemmParams p) {
   store_tile<BM, NW, GATEUP, F8>(p, acc, ta);
 }
 
+// The same sum for bf16 outputs, by wave rows: workgroup b (two waves) takes
+// wave row (b / 8) % 4 of tail tile b / 32 of XCD b % 8, i.e. the partials of
+// the GEMM's waves 2 wm and 2 wm + 1, and stores them with store_tile16.  Four
+// workgroups per tile keep more loads in flight than one.
+template <int BM, bool GATEUP, bool SAVE>
+__global__ __launch_bounds__(128) void ksplit_sum_kernel(GemmParams p) {
+  constexpr int NW = kWaves, RBLK = (2 * BM / NW) / 32;
+  const int mtiles = p.tmap[p.E];
+  const int xcd = blockIdx.x & 7, rest = blockIdx.x >> 3, q = rest >> 2, wm = rest & 3;
+  const XcdShare xs = xcd_share(mtiles * p.ntiles, xcd, p.grid, p.K / BK, p.split_max);
+  if (xs.ks <= 1 || q >= xs.rem) return;
+  const TileAt ta = tile_at<BM>(p, xs.tbeg + xs.full + q, mtiles);
+  const int wave = 2 * wm + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tid = wave * 64 + lane;  // the GEMM thread that wrote these partials
+  floatx16 acc[RBLK][4];
+#pragma unroll
+  for (int i = 0; i < RBLK; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  for (int c = 0; c < xs.ks; ++c) {  // in chunk order
+    const float4* slot =
+        reinterpret_cast<const float4*>(p.part + (size_t)(xcd * xs.nloc + q * xs.ks + c) * BM * BN);
+#pragma unroll
+    for (int i = 0; i < RBLK; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const float4 x = slot[(size_t)((i * 4 + j) * 4 + v4) * 64 * NW + tid];
+          acc[i][j][4 * v4] += x.x;
+          acc[i][j][4 * v4 + 1] += x.y;
+          acc[i][j][4 * v4 + 2] += x.z;
+          acc[i][j][4 * v4 + 3] += x.w;
+        }
+  }
+  store_tile16<BM, NW, GATEUP, SAVE>(p, acc, ta.row0, ta.nvalid, ta.nt, wave, lane);
+}
+
 // float32 path: one thread per output, plain dot products (small workloads).
 template <bool GATEUP>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* A, const int32_t* offset,
@@ -1613,13 +1665,23 @@ void launch_gemm(int bm, const GemmParams& p, hipStream_t s) {
       hipLaunchKernelGGL((gemm_chain_kernel<256, 2, 3, GATEUP, GATEUP>), grid, block, 0, s, p);
     else
       hipLaunchKernelGGL((gemm_chain_kernel<256, 2, 3, GATEUP, false>), grid, block, 0, s, p);
-    hipLaunchKernelGGL((ksplit_reduce_kernel<256, kWaves, GATEUP, false>), grid, block, 0, s, p);
+    if (save)
+      hipLaunchKernelGGL((ksplit_sum_kernel<256, GATEUP, GATEUP>), dim3(4 * p.grid), dim3(128), 0,
+                         s, p);
+    else
+      hipLaunchKernelGGL((ksplit_sum_kernel<256, GATEUP, false>), dim3(4 * p.grid), dim3(128), 0,
+                         s, p);
   } else {
     if (save)
       hipLaunchKernelGGL((gemm_chain_kernel<128, 3, 3, GATEUP, GATEUP>), grid, block, 0, s, p);
     else
       hipLaunchKernelGGL((gemm_chain_kernel<128, 3, 3, GATEUP, false>), grid, block, 0, s, p);
-    hipLaunchKernelGGL((ksplit_reduce_kernel<128, kWaves, GATEUP, false>), grid, block, 0, s, p);
+    if (save)
+      hipLaunchKernelGGL((ksplit_sum_kernel<128, GATEUP, GATEUP>), dim3(4 * p.grid), dim3(128), 0,
+                         s, p);
+    else
+      hipLaunchKernelGGL((ksplit_sum_kernel<128, GATEUP, false>), dim3(4 * p.grid), dim3(128), 0,
+                         s, p);
   }
 }
 
@@ -1627,10 +1689,12 @@ void launch_gemm_bt(int bm, const GemmParams& p, hipStream_t s) {
   const dim3 grid(p.grid), block(64 * kWaves);
   if (bm == 256) {
     hipLaunchKernelGGL((gemm_bt_kernel<256, kWaves, 2, 3>), grid, block, 0, s, p);
-    hipLaunchKernelGGL((ksplit_reduce_kernel<256, kWaves, false, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ksplit_sum_kernel<256, false, false>), dim3(4 * p.grid), dim3(128), 0, s,
+                       p);
   } else {
     hipLaunchKernelGGL((gemm_bt_kernel<128, kWaves, 3, 3>), grid, block, 0, s, p);
-    hipLaunchKernelGGL((ksplit_reduce_kernel<128, kWaves, false, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((ksplit_sum_kernel<128, false, false>), dim3(4 * p.grid), dim3(128), 0, s,
+                       p);
   }
 }
 
