@@ -1148,10 +1148,11 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_stream_kernel(GemmPara
 // (l32, khalf) holds columns 16 h + 8 khalf + 0..7 of the block for h = 0, 1.
 // Gate/up: a = SiLU(g) u, and with SAVE also g and u into C2.  Stores per
 // lane: RBLK * (GATEUP ? 2 : 4) * 2, three times that with SAVE.
-template <int BM, int NW, bool GATEUP, bool SAVE>
+template <int BM, int NW, bool GATEUP, bool SAVE, bool F8 = false>
 __device__ __forceinline__ void store_tile16(const GemmParams& p,
                                              const floatx16 (&acc)[(2 * BM / NW) / 32][4],
-                                             int row0, int nvalid, int nt, int wave, int lane) {
+                                             int row0, int nvalid, int nt, int wave, int lane,
+                                             int e = 0) {
   constexpr int WR = 2 * BM / NW, RBLK = WR / 32;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, khalf = lane >> 5;
   auto pack8 = [&](const float* x, const float* y) __attribute__((always_inline)) {
@@ -1169,6 +1170,9 @@ __device__ __forceinline__ void store_tile16(const GemmParams& p,
 #pragma unroll
   for (int i = 0; i < RBLK; ++i) {
     const int r = wm * WR + i * 32 + l32;
+    // FP8: the row's power-of-two scale (rows past the valid ones, never
+    // stored, take the last valid row's)
+    const float sa = F8 ? p.sa[row0 + min(r, nvalid - 1)] : 1.f;
 #pragma unroll
     for (int j = 0; j < (GATEUP ? 2 : 4); ++j)
 #pragma unroll
@@ -1176,15 +1180,34 @@ __device__ __forceinline__ void store_tile16(const GemmParams& p,
         const int col = (GATEUP ? nt * 128 + wn * 64 : nt * BN + wn * 128) + j * 32 + 16 * h +
                         8 * khalf;
         const bool in = col < p.Nout;
-        // runs 2 h (x) and 2 h + 1 (y) of this lane's columns
+        // runs 2 h (x) and 2 h + 1 (y) of this lane's own columns (before
+        // the swap): they start at cx and cx + 8
+        const int cx = (GATEUP ? nt * 128 + wn * 64 : nt * BN + wn * 128) + j * 32 + 16 * h +
+                       4 * khalf;
+        float sgx[4] = {1.f, 1.f, 1.f, 1.f}, sgy[4] = {1.f, 1.f, 1.f, 1.f};
+        float sux[4] = {1.f, 1.f, 1.f, 1.f}, suy[4] = {1.f, 1.f, 1.f, 1.f};
+        if (F8) {  // power-of-two scales: the products are exact
+          const size_t b = (size_t)e * p.N;
+          const int c0 = cx < p.Nout ? cx : 0, c1 = cx + 8 < p.Nout ? cx + 8 : 0;
+          const float4 a0 = *reinterpret_cast<const float4*>(p.sw0 + b + c0);
+          const float4 a1 = *reinterpret_cast<const float4*>(p.sw0 + b + c1);
+          sgx[0] = sa * a0.x; sgx[1] = sa * a0.y; sgx[2] = sa * a0.z; sgx[3] = sa * a0.w;
+          sgy[0] = sa * a1.x; sgy[1] = sa * a1.y; sgy[2] = sa * a1.z; sgy[3] = sa * a1.w;
+          if (GATEUP) {
+            const float4 b0 = *reinterpret_cast<const float4*>(p.sw1 + b + c0);
+            const float4 b1 = *reinterpret_cast<const float4*>(p.sw1 + b + c1);
+            sux[0] = sa * b0.x; sux[1] = sa * b0.y; sux[2] = sa * b0.z; sux[3] = sa * b0.w;
+            suy[0] = sa * b1.x; suy[1] = sa * b1.y; suy[2] = sa * b1.z; suy[3] = sa * b1.w;
+          }
+        }
         float x[4], y[4], gx[4], gy[4], ux[4], uy[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          gx[t] = acc[i][j][8 * h + t];
-          gy[t] = acc[i][j][8 * h + 4 + t];
+          gx[t] = acc[i][j][8 * h + t] * sgx[t];
+          gy[t] = acc[i][j][8 * h + 4 + t] * sgy[t];
           if (GATEUP) {  // SiLU(g) u with the hardware reciprocal, as in store_tile
-            ux[t] = acc[i][j + 2][8 * h + t];
-            uy[t] = acc[i][j + 2][8 * h + 4 + t];
+            ux[t] = acc[i][j + 2][8 * h + t] * sux[t];
+            uy[t] = acc[i][j + 2][8 * h + 4 + t] * suy[t];
             x[t] = gx[t] * ux[t] * __builtin_amdgcn_rcpf(1.f + __expf(-gx[t]));
             y[t] = gy[t] * uy[t] * __builtin_amdgcn_rcpf(1.f + __expf(-gy[t]));
           } else {
@@ -1263,7 +1286,7 @@ __device__ __forceinline__ FwUnit fw_unit(const GemmParams& p, const XcdShare& x
   return c;
 }
 
-template <int BM, int NA, int NB, bool GATEUP, bool SAVE>
+template <int BM, int NA, int NB, bool GATEUP, bool SAVE, bool F8 = false>
 __global__ __launch_bounds__(64 * kWaves) void gemm_chain_kernel(GemmParams p) {
   constexpr int NW = kWaves, WR = 2 * BM / NW, RBLK = WR / 32;
   constexpr int P = NA == NB ? NA : NA * NB;  // the slots line up again after P steps
@@ -1272,18 +1295,20 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_chain_kernel(GemmParams p) {
   MOE_GEMM_LDS_RING
   typedef __attribute__((address_space(4))) const int32_t cint;
   const int mtiles = ((cint*)p.tmap)[p.E];
-  const int KT = p.K / BK;
+  const int KT = p.K / Elt<F8>::kStep;
   const int xcd = blockIdx.x & 7;
   const XcdShare xs = xcd_share(mtiles * p.ntiles, xcd, p.grid, KT, p.split_max);
   const int units = xs.full + xs.rem * xs.ks;
   if ((int)(blockIdx.x >> 3) >= units) return;
-  using CP = CopyPlan<BM, NW, GATEUP, false>;
+  using CP = CopyPlan<BM, NW, GATEUP, F8>;
   constexpr int AG = CP::AG, BG = CP::BG;
   const CP cp(p.K, p.N);
   const int wave = cp.wave, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, khalf = lane >> 5;
   const int sw = (l32 >> 1) & 7;  // (row >> 1) & 7 of every fragment row of this lane
-  const size_t rb = (size_t)p.K * 2;  // bytes per row of A and of the weights
+  const size_t rb = (size_t)p.K * Elt<F8>::kBytes;  // bytes per row of A and of the weights
+  constexpr int FC = F8 ? 2 : 1;  // 16-byte chunks per fragment and lane
+  using Frag = typename Elt<F8>::Frag;
   int aoff[RBLK], boff[4];
 #pragma unroll
   for (int i = 0; i < RBLK; ++i) aoff[i] = (wm * WR + i * 32 + l32) * 128;
@@ -1293,15 +1318,23 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_chain_kernel(GemmParams p) {
                          : (wn * 128 + j * 32 + l32);
     boff[j] = r * 128;
   }
-  bf16x8 fa[2][RBLK], fb[2][4];
+  Frag fa[2][RBLK], fb[2][4];
+  // one fragment: FC chunks of 16 bytes of a row, at physical chunks c ^ sw
   auto frag = [&](const bf16* slot, int off, int c0) __attribute__((always_inline)) {
-    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(slot) + off +
-                                            ((c0 ^ sw) * 16));
+    const char* row = reinterpret_cast<const char*>(slot) + off;
+    if constexpr (F8) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(row + ((c0 ^ sw) * 16));
+      const u32x4 y = *reinterpret_cast<const u32x4*>(row + (((c0 + 1) ^ sw) * 16));
+      return Frag{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
+                  (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+    } else {
+      return *reinterpret_cast<const Frag*>(row + ((c0 ^ sw) * 16));
+    }
   };
   // all the fragments of a slice (the next unit's slice 0 is read whatever
   // its rows)
   auto fetch = [&](const bf16* as, const bf16* bs, int slice, int st) __attribute__((always_inline)) {
-    const int c0 = 2 * slice + khalf;
+    const int c0 = FC * (2 * slice + khalf);
 #pragma unroll
     for (int i = 0; i < RBLK; ++i) fa[st][i] = frag(as, aoff[i], c0);
 #pragma unroll
@@ -1326,7 +1359,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_chain_kernel(GemmParams p) {
       dma16((GATEUP && q >= BG / 2) ? r1 : r0, bs + (wave + NW * q) * 8 * BK, cp.voB[q], kb);
   };
 
-  constexpr int NSL = Elt<false>::kSlices;
+  constexpr int NSL = Elt<F8>::kSlices;
   constexpr int kWaitBase = BG + (NA == 3 ? AG : 0);
   const char* const pA = static_cast<const char*>(p.A);
   const char* const pW0 = static_cast<const char*>(p.W0);
@@ -1361,10 +1394,14 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_chain_kernel(GemmParams p) {
       for (int i = 0; i < R; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[st][j], fa[st][i], acc[i][j], 0, 0, 0);
+          if constexpr (F8)  // format codes 0, 0: both operands E4M3; no block scales
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fb[st][j], fa[st][i], acc[i][j], 0, 0, 0, 0, 0, 0);
+          else
+            acc[i][j] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[st][j], fa[st][i], acc[i][j], 0, 0, 0);
     };
-    constexpr int NM = R * 4, NR = RBLK + 4, NC = AG + BG;
+    constexpr int NM = R * 4, NR = (RBLK + 4) * FC, NC = AG + BG;
     constexpr int CPM = NM > 0 ? (NC + NM - 1) / NM : NC, RPM = NM > 0 ? (NR + NM - 1) / NM : NR;
     auto order = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -1446,7 +1483,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_chain_kernel(GemmParams p) {
                             acc[i][jj][4 * v4 + 3]);
       return;
     }
-    store_tile16<BM, NW, GATEUP, SAVE>(p, acc, cur.row0, cur.nvalid, cur.nt, wave, lane);
+    store_tile16<BM, NW, GATEUP, SAVE, F8>(p, acc, cur.row0, cur.nvalid, cur.nt, wave, lane, cur.e);
   };
   // the first unit's first copies, into slot phase 0 (its own restrict scope)
   FwUnit cur = fw_unit(p, xs, units, mtiles, KT, blockIdx.x >> 3);
@@ -1702,10 +1739,10 @@ template <bool GATEUP>
 void launch_gemm_fp8(int bm, const GemmParams& p, hipStream_t s) {
   const dim3 grid(p.grid), block(64 * kWaves);
   if (bm == 256) {
-    hipLaunchKernelGGL((gemm_fp8_kernel<256, kWaves, GATEUP, 2, 3>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gemm_chain_kernel<256, 2, 3, GATEUP, false, true>), grid, block, 0, s, p);
     hipLaunchKernelGGL((ksplit_reduce_kernel<256, kWaves, GATEUP, true>), grid, block, 0, s, p);
   } else {
-    hipLaunchKernelGGL((gemm_fp8_kernel<128, kWaves, GATEUP, 3, 3>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gemm_chain_kernel<128, 3, 3, GATEUP, false, true>), grid, block, 0, s, p);
     hipLaunchKernelGGL((ksplit_reduce_kernel<128, kWaves, GATEUP, true>), grid, block, 0, s, p);
   }
 }
