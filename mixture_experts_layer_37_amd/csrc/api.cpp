@@ -140,14 +140,17 @@ struct Plan {
 };
 
 struct RouteWs {
-  size_t wt, wnt, part, total;
+  size_t wp, wnp, lpart, part, total;
   RouteShape rs;
 };
 RouteWs plan_route(const Dims& d, int noisy, Plan& pl) {
   RouteWs w;
-  w.rs = route_shape((int)d.T, (int)d.E, d.bf16, noisy);
-  w.wt = d.bf16 ? pl.add((size_t)w.rs.EP * d.h * 2) : 0;
-  w.wnt = (d.bf16 && noisy) ? pl.add((size_t)w.rs.EP * d.h * 2) : 0;
+  w.rs = route_shape((int)d.T, (int)d.E, (int)d.h, d.bf16, noisy);
+  // bf16: zero-padded copies of W_r and W_noise (used when E % 8 != 0 or a
+  // weight is not 16-byte aligned), and the logits GEMM's float32 products
+  w.wp = d.bf16 ? pl.add((size_t)w.rs.Ew * d.h * 2) : 0;
+  w.wnp = (d.bf16 && noisy) ? pl.add((size_t)w.rs.Ew * d.h * 2) : 0;
+  w.lpart = d.bf16 ? pl.add((size_t)(noisy ? 2 : 1) * w.rs.KS * d.T * w.rs.EP * sizeof(float)) : 0;
   // per-workgroup partials: EP score columns and one LSE^2 column
   w.part = pl.add((size_t)(w.rs.nblk > 0 ? w.rs.nblk : 1) * (w.rs.EP + 1) * sizeof(double));
   w.total = pl.add((size_t)(w.rs.EP + 1) * sizeof(double));
@@ -370,18 +373,22 @@ int32_t run_route(const Dims& d, const moe_config* c, const RouteWs& w, const vo
   p.topk_gate = gate;
   p.logits = logits;
   p.prob_part = at<double>(ws, w.part);
+  p.W = W_r;
+  p.Wn = c->noisy ? W_noise : nullptr;
+  p.lpart = nullptr;
   if (d.bf16) {
-    MOE_TRY(launch_transpose_router_w(W_r, at<void>(ws, w.wt), (int)d.h, (int)d.E, w.rs.EP, s));
-    p.Wt = at<void>(ws, w.wt);
-    p.Wnt = nullptr;
-    if (c->noisy) {
-      MOE_TRY(launch_transpose_router_w(W_noise, at<void>(ws, w.wnt), (int)d.h, (int)d.E,
-                                        w.rs.EP, s));
-      p.Wnt = at<void>(ws, w.wnt);
+    // the logits GEMM reads the weights in place in rows of a multiple of 8
+    // columns at 16-byte alignment; anything else goes through a padded copy
+    auto in_place = [&](const void* W) { return d.E % 8 == 0 && (uintptr_t)W % 16 == 0; };
+    if (!in_place(W_r)) {
+      MOE_TRY(launch_pad_router_w(W_r, at<void>(ws, w.wp), (int)d.h, (int)d.E, w.rs.Ew, s));
+      p.W = at<void>(ws, w.wp);
     }
-  } else {
-    p.Wt = W_r;
-    p.Wnt = c->noisy ? W_noise : nullptr;
+    if (c->noisy && !in_place(W_noise)) {
+      MOE_TRY(launch_pad_router_w(W_noise, at<void>(ws, w.wnp), (int)d.h, (int)d.E, w.rs.Ew, s));
+      p.Wn = at<void>(ws, w.wnp);
+    }
+    p.lpart = at<float>(ws, w.lpart);
   }
   MOE_TRY(launch_route(w.rs, p, d.bf16, c->noisy, s));
   return MOE_OK;

@@ -187,6 +187,43 @@ __device__ __forceinline__ uint64_t match_lanes(int mine, int theirs, bool valid
   return m;
 }
 
+// ------------------------------------------------ LDS-direct copies, waits
+// Third dword of a raw buffer resource on gfx9-family parts (32-bit data
+// format, no swizzle); loads outside num_records bytes return zero without
+// touching memory.
+constexpr int kBufFlags = 0x00020000;
+constexpr int kPastEnd = 0x7ffffff0;  // a byte offset past every resource
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  const int n = bytes > 0x7fffffffull ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kBufFlags);
+}
+
+// One wave-wide 16-byte-per-lane load straight into LDS: lane i's 16 bytes
+// land at lds + 16 * i.  voff: per-lane byte offset, soff: uniform byte offset.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
+}
+
+// Workgroup barrier without the release fence of __syncthreads(): that fence
+// would wait for every load in flight, including the LDS copies of the next
+// stages.  Callers make their own data visible first (wait_vm_seen); the
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt through the builtin rather than inline asm, so that the
+// compiler's own wait insertion sees it and knows which copies have landed
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8;
+// the counters not waited on are left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm_seen() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0_seen() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
 // Workgroups are handed to the 8 XCDs round-robin (workgroup i -> XCD i % 8).
 // Remap so each XCD walks one contiguous range of logical tiles: tiles that
 // share operands then run together and hit the same L2.  nblk % 8 == 0.

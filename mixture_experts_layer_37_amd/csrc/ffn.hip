@@ -73,9 +73,6 @@ struct Elt {
   static constexpr int kSlices = F8 ? 2 : 4;   // MFMA K slices per step
   using Frag = std::conditional_t<F8, v8i, bf16x8>;
 };
-// Third dword of a raw buffer resource on gfx9-family parts (32-bit data
-// format, no swizzle); loads outside num_records bytes return zero.
-constexpr int kBufFlags = 0x00020000;
 
 struct GemmParams {
   const void* A;         // [rows][K], experts' row blocks back to back (bf16 or FP8)
@@ -231,27 +228,12 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const floatx16 (
   }
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
-  const int n = bytes > 0x7fffffffull ? 0x7fffffff : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kBufFlags);
-}
-
-// One wave-wide 16-byte-per-lane load straight into LDS: lane i's 16 bytes
-// land at lds + 16 * i.  voff: per-lane byte offset, soff: uniform byte offset.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
-}
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Workgroup barrier without the release fence of __syncthreads(): that fence
-// would wait for every load in flight, including the LDS copies of the next
-// stages.  Callers make their own data visible first (wait_vm); the memory
-// clobber keeps the compiler from moving LDS accesses across the barrier.
-__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 // LDS slots of the copy pipeline: NA slots of A tiles and NB of B tiles
 // (2 or 3 each); operand X of step j is copied N_X steps ahead.
@@ -873,20 +855,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wgrad_kernel(GemmParams p) {
   }
 }
 
-// s_waitcnt through the builtin rather than inline asm, so that the
-// compiler's own wait insertion sees it and knows which copies have landed
-// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8;
-// the counters not waited on are left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vm_seen() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void wait_lgkm0_seen() {
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
-}
 constexpr int kWgStores = 16;  // 2 row blocks x 4 column blocks x 2 runs of 8 columns
-constexpr int kPastEnd = 0x7ffffff0;  // a byte offset past every output resource
 // A copy cursor: plain integers (uniform, kept in SGPRs); the buffer
 // resources are rebuilt from them at each copy.
 struct WgCursor {

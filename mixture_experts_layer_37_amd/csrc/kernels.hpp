@@ -22,8 +22,9 @@ struct RouteParams {
   uint64_t seed;        // noisy routing: key of the draws' generator
   uint64_t rng_offset;  // ... and the counter of token 0, expert 0
   float* noise_out;     // optional [T][E]: the standard-normal draws used
-  const void* Wt;    // bf16: W_r transposed to [EP][h], zero rows past E; f32: W_r [h][E]
-  const void* Wnt;   // same for W_noise (noisy only)
+  const void* W;     // W_r [h][E]; bf16: [h][Ew] (see RouteShape), 16-byte aligned
+  const void* Wn;    // same for W_noise (noisy only)
+  float* lpart;      // bf16: [1 + noisy][KS][T][EP] float32 products over the K ranges
   int32_t* topk_idx;
   float* topk_gate;
   float* logits;     // optional [T][E]
@@ -34,14 +35,17 @@ struct RouteParams {
 struct RouteShape {
   int EP;    // experts padded to 16 * NB (NB a power of two)
   int NB;
-  int MW;    // 16-row blocks per wave (bf16) ; rows per block = 16 * MW
-  int RB;    // tokens per workgroup
-  int nblk;  // workgroups
+  int RB;    // tokens per selection workgroup (float32: per fused workgroup)
+  int nblk;  // selection (float32: fused) workgroups
+  // bf16 logits GEMM: 64-token x BN-expert tiles over KS ranges of K
+  int Ew;    // row pitch of the weights it reads: E rounded up to 8
+  int BN, WM, KS, mblocks, nblocks;
 };
 
-RouteShape route_shape(int T, int E, int bf16, int noisy);
-hipError_t launch_transpose_router_w(const void* W, void* WT, int h, int E, int EP,
-                                     hipStream_t s);
+RouteShape route_shape(int T, int E, int h, int bf16, int noisy);
+// W [h][E] -> Wp [h][Ew], zero columns E..Ew-1 (bf16; for E % 8 != 0 or a
+// W that is not 16-byte aligned).
+hipError_t launch_pad_router_w(const void* W, void* Wp, int h, int E, int Ew, hipStream_t s);
 hipError_t launch_route(const RouteShape& rs, const RouteParams& p, int bf16, int noisy,
                         hipStream_t s);
 // total[e] (double, optional; E + 1 entries, the last the sum over tokens of

@@ -10,14 +10,17 @@
 // "softmax 门控还是 sigmoid 门控", and P_i of section "负载均衡辅助损失：推导与梯度"
 // (for sigmoid scores P averages s / sum_j s).
 //
-// bf16 path: the logits GEMM runs on v_mfma_f32_16x16x32_bf16 with float32
-// accumulation.  The four waves of a workgroup split K round-robin in 32-wide
-// steps (adjacent 64-byte pieces of each U row go to different waves, so a
-// row is read as one contiguous 256-byte run) and each wave keeps every
-// expert column of its 16*MW tokens in registers.  The four partial sums are
-// added in wave order through LDS, so the result does not depend on timing.
-// The epilogue then gives each wave whole tokens: one token's E logits are
-// spread over the 64 lanes, max / sum / argmax are butterfly reductions.
+// bf16 path, two kernels.  route_logits_kernel computes H = U W_r (and
+// U W_noise) as a tiled GEMM on v_mfma_f32_16x16x32_bf16 with float32
+// accumulation: a workgroup owns 64 tokens x BN experts (of both matrices when
+// noisy) over one of KS ranges of K.  64-wide K chunks of the U rows and of
+// the weight rows, read in their own [h][E] layout, are copied straight into
+// a ring of LDS stages; the weight fragments come out K-contiguous through
+// the transposing LDS read.  Each range's float32 products go to a
+// workspace.  route_select_kernel then gives each wave whole tokens: it adds
+// a token's K ranges in range order (so the result does not depend on
+// timing), and the epilogue spreads its E logits over the 64 lanes, with
+// max / sum / argmax as butterfly reductions.
 #include <math.h>
 
 #include "common.hpp"
@@ -31,11 +34,12 @@ __device__ __forceinline__ float softplus_f(float x) {
   return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
 }
 
-// Shared epilogue.  L (and Ln) hold the [RB][EP] float32 products of this
-// workgroup's tokens.
-template <int EP, int RB, bool NOISY>
-__device__ void route_epilogue(const float* L, const float* Ln, double (*Ps)[EP + 1],
-                               const RouteParams& p, int t0) {
+// Shared epilogue over the workgroup's tokens t0 .. t0 + RB - 1.  src(tt, e,
+// hv, hn) gives token t0 + tt's float32 product with W_r column e (hv) and,
+// when noisy, with W_noise column e (hn).
+template <int EP, bool NOISY, class Src>
+__device__ void route_epilogue(const Src& src, double (*Ps)[EP + 1], const RouteParams& p, int t0,
+                               int RB) {
   constexpr int J = (EP + 63) / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int E = p.E, k = p.k;
@@ -53,13 +57,15 @@ __device__ void route_epilogue(const float* L, const float* Ln, double (*Ps)[EP 
       const int e = lane + 64 * j;
       float x = -INFINITY;
       if (e < E) {
-        x = L[tt * EP + e];
+        float hv, hn = 0.f;
+        src(tt, e, hv, hn);
+        x = hv;
         if (p.b_r) x += p.b_r[e];
         if (NOISY) {
           // the draw of pair (t, e): counter t * E + e + rng_offset (mod 2^64)
           const float z = (float)philox_normal(p.seed, (uint64_t)t * E + e + p.rng_offset);
           if (p.noise_out) p.noise_out[(size_t)t * E + e] = z;
-          x += z * softplus_f(Ln[tt * EP + e]);
+          x += z * softplus_f(hn);
         }
         if (p.logits) p.logits[(size_t)t * E + e] = x;
       }
@@ -239,87 +245,227 @@ __device__ void route_epilogue(const float* L, const float* Ln, double (*Ps)[EP 
         ((Ps[0][e] + Ps[1][e]) + Ps[2][e]) + Ps[3][e];
 }
 
-template <int NB, int MW, bool NOISY>
-__global__ __launch_bounds__(256) void route_bf16_kernel(RouteParams p) {
-  constexpr int EP = 16 * NB, RB = 16 * MW;
-  __shared__ float L[RB * EP];
-  __shared__ float Ln[NOISY ? RB * EP : 1];
-  __shared__ double Ps[4][EP + 1];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t0 = blockIdx.x * RB;
-  const int h = p.h;
+// ------------------------------------------------------ bf16 logits GEMM
+struct LogitsArgs {
+  const bf16* U;        // [T][h]
+  const bf16* W0;       // W_r [h][Ew]
+  const bf16* W1;       // W_noise [h][Ew] (noisy)
+  float* part;          // [NSRC][KS][T][EP]
+  int T, h, Ew, EP, KS, KT, nblocks;  // KT: 64-wide K chunks (h / 64)
+};
 
-  floatx4 acc[MW][NB];
-  floatx4 accn[NOISY ? MW : 1][NOISY ? NB : 1];
+// Stage geometry: one stage holds a 64-wide K chunk of 64 U rows (128 bytes a
+// row) and of BN columns of each weight matrix (64 k-rows of 2 BN bytes).
+// Every wave issues the same copies per stage (a 1 KB region each), so a
+// stage smaller than 4 KB is padded.
+template <int BN, int NSRC>
+struct LogitsCfg {
+  static constexpr int BM = 64;
+  static constexpr int ABYTES = BM * 128;
+  static constexpr int BBYTES = BN * 128 >= 4096 ? BN * 128 : 4096;
+  static constexpr int SBYTES = ABYTES + NSRC * BBYTES;
+  static constexpr int NS = 163840 / SBYTES < 8 ? 163840 / SBYTES : 8;  // stages in the ring
+  static constexpr int NAI = ABYTES / 4096, NBI = BBYTES / 4096;     // copies per wave
+  static constexpr int NCOPY = NAI + NSRC * NBI;
+  static_assert(NS >= 3 && (NS - 2) * NCOPY < 64, "ring");
+};
+
+// Weight rows in LDS: k-row r (BN columns, NCH = BN / 8 chunks of 16 bytes)
+// keeps logical chunk c at chunk c ^ wsw(r).  A transposing read of one
+// fragment touches, per half-wave, 8 k-rows (rows 8 g + q, g = 0/1, q = 0..3)
+// x 2 adjacent chunks; wsw spreads those 16 pieces over distinct 16-byte bank
+// groups (for NCH >= 4; two-chunk rows keep a two-way conflict).
+template <int NCH>
+__device__ __forceinline__ int wsw(int r) {
+  const int g1 = (r >> 3) & 1, q = r & 3;
+  if constexpr (NCH >= 16) return 2 * (4 * g1 + q);
+  else if constexpr (NCH == 8) return 4 * g1 + 2 * (q >> 1);
+  else if constexpr (NCH == 4) return 2 * g1;
+  else return 0;
+}
+
+template <int BN, int NSRC, int WM>
+__global__ __launch_bounds__(256) void route_logits_kernel(LogitsArgs p) {
+  using C = LogitsCfg<BN, NSRC>;
+  constexpr int BM = C::BM, NS = C::NS, NCH = BN / 8;
+  constexpr int WN = 4 / WM, TM = BM / WM, TN = NSRC * BN / WN;
+  constexpr int MB = TM / 16, NB = TN / 16;
+  static_assert(TM % 16 == 0 && TN % 16 == 0 && BN % TN == 0, "wave tile");
+  __shared__ __attribute__((aligned(16))) char lds[NS * C::SBYTES];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave / WN, wn = wave % WN;
+  const int l16 = lane & 15, g = lane >> 4, q = l16 >> 2, j = l16 & 3;
+  // workgroup -> (token block, K range, expert block), consecutive ids on one XCD
+  const int G = gridDim.x;
+  const int L = (G & 7) == 0 ? xcd_remap(blockIdx.x, G) : blockIdx.x;
+  const int nbk = L % p.nblocks, rest = L / p.nblocks;
+  const int ks = rest % p.KS, mbk = rest / p.KS;
+  const int m0 = mbk * BM, n0 = nbk * BN;
+  const int kc0 = ks * p.KT / p.KS, KTl = (ks + 1) * p.KT / p.KS - kc0;
+  const int rows = min(BM, p.T - m0);
+  const int h = p.h, Ew = p.Ew;
+
+  // loop-invariant parts of this lane's copy offsets
+  int offA[C::NAI], offB[C::NBI];
 #pragma unroll
-  for (int mb = 0; mb < MW; ++mb)
+  for (int i = 0; i < C::NAI; ++i) {
+    const int byte = (wave * C::NAI + i) * 1024 + lane * 16;
+    const int r = byte >> 7, c = ((byte >> 4) & 7) ^ ((r >> 1) & 7);
+    offA[i] = r * h * 2 + c * 16;  // rows past `rows` fall outside the resource
+  }
+#pragma unroll
+  for (int i = 0; i < C::NBI; ++i) {
+    const int byte = (wave * C::NBI + i) * 1024 + lane * 16;
+    const int r = byte / (BN * 2), c = ((byte % (BN * 2)) >> 4) ^ wsw<NCH>(r);
+    offB[i] = (r < 64 && n0 + 8 * c < Ew) ? (r * Ew + 8 * c) * 2 : kPastEnd;
+  }
+  const size_t bbytes = ((size_t)(h - kc0 * 64) * Ew - n0) * 2;
+  const size_t abytes = (size_t)rows * h * 2 - (size_t)kc0 * 128;
+
+  // loop-invariant parts of this lane's fragment reads: U rows (16-byte
+  // chunk 4 s + g of row r at chunk ^ ((r >> 1) & 7)) and transposing reads
+  // of weight k-rows 32 s + 8 g + q (+ 4)
+  int fa[2][MB], fb[2][NB];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = wm * TM + 16 * mb + l16, c = 4 * s + g;
+      fa[s][mb] = r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (NOISY) accn[NOISY ? mb : 0][NOISY ? nb : 0] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const int col = wn * TN + 16 * nb, src = col / BN, cs = col % BN;
+      const int r = 32 * s + 8 * g + q, c = (cs >> 3) + (j >> 1);
+      fb[s][nb] = C::ABYTES + src * C::BBYTES + r * (BN * 2) + ((c ^ wsw<NCH>(r)) << 4) + 8 * (j & 1);
     }
-
-  // A fragment: lane holds row (lane % 16), k = (lane / 16) * 8 .. +8.
-  // B fragment: lane holds column (lane % 16) with the same k.
-  const int lrow = lane & 15, lk = (lane >> 4) * 8;
-  const bf16* U = static_cast<const bf16*>(p.U);
-  const bf16* Wt = static_cast<const bf16*>(p.Wt);
-  const bf16* Wnt = static_cast<const bf16*>(p.Wnt);
-  const bf16* arow[MW];
-#pragma unroll
-  for (int mb = 0; mb < MW; ++mb) {
-    const int t = min(t0 + 16 * mb + lrow, p.T - 1);
-    arow[mb] = U + (size_t)t * h + lk;
   }
-  const int ksteps = h / 32;
 
-  for (int ks = wave; ks < ksteps; ks += 4) {
-    const int k0 = ks * 32;
-    bf16x8 a[MW], b[NB];
+  floatx4 acc[MB][NB];
 #pragma unroll
-    for (int mb = 0; mb < MW; ++mb) a[mb] = *reinterpret_cast<const bf16x8*>(arow[mb] + k0);
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      b[nb] = *reinterpret_cast<const bf16x8*>(Wt + (size_t)(16 * nb + lrow) * h + lk + k0);
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // The ring's slots are passed as restrict parameters (and the copies'
+  // sources built from restrict pointers), so the compiler can tell the
+  // copies into one slot from the reads of another and adds no waits of its
+  // own beyond the one at each step.
+  auto run = [&](char* __restrict__ s0, char* __restrict__ s1, char* __restrict__ s2,
+                 char* __restrict__ s3, char* __restrict__ s4, char* __restrict__ s5,
+                 char* __restrict__ s6, char* __restrict__ s7, const char* __restrict__ gU,
+                 const char* __restrict__ gW0, const char* __restrict__ gW1)
+                 __attribute__((always_inline)) {
+    char* const S[8] = {s0, s1, s2, s3, s4, s5, s6, s7};
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(gU, abytes);
+    const __amdgpu_buffer_rsrc_t rB0 = make_rsrc(gW0, bbytes);
+    const __amdgpu_buffer_rsrc_t rB1 = make_rsrc(NSRC == 2 ? gW1 : gW0, bbytes);
+    // copies of local chunk cc into slot sl (past the range: no memory
+    // traffic, the slot is never read again)
+    auto issue = [&](int cc, char* sl) __attribute__((always_inline)) {
+      const bool live = cc < KTl;
 #pragma unroll
-    for (int mb = 0; mb < MW; ++mb)
+      for (int i = 0; i < C::NAI; ++i)
+        dma16(rA, sl + (wave * C::NAI + i) * 1024, live ? offA[i] + cc * 128 : kPastEnd, 0);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+      for (int i = 0; i < C::NBI; ++i)
+        dma16(rB0, sl + C::ABYTES + (wave * C::NBI + i) * 1024,
+              live ? (int)((unsigned)offB[i] + (unsigned)(cc * 128 * Ew)) : kPastEnd, 0);
+      if constexpr (NSRC == 2) {
+#pragma unroll
+        for (int i = 0; i < C::NBI; ++i)
+          dma16(rB1, sl + C::ABYTES + C::BBYTES + (wave * C::NBI + i) * 1024,
+                live ? (int)((unsigned)offB[i] + (unsigned)(cc * 128 * Ew)) : kPastEnd, 0);
+      }
+    };
+    auto compute = [&](const char* sl) __attribute__((always_inline)) {
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4s lds_v4s;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 a[MB], b[NB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) a[mb] = *reinterpret_cast<const bf16x8*>(sl + fa[s][mb]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const char* bp = sl + fb[s][nb];
+          const v4s v[2] = {__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(bp)),
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(bp + 4 * BN * 2))};
+          __builtin_memcpy(&b[nb], v, 16);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+      }
+    };
+    // chunk c sits in slot c % NS; step c waits for it, then refills the slot
+    // of chunk c - 1 (every wave is past it) with chunk c + NS - 1
+    auto step = [&](int c, int u) __attribute__((always_inline)) {
+      wait_vm_seen<(NS - 2) * C::NCOPY>();
+      wait_lgkm0_seen();
+      barrier_only();
+      issue(c + NS - 1, S[(u + NS - 1) % NS]);
+      compute(S[u]);
+    };
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) issue(u, S[u]);
+    int c = 0;
+    for (; c + NS <= KTl; c += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) step(c + u, u);
+    }
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u)
+      if (c + u < KTl) step(c + u, u);
+    wait_vm_seen<0>();  // the last copies (past the range) land before the slots go away
+  };
+  char* const b0 = lds;
+  run(b0, b0 + C::SBYTES * (1 % NS), b0 + C::SBYTES * (2 % NS), b0 + C::SBYTES * (3 % NS),
+      b0 + C::SBYTES * (4 % NS), b0 + C::SBYTES * (5 % NS), b0 + C::SBYTES * (6 % NS),
+      b0 + C::SBYTES * (7 % NS), reinterpret_cast<const char*>(p.U + (size_t)m0 * h + kc0 * 64),
+      reinterpret_cast<const char*>(p.W0 + (size_t)kc0 * 64 * Ew + n0),
+      reinterpret_cast<const char*>((NSRC == 2 ? p.W1 : p.W0) + (size_t)kc0 * 64 * Ew + n0));
+
+  // D layout: lane holds column l16, rows 4 g + i
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int col = wn * TN + 16 * nb, src = col / BN;
+    float* out = p.part + ((size_t)(src * p.KS + ks) * p.T) * p.EP + n0 + col % BN + l16;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * TM + 16 * mb + 4 * g + i;
+        if (r < rows) out[(size_t)(m0 + r) * p.EP] = acc[mb][nb][i];
+      }
+  }
+}
+
+// One wave per token: the K ranges' products added in range order, then the
+// epilogue.
+template <int NB, bool NOISY>
+__global__ __launch_bounds__(256) void route_select_kernel(RouteParams p, int RB, int KS) {
+  constexpr int EP = 16 * NB;
+  __shared__ double Ps[4][EP + 1];
+  const int t0 = blockIdx.x * RB;
+  const size_t split = (size_t)p.T * EP;
+  const float* part = p.lpart;
+  auto src = [&](int tt, int e, float& hv, float& hn) {
+    const size_t o = (size_t)(t0 + tt) * EP + e;
+    float x = part[o];
+    for (int s = 1; s < KS; ++s) x += part[o + s * split];
+    hv = x;
     if (NOISY) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        b[nb] = *reinterpret_cast<const bf16x8*>(Wnt + (size_t)(16 * nb + lrow) * h + lk + k0);
-#pragma unroll
-      for (int mb = 0; mb < MW; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          accn[NOISY ? mb : 0][NOISY ? nb : 0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              a[mb], b[nb], accn[NOISY ? mb : 0][NOISY ? nb : 0], 0, 0, 0);
+      const float* pn = part + KS * split;
+      float y = pn[o];
+      for (int s = 1; s < KS; ++s) y += pn[o + s * split];
+      hn = y;
     }
-  }
-  // D layout: lane holds column (lane % 16), rows 4 * (lane / 16) + i.
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int mb = 0; mb < MW; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int o = (16 * mb + 4 * (lane >> 4) + i) * EP + 16 * nb + (lane & 15);
-            if (w == 0) {
-              L[o] = acc[mb][nb][i];
-              if (NOISY) Ln[o] = accn[NOISY ? mb : 0][NOISY ? nb : 0][i];
-            } else {
-              L[o] += acc[mb][nb][i];
-              if (NOISY) Ln[o] += accn[NOISY ? mb : 0][NOISY ? nb : 0][i];
-            }
-          }
-    }
-    __syncthreads();
-  }
-  route_epilogue<EP, RB, NOISY>(L, Ln, Ps, p, t0);
+  };
+  route_epilogue<EP, NOISY>(src, Ps, p, t0, RB);
 }
 
 // float32 path: plain sequential dot products (small workloads only).
@@ -331,8 +477,8 @@ __global__ __launch_bounds__(256) void route_f32_kernel(RouteParams p) {
   __shared__ double Ps[4][EP + 1];
   const int t0 = blockIdx.x * RB;
   const float* U = static_cast<const float*>(p.U);
-  const float* W = static_cast<const float*>(p.Wt);
-  const float* Wn = static_cast<const float*>(p.Wnt);
+  const float* W = static_cast<const float*>(p.W);
+  const float* Wn = static_cast<const float*>(p.Wn);
   for (int i = threadIdx.x; i < RB * EP; i += blockDim.x) {
     const int tt = i / EP, e = i % EP, t = t0 + tt;
     float acc = 0.f, accn = 0.f;
@@ -347,21 +493,19 @@ __global__ __launch_bounds__(256) void route_f32_kernel(RouteParams p) {
     if (NOISY) Ln[i] = accn;
   }
   __syncthreads();
-  route_epilogue<EP, RB, NOISY>(L, Ln, Ps, p, t0);
+  auto src = [&](int tt, int e, float& hv, float& hn) {
+    hv = L[tt * EP + e];
+    if (NOISY) hn = Ln[tt * EP + e];
+  };
+  route_epilogue<EP, NOISY>(src, Ps, p, t0, RB);
 }
 
-__global__ void transpose_kernel(const bf16* W, bf16* WT, int h, int E, int EP) {
-  __shared__ bf16 tile[32][33];
-  const int k0 = blockIdx.x * 32, n0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int i = ty; i < 32; i += 8) {
-    const int kk = k0 + i, n = n0 + tx;
-    tile[i][tx] = (kk < h && n < E) ? W[(size_t)kk * E + n] : bf16(0);
-  }
-  __syncthreads();
-  for (int i = ty; i < 32; i += 8) {
-    const int n = n0 + i, kk = k0 + tx;
-    if (n < EP && kk < h) WT[(size_t)n * h + kk] = tile[tx][i];
+__global__ void pad_rows_kernel(const bf16* W, bf16* Wp, int h, int E, int Ew) {
+  const size_t n = (size_t)h * Ew;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const size_t k = i / Ew;
+    const int e = (int)(i - k * Ew);
+    Wp[i] = e < E ? W[k * E + e] : bf16(0);
   }
 }
 
@@ -390,38 +534,51 @@ __global__ __launch_bounds__(256) void prob_reduce_kernel(const double* part, in
 
 }  // namespace
 
-RouteShape route_shape(int T, int E, int bf16, int noisy) {
-  RouteShape rs;
+RouteShape route_shape(int T, int E, int h, int bf16, int noisy) {
+  RouteShape rs{};
   int NB = 1;
   while (16 * NB < E) NB *= 2;
   rs.NB = NB;
   rs.EP = 16 * NB;
   if (bf16) {
-    int MW = 32 / (NB * (noisy ? 2 : 1));
-    MW = MW > 4 ? 4 : (MW < 1 ? 1 : MW);
-    while (MW > 1 && (T + 16 * MW - 1) / (16 * MW) < 256) MW /= 2;
-    rs.MW = MW;
+    rs.Ew = (E + 7) & ~7;
+    rs.BN = rs.EP < 128 ? rs.EP : 128;
+    // waves along tokens: a wave's columns stay inside one weight matrix
+    rs.WM = rs.BN == 16 ? (noisy ? 2 : 4) : (rs.BN == 128 || noisy) ? 1 : 2;
+    rs.mblocks = (T + 63) / 64;
+    rs.nblocks = rs.EP / rs.BN;
+    // split K until the grid covers the chip, keeping at least 4 chunks a range
+    const int KT = h / 64;
+    rs.KS = 1;
+    while (rs.mblocks * rs.nblocks * rs.KS < 256 && KT / (2 * rs.KS) >= 4) rs.KS *= 2;
+    // one token per wave, more per workgroup on long inputs (fewer partials)
+    rs.RB = 4;
+    while (rs.RB < 32 && (T + rs.RB - 1) / rs.RB > 1024) rs.RB *= 2;
   } else {
-    rs.MW = 1;
+    rs.RB = 16;
   }
-  rs.RB = 16 * rs.MW;
   rs.nblk = (T + rs.RB - 1) / rs.RB;
   return rs;
 }
 
-hipError_t launch_transpose_router_w(const void* W, void* WT, int h, int E, int EP,
-                                     hipStream_t s) {
-  dim3 grid((h + 31) / 32, (EP + 31) / 32);
-  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, static_cast<const bf16*>(W),
-                     static_cast<bf16*>(WT), h, E, EP);
+hipError_t launch_pad_router_w(const void* W, void* Wp, int h, int E, int Ew, hipStream_t s) {
+  const size_t n = (size_t)h * Ew;
+  const size_t nb = (n + 255) / 256;
+  hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)(nb < 2048 ? nb : 2048)), dim3(256), 0, s,
+                     static_cast<const bf16*>(W), static_cast<bf16*>(Wp), h, E, Ew);
   return hipGetLastError();
 }
 
-#define MOE_ROUTE_BF16(NB_, MW_, NZ_)                                                     \
-  if (rs.NB == NB_ && rs.MW == MW_ && (noisy != 0) == NZ_) {                              \
-    hipLaunchKernelGGL((route_bf16_kernel<NB_, MW_, NZ_>), dim3(rs.nblk), dim3(256), 0, s, \
-                       p);                                                                \
-    return hipGetLastError();                                                             \
+#define MOE_ROUTE_LOGITS(BN_, NS_, WM_)                                                    \
+  if (rs.BN == BN_ && nsrc == NS_ && rs.WM == WM_) {                                        \
+    hipLaunchKernelGGL((route_logits_kernel<BN_, NS_, WM_>), dim3(grid), dim3(256), 0, s, a); \
+    launched = true;                                                                         \
+  }
+#define MOE_ROUTE_SELECT(NB_, NZ_)                                                               \
+  if (rs.NB == NB_ && (noisy != 0) == NZ_) {                                                     \
+    hipLaunchKernelGGL((route_select_kernel<NB_, NZ_>), dim3(rs.nblk), dim3(256), 0, s, p, rs.RB, \
+                       rs.KS);                                                                   \
+    return hipGetLastError();                                                                    \
   }
 #define MOE_ROUTE_F32(NB_, NZ_)                                                            \
   if (rs.NB == NB_ && (noisy != 0) == NZ_) {                                               \
@@ -429,20 +586,35 @@ hipError_t launch_transpose_router_w(const void* W, void* WT, int h, int E, int 
     return hipGetLastError();                                                              \
   }
 
-hipError_t launch_route(const RouteShape& rs, const RouteParams& p, int bf16, int noisy,
+hipError_t launch_route(const RouteShape& rs, const RouteParams& p, int use_bf16, int noisy,
                         hipStream_t s) {
   if (rs.nblk == 0) return hipSuccess;
-  if (bf16) {
-    MOE_ROUTE_BF16(1, 1, false) MOE_ROUTE_BF16(1, 2, false) MOE_ROUTE_BF16(1, 4, false)
-    MOE_ROUTE_BF16(2, 1, false) MOE_ROUTE_BF16(2, 2, false) MOE_ROUTE_BF16(2, 4, false)
-    MOE_ROUTE_BF16(4, 1, false) MOE_ROUTE_BF16(4, 2, false) MOE_ROUTE_BF16(4, 4, false)
-    MOE_ROUTE_BF16(8, 1, false) MOE_ROUTE_BF16(8, 2, false) MOE_ROUTE_BF16(8, 4, false)
-    MOE_ROUTE_BF16(16, 1, false) MOE_ROUTE_BF16(16, 2, false)
-    MOE_ROUTE_BF16(1, 1, true) MOE_ROUTE_BF16(1, 2, true) MOE_ROUTE_BF16(1, 4, true)
-    MOE_ROUTE_BF16(2, 1, true) MOE_ROUTE_BF16(2, 2, true) MOE_ROUTE_BF16(2, 4, true)
-    MOE_ROUTE_BF16(4, 1, true) MOE_ROUTE_BF16(4, 2, true) MOE_ROUTE_BF16(4, 4, true)
-    MOE_ROUTE_BF16(8, 1, true) MOE_ROUTE_BF16(8, 2, true)
-    MOE_ROUTE_BF16(16, 1, true)
+  if (use_bf16) {
+    LogitsArgs a;
+    a.U = static_cast<const bf16*>(p.U);
+    a.W0 = static_cast<const bf16*>(p.W);
+    a.W1 = static_cast<const bf16*>(noisy ? p.Wn : p.W);
+    a.part = p.lpart;
+    a.T = p.T;
+    a.h = p.h;
+    a.Ew = rs.Ew;
+    a.EP = rs.EP;
+    a.KS = rs.KS;
+    a.KT = p.h / 64;
+    a.nblocks = rs.nblocks;
+    const int nsrc = noisy ? 2 : 1;
+    const unsigned grid = (unsigned)(rs.mblocks * rs.nblocks * rs.KS);
+    bool launched = false;
+    MOE_ROUTE_LOGITS(16, 1, 4) MOE_ROUTE_LOGITS(16, 2, 2) MOE_ROUTE_LOGITS(32, 1, 2)
+    MOE_ROUTE_LOGITS(32, 2, 1) MOE_ROUTE_LOGITS(64, 1, 2) MOE_ROUTE_LOGITS(64, 2, 1)
+    MOE_ROUTE_LOGITS(128, 1, 1) MOE_ROUTE_LOGITS(128, 2, 1)
+    if (!launched) return hipErrorInvalidValue;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    MOE_ROUTE_SELECT(1, false) MOE_ROUTE_SELECT(2, false) MOE_ROUTE_SELECT(4, false)
+    MOE_ROUTE_SELECT(8, false) MOE_ROUTE_SELECT(16, false)
+    MOE_ROUTE_SELECT(1, true) MOE_ROUTE_SELECT(2, true) MOE_ROUTE_SELECT(4, true)
+    MOE_ROUTE_SELECT(8, true) MOE_ROUTE_SELECT(16, true)
   } else {
     MOE_ROUTE_F32(1, false) MOE_ROUTE_F32(2, false) MOE_ROUTE_F32(4, false)
     MOE_ROUTE_F32(8, false) MOE_ROUTE_F32(16, false)

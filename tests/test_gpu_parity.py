@@ -220,6 +220,61 @@ def test_all_logits_equal_and_one_hot_load():
                                rtol=1e-6)
 
 
+# Router shapes covering each tile of the bf16 logits GEMM (16, 32, 64 and 128
+# experts per tile, with and without the noise matrix), K cut into several
+# ranges (h = 4096 over 5 token blocks) and loops shorter than the copy ring,
+# ragged token blocks, expert counts that are not a multiple of 8 and a weight
+# matrix 2 bytes off 16-byte alignment (both read through a padded copy).
+ROUTER = {
+    "E8_h4096_ksplit": L.SMALL["mixtral_small"].replace(T=257, h=4096, E=8, k=2),
+    "E8_noisy": L.SMALL["noisy_small"].replace(T=130, h=320, E=8, k=2),
+    "E24_noisy": L.SMALL["noisy_small"].replace(T=200, h=256, E=24, k=2),
+    "E30_padded": L.SMALL["switch_small"].replace(T=65, h=192, E=30, k=3),
+    "E64": L.SMALL["deepseek_small"].replace(T=333, h=448, E=64, k=6, score="softmax"),
+    "E100_noisy_padded": L.SMALL["noisy_small"].replace(T=100, h=128, E=100, k=4),
+    "E128_long": L.SMALL["switch_small"].replace(T=4096, h=2048, E=128, k=1),
+    "E256_sigmoid": L.SMALL["deepseek_small"].replace(T=70, h=1024, E=256, k=8),
+    "E16_misaligned": L.SMALL["mixtral_small"].replace(T=90, h=192, E=16, k=2),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTER))
+def test_router_shapes(name):
+    w = ROUTER[name]
+    L.log(f"[router] {name} {w}")
+    x = I.make_inputs(w, seed=3, device=DEV, with_experts=False)
+    if name.endswith("misaligned"):
+        for key in ("W_r", "W_noise"):
+            if x[key] is not None:
+                buf = torch.empty(x[key].numel() + 1, dtype=x[key].dtype, device=DEV)
+                buf[1:].copy_(x[key].reshape(-1))
+                x[key] = buf[1:].view(x[key].shape)
+                assert x[key].data_ptr() % 16 != 0
+    cfg = B.make_config(w)
+    T, E, k = w.T, w.E, w.k
+    f32 = dict(dtype=torch.float32, device=DEV)
+    g = {"topk_idx": torch.empty((T, k), dtype=torch.int32, device=DEV),
+         "topk_gate": torch.empty((T, k), **f32), "logits": torch.empty((T, E), **f32),
+         "prob_sum": torch.empty((E,), **f32)}
+    if w.noisy:
+        g["noise"] = torch.empty((T, E), **f32)
+    B.moe_route(cfg, x["U"], x["W_r"], x["b_r"], x["W_noise"], g["topk_idx"], g["topk_gate"],
+                logits=g["logits"], prob_sum=g["prob_sum"], noise_out=g.get("noise"))
+    torch.cuda.synchronize()
+    info = L.check_logits_end_to_end(w, g, cpu_copy(x))
+    # selection, gates and the P sums from the GPU's own logits, as the oracle
+    # takes them
+    H = L.to_np(g["logits"]).astype(np.float64)
+    idx = L.to_np(g["topk_idx"]).astype(np.int64)
+    np.testing.assert_array_equal(idx, O.select_topk(H, k), err_msg="topk_idx")
+    r = L.route_given_selection(w, H, idx)
+    np.testing.assert_allclose(L.to_np(g["topk_gate"]), r["gate"], rtol=1e-6, atol=1e-7,
+                               err_msg="topk_gate")
+    np.testing.assert_allclose(L.to_np(g["prob_sum"]), r["prob_sum"], rtol=1e-5, atol=1e-6,
+                               err_msg="prob_sum")
+    L.log(f"  logit_err={info['logit_err']:.2e} near_ties={info['near_ties']}")
+
+
 @pytest.mark.parametrize("T,E,scale", [(1, 8, 1.0), (300, 64, 4.0), (2049, 256, 30.0), (0, 8, 1.0)])
 def test_router_z_loss_entry(T, E, scale):
     """moe_router_z_loss on given logits (wide and large ones included) against
