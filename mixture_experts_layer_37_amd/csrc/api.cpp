@@ -395,11 +395,14 @@ int32_t run_route(const Dims& d, const moe_config* c, const RouteWs& w, const vo
 }
 
 // xs != NULL: FP8 dispatch (X receives E4M3 codes, xs the row scales).
+// fused: steps the scan workgroup also runs (the layer forward's tile maps
+// and statistics), or NULL.
 int32_t run_dispatch(const Dims& d, const moe_config* c, const DispatchWs& w, const void* U,
                      const int32_t* idx, void* X, int32_t* row_token, int32_t* slot,
                      int32_t* count, int32_t* kept, int32_t* offset, void* ws, hipStream_t s,
-                     float* xs = nullptr) {
+                     float* xs = nullptr, const DispatchParams* fused = nullptr) {
   DispatchParams p;
+  if (fused) p = *fused;
   p.T = (int)d.T;
   p.E = (int)d.E;
   p.k = (int)d.k;
@@ -771,10 +774,26 @@ int32_t layer_impl(const moe_config* cfg, const void* U, const void* W_r, const 
   st = run_route(d, cfg, w.route, U, W_r, b_r, b_sel, W_noise, o.noise, idx, gate, o.logits,
                  ws, s);
   if (st != MOE_OK) return st;
+  MOE_TRY(launch_prob_reduce(at<double>(ws, w.route.part), w.route.rs.nblk, w.route.rs.EP,
+                             (int)d.E, at<double>(ws, w.route.total), o.prob_sum, s));
   MOE_TRY(mark(1));
-  st = run_dispatch(d, cfg, w.disp, U, idx, X, row_token, slot, count, kept, offset, ws, s, xs);
-  if (st != MOE_OK) return st;
-  st = run_tile_map(d, w.ffn, offset, ws, s);
+  // the dispatch's scan workgroup also writes the GEMMs' tile maps and the
+  // load statistics
+  DispatchParams fused;
+  if (d.bf16) {
+    fused.bm1 = w.ffn.fs.bm1;
+    fused.bm2 = w.ffn.fs.bm2;
+    fused.map1 = at<int32_t>(ws, w.ffn.map1);
+    fused.map2 = at<int32_t>(ws, w.ffn.map2);
+  }
+  fused.stats_on = 1;
+  fused.stats = StatsParams{(int)d.T, (int)d.E, (int)d.k, count, kept,
+                            at<double>(ws, w.route.total), nullptr, o.f, o.P,
+                            o.aux_loss ? o.aux_loss : at<float>(ws, w.scal),
+                            o.maxvio ? o.maxvio : at<float>(ws, w.scal) + 1,
+                            o.n_dropped ? o.n_dropped : at<int32_t>(ws, w.scal) + 2, o.z_loss};
+  st = run_dispatch(d, cfg, w.disp, U, idx, X, row_token, slot, count, kept, offset, ws, s, xs,
+                    &fused);
   if (st != MOE_OK) return st;
   MOE_TRY(mark(2));
   st = run_gate_up(d, w.ffn, X, offset, W_gate, W_up, W_down, Y, ws, s, f8, o.A, o.GU);
@@ -790,14 +809,6 @@ int32_t layer_impl(const moe_config* cfg, const void* U, const void* W_r, const 
   MOE_TRY(launch_combine(U, Y, slot, gate, Ys, (int)d.ns, out, (int)d.T, (int)d.h, (int)d.k,
                          d.bf16, s));
   MOE_TRY(mark(5));
-  MOE_TRY(launch_prob_reduce(at<double>(ws, w.route.part), w.route.rs.nblk, w.route.rs.EP,
-                             (int)d.E, at<double>(ws, w.route.total), o.prob_sum, s));
-  StatsParams sp{(int)d.T, (int)d.E, (int)d.k, count, kept, at<double>(ws, w.route.total),
-                 nullptr, o.f, o.P,
-                 o.aux_loss ? o.aux_loss : at<float>(ws, w.scal),
-                 o.maxvio ? o.maxvio : at<float>(ws, w.scal) + 1,
-                 o.n_dropped ? o.n_dropped : at<int32_t>(ws, w.scal) + 2, o.z_loss};
-  MOE_TRY(launch_stats(sp, s));
   MOE_TRY(mark(6));
   return MOE_OK;
 }

@@ -12,6 +12,7 @@
 // deterministic and each output byte is written exactly once.
 #include <limits.h>
 
+#include "blocks.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -58,42 +59,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const TE* U, const TE* Y,
 }
 
 __global__ __launch_bounds__(256) void stats_kernel(StatsParams p) {
-  __shared__ double s_fp[256];
-  __shared__ int s_max[256];
-  __shared__ int s_drop[256];
   const int e = threadIdx.x;
-  double fp = 0.0;
-  int cnt = INT_MIN, drop = 0;
-  if (e < p.E) {
-    cnt = p.count[e];
-    drop = cnt - p.kept[e];
-    const double ps = p.prob_total ? p.prob_total[e] : (double)p.prob_sum[e];
-    const double f = p.T > 0 ? (double)cnt / ((double)p.T * p.k) : 0.0;
-    const double P = p.T > 0 ? ps / p.T : 0.0;
-    if (p.f) p.f[e] = (float)f;
-    if (p.P) p.P[e] = (float)P;
-    fp = f * P;
-  }
-  s_fp[e] = fp;
-  s_max[e] = cnt;
-  s_drop[e] = drop;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (e < w) {
-      s_fp[e] += s_fp[e + w];
-      s_max[e] = max(s_max[e], s_max[e + w]);
-      s_drop[e] += s_drop[e + w];
-    }
-    __syncthreads();
-  }
-  if (e == 0) {
-    const double mean = (double)p.T * p.k / p.E;
-    if (p.aux) p.aux[0] = (float)(p.E * s_fp[0]);
-    if (p.maxvio) p.maxvio[0] = p.T > 0 ? (float)((s_max[0] - mean) / mean) : 0.f;
-    if (p.n_dropped) p.n_dropped[0] = s_drop[0];
-    if (p.z_loss && p.prob_total)
-      p.z_loss[0] = p.T > 0 ? (float)(p.prob_total[p.E] / p.T) : 0.f;
-  }
+  stats_block(p, e, e < p.E ? p.count[e] : 0, e < p.E ? p.kept[e] : 0);
 }
 
 // Loss-free balancing bias step (page "MoE 与专家并行", section

@@ -143,15 +143,44 @@ __device__ __forceinline__ double philox_normal(uint64_t seed, uint64_t n) {
   return sqrt(-2.0 * log(u1)) * cos(2.0 * M_PI * u2);
 }
 
+// Wave-wide butterflies without LDS traffic.  Step S pairs every lane with
+// one lane of the other half of its group of 2^(S+1) lanes: quad
+// permutations (S = 0, 1), mirrors within 8 and within 16 lanes (DPP,
+// S = 2, 3), then the row swap and the half swap of gfx950 (S = 4, 5).  A
+// commutative, associative combine applied after each of the six steps
+// leaves the whole wave's result, bit-identical, in every lane.
+template <int S>
+__device__ __forceinline__ int wave_partner(int v) {
+  if constexpr (S == 0) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (S == 1) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (S == 2) return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+  else if constexpr (S == 3) return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+  else if constexpr (S == 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)((threadIdx.x & 16) ? r[0] : r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)((threadIdx.x & 32) ? r[0] : r[1]);
+  }
+}
+template <int S>
+__device__ __forceinline__ float wave_partner(float v) {
+  return __int_as_float(wave_partner<S>(__float_as_int(v)));
+}
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, wave_partner<0>(v));
+  v = op(v, wave_partner<1>(v));
+  v = op(v, wave_partner<2>(v));
+  v = op(v, wave_partner<3>(v));
+  v = op(v, wave_partner<4>(v));
+  return op(v, wave_partner<5>(v));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 
 // Lanes whose value `theirs` equals `mine`, among lanes with `valid` set.

@@ -20,6 +20,7 @@
 //     it); position < C keeps it at row offset[e] + position.
 #include <mutex>
 
+#include "blocks.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -100,6 +101,12 @@ __global__ __launch_bounds__(256) void scan_kernel(DispatchParams p, int nchunk)
     p.offset[e] = off;
   }
   if (e == 0) p.offset[p.E] = total;
+  // the layer forward's follow-up steps, on the values in hand
+  if (p.map1) {
+    __shared__ int tmp2[8];
+    tile_maps_block(e, p.E, e < p.E ? kp : 0, off, p.bm1, p.bm2, p.map1, p.map2, tmp2);
+  }
+  if (p.stats_on) stats_block(p.stats, e, run, kp);
 }
 
 __global__ __launch_bounds__(256) void assign_kernel(DispatchParams p) {

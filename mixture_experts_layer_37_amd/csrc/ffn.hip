@@ -51,6 +51,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "blocks.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -1618,33 +1619,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* A, const int
   }
 }
 
-// Tile maps of both GEMMs' row tiles.  Map layout: [E+1] first m-tile of
-// every expert (exclusive scan of ceil(rows_e / bm) over the experts, E <= 256,
-// one thread each), padded to an even count, then one int2 per m-tile:
-// {first row, expert | valid rows << 16}.
+// Tile maps of both GEMMs' row tiles (see tile_maps_block) from the offsets.
 __global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* offset, int E, int bm1,
                                                        int bm2, int32_t* m1, int32_t* m2) {
-  __shared__ int tmp[2][4];
+  __shared__ int tmp[8];
   const int e = threadIdx.x;
   const int n = e < E ? offset[e + 1] - offset[e] : 0;
-  int t1, t2;
-  const int a = block_excl_scan256((n + bm1 - 1) / bm1, tmp[0], &t1);
-  const int b = block_excl_scan256((n + bm2 - 1) / bm2, tmp[1], &t2);
-  if (e < E) {
-    m1[e] = a;
-    m2[e] = b;
-    const int o = offset[e];
-    int2* tab1 = reinterpret_cast<int2*>(m1 + ((E + 2) & ~1));
-    int2* tab2 = reinterpret_cast<int2*>(m2 + ((E + 2) & ~1));
-    for (int q = 0; q * bm1 < n; ++q)
-      tab1[a + q] = make_int2(o + q * bm1, e | (min(bm1, n - q * bm1) << 16));
-    for (int q = 0; q * bm2 < n; ++q)
-      tab2[b + q] = make_int2(o + q * bm2, e | (min(bm2, n - q * bm2) << 16));
-  }
-  if (e == 0) {
-    m1[E] = t1;
-    m2[E] = t2;
-  }
+  tile_maps_block(e, E, n, e < E ? offset[e] : 0, bm1, bm2, m1, m2, tmp);
 }
 
 // Offsets of a dense pass over all T rows as one "expert" (the shared

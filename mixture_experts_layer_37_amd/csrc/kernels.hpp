@@ -28,8 +28,8 @@ struct RouteParams {
   int32_t* topk_idx;
   float* topk_gate;
   float* logits;     // optional [T][E]
-  double* prob_part; // [nblk][EP + 1] per-block sums of the score entering P;
-                     // column EP: sum over the block's tokens of LSE(H_t)^2
+  double* prob_part; // [EP + 1][nblk] per-block sums of the score entering P;
+                     // row EP: sum over the block's tokens of LSE(H_t)^2
 };
 
 struct RouteShape {
@@ -37,9 +37,9 @@ struct RouteShape {
   int NB;
   int RB;    // tokens per selection workgroup (float32: per fused workgroup)
   int nblk;  // selection (float32: fused) workgroups
-  // bf16 logits GEMM: 64-token x BN-expert tiles over KS ranges of K
+  // bf16 logits GEMM: BM-token x BN-expert tiles over KS ranges of K
   int Ew;    // row pitch of the weights it reads: E rounded up to 8
-  int BN, WM, KS, mblocks, nblocks;
+  int BM, BN, WM, KS, mblocks, nblocks;
 };
 
 RouteShape route_shape(int T, int E, int h, int bf16, int noisy);
@@ -63,6 +63,19 @@ hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int
 // ---------------------------------------------------------------- dispatch
 constexpr int kChunk = 256;  // tokens per dispatch workgroup
 
+struct StatsParams {
+  int T, E, k;
+  const int32_t* count;
+  const int32_t* kept;
+  const double* prob_total;  // [E + 1] (layer; entry E: sum of LSE^2) or NULL
+  const float* prob_sum;     // [E] (standalone) or NULL
+  float* f;
+  float* P;
+  float* aux;
+  float* maxvio;
+  int32_t* n_dropped;
+  float* z_loss;             // mean over tokens of LSE^2 (needs prob_total), or NULL
+};
 struct DispatchParams {
   int T, E, k, C;
   int token_major;
@@ -74,6 +87,14 @@ struct DispatchParams {
   int32_t* offset; // [E+1]
   int32_t* slot;   // [T][k]
   int32_t* row_token;
+  // Optional steps of the scan workgroup (the layer forward): the grouped
+  // GEMMs' tile maps (map1 != NULL, tiles of bm1 and bm2 rows) and the load
+  // statistics (stats_on, from count, kept and stats.prob_total).
+  int bm1 = 0, bm2 = 0;
+  int32_t* map1 = nullptr;
+  int32_t* map2 = nullptr;
+  int stats_on = 0;
+  StatsParams stats{};
 };
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s);
 // Bytes of the fixed device array behind moe_dispatch_noalloc, and its
@@ -146,19 +167,6 @@ hipError_t launch_combine(const void* U, const void* Y, const int32_t* slot, con
 // b[e] += gamma * sign(mean count - count[e])
 hipError_t launch_update_bias(const int32_t* count, float* b, float gamma, int E, hipStream_t s);
 
-struct StatsParams {
-  int T, E, k;
-  const int32_t* count;
-  const int32_t* kept;
-  const double* prob_total;  // [E + 1] (layer; entry E: sum of LSE^2) or NULL
-  const float* prob_sum;     // [E] (standalone) or NULL
-  float* f;
-  float* P;
-  float* aux;
-  float* maxvio;
-  int32_t* n_dropped;
-  float* z_loss;             // mean over tokens of LSE^2 (needs prob_total), or NULL
-};
 hipError_t launch_stats(const StatsParams& p, hipStream_t s);
 // z_loss[0] = mean over the T tokens of LSE(logits[t, :E])^2 (E <= 256).
 hipError_t launch_z_loss(const float* logits, int T, int E, float* z_loss, hipStream_t s);

@@ -34,9 +34,9 @@ __device__ __forceinline__ float softplus_f(float x) {
   return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
 }
 
-// Shared epilogue over the workgroup's tokens t0 .. t0 + RB - 1.  src(tt, e,
-// hv, hn) gives token t0 + tt's float32 product with W_r column e (hv) and,
-// when noisy, with W_noise column e (hn).
+// Shared epilogue over the workgroup's tokens t0 .. t0 + RB - 1.  src(tt, j,
+// e, hv, hn) gives token t0 + tt's float32 product with W_r column
+// e = lane + 64 j (hv) and, when noisy, with W_noise column e (hn).
 template <int EP, bool NOISY, class Src>
 __device__ void route_epilogue(const Src& src, double (*Ps)[EP + 1], const RouteParams& p, int t0,
                                int RB) {
@@ -47,29 +47,43 @@ __device__ void route_epilogue(const Src& src, double (*Ps)[EP + 1], const Route
 #pragma unroll
   for (int j = 0; j < J; ++j) pacc[j] = 0.0;
   double zacc = 0.0;  // sum over this wave's tokens of LSE(H_t)^2 (wave-uniform)
+  // the biases of this lane's experts, loaded once for all tokens
+  float br[J], bs[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = lane + 64 * j;
+    br[j] = (p.b_r && e < E) ? p.b_r[e] : 0.f;
+    bs[j] = (p.b_sel && e < E) ? p.b_sel[e] : 0.f;
+  }
 
   for (int tt = wave; tt < RB; tt += 4) {
     const int t = t0 + tt;
     if (t >= p.T) break;
-    float v[J];
+    float v[J], zn[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int e = lane + 64 * j;
       float x = -INFINITY;
+      zn[j] = 0.f;
       if (e < E) {
         float hv, hn = 0.f;
-        src(tt, e, hv, hn);
+        src(tt, j, e, hv, hn);
         x = hv;
-        if (p.b_r) x += p.b_r[e];
+        if (p.b_r) x += br[j];
         if (NOISY) {
           // the draw of pair (t, e): counter t * E + e + rng_offset (mod 2^64)
-          const float z = (float)philox_normal(p.seed, (uint64_t)t * E + e + p.rng_offset);
-          if (p.noise_out) p.noise_out[(size_t)t * E + e] = z;
-          x += z * softplus_f(hn);
+          zn[j] = (float)philox_normal(p.seed, (uint64_t)t * E + e + p.rng_offset);
+          x += zn[j] * softplus_f(hn);
         }
-        if (p.logits) p.logits[(size_t)t * E + e] = x;
       }
       v[j] = x;
+    }
+    // the optional outputs are stored together, after the last read
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E && p.logits) p.logits[(size_t)t * E + e] = v[j];
+      if (NOISY && e < E && p.noise_out) p.noise_out[(size_t)t * E + e] = zn[j];
     }
     // scores
     float s[J];
@@ -124,7 +138,7 @@ __device__ void route_epilogue(const Src& src, double (*Ps)[EP + 1], const Route
     for (int j = 0; j < J; ++j) {
       const int e = lane + 64 * j;
       key[j] = v[j];
-      if (keyed) key[j] = e < E ? s[j] + (p.b_sel ? p.b_sel[e] : 0.f) : -INFINITY;
+      if (keyed) key[j] = e < E ? s[j] + bs[j] : -INFINITY;
     }
     // arg-max over the keys of the experts with allow[j] set: larger key
     // first, lower expert index on ties (wave-uniform result)
@@ -139,15 +153,18 @@ __device__ void route_epilogue(const Src& src, double (*Ps)[EP + 1], const Route
           be = e;
         }
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oe = __shfl_xor(be, o, 64);
+      auto take = [&](float ov, int oe) {
         if (ov > bv || (ov == bv && oe < be)) {
           bv = ov;
           be = oe;
         }
-      }
+      };
+      take(wave_partner<0>(bv), wave_partner<0>(be));
+      take(wave_partner<1>(bv), wave_partner<1>(be));
+      take(wave_partner<2>(bv), wave_partner<2>(be));
+      take(wave_partner<3>(bv), wave_partner<3>(be));
+      take(wave_partner<4>(bv), wave_partner<4>(be));
+      take(wave_partner<5>(bv), wave_partner<5>(be));
     };
     if (p.n_groups > 1) {
       const int gsize = E / p.n_groups, q = k / p.topk_groups;
@@ -218,7 +235,9 @@ __device__ void route_epilogue(const Src& src, double (*Ps)[EP + 1], const Route
 #pragma unroll
       for (int j = 0; j < J; ++j)
         if (j == (be >> 6)) mine = s[j];
-      const float sv = keyed ? __shfl(mine, be & 63, 64)
+      // be is the same in every lane: read the chosen lane's score directly
+      const int src_lane = __builtin_amdgcn_readfirstlane(be) & 63;
+      const float sv = keyed ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), src_lane))
                              : ((p.score == 0) ? expf(bv - m) / Z : 1.f / (1.f + expf(-bv)));
       gsum += sv;
       if (lane == r) {
@@ -241,7 +260,7 @@ __device__ void route_epilogue(const Src& src, double (*Ps)[EP + 1], const Route
   if (lane == 0) Ps[wave][EP] = zacc;
   __syncthreads();
   for (int e = threadIdx.x; e <= EP; e += blockDim.x)
-    p.prob_part[(size_t)blockIdx.x * (EP + 1) + e] =
+    p.prob_part[(size_t)e * gridDim.x + blockIdx.x] =
         ((Ps[0][e] + Ps[1][e]) + Ps[2][e]) + Ps[3][e];
 }
 
@@ -254,13 +273,13 @@ struct LogitsArgs {
   int T, h, Ew, EP, KS, KT, nblocks;  // KT: 64-wide K chunks (h / 64)
 };
 
-// Stage geometry: one stage holds a 64-wide K chunk of 64 U rows (128 bytes a
-// row) and of BN columns of each weight matrix (64 k-rows of 2 BN bytes).
+// Stage geometry: one stage holds a 64-wide K chunk of BM U rows (128 bytes
+// a row) and of BN columns of each weight matrix (64 k-rows of 2 BN bytes).
 // Every wave issues the same copies per stage (a 1 KB region each), so a
 // stage smaller than 4 KB is padded.
-template <int BN, int NSRC>
+template <int BM_, int BN, int NSRC>
 struct LogitsCfg {
-  static constexpr int BM = 64;
+  static constexpr int BM = BM_;
   static constexpr int ABYTES = BM * 128;
   static constexpr int BBYTES = BN * 128 >= 4096 ? BN * 128 : 4096;
   static constexpr int SBYTES = ABYTES + NSRC * BBYTES;
@@ -284,9 +303,9 @@ __device__ __forceinline__ int wsw(int r) {
   else return 0;
 }
 
-template <int BN, int NSRC, int WM>
+template <int BM_, int BN, int NSRC, int WM>
 __global__ __launch_bounds__(256) void route_logits_kernel(LogitsArgs p) {
-  using C = LogitsCfg<BN, NSRC>;
+  using C = LogitsCfg<BM_, BN, NSRC>;
   constexpr int BM = C::BM, NS = C::NS, NCH = BN / 8;
   constexpr int WN = 4 / WM, TM = BM / WM, TN = NSRC * BN / WN;
   constexpr int MB = TM / 16, NB = TN / 16;
@@ -444,31 +463,46 @@ __global__ __launch_bounds__(256) void route_logits_kernel(LogitsArgs p) {
   }
 }
 
-// One wave per token: the K ranges' products added in range order, then the
-// epilogue.
+// One wave per token (4 tokens a workgroup): all of the token's K-range
+// products are loaded first (columns up to EP exist, so no lane branches),
+// then added in range order, then the epilogue.
+constexpr int kMaxKRanges = 8;
 template <int NB, bool NOISY>
-__global__ __launch_bounds__(256) void route_select_kernel(RouteParams p, int RB, int KS) {
-  constexpr int EP = 16 * NB;
+__global__ __launch_bounds__(256) void route_select_kernel(RouteParams p, int KS) {
+  constexpr int EP = 16 * NB, J = (EP + 63) / 64, NM = NOISY ? 2 : 1;
   __shared__ double Ps[4][EP + 1];
-  const int t0 = blockIdx.x * RB;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = blockIdx.x * 4, t = t0 + wave;
   const size_t split = (size_t)p.T * EP;
-  const float* part = p.lpart;
-  auto src = [&](int tt, int e, float& hv, float& hn) {
-    const size_t o = (size_t)(t0 + tt) * EP + e;
-    float x = part[o];
-    for (int s = 1; s < KS; ++s) x += part[o + s * split];
-    hv = x;
-    if (NOISY) {
-      const float* pn = part + KS * split;
-      float y = pn[o];
-      for (int s = 1; s < KS; ++s) y += pn[o + s * split];
-      hn = y;
-    }
+  float hv[NM][J];
+  if (t < p.T) {
+    const float* base = p.lpart + (size_t)t * EP + lane;
+    float x[NM][kMaxKRanges][J];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int r = 0; r < kMaxKRanges; ++r)
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          if (r < KS && lane + 64 * j < EP) x[m][r][j] = base[(m * KS + r) * split + 64 * j];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        float v = lane + 64 * j < EP ? x[m][0][j] : 0.f;
+#pragma unroll
+        for (int r = 1; r < kMaxKRanges; ++r)
+          if (r < KS && lane + 64 * j < EP) v += x[m][r][j];
+        hv[m][j] = v;
+      }
+  }
+  auto src = [&](int, int j, int, float& a, float& b) {
+    a = hv[0][j];
+    if (NOISY) b = hv[NM - 1][j];
   };
-  route_epilogue<EP, NOISY>(src, Ps, p, t0, RB);
+  route_epilogue<EP, NOISY>(src, Ps, p, t0, 4);
 }
 
-// float32 path: plain sequential dot products (small workloads only).
 template <int NB, bool NOISY>
 __global__ __launch_bounds__(256) void route_f32_kernel(RouteParams p) {
   constexpr int EP = 16 * NB, RB = 16;
@@ -493,7 +527,7 @@ __global__ __launch_bounds__(256) void route_f32_kernel(RouteParams p) {
     if (NOISY) Ln[i] = accn;
   }
   __syncthreads();
-  auto src = [&](int tt, int e, float& hv, float& hn) {
+  auto src = [&](int tt, int, int e, float& hv, float& hn) {
     hv = L[tt * EP + e];
     if (NOISY) hn = Ln[tt * EP + e];
   };
@@ -509,17 +543,26 @@ __global__ void pad_rows_kernel(const bf16* W, bf16* Wp, int h, int E, int Ew) {
   }
 }
 
-// One workgroup per column (E experts, then the LSE^2 column): thread j adds
-// partials j, j + 256, ... in order, then a fixed-shape tree adds the 256
-// sums (deterministic).  Column E lands in total[E] (z-loss numerator); out
-// gets the E expert sums only.
+// One workgroup per expert (then one for the LSE^2 row), over that row of
+// the [EP + 1][nblk] partials: thread j adds partials j, j + 256, ... in
+// order, then a fixed-shape tree adds the 256 sums (deterministic).  The
+// LSE^2 sum lands in total[E] (z-loss numerator); out gets the E expert sums
+// only.
 __global__ __launch_bounds__(256) void prob_reduce_kernel(const double* part, int nblk, int EP,
                                                           int E, double* total, float* out) {
   __shared__ double sh[256];
   const int e = blockIdx.x;
   const int col = e < E ? e : EP;
+  const double* row = part + (size_t)col * nblk;
   double s = 0.0;
-  for (int b = threadIdx.x; b < nblk; b += 256) s += part[(size_t)b * (EP + 1) + col];
+  for (int b0 = threadIdx.x; b0 < nblk; b0 += 8 * 256) {
+    double v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = b0 + i * 256 < nblk ? row[b0 + i * 256] : 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (b0 + i * 256 < nblk) s += v[i];
+  }
   sh[threadIdx.x] = s;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
@@ -543,17 +586,20 @@ RouteShape route_shape(int T, int E, int h, int bf16, int noisy) {
   if (bf16) {
     rs.Ew = (E + 7) & ~7;
     rs.BN = rs.EP < 128 ? rs.EP : 128;
-    // waves along tokens: a wave's columns stay inside one weight matrix
-    rs.WM = rs.BN == 16 ? (noisy ? 2 : 4) : (rs.BN == 128 || noisy) ? 1 : 2;
-    rs.mblocks = (T + 63) / 64;
     rs.nblocks = rs.EP / rs.BN;
-    // split K until the grid covers the chip, keeping at least 4 chunks a range
     const int KT = h / 64;
+    // 128-token tiles halve the weight bytes read per U byte on wide routers
+    // when they still give the chip 256 workgroups
+    const int ks_max = std::min(8, std::max(1, KT / 8));
+    rs.BM = (rs.BN >= 64 && (T + 127) / 128 * rs.nblocks * ks_max >= 256) ? 128 : 64;
+    // waves along tokens: a wave's columns stay inside one weight matrix
+    if (rs.BM == 128) rs.WM = 2;
+    else rs.WM = rs.BN == 16 ? (noisy ? 2 : 4) : (rs.BN == 128 || noisy) ? 1 : 2;
+    rs.mblocks = (T + rs.BM - 1) / rs.BM;
+    // split K until the grid covers the chip, keeping at least 4 chunks a range
     rs.KS = 1;
-    while (rs.mblocks * rs.nblocks * rs.KS < 256 && KT / (2 * rs.KS) >= 4) rs.KS *= 2;
-    // one token per wave, more per workgroup on long inputs (fewer partials)
-    rs.RB = 4;
-    while (rs.RB < 32 && (T + rs.RB - 1) / rs.RB > 1024) rs.RB *= 2;
+    while (rs.mblocks * rs.nblocks * rs.KS < 256 && KT / (2 * rs.KS) >= 4 && rs.KS < 8) rs.KS *= 2;
+    rs.RB = 4;  // one token per wave
   } else {
     rs.RB = 16;
   }
@@ -569,15 +615,14 @@ hipError_t launch_pad_router_w(const void* W, void* Wp, int h, int E, int Ew, hi
   return hipGetLastError();
 }
 
-#define MOE_ROUTE_LOGITS(BN_, NS_, WM_)                                                    \
-  if (rs.BN == BN_ && nsrc == NS_ && rs.WM == WM_) {                                        \
-    hipLaunchKernelGGL((route_logits_kernel<BN_, NS_, WM_>), dim3(grid), dim3(256), 0, s, a); \
-    launched = true;                                                                         \
+#define MOE_ROUTE_LOGITS(BM_, BN_, NS_, WM_)                                                    \
+  if (rs.BM == BM_ && rs.BN == BN_ && nsrc == NS_ && rs.WM == WM_) {                              \
+    hipLaunchKernelGGL((route_logits_kernel<BM_, BN_, NS_, WM_>), dim3(grid), dim3(256), 0, s, a); \
+    launched = true;                                                                               \
   }
 #define MOE_ROUTE_SELECT(NB_, NZ_)                                                               \
   if (rs.NB == NB_ && (noisy != 0) == NZ_) {                                                     \
-    hipLaunchKernelGGL((route_select_kernel<NB_, NZ_>), dim3(rs.nblk), dim3(256), 0, s, p, rs.RB, \
-                       rs.KS);                                                                   \
+    hipLaunchKernelGGL((route_select_kernel<NB_, NZ_>), dim3(rs.nblk), dim3(256), 0, s, p, rs.KS); \
     return hipGetLastError();                                                                    \
   }
 #define MOE_ROUTE_F32(NB_, NZ_)                                                            \
@@ -605,9 +650,11 @@ hipError_t launch_route(const RouteShape& rs, const RouteParams& p, int use_bf16
     const int nsrc = noisy ? 2 : 1;
     const unsigned grid = (unsigned)(rs.mblocks * rs.nblocks * rs.KS);
     bool launched = false;
-    MOE_ROUTE_LOGITS(16, 1, 4) MOE_ROUTE_LOGITS(16, 2, 2) MOE_ROUTE_LOGITS(32, 1, 2)
-    MOE_ROUTE_LOGITS(32, 2, 1) MOE_ROUTE_LOGITS(64, 1, 2) MOE_ROUTE_LOGITS(64, 2, 1)
-    MOE_ROUTE_LOGITS(128, 1, 1) MOE_ROUTE_LOGITS(128, 2, 1)
+    MOE_ROUTE_LOGITS(64, 16, 1, 4) MOE_ROUTE_LOGITS(64, 16, 2, 2) MOE_ROUTE_LOGITS(64, 32, 1, 2)
+    MOE_ROUTE_LOGITS(64, 32, 2, 1) MOE_ROUTE_LOGITS(64, 64, 1, 2) MOE_ROUTE_LOGITS(64, 64, 2, 1)
+    MOE_ROUTE_LOGITS(64, 128, 1, 1) MOE_ROUTE_LOGITS(64, 128, 2, 1)
+    MOE_ROUTE_LOGITS(128, 64, 1, 2) MOE_ROUTE_LOGITS(128, 64, 2, 2)
+    MOE_ROUTE_LOGITS(128, 128, 1, 2) MOE_ROUTE_LOGITS(128, 128, 2, 2)
     if (!launched) return hipErrorInvalidValue;
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -220,8 +220,8 @@ def test_all_logits_equal_and_one_hot_load():
                                rtol=1e-6)
 
 
-# Router shapes covering each tile of the bf16 logits GEMM (16, 32, 64 and 128
-# experts per tile, with and without the noise matrix), K cut into several
+# Router shapes covering each tile of the bf16 logits GEMM (64 or 128 tokens x
+# 16, 32, 64 and 128 experts, with and without the noise matrix), K cut into several
 # ranges (h = 4096 over 5 token blocks) and loops shorter than the copy ring,
 # ragged token blocks, expert counts that are not a multiple of 8 and a weight
 # matrix 2 bytes off 16-byte alignment (both read through a padded copy).
@@ -235,6 +235,10 @@ ROUTER = {
     "E128_long": L.SMALL["switch_small"].replace(T=4096, h=2048, E=128, k=1),
     "E256_sigmoid": L.SMALL["deepseek_small"].replace(T=70, h=1024, E=256, k=8),
     "E16_misaligned": L.SMALL["mixtral_small"].replace(T=90, h=192, E=16, k=2),
+    # 128-token tiles (wide routers with enough tokens)
+    "E64_noisy_bm128": L.SMALL["noisy_small"].replace(T=4100, h=4096, E=64, k=2),
+    "E100_noisy_bm128": L.SMALL["noisy_small"].replace(T=4100, h=4096, E=100, k=3),
+    "E256_bm128": L.SMALL["deepseek_small"].replace(T=2100, h=4096, E=256, k=8),
 }
 
 
