@@ -166,7 +166,9 @@ typedef enum {
 } moe_ws_entry;
 
 /* Stage boundaries recorded by moe_layer_forward when stage_events != NULL:
- * events[0] before the router ... events[MOE_NUM_STAGES] after the last stage. */
+ * events[0] before the router ... events[MOE_NUM_STAGES] after the last stage.
+ * The router's P sums are reduced in the route stage and the load statistics
+ * are computed inside the dispatch stage, so the stats stage is empty. */
 enum { MOE_NUM_STAGES = 6 }; /* route, dispatch, gate_up, down, combine, stats */
 
 /* Human-readable name of a status code (static string, never NULL). */
