@@ -12,15 +12,15 @@
 //
 // bf16 path, two kernels.  route_logits_kernel computes H = U W_r (and
 // U W_noise) as a tiled GEMM on v_mfma_f32_16x16x32_bf16 with float32
-// accumulation: a workgroup owns 64 tokens x BN experts (of both matrices when
-// noisy) over one of KS ranges of K.  64-wide K chunks of the U rows and of
+// accumulation: a workgroup owns 64 or 128 tokens x BN <= 128 experts (of
+// both matrices when noisy) over one of KS ranges of K.  64-wide K chunks of the U rows and of
 // the weight rows, read in their own [h][E] layout, are copied straight into
 // a ring of LDS stages; the weight fragments come out K-contiguous through
 // the transposing LDS read.  Each range's float32 products go to a
 // workspace.  route_select_kernel then gives each wave whole tokens: it adds
 // a token's K ranges in range order (so the result does not depend on
 // timing), and the epilogue spreads its E logits over the 64 lanes, with
-// max / sum / argmax as butterfly reductions.
+// max / sum / argmax as butterfly reductions (DPP and lane swaps, no LDS).
 #include <math.h>
 
 #include "common.hpp"
