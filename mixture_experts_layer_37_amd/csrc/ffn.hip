@@ -99,6 +99,7 @@ struct GemmParams {
   // BT kernels (weights stored [K][N]): W0 holds K rows 0..K0-1 of each
   // expert's [K][N] operand and W1 the rest ([E][K0][N] and [E][K-K0][N])
   int K0 = 0;
+  int gn = GN;  // n-tiles per group of the tile numbering
 };
 
 // A K chunk of a tail tile (see xcd_share); ks == 1: a whole tile.
@@ -133,7 +134,8 @@ __device__ __forceinline__ XcdShare xcd_share(int total, int xcd, int grid, int 
   return x;
 }
 
-// Tile t of the numbering: groups of GN n-tiles, m-tile major inside a group.
+// Tile t of the numbering: groups of p.gn n-tiles (GN unless the host widens
+// them), m-tile major inside a group.
 // The m-tile's expert, first row and valid rows come from one 8-byte entry of
 // the tile map's table.
 struct TileAt {
@@ -144,13 +146,13 @@ __device__ __forceinline__ const int2* mtile_table(const int32_t* tmap, int E) {
 }
 template <int BM>
 __device__ __forceinline__ TileAt tile_at(const GemmParams& p, int t, int mtiles) {
-  const int g = t / (mtiles * GN);
-  const int r = t - g * mtiles * GN;
-  const int gw = min(GN, p.ntiles - g * GN);
+  const int g = t / (mtiles * p.gn);
+  const int r = t - g * mtiles * p.gn;
+  const int gw = min(p.gn, p.ntiles - g * p.gn);
   const int mt = r / gw;
   const int2 m = mtile_table(p.tmap, p.E)[mt];
   TileAt x;
-  x.nt = g * GN + r % gw;
+  x.nt = g * p.gn + r % gw;
   x.e = m.y & 0xffff;
   x.row0 = m.x;
   x.nvalid = m.y >> 16;
@@ -671,7 +673,7 @@ __device__ __forceinline__ Unit unit_at(const GemmParams& p, const XcdShare& xs,
 // Persistent grouped GEMM.  The grid holds a fixed number of workgroups (a
 // multiple of 8, about one per CU); the real number of tiles is only known on
 // the device (tmap[E] m-tiles x ntiles n-tiles).  Tiles are numbered in
-// groups of GN n-tiles, m-tile major inside a group, and split into 8
+// groups of p.gn n-tiles, m-tile major inside a group, and split into 8
 // contiguous slices, one per XCD (workgroup i runs on XCD i % 8): each XCD gets
 // the same share of real tiles, and the workgroups running together on one
 // XCD hold neighbouring tiles, which share A row panels and weight panels in
@@ -1242,13 +1244,13 @@ __device__ __forceinline__ FwUnit fw_unit(const GemmParams& p, const XcdShare& x
     c.KT = (kc + 1) * KT / xs.ks - c.kbeg;
   }
   // tile t of the numbering of tile_at, read with scalar loads
-  const int g = t / (mtiles * GN);
-  const int r = t - g * mtiles * GN;
-  const int gw = min(GN, p.ntiles - g * GN);
+  const int g = t / (mtiles * p.gn);
+  const int r = t - g * mtiles * p.gn;
+  const int gw = min(p.gn, p.ntiles - g * p.gn);
   const int mt = r / gw;
   const cint* tab = (cint*)p.tmap + ((p.E + 2) & ~1);
   const int m0 = tab[2 * mt], m1 = tab[2 * mt + 1];
-  c.nt = g * GN + r % gw;
+  c.nt = g * p.gn + r % gw;
   c.e = m1 & 0xffff;
   c.row0 = m0;
   c.nvalid = m1 >> 16;
@@ -1726,6 +1728,13 @@ FfnShape ffn_shape(int64_t rows_max, int E, int h, int f, int T, int k, int bf16
   // partial (256 KB) is written and read back once by the reduction
   fs.split_max = 4;
   fs.part_slots = std::max(fs.grid1, fs.grid2);
+  // Groups of 8 n-tiles, except for the down product of experts that fit
+  // one m-tile: there each weight panel is read once anyway, and a group of
+  // (up to 32) n-tiles reads an expert's A panel from the fabric once instead
+  // of once per group (DeepSeek-V3 shape, 28 n-tiles: down 4.8% faster; the
+  // gate/up product measured 0.6% slower with wide groups).
+  fs.gn1 = fs.gn2 = GN;
+  if (avg <= (double)fs.bm2) fs.gn2 = std::min(fs.nt2, 32);
   return fs;
 }
 
@@ -1750,6 +1759,7 @@ hipError_t launch_gate_up(const FfnShape& fs, const void* X, const int32_t* offs
   if (fs.grid1 == 0) return hipSuccess;
   GemmParams p{X, offset, map1, Wg, Wu, static_cast<bf16*>(A), nullptr, nullptr, nullptr,
                E, h, f, f, fs.nt1, fs.mt1, part, fs.split_max, fs.grid1};
+  p.gn = fs.gn1;
   launch_gemm<true>(fs.bm1, p, s);
   return hipGetLastError();
 }
@@ -1761,6 +1771,7 @@ hipError_t launch_gate_up_fp8(const FfnShape& fs, const void* X8, const float* x
   if (fs.grid1 == 0) return hipSuccess;
   GemmParams p{X8, offset, map1, Wg8, Wu8, static_cast<bf16*>(A), x_scale, s_gate, s_up,
                E, h, f, f, fs.nt1, fs.mt1, part, fs.split_max, fs.grid1};
+  p.gn = fs.gn1;
   launch_gemm_fp8<true>(fs.bm1, p, s);
   return hipGetLastError();
 }
@@ -1772,6 +1783,7 @@ hipError_t launch_gate_up_save(const FfnShape& fs, const void* X, const int32_t*
   GemmParams p{X, offset, map1, Wg, Wu, static_cast<bf16*>(A), nullptr, nullptr, nullptr,
                E, h, f, f, fs.nt1, fs.mt1, part, fs.split_max, fs.grid1};
   p.C2 = static_cast<bf16*>(GU);
+  p.gn = fs.gn1;
   launch_gemm<true>(fs.bm1, p, s);
   return hipGetLastError();
 }
@@ -1802,6 +1814,7 @@ hipError_t launch_down(const FfnShape& fs, const void* A, const int32_t* offset,
   if (fs.grid2 == 0) return hipSuccess;
   GemmParams p{A, offset, map2, Wd, nullptr, static_cast<bf16*>(Y), nullptr, nullptr, nullptr,
                E, f, h, h, fs.nt2, fs.mt2, part, fs.split_max, fs.grid2};
+  p.gn = fs.gn2;
   launch_gemm<false>(fs.bm2, p, s);
   return hipGetLastError();
 }

@@ -122,6 +122,7 @@ struct FfnShape {
   int rows_cap;     // rows allocated in X and in the SwiGLU intermediate
   int split_max;    // most K chunks of a tail tile
   int part_slots;   // K-split partial tiles (256 x 256 float32 each), shared by the two GEMMs
+  int gn1, gn2;     // n-tiles per group of each GEMM's tile numbering
 };
 constexpr size_t kPartSlotBytes = 256 * 256 * sizeof(float);
 // ncu: compute units of the device (the persistent grid size)
