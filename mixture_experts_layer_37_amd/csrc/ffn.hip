@@ -1826,6 +1826,7 @@ hipError_t launch_dgrad(const FfnShape& fs, const void* A, const int32_t* offset
   GemmParams p{A, offset, map2, W0, W1, static_cast<bf16*>(C), nullptr, nullptr, nullptr,
                E, K, N, N, fs.nt2, fs.mt2, part, fs.split_max, fs.grid2};
   p.K0 = K0;
+  p.gn = fs.gn2;  // the product's shape decides, as for the forward down product
   launch_gemm_bt(fs.bm2, p, s);
   return hipGetLastError();
 }
