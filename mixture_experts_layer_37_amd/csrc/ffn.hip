@@ -1604,19 +1604,25 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* A, const int
     const int mid = (lo + hi) >> 1;
     if (offset[mid] <= row) lo = mid; else hi = mid;
   }
-  const float* a = A + (size_t)row * K;
-  const float* w0 = W0 + ((size_t)lo * N + col) * K;
+  // 16-byte loads (K is a multiple of 4): each lane's weight row is read four
+  // elements per load, the products still added in k order
+  const float4* a = reinterpret_cast<const float4*>(A + (size_t)row * K);
+  const float4* w0 = reinterpret_cast<const float4*>(W0 + ((size_t)lo * N + col) * K);
   float s0 = 0.f;
   if (GATEUP) {
-    const float* w1 = W1 + ((size_t)lo * N + col) * K;
+    const float4* w1 = reinterpret_cast<const float4*>(W1 + ((size_t)lo * N + col) * K);
     float s1 = 0.f;
-    for (int j = 0; j < K; ++j) {
-      s0 = fmaf(a[j], w0[j], s0);
-      s1 = fmaf(a[j], w1[j], s1);
+    for (int j = 0; j < K / 4; ++j) {
+      const float4 x = a[j], g = w0[j], u = w1[j];
+      s0 = fmaf(x.w, g.w, fmaf(x.z, g.z, fmaf(x.y, g.y, fmaf(x.x, g.x, s0))));
+      s1 = fmaf(x.w, u.w, fmaf(x.z, u.z, fmaf(x.y, u.y, fmaf(x.x, u.x, s1))));
     }
     C[i] = s0 / (1.f + expf(-s0)) * s1;
   } else {
-    for (int j = 0; j < K; ++j) s0 = fmaf(a[j], w0[j], s0);
+    for (int j = 0; j < K / 4; ++j) {
+      const float4 x = a[j], g = w0[j];
+      s0 = fmaf(x.w, g.w, fmaf(x.z, g.z, fmaf(x.y, g.y, fmaf(x.x, g.x, s0))));
+    }
     C[i] = s0;
   }
 }
