@@ -12,6 +12,8 @@
 // deterministic and each output byte is written exactly once.
 #include <limits.h>
 
+#include <type_traits>
+
 #include "blocks.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -20,7 +22,9 @@ namespace moe {
 
 namespace {
 
-template <typename TE>
+// KM: the most ranks a token may have (k <= KM), which sizes the loads held
+// in flight
+template <typename TE, int KM>
 __global__ __launch_bounds__(256) void combine_kernel(const TE* U, const TE* Y,
                                                       const int32_t* slot, const float* gate,
                                                       const TE* Ys, int ns, TE* out, int T, int h,
@@ -28,10 +32,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const TE* U, const TE* Y,
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  int sl[8];
-  float g[8];
+  int sl[KM];
+  float g[KM];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
+  for (int r = 0; r < KM; ++r) {
     sl[r] = r < k ? slot[(size_t)t * k + r] : -1;
     g[r] = r < k ? gate[(size_t)t * k + r] : 0.f;
   }
@@ -39,22 +43,49 @@ __global__ __launch_bounds__(256) void combine_kernel(const TE* U, const TE* Y,
   const int nvec = h / V;
   const TE* u = U + (size_t)t * h;
   TE* o = out + (size_t)t * h;
-  for (int i = lane; i < nvec; i += 64) {
-    float acc[V], y[V];
-    Elem<TE>::unpack(ld16(u + (size_t)i * V), acc);
+  // a dropped rank reads the token's own row (always valid) and adds nothing
+  const TE* src[KM];
+#pragma unroll
+  for (int r = 0; r < KM; ++r) src[r] = sl[r] >= 0 ? Y + (size_t)sl[r] * h : u;
+  // two 16-byte vectors per lane and pass, every row's loads issued before
+  // the sums (which stay in the same order: residual, shared experts, ranks)
+  for (int i0 = lane; i0 < nvec; i0 += 128) {
+    const int i1 = i0 + 64;
+    const bool two = i1 < nvec;
+    const size_t v0 = (size_t)i0 * V, v1 = (size_t)(two ? i1 : i0) * V;
+    const u32x4 a0 = ld16(u + v0), a1 = ld16(u + v1);
+    u32x4 b0[KM], b1[KM];
+#pragma unroll
+    for (int r = 0; r < KM; ++r)
+      if (r < k) {
+        b0[r] = ld16(src[r] + v0);
+        b1[r] = ld16(src[r] + v1);
+      }
+    float acc0[V], acc1[V], y[V];
+    Elem<TE>::unpack(a0, acc0);
+    Elem<TE>::unpack(a1, acc1);
     for (int q = 0; q < ns; ++q) {  // shared experts, weight 1, in order
-      Elem<TE>::unpack(ld16(Ys + ((size_t)q * T + t) * h + (size_t)i * V), y);
+      const TE* ys = Ys + ((size_t)q * T + t) * h;
+      Elem<TE>::unpack(ld16(ys + v0), y);
 #pragma unroll
-      for (int c = 0; c < V; ++c) acc[c] += y[c];
+      for (int c = 0; c < V; ++c) acc0[c] += y[c];
+      Elem<TE>::unpack(ld16(ys + v1), y);
+#pragma unroll
+      for (int c = 0; c < V; ++c) acc1[c] += y[c];
     }
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      if (sl[r] < 0) continue;
-      Elem<TE>::unpack(ld16(Y + (size_t)sl[r] * h + (size_t)i * V), y);
+    for (int r = 0; r < KM; ++r) {
+      if (r >= k) continue;
+      const bool kept = sl[r] >= 0;
+      Elem<TE>::unpack(b0[r], y);
 #pragma unroll
-      for (int q = 0; q < V; ++q) acc[q] = fmaf(g[r], y[q], acc[q]);
+      for (int c = 0; c < V; ++c) acc0[c] = kept ? fmaf(g[r], y[c], acc0[c]) : acc0[c];
+      Elem<TE>::unpack(b1[r], y);
+#pragma unroll
+      for (int c = 0; c < V; ++c) acc1[c] = kept ? fmaf(g[r], y[c], acc1[c]) : acc1[c];
     }
-    st16(o + (size_t)i * V, Elem<TE>::pack(acc));
+    st16(o + v0, Elem<TE>::pack(acc0));
+    if (two) st16(o + v1, Elem<TE>::pack(acc1));
   }
 }
 
@@ -128,14 +159,19 @@ hipError_t launch_combine(const void* U, const void* Y, const int32_t* slot, con
   if (T == 0) return hipSuccess;
   if (!Ys) ns = 0;
   dim3 grid((T + 3) / 4);
-  if (bf16_)
-    hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(256), 0, s, static_cast<const bf16*>(U),
-                       static_cast<const bf16*>(Y), slot, gate, static_cast<const bf16*>(Ys),
-                       ns, static_cast<bf16*>(out), T, h, k);
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(U), static_cast<const float*>(Y), slot, gate,
-                       static_cast<const float*>(Ys), ns, static_cast<float*>(out), T, h, k);
+  auto go = [&](auto km) {
+    constexpr int KM = decltype(km)::value;
+    if (bf16_)
+      hipLaunchKernelGGL((combine_kernel<bf16, KM>), grid, dim3(256), 0, s,
+                         static_cast<const bf16*>(U), static_cast<const bf16*>(Y), slot, gate,
+                         static_cast<const bf16*>(Ys), ns, static_cast<bf16*>(out), T, h, k);
+    else
+      hipLaunchKernelGGL((combine_kernel<float, KM>), grid, dim3(256), 0, s,
+                         static_cast<const float*>(U), static_cast<const float*>(Y), slot, gate,
+                         static_cast<const float*>(Ys), ns, static_cast<float*>(out), T, h, k);
+  };
+  if (k <= 2) go(std::integral_constant<int, 2>{});
+  else go(std::integral_constant<int, 8>{});
   return hipGetLastError();
 }
 
