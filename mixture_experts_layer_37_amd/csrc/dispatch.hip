@@ -193,11 +193,24 @@ __global__ __launch_bounds__(256) void permute_kernel(const TE* U, const int32_t
   constexpr int V = Elem<TE>::kPer16B;
   const int nvec = h / V;
   const TE* src = U + (size_t)t * h;
-  for (int i = lane; i < nvec; i += 64) {
-    const u32x4 v = ld16(src + (size_t)i * V);
+  // four vectors per lane and pass, loaded before any of their stores (a load
+  // issued after stores would wait for them: memory operations retire in
+  // order)
+  for (int i0 = lane; i0 < nvec; i0 += 256) {
+    u32x4 v[4];
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-      if (sl[r] >= 0) st16(X + (size_t)sl[r] * h + (size_t)i * V, v);
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + 64 * q;
+      v[q] = ld16(src + (size_t)(i < nvec ? i : i0) * V);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + 64 * q;
+      if (i >= nvec) break;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (sl[r] >= 0) st16(X + (size_t)sl[r] * h + (size_t)i * V, v[q]);
+    }
   }
 }
 
