@@ -192,80 +192,224 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* logits, co
 
 // dU = dOut + sum over kept ranks of dX[slot] + dH W_r^T (+ dZ W_noise^T
 // for noisy routing, + the shared experts' dXs[i]).  A workgroup takes 64
-// tokens x 128 columns j (a thread 4 tokens x 8 consecutive columns, so dOut,
-// dX and dU move 16 bytes at a time); the products over the experts run in
-// chunks of 32 with dH^T and W_r^T staged in LDS as float32.
-constexpr int kGiT = 64, kGiJ = 128, kGiK = 32;
+// tokens x 128 columns j; its four waves (2 x 2) each form 32 tokens x 64
+// columns of the product on 16x16x32 bf16 MFMA, with the experts as the
+// contraction.  Both operands are read straight from memory, since rows of dH
+// [T, E] and of W_r [h, E] already run along the experts.  dH (float32) enters
+// as hi + lo, hi = bf16(dH) and lo = bf16(dH - hi); W_r is exact in bf16, so
+// the two products carry dH to about 2^-17 relative, summed in float32.  The
+// float32 tile then passes through LDS to a layout of 4 rows x 8 consecutive
+// columns per thread, in which dOut and the dX rows (16 bytes a load) are
+// added.  Row i + 1's loads are issued before row i's store, since a load
+// queued behind a store waits for it.  VEC: E % 8 == 0 and 16-byte aligned
+// operands; KM: the bound on k the gather is unrolled for; SH: the first
+// shared expert's row joins the rows loaded ahead (ns > 0).
+constexpr int kGiT = 64, kGiJ = 128;
 
+// The operand loads read D[row][e .. e + 7] and W[row][e .. e + 7] with the
+// address clamped into the row, so no lane reads out of bounds; the values
+// past E are zeroed when the step is consumed (gi_mask), not at the load,
+// so that waiting for them does not hold up the step before.
+template <bool VEC>
+__device__ __forceinline__ void gi_load_a(const float* D, size_t row, int e, int E, float* v) {
+  if constexpr (VEC) {
+    const float* p = D + row * E + min(e, E - 8);
+    Elem<float>::unpack(ld16(p), v);
+    Elem<float>::unpack(ld16(p + 4), v + 4);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = D[row * E + min(e + q, E - 1)];
+  }
+}
+
+template <bool VEC>
+__device__ __forceinline__ u32x4 gi_load_b(const bf16* W, size_t row, int e, int E) {
+  if constexpr (VEC) {
+    return ld16(W + row * E + min(e, E - 8));
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = uint32_t(W[row * E + min(e + 2 * q, E - 1)]) |
+             (uint32_t(W[row * E + min(e + 2 * q + 1, E - 1)]) << 16);
+    return u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// zero the values of experts e + q >= E (q = 0 .. 7); with VEC, E % 8 == 0,
+// so the eight are all in or all out
+template <bool VEC>
+__device__ __forceinline__ void gi_mask_a(float* v, int e, int E) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) v[q] = (VEC ? e : e + q) < E ? v[q] : 0.f;
+}
+
+template <bool VEC>
+__device__ __forceinline__ bf16x8 gi_mask_b(u32x4 w, int e, int E) {
+  if constexpr (VEC) {
+    if (e >= E) w = u32x4{0u, 0u, 0u, 0u};
+  } else {
+    uint32_t m[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      m[q] = (e + 2 * q < E ? 0xffffu : 0u) | (e + 2 * q + 1 < E ? 0xffff0000u : 0u);
+    w &= u32x4{m[0], m[1], m[2], m[3]};
+  }
+  bf16x8 r;
+  __builtin_memcpy(&r, &w, 16);
+  return r;
+}
+
+// x = hi + lo + O(2^-18 |x|), both halves bf16 (round to nearest even)
+__device__ __forceinline__ void gi_split(const float* x, bf16x8& hi, bf16x8& lo) {
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    hw[q] = pack_bf16x2(x[2 * q], x[2 * q + 1]);
+    const float r0 = x[2 * q] - __uint_as_float(hw[q] << 16);
+    const float r1 = x[2 * q + 1] - __uint_as_float(hw[q] & 0xffff0000u);
+    lw[q] = pack_bf16x2(r0, r1);
+  }
+  __builtin_memcpy(&hi, hw, 16);
+  __builtin_memcpy(&lo, lw, 16);
+}
+
+template <bool VEC, int KM, bool SH>
 __global__ __launch_bounds__(256) void grad_input_kernel(const bf16* dOut, const bf16* dX,
                                                          const int32_t* slot, const float* dH,
                                                          const bf16* W_r, const float* dZ,
                                                          const bf16* W_n, const bf16* dXs,
                                                          int ns, bf16* dU, int T, int h, int E,
                                                          int k) {
-  __shared__ __align__(16) float sh[kGiK][kGiT];  // sh[e][t] = dH[t0 + t][e0 + e]
-  __shared__ __align__(16) float sw[kGiK][kGiJ];  // sw[e][j] = W_r[j0 + j][e0 + e]
+  __shared__ __align__(16) float tile[kGiT][kGiJ + 4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave & 1, wn = wave >> 1, l16 = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * kGiT, j0 = blockIdx.y * kGiJ;
+  floatx4 acc[2][4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // this lane's operand rows: tokens past T read row T - 1 and columns past
+  // h row h - 1 (their results are never stored)
+  size_t ar[2], br[4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) ar[mb] = (size_t)min(t0 + wm * 32 + 16 * mb + l16, T - 1);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) br[nb] = (size_t)min(j0 + wn * 64 + 16 * nb + l16, h - 1);
+  // the experts of (dH, W_r), then those of (dZ, W_noise), 32 per step
+  const int per = (E + 31) / 32, steps = dZ ? 2 * per : per;
+  float a[2][8];
+  u32x4 b[4];
+  int el = 0;  // this lane's first expert in the loaded step
+  auto load = [&](int st) __attribute__((always_inline)) {
+    const bool second = st >= per;
+    const float* D = second ? dZ : dH;
+    const bf16* W = second ? W_n : W_r;
+    el = (second ? st - per : st) * 32 + 8 * g;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) gi_load_a<VEC>(D, ar[mb], el, E, a[mb]);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) b[nb] = gi_load_b<VEC>(W, br[nb], el, E);
+  };
+  load(0);
+  for (int st = 0; st < steps; ++st) {
+    bf16x8 hi[2], lo[2], bc[4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      float am[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) am[q] = a[mb][q];
+      gi_mask_a<VEC>(am, el, E);
+      gi_split(am, hi[mb], lo[mb]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) bc[nb] = gi_mask_b<VEC>(b[nb], el, E);
+    if (st + 1 < steps) load(st + 1);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[mb], bc[nb], acc[mb][nb], 0, 0, 0);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[mb], bc[nb], acc[mb][nb], 0, 0, 0);
+      }
+  }
+  // D layout: lane holds column l16 of rows 4 g + i
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        tile[wm * 32 + 16 * mb + 4 * g + i][wn * 64 + 16 * nb + l16] = acc[mb][nb][i];
+  __syncthreads();
+
+  // a thread's rows: ty + 16 i (rows past T read row T - 1, store nothing);
+  // its columns: 8 tx .. 8 tx + 7
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][8];
+  if (j0 + tx * 8 >= h) return;  // h % 64 == 0: the last tile may hold 64 columns
+  const size_t j = (size_t)j0 + tx * 8;
+  int tr[4], sl[4][KM];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tr[i] = min(t0 + ty + 16 * i, T - 1);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[i][q] = 0.f;
-  // the experts of (dH, W_r), then those of (dZ, W_noise), kGiK at a time
-  const int chunks = (E + kGiK - 1) / kGiK;
-  for (int c = 0; c < (dZ ? 2 * chunks : chunks); ++c) {
-    const bool second = c >= chunks;
-    const float* D = second ? dZ : dH;
-    const bf16* W = second ? W_n : W_r;
-    const int eb = (second ? c - chunks : c) * kGiK;
-    const int kc = min(kGiK, E - eb);
-    for (int i = threadIdx.x; i < kGiT * kGiK; i += 256) {
-      const int tt = i / kGiK, ee = i % kGiK, t = t0 + tt, e = eb + ee;
-      sh[ee][tt] = (t < T && ee < kc) ? D[(size_t)t * E + e] : 0.f;
+    for (int q = 0; q < KM; ++q) {
+      const int v = slot[(size_t)tr[i] * k + min(q, k - 1)];
+      sl[i][q] = q < k ? v : -1;
     }
-    for (int i = threadIdx.x; i < kGiJ * kGiK; i += 256) {
-      const int jj = i / kGiK, ee = i % kGiK, j = j0 + jj;
-      sw[ee][jj] = (j < h && ee < kc) ? bf16_to_f32(W[(size_t)j * E + eb + ee]) : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int ee = 0; ee < kc; ++ee) {
-      const float4 a = *reinterpret_cast<const float4*>(&sh[ee][ty * 4]);
-      const float4 b0 = *reinterpret_cast<const float4*>(&sw[ee][tx * 8]);
-      const float4 b1 = *reinterpret_cast<const float4*>(&sw[ee][tx * 8 + 4]);
-      const float av[4] = {a.x, a.y, a.z, a.w};
-      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  // per row: dOut, KM rank rows (a dropped or absent rank reads the dOut row
+  // again, and its bits are masked to +0) and, with SH, the first shared
+  // expert's row.  The rank rows' addresses pass through an empty asm, so
+  // that the compiler sees each load as needed and keeps it ahead of the
+  // store before it instead of branching around it.
+  constexpr int NL = 1 + KM + (SH ? 1 : 0);
+  u32x4 buf[2][NL];
+  auto issue = [&](int i, u32x4* bb) __attribute__((always_inline)) {
+    const bf16* orow = dOut + (size_t)tr[i] * h + j;
+    bb[0] = ld16(orow);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc[i][q] = fmaf(av[i], bv[q], acc[i][q]);
+    for (int q = 0; q < KM; ++q) {
+      const bf16* src = sl[i][q] >= 0 ? dX + (size_t)sl[i][q] * h + j : orow;
+      asm("" : "+v"(src));
+      const uint32_t keep = sl[i][q] >= 0 ? 0xffffffffu : 0u;
+      // the address space the asm hid: global memory
+      const __attribute__((address_space(1))) u32x4* gp =
+          (const __attribute__((address_space(1))) u32x4*)src;
+      bb[1 + q] = *gp & u32x4{keep, keep, keep, keep};
     }
-    __syncthreads();
-  }
-  const int j = j0 + tx * 8;
-  if (j >= h) return;
+    if constexpr (SH) bb[1 + KM] = ld16(dXs + (size_t)tr[i] * h + j);
+  };
+  issue(0, buf[0]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= T) break;
+    if (i + 1 < 4) issue(i + 1, buf[(i + 1) & 1]);
+    const u32x4* bb = buf[i & 1];
+    const int r = ty + 16 * i;
     float v[8], x[8];
-    Elem<bf16>::unpack(ld16(dOut + (size_t)t * h + j), v);
+    Elem<bf16>::unpack(bb[0], v);
+    const float4 p0 = *reinterpret_cast<const float4*>(&tile[r][tx * 8]);
+    const float4 p1 = *reinterpret_cast<const float4*>(&tile[r][tx * 8 + 4]);
+    v[0] += p0.x, v[1] += p0.y, v[2] += p0.z, v[3] += p0.w;
+    v[4] += p1.x, v[5] += p1.y, v[6] += p1.z, v[7] += p1.w;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] += acc[i][q];
-    for (int r = 0; r < k; ++r) {
-      const int row = slot[(size_t)t * k + r];
-      if (row < 0) continue;
-      Elem<bf16>::unpack(ld16(dX + (size_t)row * h + j), x);
+    for (int q = 0; q < KM; ++q) {
+      Elem<bf16>::unpack(bb[1 + q], x);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] += x[q];
+      for (int c = 0; c < 8; ++c) v[c] += x[c];
     }
-    for (int i2 = 0; i2 < ns; ++i2) {
-      Elem<bf16>::unpack(ld16(dXs + ((size_t)i2 * T + t) * h + j), x);
+    if constexpr (SH) {
+      Elem<bf16>::unpack(bb[1 + KM], x);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] += x[q];
+      for (int c = 0; c < 8; ++c) v[c] += x[c];
+      for (int i2 = 1; i2 < ns; ++i2) {
+        Elem<bf16>::unpack(ld16(dXs + ((size_t)i2 * T + tr[i]) * h + j), x);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[c] += x[c];
+      }
     }
-    st16(dU + (size_t)t * h + j, Elem<bf16>::pack(v));
+    if (t0 + r < T) st16(dU + (size_t)(t0 + r) * h + j, Elem<bf16>::pack(v));
   }
 }
 
@@ -458,11 +602,30 @@ hipError_t launch_grad_input(const void* dOut, const void* dX, const int32_t* sl
                              const void* W_noise, const void* dXs, int ns, void* dU, int T, int h,
                              int E, int k, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(grad_input_kernel, dim3((T + kGiT - 1) / kGiT, (h + kGiJ - 1) / kGiJ),
-                     dim3(256), 0, s, static_cast<const bf16*>(dOut),
-                     static_cast<const bf16*>(dX), slot, dH, static_cast<const bf16*>(W_r), dZ,
-                     static_cast<const bf16*>(W_noise), static_cast<const bf16*>(dXs), ns,
-                     static_cast<bf16*>(dU), T, h, E, k);
+  if (h % 64 != 0 || k < 1 || k > 8) return hipErrorInvalidValue;
+  const dim3 grid((T + kGiT - 1) / kGiT, (h + kGiJ - 1) / kGiJ);
+  auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  const bool vec = E % 8 == 0 && al16(dH) && al16(W_r) && (!dZ || (al16(dZ) && al16(W_noise)));
+#define MOE_GI(V, KM, SH)                                                                     \
+  hipLaunchKernelGGL((grad_input_kernel<V, KM, SH>), grid, dim3(256), 0, s,                   \
+                     static_cast<const bf16*>(dOut), static_cast<const bf16*>(dX), slot, dH,  \
+                     static_cast<const bf16*>(W_r), dZ, static_cast<const bf16*>(W_noise),    \
+                     static_cast<const bf16*>(dXs), ns, static_cast<bf16*>(dU), T, h, E, k)
+  const bool sh = ns > 0;
+  if (vec) {
+    if (k <= 2) {
+      if (sh) MOE_GI(true, 2, true); else MOE_GI(true, 2, false);
+    } else {
+      if (sh) MOE_GI(true, 8, true); else MOE_GI(true, 8, false);
+    }
+  } else {
+    if (k <= 2) {
+      if (sh) MOE_GI(false, 2, true); else MOE_GI(false, 2, false);
+    } else {
+      if (sh) MOE_GI(false, 8, true); else MOE_GI(false, 8, false);
+    }
+  }
+#undef MOE_GI
   return hipGetLastError();
 }
 
