@@ -276,16 +276,22 @@ FfnBwdWs plan_ffn_backward(const Dims& d, Plan& pl, int min_slots = 0) {
   return w;
 }
 
-// The router's backward: dH, dZ (noisy routing) and the dW_r partials.
+// The router's backward: dH, dZ (noisy routing), the dW_r product's space,
+// and for noisy routing the products Z = U W_noise (from the logits GEMM)
+// and a padded copy of W_noise when it cannot be read in place.
 struct RouterBwdWs {
-  size_t dH, dZ, dwr;
+  size_t dH, dZ, dwr, zpart, wnp;
+  RouteShape zs;
 };
-RouterBwdWs plan_router_backward(const Dims& d, Plan& pl) {
+RouterBwdWs plan_router_backward(const Dims& d, int noisy, Plan& pl) {
   RouterBwdWs w;
   const size_t T1 = (size_t)(d.T > 0 ? d.T : 1);
   w.dH = pl.add(T1 * d.E * 4);
   w.dZ = pl.add(T1 * d.E * 4);
   w.dwr = pl.add(dwr_part_bytes(d.T, (int)d.h, (int)d.E));
+  w.zs = route_shape((int)d.T, (int)d.E, (int)d.h, 1, 0);
+  w.zpart = noisy ? pl.add((size_t)w.zs.KS * T1 * w.zs.EP * 4) : 0;
+  w.wnp = noisy ? pl.add((size_t)w.zs.Ew * d.h * 2) : 0;
   return w;
 }
 
@@ -301,7 +307,7 @@ struct BackwardWs {
   FfnShape shA, shX;
   size_t sGU, sdA, sdGU, sdX;
 };
-BackwardWs plan_backward(const Dims& d, Plan& pl) {
+BackwardWs plan_backward(const Dims& d, int noisy, Plan& pl) {
   BackwardWs w;
   const int ncu = device_cus();
   w.sh = plan_shared(d, false, pl);
@@ -317,7 +323,7 @@ BackwardWs plan_backward(const Dims& d, Plan& pl) {
     sh_slots = std::max(w.sh.fs.part_slots, std::max(w.shA.part_slots, w.shX.part_slots));
   }
   w.fb = plan_ffn_backward(d, pl, sh_slots);
-  w.rb = plan_router_backward(d, pl);
+  w.rb = plan_router_backward(d, noisy, pl);
   const size_t rows = (size_t)(d.rows_max > 0 ? d.rows_max : 1);
   w.X = pl.add(rows * d.h * 2);
   w.Y = pl.add(rows * d.h * 2);
@@ -577,9 +583,9 @@ int32_t moe_workspace_size(const moe_config* cfg, int32_t entry, size_t* bytes) 
     case MOE_WS_EXPERT_FFN: plan_ffn(d, pl); break;
     case MOE_WS_LAYER: plan_layer(d, cfg->noisy, pl); break;
     case MOE_WS_SHARED_FFN: plan_shared(d, false, pl); break;
-    case MOE_WS_BACKWARD: plan_backward(d, pl); break;
+    case MOE_WS_BACKWARD: plan_backward(d, cfg->noisy, pl); break;
     case MOE_WS_EXPERT_FFN_BACKWARD: plan_ffn_backward(d, pl); break;
-    case MOE_WS_ROUTER_BACKWARD: plan_router_backward(d, pl); break;
+    case MOE_WS_ROUTER_BACKWARD: plan_router_backward(d, cfg->noisy, pl); break;
     default: return MOE_ERR_INVALID_ARG;
   }
   *bytes = pl.bytes;
@@ -911,7 +917,16 @@ int32_t run_router_backward(const moe_config* cfg, const Dims& d, const RouterBw
   float* dZ = nullptr;
   if (cfg->noisy) {
     dZ = at<float>(ws, w.dZ);
-    MOE_TRY(launch_noise_grad(U, extra->W_noise, dH, cfg->seed, cfg->rng_offset, dZ, T, h, E,
+    // Z = U W_noise again, by the logits GEMM (rows of a multiple of 8
+    // columns at 16-byte alignment, else from a padded copy)
+    const void* Wn = extra->W_noise;
+    if (E % 8 != 0 || (uintptr_t)Wn % 16 != 0) {
+      MOE_TRY(launch_pad_router_w(Wn, at<void>(ws, w.wnp), h, E, w.zs.Ew, s));
+      Wn = at<void>(ws, w.wnp);
+    }
+    float* zpart = at<float>(ws, w.zpart);
+    MOE_TRY(launch_route_products(w.zs, U, Wn, zpart, T, h, s));
+    MOE_TRY(launch_noise_grad(zpart, w.zs.KS, w.zs.EP, dH, cfg->seed, cfg->rng_offset, dZ, T, E,
                               s));
   }
   MOE_TRY(launch_grad_input(dOut, dX, slot, dH, W_r, dZ, cfg->noisy ? extra->W_noise : nullptr,
@@ -1038,7 +1053,7 @@ int32_t moe_router_backward(const moe_config* cfg, const void* U, const void* W_
     return MOE_ERR_INVALID_ARG;
   if (!isfinite(alpha) || !isfinite(c_z)) return MOE_ERR_INVALID_ARG;
   Plan pl;
-  const RouterBwdWs w = plan_router_backward(d, pl);
+  const RouterBwdWs w = plan_router_backward(d, cfg->noisy, pl);
   if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
   return run_router_backward(cfg, d, w, ws, U, W_r, logits, topk_idx, topk_gate, slot, count,
                              dgate, dOut, dX, nullptr, 0, alpha, c_z, extra, dU, dW_r, db_r,
@@ -1078,7 +1093,7 @@ int32_t moe_layer_backward(const moe_config* cfg, const void* U, const void* W_r
   }
   if (!backward_offsets_fit(d)) return MOE_ERR_UNSUPPORTED;
   Plan pl;
-  const BackwardWs w = plan_backward(d, pl);
+  const BackwardWs w = plan_backward(d, cfg->noisy, pl);
   if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int E = (int)d.E, h = (int)d.h, f = (int)d.f, T = (int)d.T, k = (int)d.k;

@@ -416,152 +416,278 @@ __global__ __launch_bounds__(256) void grad_input_kernel(const bf16* dOut, const
 // Noisy routing: the logits hold z * softplus(Z) with Z = U W_noise, so
 // dZ = dH * z * sigmoid(Z) (softplus' = sigmoid; page "MoE 与专家并行",
 // router section, eq. G(x)); z, the forward's standard-normal draw of the
-// pair, is drawn again from its counter.  Z is recomputed in float32: a workgroup takes
-// 64 tokens x 64 experts, stages 32 columns of U (transposed) and of W_noise
-// at a time in LDS, and a thread accumulates 4 tokens x 4 experts.
-__global__ __launch_bounds__(256) void noise_grad_kernel(const bf16* U, const bf16* W_n,
+// pair, is drawn again from its counter.  Z comes from the router's logits
+// GEMM run again on W_noise (bf16 MFMA, float32 sums over KS ranges of h),
+// summed here in range order.
+__global__ __launch_bounds__(256) void noise_grad_kernel(const float* zpart, int KS, int EP,
                                                          const float* dH, uint64_t seed,
                                                          uint64_t rng_offset, float* dZ, int T,
-                                                         int h, int E) {
-  __shared__ __align__(16) float su[32][64];  // su[j][t] = U[t0 + t][j0 + j]
-  __shared__ __align__(16) float sw[32][64];  // sw[j][e] = W_noise[j0 + j][e0 + e]
-  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;  // 4 experts, 4 tokens
-  float acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[i][q] = 0.f;
-  for (int j0 = 0; j0 < h; j0 += 32) {  // h is a multiple of 64
-    {
-      const int tt = threadIdx.x >> 2, jj = (threadIdx.x & 3) * 8, t = t0 + tt;
-      float v[8];
-      if (t < T) {
-        Elem<bf16>::unpack(ld16(U + (size_t)t * h + j0 + jj), v);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = 0.f;
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) su[jj + q][tt] = v[q];
-    }
-    for (int i = threadIdx.x; i < 32 * 64; i += 256) {
-      const int jj = i >> 6, ee = i & 63, e = e0 + ee;
-      sw[jj][ee] = e < E ? bf16_to_f32(W_n[(size_t)(j0 + jj) * E + e]) : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int jj = 0; jj < 32; ++jj) {
-      const float4 a = *reinterpret_cast<const float4*>(&su[jj][ty * 4]);
-      const float4 b = *reinterpret_cast<const float4*>(&sw[jj][tx * 4]);
-      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][q] = fmaf(av[i], bv[q], acc[i][q]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= T) break;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = e0 + tx * 4 + q;
-      if (e >= E) break;
-      const size_t o = (size_t)t * E + e;
-      const float z = (float)philox_normal(seed, (uint64_t)o + rng_offset);
-      dZ[o] = dH[o] * z / (1.f + __expf(-acc[i][q]));
-    }
-  }
+                                                         int E) {
+  const size_t o = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= (size_t)T * E) return;
+  const int t = (int)(o / E), e = (int)(o % E);
+  float z = 0.f;
+  for (int ks = 0; ks < KS; ++ks) z += zpart[((size_t)ks * T + t) * EP + e];
+  const float n = (float)philox_normal(seed, (uint64_t)o + rng_offset);
+  dZ[o] = dH[o] * n / (1.f + __expf(-z));
 }
 
-// dW_r[j][e] = sum_t U[t][j] dH[t][e] and db_r[e] = sum_t dH[t][e] in
-// float32, computed as one product in which U has an extra column of ones
-// (j = h).  Workgroup (jt, et, s) takes TJ x TE outputs over the tokens of
-// split s, stages 16 tokens of U and dH at a time in LDS as float32, and a
-// thread accumulates 4 x 4 outputs; the splits' partials part[s][j][e] are
-// summed in split order by dwr_reduce_kernel (deterministic).
-template <int TE>
-__global__ __launch_bounds__(256) void dwr_part_kernel(const bf16* U, const float* dH,
-                                                       float* part, int T, int h, int E,
-                                                       int tchunk) {
-  constexpr int NE = TE / 4, NJ = 256 / NE, TJ = 4 * NJ, KC = 16;
-  __shared__ __align__(16) float su[KC][TJ];
-  __shared__ __align__(16) float sd[KC][TE];
-  const int j0 = blockIdx.x * TJ, e0 = blockIdx.y * TE;
-  const int tb = blockIdx.z * tchunk, tend = min(T, tb + tchunk);
-  const int tx = threadIdx.x % NE, ty = threadIdx.x / NE;
-  float acc[4][4];
+// dW_r[j][e] = sum_t U[t][j] dH[t][e] and db_r[e] = sum_t dH[t][e]: a
+// product with the tokens as the contraction, in three launches.
+//
+// dwr_split_kernel writes dH as bf16 pairs: row t of HL holds, for each tile
+// of TE experts, hi = bf16(dH) then lo = bf16(dH - hi) (experts past E zero),
+// so that U, exact in bf16, times hi + lo carries dH to about 2^-17
+// relative.  A thread takes 8 consecutive experts of one token.
+__global__ __launch_bounds__(256) void dwr_split_kernel(const float* D, int T, int E, int TE,
+                                                        int EP, bool vec, bf16* HL) {
+  const int per = EP / 8;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)T * per) return;
+  const int t = (int)(i / per), e = (int)(i % per) * 8;
+  float x[8];
+  const float* src = D + (size_t)t * E + e;
+  if (vec && e < E) {  // E % 8 == 0, 16-byte aligned rows
+    Elem<float>::unpack(ld16(src), x);
+    Elem<float>::unpack(ld16(src + 4), x + 4);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < 8; ++q) x[q] = e + q < E ? src[q] : 0.f;
+  }
+  float hi[8], lo[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[i][q] = 0.f;
-  const bool vec_e = (E & 3) == 0;
-  for (int t0 = tb; t0 < tend; t0 += KC) {
-    for (int i = threadIdx.x; i < KC * (TJ / 8); i += 256) {
-      const int tt = i / (TJ / 8), jj = (i % (TJ / 8)) * 8, t = t0 + tt, j = j0 + jj;
-      float v[8];
-      if (t < tend && j < h) {  // h is a multiple of 8
-        Elem<bf16>::unpack(ld16(U + (size_t)t * h + j), v);
-      } else {
+  for (int q = 0; q < 8; ++q) {
+    hi[q] = bf16_to_f32(f32_to_bf16(x[q]));
+    lo[q] = x[q] - hi[q];
+  }
+  bf16* row = HL + (size_t)t * 2 * EP + (size_t)(e / TE) * 2 * TE + e % TE;
+  st16(row, Elem<bf16>::pack(hi));
+  st16(row + TE, Elem<bf16>::pack(lo));
+}
+
+// dwr_mfma_kernel: workgroup (expert tile, column tile, token split) forms
+// part[split][j][e] for TJ columns j x TE experts over its split's tokens on
+// 16x16x32 bf16 MFMA, twice per step (hi, then lo).  Each step's 32 tokens of
+// U [32][TJ] and of HL [32][hi TE | lo TE] reach LDS by direct copies (a ring
+// of NS stages, 1 KB per copy, rows of the split past T read as zeros), and
+// both operands come out of LDS by transposing reads, since U and HL run
+// along j and e, not along the tokens.  Waves: GJ x GE, each 64 columns x WE
+// experts.  With dsum, the first column tile's first waves also add up the hi
+// and lo values they read, per expert, into db_r's partial (row h of part).
+struct DwArgs {
+  const bf16* U;
+  const bf16* HL;
+  float* part;  // [nsplit][h + 1][E]
+  int T, h, E, EP, tchunk, jtiles, etiles, dsum;
+};
+
+template <int TJ, int TE>
+struct DwCfg {
+  static constexpr int GJ = TJ / 64, GE = 4 / GJ, WE = TE / GE, FE = WE / 16;
+  static constexpr int UB = 32 * TJ * 2, HB = 32 * 4 * TE, SB = UB + HB;
+  static constexpr int NQ = SB / 1024, NC = (NQ + 3) / 4, NS = 3;
+  static_assert(GJ * GE == 4 && FE >= 1 && UB % 1024 == 0 && HB % 1024 == 0, "tile");
+};
+
+template <int TJ, int TE>
+__global__ __launch_bounds__(256, 2) void dwr_mfma_kernel(DwArgs p) {
+  using C = DwCfg<TJ, TE>;
+  constexpr int NS = C::NS, NC = C::NC, FE = C::FE, UQ = C::UB / 1024;
+  __shared__ __attribute__((aligned(16))) char lds[NS * C::SB];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wj = wave % C::GJ, we = wave / C::GJ;
+  const int l16 = lane & 15, g = lane >> 4, q = l16 >> 2, jl = l16 & 3;
+  // workgroup -> (split, column tile, expert tile); the expert tiles of one
+  // column tile, which copy the same U, are consecutive on one XCD
+  const int G = gridDim.x;
+  const int L = (G & 7) == 0 ? xcd_remap(blockIdx.x, G) : blockIdx.x;
+  const int et = L % p.etiles, rest = L / p.etiles;
+  const int jt = rest % p.jtiles, sp = rest / p.jtiles;
+  const int j0 = jt * TJ, e0 = et * TE;
+  const int tb = sp * p.tchunk, tn = max(0, min(p.T, tb + p.tchunk) - tb);
+  const int KT = (tn + 31) / 32, h = p.h, HLP = 2 * p.EP;
+
+  // this wave's copies: 1 KB chunks wave + 4 i of a stage (the last chunk
+  // repeated where the stage has fewer), U rows then HL rows, each row's
+  // 16-byte chunks placed by the wsw swizzle
+  int voff[NC], dst[NC];
+  bool isu[NC];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = (t < tend && j + q == h) ? 1.f : 0.f;
-      }
-      *reinterpret_cast<float4*>(&su[tt][jj]) = make_float4(v[0], v[1], v[2], v[3]);
-      *reinterpret_cast<float4*>(&su[tt][jj + 4]) = make_float4(v[4], v[5], v[6], v[7]);
+  for (int i = 0; i < NC; ++i) {
+    const int qq = min(wave + 4 * i, C::NQ - 1);
+    const int byte = qq * 1024 + lane * 16;
+    dst[i] = qq * 1024;
+    isu[i] = qq < UQ;
+    if (qq < UQ) {
+      const int r = byte / (TJ * 2), c = ((byte % (TJ * 2)) >> 4) ^ wsw<TJ / 8>(r);
+      voff[i] = r * h * 2 + j0 * 2 + c * 16;
+    } else {
+      const int b = byte - C::UB, r = b / (4 * TE), c = ((b % (4 * TE)) >> 4) ^ wsw<TE / 4>(r);
+      voff[i] = r * HLP * 2 + c * 16;
     }
-    for (int i = threadIdx.x; i < KC * NE; i += 256) {
-      const int tt = i / NE, ee = (i % NE) * 4, t = t0 + tt, e = e0 + ee;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t < tend) {
-        const float* src = dH + (size_t)t * E + e;
-        if (vec_e && e + 4 <= E) {
-          v = *reinterpret_cast<const float4*>(src);
-        } else {
-          v.x = e < E ? src[0] : 0.f;
-          v.y = e + 1 < E ? src[1] : 0.f;
-          v.z = e + 2 < E ? src[2] : 0.f;
-          v.w = e + 3 < E ? src[3] : 0.f;
+  }
+  // this lane's transposing reads: k-rows 8 g + q (+ 4), columns 4 jl .. +3
+  // of fragment column block col0
+  int fa[4], fh[FE], fl[FE];
+#pragma unroll
+  for (int fj = 0; fj < 4; ++fj) {
+    const int r = 8 * g + q, c = ((wj * 64 + 16 * fj) >> 3) + (jl >> 1);
+    fa[fj] = r * (TJ * 2) + ((c ^ wsw<TJ / 8>(r)) << 4) + 8 * (jl & 1);
+  }
+#pragma unroll
+  for (int fe = 0; fe < FE; ++fe) {
+    const int r = 8 * g + q, col = we * C::WE + 16 * fe;
+    const int ch = (col >> 3) + (jl >> 1), cl = ((col + TE) >> 3) + (jl >> 1);
+    fh[fe] = C::UB + r * (4 * TE) + ((ch ^ wsw<TE / 4>(r)) << 4) + 8 * (jl & 1);
+    fl[fe] = C::UB + r * (4 * TE) + ((cl ^ wsw<TE / 4>(r)) << 4) + 8 * (jl & 1);
+  }
+
+  floatx4 acc[4][FE];
+#pragma unroll
+  for (int fj = 0; fj < 4; ++fj)
+#pragma unroll
+    for (int fe = 0; fe < FE; ++fe) acc[fj][fe] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // db_r: this lane's 8 tokens per step of expert column l16, per fragment
+  const bool dsum = p.dsum && jt == 0 && wj == 0;
+  float ds[FE];
+#pragma unroll
+  for (int fe = 0; fe < FE; ++fe) ds[fe] = 0.f;
+
+  const size_t ubytes = (size_t)tn * h * 2;
+  const size_t hbytes = tn > 0 ? (size_t)tn * HLP * 2 - (size_t)et * TE * 4 : 0;
+  // the ring's slots as restrict parameters (and the copies' sources built
+  // from restrict pointers): the compiler then tells the copies into one slot
+  // from the reads of another and adds no waits beyond the one per step
+  auto run = [&](char* __restrict__ s0, char* __restrict__ s1, char* __restrict__ s2,
+                 const char* __restrict__ gU, const char* __restrict__ gH)
+                 __attribute__((always_inline)) {
+    char* const S[3] = {s0, s1, s2};
+    const __amdgpu_buffer_rsrc_t rU = make_rsrc(gU, ubytes);
+    const __amdgpu_buffer_rsrc_t rH = make_rsrc(gH, hbytes);
+    // copies of step cc into slot sl (past the range: no memory traffic, the
+    // slot is never read again)
+    auto issue = [&](int cc, char* sl) __attribute__((always_inline)) {
+      const bool live = cc < KT;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        // the step's offset goes into the lane offset: the range check (rows
+        // past the split read as zeros) covers only that one
+        if (isu[i])
+          dma16(rU, sl + dst[i], live ? voff[i] + cc * 64 * h : kPastEnd, 0);
+        else
+          dma16(rH, sl + dst[i], live ? voff[i] + cc * 64 * HLP : kPastEnd, 0);
+      }
+    };
+    auto compute = [&](const char* sl) __attribute__((always_inline)) {
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4s lds_v4s;
+      auto tr = [&](const char* bp, int step) __attribute__((always_inline)) {
+        const v4s v[2] = {__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(bp)),
+                          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(bp + step))};
+        bf16x8 r;
+        __builtin_memcpy(&r, v, 16);
+        return r;
+      };
+      bf16x8 a[4], bh[FE], bl[FE];
+#pragma unroll
+      for (int fj = 0; fj < 4; ++fj) a[fj] = tr(sl + fa[fj], 4 * TJ * 2);
+#pragma unroll
+      for (int fe = 0; fe < FE; ++fe) {
+        bh[fe] = tr(sl + fh[fe], 4 * 4 * TE);
+        bl[fe] = tr(sl + fl[fe], 4 * 4 * TE);
+      }
+#pragma unroll
+      for (int fj = 0; fj < 4; ++fj)
+#pragma unroll
+        for (int fe = 0; fe < FE; ++fe) {
+          acc[fj][fe] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fj], bh[fe], acc[fj][fe], 0, 0, 0);
+          acc[fj][fe] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fj], bl[fe], acc[fj][fe], 0, 0, 0);
+        }
+      if (dsum) {
+#pragma unroll
+        for (int fe = 0; fe < FE; ++fe) {
+          u32x4 uh, ul;
+          __builtin_memcpy(&uh, &bh[fe], 16);
+          __builtin_memcpy(&ul, &bl[fe], 16);
+          float vh[8], vl[8];
+          Elem<bf16>::unpack(uh, vh);
+          Elem<bf16>::unpack(ul, vl);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) ds[fe] += vh[k] + vl[k];
         }
       }
-      *reinterpret_cast<float4*>(&sd[tt][ee]) = v;
+    };
+    // step c sits in slot c % NS; it waits for its copies, then refills the
+    // slot of step c - 1 (every wave is past it) with step c + NS - 1
+    auto step = [&](int c, int u) __attribute__((always_inline)) {
+      wait_vm_seen<(NS - 2) * NC>();
+      wait_lgkm0_seen();
+      barrier_only();
+      issue(c + NS - 1, S[(u + NS - 1) % NS]);
+      compute(S[u]);
+    };
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) issue(u, S[u]);
+    int c = 0;
+    for (; c + NS <= KT; c += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) step(c + u, u);
     }
-    __syncthreads();
 #pragma unroll
-    for (int tt = 0; tt < KC; ++tt) {
-      const float4 a = *reinterpret_cast<const float4*>(&su[tt][ty * 4]);
-      const float4 b = *reinterpret_cast<const float4*>(&sd[tt][tx * 4]);
-      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+    for (int u = 0; u < NS - 1; ++u)
+      if (c + u < KT) step(c + u, u);
+    wait_vm_seen<0>();  // the last copies (past the range) land before the slots go away
+  };
+  run(lds, lds + C::SB, lds + 2 * C::SB,
+      reinterpret_cast<const char*>(p.U + (size_t)tb * h),
+      reinterpret_cast<const char*>(p.HL + (size_t)tb * HLP + (size_t)et * 2 * TE));
+
+  // D layout: lane holds expert column l16 of column rows 4 g + i
+  float* P = p.part + (size_t)sp * (h + 1) * p.E;
+  if (dsum) {  // the four token groups g of a column, in a fixed order
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][q] = fmaf(av[i], bv[q], acc[i][q]);
+    for (int fe = 0; fe < FE; ++fe) {
+      float v = ds[fe];
+      v += wave_partner<4>(v);
+      v += wave_partner<5>(v);
+      const int e = e0 + we * C::WE + 16 * fe + l16;
+      if (g == 0 && e < p.E) P[(size_t)h * p.E + e] = v;
     }
-    __syncthreads();
   }
-  float* P = part + (size_t)blockIdx.z * (size_t)(h + 1) * E;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = j0 + ty * 4 + i;
-    if (j > h) break;
+  for (int fe = 0; fe < FE; ++fe) {
+    const int e = e0 + we * C::WE + 16 * fe + l16;
+    if (e >= p.E) continue;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = e0 + tx * 4 + q;
-      if (e < E) P[(size_t)j * E + e] = acc[i][q];
-    }
+    for (int fj = 0; fj < 4; ++fj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + wj * 64 + 16 * fj + 4 * g + i;
+        if (j < h) P[(size_t)j * p.E + e] = acc[fj][fe][i];
+      }
   }
 }
 
+// dW_r (and db_r, row h) = sum over splits of part[s], in split order:
+// deterministic.  Eight partials are loaded at a time, then added in order.
 __global__ __launch_bounds__(256) void dwr_reduce_kernel(const float* part, int nsplit, int h,
                                                          int E, float* dWr, float* db) {
-  const size_t n = (size_t)(h + 1) * E;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+  const size_t n = (size_t)h * E, pitch = n + E, tot = db ? pitch : n;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < tot;
+       i += (size_t)gridDim.x * 256) {
+    const float* src = part + i;
     float s = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) s += part[(size_t)sp * n + i];
-    if (i < (size_t)h * E) dWr[i] = s;
-    else if (db) db[i - (size_t)h * E] = s;
+    int c = 0;
+    for (; c + 8 <= nsplit; c += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(c + u) * pitch];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; c < nsplit; ++c) s += src[(size_t)c * pitch];
+    if (i < n) dWr[i] = s;
+    else db[i - n] = s;
   }
 }
 
@@ -629,42 +755,41 @@ hipError_t launch_grad_input(const void* dOut, const void* dX, const int32_t* sl
   return hipGetLastError();
 }
 
-hipError_t launch_noise_grad(const void* U, const void* W_noise, const float* dH,
-                             uint64_t seed, uint64_t rng_offset, float* dZ, int T, int h, int E,
-                             hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(noise_grad_kernel, dim3((T + 63) / 64, (E + 63) / 64), dim3(256), 0, s,
-                     static_cast<const bf16*>(U), static_cast<const bf16*>(W_noise), dH, seed,
-                     rng_offset, dZ, T, h, E);
+hipError_t launch_noise_grad(const float* zpart, int KS, int EP, const float* dH, uint64_t seed,
+                             uint64_t rng_offset, float* dZ, int T, int E, hipStream_t s) {
+  const size_t n = (size_t)T * E;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(noise_grad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, zpart,
+                     KS, EP, dH, seed, rng_offset, dZ, T, E);
   return hipGetLastError();
 }
 
-hipError_t launch_dwr(const void* U, const float* dH, float* dWr, float* db, float* part, int T,
+hipError_t launch_dwr(const void* U, const float* dH, float* dWr, float* db, void* ws, int T,
                       int h, int E, hipStream_t s) {
   const DwrPlan p = dwr_plan(T, h, E);
-  const dim3 grid(p.jt, p.et, p.nsplit);
-  const bf16* u = static_cast<const bf16*>(U);
-  switch (p.te) {
-    case 8:
-      hipLaunchKernelGGL(dwr_part_kernel<8>, grid, dim3(256), 0, s, u, dH, part, T, h, E,
-                         p.tchunk);
-      break;
-    case 16:
-      hipLaunchKernelGGL(dwr_part_kernel<16>, grid, dim3(256), 0, s, u, dH, part, T, h, E,
-                         p.tchunk);
-      break;
-    case 32:
-      hipLaunchKernelGGL(dwr_part_kernel<32>, grid, dim3(256), 0, s, u, dH, part, T, h, E,
-                         p.tchunk);
-      break;
-    default:
-      hipLaunchKernelGGL(dwr_part_kernel<64>, grid, dim3(256), 0, s, u, dH, part, T, h, E,
-                         p.tchunk);
-      break;
+  char* w = static_cast<char*>(ws);
+  float* part = reinterpret_cast<float*>(w);
+  bf16* HL = reinterpret_cast<bf16*>(w + p.hl_off);
+  if (T > 0) {
+    const size_t n = (size_t)T * (p.ep / 8);
+    const bool vec = E % 8 == 0 && (reinterpret_cast<uintptr_t>(dH) & 15) == 0;
+    hipLaunchKernelGGL(dwr_split_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dH,
+                       T, E, p.te, p.ep, vec, HL);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
   }
-  const hipError_t err = hipGetLastError();
+  DwArgs a{static_cast<const bf16*>(U), HL, part, T, h, E, p.ep, p.tchunk, p.jt, p.et,
+           db != nullptr};
+  const dim3 grid((unsigned)(p.jt * p.et * p.nsplit));
+  switch (p.te) {
+    case 16: hipLaunchKernelGGL((dwr_mfma_kernel<256, 16>), grid, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((dwr_mfma_kernel<256, 32>), grid, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((dwr_mfma_kernel<256, 64>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((dwr_mfma_kernel<128, 128>), grid, dim3(256), 0, s, a); break;
+  }
+  hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const size_t n = (size_t)(h + 1) * E;
+  const size_t n = (size_t)h * E + (db ? E : 0);
   const unsigned nb = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
   hipLaunchKernelGGL(dwr_reduce_kernel, dim3(nb), dim3(256), 0, s, part, p.nsplit, h, E, dWr, db);
   return hipGetLastError();

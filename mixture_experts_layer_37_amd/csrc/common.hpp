@@ -260,4 +260,19 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
   return (bid & 7) * (nblk >> 3) + (bid >> 3);
 }
 
+// Rows of a [K][N] bf16 tile in LDS that transposing fragment reads take:
+// k-row r (NCH chunks of 16 bytes) keeps logical chunk c at chunk c ^ wsw(r).
+// A transposing read of one fragment touches, per half-wave, 8 k-rows (rows
+// 8 g + q, g = 0/1, q = 0..3) x 2 adjacent chunks; wsw spreads those 16
+// pieces over distinct 16-byte bank groups (for NCH >= 4; two-chunk rows keep
+// a two-way conflict).
+template <int NCH>
+__device__ __forceinline__ int wsw(int r) {
+  const int g1 = (r >> 3) & 1, q = r & 3;
+  if constexpr (NCH >= 16) return 2 * (4 * g1 + q);
+  else if constexpr (NCH == 8) return 4 * g1 + 2 * (q >> 1);
+  else if constexpr (NCH == 4) return 2 * g1;
+  else return 0;
+}
+
 }  // namespace moe

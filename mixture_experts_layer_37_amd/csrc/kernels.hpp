@@ -48,6 +48,11 @@ RouteShape route_shape(int T, int E, int h, int bf16, int noisy);
 hipError_t launch_pad_router_w(const void* W, void* Wp, int h, int E, int Ew, hipStream_t s);
 hipError_t launch_route(const RouteShape& rs, const RouteParams& p, int bf16, int noisy,
                         hipStream_t s);
+// bf16 only: the logits GEMM alone, part[ks][t][e] = the products of U and W
+// ([h][rs.Ew], 16-byte aligned) over K range ks, for rs = route_shape(T, E,
+// h, 1, 0) (the backward's recomputation of the noise term's Z = U W_noise).
+hipError_t launch_route_products(const RouteShape& rs, const void* U, const void* W, float* part,
+                                 int T, int h, hipStream_t s);
 // total[e] (double, optional; E + 1 entries, the last the sum over tokens of
 // LSE(H_t)^2) and prob_sum[e] (float, optional, E entries): sums over the
 // router's per-workgroup partials.
@@ -211,34 +216,40 @@ hipError_t launch_grad_input(const void* dOut, const void* dX, const int32_t* sl
                              const float* dH, const void* W_r, const float* dZ,
                              const void* W_noise, const void* dXs, int ns, void* dU, int T, int h,
                              int E, int k, hipStream_t s);
-// dZ = dH * noise * sigmoid(U W_noise), [T][E] float32.
-hipError_t launch_noise_grad(const void* U, const void* W_noise, const float* dH,
-                             uint64_t seed, uint64_t rng_offset, float* dZ, int T, int h, int E,
-                             hipStream_t s);
-// dW_r = U^T dH, db_r = column sums of dH: TE experts x TJ rows of U per
-// workgroup, the tokens cut into nsplit chunks of tchunk (a multiple of 16)
-// whose float32 partials [nsplit][h + 1][E] are summed afterwards.
+// dZ = dH * noise * sigmoid(Z), [T][E] float32, with Z the sum over the KS
+// ranges of zpart [KS][T][EP] (launch_route_products with W_noise).
+hipError_t launch_noise_grad(const float* zpart, int KS, int EP, const float* dH, uint64_t seed,
+                             uint64_t rng_offset, float* dZ, int T, int E, hipStream_t s);
+// dW_r = U^T dH on MFMA (backward.hip): column tiles of tj, expert tiles of
+// te (E padded to ep = et * te), token splits of tchunk (a multiple of 32)
+// whose float32 partials [nsplit][h + 1][E] (row h: db_r) are summed in
+// order; dH as bf16 hi | lo rows [T][2 ep] at hl_off.
 struct DwrPlan {
-  int te, tj, jt, et, nsplit, tchunk;
+  int te, tj, jt, et, ep, nsplit, tchunk;
+  size_t hl_off, bytes;
 };
 inline DwrPlan dwr_plan(int64_t T, int h, int E) {
   DwrPlan p;
-  p.te = E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64;
-  p.tj = 4 * (256 / (p.te / 4));
-  p.jt = (h + 1 + p.tj - 1) / p.tj;
+  p.te = E <= 16 ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : 128;
+  p.tj = p.te == 128 ? 128 : 256;
+  p.jt = (h + p.tj - 1) / p.tj;
   p.et = (E + p.te - 1) / p.te;
+  p.ep = p.et * p.te;
   const int64_t tiles = (int64_t)p.jt * p.et;
-  const int64_t want = (2048 + tiles - 1) / tiles;  // about 2048 workgroups
+  const int64_t want = std::max<int64_t>(1, (256 + tiles - 1) / tiles);  // about 256 workgroups
   int64_t chunk = (T + want - 1) / want;
-  chunk = std::max<int64_t>(32, (chunk + 15) / 16 * 16);
+  chunk = std::max<int64_t>(32, (chunk + 31) / 32 * 32);
+  // a split's byte offsets (chunk * h * 2 for U) stay below 2^30
+  chunk = std::min<int64_t>(chunk, std::max<int64_t>(32, ((int64_t(1) << 29) / h) / 32 * 32));
   p.tchunk = (int)chunk;
   p.nsplit = T > 0 ? (int)((T + chunk - 1) / chunk) : 1;
+  auto al = [](size_t n) { return (n + 255) & ~size_t(255); };
+  p.hl_off = al((size_t)p.nsplit * (h + 1) * E * 4);
+  p.bytes = p.hl_off + al((size_t)std::max<int64_t>(T, 1) * 2 * p.ep * 2);
   return p;
 }
-inline size_t dwr_part_bytes(int64_t T, int h, int E) {
-  return (size_t)dwr_plan(T, h, E).nsplit * (size_t)(h + 1) * E * 4;
-}
-hipError_t launch_dwr(const void* U, const float* dH, float* dWr, float* db, float* part, int T,
+inline size_t dwr_part_bytes(int64_t T, int h, int E) { return dwr_plan(T, h, E).bytes; }
+hipError_t launch_dwr(const void* U, const float* dH, float* dWr, float* db, void* ws, int T,
                       int h, int E, hipStream_t s);
 
 }  // namespace moe

@@ -289,20 +289,6 @@ struct LogitsCfg {
   static_assert(NS >= 3 && (NS - 2) * NCOPY < 64, "ring");
 };
 
-// Weight rows in LDS: k-row r (BN columns, NCH = BN / 8 chunks of 16 bytes)
-// keeps logical chunk c at chunk c ^ wsw(r).  A transposing read of one
-// fragment touches, per half-wave, 8 k-rows (rows 8 g + q, g = 0/1, q = 0..3)
-// x 2 adjacent chunks; wsw spreads those 16 pieces over distinct 16-byte bank
-// groups (for NCH >= 4; two-chunk rows keep a two-way conflict).
-template <int NCH>
-__device__ __forceinline__ int wsw(int r) {
-  const int g1 = (r >> 3) & 1, q = r & 3;
-  if constexpr (NCH >= 16) return 2 * (4 * g1 + q);
-  else if constexpr (NCH == 8) return 4 * g1 + 2 * (q >> 1);
-  else if constexpr (NCH == 4) return 2 * g1;
-  else return 0;
-}
-
 template <int BM_, int BN, int NSRC, int WM>
 __global__ __launch_bounds__(256) void route_logits_kernel(LogitsArgs p) {
   using C = LogitsCfg<BM_, BN, NSRC>;
@@ -669,6 +655,29 @@ hipError_t launch_route(const RouteShape& rs, const RouteParams& p, int use_bf16
     MOE_ROUTE_F32(8, true) MOE_ROUTE_F32(16, true)
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_route_products(const RouteShape& rs, const void* U, const void* W, float* part,
+                                 int T, int h, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  LogitsArgs a;
+  a.U = static_cast<const bf16*>(U);
+  a.W0 = a.W1 = static_cast<const bf16*>(W);
+  a.part = part;
+  a.T = T;
+  a.h = h;
+  a.Ew = rs.Ew;
+  a.EP = rs.EP;
+  a.KS = rs.KS;
+  a.KT = h / 64;
+  a.nblocks = rs.nblocks;
+  const int nsrc = 1;
+  const unsigned grid = (unsigned)(rs.mblocks * rs.nblocks * rs.KS);
+  bool launched = false;
+  MOE_ROUTE_LOGITS(64, 16, 1, 4) MOE_ROUTE_LOGITS(64, 32, 1, 2) MOE_ROUTE_LOGITS(64, 64, 1, 2)
+  MOE_ROUTE_LOGITS(64, 128, 1, 1) MOE_ROUTE_LOGITS(128, 64, 1, 2) MOE_ROUTE_LOGITS(128, 128, 1, 2)
+  if (!launched) return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_prob_reduce(const double* part, int nblk, int EP, int E, double* total,
