@@ -33,7 +33,13 @@ namespace moe {
 namespace {
 
 // Combine backward, one wave per token: dY[slot] = g dOut_t for every kept
-// rank, and dgate[t, r] = dOut_t . Y[slot] (0 for a dropped rank).
+// rank, and dgate[t, r] = dOut_t . Y[slot] (0 for a dropped rank).  A lane
+// takes one 16-byte vector of the row per pass: dOut's once, and those of the
+// KM rank rows (a dropped or absent rank reads dOut's row, masked to +0, and
+// stores nothing).  The next pass's loads are issued before this pass's
+// stores, since a load queued behind a store waits for it; each rank's dot
+// product runs over the lane's vectors in row order, as before the split.
+template <int KM>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16* dOut, const bf16* Y,
                                                           const int32_t* slot, const float* gate,
                                                           bf16* dY, float* dgate, int T, int h,
@@ -41,29 +47,85 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16* dOut, cons
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  const int nvec = h / 8;
+  const int nvec = h / 8, iters = (nvec + 63) / 64;
   const bf16* d = dOut + (size_t)t * h;
-  for (int r = 0; r < k; ++r) {
-    const int row = slot[(size_t)t * k + r];
-    float acc = 0.f;
-    if (row >= 0) {
-      const float g = gate[(size_t)t * k + r];
-      const bf16* y = Y + (size_t)row * h;
-      bf16* dy = dY + (size_t)row * h;
-      for (int i = lane; i < nvec; i += 64) {
-        float a[8], b[8];
-        Elem<bf16>::unpack(ld16(d + (size_t)i * 8), a);
-        Elem<bf16>::unpack(ld16(y + (size_t)i * 8), b);
+  int sl[KM];
+  float g[KM], acc[KM];
+  const bf16* src[KM];
+  uint32_t keep[KM];
+  int sv[KM];
+  float gv[KM];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          acc = fmaf(a[q], b[q], acc);
-          a[q] *= g;
-        }
-        st16(dy + (size_t)i * 8, Elem<bf16>::pack(a));
-      }
+  for (int r = 0; r < KM; ++r) {  // all issued at once, clamped to rank k - 1
+    sv[r] = slot[(size_t)t * k + min(r, k - 1)];
+    gv[r] = gate[(size_t)t * k + min(r, k - 1)];
+  }
+#pragma unroll
+  for (int r = 0; r < KM; ++r) {
+    sl[r] = r < k ? sv[r] : -1;
+    g[r] = r < k ? gv[r] : 0.f;
+    acc[r] = 0.f;
+    src[r] = sl[r] >= 0 ? Y + (size_t)sl[r] * h : d;
+    keep[r] = sl[r] >= 0 ? 0xffffffffu : 0u;
+  }
+  // rank r's dY row as a buffer (the wave's token, so the row is uniform)
+  __amdgpu_buffer_rsrc_t rdy[KM];
+#pragma unroll
+  for (int r = 0; r < KM; ++r) {
+    const int row = __builtin_amdgcn_readfirstlane(sl[r]);
+    rdy[r] = make_rsrc(dY + (size_t)(row >= 0 ? row : 0) * h, row >= 0 ? (size_t)h * 2 : 0);
+  }
+  u32x4 bd[2], by[2][KM];
+  // loads of pass it (lanes past the row re-read its last vector, and their
+  // rank vectors are masked to +0)
+  auto issue = [&](int it, u32x4& od, u32x4* oy) __attribute__((always_inline)) {
+    const int i = lane + 64 * it;
+    const size_t v = (size_t)min(i, nvec - 1) * 8;
+    const uint32_t in = i < nvec ? 0xffffffffu : 0u;
+    od = ld16(d + v);
+#pragma unroll
+    for (int r = 0; r < KM; ++r) {
+      const bf16* q = src[r] + v;
+      asm("" : "+v"(q));  // keeps the load unconditional (see grad_input_kernel)
+      const uint32_t m = keep[r] & in;
+      oy[r] = *(const __attribute__((address_space(1))) u32x4*)q & u32x4{m, m, m, m};
     }
-    acc = wave_sum(acc);
-    if (lane == 0) dgate[(size_t)t * k + r] = acc;
+  };
+  auto consume = [&](int it, const u32x4& od, const u32x4* oy) __attribute__((always_inline)) {
+    const int i = lane + 64 * it;
+    float a[8], y[8];
+    Elem<bf16>::unpack(od, a);
+#pragma unroll
+    for (int r = 0; r < KM; ++r) {
+      Elem<bf16>::unpack(oy[r], y);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[r] = fmaf(a[q], y[q], acc[r]);
+    }
+    // buffer stores, one per rank and pass whatever the rank: a dropped
+    // rank's or a lane's past the row is sent past the row's end and
+    // dropped, so no branch hides from the waits how many are in flight
+#pragma unroll
+    for (int r = 0; r < KM; ++r) {
+      float o[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[q] = a[q] * g[r];
+      __builtin_amdgcn_raw_buffer_store_b128(Elem<bf16>::pack(o), rdy[r],
+                                             sl[r] >= 0 && i < nvec ? i * 16 : kPastEnd, 0, 0);
+    }
+  };
+  issue(0, bd[0], by[0]);
+  for (int it = 0; it < iters; it += 2) {
+    if (it + 1 < iters) issue(it + 1, bd[1], by[1]);
+    consume(it, bd[0], by[0]);
+    if (it + 1 >= iters) break;
+    if (it + 2 < iters) issue(it + 2, bd[0], by[0]);
+    consume(it + 1, bd[1], by[1]);
+  }
+#pragma unroll
+  for (int r = 0; r < KM; ++r) {
+    if (r >= k) break;
+    const float v = wave_sum(acc[r]);
+    if (lane == 0) dgate[(size_t)t * k + r] = v;
   }
 }
 
@@ -697,9 +759,15 @@ hipError_t launch_combine_bwd(const void* dOut, const void* Y, const int32_t* sl
                               const float* gate, void* dY, float* dgate, int T, int h, int k,
                               hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_bwd_kernel, dim3((T + 3) / 4), dim3(256), 0, s,
-                     static_cast<const bf16*>(dOut), static_cast<const bf16*>(Y), slot, gate,
-                     static_cast<bf16*>(dY), dgate, T, h, k);
+  if (k < 1 || k > 8) return hipErrorInvalidValue;
+  if (k <= 2)
+    hipLaunchKernelGGL(combine_bwd_kernel<2>, dim3((T + 3) / 4), dim3(256), 0, s,
+                       static_cast<const bf16*>(dOut), static_cast<const bf16*>(Y), slot, gate,
+                       static_cast<bf16*>(dY), dgate, T, h, k);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<8>, dim3((T + 3) / 4), dim3(256), 0, s,
+                       static_cast<const bf16*>(dOut), static_cast<const bf16*>(Y), slot, gate,
+                       static_cast<bf16*>(dY), dgate, T, h, k);
   return hipGetLastError();
 }
 
