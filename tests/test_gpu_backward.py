@@ -55,6 +55,12 @@ BWD = {
     # weight gradients must be written as exact zeros
     "idle_experts": I.WORKLOADS["mixtral_bf16"].replace(name="idle_experts", T=6, h=128, f=192,
                                                         E=16, k=1),
+    # 200 experts: two expert tiles of 128 in the router weight gradient, the
+    # second zero-padded, and a last 32-expert step of dU's product that is
+    # partly past E; k = 6 under the 8-rank gathers of dU and the combine
+    # backward (two absent ranks)
+    "wide_e200_k6": I.WORKLOADS["mixtral_bf16"].replace(name="wide_e200_k6", T=600, h=256,
+                                                        f=128, E=200, k=6, capacity_factor=1.0),
 }
 
 
@@ -369,6 +375,11 @@ EXTRA = {
     "ragged_noisy_shared": L.SMALL["noisy_small"].replace(name="ragged_noisy_shared", T=777,
                                                           h=192, f=192, E=6, n_shared=1,
                                                           f_shared=64),
+    # E = 100 (not a multiple of 8: element-wise operand loads in dU's
+    # product, a padded W_noise for the recomputed Z, one zero-padded expert
+    # tile of 128 in dW_r and dW_noise) with k = 3 and a shared expert
+    "noisy_e100_k3": L.SMALL["noisy_small"].replace(name="noisy_e100_k3", T=500, h=192, f=128,
+                                                    E=100, k=3, n_shared=1, f_shared=64),
 }
 
 
