@@ -289,8 +289,13 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams& p,
     const int rr = (wave & 1) * 32 + 2 * q + kh;  // row within the slot
     const int r = wm * 64 + rr;                   // row within the tile
     const uint4 v = *reinterpret_cast<const uint4*>(src + rr * 512 + ((l32 ^ (rr & 31)) * 16));
+    // non-temporal: the gradient is not read again here, and a stream of
+    // whole lines that bypasses L2's retention leaves the operand panels
+    // there (5% on the Mixtral shape; the streaming kernel's stores, which
+    // cover a line only across instructions, ran 3.6x slower so marked)
     if (r < ta.nvalid && col < p.Nout)
-      *reinterpret_cast<uint4*>(p.C + (size_t)(ta.row0 + r) * p.Nout + col) = v;
+      __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
+                                  reinterpret_cast<u32x4*>(p.C + (size_t)(ta.row0 + r) * p.Nout + col));
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   barrier_only();  // the slots are free for the next unit's copies
