@@ -374,43 +374,15 @@ __global__ __launch_bounds__(256) void grad_input_kernel(const bf16* dOut, const
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) b[nb] = gi_load_b<VEC>(W, br[nb], el, E);
   };
-  load(0);
-  for (int st = 0; st < steps; ++st) {
-    bf16x8 hi[2], lo[2], bc[4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      float am[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) am[q] = a[mb][q];
-      gi_mask_a<VEC>(am, el, E);
-      gi_split(am, hi[mb], lo[mb]);
-    }
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) bc[nb] = gi_mask_b<VEC>(b[nb], el, E);
-    if (st + 1 < steps) load(st + 1);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[mb], bc[nb], acc[mb][nb], 0, 0, 0);
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[mb], bc[nb], acc[mb][nb], 0, 0, 0);
-      }
-  }
-  // D layout: lane holds column l16 of rows 4 g + i
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        tile[wm * 32 + 16 * mb + 4 * g + i][wn * 64 + 16 * nb + l16] = acc[mb][nb][i];
-  __syncthreads();
-
-  // a thread's rows: ty + 16 i (rows past T read row T - 1, store nothing);
-  // its columns: 8 tx .. 8 tx + 7
+  // The gather: a thread's rows are ty + 16 i (rows past T read row T - 1
+  // and store nothing), its columns 8 tx .. 8 tx + 7.  Its first row's loads
+  // go out right after the product's first operand loads, so that their
+  // latency overlaps the product.
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  if (j0 + tx * 8 >= h) return;  // h % 64 == 0: the last tile may hold 64 columns
-  const size_t j = (size_t)j0 + tx * 8;
+  // h % 64 == 0: the last tile may hold only 64 columns; the threads past
+  // them read the last valid columns and store nothing
+  const bool jin = j0 + tx * 8 < h;
+  const size_t j = (size_t)min(j0 + tx * 8, h - 8);
   int tr[4], sl[4][KM];
 #pragma unroll
   for (int i = 0; i < 4; ++i) tr[i] = min(t0 + ty + 16 * i, T - 1);
@@ -443,7 +415,40 @@ __global__ __launch_bounds__(256) void grad_input_kernel(const bf16* dOut, const
     }
     if constexpr (SH) bb[1 + KM] = ld16(dXs + (size_t)tr[i] * h + j);
   };
+  load(0);
   issue(0, buf[0]);
+  for (int st = 0; st < steps; ++st) {
+    bf16x8 hi[2], lo[2], bc[4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      float am[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) am[q] = a[mb][q];
+      gi_mask_a<VEC>(am, el, E);
+      gi_split(am, hi[mb], lo[mb]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) bc[nb] = gi_mask_b<VEC>(b[nb], el, E);
+    if (st + 1 < steps) load(st + 1);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[mb], bc[nb], acc[mb][nb], 0, 0, 0);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[mb], bc[nb], acc[mb][nb], 0, 0, 0);
+      }
+  }
+  // D layout: lane holds column l16 of rows 4 g + i
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        tile[wm * 32 + 16 * mb + 4 * g + i][wn * 64 + 16 * nb + l16] = acc[mb][nb][i];
+  __syncthreads();
+
+  if (!jin) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i + 1 < 4) issue(i + 1, buf[(i + 1) & 1]);
