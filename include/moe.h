@@ -365,7 +365,10 @@ typedef struct {
  *  extra: required (with every pointer of the part) for noisy layers and
  *  layers with shared experts, else may be NULL.
  *  Outputs: dU [T,h] and dW_gate, dW_up [E,f,h], dW_down [E,h,f] in bf16;
- *  dW_r [h,E] and db_r [E] (nullable) in float32.
+ *  dW_r [h,E] and db_r [E] (nullable) in float32.  The logits' gradient dH
+ *  is float32; its products with W_r (into dU) and with U (dW_r) run on bf16
+ *  matrix cores with dH as a bf16 pair hi + lo (about 2^-17 relative), summed
+ *  in float32, as do the noise term's (dZ, dW_noise).
  *  Supported: cfg->dtype == MOE_BF16 (else MOE_ERR_UNSUPPORTED); the routing
  *  may come from a selection bias or groups.  One expert's rows (at most
  *  min(C, T); T for a shared expert), plus 192, times 2 max(2 f, h, 2 f_shared)
@@ -430,7 +433,8 @@ int32_t moe_expert_ffn_backward_fp8(const moe_config* cfg, const void* X, const 
  * db_r (nullable) = column sums of dH.  dOut is the gradient that reaches u_t
  * directly (the residual; add the shared experts' input gradients to it);
  * dX [rows_max,h] the experts' input gradients.  extra: the noise part
- * (W_noise, dW_noise) for noisy layers.  ws: MOE_WS_ROUTER_BACKWARD. */
+ * (W_noise, dW_noise) for noisy layers.  ws: MOE_WS_ROUTER_BACKWARD.  The
+ * products with dH run as in moe_layer_backward (bf16 hi + lo pair). */
 int32_t moe_router_backward(const moe_config* cfg, const void* U, const void* W_r,
                             const float* logits, const int32_t* topk_idx, const float* topk_gate,
                             const int32_t* slot, const int32_t* count, const float* dgate,
