@@ -166,9 +166,10 @@ typedef enum {
 } moe_ws_entry;
 
 /* Stage boundaries recorded by moe_layer_forward when stage_events != NULL:
- * events[0] before the router ... events[MOE_NUM_STAGES] after the last stage.
- * The router's P sums are reduced in the route stage and the load statistics
- * are computed inside the dispatch stage, so the stats stage is empty. */
+ * events[0] before the router ... events[MOE_NUM_STAGES] after the last stage;
+ * a NULL entry leaves that boundary unrecorded.  The router's P sums and the
+ * load statistics are computed inside the dispatch stage, so the stats stage
+ * is empty. */
 enum { MOE_NUM_STAGES = 6 }; /* route, dispatch, gate_up, down, combine, stats */
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -299,8 +300,8 @@ int32_t moe_router_z_loss(const moe_config* cfg, const float* logits, float* z_l
  *  shared-expert weights as in moe_shared_ffn, required iff cfg->n_shared > 0;
  *  their products run in the gate_up and down stages.
  *  out [T,h] required.  aux: optional outputs (struct pointer may be NULL).
- *  stage_events: NULL, or MOE_NUM_STAGES + 1 hipEvent_t handles recorded on
- *  `stream` at the stage boundaries (for timing).  ws: MOE_WS_LAYER bytes. */
+ *  stage_events: NULL, or MOE_NUM_STAGES + 1 hipEvent_t handles (each may be
+ *  NULL) recorded on `stream` at the stage boundaries (for timing).  ws: MOE_WS_LAYER bytes. */
 int32_t moe_layer_forward(const moe_config* cfg, const void* U, const void* W_r,
                           const float* b_r, const float* b_sel, const void* W_noise,
                           const void* W_gate, const void* W_up,

@@ -414,6 +414,9 @@ def _layer_call(fn_name, cfg, U, W_r, b_r, W_noise, weights, W_down, out, aux,
             raise ValueError("stage_events needs MOE_NUM_STAGES + 1 events")
         handles = []
         for e in stage_events:
+            if e is None:  # that boundary is not recorded
+                handles.append(None)
+                continue
             if e.cuda_event == 0:  # torch creates the HIP event lazily
                 e.record()
             handles.append(e.cuda_event)
@@ -441,7 +444,7 @@ def moe_layer_forward(cfg, U, W_r, b_r, W_noise, W_gate, W_up, W_down, out, aux=
                       stage_events=None, ws=None, stream=None, b_sel=None, Ws_gate=None,
                       Ws_up=None, Ws_down=None):
     """The whole layer.  aux: dict of optional output tensors (see alloc_aux).
-    stage_events: list of MOE_NUM_STAGES + 1 torch.cuda.Event(enable_timing=True),
+    stage_events: list of MOE_NUM_STAGES + 1 torch.cuda.Event(enable_timing=True) or None,
     recorded inside the library on the same stream.  b_sel, Ws_*: the
     selection bias and the shared-expert weights (cfg.n_shared > 0)."""
     E, f, h, dt = cfg.E, cfg.f, cfg.h, _elem_dtype(cfg)

@@ -359,7 +359,7 @@ int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP
 int32_t run_route(const Dims& d, const moe_config* c, const RouteWs& w, const void* U,
                   const void* W_r, const float* b_r, const float* b_sel, const void* W_noise,
                   float* noise_out, int32_t* idx, float* gate, float* logits, void* ws,
-                  hipStream_t s) {
+                  hipStream_t s, int32_t* hist = nullptr) {
   RouteParams p;
   p.T = (int)d.T;
   p.h = (int)d.h;
@@ -395,6 +395,7 @@ int32_t run_route(const Dims& d, const moe_config* c, const RouteWs& w, const vo
       p.Wn = at<void>(ws, w.wnp);
     }
     p.lpart = at<float>(ws, w.lpart);
+    p.hist = hist;
   }
   MOE_TRY(launch_route(w.rs, p, d.bf16, c->noisy, s));
   return MOE_OK;
@@ -748,9 +749,6 @@ int32_t layer_impl(const moe_config* cfg, const void* U, const void* W_r, const 
   if (cfg->noisy && !W_noise) return MOE_ERR_INVALID_ARG;
   if (d.T > 0 && out == U) return MOE_ERR_INVALID_ARG;
   if (aux && aux->GU && (!d.bf16 || f8)) return MOE_ERR_UNSUPPORTED;
-  if (stage_events)
-    for (int i = 0; i <= MOE_NUM_STAGES; ++i)
-      if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
   Plan pl;
   const LayerWs w = plan_layer(d, cfg->noisy, pl);
   if (ws_bytes < pl.bytes) return MOE_ERR_WORKSPACE;
@@ -772,20 +770,26 @@ int32_t layer_impl(const moe_config* cfg, const void* U, const void* W_r, const 
   void* Ys = d.ns == 0 ? nullptr : (o.Y_shared ? o.Y_shared : at<void>(ws, w.sh.Ys));
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto mark = [&](int i) -> hipError_t {
-    return stage_events ? hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s)
-                        : hipSuccess;
+    return (stage_events && stage_events[i])
+               ? hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s)
+               : hipSuccess;
   };
 
   MOE_TRY(mark(0));
+  // bf16: the selection kernel also counts the dispatch histograms
   st = run_route(d, cfg, w.route, U, W_r, b_r, b_sel, W_noise, o.noise, idx, gate, o.logits,
-                 ws, s);
+                 ws, s, d.bf16 ? at<int32_t>(ws, w.disp.hist) : nullptr);
   if (st != MOE_OK) return st;
-  MOE_TRY(launch_prob_reduce(at<double>(ws, w.route.part), w.route.rs.nblk, w.route.rs.EP,
-                             (int)d.E, at<double>(ws, w.route.total), o.prob_sum, s));
   MOE_TRY(mark(1));
-  // the dispatch's scan workgroup also writes the GEMMs' tile maps and the
-  // load statistics
+  // the dispatch's scan launch also writes the GEMMs' tile maps and sums the
+  // router's P partials; its assignment launch computes the load statistics
   DispatchParams fused;
+  fused.hist_ready = d.bf16;
+  fused.prob_part = at<double>(ws, w.route.part);
+  fused.prob_nblk = w.route.rs.nblk;
+  fused.prob_EP = w.route.rs.EP;
+  fused.prob_total = at<double>(ws, w.route.total);
+  fused.prob_out = o.prob_sum;
   if (d.bf16) {
     fused.bm1 = w.ffn.fs.bm1;
     fused.bm2 = w.ffn.fs.bm2;

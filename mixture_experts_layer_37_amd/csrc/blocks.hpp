@@ -79,4 +79,35 @@ __device__ __forceinline__ void stats_block(const StatsParams& p, int e, int cnt
   }
 }
 
+// Router P sums: workgroup e of E + 1 reduces row e (row EP for e == E, the
+// LSE^2 row) of the [EP + 1][nblk] per-block partials.  Thread j adds
+// partials j, j + 256, ... in order, then a fixed-shape tree adds the 256
+// sums (deterministic).  The LSE^2 sum lands in total[E] (z-loss numerator);
+// out gets the E expert sums only.
+__device__ __forceinline__ void prob_reduce_block(const double* part, int nblk, int EP, int E,
+                                                  double* total, float* out, int e) {
+  __shared__ double sh[256];
+  const int col = e < E ? e : EP;
+  const double* row = part + (size_t)col * nblk;
+  double s = 0.0;
+  for (int b0 = threadIdx.x; b0 < nblk; b0 += 8 * 256) {
+    double v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = b0 + i * 256 < nblk ? row[b0 + i * 256] : 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (b0 + i * 256 < nblk) s += v[i];
+  }
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    if (total) total[e] = sh[0];
+    if (out && e < E) out[e] = (float)sh[0];
+  }
+}
+
 }  // namespace moe

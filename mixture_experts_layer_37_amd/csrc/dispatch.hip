@@ -61,6 +61,11 @@ __global__ __launch_bounds__(256) void hist_kernel(DispatchParams p) {
 }
 
 __global__ __launch_bounds__(256) void scan_kernel(DispatchParams p, int nchunk) {
+  if (blockIdx.x > 0) {  // the router's P sums (layer forward)
+    prob_reduce_block(p.prob_part, p.prob_nblk, p.prob_EP, p.E, p.prob_total, p.prob_out,
+                      blockIdx.x - 1);
+    return;
+  }
   __shared__ int tmp[4];
   const int e = threadIdx.x;
   int run = 0;
@@ -106,12 +111,17 @@ __global__ __launch_bounds__(256) void scan_kernel(DispatchParams p, int nchunk)
     __shared__ int tmp2[8];
     tile_maps_block(e, p.E, e < p.E ? kp : 0, off, p.bm1, p.bm2, p.map1, p.map2, tmp2);
   }
-  if (p.stats_on) stats_block(p.stats, e, run, kp);
+  if (p.stats_on && !p.prob_part) stats_block(p.stats, e, run, kp);
 }
 
-__global__ __launch_bounds__(256) void assign_kernel(DispatchParams p) {
+__global__ __launch_bounds__(256) void assign_kernel(DispatchParams p, int nchunk) {
+  if (blockIdx.x >= nchunk) {  // the load statistics, once the scan launch's P sums are in
+    const int e = threadIdx.x;
+    stats_block(p.stats, e, e < p.E ? p.count[e] : 0, e < p.E ? p.kept[e] : 0);
+    return;
+  }
   __shared__ int wc[4][256];
-  const int nchunk = gridDim.x, c = blockIdx.x;
+  const int c = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = c * kChunk + threadIdx.x;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -352,15 +362,19 @@ hipError_t dispatch_scratch(int32_t** out) {
 
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s) {
   const int nchunk = (p.T + kChunk - 1) / kChunk;
-  if (nchunk > 0) {
+  if (nchunk > 0 && !p.hist_ready) {
     hipLaunchKernelGGL(hist_kernel, dim3(nchunk), dim3(256), 0, s, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, p, nchunk);
+  // with the P sums folded in, workgroups 1 .. E+1 sum them and the
+  // statistics move to one more workgroup of the assignment launch
+  const bool psum = p.prob_part != nullptr;
+  hipLaunchKernelGGL(scan_kernel, dim3(psum ? p.E + 2 : 1), dim3(256), 0, s, p, nchunk);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || nchunk == 0) return err;
-  hipLaunchKernelGGL(assign_kernel, dim3(nchunk), dim3(256), 0, s, p);
+  const int ablocks = nchunk + ((psum && p.stats_on) ? 1 : 0);
+  if (err != hipSuccess || ablocks == 0) return err;
+  hipLaunchKernelGGL(assign_kernel, dim3(ablocks), dim3(256), 0, s, p, nchunk);
   return hipGetLastError();
 }
 

@@ -30,6 +30,9 @@ struct RouteParams {
   float* logits;     // optional [T][E]
   double* prob_part; // [EP + 1][nblk] per-block sums of the score entering P;
                      // row EP: sum over the block's tokens of LSE(H_t)^2
+  // bf16 path, optional: the dispatch histograms [k][nchunk][E] (kChunk-token
+  // chunks), cleared by the logits kernel and counted by the selection kernel
+  int32_t* hist = nullptr;
 };
 
 struct RouteShape {
@@ -100,6 +103,16 @@ struct DispatchParams {
   int32_t* map2 = nullptr;
   int stats_on = 0;
   StatsParams stats{};
+  // The layer forward: hist already holds the histograms (counted by the
+  // selection kernel), and the scan launch's workgroups 1 .. E+1 also sum the
+  // router's per-block P partials [prob_EP + 1][prob_nblk] into prob_total
+  // (and prob_out, the E expert sums), the statistics then running in one
+  // more workgroup of the assignment launch.
+  int hist_ready = 0;
+  const double* prob_part = nullptr;
+  int prob_nblk = 0, prob_EP = 0;
+  double* prob_total = nullptr;
+  float* prob_out = nullptr;
 };
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s);
 // Bytes of the fixed device array behind moe_dispatch_noalloc, and its

@@ -23,6 +23,7 @@
 // max / sum / argmax as butterfly reductions (DPP and lane swaps, no LDS).
 #include <math.h>
 
+#include "blocks.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -248,6 +249,11 @@ __device__ void route_epilogue(const Src& src, double (*Ps)[EP + 1], const Route
     if (lane < k) {
       p.topk_idx[(size_t)t * k + lane] = my_idx;
       p.topk_gate[(size_t)t * k + lane] = (p.gate == 1) ? my_s / gsum : my_s;
+      // the dispatch's per-(rank, 256-token chunk) expert histogram: integer
+      // sums, the same whatever order the increments land in
+      if (p.hist)
+        atomicAdd(p.hist + ((size_t)lane * ((p.T + kChunk - 1) / kChunk) + t / kChunk) * E + my_idx,
+                  1);
     }
   }
   // per-workgroup sums of the P score and (column EP) of LSE^2, waves added
@@ -271,6 +277,8 @@ struct LogitsArgs {
   const bf16* W1;       // W_noise [h][Ew] (noisy)
   float* part;          // [NSRC][KS][T][EP]
   int T, h, Ew, EP, KS, KT, nblocks;  // KT: 64-wide K chunks (h / 64)
+  int32_t* zero = nullptr;  // nzero ints this launch clears (the dispatch
+  int nzero = 0;            // histograms the selection kernel then fills)
 };
 
 // Stage geometry: one stage holds a 64-wide K chunk of BM U rows (128 bytes
@@ -310,6 +318,7 @@ __global__ __launch_bounds__(256) void route_logits_kernel(LogitsArgs p) {
   const int kc0 = ks * p.KT / p.KS, KTl = (ks + 1) * p.KT / p.KS - kc0;
   const int rows = min(BM, p.T - m0);
   const int h = p.h, Ew = p.Ew;
+  for (int i = blockIdx.x * 256 + tid; i < p.nzero; i += G * 256) p.zero[i] = 0;
 
   // loop-invariant parts of this lane's copy offsets
   int offA[C::NAI], offB[C::NBI];
@@ -529,36 +538,9 @@ __global__ void pad_rows_kernel(const bf16* W, bf16* Wp, int h, int E, int Ew) {
   }
 }
 
-// One workgroup per expert (then one for the LSE^2 row), over that row of
-// the [EP + 1][nblk] partials: thread j adds partials j, j + 256, ... in
-// order, then a fixed-shape tree adds the 256 sums (deterministic).  The
-// LSE^2 sum lands in total[E] (z-loss numerator); out gets the E expert sums
-// only.
 __global__ __launch_bounds__(256) void prob_reduce_kernel(const double* part, int nblk, int EP,
                                                           int E, double* total, float* out) {
-  __shared__ double sh[256];
-  const int e = blockIdx.x;
-  const int col = e < E ? e : EP;
-  const double* row = part + (size_t)col * nblk;
-  double s = 0.0;
-  for (int b0 = threadIdx.x; b0 < nblk; b0 += 8 * 256) {
-    double v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = b0 + i * 256 < nblk ? row[b0 + i * 256] : 0.0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (b0 + i * 256 < nblk) s += v[i];
-  }
-  sh[threadIdx.x] = s;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    if (total) total[e] = sh[0];
-    if (out && e < E) out[e] = (float)sh[0];
-  }
+  prob_reduce_block(part, nblk, EP, E, total, out, blockIdx.x);
 }
 
 }  // namespace
@@ -633,6 +615,10 @@ hipError_t launch_route(const RouteShape& rs, const RouteParams& p, int use_bf16
     a.KS = rs.KS;
     a.KT = p.h / 64;
     a.nblocks = rs.nblocks;
+    if (p.hist) {
+      a.zero = p.hist;
+      a.nzero = p.k * ((p.T + kChunk - 1) / kChunk) * p.E;
+    }
     const int nsrc = noisy ? 2 : 1;
     const unsigned grid = (unsigned)(rs.mblocks * rs.nblocks * rs.KS);
     bool launched = false;
