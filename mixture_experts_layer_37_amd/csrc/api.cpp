@@ -776,15 +776,19 @@ int32_t layer_impl(const moe_config* cfg, const void* U, const void* W_r, const 
   };
 
   MOE_TRY(mark(0));
-  // bf16: the selection kernel also counts the dispatch histograms
+  // bf16 with many experts: the selection kernel also counts the dispatch
+  // histograms.  Each 256-token chunk and rank adds about 256 / E increments
+  // to each counter; with few experts (E = 8: 32) those atomics queue on the
+  // same addresses and cost more than the histogram launch they replace.
+  const bool hist_in_select = d.bf16 && d.E >= 32;
   st = run_route(d, cfg, w.route, U, W_r, b_r, b_sel, W_noise, o.noise, idx, gate, o.logits,
-                 ws, s, d.bf16 ? at<int32_t>(ws, w.disp.hist) : nullptr);
+                 ws, s, hist_in_select ? at<int32_t>(ws, w.disp.hist) : nullptr);
   if (st != MOE_OK) return st;
   MOE_TRY(mark(1));
   // the dispatch's scan launch also writes the GEMMs' tile maps and sums the
   // router's P partials; its assignment launch computes the load statistics
   DispatchParams fused;
-  fused.hist_ready = d.bf16;
+  fused.hist_ready = hist_in_select;
   fused.prob_part = at<double>(ws, w.route.part);
   fused.prob_nblk = w.route.rs.nblk;
   fused.prob_EP = w.route.rs.EP;
