@@ -74,6 +74,8 @@ EDGE = {
     "E1": L.SMALL["mixtral_small"].replace(T=300, E=1, k=1),
     "C1": L.SMALL["mixtral_small"].replace(T=700, capacity_factor=1e-3),
     "token_major": L.SMALL["noisy_small"].replace(fill="token_major", capacity_factor=0.6),
+    # 32 experts: the selection kernel counts the dispatch histograms
+    "token_major_E32": L.SMALL["switch_small"].replace(fill="token_major", capacity_factor=0.6),
     "cap_tokens": L.SMALL["mixtral_small"].replace(cap_mode="tokens"),
     "min_capacity": L.SMALL["switch_small"].replace(capacity_factor=0.2, min_capacity=40),
     "dropless": L.SMALL["switch_small"].replace(capacity_factor=0.0),
@@ -294,9 +296,10 @@ def test_router_z_loss_entry(T, E, scale):
     np.testing.assert_allclose(float(z.cpu()[0]), want, rtol=2e-6, atol=1e-7)
 
 
-def test_empty_batch():
-    w = L.SMALL["mixtral_small"].replace(T=0)
-    L.log("[edge] T = 0")
+@pytest.mark.parametrize("name", ["mixtral_small", "switch_small"])
+def test_empty_batch(name):
+    w = L.SMALL[name].replace(T=0)
+    L.log(f"[edge] T = 0 ({name})")
     x = I.make_inputs(w, seed=0, device=DEV)
     cfg, g = L.run_layer(w, x)
     assert (L.to_np(g["count"]) == 0).all() and (L.to_np(g["offset"]) == 0).all()
