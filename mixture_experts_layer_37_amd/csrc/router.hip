@@ -251,9 +251,10 @@ __device__ void route_epilogue(const Src& src, double (*Ps)[EP + 1], const Route
       p.topk_gate[(size_t)t * k + lane] = (p.gate == 1) ? my_s / gsum : my_s;
       // the dispatch's per-(rank, 256-token chunk) expert histogram: integer
       // sums, the same whatever order the increments land in
-      if (p.hist)
-        atomicAdd(p.hist + ((size_t)lane * ((p.T + kChunk - 1) / kChunk) + t / kChunk) * E + my_idx,
-                  1);
+      if (p.hist) {
+        const int nchunk = (p.T + kChunk - 1) / kChunk;
+        atomicAdd(p.hist + ((size_t)lane * nchunk + t / kChunk) * E + my_idx, 1);
+      }
     }
   }
   // per-workgroup sums of the P score and (column EP) of LSE^2, waves added
