@@ -141,6 +141,7 @@ struct FfnShape {
   int split_max;    // most K chunks of a tail tile
   int part_slots;   // K-split partial tiles (256 x 256 float32 each), shared by the two GEMMs
   int gn1, gn2;     // n-tiles per group of each GEMM's tile numbering
+  int wstream;      // 1: experts fit one m-tile (weight-streaming copy schedule)
 };
 constexpr size_t kPartSlotBytes = 256 * 256 * sizeof(float);
 // ncu: compute units of the device (the persistent grid size)
