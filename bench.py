@@ -49,6 +49,9 @@ def parse():
                          "recomputes them")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the forward captured once in a HIP graph and replayed "
+                         "(reported beside the eager figures, never as the value)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -265,6 +268,39 @@ def cpu_baseline(w, x, g, budget_s: float) -> dict:
                        f"{est:.1f} s per full forward")}
 
 
+def graph_replay(step, out, steps: int) -> dict:
+    """The same forward captured once in a HIP graph and replayed `steps` times.
+
+    Every kernel of the forward is enqueued on the current stream with no
+    host synchronisation, memset or allocation, so it can be captured; the
+    replays' output is checked bit for bit against an eager forward's first.
+    """
+    import torch
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    out.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out, eager))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return {"ms_per_step": e0.elapsed_time(e1) / steps, "identical_to_eager": same}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -455,6 +491,8 @@ def main():
         "stage_ms": stage_ms,
         "stage_gbs": stage_bandwidth(w, stage_ms, kept, e_active, eb),
     }
+    if args.graph and not args.backward:
+        res["graph"] = graph_replay(step, out, args.steps)
     if args.backward:
         # the backward's products: dgrad 6 h f and wgrad 6 h f per kept row and
         # per token and shared expert (useful); executed adds the recomputed
